@@ -1,0 +1,27 @@
+"""CPU oracle for group-wise asymmetric INT4 weight quantization, the W4A16
+linear layer and the activation-aware scale search.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline may import this package. It shares no code with the HIP library and
+imports nothing from it.
+"""
+
+from .awq_oracle import (  # noqa: F401
+    QMAX,
+    RANGE_FLOOR,
+    MEAN_FLOOR,
+    group_quantize,
+    pack_codes,
+    unpack_codes,
+    quantize,
+    dequantize,
+    linear_ref,
+    activation_absmean,
+    alpha_grid,
+    channel_scales,
+    searched_weight,
+    search_loss_direct,
+    gram,
+    search_loss_gram,
+    scale_search,
+)

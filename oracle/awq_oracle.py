@@ -1,0 +1,232 @@
+"""Plain, slow CPU oracle for the AWQ W4A16 hot path.
+
+TEST INFRASTRUCTURE. This module is imported only by the tests, by the smoke
+check and by the benchmark's CPU-baseline leg. It never touches the HIP
+library, and the HIP library never touches it.
+
+Sources (the pages this follows):
+  [P1] rskf.cn AWQ article (news/13914): §1.1 RTN baseline, §2.1
+       "激活感知的缩放因子设计" (weights x s, activations / s, s searched to
+       minimise the quantized-vs-original output difference), §2.2 salient
+       channels, §2.3 / §4.1 scales folded ahead of inference.
+  [P3] "模型量化实战：INT8/INT4、GPTQ、AWQ与精度-速度权衡", sections
+       "量化粒度" (per-group, group_size=128) and "对称/非对称量化"
+       (asymmetric: zero-point != 0).
+  [P4] "AWQ 模型量化技术：激活感知的权重量化革命", "核心原理" (error =
+       |Q(w) - w| x |activation|) and "Per-channel Scaling 优化".
+  [P5] "模型量化:GGUF/AWQ/GPTQ部署方案", §1.2 "量化映射" (the affine map
+       q = clamp(round(x/scale) + zero_point, 0, 2^bits - 1), its inverse
+       x_hat = (q - zero_point) * scale, scale set by the weight range, and the
+       worked example: range [-1, 1] -> scale 2/15), §1.4 "量化粒度"
+       (128 weights per group).
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+  * scale = (wmax - wmin) / 15 over the group's own [min, max], computed as an
+    fp32 subtraction and an IEEE fp32 division; a range below 1e-5 is raised
+    to 1e-5 so a constant group still has a non-zero scale.
+  * the scale is stored as fp16 (round-to-nearest-even) and the codes are made
+    with that stored fp16 value, so dequantization uses exactly the scale the
+    codes were made with.
+  * zero_point = clamp(rint(-wmin / scale), 0, 15), stored as an integer-valued
+    fp16.
+  * "round" is round-half-to-even (np.rint); rounding happens before the
+    zero-point is added, as the formula on [P5 §1.2] is written.
+  * packing: eight codes along K per uint32, code k = 8c + j in bits 4j..4j+3.
+  * scale search: s = mean|x|^alpha per input channel, alpha_i = i / n_alpha;
+    ties between alphas go to the smallest alpha.
+
+Floating point: the quantizer's steps are taken in float32 exactly as the
+reading states them (NumPy float32 division and subtraction are IEEE
+correctly rounded, np.rint is half-to-even, astype(float16) is
+round-to-nearest-even). Every matrix product is float64.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+QMAX = 15                       # 2^bits - 1 for bits = 4   [P5 §1.2]
+RANGE_FLOOR = np.float32(1e-5)  # degenerate-group guard (reading)
+MEAN_FLOOR = 1e-8               # zero-activation-channel guard (reading)
+
+
+def _check_groups(K: int, group_size: int) -> None:
+    if group_size <= 0 or K % group_size != 0:
+        raise ValueError(f"K={K} is not a multiple of group_size={group_size}")
+
+
+def group_quantize(w, group_size: int, channel_scale=None):
+    """Group-wise asymmetric INT4 quantization of a weight matrix.
+
+    Follows the affine map of [P5 §1.2] with per-group granularity of
+    [P5 §1.4] / [P3 "量化粒度"] and a non-zero zero-point of
+    [P3 "对称/非对称量化"].
+
+    w:             [N, K] array (float16 weights; row n = output channel,
+                   column k = input channel). Groups run along K.
+    group_size:    G, the number of consecutive k sharing a scale/zero.
+    channel_scale: optional float32 [K]; when given, the weights quantized are
+                   float32(w[n, k] * channel_scale[k]) (AWQ's W * diag(s),
+                   [P1 §2.1]), one IEEE float32 product per element.
+
+    Returns (codes uint8 [N, K] in 0..15, scales float16 [N, K/G],
+    zeros float16 [N, K/G]).
+    """
+    w32 = np.asarray(w).astype(np.float32)
+    N, K = w32.shape
+    _check_groups(K, group_size)
+    if channel_scale is not None:
+        cs = np.asarray(channel_scale, dtype=np.float32).reshape(1, K)
+        w32 = w32 * cs                                  # float32 product
+    wg = w32.reshape(N, K // group_size, group_size)
+
+    # Range of each group: its own min and max.
+    wmin = wg.min(axis=2)
+    wmax = wg.max(axis=2)
+    rng = np.maximum(wmax - wmin, RANGE_FLOOR)          # float32 subtraction
+    # scale = range / (2^bits - 1), then stored as fp16.
+    s32 = rng / np.float32(QMAX)                        # IEEE float32 divide
+    s16 = s32.astype(np.float16)
+    sf = s16.astype(np.float32)
+    # zero-point: the integer that wmin maps to code 0.
+    z = np.clip(np.rint(-wmin / sf), 0, QMAX).astype(np.float32)
+    # codes: round(x / scale) first, then add the zero-point, then clamp.
+    q = np.rint(wg / sf[:, :, None]) + z[:, :, None]
+    q = np.clip(q, 0, QMAX)
+    codes = q.reshape(N, K).astype(np.uint8)
+    return codes, s16, z.astype(np.float16)
+
+
+def pack_codes(codes) -> np.ndarray:
+    """Pack eight 4-bit codes along K into one uint32.
+
+    Code of column k = 8c + j lands in bits 4j..4j+3 of word c (the plain
+    little-endian nibble order; the pages give none).
+    codes [N, K] (values 0..15) -> qweight uint32 [N, K/8].
+    """
+    c = np.asarray(codes).astype(np.uint32)
+    N, K = c.shape
+    if K % 8 != 0:
+        raise ValueError("K must be a multiple of 8 to pack nibbles")
+    c = c.reshape(N, K // 8, 8)
+    out = np.zeros((N, K // 8), dtype=np.uint32)
+    for j in range(8):
+        out |= c[:, :, j] << np.uint32(4 * j)
+    return out
+
+
+def unpack_codes(qweight, K: int) -> np.ndarray:
+    """Inverse of pack_codes: uint32 [N, K/8] -> uint8 codes [N, K]."""
+    q = np.asarray(qweight, dtype=np.uint32)
+    N = q.shape[0]
+    out = np.empty((N, K // 8, 8), dtype=np.uint8)
+    for j in range(8):
+        out[:, :, j] = (q >> np.uint32(4 * j)) & np.uint32(0xF)
+    return out.reshape(N, K)
+
+
+def quantize(w, group_size: int, channel_scale=None):
+    """The library's quantize call: (qweight uint32 [N,K/8], scales fp16
+    [N,K/G], zeros fp16 [N,K/G])."""
+    codes, s16, z16 = group_quantize(w, group_size, channel_scale)
+    return pack_codes(codes), s16, z16
+
+
+def dequantize(qweight, scales, zeros, group_size: int, K: int) -> np.ndarray:
+    """x_hat = (q - zero_point) * scale   [P5 §1.2], float64 [N, K].
+
+    Every value is exact in float64 (a 4-bit difference times an fp16)."""
+    codes = unpack_codes(qweight, K).astype(np.float64)
+    N = codes.shape[0]
+    _check_groups(K, group_size)
+    s = np.asarray(scales).astype(np.float64)
+    z = np.asarray(zeros).astype(np.float64)
+    cg = codes.reshape(N, K // group_size, group_size)
+    return ((cg - z[:, :, None]) * s[:, :, None]).reshape(N, K)
+
+
+def linear_ref(x, qweight, scales, zeros, group_size: int) -> np.ndarray:
+    """The W4A16 linear layer y = x . dequant(Wq)^T, float64 [M, N].
+
+    x: [M, K] (float16 activations). One float64 matrix product."""
+    x64 = np.asarray(x).astype(np.float64)
+    K = x64.shape[1]
+    w_hat = dequantize(qweight, scales, zeros, group_size, K)
+    return x64 @ w_hat.T
+
+
+# ---------------------------------------------------------------------------
+# Activation-aware scale search   [P1 §2.1], [P4 "Per-channel Scaling 优化"]
+# ---------------------------------------------------------------------------
+
+def activation_absmean(x) -> np.ndarray:
+    """m[k] = mean over tokens of |x[t, k]|, float64, floored at 1e-8."""
+    x64 = np.abs(np.asarray(x).astype(np.float64))
+    return np.maximum(x64.mean(axis=0), MEAN_FLOOR)
+
+
+def alpha_grid(n_alpha: int = 20) -> np.ndarray:
+    """alpha_i = i / n_alpha for i = 0..n_alpha-1, in float64."""
+    return np.arange(n_alpha, dtype=np.float64) / float(n_alpha)
+
+
+def channel_scales(m, alpha: float) -> np.ndarray:
+    """s[k] = m[k]^alpha computed in float64, rounded to float32."""
+    return np.power(np.asarray(m, dtype=np.float64), float(alpha)).astype(np.float32)
+
+
+def searched_weight(w, s32, group_size: int) -> np.ndarray:
+    """W_hat_alpha = dequant(Q(W . diag(s))) / s, float64 [N, K].
+
+    Q(W diag(s)) (X / s)^T == X W_hat_alpha^T, so this is the effective
+    weight the scaled layer applies to the unscaled activations."""
+    w = np.asarray(w)
+    K = w.shape[1]
+    qw, sc, zr = quantize(w, group_size, channel_scale=s32)
+    return dequantize(qw, sc, zr, group_size, K) / np.asarray(s32, np.float64)[None, :]
+
+
+def search_loss_direct(w, x, s32, group_size: int) -> float:
+    """L = || Q(W diag(s)) (X / s)^T - W X^T ||_F^2  (float64, direct form)."""
+    w64 = np.asarray(w).astype(np.float64)
+    x64 = np.asarray(x).astype(np.float64)
+    y = x64 @ w64.T
+    y_hat = x64 @ searched_weight(w, s32, group_size).T
+    d = y_hat - y
+    return float(np.sum(d * d))
+
+
+def gram(x) -> np.ndarray:
+    """G = X^T X in float64 [K, K]."""
+    x64 = np.asarray(x).astype(np.float64)
+    return x64.T @ x64
+
+
+def search_loss_gram(w, g, s32, group_size: int) -> float:
+    """Same loss through the Gram matrix: with D = W_hat_alpha - W,
+    ||D X^T||_F^2 = sum_n D_n G D_n^T = sum((D G) * D)."""
+    d = searched_weight(w, s32, group_size) - np.asarray(w).astype(np.float64)
+    return float(np.sum((d @ g) * d))
+
+
+def scale_search(w, x, group_size: int, alphas=None, use_gram: bool = True):
+    """AWQ's per-input-channel scale search over an alpha grid.
+
+    For every alpha: s = mean|x|^alpha, quantize W diag(s), and measure the
+    squared output error against the unquantized layer. Returns
+    (losses float64 [n_alpha], best index, best scales float32 [K]).
+    The best index is the first minimum (ties go to the smallest alpha)."""
+    if alphas is None:
+        alphas = alpha_grid(20)
+    m = activation_absmean(x)
+    g = gram(x) if use_gram else None
+    losses = np.empty(len(alphas), dtype=np.float64)
+    for i, a in enumerate(alphas):
+        s32 = channel_scales(m, a)
+        if use_gram:
+            losses[i] = search_loss_gram(w, g, s32, group_size)
+        else:
+            losses[i] = search_loss_direct(w, x, s32, group_size)
+    best = int(np.argmin(losses))   # np.argmin returns the first minimum
+    return losses, best, channel_scales(m, alphas[best])
