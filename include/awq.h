@@ -1,0 +1,177 @@
+/*
+ * awq.h - C ABI of the MI355X (gfx950) W4A16 library: group-wise asymmetric
+ * INT4 weight quantization, the fused dequantize-and-multiply linear layer
+ * and AWQ's activation-aware per-input-channel scale search.
+ *
+ * Sources for the operations (cited by page title and section):
+ *   "模型量化:GGUF/AWQ/GPTQ部署方案" (xxmr.cn), §1.2 量化映射: the affine map
+ *       q = clamp(round(x / scale) + zero_point, 0, 2^bits - 1) and its
+ *       inverse x_hat = (q - zero_point) * scale, the scale set by the range
+ *       of the weights; §1.4 量化粒度: one scale per group of 128 weights.
+ *   "模型量化实战：INT8/INT4、GPTQ、AWQ与精度-速度权衡" (aissn.com), sections
+ *       量化粒度 (per-group, group_size=128) and 对称/非对称量化 (asymmetric,
+ *       zero-point != 0).
+ *   rskf.cn AWQ article: §2.1 (per-input-channel factor s: weights times s,
+ *       activations divided by s, s searched to minimise the difference
+ *       between the quantized and the original output), §2.3 / §4.1 (the
+ *       factor is folded ahead of inference), §1.3 / §3.3 (INT4 -> FP16
+ *       dequantization inside the matmul; a GEMV kernel for single-stream
+ *       decode, a GEMM kernel for batches).
+ *   "AWQ 模型量化技术：激活感知的权重量化革命", Per-channel Scaling 优化.
+ *
+ * Conventions shared by every call:
+ *   - Matrices are row-major and densely packed. W[N, K]: row n is output
+ *     channel n, column k is input channel k. Groups of G consecutive k share
+ *     one scale and one zero-point (G = 64 or 128).
+ *   - qweight is uint32 [N, K/8]: the 4-bit code of column k = 8c + j sits in
+ *     bits 4j..4j+3 of word c. scales and zeros are fp16 [N, K/G]; every zero
+ *     is an integer 0..15.
+ *   - Pointers marked "device" point to GPU memory of the current HIP device;
+ *     they must be 16-byte aligned. The caller allocates and owns every
+ *     buffer; the library keeps no state between calls and allocates no
+ *     device memory (the scale search takes a caller-provided workspace).
+ *   - stream is a hipStream_t (NULL means the null stream). awq_quantize,
+ *     awq_gemm and awq_activation_absmean only enqueue work on it and return.
+ *   - Argument checks run on the host before anything is enqueued; a failed
+ *     check launches nothing. No C++ exception crosses this interface.
+ *   - Non-finite inputs give undefined (but memory-safe) results.
+ */
+#ifndef AWQ_MI355X_H
+#define AWQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    AWQ_OK = 0,
+    AWQ_ERR_NULL = 1,      /* a required pointer is NULL */
+    AWQ_ERR_SHAPE = 2,     /* negative size, K not a multiple of G, ... */
+    AWQ_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned */
+    AWQ_ERR_CONFIG = 4,    /* group_size not 64/128, bad alpha grid, ... */
+    AWQ_ERR_WORKSPACE = 5, /* workspace smaller than the size query says */
+    AWQ_ERR_HIP = 6        /* the HIP runtime reported an error */
+} awq_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* awq_status_string(int status);
+
+/* Interface version (major * 100 + minor). */
+int awq_version(void);
+
+/*
+ * awq_quantize - group-wise asymmetric INT4 quantization of W.
+ * (xxmr.cn §1.2 / §1.4; aissn.com 量化粒度, 对称/非对称量化)
+ *
+ * For every row n and group g, over w' = float32(w[n,k] * channel_scale[k])
+ * (or w' = w when channel_scale is NULL), in IEEE float32:
+ *   range = max(max(w') - min(w'), 1e-5)
+ *   scale = fp16_rne(range / 15)            (stored in scales[n, g])
+ *   zero  = clamp(rint(-min(w') / scale), 0, 15)   (stored in zeros[n, g])
+ *   code  = clamp(rint(w' / scale) + zero, 0, 15)
+ * where rint is round-half-to-even and the division is correctly rounded.
+ *
+ *   w_f16          device, fp16 [N, K]
+ *   channel_scale  device, fp32 [K] or NULL (AWQ's W * diag(s), rskf.cn §2.1)
+ *   N, K           N >= 0; K > 0, K % group_size == 0
+ *   group_size     64 or 128
+ *   qweight        device, uint32 [N, K/8]            (output)
+ *   scales_f16     device, fp16 [N, K/G]              (output)
+ *   zeros_f16      device, fp16 [N, K/G]              (output)
+ * N == 0 returns AWQ_OK without work. Results are bit-identical on every run.
+ * Scales that overflow fp16 (range / 15 > 65504) are undefined.
+ */
+awq_status awq_quantize(const void* w_f16, const float* channel_scale,
+                        int64_t N, int64_t K, int group_size,
+                        uint32_t* qweight, void* scales_f16, void* zeros_f16,
+                        void* stream);
+
+/*
+ * awq_gemm - the W4A16 linear layer y = x . dequant(Wq)^T.
+ * (xxmr.cn §1.2 inverse map; rskf.cn §1.3 / §3.3 GEMV and GEMM kernels)
+ *
+ *   y[m, n] = sum_k x[m, k] * (code[n, k] - zeros[n, k/G]) * scales[n, k/G]
+ * accumulated in fp32 and stored as fp16 (round-to-nearest-even).
+ *
+ *   x_f16        device, fp16 [M, K] (activations already divided by any
+ *                AWQ factor s, which is folded upstream: rskf.cn §2.3)
+ *   qweight, scales_f16, zeros_f16   device, as written by awq_quantize
+ *   M, N, K      M, N >= 0; K > 0, K % group_size == 0
+ *   group_size   64 or 128
+ *   y_f16        device, fp16 [M, N] (output; must not alias the inputs)
+ * M == 0 or N == 0 returns AWQ_OK without work. Small M (decode) runs a
+ * bandwidth-bound GEMV; larger M runs an MFMA GEMM. Results do not depend on
+ * run-to-run scheduling.
+ */
+awq_status awq_gemm(const void* x_f16, const uint32_t* qweight,
+                    const void* scales_f16, const void* zeros_f16,
+                    int64_t M, int64_t N, int64_t K, int group_size,
+                    void* y_f16, void* stream);
+
+/*
+ * awq_gemm_path - awq_gemm with the kernel chosen by the caller:
+ * path 0 = automatic (as awq_gemm), 1 = GEMV (requires M <= 8),
+ * 2 = MFMA GEMM. Any other path returns AWQ_ERR_CONFIG.
+ */
+awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight,
+                         const void* scales_f16, const void* zeros_f16,
+                         int64_t M, int64_t N, int64_t K, int group_size,
+                         void* y_f16, int path, void* stream);
+
+/*
+ * awq_activation_absmean - m[k] = max(mean_t |x[t, k]|, 1e-8), the
+ * per-input-channel activation statistic AWQ's scale is built from
+ * (rskf.cn §2.1-2.2; "AWQ 模型量化技术", Per-channel Scaling 优化).
+ *
+ *   x_f16    device, fp16 [T, K], T > 0, K > 0, K % 8 == 0
+ *   m_f64    device, fp64 [K] (output)
+ *   workspace, workspace_bytes  device scratch of at least
+ *            awq_activation_absmean_workspace_bytes(T, K) bytes
+ * Accumulation is in fp64 in a fixed order (bit-identical run to run).
+ */
+size_t awq_activation_absmean_workspace_bytes(int64_t T, int64_t K);
+awq_status awq_activation_absmean(const void* x_f16, int64_t T, int64_t K,
+                                  double* m_f64, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
+ * awq_scale_search - AWQ's per-input-channel scale search over an alpha grid
+ * (rskf.cn §2.1; "AWQ 模型量化技术", Per-channel Scaling 优化).
+ *
+ * With m = awq_activation_absmean(x) and, for every alpha_i,
+ *   s_i[k] = float32(m[k] ^ alpha_i)   (pow in fp64, then rounded)
+ *   loss_i = || Q(W . diag(s_i)) . (x / s_i)^T  -  W . x^T ||_F^2
+ * where Q is awq_quantize with channel_scale = s_i and the product is the
+ * W4A16 GEMM on fp16(x / s_i) (fp32 accumulation); the reference W . x^T is
+ * computed once (fp16 MFMA, fp32 accumulation) and kept in the workspace.
+ * The best index is the first minimum of the losses (ties go to the
+ * smallest alpha).
+ *
+ *   w_f16         device, fp16 [N, K]
+ *   x_f16         device, fp16 [T, K] (calibration activations)
+ *   N, K, T       N > 0, T > 0, K > 0, K % group_size == 0
+ *   group_size    64 or 128
+ *   alphas        host, float64 [n_alpha], every alpha finite (1 <= n_alpha <= 64)
+ *   workspace     device, >= awq_scale_search_workspace_bytes(N, K, T, G, n_alpha)
+ *   losses        host, float64 [n_alpha] (output)
+ *   best_index    host, int (output)
+ *   best_scales   device, fp32 [K] (output: s at the best alpha)
+ * Synchronises the stream once, at the end, to read the losses back.
+ */
+size_t awq_scale_search_workspace_bytes(int64_t N, int64_t K, int64_t T,
+                                        int group_size, int n_alpha);
+awq_status awq_scale_search(const void* w_f16, const void* x_f16,
+                            int64_t N, int64_t K, int64_t T, int group_size,
+                            const double* alphas, int n_alpha,
+                            void* workspace, size_t workspace_bytes,
+                            double* losses, int* best_index,
+                            float* best_scales, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_MI355X_H */

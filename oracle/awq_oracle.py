@@ -89,8 +89,9 @@ def group_quantize(w, group_size: int, channel_scale=None):
     s32 = rng / np.float32(QMAX)                        # IEEE float32 divide
     s16 = s32.astype(np.float16)
     sf = s16.astype(np.float32)
-    # zero-point: the integer that wmin maps to code 0.
-    z = np.clip(np.rint(-wmin / sf), 0, QMAX).astype(np.float32)
+    # zero-point: the integer that wmin maps to code 0 (held as an integer,
+    # so a clamped -0.0 is stored as +0.0).
+    z = np.clip(np.rint(-wmin / sf), 0, QMAX).astype(np.int32).astype(np.float32)
     # codes: round(x / scale) first, then add the zero-point, then clamp.
     q = np.rint(wg / sf[:, :, None]) + z[:, :, None]
     q = np.clip(q, 0, QMAX)

@@ -1,0 +1,138 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+include/awq.h declares, and rejects bad arguments on the host (status codes,
+nothing launched). Fake device addresses are never dereferenced because every
+check here fails before a kernel would be enqueued."""
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import weight_only_int4_quantize_amd as awq
+
+OK, NULL, SHAPE, ALIGN, CONFIG, WORKSPACE = 0, 1, 2, 3, 4, 5
+FAKE = 0x10000          # aligned fake device address (never dereferenced)
+FAKE_ODD = 0x10008      # 8-byte but not 16-byte aligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    return awq.load()
+
+
+def test_library_exports_every_header_function(L):
+    names = awq.header_functions()
+    assert {"awq_quantize", "awq_gemm", "awq_scale_search"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", awq.lib_path()], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_library_is_built_for_gfx950_only():
+    """The embedded offload bundle names gfx950 and no other GPU target."""
+    import re
+    with open(awq.lib_path(), "rb") as f:
+        blob = f.read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa-[a-z-]*(gfx[0-9a-f]+)", blob))
+    assert targets == {b"gfx950"}
+
+
+def test_status_strings(L):
+    assert L.awq_status_string(OK) == b"AWQ_OK"
+    for s in range(1, 7):
+        assert L.awq_status_string(s).startswith(b"AWQ_ERR_")
+    assert L.awq_status_string(99) == b"unknown awq_status"
+    assert L.awq_version() == 100
+
+
+@pytest.mark.parametrize("N,K,G,expect", [
+    (16, 128, 32, CONFIG),      # unsupported group size
+    (16, 128, 256, CONFIG),
+    (16, 100, 64, SHAPE),       # K not a multiple of G
+    (16, 0, 64, SHAPE),         # empty K
+    (-1, 128, 64, SHAPE),
+    (0, 128, 64, OK),           # empty N: nothing to do
+])
+def test_quantize_shape_checks(L, N, K, G, expect):
+    assert L.awq_quantize(FAKE, None, N, K, G, FAKE, FAKE, FAKE, None) == expect
+
+
+def test_quantize_null_and_alignment(L):
+    assert L.awq_quantize(None, None, 4, 128, 128, FAKE, FAKE, FAKE, None) == NULL
+    assert L.awq_quantize(FAKE, None, 4, 128, 128, None, FAKE, FAKE, None) == NULL
+    assert L.awq_quantize(FAKE_ODD, None, 4, 128, 128, FAKE, FAKE, FAKE, None) == ALIGN
+    assert L.awq_quantize(FAKE, FAKE_ODD, 4, 128, 128, FAKE, FAKE, FAKE, None) == ALIGN
+    assert L.awq_quantize(FAKE, None, 4, 128, 128, FAKE, FAKE + 1, FAKE, None) == ALIGN
+
+
+def test_gemm_checks(L):
+    g = L.awq_gemm_path
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, 16, 100, 64, FAKE, 0, None) == SHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, -1, 16, 128, 64, FAKE, 0, None) == SHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 96, FAKE, 0, None) == CONFIG
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 64, FAKE, 3, None) == CONFIG
+    assert g(FAKE, FAKE, FAKE, FAKE, 9, 16, 128, 64, FAKE, 1, None) == CONFIG   # GEMV is M <= 8
+    assert g(FAKE, FAKE, FAKE, FAKE, 0, 16, 128, 64, FAKE, 0, None) == OK       # empty M
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 0, 128, 64, FAKE, 0, None) == OK        # empty N
+    assert g(None, FAKE, FAKE, FAKE, 1, 16, 128, 64, FAKE, 0, None) == NULL
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 64, None, 0, None) == NULL
+    assert g(FAKE_ODD, FAKE, FAKE, FAKE, 1, 16, 128, 64, FAKE, 0, None) == ALIGN
+    assert g(FAKE, FAKE_ODD, FAKE, FAKE, 1, 16, 128, 64, FAKE, 0, None) == ALIGN
+    assert L.awq_gemm(FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 64, FAKE + 1, None) == ALIGN
+
+
+def test_absmean_checks(L):
+    need = L.awq_activation_absmean_workspace_bytes(1000, 512)
+    assert need >= 512 * 8
+    assert L.awq_activation_absmean_workspace_bytes(0, 512) == 0
+    assert L.awq_activation_absmean(FAKE, 1000, 512, FAKE, FAKE, need - 8, None) == WORKSPACE
+    assert L.awq_activation_absmean(FAKE, 0, 512, FAKE, FAKE, need, None) == SHAPE
+    assert L.awq_activation_absmean(FAKE, 10, 12, FAKE, FAKE, need, None) == SHAPE
+    assert L.awq_activation_absmean(None, 10, 512, FAKE, FAKE, need, None) == NULL
+
+
+def test_scale_search_checks(L):
+    alphas = np.arange(20, dtype=np.float64) / 20
+    a = alphas.ctypes.data_as(ctypes.c_void_p)
+    losses = np.zeros(20)
+    lp = losses.ctypes.data_as(ctypes.c_void_p)
+    best = ctypes.c_int(-1)
+    bp = ctypes.addressof(best)
+    need = L.awq_scale_search_workspace_bytes(256, 512, 1024, 128, 20)
+    # the layout holds at least Y (T x N fp32), x / s (T x K fp16) and the packed weight
+    assert need >= 1024 * 256 * 4 + 1024 * 512 * 2 + 256 * 512 // 2
+    assert L.awq_scale_search_workspace_bytes(256, 500, 1024, 128, 20) == 0
+    s = L.awq_scale_search
+    assert s(FAKE, FAKE, 256, 512, 1024, 128, a, 20, FAKE, need - 256, lp, bp, FAKE, None) == WORKSPACE
+    assert s(FAKE, FAKE, 256, 512, 1024, 128, a, 0, FAKE, need, lp, bp, FAKE, None) == CONFIG
+    assert s(FAKE, FAKE, 256, 512, 1024, 100, a, 20, FAKE, need, lp, bp, FAKE, None) == CONFIG
+    assert s(FAKE, FAKE, 0, 512, 1024, 128, a, 20, FAKE, need, lp, bp, FAKE, None) == SHAPE
+    assert s(FAKE, FAKE, 256, 512, 0, 128, a, 20, FAKE, need, lp, bp, FAKE, None) == SHAPE
+    assert s(FAKE, None, 256, 512, 1024, 128, a, 20, FAKE, need, lp, bp, FAKE, None) == NULL
+    assert s(FAKE, FAKE, 256, 512, 1024, 128, None, 20, FAKE, need, lp, bp, FAKE, None) == NULL
+    bad = np.array([0.0, np.nan])
+    assert s(FAKE, FAKE, 256, 512, 1024, 128, bad.ctypes.data_as(ctypes.c_void_p), 2, FAKE, need, lp, bp,
+             FAKE, None) == CONFIG
+    assert s(FAKE_ODD, FAKE, 256, 512, 1024, 128, a, 20, FAKE, need, lp, bp, FAKE, None) == ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    w = torch.zeros(4, 128, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        awq.awq_quantize(w, 128)
+
+
+def test_oracle_is_not_reachable_from_the_package():
+    """The product package never imports or reads the oracle."""
+    pkg = os.path.dirname(awq.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                with open(os.path.join(root, f), encoding="utf-8") as fh:
+                    text = fh.read()
+                assert "import oracle" not in text and "from oracle" not in text, f

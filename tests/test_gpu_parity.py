@@ -1,0 +1,360 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Quantize/pack/zero-points: bit-exact. Linear-layer outputs: relative
+Frobenius error <= 1e-3 and |y - y_ref| <= 1e-2 * (|y_ref| + 1) per element.
+Scale search: the same alpha as the oracle. Inputs come from the seeded
+generators; expected values come only from the oracle (or from golden files
+written by a script that calls only the oracle).
+"""
+
+import base64
+import hashlib
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import weight_only_int4_quantize_amd as awq  # noqa: E402
+
+DEV = "cuda:0"
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+REL_FRO = 1e-3
+ELEM = 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def gpu_quantize(w16, G, cs=None):
+    qw, sc, zr = awq.awq_quantize(dev(w16), G, None if cs is None else dev(cs.astype(np.float32)))
+    torch.cuda.synchronize()
+    return host(qw).view(np.uint32), host(sc), host(zr)
+
+
+def assert_quant_equal(got, exp):
+    qw, sc, zr = got
+    eqw, esc, ezr = exp
+    assert qw.shape == eqw.shape and sc.shape == esc.shape
+    nq = int(np.count_nonzero(qw != eqw))
+    ns = int(np.count_nonzero(sc.view(np.uint16) != esc.view(np.uint16)))
+    nz = int(np.count_nonzero(zr.view(np.uint16) != ezr.view(np.uint16)))
+    assert (nq, ns, nz) == (0, 0, 0), f"mismatching words {nq}, scales {ns}, zeros {nz}"
+
+
+def assert_linear_close(y, y_ref):
+    y = y.astype(np.float64)
+    assert y.shape == y_ref.shape
+    assert np.all(np.isfinite(y))
+    rel = np.linalg.norm(y - y_ref) / max(np.linalg.norm(y_ref), 1e-30)
+    worst = np.max(np.abs(y - y_ref) / (np.abs(y_ref) + 1.0)) if y.size else 0.0
+    assert rel <= REL_FRO, f"relative Frobenius error {rel:.3e}"
+    assert worst <= ELEM, f"worst element error {worst:.3e}"
+    return rel
+
+
+# ---------------------------------------------------------------- quantize
+
+def test_quantize_tiny_layer_bit_exact():
+    lay = synth.tiny_layer()
+    say("quantize tiny 512x512 G128")
+    assert_quant_equal(gpu_quantize(lay["w"], 128), oracle.quantize(lay["w"], 128))
+
+
+@pytest.mark.parametrize("N,K", synth.DECODE_SHAPES)
+def test_quantize_decode_shapes_bit_exact(N, K):
+    lay = synth.decode_layer(N, K, 0)
+    say("quantize", N, K)
+    assert_quant_equal(gpu_quantize(lay["w"], 128), oracle.quantize(lay["w"], 128))
+
+
+@pytest.mark.parametrize("G", synth.SWEEP_G)
+@pytest.mark.parametrize("N,K", synth.SWEEP_SHAPES)
+def test_quantize_sweep_shapes_bit_exact(N, K, G):
+    lay = synth.sweep_layer(N, K, 0, G)
+    say("quantize", N, K, G)
+    assert_quant_equal(gpu_quantize(lay["w"], G), oracle.quantize(lay["w"], G))
+
+
+@pytest.mark.parametrize("N,K,G", [(1, 64, 64), (3, 128, 64), (7, 128, 128), (129, 192, 64), (33, 384, 128)])
+def test_quantize_ragged_bit_exact(N, K, G):
+    lay = synth.make_layer(N, K, 0, seed=[100, N, K, G], w_std=0.05, salient_frac=0.05)
+    assert_quant_equal(gpu_quantize(lay["w"], G), oracle.quantize(lay["w"], G))
+
+
+def test_quantize_with_channel_scale_bit_exact():
+    lay = synth.make_layer(300, 1024, 64, seed=[101], w_std=0.02)
+    m = oracle.activation_absmean(lay["x"])
+    for a in (0.0, 0.35, 0.95):
+        s = oracle.channel_scales(m, a)
+        for G in (64, 128):
+            assert_quant_equal(gpu_quantize(lay["w"], G, s), oracle.quantize(lay["w"], G, channel_scale=s))
+
+
+def test_quantize_special_groups_bit_exact():
+    """The worked example, constructed half-way ties, fp16 subnormals,
+    constant groups, all-positive groups, and large magnitudes."""
+    K = 128
+    rows = []
+    rows.append([-1.0, 1.0, 0.5] + [0.0] * (K - 3))
+    s = 0.13330078125
+    ties = [(k + 0.5) * s for k in range(4)]
+    rows.append([-1.0, 1.0] + ties + [-t for t in ties] + [0.0] * (K - 10))
+    rng = np.random.default_rng(102)
+    rows.append(list(rng.uniform(-6e-5, 6e-5, K)))             # fp16 subnormals
+    rows.append([0.0] * K)                                       # constant zero
+    rows.append([0.25] * K)                                      # constant positive
+    rows.append([-3.0] * K)                                      # constant negative
+    rows.append(list(rng.uniform(0.1, 0.9, K)))                  # all positive
+    rows.append(list(rng.uniform(-0.9, -0.1, K)))                # all negative
+    rows.append(list(rng.uniform(-60000, 60000, K)))             # large
+    rows.append([-0.0] * (K // 2) + [0.0] * (K // 2))            # signed zeros
+    w = np.array(rows, dtype=np.float16)
+    assert_quant_equal(gpu_quantize(w, 128), oracle.quantize(w, 128))
+    assert_quant_equal(gpu_quantize(w, 64), oracle.quantize(w, 64))
+    qw, sc, zr = gpu_quantize(w, 128)
+    assert float(sc[0, 0]) == 0.13330078125 and float(zr[0, 0]) == 8.0
+    assert oracle.unpack_codes(qw, K)[0, 2] == 12
+
+
+def test_quantize_round_before_zero_point_tie():
+    """w / s one fp32 step above a tie (made through the channel scale): the
+    code is 9, not 8."""
+    s = np.float32(0.13330078125)
+    c_tie = np.nextafter(np.float32(0.5) * s, np.float32(1))
+    w = np.zeros((1, 128), dtype=np.float16)
+    w[0, :3] = [-1.0, 1.0, 1.0]
+    cs = np.ones(128, dtype=np.float32)
+    cs[2] = c_tie
+    got = gpu_quantize(w, 128, cs)
+    assert_quant_equal(got, oracle.quantize(w, 128, channel_scale=cs))
+    assert oracle.unpack_codes(got[0], 128)[0, 2] == 9
+
+
+def test_quantize_is_deterministic_and_empty_ok():
+    lay = synth.make_layer(64, 512, 0, seed=[103])
+    a = gpu_quantize(lay["w"], 128)
+    b = gpu_quantize(lay["w"], 128)
+    assert_quant_equal(a, b)
+    w0 = torch.empty((0, 128), dtype=torch.float16, device=DEV)
+    qw, sc, zr = awq.awq_quantize(w0, 128)
+    assert qw.shape == (0, 16)
+
+
+# ---------------------------------------------------------------- linear layer
+
+def run_linear(x16, qw, sc, zr, G, path=awq.PATH_AUTO):
+    y = awq.awq_gemm(dev(x16), dev(qw.view(np.int32)), dev(sc), dev(zr), G, path=path)
+    torch.cuda.synchronize()
+    return host(y)
+
+
+def test_gemv_tiny_layer():
+    lay = synth.tiny_layer()
+    say("gemv tiny")
+    qw, sc, zr = oracle.quantize(lay["w"], 128)
+    y = run_linear(lay["x"], qw, sc, zr, 128)
+    assert_linear_close(y, oracle.linear_ref(lay["x"], qw, sc, zr, 128))
+
+
+def test_end_to_end_tiny_layer():
+    """GPU quantize -> GPU linear against oracle quantize -> oracle linear."""
+    lay = synth.tiny_layer()
+    w, x = dev(lay["w"]), dev(lay["x"])
+    qw, sc, zr = awq.awq_quantize(w, 128)
+    y = host(awq.awq_gemm(x, qw, sc, zr, 128))
+    eq = oracle.quantize(lay["w"], 128)
+    assert_linear_close(y, oracle.linear_ref(lay["x"], *eq, 128))
+
+
+@pytest.mark.parametrize("M", synth.DECODE_M)
+@pytest.mark.parametrize("N,K", synth.DECODE_SHAPES)
+def test_decode_linear(N, K, M):
+    lay = synth.decode_layer(N, K, M)
+    say("decode linear", N, K, M)
+    qw, sc, zr = oracle.quantize(lay["w"], 128)
+    y = run_linear(lay["x"], qw, sc, zr, 128)
+    assert_linear_close(y, oracle.linear_ref(lay["x"], qw, sc, zr, 128))
+
+
+def sampled_rows(N, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(N, size=min(n, N), replace=False))
+    # always include both ends (first and last tiles)
+    return np.unique(np.concatenate([[0, N - 1], rows]))
+
+
+def check_sampled_end_to_end(lay, G, M, n_rows=192, seed=0):
+    """GPU quantizes the whole W and runs the full product; the oracle
+    quantizes only the sampled rows (rows are independent) and computes those
+    output columns."""
+    w, x = lay["w"], lay["x"]
+    N = w.shape[0]
+    qw, sc, zr = awq.awq_quantize(dev(w), G)
+    y = host(awq.awq_gemm(dev(x), qw, sc, zr, G))
+    rows = sampled_rows(N, n_rows, seed)
+    eq = oracle.quantize(w[rows], G)
+    y_ref = oracle.linear_ref(x, *eq, G)
+    assert_linear_close(y[:, rows], y_ref)
+    assert np.all(np.isfinite(y.astype(np.float32)))
+
+
+@pytest.mark.parametrize("N,K", synth.PREFILL_SHAPES)
+def test_prefill_gemm_full_size_sampled(N, K):
+    lay = synth.prefill_layer(N, K)
+    say("prefill", N, K)
+    check_sampled_end_to_end(lay, 128, synth.PREFILL_M, seed=N)
+
+
+@pytest.mark.parametrize("M", synth.SWEEP_M)
+@pytest.mark.parametrize("G", synth.SWEEP_G)
+@pytest.mark.parametrize("N,K", synth.SWEEP_SHAPES)
+def test_sweep_linear_full_size_sampled(N, K, G, M):
+    lay = synth.sweep_layer(N, K, M, G)
+    say("sweep", N, K, G, M)
+    check_sampled_end_to_end(lay, G, M, seed=N + M + G)
+
+
+@pytest.mark.parametrize("M,N,K,G", [
+    (1, 1, 64, 64), (3, 17, 128, 64), (8, 130, 256, 128), (9, 64, 64, 64),
+    (127, 129, 192, 64), (300, 200, 384, 128), (257, 255, 640, 64),
+])
+def test_linear_ragged_both_paths(M, N, K, G):
+    lay = synth.make_layer(N, K, M, seed=[104, M, N, K, G], w_std=0.02)
+    qw, sc, zr = oracle.quantize(lay["w"], G)
+    y_ref = oracle.linear_ref(lay["x"], qw, sc, zr, G)
+    assert_linear_close(run_linear(lay["x"], qw, sc, zr, G, awq.PATH_GEMM), y_ref)
+    assert_linear_close(run_linear(lay["x"], qw, sc, zr, G, awq.PATH_AUTO), y_ref)
+    if M <= 8:
+        assert_linear_close(run_linear(lay["x"], qw, sc, zr, G, awq.PATH_GEMV), y_ref)
+
+
+@pytest.mark.parametrize("path", [awq.PATH_GEMV, awq.PATH_GEMM])
+def test_one_hot_input_returns_dequantized_column(path):
+    """x = e_k: y = fp16 of the dequantized column k, exactly, on both paths."""
+    N, K, G = 96, 256, 64
+    lay = synth.make_layer(N, K, 0, seed=[105], w_std=0.02)
+    qw, sc, zr = oracle.quantize(lay["w"], G)
+    w_hat = oracle.dequantize(qw, sc, zr, G, K)
+    ks = [0, 5, 63, 64, 200, 255]
+    x = np.zeros((len(ks), K), dtype=np.float16)
+    for i, k in enumerate(ks):
+        x[i, k] = 1.0
+    if path == awq.PATH_GEMV:
+        for i in range(len(ks)):
+            y = run_linear(x[i:i + 1], qw, sc, zr, G, path)
+            assert np.array_equal(y[0], w_hat[:, ks[i]].astype(np.float16))
+    else:
+        y = run_linear(x, qw, sc, zr, G, path)
+        assert np.array_equal(y, w_hat[:, ks].T.astype(np.float16))
+
+
+def test_linear_is_linear_in_x():
+    N, K, G = 256, 512, 128
+    lay = synth.make_layer(N, K, 8, seed=[106], w_std=0.02)
+    qw, sc, zr = oracle.quantize(lay["w"], G)
+    x1 = lay["x"][:4].astype(np.float32)
+    x2 = lay["x"][4:].astype(np.float32)
+    for path in (awq.PATH_GEMV, awq.PATH_GEMM):
+        ya = run_linear(x1.astype(np.float16), qw, sc, zr, G, path).astype(np.float64)
+        yb = run_linear(x2.astype(np.float16), qw, sc, zr, G, path).astype(np.float64)
+        # doubling an fp16 input is exact, so y(2x) = 2 y(x) up to the output rounding
+        y2 = run_linear((2 * x1).astype(np.float16), qw, sc, zr, G, path).astype(np.float64)
+        assert np.allclose(y2, 2 * ya, rtol=2e-3, atol=1e-3)
+        ysum = oracle.linear_ref((x1 + x2).astype(np.float16), qw, sc, zr, G)
+        assert np.linalg.norm(ya + yb - ysum) <= 5e-3 * np.linalg.norm(ysum)
+
+
+def test_linear_empty_shapes_are_no_ops():
+    qw = torch.zeros((4, 16), dtype=torch.int32, device=DEV)
+    sc = torch.ones((4, 1), dtype=torch.float16, device=DEV)
+    zr = torch.zeros((4, 1), dtype=torch.float16, device=DEV)
+    x = torch.empty((0, 128), dtype=torch.float16, device=DEV)
+    y = awq.awq_gemm(x, qw, sc, zr, 128)
+    assert y.shape == (0, 4)
+
+
+def test_linear_does_not_write_outside_y():
+    """A guard band around y stays untouched (ragged tiles on both paths)."""
+    M, N, K, G = 5, 77, 256, 64
+    lay = synth.make_layer(N, K, M, seed=[107], w_std=0.02)
+    qw, sc, zr = oracle.quantize(lay["w"], G)
+    for path in (awq.PATH_GEMV, awq.PATH_GEMM):
+        buf = torch.full((M * N + 2048,), 7.0, dtype=torch.float16, device=DEV)
+        y = buf[1024:1024 + M * N].view(M, N)
+        awq.awq_gemm(dev(lay["x"]), dev(qw.view(np.int32)), dev(sc), dev(zr), G, path=path, out=y)
+        torch.cuda.synchronize()
+        b = host(buf)
+        assert np.all(b[:1024] == 7.0) and np.all(b[1024 + M * N:] == 7.0)
+        assert_linear_close(host(y), oracle.linear_ref(lay["x"], qw, sc, zr, G))
+
+
+# ---------------------------------------------------------------- scale search
+
+@pytest.mark.parametrize("T,K", [(1000, 512), (64, 4104)])
+def test_absmean(T, K):
+    x = synth.make_layer(0, K, T, seed=[108, T, K])["x"]
+    m = host(awq.awq_activation_absmean(dev(x)))
+    np.testing.assert_allclose(m, oracle.activation_absmean(x), rtol=1e-13, atol=0)
+
+
+def test_scale_search_small_interior_minimum():
+    lay = synth.make_layer(256, 512, 512, seed=[109], w_std=0.02, w_mult=1.0)
+    w, x = lay["w"], lay["x"]
+    losses_o, best_o, s_o = oracle.scale_search(w, x, 128)
+    losses, best, s = awq.awq_scale_search(dev(w), dev(x), 128)
+    say("search small: gpu", best, "oracle", best_o)
+    check_search(losses, best, host(s), losses_o, best_o, s_o)
+
+
+def check_search(losses, best, s, losses_o, best_o, s_o, rtol=2e-3):
+    rel = np.abs(losses - losses_o) / losses_o
+    assert np.all(rel <= rtol), f"loss deviation {rel.max():.2e}"
+    if best != best_o:
+        # accepted only for a near-tie inside the loss tolerance
+        assert (losses_o[best] - losses_o[best_o]) <= rtol * losses_o[best_o], (best, best_o)
+    else:
+        np.testing.assert_array_equal(s, s_o)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("w_mult", [1.0, 10.0])
+def test_scale_search_full_size(w_mult):
+    path = os.path.join(GOLDEN, f"search_7b_mlp_wmult{int(w_mult)}.json")
+    with open(path) as f:
+        g = json.load(f)
+    lay = synth.search_layer(w_mult=w_mult)
+    w, x = lay["w"], lay["x"]
+    h = hashlib.sha256()
+    h.update(np.ascontiguousarray(w).tobytes())
+    h.update(np.ascontiguousarray(x).tobytes())
+    assert h.hexdigest() == g["inputs_sha256"], "generator output changed"
+    say("search full size", w.shape, x.shape, "w_mult", w_mult)
+    wd, xd = dev(w), dev(x)
+    m = host(awq.awq_activation_absmean(xd))
+    m_o = np.frombuffer(base64.b64decode(g["m_f64_b64"]), dtype="<f8")
+    np.testing.assert_allclose(m, m_o, rtol=1e-13, atol=0)
+    losses, best, s = awq.awq_scale_search(wd, xd, 128, alphas=np.array(g["alphas"]))
+    losses_o = np.array(g["losses"])
+    s_o = np.frombuffer(base64.b64decode(g["best_scales_f32_b64"]), dtype="<f4")
+    say("gpu best", best, "oracle best", g["best_index"], "max loss dev",
+        float(np.max(np.abs(losses - losses_o) / losses_o)))
+    check_search(losses, best, host(s), losses_o, g["best_index"], s_o)
+    assert best == g["best_index"]

@@ -405,3 +405,11 @@ def test_search_keeps_rtn_when_salient_weights_set_the_range():
     losses, best, _ = oracle.scale_search(lay["w"], lay["x"], 128)
     assert best == 0
     assert np.all(np.diff(losses) > 0)
+
+
+def test_zero_point_is_positive_zero_when_clamped():
+    """A group whose minimum is positive clamps its zero-point to 0, stored
+    as +0.0 (the zero-point is an integer)."""
+    w = _row([0.5, 0.75, 1.0] + [0.25] * 125)
+    _, _, z16 = oracle.group_quantize(w, 128)
+    assert z16[0, 0].view(np.uint16) == 0x0000

@@ -1,0 +1,221 @@
+"""Python binding of libawq_mi355x.so, the MI355X (gfx950) W4A16 library.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream. The binding raises
+if the library has not been built or a tensor is not a GPU tensor; there is
+no CPU fallback.
+
+Entry points (same names as the C ABI in include/awq.h):
+    awq_quantize(w, group_size=128, channel_scale=None)  -> qweight, scales, zeros
+    awq_gemm(x, qweight, scales, zeros, group_size=128, path=0) -> y
+    awq_activation_absmean(x) -> m
+    awq_scale_search(w, x, group_size=128, alphas=None) -> losses, best_index, best_scales
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libawq_mi355x.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "awq.h")
+
+AWQ_OK = 0
+STATUS_NAMES = {
+    0: "AWQ_OK", 1: "AWQ_ERR_NULL", 2: "AWQ_ERR_SHAPE", 3: "AWQ_ERR_ALIGN",
+    4: "AWQ_ERR_CONFIG", 5: "AWQ_ERR_WORKSPACE", 6: "AWQ_ERR_HIP",
+}
+PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
+
+_lib = None
+
+
+class AwqError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed: {message}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Loads the built library (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m weight_only_int4_quantize_amd.build` "
+            "(there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    c_i64, c_int, c_vp, c_sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    L.awq_status_string.restype = ctypes.c_char_p
+    L.awq_status_string.argtypes = [c_int]
+    L.awq_version.restype = c_int
+    L.awq_version.argtypes = []
+    L.awq_quantize.restype = c_int
+    L.awq_quantize.argtypes = [c_vp, c_vp, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp]
+    L.awq_gemm.restype = c_int
+    L.awq_gemm.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_vp]
+    L.awq_gemm_path.restype = c_int
+    L.awq_gemm_path.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_int, c_vp]
+    L.awq_activation_absmean_workspace_bytes.restype = c_sz
+    L.awq_activation_absmean_workspace_bytes.argtypes = [c_i64, c_i64]
+    L.awq_activation_absmean.restype = c_int
+    L.awq_activation_absmean.argtypes = [c_vp, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]
+    L.awq_scale_search_workspace_bytes.restype = c_sz
+    L.awq_scale_search_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_int, c_int]
+    L.awq_scale_search.restype = c_int
+    L.awq_scale_search.argtypes = [c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_int, c_vp, c_sz,
+                                   c_vp, c_vp, c_vp, c_vp]
+    _lib = L
+    return L
+
+
+def header_functions() -> list:
+    """Names of the functions include/awq.h declares."""
+    with open(HEADER, encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(awq_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(fn: str, status: int) -> None:
+    if status != AWQ_OK:
+        msg = load().awq_status_string(status).decode()
+        raise AwqError(fn, status, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need_gpu(name: str, t, dtype=None) -> None:
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def awq_quantize(w, group_size: int = 128, channel_scale=None, out=None):
+    """Group-wise asymmetric INT4 quantization of w[N, K] (fp16).
+
+    Returns (qweight int32 [N, K/8] holding the uint32 words, scales fp16
+    [N, K/G], zeros fp16 [N, K/G]). channel_scale: optional fp32 [K]."""
+    torch = _torch()
+    _need_gpu("w", w, torch.float16)
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    N, K = w.shape
+    if channel_scale is not None:
+        _need_gpu("channel_scale", channel_scale, torch.float32)
+        if channel_scale.numel() != K:
+            raise ValueError("channel_scale must have K elements")
+    if out is None:
+        dev = w.device
+        qweight = torch.empty((N, max(K // 8, 0)), dtype=torch.int32, device=dev)
+        ng = K // group_size if group_size > 0 else 0
+        scales = torch.empty((N, ng), dtype=torch.float16, device=dev)
+        zeros = torch.empty((N, ng), dtype=torch.float16, device=dev)
+    else:
+        qweight, scales, zeros = out
+    st = load().awq_quantize(_ptr(w), _ptr(channel_scale), N, K, group_size, _ptr(qweight),
+                             _ptr(scales), _ptr(zeros), _stream(w.device))
+    _check("awq_quantize", st)
+    return qweight, scales, zeros
+
+
+def awq_gemm(x, qweight, scales, zeros, group_size: int = 128, path: int = PATH_AUTO, out=None):
+    """y[M, N] = x[M, K] . dequant(Wq)^T in fp16 (fp32 accumulation)."""
+    torch = _torch()
+    _need_gpu("x", x, torch.float16)
+    _need_gpu("qweight", qweight, torch.int32)
+    _need_gpu("scales", scales, torch.float16)
+    _need_gpu("zeros", zeros, torch.float16)
+    if x.dim() != 2 or qweight.dim() != 2:
+        raise ValueError("x and qweight must be 2-D")
+    M, K = x.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * 8 != K:
+        raise ValueError(f"qweight has {qweight.shape[1]} words per row, K={K} needs {K // 8}")
+    if scales.shape != (N, K // group_size) or zeros.shape != scales.shape:
+        raise ValueError("scales/zeros must be [N, K/group_size]")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
+    if out is not None:
+        _need_gpu("out", y, torch.float16)
+        if tuple(y.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    st = load().awq_gemm_path(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), M, N, K, group_size,
+                              _ptr(y), int(path), _stream(x.device))
+    _check("awq_gemm", st)
+    return y
+
+
+def awq_activation_absmean(x):
+    """m[k] = max(mean_t |x[t, k]|, 1e-8) in fp64, x fp16 [T, K]."""
+    torch = _torch()
+    _need_gpu("x", x, torch.float16)
+    T, K = x.shape
+    L = load()
+    m = torch.empty(K, dtype=torch.float64, device=x.device)
+    nbytes = L.awq_activation_absmean_workspace_bytes(T, K)
+    ws = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=x.device)
+    st = L.awq_activation_absmean(_ptr(x), T, K, _ptr(m), _ptr(ws), nbytes, _stream(x.device))
+    _check("awq_activation_absmean", st)
+    return m
+
+
+def scale_search_workspace_bytes(N: int, K: int, T: int, group_size: int = 128, n_alpha: int = 20) -> int:
+    return int(load().awq_scale_search_workspace_bytes(N, K, T, group_size, n_alpha))
+
+
+def awq_scale_search(w, x, group_size: int = 128, alphas=None, workspace=None):
+    """AWQ scale search over an alpha grid.
+
+    Returns (losses: numpy float64 [n_alpha], best_index: int,
+    best_scales: fp32 GPU tensor [K])."""
+    import numpy as np
+    torch = _torch()
+    _need_gpu("w", w, torch.float16)
+    _need_gpu("x", x, torch.float16)
+    N, K = w.shape
+    T = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x must be [T, K] with the K of w")
+    if alphas is None:
+        alphas = np.arange(20, dtype=np.float64) / 20.0
+    alphas = np.ascontiguousarray(alphas, dtype=np.float64)
+    n_alpha = int(alphas.size)
+    L = load()
+    nbytes = L.awq_scale_search_workspace_bytes(N, K, T, group_size, n_alpha)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=w.device)
+    losses = np.zeros(n_alpha, dtype=np.float64)
+    best = ctypes.c_int(-1)
+    best_scales = torch.empty(K, dtype=torch.float32, device=w.device)
+    st = L.awq_scale_search(_ptr(w), _ptr(x), N, K, T, group_size,
+                            alphas.ctypes.data_as(ctypes.c_void_p), n_alpha,
+                            _ptr(workspace), workspace.numel(),
+                            losses.ctypes.data_as(ctypes.c_void_p), ctypes.addressof(best),
+                            _ptr(best_scales), _stream(w.device))
+    _check("awq_scale_search", st)
+    return losses, int(best.value), best_scales

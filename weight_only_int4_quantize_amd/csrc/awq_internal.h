@@ -1,0 +1,74 @@
+// Internal declarations shared by the HIP translation units of the library.
+// Only gfx950 (CDNA4) is targeted: 64-lane wavefronts, fp16 MFMA, 160 KB LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/awq.h"
+
+namespace awq {
+
+typedef _Float16 half_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kQMax = 15;          // 2^4 - 1
+constexpr float kRangeFloor = 1e-5f;
+constexpr double kMeanFloor = 1e-8;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+inline awq_status hip_status(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP; }
+inline awq_status last_launch_status() { return hip_status(hipGetLastError()); }
+
+// ---- launchers (each returns after enqueueing on `stream`) ----
+
+// Group-wise INT4 quantization of W[N, K] (optionally times channel_scale[K]).
+awq_status launch_quantize(const half_t* w, const float* channel_scale, int64_t N, int64_t K,
+                           int group_size, uint32_t* qweight, half_t* scales, half_t* zeros,
+                           hipStream_t stream);
+
+// Decode GEMV y[M, N] = x[M, K] . dequant(Wq)^T for M <= kGemvMaxM.
+constexpr int kGemvMaxM = 8;
+bool gemv_supported(int64_t M, int64_t K);
+awq_status launch_gemv(const half_t* x, const uint32_t* qweight, const half_t* scales,
+                       const half_t* zeros, int64_t M, int64_t N, int64_t K, int group_size,
+                       half_t* y, hipStream_t stream);
+
+// MFMA GEMM. The B operand is either INT4 (qweight/scales/zeros) or fp16 W[N, K].
+enum class GemmB { kInt4, kF16 };
+enum class GemmOut { kF16, kF32, kLoss };
+struct GemmArgs {
+    const half_t* a = nullptr;        // [M, K]
+    const uint32_t* qweight = nullptr;
+    const half_t* scales = nullptr;
+    const half_t* zeros = nullptr;
+    const half_t* w = nullptr;        // fp16 B, [N, K]
+    int group_size = 128;
+    int64_t M = 0, N = 0, K = 0;
+    half_t* y16 = nullptr;            // kF16 output [M, N]
+    float* y32 = nullptr;             // kF32 output [M, N]
+    const float* yref = nullptr;      // kLoss reference [M, N]
+    double* partials = nullptr;       // kLoss: one double per tile
+};
+int64_t gemm_tile_count(int64_t M, int64_t N);
+awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t stream);
+
+// Scale-search helpers.
+size_t absmean_workspace_bytes(int64_t T, int64_t K);
+awq_status launch_absmean(const half_t* x, int64_t T, int64_t K, double* m, double* partials,
+                          hipStream_t stream);
+awq_status launch_pow_scales(const double* m, int64_t K, double alpha, float* s, hipStream_t stream);
+awq_status launch_divide_columns(const half_t* x, const float* s, int64_t T, int64_t K, half_t* xs,
+                                 hipStream_t stream);
+awq_status launch_sum_partials(const double* partials, int64_t n, double* out, hipStream_t stream);
+
+}  // namespace awq

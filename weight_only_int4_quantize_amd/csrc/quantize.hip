@@ -1,0 +1,103 @@
+// Group-wise asymmetric INT4 quantization (min/max -> scale/zero -> codes -> pack).
+//
+// The map is the one of "模型量化:GGUF/AWQ/GPTQ部署方案" §1.2 (q = clamp(round(x /
+// scale) + zero_point, 0, 15), scale from the weight range) with one scale and
+// zero-point per group of G consecutive input channels (§1.4; aissn.com
+// "量化粒度"), asymmetric (aissn.com "对称/非对称量化").
+//
+// Layout: one thread per packed word, i.e. 8 consecutive k of one row, read as
+// one 16-byte load. The G/8 threads of a group are adjacent lanes of one
+// wavefront, so a wave streams 64 * 16 B = 1 KB of contiguous weights and the
+// group min/max is a 3- or 4-step butterfly over lanes. Every arithmetic step
+// is IEEE fp32 (correctly rounded divide, round-half-to-even rint) so the
+// codes, scales and zeros are bit-identical to a plain fp32 evaluation.
+#include "awq_internal.h"
+
+namespace awq {
+namespace {
+
+#pragma clang fp contract(off)
+
+template <int G>
+__global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict__ w,
+                                                       const float* __restrict__ channel_scale,
+                                                       int64_t n_words, int64_t words_per_row,
+                                                       uint32_t* __restrict__ qweight,
+                                                       half_t* __restrict__ scales,
+                                                       half_t* __restrict__ zeros) {
+    constexpr int kLanes = G / 8;  // threads per group: 8 (G=64) or 16 (G=128)
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    // n_words is a multiple of kLanes and kLanes divides 64, so a group's
+    // lanes are either all in range or all out of range.
+    if (t >= n_words) return;
+
+    const uint4 raw = reinterpret_cast<const uint4*>(w)[t];
+    const uint32_t parts[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(parts[i] & 0xFFFFu)));
+        v[2 * i + 1] = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(parts[i] >> 16)));
+    }
+    if (channel_scale != nullptr) {
+        const int64_t k0 = (t % words_per_row) * 8;
+        const float4 c0 = *reinterpret_cast<const float4*>(channel_scale + k0);
+        const float4 c1 = *reinterpret_cast<const float4*>(channel_scale + k0 + 4);
+        v[0] = v[0] * c0.x; v[1] = v[1] * c0.y; v[2] = v[2] * c0.z; v[3] = v[3] * c0.w;
+        v[4] = v[4] * c1.x; v[5] = v[5] * c1.y; v[6] = v[6] * c1.z; v[7] = v[7] * c1.w;
+    }
+
+    float lo = v[0], hi = v[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+        lo = fminf(lo, v[i]);
+        hi = fmaxf(hi, v[i]);
+    }
+#pragma unroll
+    for (int o = 1; o < kLanes; o <<= 1) {
+        lo = fminf(lo, __shfl_xor(lo, o, kLanes));
+        hi = fmaxf(hi, __shfl_xor(hi, o, kLanes));
+    }
+
+    const float range = fmaxf(hi - lo, kRangeFloor);
+    const float s32 = range / 15.0f;                 // IEEE divide
+    const half_t s16 = static_cast<half_t>(s32);      // round-to-nearest-even
+    const float sf = static_cast<float>(s16);
+    const int zi = static_cast<int>(fminf(fmaxf(rintf(-lo / sf), 0.0f), 15.0f));
+    const float z = static_cast<float>(zi);
+
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float q = fminf(fmaxf(rintf(v[j] / sf) + z, 0.0f), 15.0f);
+        packed |= static_cast<uint32_t>(q) << (4 * j);
+    }
+    qweight[t] = packed;
+    if ((t & (kLanes - 1)) == 0) {
+        const int64_t gi = t / kLanes;
+        scales[gi] = s16;
+        zeros[gi] = static_cast<half_t>(z);
+    }
+}
+
+}  // namespace
+
+awq_status launch_quantize(const half_t* w, const float* channel_scale, int64_t N, int64_t K,
+                           int group_size, uint32_t* qweight, half_t* scales, half_t* zeros,
+                           hipStream_t stream) {
+    const int64_t words_per_row = K / 8;
+    const int64_t n_words = N * words_per_row;
+    if (n_words == 0) return AWQ_OK;
+    const int threads = 256;
+    const int64_t blocks = ceil_div(n_words, threads);
+    if (group_size == 128) {
+        hipLaunchKernelGGL(quantize_kernel<128>, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0,
+                           stream, w, channel_scale, n_words, words_per_row, qweight, scales, zeros);
+    } else {
+        hipLaunchKernelGGL(quantize_kernel<64>, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0,
+                           stream, w, channel_scale, n_words, words_per_row, qweight, scales, zeros);
+    }
+    return last_launch_status();
+}
+
+}  // namespace awq
