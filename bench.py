@@ -72,7 +72,7 @@ class StreamTimer:
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true")
@@ -117,14 +117,45 @@ def main():
         for (qw, sc, zr, x, y, N, K) in copies[i % n_copies]:
             awq.awq_gemm(x, qw, sc, zr, G, out=y)
 
-    for i in range(args.warmup):
+    for i in range(max(args.warmup, 1)):
         step(i)
-    t_steps = timer.time(step, args.steps)
+    torch.cuda.synchronize()
+
+    def capture(fn, count):
+        """HIP graph of `count` calls fn(0..count-1); replays have no host
+        launch cost between kernels."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(count):
+                    fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        return g
+
+    # one graph per full rotation over the weight copies, one for the rest,
+    # so that exactly args.steps steps are timed
+    g_full = capture(step, n_copies)
+    rem = args.steps % n_copies
+    g_rem = capture(step, rem) if rem else None
+    n_full = args.steps // n_copies
+
+    def timed_steps(_):
+        for _r in range(n_full):
+            g_full.replay()
+        if g_rem is not None:
+            g_rem.replay()
+
+    g_full.replay()
+    t_steps = timer.time(timed_steps, 1)
     ms_per_step = t_steps / args.steps * 1e3
     value = step_bytes * args.steps / t_steps / 1e9
     log(f"decode layer: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s")
 
-    # per-shape GEMV launch durations (back-to-back launches, rotated copies)
+    # per-shape GEMV launch durations (graph of back-to-back launches over the
+    # rotated copies)
     per_shape = {}
     for (N, K) in synth.DECODE_SHAPES:
         idx = [j for j, (_, n, k) in enumerate(linears) if (n, k) == (N, K)][0]
@@ -134,13 +165,14 @@ def main():
             qw, sc, zr, x, y, _, _ = bufs[i % len(bufs)]
             awq.awq_gemm(x, qw, sc, zr, G, out=y)
 
-        reps = 400
-        for i in range(20):
-            one(i)
-        t = timer.time(one, reps) / reps
+        reps = 8 * n_copies
+        g1 = capture(one, reps)
+        g1.replay()
+        t = timer.time(lambda _: g1.replay(), 4) / (4 * reps)
         b = gemv_bytes(1, N, K)
         per_shape[f"{N}x{K}"] = {"us": round(t * 1e6, 3), "GB/s": round(b / t / 1e9, 1), "bytes": b}
         log(f"gemv {N}x{K}: {t * 1e6:.2f} us, {b / t / 1e9:.0f} GB/s")
+        del g1
     big = per_shape[f"{11008}x{4096}"]
 
     # ---------------------------------------------------------------- prefill GEMM

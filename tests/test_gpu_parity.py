@@ -358,3 +358,36 @@ def test_scale_search_full_size(w_mult):
         float(np.max(np.abs(losses - losses_o) / losses_o)))
     check_search(losses, best, host(s), losses_o, g["best_index"], s_o)
     assert best == g["best_index"]
+
+
+# ---------------------------------------------------------------- graphs
+
+def test_graph_replay_matches_eager():
+    """awq_gemm captured in a HIP graph (GEMV and MFMA paths) gives the eager
+    result, bit for bit, on every replay, with eager work between replays."""
+    lay = synth.make_layer(1024, 1024, 64, seed=[110], w_std=0.02)
+    qw, sc, zr = awq.awq_quantize(dev(lay["w"]), 128)
+    x1, x64 = dev(lay["x"][:1]), dev(lay["x"])
+    e1 = awq.awq_gemm(x1, qw, sc, zr, 128).clone()
+    e64 = awq.awq_gemm(x64, qw, sc, zr, 128).clone()
+    y1 = torch.empty_like(e1)
+    y64 = torch.empty_like(e64)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            awq.awq_gemm(x1, qw, sc, zr, 128, out=y1)
+            awq.awq_gemm(x64, qw, sc, zr, 128, out=y64)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    w2 = dev(synth.make_layer(512, 512, 0, seed=[111])["w"])
+    for r in range(4):
+        y1.fill_(0)
+        y64.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        awq.awq_quantize(w2, 128)           # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y1, e1), r
+        assert torch.equal(y64, e64), r
