@@ -248,7 +248,10 @@ def test_linear_ragged_both_paths(M, N, K, G):
 
 @pytest.mark.parametrize("path", [awq.PATH_GEMV, awq.PATH_GEMM])
 def test_one_hot_input_returns_dequantized_column(path):
-    """x = e_k: y = fp16 of the dequantized column k, exactly, on both paths."""
+    """x = e_k: y = fp16 of the dequantized column k. Exact on the GEMV path
+    (one scale multiply); on the MFMA path the accumulator is carried in units
+    of the running group's scale, so the result is w_hat * (1 + e) with
+    |e| <= (K / G) fp32 roundings, and y is the fp16 rounding of that."""
     N, K, G = 96, 256, 64
     lay = synth.make_layer(N, K, 0, seed=[105], w_std=0.02)
     qw, sc, zr = oracle.quantize(lay["w"], G)
@@ -262,8 +265,12 @@ def test_one_hot_input_returns_dequantized_column(path):
             y = run_linear(x[i:i + 1], qw, sc, zr, G, path)
             assert np.array_equal(y[0], w_hat[:, ks[i]].astype(np.float16))
     else:
-        y = run_linear(x, qw, sc, zr, G, path)
-        assert np.array_equal(y, w_hat[:, ks].T.astype(np.float16))
+        y = run_linear(x, qw, sc, zr, G, path).astype(np.float64)
+        ref = w_hat[:, ks].T
+        half_ulp = np.abs(ref.astype(np.float16).astype(np.float64) -
+                          np.nextafter(ref.astype(np.float16), np.float16(np.inf)).astype(np.float64)) / 2
+        bound = half_ulp * (1 + 1e-3) + np.abs(ref) * (K // G + 1) * 2.0 ** -23
+        assert np.all(np.abs(y - ref) <= bound)
 
 
 def test_linear_is_linear_in_x():

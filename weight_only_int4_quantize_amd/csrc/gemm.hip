@@ -7,22 +7,28 @@
 // Exactness: the dequantized weight (q - z) * s has up to 15 significant bits,
 // more than fp16 holds, and rounding it before the MFMA costs up to ~2e-2
 // absolute on outputs fed by salient channels. So the B operand is the exact
-// integer (q - z) in fp16, and the group's scale is applied in fp32: each
-// group's MFMA partial T = A . (Q - Z)^T over its G columns of k accumulates
-// in fresh registers, then C += s[n, g] * T (one FMA per element per group).
+// integer (q - z) in fp16, and the group's scale is applied in fp32 to the
+// accumulator, which is kept in units of the current group's scale:
+// C' = C / s_g. Crossing into group g + 1 multiplies C' by s_g / s_{g+1}
+// (one v_mul per accumulator element per group); the end multiplies by the
+// last scale. Each step rounds once in fp32, ~1e-7 relative per group.
 //
-// Tiling (gfx950): a 256-thread block computes a BM x BN tile of y with 4
-// wavefronts in a 2 x 2 arrangement; each wave owns (BM/2) x (BN/2) as a grid
-// of v_mfma_f32_32x32x16_f16 tiles. K advances in steps of BK = 64 (a group
-// is one or two steps):
-//  * A (activations, fp16) is copied global -> LDS with 16-byte loads;
-//  * B (packed INT4) is read one 16-byte word group (32 codes) per thread,
-//    turned into exact fp16 (q - z) once per block and written to LDS in
-//    natural k order; the fp16-B variant copies W directly;
-//  * LDS rows are padded by 16 bytes so the 16-byte fragment reads of 32
-//    consecutive rows spread over all banks;
-//  * two LDS stages: the next step's global loads are issued before the
-//    current step's MFMAs and stored after them.
+// Tiling (gfx950, 160 KB LDS, 4 SIMDs per CU):
+//  * a 256-thread block owns a BM x BN tile of y, 4 wavefronts in a 2 x 2
+//    arrangement; the 256 x 128 shape gives each wave 128 x 64 outputs as
+//    4 x 2 v_mfma_f32_32x32x16_f16 accumulators (128 VGPRs, VGPR form), so
+//    every 16-byte fragment read from LDS feeds 2-4 MFMAs;
+//  * K advances in steps of BK = 32. A (fp16) moves global -> registers ->
+//    LDS; B (packed INT4) is read as raw words, turned into exact fp16
+//    (q - z) once per block and written to LDS in natural k order (the
+//    fp16-B variant copies W). The next step's global loads are in flight
+//    while the current step's MFMAs run (two LDS stages, 60 KB, so two
+//    blocks fit on a CU);
+//  * LDS rows are 64 bytes with an XOR swizzle of their four 16-byte chunks
+//    (see swz), so fragment reads and staging writes are bank-conflict free;
+//  * blocks are dealt to the 8 XCDs round-robin by the dispatcher; the tile
+//    order is remapped so each XCD works through a contiguous, m-major range
+//    of tiles and keeps the shared A rows in its own L2.
 // MFMA operand layout (32x32x16 f16): lane l supplies row (l mod 32) of A and
 // column (l mod 32) of B, with k-slice 8 * (l / 32) .. +7 of the 16; the
 // accumulator element i of lane l is C[8 * (i / 4) + 4 * (l / 32) + i mod 4]
@@ -32,23 +38,46 @@
 namespace awq {
 namespace {
 
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;          // padded LDS row (halves)
+constexpr int BK = 32;
+constexpr int LDK = BK;              // LDS row (halves): 64 bytes, 4 chunks of 16 bytes
+
+// gfx950 LDS: 64 banks of 4 bytes; a 16-byte-per-lane access is served 16
+// lanes at a time, which is conflict-free when those 16 lanes hit 16 distinct
+// 16-byte slots modulo 256 bytes. 16-byte chunk c of LDS row r is stored at
+// chunk position c ^ ((r >> 2) & 3): the fragment reads (16 consecutive rows,
+// one chunk), the A stores (4 rows x 4 chunks) and the B stores (8 rows x 2
+// chunks) then each cover all 64 banks once.
+__device__ __forceinline__ int swz(int r, int c) { return r * LDK + ((c ^ ((r >> 2) & 3)) << 3); }
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;
+// A zero group scale would make the rescale ratio infinite; it is taken as
+// the smallest positive fp16 value instead.
+constexpr float kTinyScale = 5.9604645e-08f;
 
 __device__ inline half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 __device__ inline uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 
+struct UnpackConsts {
+    uint32_t lo_mask, hi_mask, lo_magic, hi_magic;
+};
+// Held in VGPRs so each (w & mask) | magic is one v_and_or_b32 (gfx9 VOP3
+// takes no 32-bit literal and one SGPR at most).
+__device__ inline UnpackConsts unpack_consts() {
+    UnpackConsts k{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
+    asm volatile("" : "+v"(k.lo_mask), "+v"(k.hi_mask), "+v"(k.lo_magic), "+v"(k.hi_magic));
+    return k;
+}
+
 // One packed word (codes k0..k7) -> 8 exact fp16 values (q - z), natural k
 // order, as 4 packed pairs. zc_hi = 1024 + z, zc_lo = 64 + z (both exact).
-__device__ inline uint4 unpack_word(uint32_t wq, half2_t zc_hi, half2_t zc_lo) {
+__device__ inline uint4 unpack_word(uint32_t wq, half2_t zc_hi, half2_t zc_lo, const UnpackConsts& k) {
     const uint32_t w8 = wq >> 8;
     // OR-ing a nibble into an fp16 mantissa gives an exact integer:
     // (1024 + q0, 1024 + q4), (64 + q1, 64 + q5), (1024 + q2, 1024 + q6), (64 + q3, 64 + q7)
-    const half2_t a = as_h2((wq & 0x000F000Fu) | 0x64006400u) - zc_hi;
-    const half2_t b = as_h2((wq & 0x00F000F0u) | 0x54005400u) - zc_lo;
-    const half2_t c = as_h2((w8 & 0x000F000Fu) | 0x64006400u) - zc_hi;
-    const half2_t d = as_h2((w8 & 0x00F000F0u) | 0x54005400u) - zc_lo;
+    const half2_t a = as_h2((wq & k.lo_mask) | k.lo_magic) - zc_hi;
+    const half2_t b = as_h2((wq & k.hi_mask) | k.hi_magic) - zc_lo;
+    const half2_t c = as_h2((w8 & k.lo_mask) | k.lo_magic) - zc_hi;
+    const half2_t d = as_h2((w8 & k.hi_mask) | k.hi_magic) - zc_lo;
     const uint32_t ua = as_u32(a), ub = as_u32(b), uc = as_u32(c), ud = as_u32(d);
     uint4 r;
     r.x = (ua & 0xFFFFu) | (ub << 16);          // (k0, k1)
@@ -58,17 +87,83 @@ __device__ inline uint4 unpack_word(uint32_t wq, half2_t zc_hi, half2_t zc_lo) {
     return r;
 }
 
+// Registers carrying one K step from global memory to LDS.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Registers carrying one K step from global memory to LDS (native vector
+// types, which the compiler keeps in registers).
+template <int A_VECS, int B_VECS>
+struct Stage {
+    u32x4 a[A_VECS];
+    u32x4 b[B_VECS];      // fp16 B
+    u32x2 braw;           // int4 B: 16 codes
+    half_t bz;            // int4 B: their zero-point
+};
+
+// column (in halves) of the 16-byte A/B chunk a thread stages
+__device__ __forceinline__ int c8_of(int tid) { return (tid % (BK / 8)) * 8; }
+
+template <bool INT4, int A_VECS, int B_VECS>
+__device__ __forceinline__ void load_stage(Stage<A_VECS, B_VECS>& st, const half_t* a_base, const int (&a_row)[A_VECS],
+                                           int K, const uint32_t* b_words, const half_t* b_zeros, int G,
+                                           const half_t* w_base, const int (&b_row)[B_VECS], int k0) {
+#pragma unroll
+    for (int i = 0; i < A_VECS; ++i)
+        st.a[i] = *reinterpret_cast<const u32x4*>(a_base + static_cast<int64_t>(a_row[i]) * K + k0);
+    if constexpr (INT4) {
+        st.braw = *reinterpret_cast<const u32x2*>(b_words + k0 / 8);
+        st.bz = b_zeros[k0 / G];
+    } else {
+#pragma unroll
+        for (int i = 0; i < B_VECS; ++i)
+            st.b[i] = *reinterpret_cast<const u32x4*>(w_base + static_cast<int64_t>(b_row[i]) * K + k0);
+    }
+}
+
+template <bool INT4, int BM, int BN, int A_VECS, int B_VECS>
+__device__ __forceinline__ void store_stage(const Stage<A_VECS, B_VECS>& st, half_t* as, half_t* bs, int tid,
+                                            int b_row, int b_half, const UnpackConsts& uk) {
+#pragma unroll
+    for (int i = 0; i < A_VECS; ++i) {
+        const int idx = tid + i * kThreads;
+        *reinterpret_cast<u32x4*>(&as[swz(idx / (BK / 8), idx % (BK / 8))]) = st.a[i];
+    }
+    if constexpr (INT4) {
+        const half_t zh = static_cast<half_t>(1024.0f) + st.bz;   // exact
+        const half_t zl = static_cast<half_t>(64.0f) + st.bz;     // exact
+        const half2_t zc_hi{zh, zh}, zc_lo{zl, zl};
+        *reinterpret_cast<uint4*>(&bs[swz(b_row, b_half * 2)]) = unpack_word(st.braw.x, zc_hi, zc_lo, uk);
+        *reinterpret_cast<uint4*>(&bs[swz(b_row, b_half * 2 + 1)]) = unpack_word(st.braw.y, zc_hi, zc_lo, uk);
+    } else {
+#pragma unroll
+        for (int i = 0; i < B_VECS; ++i) {
+            const int idx = tid + i * kThreads;
+            *reinterpret_cast<u32x4*>(&bs[swz(idx / (BK / 8), idx % (BK / 8))]) = st.b[i];
+        }
+    }
+}
+
+// Block index -> tile index: XCD x (= block mod 8) gets a contiguous range.
+__device__ inline int xcd_tile(int block, int tiles) {
+    const int q = tiles / kXcds, r = tiles % kXcds;
+    const int x = block % kXcds, local = block / kXcds;
+    return x * q + min(x, r) + local;
+}
+
 template <int BM, int BN, GemmB BMODE, GemmOut OMODE>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs args, int tiles_n) {
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int tiles_n) {
     constexpr int WTM = BM / 2;                 // wave tile rows
     constexpr int WTN = BN / 2;                 // wave tile cols
     constexpr int TM = WTM / 32;                // 32x32 MFMA tiles per wave (M)
     constexpr int TN = WTN / 32;                // 32x32 MFMA tiles per wave (N)
-    constexpr int A_VECS = BM * BK / 8 / kThreads;   // uint4 of A per thread per step
+    constexpr int A_VECS = BM * BK / 8 / kThreads;        // uint4 of A per thread per step
     constexpr bool INT4 = BMODE == GemmB::kInt4;
-    constexpr int B_VECS = INT4 ? 1 : BN * BK / 8 / kThreads;
-    static_assert(TM >= 1 && TN >= 1 && A_VECS >= 1 && B_VECS >= 1, "tile shape");
-    static_assert(!INT4 || BN * 2 == kThreads, "int4 B staging assumes 2 threads per row");
+    constexpr int B_WORDS = BN * BK / 8 / kThreads;       // packed words per thread per step
+    constexpr int B_VECS = BN * BK / 8 / kThreads;        // fp16 B: uint4 per thread per step (int4: unused)
+    static_assert(TM >= 1 && TN >= 1 && A_VECS >= 1, "tile shape");
+    static_assert(!INT4 || B_WORDS == 2, "int4 B staging: 2 words (16 codes) per thread");
+    static_assert(INT4 || B_VECS >= 1, "fp16 B staging");
 
     __shared__ __attribute__((aligned(16))) half_t As[2][BM * LDK];
     __shared__ __attribute__((aligned(16))) half_t Bs[2][BN * LDK];
@@ -78,93 +173,52 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs args, int tiles
     const int K = static_cast<int>(args.K);
     const int G = args.group_size;
     const int ngroups = K / G;
-    const int tile = blockIdx.x;
+    const int tile = xcd_tile(blockIdx.x, gridDim.x);
     const int tm = (tile / tiles_n) * BM;
     const int tn = (tile % tiles_n) * BN;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int wm = (wave >> 1) * WTM;
     const int wn = (wave & 1) * WTN;
+    const UnpackConsts uk = unpack_consts();
 
-    uint4 a_reg[A_VECS];
-    uint4 b_reg[B_VECS];
-    half2_t b_zhi, b_zlo;
-    const int b_row = tid >> 1;          // int4 staging: row within tile
-    const int b_half = tid & 1;          // int4 staging: which 32 codes of BK
+    // ---- staging: rows past M / N read the last row (their outputs are
+    //      never stored), so every load is in bounds and unconditional ----
+    Stage<A_VECS, B_VECS> st;
+    const half_t* a_base = args.a + c8_of(tid) ;
+    int a_off[A_VECS];
+#pragma unroll
+    for (int i = 0; i < A_VECS; ++i) {
+        const int r = (tid + i * kThreads) / (BK / 8);
+        a_off[i] = min(tm + r, M - 1);
+    }
+    // int4 B: thread t stages row t / 2, codes 16 * (t % 2) .. +15 of the step
+    const int b_row = tid >> 1;
+    const int b_half = tid & 1;
+    const int64_t b_n = min(tn + b_row, N - 1);
+    const uint32_t* b_words = args.qweight + b_n * (K / 8) + b_half * 2;
+    const half_t* b_zeros = args.zeros + b_n * ngroups;
+    int b_off[B_VECS];
+#pragma unroll
+    for (int i = 0; i < B_VECS; ++i) b_off[i] = min(tn + (tid + i * kThreads) / (BK / 8), N - 1);
 
-    auto load_stage = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < A_VECS; ++i) {
-            const int idx = tid + i * kThreads;
-            const int r = idx >> 3, c8 = (idx & 7) * 8;
-            const int gm = tm + r;
-            a_reg[i] = gm < M ? *reinterpret_cast<const uint4*>(args.a + static_cast<int64_t>(gm) * K + k0 + c8)
-                              : make_uint4(0, 0, 0, 0);
-        }
-        if constexpr (INT4) {
-            const int gn = tn + b_row;
-            if (gn < N) {
-                const int kq = k0 + b_half * 32;
-                b_reg[0] = *reinterpret_cast<const uint4*>(args.qweight + static_cast<int64_t>(gn) * (K / 8) + kq / 8);
-                const half_t z = args.zeros[static_cast<int64_t>(gn) * ngroups + kq / G];
-                const half_t zh = static_cast<half_t>(1024.0f) + z;   // exact
-                const half_t zl = static_cast<half_t>(64.0f) + z;     // exact
-                b_zhi = half2_t{zh, zh};
-                b_zlo = half2_t{zl, zl};
-            } else {
-                // rows past N: codes 0 with zero 0 -> exact zeros
-                b_reg[0] = make_uint4(0, 0, 0, 0);
-                b_zhi = half2_t{1024, 1024};
-                b_zlo = half2_t{64, 64};
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < B_VECS; ++i) {
-                const int idx = tid + i * kThreads;
-                const int r = idx >> 3, c8 = (idx & 7) * 8;
-                const int gn = tn + r;
-                b_reg[i] = gn < N ? *reinterpret_cast<const uint4*>(args.w + static_cast<int64_t>(gn) * K + k0 + c8)
-                                  : make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-
-    auto store_stage = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < A_VECS; ++i) {
-            const int idx = tid + i * kThreads;
-            const int r = idx >> 3, c8 = (idx & 7) * 8;
-            *reinterpret_cast<uint4*>(&As[buf][r * LDK + c8]) = a_reg[i];
-        }
-        if constexpr (INT4) {
-            const uint32_t words[4] = {b_reg[0].x, b_reg[0].y, b_reg[0].z, b_reg[0].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<uint4*>(&Bs[buf][b_row * LDK + b_half * 32 + j * 8]) =
-                    unpack_word(words[j], b_zhi, b_zlo);
-        } else {
-#pragma unroll
-            for (int i = 0; i < B_VECS; ++i) {
-                const int idx = tid + i * kThreads;
-                const int r = idx >> 3, c8 = (idx & 7) * 8;
-                *reinterpret_cast<uint4*>(&Bs[buf][r * LDK + c8]) = b_reg[i];
-            }
-        }
-    };
-
-    // scales of this lane's output columns for one group (int4 mode)
+    // scales of this lane's output columns (int4 mode)
     const int lcol = lane & 31;
-    auto load_scales = [&](int g, float (&s)[TN]) {
+    const half_t* s_src[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = tn + wn + j * 32 + lcol;
-            s[j] = n < N ? static_cast<float>(args.scales[static_cast<int64_t>(n) * ngroups + g]) : 0.f;
-        }
+    for (int j = 0; j < TN; ++j) s_src[j] = args.scales + static_cast<int64_t>(min(tn + wn + j * 32 + lcol, N - 1)) * ngroups;
+    // scales travel as raw fp16 bits and are converted only when used, a
+    // group after their load, so no wait is forced on the loads in flight
+    const uint16_t* s_bits[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) s_bits[j] = reinterpret_cast<const uint16_t*>(s_src[j]);
+    auto to_scale = [](uint16_t bits) {
+        const float s = static_cast<float>(__builtin_bit_cast(half_t, bits));
+        return s == 0.f ? kTinyScale : s;
     };
 
     float16_t acc[TM][TN];
-    float16_t part[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -172,71 +226,97 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs args, int tiles
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    const int lrow = lane & 31;
-    const int lk = (lane >> 5) * 8;
     const int nk = K / BK;
-    float sc[TN];
-    if constexpr (INT4) load_scales(0, sc);
+    const int steps_per_group = INT4 ? G / BK : nk + 1;
+    int g = 0;
+    float s_cur[TN];
+    uint16_t s_next[TN];
+    if constexpr (INT4) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            s_cur[j] = to_scale(s_bits[j][0]);
+            s_next[j] = s_bits[j][ngroups > 1 ? 1 : 0];
+        }
+    }
 
-    load_stage(0);
-    store_stage(0);
+    // Two register stages: the loads for step kt + 2 are issued while step kt
+    // computes, and land in LDS at the end of step kt + 1. Loads past the
+    // last step re-read it (in bounds, never stored), so nothing branches.
+    Stage<A_VECS, B_VECS> st1;
+    const int last_k0 = K - BK;
+    auto load = [&](Stage<A_VECS, B_VECS>& dst, int k0) {
+        load_stage<INT4>(dst, a_base, a_off, K, b_words, b_zeros, G, args.w + c8_of(tid), b_off, min(k0, last_k0));
+    };
+    load(st, 0);
+    load(st1, BK);
+    store_stage<INT4, BM, BN>(st, As[0], Bs[0], tid, b_row, b_half, uk);
     __syncthreads();
 
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) load_stage((kt + 1) * BK);
-        const int k0 = kt * BK;
-        const bool group_start = INT4 && (k0 % G) == 0;
-        const bool group_end = INT4 && ((k0 + BK) % G) == 0;
+    const int lrow = lane & 31;
+    const int lchunk = lane >> 5;          // which 8-k half of a 16-k MFMA step
+    auto compute = [&](const half_t* as, const half_t* bs, int kt) {
+        if constexpr (INT4) {
+            if (kt > 0 && (kt % steps_per_group) == 0) {
+                // entering the next group: C' <- C' * s_g / s_{g+1}
+                ++g;
+                float r[TN];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const float sn = to_scale(s_next[j]);
+                    r[j] = s_cur[j] / sn;
+                    s_cur[j] = sn;
+                }
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) acc[i][j][e] *= r[j];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) s_next[j] = s_bits[j][min(g + 1, ngroups - 1)];
+            }
+        }
+        // raised priority while this wave feeds the matrix core, so the other
+        // block's wave on the SIMD does its memory work in the gaps
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             half8_t af[TM], bf[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const half8_t*>(&As[buf][(wm + i * 32 + lrow) * LDK + ks * 16 + lk]);
+                af[i] = *reinterpret_cast<const half8_t*>(&as[swz(wm + i * 32 + lrow, ks * 2 + lchunk)]);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                bf[j] = *reinterpret_cast<const half8_t*>(&Bs[buf][(wn + j * 32 + lrow) * LDK + ks * 16 + lk]);
-            if constexpr (INT4) {
-                if (group_start && ks == 0) {
-                    const float16_t zero = {};
+                bf[j] = *reinterpret_cast<const half8_t*>(&bs[swz(wn + j * 32 + lrow, ks * 2 + lchunk)]);
 #pragma unroll
-                    for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-                        for (int j = 0; j < TN; ++j)
-                            part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], zero, 0, 0, 0);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-#pragma unroll
-                        for (int j = 0; j < TN; ++j)
-                            part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], part[i][j], 0, 0, 0);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-            }
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
-        if constexpr (INT4) {
-            if (group_end) {
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) acc[i][j][e] = fmaf(sc[j], part[i][j][e], acc[i][j][e]);
-                if (more) load_scales((k0 + BK) / G, sc);
-            }
-        }
-        if (more) store_stage(buf ^ 1);
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    for (int kt = 0; kt < nk; kt += 2) {       // nk is even (K is a multiple of 64)
+        load(st, (kt + 2) * BK);
+        compute(As[0], Bs[0], kt);
+        store_stage<INT4, BM, BN>(st1, As[1], Bs[1], tid, b_row, b_half, uk);
+        __syncthreads();
+        load(st1, (kt + 3) * BK);
+        compute(As[1], Bs[1], kt + 1);
+        store_stage<INT4, BM, BN>(st, As[0], Bs[0], tid, b_row, b_half, uk);
         __syncthreads();
     }
 
     // ---- epilogue ----
+    if constexpr (INT4) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] *= s_cur[j];
+    }
     const int lrow4 = (lane >> 5) * 4;
     float sq = 0.f;
 #pragma unroll
@@ -277,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs args, int tiles
     }
 }
 
-constexpr int kBM = 128;
+constexpr int kBM = 256;
 constexpr int kBN = 128;
 
 template <GemmB BMODE, GemmOut OMODE>
