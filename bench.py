@@ -1,16 +1,25 @@
 """W4A16 benchmark on one MI355X: decode GEMV effective HBM GB/s (M = 1) and
-prefill GEMM TFLOP/s (M = 2048), each as a fraction of its roofline.
+prefill GEMM TFLOP/s (M = 2048), each against its roofline.
 
 A step is one decode pass over the seven linear layers of a Llama-7B-shaped
 decoder layer (q/k/v/o 4096x4096, gate/up 11008x4096, down 4096x11008; INT4,
-group 128, zero-points) at M = 1 through awq_gemm. Weights rotate over enough
-copies (> 1 GB) that the 256 MB last-level cache cannot hold them, so every
-step streams its weights from HBM. The same run also times the prefill GEMM
-(x[2048, K] times the two MLP shapes), the quantize kernel and one full scale
-search (W[11008, 4096], X[65536, 4096], 20 alphas), and the CPU oracle on a
-bounded sample for the baseline.
+group 128, zero-points) at M = 1 through awq_gemm. The weights rotate over
+enough copies (> 1.2 GB) that the 256 MB last-level cache cannot hold them,
+so every step streams its weights from HBM; the steps are replayed from HIP
+graphs, so host launch cost is outside the timed kernels. `value` is the
+step's algorithmic bytes over its time.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+The same run also times, each in its own section:
+  * the roofline kernel: the gate/up GEMV (11008x4096, the largest launch of
+    the step) back to back over the rotated copies;
+  * the prefill GEMM, x[2048, K] times the two MLP shapes;
+  * the quantize kernel on 11008x4096;
+  * one full scale search (W[11008, 4096], X[65536, 4096], 20 alphas);
+  * an HBM copy of 1 GiB (context for the achievable bandwidth, and the
+    calibration of the FETCH_SIZE / WRITE_SIZE counters);
+  * the CPU oracle on a bounded sample (the CPU baseline).
+
+    python bench.py [--gpus 1] [--steps 240] [--warmup 20] [--only SECTION]
 """
 
 from __future__ import annotations
@@ -32,6 +41,8 @@ METRIC = "W4A16 GEMV eff. HBM GB/s (M=1) + GEMM TFLOP/s (M=2048), % of roofline"
 HBM_PEAK_GBS = 8000.0
 F16_MFMA_PEAK_TFLOPS = 2500.0
 G = 128
+ROOFLINE_SHAPE = (11008, 4096)     # gate/up projection, the step's largest launch
+COPY_BYTES = 1 << 30
 
 
 def gemv_bytes(M, N, K, g=G):
@@ -49,14 +60,43 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-class StreamTimer:
-    """HIP events on the stream the library's kernels are enqueued on."""
+def measured_traffic():
+    """HBM bytes per launch of the roofline kernel, from the FETCH_SIZE and
+    WRITE_SIZE counter runs recorded under profiles/ (scaled by the same
+    counters read on a copy of known size). None once the kernel source has
+    changed since the counters were taken."""
+    import hashlib
 
-    def __init__(self, torch):
-        self.torch = torch
+    path = os.path.join(ROOT, "profiles", "gemv_m1_11008x4096_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            current = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None, None
+    if current != rec.get("source_sha256"):
+        return None, None
+    return int(rec["traffic_bytes_per_launch"]), rec["copy_calibration"]
+
+
+class Bench:
+    def __init__(self, args):
+        import torch
+        import weight_only_int4_quantize_amd as awq
+
+        self.torch, self.awq, self.args = torch, awq, args
+        if not torch.cuda.is_available():
+            raise SystemExit("bench.py needs a GPU")
+        self.dev = "cuda:0"
+        # HIP events recorded on the stream the library's kernels are enqueued
+        # on (the binding passes torch's current stream)
         self.stream = torch.cuda.current_stream()
 
-    def time(self, fn, reps):
+    def d(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)
+
+    def time(self, fn, reps=1):
         t = self.torch
         start = t.cuda.Event(enable_timing=True)
         stop = t.cuda.Event(enable_timing=True)
@@ -68,6 +108,204 @@ class StreamTimer:
         stop.synchronize()
         return start.elapsed_time(stop) / 1e3   # seconds
 
+    def capture(self, fn, count):
+        """HIP graph of `count` calls fn(0..count-1)."""
+        t = self.torch
+        g = t.cuda.CUDAGraph()
+        side = t.cuda.Stream()
+        side.wait_stream(t.cuda.current_stream())
+        with t.cuda.stream(side):
+            with t.cuda.graph(g, stream=side):
+                for i in range(count):
+                    fn(i)
+        t.cuda.current_stream().wait_stream(side)
+        t.cuda.synchronize()
+        return g
+
+    # ------------------------------------------------------------ decode layer
+    def setup_decode(self):
+        torch, awq = self.torch, self.awq
+        log("setup decode layer")
+        shapes = {}
+        for (N, K) in synth.DECODE_SHAPES:
+            lay = synth.decode_layer(N, K, 1)
+            qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), G)
+            shapes[(N, K)] = (qw, sc, zr, self.d(lay["x"]))
+        self.linears = list(synth.LLAMA7B_LAYER)
+        self.step_bytes = sum(gemv_bytes(1, N, K) for (_, N, K) in self.linears)
+        self.n_copies = max(2, int(np.ceil(1.2e9 / self.step_bytes)))
+        self.copies = []
+        for _ in range(self.n_copies):
+            layer = []
+            for (_, N, K) in self.linears:
+                qw, sc, zr, x = shapes[(N, K)]
+                y = torch.empty((1, N), dtype=torch.float16, device=self.dev)
+                layer.append((qw.clone(), sc.clone(), zr.clone(), x, y, N, K))
+            self.copies.append(layer)
+        torch.cuda.synchronize()
+
+    def decode_step(self, i):
+        for (qw, sc, zr, x, y, N, K) in self.copies[i % self.n_copies]:
+            self.awq.awq_gemm(x, qw, sc, zr, G, out=y)
+
+    def run_decode(self):
+        args = self.args
+        for i in range(max(args.warmup, 1)):
+            self.decode_step(i)
+        self.torch.cuda.synchronize()
+        # one graph per full rotation over the copies, one for the rest, so
+        # that exactly args.steps steps are timed
+        g_full = self.capture(self.decode_step, self.n_copies)
+        rem = args.steps % self.n_copies
+        g_rem = self.capture(self.decode_step, rem) if rem else None
+        n_full = args.steps // self.n_copies
+
+        def steps(_):
+            for _r in range(n_full):
+                g_full.replay()
+            if g_rem is not None:
+                g_rem.replay()
+
+        g_full.replay()
+        t = self.time(steps)
+        ms = t / args.steps * 1e3
+        value = self.step_bytes * args.steps / t / 1e9
+        log(f"decode layer: {ms * 1e3:.2f} us/step, {value:.0f} GB/s")
+        return value, ms
+
+    def run_gemv_shapes(self, shapes):
+        """Back-to-back launches of one shape over the rotated copies."""
+        out = {}
+        for (N, K) in shapes:
+            idx = [j for j, (_, n, k) in enumerate(self.linears) if (n, k) == (N, K)][0]
+            bufs = [self.copies[c][idx] for c in range(self.n_copies)]
+
+            def one(i, bufs=bufs):
+                qw, sc, zr, x, y, _, _ = bufs[i % len(bufs)]
+                self.awq.awq_gemm(x, qw, sc, zr, G, out=y)
+
+            reps = 8 * self.n_copies
+            g1 = self.capture(one, reps)
+            g1.replay()
+            t = self.time(lambda _: g1.replay(), 4) / (4 * reps)
+            b = gemv_bytes(1, N, K)
+            out[f"{N}x{K}"] = {"us": round(t * 1e6, 3), "GB/s": round(b / t / 1e9, 1), "bytes": b,
+                               "launches_timed": 4 * reps}
+            log(f"gemv {N}x{K}: {t * 1e6:.2f} us, {b / t / 1e9:.0f} GB/s")
+            del g1
+        return out
+
+    # ------------------------------------------------------------ prefill GEMM
+    def run_gemm(self):
+        torch, awq = self.torch, self.awq
+        log("setup prefill")
+        per_shape, tot_flop, tot_t = {}, 0.0, 0.0
+        for (N, K) in synth.PREFILL_SHAPES:
+            lay = synth.prefill_layer(N, K)
+            qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), G)
+            x = self.d(lay["x"])
+            y = torch.empty((synth.PREFILL_M, N), dtype=torch.float16, device=self.dev)
+
+            def g(i, x=x, qw=qw, sc=sc, zr=zr, y=y):
+                awq.awq_gemm(x, qw, sc, zr, G, out=y)
+
+            for i in range(5):
+                g(i)
+            reps = 50
+            t = self.time(g, reps) / reps
+            flop = 2.0 * synth.PREFILL_M * N * K
+            tot_flop += flop
+            tot_t += t
+            per_shape[f"{synth.PREFILL_M}x{N}x{K}"] = {"us": round(t * 1e6, 2),
+                                                       "TFLOP/s": round(flop / t / 1e12, 1)}
+            log(f"gemm M={synth.PREFILL_M} {N}x{K}: {t * 1e6:.1f} us, {flop / t / 1e12:.0f} TFLOP/s")
+        tflops = tot_flop / tot_t / 1e12
+        return {"M": synth.PREFILL_M, "TFLOP/s": round(tflops, 1),
+                "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": F16_MFMA_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tflops / F16_MFMA_PEAK_TFLOPS, 4)},
+                "per_shape": per_shape}
+
+    # ------------------------------------------------------------ quantize
+    def run_quantize(self):
+        N, K = 11008, 4096
+        w16 = self.d(synth.decode_layer(N, K, 0)["w"])
+        outs = self.awq.awq_quantize(w16, G)
+
+        def q(i):
+            self.awq.awq_quantize(w16, G, out=outs)
+
+        for i in range(5):
+            q(i)
+        tq = self.time(q, 50) / 50
+        gbs = quantize_bytes(N, K) / tq / 1e9
+        log(f"quantize {N}x{K}: {tq * 1e6:.1f} us, {gbs:.0f} GB/s")
+        return {"shape": f"{N}x{K}", "us": round(tq * 1e6, 2), "GB/s": round(gbs, 1),
+                "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+    # ------------------------------------------------------------ scale search
+    def run_search(self):
+        torch, awq = self.torch, self.awq
+        log("setup scale search")
+        lay = synth.search_layer()
+        ws, xs = self.d(lay["w"]), self.d(lay["x"])
+        del lay
+        nb = awq.scale_search_workspace_bytes(ws.shape[0], ws.shape[1], xs.shape[0], G, 20)
+        wsp = torch.empty(nb, dtype=torch.uint8, device=self.dev)
+        awq.awq_scale_search(ws, xs, G, workspace=wsp)   # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _, best, _ = awq.awq_scale_search(ws, xs, G, workspace=wsp)
+        ts = time.perf_counter() - t0
+        flop = 21 * 2.0 * xs.shape[0] * ws.shape[0] * ws.shape[1]
+        log(f"scale search: {ts * 1e3:.1f} ms, alpha* = {best / 20}")
+        return {"ms": round(ts * 1e3, 2), "best_alpha": best / 20, "TFLOP/s": round(flop / ts / 1e12, 1),
+                "frac_of_f16_peak": round(flop / ts / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
+                "workload": "W[11008,4096], X[65536,4096], 20 alphas, G=128 (21 GEMMs)"}
+
+    # ------------------------------------------------------------ HBM copy
+    def run_copy(self):
+        torch = self.torch
+        a = torch.empty(COPY_BYTES // 2, dtype=torch.float16, device=self.dev)
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        for _ in range(3):
+            b.copy_(a)
+        t = self.time(lambda _: b.copy_(a), 10) / 10
+        gbs = 2 * COPY_BYTES / t / 1e9
+        log(f"copy 1 GiB: {t * 1e6:.0f} us, {gbs:.0f} GB/s (read + write)")
+        return {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES, "us": round(t * 1e6, 1),
+                "GB/s": round(gbs, 1)}
+
+    # ------------------------------------------------------------ CPU oracle
+    def run_cpu_baseline(self):
+        import oracle
+
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:
+            blas_threads = 1
+        t_cpu, b_cpu, n = 0.0, 0, 0
+        cache = {}
+        t_start = time.perf_counter()
+        while time.perf_counter() - t_start < 12.0:
+            for (_, N, K) in self.linears:
+                if (N, K) not in cache:
+                    lay = synth.decode_layer(N, K, 1)
+                    cache[(N, K)] = (oracle.quantize(lay["w"], G), lay["x"])
+                (qw, sc, zr), x = cache[(N, K)]
+                t0 = time.perf_counter()
+                oracle.linear_ref(x, qw, sc, zr, G)
+                t_cpu += time.perf_counter() - t0
+                b_cpu += gemv_bytes(1, N, K)
+                n += 1
+        value = b_cpu / t_cpu / 1e9
+        log(f"cpu oracle: {value:.2f} GB/s over {n} products")
+        return {"value": round(value, 3), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+                "sample": f"{n} M=1 products over the 7 Llama-7B linear shapes, each the oracle's fp64 "
+                          f"dequantize (single-threaded NumPy) + fp64 matrix-vector product "
+                          f"({blas_threads} BLAS threads); {t_cpu:.1f} s of CPU work"}
+
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -76,185 +314,43 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true")
+    ap.add_argument("--only", choices=["decode", "gemv-roofline", "gemm", "quantize", "search", "copy"],
+                    help="run one section (for profiler runs); timings go to stderr")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; the library has no multi-GPU "
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the library has no multi-GPU "
                                    "path (--gpus must be 1)"}))
         sys.exit(2)
 
-    import torch
-    import weight_only_int4_quantize_amd as awq
+    b = Bench(args)
+    if args.only:
+        if args.only in ("decode", "gemv-roofline"):
+            b.setup_decode()
+            if args.only == "decode":
+                b.run_decode()
+            else:
+                b.run_gemv_shapes([ROOFLINE_SHAPE])
+        elif args.only == "gemm":
+            b.run_gemm()
+        elif args.only == "quantize":
+            b.run_quantize()
+        elif args.only == "search":
+            b.run_search()
+        else:
+            b.run_copy()
+        return
 
-    if not torch.cuda.is_available():
-        raise SystemExit("bench.py needs a GPU")
-    dev = "cuda:0"
-    timer = StreamTimer(torch)
+    b.setup_decode()
+    value, ms_per_step = b.run_decode()
+    per_shape = b.run_gemv_shapes(synth.DECODE_SHAPES)
+    roof = per_shape[f"{ROOFLINE_SHAPE[0]}x{ROOFLINE_SHAPE[1]}"]
+    copy = b.run_copy()
+    gemm = b.run_gemm()
+    quant = b.run_quantize()
+    search = None if args.no_search else b.run_search()
+    cpu = None if args.no_cpu_baseline else b.run_cpu_baseline()
 
-    def d(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    # ---------------------------------------------------------------- decode layer
-    log("setup decode layer")
-    shapes = {}
-    for (N, K) in synth.DECODE_SHAPES:
-        lay = synth.decode_layer(N, K, 1)
-        qw, sc, zr = awq.awq_quantize(d(lay["w"]), G)
-        shapes[(N, K)] = (qw, sc, zr, d(lay["x"]))
-    linears = [(name, N, K) for (name, N, K) in synth.LLAMA7B_LAYER]
-    step_bytes = sum(gemv_bytes(1, N, K) for (_, N, K) in linears)
-    n_copies = max(2, int(np.ceil(1.2e9 / step_bytes)))
-    copies = []
-    for c in range(n_copies):
-        layer = []
-        for (name, N, K) in linears:
-            qw, sc, zr, x = shapes[(N, K)]
-            layer.append((qw.clone(), sc.clone(), zr.clone(), x, torch.empty((1, N), dtype=torch.float16, device=dev),
-                          N, K))
-        copies.append(layer)
-    torch.cuda.synchronize()
-
-    def step(i):
-        for (qw, sc, zr, x, y, N, K) in copies[i % n_copies]:
-            awq.awq_gemm(x, qw, sc, zr, G, out=y)
-
-    for i in range(max(args.warmup, 1)):
-        step(i)
-    torch.cuda.synchronize()
-
-    def capture(fn, count):
-        """HIP graph of `count` calls fn(0..count-1); replays have no host
-        launch cost between kernels."""
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g, stream=side):
-                for i in range(count):
-                    fn(i)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        return g
-
-    # one graph per full rotation over the weight copies, one for the rest,
-    # so that exactly args.steps steps are timed
-    g_full = capture(step, n_copies)
-    rem = args.steps % n_copies
-    g_rem = capture(step, rem) if rem else None
-    n_full = args.steps // n_copies
-
-    def timed_steps(_):
-        for _r in range(n_full):
-            g_full.replay()
-        if g_rem is not None:
-            g_rem.replay()
-
-    g_full.replay()
-    t_steps = timer.time(timed_steps, 1)
-    ms_per_step = t_steps / args.steps * 1e3
-    value = step_bytes * args.steps / t_steps / 1e9
-    log(f"decode layer: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s")
-
-    # per-shape GEMV launch durations (graph of back-to-back launches over the
-    # rotated copies)
-    per_shape = {}
-    for (N, K) in synth.DECODE_SHAPES:
-        idx = [j for j, (_, n, k) in enumerate(linears) if (n, k) == (N, K)][0]
-        bufs = [copies[c][idx] for c in range(n_copies)]
-
-        def one(i, bufs=bufs):
-            qw, sc, zr, x, y, _, _ = bufs[i % len(bufs)]
-            awq.awq_gemm(x, qw, sc, zr, G, out=y)
-
-        reps = 8 * n_copies
-        g1 = capture(one, reps)
-        g1.replay()
-        t = timer.time(lambda _: g1.replay(), 4) / (4 * reps)
-        b = gemv_bytes(1, N, K)
-        per_shape[f"{N}x{K}"] = {"us": round(t * 1e6, 3), "GB/s": round(b / t / 1e9, 1), "bytes": b}
-        log(f"gemv {N}x{K}: {t * 1e6:.2f} us, {b / t / 1e9:.0f} GB/s")
-        del g1
-    big = per_shape[f"{11008}x{4096}"]
-
-    # ---------------------------------------------------------------- prefill GEMM
-    log("setup prefill")
-    gemm = {}
-    tot_flop, tot_t = 0.0, 0.0
-    for (N, K) in synth.PREFILL_SHAPES:
-        lay = synth.prefill_layer(N, K)
-        qw, sc, zr = awq.awq_quantize(d(lay["w"]), G)
-        x = d(lay["x"])
-        y = torch.empty((synth.PREFILL_M, N), dtype=torch.float16, device=dev)
-
-        def g(i, x=x, qw=qw, sc=sc, zr=zr, y=y):
-            awq.awq_gemm(x, qw, sc, zr, G, out=y)
-
-        for i in range(5):
-            g(i)
-        reps = 50
-        t = timer.time(g, reps) / reps
-        flop = 2.0 * synth.PREFILL_M * N * K
-        tot_flop += flop
-        tot_t += t
-        gemm[f"{synth.PREFILL_M}x{N}x{K}"] = {"us": round(t * 1e6, 2), "TFLOP/s": round(flop / t / 1e12, 1)}
-        log(f"gemm M={synth.PREFILL_M} {N}x{K}: {t * 1e6:.1f} us, {flop / t / 1e12:.0f} TFLOP/s")
-    gemm_tflops = tot_flop / tot_t / 1e12
-
-    # ---------------------------------------------------------------- quantize
-    N, K = 11008, 4096
-    w16 = d(synth.decode_layer(N, K, 0)["w"])
-    outs = awq.awq_quantize(w16, G)
-
-    def q(i):
-        awq.awq_quantize(w16, G, out=outs)
-
-    for i in range(5):
-        q(i)
-    tq = timer.time(q, 50) / 50
-    quant = {"shape": f"{N}x{K}", "us": round(tq * 1e6, 2),
-             "GB/s": round(quantize_bytes(N, K) / tq / 1e9, 1)}
-    log(f"quantize {N}x{K}: {tq * 1e6:.1f} us, {quant['GB/s']} GB/s")
-
-    # ---------------------------------------------------------------- scale search
-    search = None
-    if not args.no_search:
-        log("setup scale search")
-        lay = synth.search_layer()
-        ws, xs = d(lay["w"]), d(lay["x"])
-        del lay
-        nb = awq.scale_search_workspace_bytes(ws.shape[0], ws.shape[1], xs.shape[0], G, 20)
-        wsp = torch.empty(nb, dtype=torch.uint8, device=dev)
-        awq.awq_scale_search(ws, xs, G, workspace=wsp)   # warm-up
-        t0 = time.perf_counter()
-        losses, best, _ = awq.awq_scale_search(ws, xs, G, workspace=wsp)
-        ts = time.perf_counter() - t0
-        flop = 21 * 2.0 * xs.shape[0] * ws.shape[0] * ws.shape[1]
-        search = {"ms": round(ts * 1e3, 2), "best_alpha": best / 20, "TFLOP/s": round(flop / ts / 1e12, 1),
-                  "frac_of_f16_peak": round(flop / ts / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)}
-        log(f"scale search: {ts * 1e3:.1f} ms, alpha* = {best / 20}")
-
-    # ---------------------------------------------------------------- CPU oracle
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        cores = len(os.sched_getaffinity(0))
-        t_cpu, b_cpu, n = 0.0, 0, 0
-        lay_cache = {}
-        t_start = time.perf_counter()
-        while time.perf_counter() - t_start < 12.0:
-            for (name, N, K) in linears:
-                if (N, K) not in lay_cache:
-                    lay = synth.decode_layer(N, K, 1)
-                    lay_cache[(N, K)] = (oracle.quantize(lay["w"], G), lay["x"])
-                (qw, sc, zr), x = lay_cache[(N, K)]
-                t0 = time.perf_counter()
-                oracle.linear_ref(x, qw, sc, zr, G)
-                t_cpu += time.perf_counter() - t0
-                b_cpu += gemv_bytes(1, N, K)
-                n += 1
-        cpu = {"value": round(b_cpu / t_cpu / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-               "sample": f"{n} M=1 products over the 7 Llama-7B linear shapes (oracle dequantize + fp64 "
-                         f"matmul), {t_cpu:.1f} s"}
-
+    traffic, calib = measured_traffic()
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -269,17 +365,19 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": "llama7b_decoder_layer_decode_m1_int4_g128", "M": 1, "group_size": G,
-                   "linears": [f"{n}:{N}x{K}" for (n, N, K) in linears], "weight_copies": n_copies},
-        "roofline": {"bound": "hbm", "achieved": big["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(big["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemv 11008x4096 M=1", "bytes_per_launch": big["bytes"],
-                     "launch_us": big["us"]},
+                   "linears": [f"{n}:{N}x{K}" for (n, N, K) in b.linears], "weight_copies": b.n_copies,
+                   "step_bytes": b.step_bytes},
+        "roofline": {"bound": "hbm", "achieved": roof["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(roof["GB/s"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "bytes per launch (FETCH_SIZE x fetch_factor + WRITE_SIZE x write_factor)",
+                     "traffic_calibration": calib,
+                     "kernel": f"gemv M=1 {ROOFLINE_SHAPE[0]}x{ROOFLINE_SHAPE[1]} (gate/up projection)",
+                     "bytes_per_launch": roof["bytes"], "launch_us": roof["us"],
+                     "frac_of_copy_bandwidth": round(roof["GB/s"] / copy["GB/s"], 4)},
         "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "hbm_copy_1GiB": copy,
         "gemv_per_shape": per_shape,
-        "gemm": {"M": synth.PREFILL_M, "TFLOP/s": round(gemm_tflops, 1),
-                 "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": F16_MFMA_PEAK_TFLOPS,
-                              "unit": "TFLOP/s", "frac": round(gemm_tflops / F16_MFMA_PEAK_TFLOPS, 4)},
-                 "per_shape": gemm},
+        "gemm": gemm,
         "quantize": quant,
         "scale_search": search,
         "cpu_baseline": cpu,
