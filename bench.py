@@ -200,6 +200,9 @@ class Bench:
         torch, awq = self.torch, self.awq
         log("setup prefill")
         per_shape, tot_flop, tot_t = {}, 0.0, 0.0
+        # one workspace serves both shapes (stream-K split where it pays)
+        ws = awq.gemm_workspace(synth.PREFILL_M, max(n for n, _ in synth.PREFILL_SHAPES),
+                                max(k for _, k in synth.PREFILL_SHAPES), self.dev)
         for (N, K) in synth.PREFILL_SHAPES:
             lay = synth.prefill_layer(N, K)
             qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), G)
@@ -207,7 +210,7 @@ class Bench:
             y = torch.empty((synth.PREFILL_M, N), dtype=torch.float16, device=self.dev)
 
             def g(i, x=x, qw=qw, sc=sc, zr=zr, y=y):
-                awq.awq_gemm(x, qw, sc, zr, G, out=y)
+                awq.awq_gemm(x, qw, sc, zr, G, out=y, workspace=ws)
 
             for i in range(5):
                 g(i)

@@ -122,6 +122,35 @@ awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight,
                          void* y_f16, int path, void* stream);
 
 /*
+ * awq_gemm_ex - awq_gemm_path with a caller-owned device workspace, which
+ * lets the MFMA GEMM split the K loop of output tiles across thread blocks
+ * (a stream-K decomposition) when the tile count would leave the GPU's
+ * resident blocks partly idle, e.g. the M = 2048 prefill of a 4096-wide
+ * layer. Same operation, arguments and results as awq_gemm (rskf.cn §3.3
+ * GEMM kernel), up to fp32 summation order; the partial sums of a split tile
+ * are added in a fixed order, so results do not depend on scheduling.
+ *
+ *   workspace        device memory of at least
+ *                    awq_gemm_workspace_bytes(M, N, K) bytes, 256-byte
+ *                    aligned, owned by the caller. It must be zero-filled
+ *                    before its first use; every call leaves it ready for
+ *                    the next one (the tile counters in it are back at zero
+ *                    when the call's kernel ends), so later calls of any
+ *                    size that fits reuse it without clearing it again.
+ *                    Calls that may run concurrently must not share one
+ *                    workspace. NULL = no split (as awq_gemm_path).
+ *   workspace_bytes  its size; too small returns AWQ_ERR_WORKSPACE,
+ *                    misaligned AWQ_ERR_ALIGN (both before any work).
+ * The GEMV path (small M) never touches the workspace.
+ */
+size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+awq_status awq_gemm_ex(const void* x_f16, const uint32_t* qweight,
+                       const void* scales_f16, const void* zeros_f16,
+                       int64_t M, int64_t N, int64_t K, int group_size,
+                       void* y_f16, int path, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
  * awq_activation_absmean - m[k] = max(mean_t |x[t, k]|, 1e-8), the
  * per-input-channel activation statistic AWQ's scale is built from
  * (rskf.cn §2.1-2.2; "AWQ 模型量化技术", Per-channel Scaling 优化).

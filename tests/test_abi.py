@@ -85,6 +85,23 @@ def test_gemm_checks(L):
     assert L.awq_gemm(FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 64, FAKE + 1, None) == ALIGN
 
 
+def test_gemm_ex_workspace_checks(L):
+    need = L.awq_gemm_workspace_bytes(2048, 4096, 4096)
+    # two fp32 256x128 partial tiles per resident block, one counter per tile
+    assert need >= 2 * 256 * 128 * 4 + (2048 // 256) * (4096 // 128) * 4
+    assert L.awq_gemm_workspace_bytes(0, 4096, 4096) == 0
+    assert L.awq_gemm_workspace_bytes(2048, 4096, -1) == 0
+    assert L.awq_gemm_workspace_bytes(4096, 4096, 4096) > need        # more tiles, more counters
+    g = L.awq_gemm_ex
+    ws = 0x100000                                                      # 256-byte aligned fake address
+    assert g(FAKE, FAKE, FAKE, FAKE, 2048, 4096, 4096, 128, FAKE, 2, ws, need - 1, None) == WORKSPACE
+    assert g(FAKE, FAKE, FAKE, FAKE, 2048, 4096, 4096, 128, FAKE, 2, ws + 16, need, None) == ALIGN
+    assert g(FAKE, FAKE, FAKE, FAKE, 2048, 4096, 100, 128, FAKE, 2, ws, need, None) == SHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, 2048, 4096, 4096, 96, FAKE, 2, ws, need, None) == CONFIG
+    assert g(None, FAKE, FAKE, FAKE, 2048, 4096, 4096, 128, FAKE, 2, ws, need, None) == NULL
+    assert g(FAKE, FAKE, FAKE, FAKE, 0, 4096, 4096, 128, FAKE, 2, ws, 0, None) == OK   # empty: no work
+
+
 def test_absmean_checks(L):
     need = L.awq_activation_absmean_workspace_bytes(1000, 512)
     assert need >= 512 * 8

@@ -7,7 +7,8 @@ no CPU fallback.
 
 Entry points (same names as the C ABI in include/awq.h):
     awq_quantize(w, group_size=128, channel_scale=None)  -> qweight, scales, zeros
-    awq_gemm(x, qweight, scales, zeros, group_size=128, path=0) -> y
+    awq_gemm(x, qweight, scales, zeros, group_size=128, path=0, workspace=None) -> y
+        (awq_gemm_ex when a workspace from gemm_workspace(M, N, K) is given)
     awq_activation_absmean(x) -> m
     awq_scale_search(w, x, group_size=128, alphas=None) -> losses, best_index, best_scales
 """
@@ -63,6 +64,10 @@ def load() -> ctypes.CDLL:
     L.awq_gemm.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_vp]
     L.awq_gemm_path.restype = c_int
     L.awq_gemm_path.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_int, c_vp]
+    L.awq_gemm_workspace_bytes.restype = c_sz
+    L.awq_gemm_workspace_bytes.argtypes = [c_i64, c_i64, c_i64]
+    L.awq_gemm_ex.restype = c_int
+    L.awq_gemm_ex.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_int, c_vp, c_sz, c_vp]
     L.awq_activation_absmean_workspace_bytes.restype = c_sz
     L.awq_activation_absmean_workspace_bytes.argtypes = [c_i64, c_i64]
     L.awq_activation_absmean.restype = c_int
@@ -144,8 +149,25 @@ def awq_quantize(w, group_size: int = 128, channel_scale=None, out=None):
     return qweight, scales, zeros
 
 
-def awq_gemm(x, qweight, scales, zeros, group_size: int = 128, path: int = PATH_AUTO, out=None):
-    """y[M, N] = x[M, K] . dequant(Wq)^T in fp16 (fp32 accumulation)."""
+def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load().awq_gemm_workspace_bytes(M, N, K))
+
+
+def gemm_workspace(M: int, N: int, K: int, device=None):
+    """A zero-filled uint8 GPU tensor usable as awq_gemm_ex's workspace for
+    every GEMM with at most as many output tiles as [M, N]; each call leaves
+    it ready for the next, without clearing."""
+    torch = _torch()
+    nbytes = gemm_workspace_bytes(M, N, K)
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device or "cuda")
+
+
+def awq_gemm(x, qweight, scales, zeros, group_size: int = 128, path: int = PATH_AUTO, out=None,
+             workspace=None):
+    """y[M, N] = x[M, K] . dequant(Wq)^T in fp16 (fp32 accumulation).
+
+    With a workspace (see gemm_workspace) the call goes to awq_gemm_ex,
+    which may split output tiles' K loops across blocks (stream-K)."""
     torch = _torch()
     _need_gpu("x", x, torch.float16)
     _need_gpu("qweight", qweight, torch.int32)
@@ -164,9 +186,15 @@ def awq_gemm(x, qweight, scales, zeros, group_size: int = 128, path: int = PATH_
         _need_gpu("out", y, torch.float16)
         if tuple(y.shape) != (M, N):
             raise ValueError("out must be [M, N]")
-    st = load().awq_gemm_path(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), M, N, K, group_size,
-                              _ptr(y), int(path), _stream(x.device))
-    _check("awq_gemm", st)
+    if workspace is None:
+        st = load().awq_gemm_path(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), M, N, K, group_size,
+                                  _ptr(y), int(path), _stream(x.device))
+        _check("awq_gemm", st)
+    else:
+        _need_gpu("workspace", workspace, torch.uint8)
+        st = load().awq_gemm_ex(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), M, N, K, group_size,
+                                _ptr(y), int(path), _ptr(workspace), workspace.numel(), _stream(x.device))
+        _check("awq_gemm_ex", st)
     return y
 
 

@@ -101,9 +101,14 @@ awq_status awq_quantize(const void* w_f16, const float* channel_scale, int64_t N
                            as_stream(stream));
 }
 
-awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight, const void* scales_f16,
-                         const void* zeros_f16, int64_t M, int64_t N, int64_t K, int group_size,
-                         void* y_f16, int path, void* stream) {
+size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+    return gemm_workspace_bytes(M, N);
+}
+
+awq_status awq_gemm_ex(const void* x_f16, const uint32_t* qweight, const void* scales_f16,
+                       const void* zeros_f16, int64_t M, int64_t N, int64_t K, int group_size,
+                       void* y_f16, int path, void* workspace, size_t workspace_bytes, void* stream) {
     awq_status st = check_dims(N, K, group_size);
     if (st != AWQ_OK) return st;
     if (path < 0 || path > 2) return AWQ_ERR_CONFIG;
@@ -123,6 +128,10 @@ awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight, const void*
     if (path == 1 && !gemv_ok) return AWQ_ERR_CONFIG;
     const bool use_gemv = path == 1 || (path == 0 && gemv_ok && M <= 4);
     if (use_gemv) return launch_gemv(x, qweight, sc, zr, M, N, K, group_size, y, as_stream(stream));
+    if (workspace != nullptr) {
+        if (reinterpret_cast<uintptr_t>(workspace) & 255) return AWQ_ERR_ALIGN;
+        if (workspace_bytes < gemm_workspace_bytes(M, N)) return AWQ_ERR_WORKSPACE;
+    }
     GemmArgs a;
     a.a = x;
     a.qweight = qweight;
@@ -133,7 +142,14 @@ awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight, const void*
     a.N = N;
     a.K = K;
     a.y16 = y;
-    return launch_gemm(a, GemmB::kInt4, GemmOut::kF16, as_stream(stream));
+    return launch_gemm(a, GemmB::kInt4, GemmOut::kF16, as_stream(stream), workspace);
+}
+
+awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight, const void* scales_f16,
+                         const void* zeros_f16, int64_t M, int64_t N, int64_t K, int group_size,
+                         void* y_f16, int path, void* stream) {
+    return awq_gemm_ex(x_f16, qweight, scales_f16, zeros_f16, M, N, K, group_size, y_f16, path, nullptr, 0,
+                       stream);
 }
 
 awq_status awq_gemm(const void* x_f16, const uint32_t* qweight, const void* scales_f16,

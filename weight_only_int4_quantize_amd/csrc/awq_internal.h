@@ -60,7 +60,11 @@ struct GemmArgs {
     double* partials = nullptr;       // kLoss: one double per tile
 };
 int64_t gemm_tile_count(int64_t M, int64_t N);
-awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t stream);
+// Workspace of the stream-K launch (fp32 partial tiles + per-tile counters);
+// with workspace == nullptr launch_gemm runs one tile per block.
+size_t gemm_workspace_bytes(int64_t M, int64_t N);
+awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t stream,
+                       void* workspace = nullptr);
 
 // Scale-search helpers.
 size_t absmean_workspace_bytes(int64_t T, int64_t K);

@@ -33,6 +33,8 @@
 // column (l mod 32) of B, with k-slice 8 * (l / 32) .. +7 of the 16; the
 // accumulator element i of lane l is C[8 * (i / 4) + 4 * (l / 32) + i mod 4]
 // [l mod 32].
+#include <algorithm>
+
 #include "awq_internal.h"
 
 namespace awq {
@@ -151,8 +153,36 @@ __device__ inline int xcd_tile(int block, int tiles) {
     return x * q + min(x, r) + local;
 }
 
-template <int BM, int BN, GemmB BMODE, GemmOut OMODE>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int tiles_n) {
+// Stream-K bookkeeping. Work unit u = (tile t, K step k) = t * ipt + k, with
+// total = tiles * ipt < 2^31 units split evenly over `grid` blocks: block b
+// owns [start(b), start(b + 1)), start(b) = b * q + min(b, r) where
+// total = q * grid + r, i.e. the first r blocks take q + 1 units.
+struct StreamK {
+    float* partials = nullptr;   // [grid][2][BM * BN] fp32
+    int* counters = nullptr;     // [tiles], zero between launches
+    int total = 0;               // tiles * ipt
+    int ipt = 0;                 // K steps per tile
+    int grid = 0;
+    int q = 0, r = 0;            // total = q * grid + r, q >= 1
+};
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int sk_start(const StreamK& sk, int b) { return b * sk.q + min(b, sk.r); }
+// block whose range contains unit u
+__device__ __forceinline__ int sk_block_of(const StreamK& sk, int u) {
+    const int big = sk.r * (sk.q + 1);
+    return u < big ? u / (sk.q + 1) : sk.r + (u - big) / sk.q;
+}
+
+constexpr int kSc1 = 16;   // cache-policy bit sc1 of buffer loads/stores (device scope)
+
+// buffer descriptor over one BM x BN fp32 partial tile
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* p) {
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, 256 * 128 * 4, 0x00020000);
+}
+
+template <int BM, int BN, GemmB BMODE, GemmOut OMODE, bool STREAMK>
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int tiles_n, StreamK sk) {
     constexpr int WTM = BM / 2;                 // wave tile rows
     constexpr int WTN = BN / 2;                 // wave tile cols
     constexpr int TM = WTM / 32;                // 32x32 MFMA tiles per wave (M)
@@ -161,229 +191,392 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
     constexpr bool INT4 = BMODE == GemmB::kInt4;
     constexpr int B_WORDS = BN * BK / 8 / kThreads;       // packed words per thread per step
     constexpr int B_VECS = BN * BK / 8 / kThreads;        // fp16 B: uint4 per thread per step (int4: unused)
+    constexpr int ACC = TM * TN * 16;                     // accumulators per lane
     static_assert(TM >= 1 && TN >= 1 && A_VECS >= 1, "tile shape");
     static_assert(!INT4 || B_WORDS == 2, "int4 B staging: 2 words (16 codes) per thread");
     static_assert(INT4 || B_VECS >= 1, "fp16 B staging");
 
     __shared__ __attribute__((aligned(16))) half_t As[2][BM * LDK];
     __shared__ __attribute__((aligned(16))) half_t Bs[2][BN * LDK];
+    __shared__ int s_flag;
 
     const int M = static_cast<int>(args.M);
     const int N = static_cast<int>(args.N);
     const int K = static_cast<int>(args.K);
     const int G = args.group_size;
     const int ngroups = K / G;
-    const int tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int tm = (tile / tiles_n) * BM;
-    const int tn = (tile % tiles_n) * BN;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int wm = (wave >> 1) * WTM;
     const int wn = (wave & 1) * WTN;
-    const UnpackConsts uk = unpack_consts();
-
-    // ---- staging: rows past M / N read the last row (their outputs are
-    //      never stored), so every load is in bounds and unconditional ----
-    Stage<A_VECS, B_VECS> st;
-    const half_t* a_base = args.a + c8_of(tid) ;
-    int a_off[A_VECS];
-#pragma unroll
-    for (int i = 0; i < A_VECS; ++i) {
-        const int r = (tid + i * kThreads) / (BK / 8);
-        a_off[i] = min(tm + r, M - 1);
-    }
-    // int4 B: thread t stages row t / 2, codes 16 * (t % 2) .. +15 of the step
-    const int b_row = tid >> 1;
-    const int b_half = tid & 1;
-    const int64_t b_n = min(tn + b_row, N - 1);
-    const uint32_t* b_words = args.qweight + b_n * (K / 8) + b_half * 2;
-    const half_t* b_zeros = args.zeros + b_n * ngroups;
-    int b_off[B_VECS];
-#pragma unroll
-    for (int i = 0; i < B_VECS; ++i) b_off[i] = min(tn + (tid + i * kThreads) / (BK / 8), N - 1);
-
-    // scales of this lane's output columns (int4 mode)
     const int lcol = lane & 31;
-    const half_t* s_src[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) s_src[j] = args.scales + static_cast<int64_t>(min(tn + wn + j * 32 + lcol, N - 1)) * ngroups;
-    // scales travel as raw fp16 bits and are converted only when used, a
-    // group after their load, so no wait is forced on the loads in flight
-    const uint16_t* s_bits[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) s_bits[j] = reinterpret_cast<const uint16_t*>(s_src[j]);
-    auto to_scale = [](uint16_t bits) {
-        const float s = static_cast<float>(__builtin_bit_cast(half_t, bits));
-        return s == 0.f ? kTinyScale : s;
-    };
-
-    float16_t acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-    const int nk = K / BK;
-    const int steps_per_group = INT4 ? G / BK : nk + 1;
-    int g = 0;
-    float s_cur[TN];
-    uint16_t s_next[TN];
-    if constexpr (INT4) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            s_cur[j] = to_scale(s_bits[j][0]);
-            s_next[j] = s_bits[j][ngroups > 1 ? 1 : 0];
-        }
-    }
-
-    // Two register stages: the loads for step kt + 2 are issued while step kt
-    // computes, and land in LDS at the end of step kt + 1. Loads past the
-    // last step re-read it (in bounds, never stored), so nothing branches.
-    Stage<A_VECS, B_VECS> st1;
-    const int last_k0 = K - BK;
-    auto load = [&](Stage<A_VECS, B_VECS>& dst, int k0) {
-        load_stage<INT4>(dst, a_base, a_off, K, b_words, b_zeros, G, args.w + c8_of(tid), b_off, min(k0, last_k0));
-    };
-    load(st, 0);
-    load(st1, BK);
-    store_stage<INT4, BM, BN>(st, As[0], Bs[0], tid, b_row, b_half, uk);
-    __syncthreads();
-
     const int lrow = lane & 31;
     const int lchunk = lane >> 5;          // which 8-k half of a 16-k MFMA step
-    auto compute = [&](const half_t* as, const half_t* bs, int kt) {
-        if constexpr (INT4) {
-            if (kt > 0 && (kt % steps_per_group) == 0) {
-                // entering the next group: C' <- C' * s_g / s_{g+1}
-                ++g;
-                float r[TN];
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const float sn = to_scale(s_next[j]);
-                    r[j] = s_cur[j] / sn;
-                    s_cur[j] = sn;
-                }
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) acc[i][j][e] *= r[j];
-#pragma unroll
-                for (int j = 0; j < TN; ++j) s_next[j] = s_bits[j][min(g + 1, ngroups - 1)];
-            }
-        }
-        // raised priority while this wave feeds the matrix core, so the other
-        // block's wave on the SIMD does its memory work in the gaps
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            half8_t af[TM], bf[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const half8_t*>(&as[swz(wm + i * 32 + lrow, ks * 2 + lchunk)]);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                bf[j] = *reinterpret_cast<const half8_t*>(&bs[swz(wn + j * 32 + lrow, ks * 2 + lchunk)]);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-        __builtin_amdgcn_s_setprio(0);
-    };
+    const UnpackConsts uk = unpack_consts();
+    const int nk = K / BK;
+    const int steps_per_group = INT4 ? G / BK : nk + 1;
+    const int b_row = tid >> 1;            // int4 staging: row t / 2,
+    const int b_half = tid & 1;            //   codes 16 * (t % 2) .. +15 of the step
 
-    for (int kt = 0; kt < nk; kt += 2) {       // nk is even (K is a multiple of 64)
-        load(st, (kt + 2) * BK);
-        compute(As[0], Bs[0], kt);
-        store_stage<INT4, BM, BN>(st1, As[1], Bs[1], tid, b_row, b_half, uk);
-        __syncthreads();
-        load(st1, (kt + 3) * BK);
-        compute(As[1], Bs[1], kt + 1);
-        store_stage<INT4, BM, BN>(st, As[0], Bs[0], tid, b_row, b_half, uk);
-        __syncthreads();
-    }
+    float16_t acc[TM][TN];
 
-    // ---- epilogue ----
-    if constexpr (INT4) {
+    // K steps [kb, ke) of one tile into acc, in true (unscaled) units.
+    auto run_segment = [&](int tm, int tn, int kb, int ke) {
+        // ---- staging: rows past M / N read the last row (their outputs
+        //      are never stored), so every load is in bounds ----
+        Stage<A_VECS, B_VECS> st, st1;
+        const half_t* a_base = args.a + c8_of(tid);
+        int a_off[A_VECS];
+#pragma unroll
+        for (int i = 0; i < A_VECS; ++i) a_off[i] = min(tm + (tid + i * kThreads) / (BK / 8), M - 1);
+        const int64_t b_n = min(tn + b_row, N - 1);
+        const uint32_t* b_words = args.qweight + b_n * (K / 8) + b_half * 2;
+        const half_t* b_zeros = args.zeros + b_n * ngroups;
+        int b_off[B_VECS];
+#pragma unroll
+        for (int i = 0; i < B_VECS; ++i) b_off[i] = min(tn + (tid + i * kThreads) / (BK / 8), N - 1);
+
+        // scales of this lane's output columns travel as raw fp16 bits and
+        // are converted only when used, a group after their load, so no wait
+        // is forced on the loads in flight
+        const uint16_t* s_bits[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            s_bits[j] = reinterpret_cast<const uint16_t*>(args.scales) +
+                        static_cast<int64_t>(min(tn + wn + j * 32 + lcol, N - 1)) * ngroups;
+        auto to_scale = [](uint16_t bits) {
+            const float v = static_cast<float>(__builtin_bit_cast(half_t, bits));
+            return v == 0.f ? kTinyScale : v;
+        };
+
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[i][j][e] *= s_cur[j];
-    }
-    const int lrow4 = (lane >> 5) * 4;
-    float sq = 0.f;
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+        int g = INT4 ? (kb * BK) / G : 0;
+        float s_cur[TN];
+        uint16_t s_next[TN];
+        if constexpr (INT4) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = tn + wn + j * 32 + lcol;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = tm + wm + i * 32 + (e >> 2) * 8 + lrow4 + (e & 3);
-                if (m < M && n < N) {
-                    const int64_t off = static_cast<int64_t>(m) * N + n;
-                    const float v = acc[i][j][e];
-                    if constexpr (OMODE == GemmOut::kF16) {
-                        args.y16[off] = static_cast<half_t>(v);
-                    } else if constexpr (OMODE == GemmOut::kF32) {
-                        args.y32[off] = v;
-                    } else {
-                        const float d = v - args.yref[off];
-                        sq += d * d;
-                    }
-                }
+            for (int j = 0; j < TN; ++j) {
+                s_cur[j] = to_scale(s_bits[j][g]);
+                s_next[j] = s_bits[j][min(g + 1, ngroups - 1)];
             }
         }
-    }
-    if constexpr (OMODE == GemmOut::kLoss) {
-        __shared__ double red[kThreads / kWave];
-        double v = static_cast<double>(sq);
+
+        // Two register stages: the loads for step kt + 2 are issued while
+        // step kt computes and land in LDS at the end of step kt + 1. Loads
+        // past the segment re-read its last step (in bounds, never used).
+        const int last_k0 = (ke - 1) * BK;
+        auto load = [&](Stage<A_VECS, B_VECS>& dst, int k0) {
+            load_stage<INT4>(dst, a_base, a_off, K, b_words, b_zeros, G, args.w + c8_of(tid), b_off,
+                             min(k0, last_k0));
+        };
+        auto compute = [&](const half_t* as, const half_t* bs, int kt) {
+            if constexpr (INT4) {
+                if (kt > kb && ((kt * BK) % G) == 0) {
+                    // entering the next group: C' <- C' * s_g / s_{g+1}
+                    ++g;
+                    float r[TN];
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-        if (lane == 0) red[wave] = v;
+                    for (int j = 0; j < TN; ++j) {
+                        const float sn = to_scale(s_next[j]);
+                        r[j] = s_cur[j] / sn;
+                        s_cur[j] = sn;
+                    }
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) acc[i][j][e] *= r[j];
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) s_next[j] = s_bits[j][min(g + 1, ngroups - 1)];
+                }
+            }
+            // raised priority while this wave feeds the matrix core, so the
+            // other block's wave on the SIMD does its memory work in the gaps
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                half8_t af[TM], bf[TN];
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    af[i] = *reinterpret_cast<const half8_t*>(&as[swz(wm + i * 32 + lrow, ks * 2 + lchunk)]);
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    bf[j] = *reinterpret_cast<const half8_t*>(&bs[swz(wn + j * 32 + lrow, ks * 2 + lchunk)]);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            }
+            __builtin_amdgcn_s_setprio(0);
+        };
+
+        load(st, kb * BK);
+        load(st1, (kb + 1) * BK);
+        store_stage<INT4, BM, BN>(st, As[0], Bs[0], tid, b_row, b_half, uk);
         __syncthreads();
-        if (tid == 0) {
-            double t = 0.0;
-            for (int w = 0; w < kThreads / kWave; ++w) t += red[w];
-            args.partials[tile] = t;
+        for (int kt = kb; kt < ke; kt += 2) {
+            load(st, (kt + 2) * BK);
+            compute(As[0], Bs[0], kt);
+            store_stage<INT4, BM, BN>(st1, As[1], Bs[1], tid, b_row, b_half, uk);
+            __syncthreads();
+            if (kt + 1 < ke) {
+                load(st1, (kt + 3) * BK);
+                compute(As[1], Bs[1], kt + 1);
+                store_stage<INT4, BM, BN>(st, As[0], Bs[0], tid, b_row, b_half, uk);
+                __syncthreads();
+            }
+        }
+        if constexpr (INT4) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[i][j][e] *= s_cur[j];
+        }
+    };
+
+    // ---- epilogue ----
+    // accumulator element e of MFMA tile (i, j) is output (row, col) =
+    // (tm + wm + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, tn + wn + 32 j + lane % 32)
+    const int lrow4 = (lane >> 5) * 4;
+    auto emit = [&](int tm, int tn, int i, int j, int e, float v, float& sq) {
+        const int n = tn + wn + j * 32 + lcol;
+        const int m = tm + wm + i * 32 + (e >> 2) * 8 + lrow4 + (e & 3);
+        if (m < M && n < N) {
+            const int64_t off = static_cast<int64_t>(m) * N + n;
+            if constexpr (OMODE == GemmOut::kF16) {
+                args.y16[off] = static_cast<half_t>(v);
+            } else if constexpr (OMODE == GemmOut::kF32) {
+                args.y32[off] = v;
+            } else {
+                const float d = v - args.yref[off];
+                sq += d * d;
+            }
+        }
+    };
+    auto finish_loss = [&](int tile, float sq) {
+        if constexpr (OMODE == GemmOut::kLoss) {
+            __shared__ double red[kThreads / kWave];
+            double v = static_cast<double>(sq);
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+            if (lane == 0) red[wave] = v;
+            __syncthreads();
+            if (tid == 0) {
+                double t = 0.0;
+                for (int w = 0; w < kThreads / kWave; ++w) t += red[w];
+                args.partials[tile] = t;
+            }
+            __syncthreads();
+        }
+    };
+    auto finish_tile = [&](int tile, int tm, int tn) {
+        float sq = 0.f;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) emit(tm, tn, i, j, e, acc[i][j][e], sq);
+        finish_loss(tile, sq);
+    };
+
+    if constexpr (!STREAMK) {
+        const int tile = xcd_tile(blockIdx.x, gridDim.x);
+        const int tm = (tile / tiles_n) * BM;
+        const int tn = (tile % tiles_n) * BN;
+        run_segment(tm, tn, 0, nk);
+        finish_tile(tile, tm, tn);
+    } else {
+        // consecutive ranges (which share tiles) go to the same XCD
+        const int b = uniform(xcd_tile(blockIdx.x, gridDim.x));
+        const int u1 = uniform(sk_start(sk, b + 1));
+        int u = uniform(sk_start(sk, b));
+        while (u < u1) {
+            const int tile = uniform(u / sk.ipt);
+            const int kb = uniform(u - tile * sk.ipt);
+            const int ke = uniform(min(sk.ipt, kb + (u1 - u)));
+            const int tm = (tile / tiles_n) * BM;
+            const int tn = (tile % tiles_n) * BN;
+            run_segment(tm, tn, kb, ke);
+            u += ke - kb;
+            if (kb == 0 && ke == sk.ipt) {
+                finish_tile(tile, tm, tn);
+                continue;
+            }
+            // Partial tile: park the sums, count in; the last of the tile's
+            // blocks to arrive adds every part in segment order (so the
+            // result does not depend on arrival order), finishes the tile and
+            // resets its counter. Nobody waits on anybody.
+            const int u_first = tile * sk.ipt;
+            const int b_first = uniform(sk_block_of(sk, u_first));
+            const int b_last = uniform(sk_block_of(sk, u_first + sk.ipt - 1));
+            // a block holds at most two partial tiles: the one it starts in
+            // (slot 0) and the one it ends in (slot 1)
+            auto slot_of = [&](int bb) {
+                const int slot = uniform(bb * 2 + (sk_start(sk, bb) / sk.ipt == tile ? 0 : 1));
+                return sk.partials + static_cast<int64_t>(slot) * (BM * BN);
+            };
+            {
+                // chunk-major layout [(i, j, e / 4)][thread][4]: one coalesced
+                // 1 KB row per wave and chunk, addressed by a scalar offset
+                const auto rs = partial_rsrc(slot_of(b));
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                                acc[i][j][4 * q + 3]};
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, tid * 16,
+                                                                   ((i * TN + j) * 4 + q) * kThreads * 16, kSc1);
+                        }
+            }
+            // The parts are written and read with the sc1 (device-coherent)
+            // cache policy, the form this target gives device-scope atomic
+            // stores and loads, so they bypass the per-XCD L2s instead of
+            // needing a device-wide L2 write-back/invalidate (a device fence),
+            // which would also flush every other block's cached tiles. All
+            // stores complete (vmcnt 0) before the counter is bumped, and the
+            // finisher issues its loads only after reading the count.
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0)
+                s_flag = __hip_atomic_fetch_add(&sk.counters[tile], 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT) == b_last - b_first;
+            __syncthreads();
+            if (!s_flag) continue;
+            // Every part, this block's own included, is read back and summed
+            // in segment order, eight float4 chunks (32 outputs) at a time,
+            // each chunk's four outputs written as soon as they are complete.
+            {
+                constexpr int kChunks = TM * TN * 4;
+                constexpr int kBatch = 8;
+                float sq = 0.f;
+#pragma unroll
+                for (int c0 = 0; c0 < kChunks; c0 += kBatch) {
+                    float4_t sum[kBatch];
+#pragma unroll
+                    for (int c = 0; c < kBatch; ++c) sum[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+                    for (int bb = b_first; bb <= b_last; ++bb) {
+                        const auto rs = partial_rsrc(slot_of(bb));
+                        float4_t v[kBatch];
+#pragma unroll
+                        for (int c = 0; c < kBatch; ++c)
+                            v[c] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                    rs, tid * 16, (c0 + c) * kThreads * 16, kSc1));
+#pragma unroll
+                        for (int c = 0; c < kBatch; ++c) sum[c] += v[c];
+                    }
+#pragma unroll
+                    for (int c = 0; c < kBatch; ++c) {
+                        const int ij = (c0 + c) / 4, q = (c0 + c) % 4;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) emit(tm, tn, ij / TN, ij % TN, 4 * q + r, sum[c][r], sq);
+                    }
+                }
+                finish_loss(tile, sq);
+            }
+            if (tid == 0) __hip_atomic_store(&sk.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+    (void)ACC;
 }
 
 constexpr int kBM = 256;
 constexpr int kBN = 128;
+constexpr int kBlocksPerCu = 2;
+
+int cu_count() {
+    static int cached = -1;
+    if (cached < 0) {
+        int dev = 0, v = 256;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            v = 256;
+        cached = v;
+    }
+    return cached;
+}
+
+constexpr int kMaxSplit = 4;        // segments per tile at most
+constexpr int kMinSteps = 8;        // K steps per block at least
+
+int64_t resident_slots() { return static_cast<int64_t>(kBlocksPerCu) * cu_count(); }
+
+// Stream-K pays off when there are fewer tiles than resident block slots:
+// one tile per block would leave CUs idle or at one block each. With more
+// tiles, the last round's blocks run one per CU at close to the per-CU rate
+// of two, and splitting costs more in partial traffic than it recovers.
+bool use_stream_k(int64_t tiles, int64_t K) {
+    if (tiles >= resident_slots()) return false;
+    return tiles * (K / BK) < (int64_t{1} << 31);
+}
+
+int stream_k_grid(int64_t tiles, int64_t K) {
+    const int64_t total = tiles * (K / BK);
+    int64_t g = std::min(resident_slots(), tiles * kMaxSplit);
+    g = std::min(g, std::max<int64_t>(1, total / kMinSteps));
+    return static_cast<int>(g);
+}
+
+// two fp32 partial tiles per resident block
+size_t partials_bytes() {
+    return round_up(static_cast<size_t>(resident_slots()) * 2 * kBM * kBN * sizeof(float), 256);
+}
 
 template <GemmB BMODE, GemmOut OMODE>
-void launch_cfg(const GemmArgs& args, hipStream_t stream) {
+void launch_cfg(const GemmArgs& args, void* workspace, hipStream_t stream) {
     const int64_t tiles_n = ceil_div(args.N, kBN);
     const int64_t tiles = ceil_div(args.M, kBM) * tiles_n;
-    hipLaunchKernelGGL((gemm_kernel<kBM, kBN, BMODE, OMODE>), dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0,
-                       stream, args, static_cast<int>(tiles_n));
+    StreamK sk;
+    if (workspace != nullptr && use_stream_k(tiles, args.K)) {
+        sk.ipt = static_cast<int>(args.K / BK);
+        sk.total = static_cast<int>(tiles * sk.ipt);
+        sk.grid = stream_k_grid(tiles, args.K);
+        sk.q = sk.total / sk.grid;
+        sk.r = sk.total % sk.grid;
+        sk.partials = static_cast<float*>(workspace);
+        sk.counters = reinterpret_cast<int*>(static_cast<char*>(workspace) + partials_bytes());
+        hipLaunchKernelGGL((gemm_kernel<kBM, kBN, BMODE, OMODE, true>), dim3(static_cast<unsigned>(sk.grid)),
+                           dim3(kThreads), 0, stream, args, static_cast<int>(tiles_n), sk);
+        return;
+    }
+    hipLaunchKernelGGL((gemm_kernel<kBM, kBN, BMODE, OMODE, false>), dim3(static_cast<unsigned>(tiles)),
+                       dim3(kThreads), 0, stream, args, static_cast<int>(tiles_n), sk);
 }
 
 }  // namespace
 
 int64_t gemm_tile_count(int64_t M, int64_t N) { return ceil_div(M, kBM) * ceil_div(N, kBN); }
 
-awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t stream) {
+size_t gemm_workspace_bytes(int64_t M, int64_t N) {
+    return partials_bytes() + round_up(static_cast<size_t>(gemm_tile_count(M, N)) * sizeof(int), 256);
+}
+
+awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t stream, void* workspace) {
     if (args.M == 0 || args.N == 0) return AWQ_OK;
     if (b == GemmB::kInt4) {
         switch (out) {
-            case GemmOut::kF16: launch_cfg<GemmB::kInt4, GemmOut::kF16>(args, stream); break;
-            case GemmOut::kF32: launch_cfg<GemmB::kInt4, GemmOut::kF32>(args, stream); break;
-            case GemmOut::kLoss: launch_cfg<GemmB::kInt4, GemmOut::kLoss>(args, stream); break;
+            case GemmOut::kF16: launch_cfg<GemmB::kInt4, GemmOut::kF16>(args, workspace, stream); break;
+            case GemmOut::kF32: launch_cfg<GemmB::kInt4, GemmOut::kF32>(args, workspace, stream); break;
+            case GemmOut::kLoss: launch_cfg<GemmB::kInt4, GemmOut::kLoss>(args, workspace, stream); break;
         }
     } else {
         switch (out) {
-            case GemmOut::kF16: launch_cfg<GemmB::kF16, GemmOut::kF16>(args, stream); break;
-            case GemmOut::kF32: launch_cfg<GemmB::kF16, GemmOut::kF32>(args, stream); break;
+            case GemmOut::kF16: launch_cfg<GemmB::kF16, GemmOut::kF16>(args, workspace, stream); break;
+            case GemmOut::kF32: launch_cfg<GemmB::kF16, GemmOut::kF32>(args, workspace, stream); break;
             case GemmOut::kLoss: return AWQ_ERR_CONFIG;
         }
     }
