@@ -12,6 +12,9 @@ step's algorithmic bytes over its time.
 The same run also times, each in its own section:
   * the roofline kernel: the gate/up GEMV (11008x4096, the largest launch of
     the step) back to back over the rotated copies;
+  * the same layer with fused q/k/v (12288x4096) and gate/up (22016x4096)
+    projections, four launches per step;
+  * the per-node floor of a graph of tiny kernels (launch cost context);
   * the prefill GEMM, x[2048, K] times the two MLP shapes;
   * the quantize kernel on 11008x4096;
   * one full scale search (W[11008, 4096], X[65536, 4096], 20 alphas);
@@ -173,6 +176,69 @@ class Bench:
         log(f"decode layer: {ms * 1e3:.2f} us/step, {value:.0f} GB/s")
         return value, ms
 
+    def run_decode_fused(self):
+        """The decoder layer with fused q/k/v and gate/up projections: four
+        launches per step instead of seven, same weight bytes."""
+        torch, awq, args = self.torch, self.awq, self.args
+        log("setup fused decode layer")
+        layer = list(synth.LLAMA7B_LAYER_FUSED)
+        step_bytes = sum(gemv_bytes(1, N, K) for (_, N, K) in layer)
+        n_copies = max(2, int(np.ceil(1.2e9 / step_bytes)))
+        base = []
+        for (_, N, K) in layer:
+            lay = synth.decode_layer(N, K, 1)
+            qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), G)
+            base.append((qw, sc, zr, self.d(lay["x"]), N, K))
+        copies = []
+        for _ in range(n_copies):
+            copies.append([(qw.clone(), sc.clone(), zr.clone(), x,
+                            torch.empty((1, N), dtype=torch.float16, device=self.dev), N, K)
+                           for (qw, sc, zr, x, N, K) in base])
+        torch.cuda.synchronize()
+
+        def step(i):
+            for (qw, sc, zr, x, y, N, K) in copies[i % n_copies]:
+                awq.awq_gemm(x, qw, sc, zr, G, out=y)
+
+        for i in range(max(args.warmup, 1)):
+            step(i)
+        g = self.capture(step, n_copies)
+        g.replay()
+        reps = max(1, args.steps // n_copies)
+        t = self.time(lambda _: [g.replay() for _r in range(reps)])
+        n = reps * n_copies
+        us = t / n * 1e6
+        gbs = step_bytes * n / t / 1e9
+        log(f"fused decode layer: {us:.2f} us/step, {gbs:.0f} GB/s")
+        per_launch = {}
+        for j, (name, N, K) in enumerate(layer):
+            def one(i, j=j):
+                qw, sc, zr, x, y, _, _ = copies[i % n_copies][j]
+                awq.awq_gemm(x, qw, sc, zr, G, out=y)
+            gj = self.capture(one, 4 * n_copies)
+            gj.replay()
+            tj = self.time(lambda _: gj.replay()) / (4 * n_copies)
+            per_launch[name] = {"shape": f"{N}x{K}", "us": round(tj * 1e6, 2),
+                                "GB/s": round(gemv_bytes(1, N, K) / tj / 1e9, 1)}
+        del copies
+        torch.cuda.synchronize()
+        return {"workload": "llama7b_decoder_layer_fused_qkv_gateup_m1_int4_g128",
+                "linears": [f"{n}:{N}x{K}" for (n, N, K) in layer], "step_bytes": step_bytes,
+                "weight_copies": n_copies, "us_per_step": round(us, 2), "GB/s": round(gbs, 1),
+                "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "per_launch": per_launch}
+
+    def run_launch_floor(self):
+        """Per-node cost of a HIP graph of tiny kernels (a one-element fill):
+        the floor under every back-to-back launch timed here."""
+        torch = self.torch
+        t1 = torch.empty(1, dtype=torch.float32, device=self.dev)
+        n = 400
+        g = self.capture(lambda i: t1.fill_(float(i)), n)
+        g.replay()
+        us = min(self.time(lambda _: g.replay()) for _ in range(3)) / n * 1e6
+        log(f"graph launch floor: {us:.2f} us per node")
+        return round(us, 3)
+
     def run_gemv_shapes(self, shapes):
         """Back-to-back launches of one shape over the rotated copies."""
         out = {}
@@ -317,7 +383,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true")
-    ap.add_argument("--only", choices=["decode", "gemv-roofline", "gemm", "quantize", "search", "copy"],
+    ap.add_argument("--only", choices=["decode", "decode-fused", "gemv-roofline", "gemm", "quantize", "search",
+                                       "copy"],
                     help="run one section (for profiler runs); timings go to stderr")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -333,6 +400,8 @@ def main():
                 b.run_decode()
             else:
                 b.run_gemv_shapes([ROOFLINE_SHAPE])
+        elif args.only == "decode-fused":
+            b.run_decode_fused()
         elif args.only == "gemm":
             b.run_gemm()
         elif args.only == "quantize":
@@ -347,6 +416,9 @@ def main():
     value, ms_per_step = b.run_decode()
     per_shape = b.run_gemv_shapes(synth.DECODE_SHAPES)
     roof = per_shape[f"{ROOFLINE_SHAPE[0]}x{ROOFLINE_SHAPE[1]}"]
+    del b.copies
+    fused = b.run_decode_fused()
+    floor_us = b.run_launch_floor()
     copy = b.run_copy()
     gemm = b.run_gemm()
     quant = b.run_quantize()
@@ -376,10 +448,12 @@ def main():
                      "traffic_calibration": calib,
                      "kernel": f"gemv M=1 {ROOFLINE_SHAPE[0]}x{ROOFLINE_SHAPE[1]} (gate/up projection)",
                      "bytes_per_launch": roof["bytes"], "launch_us": roof["us"],
-                     "frac_of_copy_bandwidth": round(roof["GB/s"] / copy["GB/s"], 4)},
+                     "frac_of_copy_bandwidth": round(roof["GB/s"] / copy["GB/s"], 4),
+                     "graph_launch_floor_us": floor_us},
         "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "hbm_copy_1GiB": copy,
         "gemv_per_shape": per_shape,
+        "decode_fused": fused,
         "gemm": gemm,
         "quantize": quant,
         "scale_search": search,

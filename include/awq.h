@@ -102,9 +102,10 @@ awq_status awq_quantize(const void* w_f16, const float* channel_scale,
  *   M, N, K      M, N >= 0; K > 0, K % group_size == 0
  *   group_size   64 or 128
  *   y_f16        device, fp16 [M, N] (output; must not alias the inputs)
- * M == 0 or N == 0 returns AWQ_OK without work. Small M (decode) runs a
- * bandwidth-bound GEMV; larger M runs an MFMA GEMM. Results do not depend on
- * run-to-run scheduling.
+ * M == 0 or N == 0 returns AWQ_OK without work. M <= 4 (decode) runs a
+ * bandwidth-bound GEMV, 4 < M <= 64 (a batch of decode tokens) a skinny
+ * MFMA kernel that streams the packed weights straight into registers, and
+ * larger M the MFMA GEMM. Results do not depend on run-to-run scheduling.
  */
 awq_status awq_gemm(const void* x_f16, const uint32_t* qweight,
                     const void* scales_f16, const void* zeros_f16,
@@ -114,7 +115,9 @@ awq_status awq_gemm(const void* x_f16, const uint32_t* qweight,
 /*
  * awq_gemm_path - awq_gemm with the kernel chosen by the caller:
  * path 0 = automatic (as awq_gemm), 1 = GEMV (requires M <= 8),
- * 2 = MFMA GEMM. Any other path returns AWQ_ERR_CONFIG.
+ * 2 = MFMA GEMM, 3 = skinny MFMA kernel (requires M <= 64 and a packed
+ * matrix under 4 GiB). Any other path, or a path whose requirement fails,
+ * returns AWQ_ERR_CONFIG.
  */
 awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight,
                          const void* scales_f16, const void* zeros_f16,
@@ -123,12 +126,14 @@ awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight,
 
 /*
  * awq_gemm_ex - awq_gemm_path with a caller-owned device workspace, which
- * lets the MFMA GEMM split the K loop of output tiles across thread blocks
- * (a stream-K decomposition) when the tile count would leave the GPU's
- * resident blocks partly idle, e.g. the M = 2048 prefill of a 4096-wide
- * layer. Same operation, arguments and results as awq_gemm (rskf.cn §3.3
- * GEMM kernel), up to fp32 summation order; the partial sums of a split tile
- * are added in a fixed order, so results do not depend on scheduling.
+ * lets the MFMA kernels split the K loop of output tiles across thread
+ * blocks when the tile count would leave the GPU's resident blocks partly
+ * idle: a stream-K decomposition for the GEMM (e.g. the M = 2048 prefill of
+ * a 4096-wide layer) and fixed K splits for the skinny kernel (e.g. M = 16
+ * on a 4096-wide layer, 32 column tiles). Same operation, arguments and
+ * results as awq_gemm (rskf.cn §3.3 GEMM kernel), up to fp32 summation
+ * order; the partial sums of a split tile are added in a fixed order, so
+ * results do not depend on scheduling.
  *
  *   workspace        device memory of at least
  *                    awq_gemm_workspace_bytes(M, N, K) bytes, 256-byte

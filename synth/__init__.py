@@ -32,6 +32,15 @@ LLAMA7B_LAYER = (
 
 # Distinct shapes of the decode sweep.
 DECODE_SHAPES = ((4096, 4096), (11008, 4096), (4096, 11008))
+# The same layer with its projections fused as a model loaded with fused
+# layers runs them: q/k/v share x (N = 3 * 4096) and so do gate/up
+# (N = 2 * 11008), so each group is one product.
+LLAMA7B_LAYER_FUSED = (
+    ("qkv_proj", 12288, 4096),
+    ("o_proj", 4096, 4096),
+    ("gate_up_proj", 22016, 4096),
+    ("down_proj", 4096, 11008),
+)
 DECODE_M = (1, 4, 16)
 # Prefill products: x[2048, K] . W[N, K]^T.
 PREFILL_SHAPES = ((11008, 4096), (4096, 11008))

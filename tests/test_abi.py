@@ -74,7 +74,8 @@ def test_gemm_checks(L):
     assert g(FAKE, FAKE, FAKE, FAKE, 1, 16, 100, 64, FAKE, 0, None) == SHAPE
     assert g(FAKE, FAKE, FAKE, FAKE, -1, 16, 128, 64, FAKE, 0, None) == SHAPE
     assert g(FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 96, FAKE, 0, None) == CONFIG
-    assert g(FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 64, FAKE, 3, None) == CONFIG
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 64, FAKE, 4, None) == CONFIG
+    assert g(FAKE, FAKE, FAKE, FAKE, 65, 16, 128, 64, FAKE, 3, None) == CONFIG  # skinny is M <= 64
     assert g(FAKE, FAKE, FAKE, FAKE, 9, 16, 128, 64, FAKE, 1, None) == CONFIG   # GEMV is M <= 8
     assert g(FAKE, FAKE, FAKE, FAKE, 0, 16, 128, 64, FAKE, 0, None) == OK       # empty M
     assert g(FAKE, FAKE, FAKE, FAKE, 4, 0, 128, 64, FAKE, 0, None) == OK        # empty N
@@ -91,7 +92,9 @@ def test_gemm_ex_workspace_checks(L):
     assert need >= 2 * 256 * 128 * 4 + (2048 // 256) * (4096 // 128) * 4
     assert L.awq_gemm_workspace_bytes(0, 4096, 4096) == 0
     assert L.awq_gemm_workspace_bytes(2048, 4096, -1) == 0
-    assert L.awq_gemm_workspace_bytes(4096, 4096, 4096) > need        # more tiles, more counters
+    assert L.awq_gemm_workspace_bytes(4096, 4096, 4096) >= need
+    # skinny K splits: 16 rows x 128 columns of fp32 per split and column tile
+    assert L.awq_gemm_workspace_bytes(16, 4096, 4096) >= 32 * 16 * 16 * 128 * 4
     g = L.awq_gemm_ex
     ws = 0x100000                                                      # 256-byte aligned fake address
     assert g(FAKE, FAKE, FAKE, FAKE, 2048, 4096, 4096, 128, FAKE, 2, ws, need - 1, None) == WORKSPACE

@@ -1,5 +1,6 @@
 // C ABI of the library (declared in include/awq.h): argument checks on the
 // host, then kernels enqueued on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <vector>
 
@@ -103,7 +104,7 @@ awq_status awq_quantize(const void* w_f16, const float* channel_scale, int64_t N
 
 size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
-    return gemm_workspace_bytes(M, N);
+    return std::max(gemm_workspace_bytes(M, N), skinny_workspace_bytes(M, N, K));
 }
 
 awq_status awq_gemm_ex(const void* x_f16, const uint32_t* qweight, const void* scales_f16,
@@ -111,7 +112,7 @@ awq_status awq_gemm_ex(const void* x_f16, const uint32_t* qweight, const void* s
                        void* y_f16, int path, void* workspace, size_t workspace_bytes, void* stream) {
     awq_status st = check_dims(N, K, group_size);
     if (st != AWQ_OK) return st;
-    if (path < 0 || path > 2) return AWQ_ERR_CONFIG;
+    if (path < 0 || path > 3) return AWQ_ERR_CONFIG;
     if (M < 0 || M > kMaxDim) return AWQ_ERR_SHAPE;
     // The MFMA kernel indexes with 32-bit row/column numbers and 64-bit offsets.
     if (M > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return AWQ_ERR_SHAPE;
@@ -125,13 +126,19 @@ awq_status awq_gemm_ex(const void* x_f16, const uint32_t* qweight, const void* s
     const half_t* zr = static_cast<const half_t*>(zeros_f16);
     half_t* y = static_cast<half_t*>(y_f16);
     const bool gemv_ok = gemv_supported(M, K);
+    const bool skinny_ok = skinny_supported(M, N, K);
     if (path == 1 && !gemv_ok) return AWQ_ERR_CONFIG;
+    if (path == 3 && !skinny_ok) return AWQ_ERR_CONFIG;
     const bool use_gemv = path == 1 || (path == 0 && gemv_ok && M <= 4);
     if (use_gemv) return launch_gemv(x, qweight, sc, zr, M, N, K, group_size, y, as_stream(stream));
+    const bool use_skinny = path == 3 || (path == 0 && skinny_ok);
     if (workspace != nullptr) {
         if (reinterpret_cast<uintptr_t>(workspace) & 255) return AWQ_ERR_ALIGN;
-        if (workspace_bytes < gemm_workspace_bytes(M, N)) return AWQ_ERR_WORKSPACE;
+        const size_t need = use_skinny ? skinny_workspace_bytes(M, N, K) : gemm_workspace_bytes(M, N);
+        if (workspace_bytes < need) return AWQ_ERR_WORKSPACE;
     }
+    if (use_skinny)
+        return launch_skinny(x, qweight, sc, zr, M, N, K, group_size, y, workspace, as_stream(stream));
     GemmArgs a;
     a.a = x;
     a.qweight = qweight;

@@ -27,6 +27,19 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 
 inline awq_status hip_status(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP; }
+
+// Compute units of the current device (queried once; 256 on MI355X).
+inline int cu_count() {
+    static int cached = -1;
+    if (cached < 0) {
+        int dev = 0, v = 256;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            v = 256;
+        cached = v;
+    }
+    return cached;
+}
 inline awq_status last_launch_status() { return hip_status(hipGetLastError()); }
 
 // ---- launchers (each returns after enqueueing on `stream`) ----
@@ -59,12 +72,30 @@ struct GemmArgs {
     const float* yref = nullptr;      // kLoss reference [M, N]
     double* partials = nullptr;       // kLoss: one double per tile
 };
+// Workspaces of the split kernels (GEMM stream-K, skinny K splits) start
+// with one shared region of tile counters: the counters of any call sit at
+// offset 0 and are back at zero when its kernel ends, so one workspace
+// serves calls of every shape and both kernels. Splits are only used for at
+// most split_counter_slots() output tiles.
+inline int split_counter_slots() { return 4 * cu_count(); }
+inline size_t split_counter_bytes() { return round_up(static_cast<size_t>(split_counter_slots()) * sizeof(int), 256); }
+
 int64_t gemm_tile_count(int64_t M, int64_t N);
 // Workspace of the stream-K launch (fp32 partial tiles + per-tile counters);
 // with workspace == nullptr launch_gemm runs one tile per block.
 size_t gemm_workspace_bytes(int64_t M, int64_t N);
 awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t stream,
                        void* workspace = nullptr);
+
+// Skinny MFMA GEMM for 4 < M <= 64 (decode batches): 16x16x32 MFMAs whose B
+// operand is one packed word per lane, K optionally split across blocks
+// (workspace != nullptr) with a fixed-order in-kernel fixup.
+constexpr int kSkinnyMaxM = 64;
+bool skinny_supported(int64_t M, int64_t N, int64_t K);
+size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K);
+awq_status launch_skinny(const half_t* x, const uint32_t* qweight, const half_t* scales,
+                         const half_t* zeros, int64_t M, int64_t N, int64_t K, int group_size,
+                         half_t* y, void* workspace, hipStream_t stream);
 
 // Scale-search helpers.
 size_t absmean_workspace_bytes(int64_t T, int64_t K);

@@ -298,9 +298,6 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
                     for (int j = 0; j < TN; ++j) s_next[j] = s_bits[j][min(g + 1, ngroups - 1)];
                 }
             }
-            // raised priority while this wave feeds the matrix core, so the
-            // other block's wave on the SIMD does its memory work in the gaps
-            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ks = 0; ks < BK / 16; ++ks) {
                 half8_t af[TM], bf[TN];
@@ -316,7 +313,6 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
             }
-            __builtin_amdgcn_s_setprio(0);
         };
 
         load(st, kb * BK);
@@ -498,18 +494,6 @@ constexpr int kBM = 256;
 constexpr int kBN = 128;
 constexpr int kBlocksPerCu = 2;
 
-int cu_count() {
-    static int cached = -1;
-    if (cached < 0) {
-        int dev = 0, v = 256;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            v = 256;
-        cached = v;
-    }
-    return cached;
-}
-
 constexpr int kMaxSplit = 4;        // segments per tile at most
 constexpr int kMinSteps = 8;        // K steps per block at least
 
@@ -520,7 +504,7 @@ int64_t resident_slots() { return static_cast<int64_t>(kBlocksPerCu) * cu_count(
 // tiles, the last round's blocks run one per CU at close to the per-CU rate
 // of two, and splitting costs more in partial traffic than it recovers.
 bool use_stream_k(int64_t tiles, int64_t K) {
-    if (tiles >= resident_slots()) return false;
+    if (tiles >= resident_slots() || tiles > split_counter_slots()) return false;
     return tiles * (K / BK) < (int64_t{1} << 31);
 }
 
@@ -547,8 +531,8 @@ void launch_cfg(const GemmArgs& args, void* workspace, hipStream_t stream) {
         sk.grid = stream_k_grid(tiles, args.K);
         sk.q = sk.total / sk.grid;
         sk.r = sk.total % sk.grid;
-        sk.partials = static_cast<float*>(workspace);
-        sk.counters = reinterpret_cast<int*>(static_cast<char*>(workspace) + partials_bytes());
+        sk.counters = static_cast<int*>(workspace);
+        sk.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_counter_bytes());
         hipLaunchKernelGGL((gemm_kernel<kBM, kBN, BMODE, OMODE, true>), dim3(static_cast<unsigned>(sk.grid)),
                            dim3(kThreads), 0, stream, args, static_cast<int>(tiles_n), sk);
         return;
@@ -562,7 +546,9 @@ void launch_cfg(const GemmArgs& args, void* workspace, hipStream_t stream) {
 int64_t gemm_tile_count(int64_t M, int64_t N) { return ceil_div(M, kBM) * ceil_div(N, kBN); }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N) {
-    return partials_bytes() + round_up(static_cast<size_t>(gemm_tile_count(M, N)) * sizeof(int), 256);
+    (void)M;
+    (void)N;
+    return split_counter_bytes() + partials_bytes();
 }
 
 awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t stream, void* workspace) {

@@ -330,18 +330,6 @@ int max_shared_bytes() {
 
 size_t gemv_lds_bytes(int64_t M, int64_t K) { return static_cast<size_t>(M) * static_cast<size_t>(K / 32) * 72; }
 
-int cu_count() {
-    static int cached = -1;
-    if (cached < 0) {
-        int dev = 0, v = 256;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            v = 256;
-        cached = v;
-    }
-    return cached;
-}
-
 template <int MT, int RPW, int CPL, int DEPTH, bool ONESHOT = false>
 awq_status launch_t(const half_t* x, const uint32_t* qweight, const half_t* scales,
                     const half_t* zeros, int64_t N, int64_t K, int log2g, half_t* y,
