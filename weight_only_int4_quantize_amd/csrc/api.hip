@@ -126,12 +126,14 @@ awq_status awq_gemm_ex(const void* x_f16, const uint32_t* qweight, const void* s
     const half_t* zr = static_cast<const half_t*>(zeros_f16);
     half_t* y = static_cast<half_t*>(y_f16);
     const bool gemv_ok = gemv_supported(M, K);
-    const bool skinny_ok = skinny_supported(M, N, K);
+    const bool skinny_ok = skinny_supported(M, N, K, group_size, workspace != nullptr);
     if (path == 1 && !gemv_ok) return AWQ_ERR_CONFIG;
     if (path == 3 && !skinny_ok) return AWQ_ERR_CONFIG;
-    const bool use_gemv = path == 1 || (path == 0 && gemv_ok && M <= 4);
+    // automatic: the GEMV up to 4 rows, the skinny kernel up to 64 where it
+    // applies, else the GEMV up to 8 rows, else the GEMM
+    const bool use_skinny = path == 3 || (path == 0 && M > 4 && skinny_ok);
+    const bool use_gemv = path == 1 || (path == 0 && gemv_ok && !use_skinny);
     if (use_gemv) return launch_gemv(x, qweight, sc, zr, M, N, K, group_size, y, as_stream(stream));
-    const bool use_skinny = path == 3 || (path == 0 && skinny_ok);
     if (workspace != nullptr) {
         if (reinterpret_cast<uintptr_t>(workspace) & 255) return AWQ_ERR_ALIGN;
         const size_t need = use_skinny ? skinny_workspace_bytes(M, N, K) : gemm_workspace_bytes(M, N);

@@ -16,13 +16,16 @@
 //   order, so the pairs line up and nothing is shuffled per weight.
 // * The group scale is applied per group: acc += s * (x . (q - z)_group),
 //   with the inner sum accumulated exactly by the MFMA in fp32.
-// * A block is 4 waves over 128 output columns (two 16-column MFMA tiles per
-//   wave) and up to 64 rows; x goes through LDS in double-buffered 256-k
-//   chunks, padded so the 16 rows of a fragment read fall in distinct banks.
-//   The packed weights stream straight into registers through a ring of
-//   groups in flight; they never touch LDS.
-// * With a workspace the K range is split across blocks so that narrow
-//   layers still fill the GPU. A block parks its fp32 partial tile, bumps a
+// * A block is 8 waves over 256 output columns (two 16-column MFMA tiles per
+//   wave) and up to 64 rows. It stages its whole K range of x in LDS once,
+//   before the main loop (rows padded so the 16 rows of a fragment read fall
+//   in distinct banks); the main loop then issues nothing but the packed
+//   weights, streamed straight into registers through a ring of groups in
+//   flight. Vector-memory loads complete in order, so keeping x out of the
+//   loop is what lets the ring stay deep.
+// * The K range of a block is bounded by the LDS; beyond that, and to fill
+//   the GPU when there are few column tiles, K is split across blocks (this
+//   needs a workspace). A block parks its fp32 partial tile, bumps a
 //   per-column-tile counter, and the last block to arrive adds every split
 //   in order and writes y: deterministic, and nobody waits on anybody.
 #include <algorithm>
@@ -32,13 +35,11 @@
 namespace awq {
 namespace {
 
-constexpr int kSkThreads = 256;
-constexpr int kSkBN = 128;              // output columns per block
-constexpr int kSkCK = 256;              // k per staged x chunk
-constexpr int kSkLdx = kSkCK + 8;       // LDS row in halves (528 bytes)
-constexpr int kSkDepth = 4;             // weight groups in flight per wave
+constexpr int kSkThreads = 512;         // 8 waves
+constexpr int kSkBN = 256;              // output columns per block
+constexpr int kSkLds = 152 * 1024;      // LDS budget for the staged x
+constexpr int kSkXP = 19;               // x pieces (16 bytes) per thread at most
 constexpr int kSc1 = 16;                // cache-policy bit sc1 (device scope)
-constexpr int kTargetBlocks = 2;        // blocks per CU the split aims for
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -85,11 +86,23 @@ __device__ inline uint4 permute8(uint4 v) {
 template <int WPL>
 struct GroupLoad {
     uint32_t w[2][WPL];     // two column tiles
-    uint16_t s[2], z[2];    // raw fp16 bits
 };
 
+// LDS row of the staged x, in halves: the K range rounded up to 128 plus 8,
+// so consecutive rows start 16 bytes apart modulo the 256-byte bank cycle.
+__host__ __device__ inline int sk_stride(int krange) { return (krange + 127) / 128 * 128 + 8; }
+// LDS row (one column) of the staged (scale, zero) pairs, in 32-bit words:
+// odd, so 16 columns read at one group fall in distinct banks.
+__host__ __device__ inline int sk_szst(int ngb) { return ngb | 1; }
+// LDS bytes of one block: x [16 MB rows][stride] halves + (scale, zero)
+// pairs [256 columns][szst] words.
+__host__ __device__ inline int sk_lds_bytes(int mb, int krange, int group_size) {
+    return 16 * mb * sk_stride(krange) * 2 + kSkBN * sk_szst(krange / group_size) * 4;
+}
+constexpr int kSkSZ = 32;               // (scale, zero) pairs per thread at most
+
 template <int MB, int WPL>
-__global__ __launch_bounds__(kSkThreads, 2) void skinny_kernel(const half_t* __restrict__ x,
+__global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __restrict__ x,
                                                               const uint32_t* __restrict__ qweight,
                                                               const half_t* __restrict__ scales,
                                                               const half_t* __restrict__ zeros,
@@ -98,8 +111,8 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_kernel(const half_t* __r
                                                               int* __restrict__ counters) {
     constexpr int G = WPL * 32;
     constexpr int MP = 16 * MB;                          // padded rows
-    constexpr int XPT = MP * (kSkCK / 8) / kSkThreads;   // x pieces per thread per chunk
-    __shared__ __attribute__((aligned(16))) half_t xs[2][MP * kSkLdx];
+    constexpr int kSkDepth = MB <= 2 ? 8 : 4;            // weight groups in flight per wave
+    extern __shared__ __attribute__((aligned(16))) half_t xs[];   // [MP][stride], then (s, z) pairs
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
@@ -114,7 +127,7 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_kernel(const half_t* __r
     const int g0 = static_cast<int>(static_cast<int64_t>(split) * ng / splits);
     const int g1 = static_cast<int>(static_cast<int64_t>(split + 1) * ng / splits);
     const int k0 = g0 * G, k1 = g1 * G;
-    const int nchunks = (k1 - k0 + kSkCK - 1) / kSkCK;
+    const int stride = sk_stride(k1 - k0);
 
     // ---- weights: buffer loads; an offset at or past a buffer's size
     //      reads zero, which is how columns past N and groups past the
@@ -126,20 +139,17 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_kernel(const half_t* __r
     const auto rw = rsrc(qweight, w_bytes);
     const auto rs = rsrc(scales, sz_bytes);
     const auto rz = rsrc(zeros, sz_bytes);
-    uint32_t w_off[2], sz_off[2];
+    uint32_t w_off[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int n = n_base + 16 * t + col;
-        const bool ok = n < N;
-        w_off[t] = ok ? static_cast<uint32_t>(n) * static_cast<uint32_t>(K / 2) + lg * WPL * 4 : w_bytes;
-        sz_off[t] = ok ? static_cast<uint32_t>(n) * static_cast<uint32_t>(ng) * 2 : sz_bytes;
+        w_off[t] = n < N ? static_cast<uint32_t>(n) * static_cast<uint32_t>(K / 2) + lg * WPL * 4 : w_bytes;
     }
     auto load_group = [&](GroupLoad<WPL>& gl, int g) {
         const bool ok = g < g1;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const uint32_t wo = ok ? w_off[t] + static_cast<uint32_t>(g) * (G / 2) : w_bytes;
-            const uint32_t so = ok ? sz_off[t] + static_cast<uint32_t>(g) * 2 : sz_bytes;
             if constexpr (WPL == 4) {
                 const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 0, 0));
 #pragma unroll
@@ -149,34 +159,70 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_kernel(const half_t* __r
 #pragma unroll
                 for (int j = 0; j < 2; ++j) gl.w[t][j] = v[j];
             }
-            gl.s[t] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
-            gl.z[t] = __builtin_amdgcn_raw_buffer_load_b16(rz, so, 0, 0);
         }
     };
 
-    // ---- x chunks: rows past M are zeros ----
-    uint4 xr[XPT];
-    auto load_x = [&](int c) {
-        const int kc0 = k0 + c * kSkCK;
+    // ---- the block's (scale, zero) pairs: consecutive lanes read
+    //      consecutive groups of one column, so these loads are coalesced
+    //      (one 2-byte load per lane and group in the main loop would cost a
+    //      cache-line request each) ----
+    const int ngb = g1 - g0;
+    const int szst = sk_szst(ngb);
+    const int nsz = kSkBN * ngb;
+    uint32_t* szs = reinterpret_cast<uint32_t*>(xs + MP * stride);
+    uint16_t sr[kSkSZ], zr[kSkSZ];
 #pragma unroll
-        for (int i = 0; i < XPT; ++i) {
-            const int p = tid + i * kSkThreads;
-            const int r = p / (kSkCK / 8), c8 = p % (kSkCK / 8);
-            const int k = kc0 + c8 * 8;
-            if (r < M && k < k1)
-                xr[i] = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(r) * K + k);
-            else
-                xr[i] = make_uint4(0u, 0u, 0u, 0u);
-        }
-    };
-    auto store_x = [&](int buf) {
+    for (int i = 0; i < kSkSZ; ++i) {
+        const int e = tid + i * kSkThreads;
+        const int c = e / ngb, gi = e - c * ngb;
+        const int n = tile * kSkBN + c;
+        const uint32_t so = (e < nsz && n < N) ? (static_cast<uint32_t>(n) * ng + g0 + gi) * 2 : sz_bytes;
+        sr[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
+        zr[i] = __builtin_amdgcn_raw_buffer_load_b16(rz, so, 0, 0);
+    }
+
+    // ---- x: the block's whole K range, rows past M as zeros (buffer
+    //      loads, no branches) ----
+    const uint32_t x_bytes = static_cast<uint32_t>(static_cast<int64_t>(M) * K * 2);
+    const auto rx = rsrc(x, x_bytes);
+    const int pr = (k1 - k0) / 8;                        // pieces per row
+    const int pieces = MP * pr;
+    uint4 xr[kSkXP];
 #pragma unroll
-        for (int i = 0; i < XPT; ++i) {
-            const int p = tid + i * kSkThreads;
-            const int r = p / (kSkCK / 8), c8 = p % (kSkCK / 8);
-            *reinterpret_cast<uint4*>(&xs[buf][r * kSkLdx + c8 * 8]) = permute8(xr[i]);
+    for (int i = 0; i < kSkXP; ++i) {
+        const int p = tid + i * kSkThreads;
+        const int r = p / pr, c8 = p - r * pr;
+        const bool ok = p < pieces && r < M;
+        const uint32_t off = ok ? (static_cast<uint32_t>(r) * K + k0 + c8 * 8) * 2 : x_bytes;
+        xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < kSkSZ; ++i) {
+        const int e = tid + i * kSkThreads;
+        if (e < nsz) {
+            const int c = e / ngb, gi = e - c * ngb;
+            szs[c * szst + gi] = static_cast<uint32_t>(sr[i]) | (static_cast<uint32_t>(zr[i]) << 16);
         }
-    };
+    }
+    // Loads complete in order: the pairs (issued first) were staged without
+    // waiting for x; x is staged below without waiting for the weights.
+    GroupLoad<WPL> ring[kSkDepth];
+    // slot by slot, as the loop refills them: the wait counts at the loop
+    // head are the smaller of this order and the loop's own
+#pragma unroll
+    for (int d = 0; d < kSkDepth; ++d) {
+        load_group(ring[d], g0 + d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < kSkXP; ++i) {
+        const int p = tid + i * kSkThreads;
+        if (p < pieces) {
+            const int r = p / pr, c8 = p - r * pr;
+            *reinterpret_cast<uint4*>(&xs[r * stride + c8 * 8]) = permute8(xr[i]);
+        }
+    }
+    __syncthreads();
 
     float4_t acc[MB][2];
 #pragma unroll
@@ -185,45 +231,31 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_kernel(const half_t* __r
         for (int t = 0; t < 2; ++t) acc[mb][t] = float4_t{0.f, 0.f, 0.f, 0.f};
     const SkConsts uk = sk_consts();
 
-    // Ring slot d holds group gb + d. x chunk c lives in LDS buffer c & 1:
-    // it is loaded into registers while chunk c - 1 is consumed and written
-    // to LDS on entering chunk c (that buffer was last read in chunk c - 2,
-    // which every wave left before the barrier on entering chunk c - 1).
-    constexpr int CG = kSkCK / G;                        // groups per chunk
-    GroupLoad<WPL> ring[kSkDepth];
-#pragma unroll
-    for (int d = 0; d < kSkDepth; ++d) load_group(ring[d], g0 + d);
-    load_x(0);
-    store_x(0);
-    if (nchunks > 1) load_x(1);
-    __syncthreads();
-
-    for (int gb = g0; gb < g1; gb += kSkDepth) {
+    // Ring slot d holds group g0 + gb + d. Refills are issued
+    // unconditionally at a fixed place, so the compiler's wait counts track
+    // the ring exactly; only the compute of groups past the range is skipped.
+    const int nblk = g1 - g0;
+    const half_t* xcol = &xs[col * stride + 8 * lg * WPL];
+    const uint32_t* szcol = &szs[(wave * 32 + col) * szst];
+    for (int gb = 0; gb < nblk; gb += kSkDepth) {
 #pragma unroll
         for (int d = 0; d < kSkDepth; ++d) {
-            const int gg = gb + d;
-            if (gg < g1) {
-                const int gi = gg - g0;
-                const int c = gi / CG;
-                if (gi % CG == 0 && c > 0) {
-                    store_x(c & 1);
-                    __syncthreads();
-                    if (c + 1 < nchunks) load_x(c + 1);
-                }
-                GroupLoad<WPL>& gl = ring[d];
+            const int gi = gb + d;
+            GroupLoad<WPL>& gl = ring[d];
+            if (gi < nblk) {
                 half8_t bf[2][WPL];
                 float s[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    const half_t z = __builtin_bit_cast(half_t, gl.z[t]);
+                    const uint32_t sz = szcol[t * 16 * szst + gi];
+                    const half_t z = __builtin_bit_cast(half_t, static_cast<uint16_t>(sz >> 16));
                     const half_t zh = static_cast<half_t>(1024.0f) + z;   // exact
                     const half_t zl = static_cast<half_t>(64.0f) + z;     // exact
 #pragma unroll
                     for (int j = 0; j < WPL; ++j) bf[t][j] = unpack8(gl.w[t][j], half2_t{zh, zh}, half2_t{zl, zl}, uk);
-                    s[t] = static_cast<float>(__builtin_bit_cast(half_t, gl.s[t]));
+                    s[t] = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(sz & 0xFFFFu)));
                 }
-                load_group(gl, gg + kSkDepth);                     // refill the slot
-                const half_t* xb = &xs[c & 1][col * kSkLdx + (gi % CG) * G + 8 * lg * WPL];
+                const half_t* xb = xcol + gi * G;
                 float4_t part[MB][2];
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
@@ -233,7 +265,7 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_kernel(const half_t* __r
                 for (int j = 0; j < WPL; ++j) {
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) {
-                        const half8_t a = *reinterpret_cast<const half8_t*>(xb + 16 * mb * kSkLdx + 8 * j);
+                        const half8_t a = *reinterpret_cast<const half8_t*>(xb + 16 * mb * stride + 8 * j);
 #pragma unroll
                         for (int t = 0; t < 2; ++t)
                             part[mb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[t][j], part[mb][t], 0, 0, 0);
@@ -246,6 +278,7 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_kernel(const half_t* __r
 #pragma unroll
                         for (int e = 0; e < 4; ++e) acc[mb][t][e] += s[t] * part[mb][t][e];
             }
+            load_group(gl, g0 + gi + kSkDepth);              // refill the slot
         }
     }
 
@@ -267,22 +300,18 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_kernel(const half_t* __r
         emit(acc);
         return;
     }
-    // partial tile of this (tile, split): [MB * 2 float4 chunks][256 threads]
+    // partial tiles of this column tile, one per split:
+    // [split][MB * 2 float4 chunks][512 threads]
     constexpr uint32_t kPartBytes = MB * 2 * kSkThreads * 16;
-    auto part_rsrc = [&](int sp) {
-        return rsrc(reinterpret_cast<char*>(partials) +
-                        (static_cast<int64_t>(tile) * splits + sp) * static_cast<int64_t>(kPartBytes),
-                    kPartBytes);
-    };
-    {
-        const auto pr = part_rsrc(split);
+    const auto prs = rsrc(reinterpret_cast<char*>(partials) +
+                              static_cast<int64_t>(tile) * splits * static_cast<int64_t>(kPartBytes),
+                          static_cast<uint32_t>(splits) * kPartBytes);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[mb][t]), pr, tid * 16,
-                                                       (mb * 2 + t) * kSkThreads * 16, kSc1);
-    }
+        for (int t = 0; t < 2; ++t)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[mb][t]), prs, tid * 16,
+                                                   split * kPartBytes + (mb * 2 + t) * kSkThreads * 16, kSc1);
     // sc1 stores and loads bypass the per-XCD L2s; every store is complete
     // before the counter moves, and the loads are issued after it is read
     __builtin_amdgcn_s_waitcnt(0);
@@ -297,14 +326,26 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_kernel(const half_t* __r
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int t = 0; t < 2; ++t) sum[mb][t] = float4_t{0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < splits; ++sp) {
-        const auto pr = part_rsrc(sp);
+    // four splits' loads in flight at a time; splits past the last read
+    // zero (past the descriptor's end), and the adds keep split order
+    constexpr int kFix = 4;
+    for (int sp = 0; sp < splits; sp += kFix) {
+        float4_t v[kFix][MB][2];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int f = 0; f < kFix; ++f)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-                sum[mb][t] += __builtin_bit_cast(
-                    float4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, tid * 16, (mb * 2 + t) * kSkThreads * 16, kSc1));
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    v[f][mb][t] = __builtin_bit_cast(
+                        float4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                      prs, tid * 16, (sp + f) * kPartBytes + (mb * 2 + t) * kSkThreads * 16, kSc1));
+#pragma unroll
+        for (int f = 0; f < kFix; ++f)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) sum[mb][t] += v[f][mb][t];
     }
     emit(sum);
     if (tid == 0) __hip_atomic_store(&counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -314,51 +355,92 @@ int64_t sk_tiles(int64_t N) { return (N + kSkBN - 1) / kSkBN; }
 
 int sk_mb(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
+// longest K range (whole groups, at most what kSkXP / kSkSZ cover) whose
+// staged x and (scale, zero) pairs fit the LDS budget
+int64_t sk_kmax(int64_t M, int group_size) {
+    const int mb = sk_mb(M);
+    const int64_t by_regs = std::min<int64_t>(static_cast<int64_t>(kSkXP) * kSkThreads * 8 / (16 * mb),
+                                              static_cast<int64_t>(kSkSZ) * kSkThreads / kSkBN * group_size);
+    int64_t kr = by_regs / group_size * group_size;
+    while (kr > 0 && sk_lds_bytes(mb, static_cast<int>(kr), group_size) > kSkLds) kr -= group_size;
+    return kr;
+}
+
 // partial tiles a workspace holds: splits x column tiles never exceed it
 int64_t sk_max_parts() { return 3 * static_cast<int64_t>(cu_count()); }
 
-// K splits when a workspace is given: enough blocks for kTargetBlocks per
-// CU, each split keeping at least two groups.
-int sk_splits(int64_t N, int64_t K, int group_size) {
+size_t sk_partial_bytes(int64_t M) { return static_cast<size_t>(sk_mb(M)) * 2 * kSkThreads * 16; }
+
+// Splits of K: at least enough for each block's x range to fit the LDS;
+// with a workspace, as many more as fill one block per CU (each split
+// keeping at least two groups). 0 = this shape cannot run here.
+int sk_splits(int64_t M, int64_t N, int64_t K, int group_size, bool have_workspace) {
     const int64_t tiles = sk_tiles(N);
-    if (tiles > split_counter_slots()) return 1;
     const int64_t ng = K / group_size;
-    int64_t s = (kTargetBlocks * cu_count() + tiles / 2) / tiles;
-    s = std::min<int64_t>(s, ng / 2);
-    while (s > 1 && s * tiles > sk_max_parts()) --s;
+    const int64_t gmax = sk_kmax(M, group_size) / group_size;
+    if (gmax < 1) return 0;
+    const int64_t s_min = (ng + gmax - 1) / gmax;
+    if (!have_workspace) return s_min == 1 ? 1 : 0;
+    if (tiles > split_counter_slots()) return s_min == 1 ? 1 : 0;
+    int64_t s = std::max<int64_t>(s_min, std::min<int64_t>(cu_count() / tiles, ng / 2));
+    while (s > s_min && s * tiles > sk_max_parts()) --s;
+    if (s > 1 && s * tiles > sk_max_parts()) return 0;
     return static_cast<int>(std::max<int64_t>(1, s));
 }
 
-size_t sk_partial_bytes(int64_t M) { return static_cast<size_t>(sk_mb(M)) * 2 * kSkThreads * 16; }
-
 template <int MB, int WPL>
-void launch_cfg(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M, int N,
-                int K, half_t* y, int splits, float* partials, int* counters, hipStream_t stream) {
+awq_status launch_cfg(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
+                      int N, int K, half_t* y, void* workspace, hipStream_t stream) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<MB, WPL>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kSkLds) != hipSuccess)
+            return AWQ_ERR_HIP;
+        attr_set = true;
+    }
+    const int splits = sk_splits(M, N, K, WPL * 32, workspace != nullptr);
+    if (splits == 0) return AWQ_ERR_CONFIG;
+    float* partials = nullptr;
+    int* counters = nullptr;
+    if (splits > 1) {
+        counters = static_cast<int*>(workspace);
+        partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_counter_bytes());
+    }
+    // the longest range of any split sets the LDS
+    const int ng = K / (WPL * 32);
+    const int gmax_split = (ng + splits - 1) / splits;
+    const size_t lds = static_cast<size_t>(sk_lds_bytes(MB, gmax_split * WPL * 32, WPL * 32));
     const int64_t blocks = sk_tiles(N) * splits;
-    hipLaunchKernelGGL((skinny_kernel<MB, WPL>), dim3(static_cast<unsigned>(blocks)), dim3(kSkThreads), 0, stream, x,
-                       qweight, scales, zeros, y, M, N, K, splits, partials, counters);
+    hipLaunchKernelGGL((skinny_kernel<MB, WPL>), dim3(static_cast<unsigned>(blocks)), dim3(kSkThreads), lds, stream,
+                       x, qweight, scales, zeros, y, M, N, K, splits, partials, counters);
+    return last_launch_status();
 }
 
 template <int WPL>
-void launch_wpl(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M, int N,
-                int K, half_t* y, int splits, float* partials, int* counters, hipStream_t stream) {
+awq_status launch_wpl(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
+                      int N, int K, half_t* y, void* workspace, hipStream_t stream) {
     switch (sk_mb(M)) {
-        case 1: launch_cfg<1, WPL>(x, qweight, scales, zeros, M, N, K, y, splits, partials, counters, stream); break;
-        case 2: launch_cfg<2, WPL>(x, qweight, scales, zeros, M, N, K, y, splits, partials, counters, stream); break;
-        default: launch_cfg<4, WPL>(x, qweight, scales, zeros, M, N, K, y, splits, partials, counters, stream); break;
+        case 1: return launch_cfg<1, WPL>(x, qweight, scales, zeros, M, N, K, y, workspace, stream);
+        case 2: return launch_cfg<2, WPL>(x, qweight, scales, zeros, M, N, K, y, workspace, stream);
+        default: return launch_cfg<4, WPL>(x, qweight, scales, zeros, M, N, K, y, workspace, stream);
     }
 }
 
 }  // namespace
 
-bool skinny_supported(int64_t M, int64_t N, int64_t K) {
+bool skinny_supported(int64_t M, int64_t N, int64_t K, int group_size, bool have_workspace) {
     // buffer offsets are 32-bit: the packed matrix plus one row of slack
-    // (the largest offset a zero-reading lane forms) must stay below 4 GiB
-    return M >= 1 && M <= kSkinnyMaxM && N >= 1 && (N + 1) * (K / 2) + 64 < (int64_t{1} << 32);
+    // (the largest offset a zero-reading lane forms), and x, stay below 4 GiB
+    if (M < 1 || M > kSkinnyMaxM || N < 1 || (N + 1) * (K / 2) + 64 >= (int64_t{1} << 32) ||
+        M * K * 2 + 64 >= (int64_t{1} << 32))
+        return false;
+    return sk_splits(M, N, K, group_size, have_workspace) > 0;
 }
 
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    if (!skinny_supported(M, N, K)) return 0;
+    (void)N;
+    (void)K;
+    if (M < 1 || M > kSkinnyMaxM) return 0;
     return split_counter_bytes() + static_cast<size_t>(sk_max_parts()) * sk_partial_bytes(M);
 }
 
@@ -366,23 +448,10 @@ awq_status launch_skinny(const half_t* x, const uint32_t* qweight, const half_t*
                          int64_t M, int64_t N, int64_t K, int group_size, half_t* y, void* workspace,
                          hipStream_t stream) {
     if (M == 0 || N == 0) return AWQ_OK;
-    if (!skinny_supported(M, N, K)) return AWQ_ERR_SHAPE;
-    int splits = 1;
-    float* partials = nullptr;
-    int* counters = nullptr;
-    if (workspace != nullptr) {
-        splits = sk_splits(N, K, group_size);
-        if (splits > 1) {
-            counters = static_cast<int*>(workspace);
-            partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_counter_bytes());
-        }
-    }
+    if (!skinny_supported(M, N, K, group_size, workspace != nullptr)) return AWQ_ERR_CONFIG;
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-    if (group_size == 128)
-        launch_wpl<4>(x, qweight, scales, zeros, m, n, k, y, splits, partials, counters, stream);
-    else
-        launch_wpl<2>(x, qweight, scales, zeros, m, n, k, y, splits, partials, counters, stream);
-    return last_launch_status();
+    if (group_size == 128) return launch_wpl<4>(x, qweight, scales, zeros, m, n, k, y, workspace, stream);
+    return launch_wpl<2>(x, qweight, scales, zeros, m, n, k, y, workspace, stream);
 }
 
 }  // namespace awq
