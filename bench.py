@@ -15,6 +15,8 @@ The same run also times, each in its own section:
   * the same layer with fused q/k/v (12288x4096) and gate/up (22016x4096)
     projections, four launches per step;
   * the per-node floor of a graph of tiny kernels (launch cost context);
+  * batched decode rows on the skinny MFMA kernel (M = 16 on the decode
+    shapes, M = 32 on the 13B/70B sweep shapes);
   * the prefill GEMM, x[2048, K] times the two MLP shapes;
   * the quantize kernel on 11008x4096;
   * one full scale search (W[11008, 4096], X[65536, 4096], 20 alphas);
@@ -227,6 +229,39 @@ class Bench:
                 "weight_copies": n_copies, "us_per_step": round(us, 2), "GB/s": round(gbs, 1),
                 "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "per_launch": per_launch}
 
+    def run_skinny(self):
+        """Batched decode rows on the skinny MFMA kernel (awq_gemm_ex with a
+        workspace): M = 16 on the decode shapes, M = 32 on the sweep shapes,
+        weights rotated over copies like the decode step."""
+        torch, awq = self.torch, self.awq
+        ws = awq.gemm_workspace(64, 1, 1, self.dev)
+        out = {}
+        cases = [(16, N, K, 128) for (N, K) in synth.DECODE_SHAPES] + \
+                [(32, N, K, 128) for (N, K) in synth.SWEEP_SHAPES]
+        for (M, N, K, g) in cases:
+            lay = synth.decode_layer(N, K, M) if M == 16 else synth.sweep_layer(N, K, M, g)
+            qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), g)
+            x = self.d(lay["x"])
+            nbytes = gemv_bytes(M, N, K, g)
+            n_copies = max(2, int(np.ceil(1.2e9 / nbytes)))
+            cps = [(qw.clone(), sc.clone(), zr.clone()) for _ in range(n_copies)]
+            y = torch.empty((M, N), dtype=torch.float16, device=self.dev)
+
+            def one(i, cps=cps, x=x, y=y, g=g):
+                q = cps[i % len(cps)]
+                awq.awq_gemm(x, q[0], q[1], q[2], g, out=y, workspace=ws)
+
+            gr = self.capture(one, 2 * n_copies)
+            gr.replay()
+            t = self.time(lambda _: gr.replay()) / (2 * n_copies)
+            key = f"M{M}_{N}x{K}"
+            out[key] = {"us": round(t * 1e6, 2), "GB/s": round(nbytes / t / 1e9, 1),
+                        "frac_of_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"skinny {key}: {t * 1e6:.2f} us, {nbytes / t / 1e9:.0f} GB/s")
+            del cps, gr
+        torch.cuda.synchronize()
+        return out
+
     def run_launch_floor(self):
         """Per-node cost of a HIP graph of tiny kernels (a one-element fill):
         the floor under every back-to-back launch timed here."""
@@ -383,8 +418,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true")
-    ap.add_argument("--only", choices=["decode", "decode-fused", "gemv-roofline", "gemm", "quantize", "search",
-                                       "copy"],
+    ap.add_argument("--only", choices=["decode", "decode-fused", "gemv-roofline", "skinny", "gemm", "quantize",
+                                       "search", "copy"],
                     help="run one section (for profiler runs); timings go to stderr")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -402,6 +437,8 @@ def main():
                 b.run_gemv_shapes([ROOFLINE_SHAPE])
         elif args.only == "decode-fused":
             b.run_decode_fused()
+        elif args.only == "skinny":
+            b.run_skinny()
         elif args.only == "gemm":
             b.run_gemm()
         elif args.only == "quantize":
@@ -419,6 +456,7 @@ def main():
     del b.copies
     fused = b.run_decode_fused()
     floor_us = b.run_launch_floor()
+    skinny = b.run_skinny()
     copy = b.run_copy()
     gemm = b.run_gemm()
     quant = b.run_quantize()
@@ -454,6 +492,7 @@ def main():
         "hbm_copy_1GiB": copy,
         "gemv_per_shape": per_shape,
         "decode_fused": fused,
+        "skinny_batched_decode": skinny,
         "gemm": gemm,
         "quantize": quant,
         "scale_search": search,

@@ -154,9 +154,10 @@ def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
 
 
 def gemm_workspace(M: int, N: int, K: int, device=None):
-    """A zero-filled uint8 GPU tensor usable as awq_gemm_ex's workspace for
-    every GEMM with at most as many output tiles as [M, N]; each call leaves
-    it ready for the next, without clearing."""
+    """A zero-filled uint8 GPU tensor of awq_gemm_workspace_bytes(M, N, K)
+    bytes: awq_gemm_ex's workspace for this shape and for any other whose
+    awq_gemm_workspace_bytes is no larger (today the size depends on M
+    only). Each call leaves it ready for the next, without clearing."""
     torch = _torch()
     nbytes = gemm_workspace_bytes(M, N, K)
     return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device or "cuda")
