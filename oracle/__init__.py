@@ -10,7 +10,11 @@ from .awq_oracle import (  # noqa: F401
     QMAX,
     RANGE_FLOOR,
     MEAN_FLOOR,
+    SYM_QMAX,
+    SYM_ZERO,
     group_quantize,
+    group_quantize_symmetric,
+    quantize_symmetric,
     pack_codes,
     unpack_codes,
     quantize,

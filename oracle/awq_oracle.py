@@ -99,6 +99,49 @@ def group_quantize(w, group_size: int, channel_scale=None):
     return codes, s16, z.astype(np.float16)
 
 
+SYM_QMAX = 7                    # 2^(bits-1) - 1: the largest signed code used
+SYM_ZERO = 8                    # stored zero-point of the symmetric form
+
+
+def group_quantize_symmetric(w, group_size: int, channel_scale=None):
+    """Group-wise symmetric INT4 quantization ([P3 "对称/非对称量化"]: the
+    zero-point is 0, which the pages call simple and hardware friendly).
+
+    Reading (the pages give no formula): the group's largest magnitude
+    a = max|w| maps to +-7, so the map is odd, q(-w) = -q(w):
+      s32 = max(a, 1e-5) / 7          (IEEE float32 divide; floor as R2)
+      s16 = float16(s32)              (codes made with the stored scale)
+      q   = clamp(rint(w / s16), -8, 7)
+    stored in the asymmetric layout as code = q + 8 with zero-point 8, so
+    x_hat = (code - 8) * s16 = q * s16 and every linear-layer path applies
+    unchanged. Round first, then add the (fixed) zero-point, as in R5.
+
+    Returns (codes uint8 [N, K] in 1..15, scales float16 [N, K/G],
+    zeros float16 [N, K/G] all 8)."""
+    w32 = np.asarray(w).astype(np.float32)
+    N, K = w32.shape
+    _check_groups(K, group_size)
+    if channel_scale is not None:
+        cs = np.asarray(channel_scale, dtype=np.float32).reshape(1, K)
+        w32 = w32 * cs
+    wg = w32.reshape(N, K // group_size, group_size)
+    a = np.maximum(np.abs(wg).max(axis=2), RANGE_FLOOR)
+    s32 = a / np.float32(SYM_QMAX)                      # IEEE float32 divide
+    s16 = s32.astype(np.float16)
+    sf = s16.astype(np.float32)
+    q = np.rint(wg / sf[:, :, None]) + np.float32(SYM_ZERO)
+    q = np.clip(q, 0, QMAX)
+    codes = q.reshape(N, K).astype(np.uint8)
+    z16 = np.full(s16.shape, SYM_ZERO, dtype=np.float16)
+    return codes, s16, z16
+
+
+def quantize_symmetric(w, group_size: int, channel_scale=None):
+    """Symmetric form of quantize: (qweight, scales, zeros = 8)."""
+    codes, s16, z16 = group_quantize_symmetric(w, group_size, channel_scale)
+    return pack_codes(codes), s16, z16
+
+
 def pack_codes(codes) -> np.ndarray:
     """Pack eight 4-bit codes along K into one uint32.
 
