@@ -17,6 +17,7 @@ The same run also times, each in its own section:
   * the per-node floor of a graph of tiny kernels (launch cost context);
   * batched decode rows on the skinny MFMA kernel (M = 16 on the decode
     shapes, M = 32 on the 13B/70B sweep shapes);
+  * the roofline GEMV at group sizes 32, 64, 128 and 256;
   * the prefill GEMM, x[2048, K] times the two MLP shapes;
   * the quantize kernel on 11008x4096;
   * one full scale search (W[11008, 4096], X[65536, 4096], 20 alphas);
@@ -262,6 +263,35 @@ class Bench:
         torch.cuda.synchronize()
         return out
 
+    def run_group_sizes(self):
+        """The roofline GEMV shape (11008x4096, M = 1) at every supported group
+        size, weights rotated over copies: the pages weigh group 128 against
+        256 (fewer scales, less traffic)."""
+        torch, awq = self.torch, self.awq
+        N, K = ROOFLINE_SHAPE
+        out = {}
+        for g in (32, 64, 128, 256):
+            lay = synth.decode_layer(N, K, 1, g)
+            qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), g)
+            x = self.d(lay["x"])
+            nbytes = gemv_bytes(1, N, K, g)
+            n_copies = max(2, int(np.ceil(1.2e9 / nbytes)))
+            cps = [(qw.clone(), sc.clone(), zr.clone()) for _ in range(n_copies)]
+            y = torch.empty((1, N), dtype=torch.float16, device=self.dev)
+
+            def one(i, cps=cps, x=x, y=y, g=g):
+                q = cps[i % len(cps)]
+                awq.awq_gemm(x, q[0], q[1], q[2], g, out=y)
+
+            gr = self.capture(one, 4 * n_copies)
+            gr.replay()
+            t = self.time(lambda _: gr.replay()) / (4 * n_copies)
+            out[f"G{g}"] = {"us": round(t * 1e6, 2), "bytes": nbytes, "GB/s": round(nbytes / t / 1e9, 1)}
+            log(f"gemv {N}x{K} G={g}: {t * 1e6:.2f} us, {nbytes / t / 1e9:.0f} GB/s")
+            del cps, gr
+        torch.cuda.synchronize()
+        return out
+
     def run_launch_floor(self):
         """Per-node cost of a HIP graph of tiny kernels (a one-element fill):
         the floor under every back-to-back launch timed here."""
@@ -324,7 +354,25 @@ class Bench:
                                                        "TFLOP/s": round(flop / t / 1e12, 1)}
             log(f"gemm M={synth.PREFILL_M} {N}x{K}: {t * 1e6:.1f} us, {flop / t / 1e12:.0f} TFLOP/s")
         tflops = tot_flop / tot_t / 1e12
-        return {"M": synth.PREFILL_M, "TFLOP/s": round(tflops, 1),
+        # the 13B/70B sweep shapes at M = 512 (not part of the prefill figure)
+        sweep = {}
+        for (N, K) in synth.SWEEP_SHAPES:
+            M = 512
+            lay = synth.sweep_layer(N, K, M, G)
+            qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), G)
+            x = self.d(lay["x"])
+            y = torch.empty((M, N), dtype=torch.float16, device=self.dev)
+
+            def g(i, x=x, qw=qw, sc=sc, zr=zr, y=y):
+                awq.awq_gemm(x, qw, sc, zr, G, out=y, workspace=ws)
+
+            for i in range(3):
+                g(i)
+            t = self.time(g, 20) / 20
+            flop = 2.0 * M * N * K
+            sweep[f"{M}x{N}x{K}"] = {"us": round(t * 1e6, 2), "TFLOP/s": round(flop / t / 1e12, 1)}
+            log(f"gemm M={M} {N}x{K}: {t * 1e6:.1f} us, {flop / t / 1e12:.0f} TFLOP/s")
+        return {"M": synth.PREFILL_M, "TFLOP/s": round(tflops, 1), "sweep_m512": sweep,
                 "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": F16_MFMA_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tflops / F16_MFMA_PEAK_TFLOPS, 4)},
                 "per_shape": per_shape}
@@ -457,6 +505,7 @@ def main():
     fused = b.run_decode_fused()
     floor_us = b.run_launch_floor()
     skinny = b.run_skinny()
+    groups = b.run_group_sizes()
     copy = b.run_copy()
     gemm = b.run_gemm()
     quant = b.run_quantize()
@@ -493,6 +542,7 @@ def main():
         "gemv_per_shape": per_shape,
         "decode_fused": fused,
         "skinny_batched_decode": skinny,
+        "gemv_group_sizes": groups,
         "gemm": gemm,
         "quantize": quant,
         "scale_search": search,

@@ -22,7 +22,7 @@
  * Conventions shared by every call:
  *   - Matrices are row-major and densely packed. W[N, K]: row n is output
  *     channel n, column k is input channel k. Groups of G consecutive k share
- *     one scale and one zero-point (G = 64 or 128).
+ *     one scale and one zero-point (G = 32, 64, 128 or 256).
  *   - qweight is uint32 [N, K/8]: the 4-bit code of column k = 8c + j sits in
  *     bits 4j..4j+3 of word c. scales and zeros are fp16 [N, K/G]; every zero
  *     is an integer 0..15.
@@ -77,7 +77,7 @@ int awq_version(void);
  *   w_f16          device, fp16 [N, K]
  *   channel_scale  device, fp32 [K] or NULL (AWQ's W * diag(s), rskf.cn §2.1)
  *   N, K           N >= 0; K > 0, K % group_size == 0
- *   group_size     64 or 128
+ *   group_size     32, 64, 128 or 256
  *   qweight        device, uint32 [N, K/8]            (output)
  *   scales_f16     device, fp16 [N, K/G]              (output)
  *   zeros_f16      device, fp16 [N, K/G]              (output)
@@ -90,6 +90,28 @@ awq_status awq_quantize(const void* w_f16, const float* channel_scale,
                         void* stream);
 
 /*
+ * awq_quantize_ex - awq_quantize with a choice of map
+ * (aissn.com 对称/非对称量化: asymmetric allows a zero-point != 0;
+ * symmetric has zero-point 0, simple and hardware friendly).
+ *
+ *   mode AWQ_QUANT_ASYMMETRIC (0): exactly awq_quantize.
+ *   mode AWQ_QUANT_SYMMETRIC (1): per row n and group g, in IEEE float32,
+ *     a     = max(max |w'|, 1e-5)
+ *     scale = fp16_rne(a / 7)                  (stored in scales[n, g])
+ *     code  = clamp(rint(w' / scale) + 8, 0, 15),  zeros[n, g] = 8
+ *   i.e. the signed code q = code - 8 = rint(w' / scale) lies in -7..7 and
+ *   q(-w) = -q(w). The stored layout is the asymmetric one, so awq_gemm and
+ *   the other linear-layer calls apply unchanged.
+ * Any other mode returns AWQ_ERR_CONFIG. Arguments otherwise as
+ * awq_quantize.
+ */
+enum { AWQ_QUANT_ASYMMETRIC = 0, AWQ_QUANT_SYMMETRIC = 1 };
+awq_status awq_quantize_ex(const void* w_f16, const float* channel_scale,
+                           int64_t N, int64_t K, int group_size, int mode,
+                           uint32_t* qweight, void* scales_f16, void* zeros_f16,
+                           void* stream);
+
+/*
  * awq_gemm - the W4A16 linear layer y = x . dequant(Wq)^T.
  * (xxmr.cn §1.2 inverse map; rskf.cn §1.3 / §3.3 GEMV and GEMM kernels)
  *
@@ -100,7 +122,7 @@ awq_status awq_quantize(const void* w_f16, const float* channel_scale,
  *                AWQ factor s, which is folded upstream: rskf.cn §2.3)
  *   qweight, scales_f16, zeros_f16   device, as written by awq_quantize
  *   M, N, K      M, N >= 0; K > 0, K % group_size == 0
- *   group_size   64 or 128
+ *   group_size   32, 64, 128 or 256
  *   y_f16        device, fp16 [M, N] (output; must not alias the inputs)
  * M == 0 or N == 0 returns AWQ_OK without work. M <= 4 (decode) runs a
  * bandwidth-bound GEMV, 4 < M <= 64 (a batch of decode tokens) a skinny
@@ -191,7 +213,7 @@ awq_status awq_activation_absmean(const void* x_f16, int64_t T, int64_t K,
  *   w_f16         device, fp16 [N, K]
  *   x_f16         device, fp16 [T, K] (calibration activations)
  *   N, K, T       N > 0, T > 0, K > 0, K % group_size == 0
- *   group_size    64 or 128
+ *   group_size    32, 64, 128 or 256
  *   alphas        host, float64 [n_alpha], every alpha finite (1 <= n_alpha <= 64)
  *   workspace     device, >= awq_scale_search_workspace_bytes(N, K, T, G, n_alpha)
  *   losses        host, float64 [n_alpha] (output)

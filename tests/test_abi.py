@@ -50,8 +50,9 @@ def test_status_strings(L):
 
 
 @pytest.mark.parametrize("N,K,G,expect", [
-    (16, 128, 32, CONFIG),      # unsupported group size
-    (16, 128, 256, CONFIG),
+    (16, 128, 16, CONFIG),      # unsupported group sizes (32, 64, 128, 256 are supported)
+    (16, 512, 512, CONFIG),
+    (16, 96, 48, CONFIG),
     (16, 100, 64, SHAPE),       # K not a multiple of G
     (16, 0, 64, SHAPE),         # empty K
     (-1, 128, 64, SHAPE),
@@ -59,6 +60,17 @@ def test_status_strings(L):
 ])
 def test_quantize_shape_checks(L, N, K, G, expect):
     assert L.awq_quantize(FAKE, None, N, K, G, FAKE, FAKE, FAKE, None) == expect
+
+
+def test_quantize_ex_checks(L):
+    q = L.awq_quantize_ex
+    assert q(FAKE, None, 16, 128, 64, 2, FAKE, FAKE, FAKE, None) == CONFIG     # unknown mode
+    assert q(FAKE, None, 16, 128, 64, -1, FAKE, FAKE, FAKE, None) == CONFIG
+    assert q(FAKE, None, 16, 128, 16, 1, FAKE, FAKE, FAKE, None) == CONFIG     # group size
+    assert q(FAKE, None, 16, 100, 64, 1, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(FAKE, None, 0, 128, 64, 1, FAKE, FAKE, FAKE, None) == OK          # empty N
+    assert q(None, None, 16, 128, 64, 1, FAKE, FAKE, FAKE, None) == NULL
+    assert q(FAKE_ODD, None, 16, 128, 64, 1, FAKE, FAKE, FAKE, None) == ALIGN
 
 
 def test_quantize_null_and_alignment(L):

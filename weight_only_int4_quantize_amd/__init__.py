@@ -29,6 +29,7 @@ STATUS_NAMES = {
     4: "AWQ_ERR_CONFIG", 5: "AWQ_ERR_WORKSPACE", 6: "AWQ_ERR_HIP",
 }
 PATH_AUTO, PATH_GEMV, PATH_GEMM, PATH_SKINNY = 0, 1, 2, 3
+QUANT_ASYMMETRIC, QUANT_SYMMETRIC = 0, 1
 
 _lib = None
 
@@ -60,6 +61,8 @@ def load() -> ctypes.CDLL:
     L.awq_version.argtypes = []
     L.awq_quantize.restype = c_int
     L.awq_quantize.argtypes = [c_vp, c_vp, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp]
+    L.awq_quantize_ex.restype = c_int
+    L.awq_quantize_ex.argtypes = [c_vp, c_vp, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp]
     L.awq_gemm.restype = c_int
     L.awq_gemm.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_vp]
     L.awq_gemm_path.restype = c_int
@@ -121,8 +124,9 @@ def _need_gpu(name: str, t, dtype=None) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
-def awq_quantize(w, group_size: int = 128, channel_scale=None, out=None):
-    """Group-wise asymmetric INT4 quantization of w[N, K] (fp16).
+def awq_quantize(w, group_size: int = 128, channel_scale=None, out=None, symmetric: bool = False):
+    """Group-wise INT4 quantization of w[N, K] (fp16), asymmetric by default
+    (awq_quantize), symmetric with symmetric=True (awq_quantize_ex mode 1).
 
     Returns (qweight int32 [N, K/8] holding the uint32 words, scales fp16
     [N, K/G], zeros fp16 [N, K/G]). channel_scale: optional fp32 [K]."""
@@ -143,9 +147,14 @@ def awq_quantize(w, group_size: int = 128, channel_scale=None, out=None):
         zeros = torch.empty((N, ng), dtype=torch.float16, device=dev)
     else:
         qweight, scales, zeros = out
-    st = load().awq_quantize(_ptr(w), _ptr(channel_scale), N, K, group_size, _ptr(qweight),
-                             _ptr(scales), _ptr(zeros), _stream(w.device))
-    _check("awq_quantize", st)
+    if symmetric:
+        st = load().awq_quantize_ex(_ptr(w), _ptr(channel_scale), N, K, group_size, QUANT_SYMMETRIC,
+                                    _ptr(qweight), _ptr(scales), _ptr(zeros), _stream(w.device))
+        _check("awq_quantize_ex", st)
+    else:
+        st = load().awq_quantize(_ptr(w), _ptr(channel_scale), N, K, group_size, _ptr(qweight),
+                                 _ptr(scales), _ptr(zeros), _stream(w.device))
+        _check("awq_quantize", st)
     return qweight, scales, zeros
 
 

@@ -13,7 +13,7 @@ namespace {
 constexpr int64_t kMaxDim = int64_t(1) << 30;      // any single extent
 constexpr int64_t kMaxElems = int64_t(1) << 40;    // any product of extents
 
-bool valid_group(int g) { return g == 64 || g == 128; }
+bool valid_group(int g) { return g == 32 || g == 64 || g == 128 || g == 256; }
 
 awq_status check_dims(int64_t N, int64_t K, int group_size) {
     if (!valid_group(group_size)) return AWQ_ERR_CONFIG;
@@ -85,9 +85,10 @@ const char* awq_status_string(int status) {
 
 int awq_version(void) { return 100; }
 
-awq_status awq_quantize(const void* w_f16, const float* channel_scale, int64_t N, int64_t K,
-                        int group_size, uint32_t* qweight, void* scales_f16, void* zeros_f16,
-                        void* stream) {
+awq_status awq_quantize_ex(const void* w_f16, const float* channel_scale, int64_t N, int64_t K,
+                           int group_size, int mode, uint32_t* qweight, void* scales_f16, void* zeros_f16,
+                           void* stream) {
+    if (mode != AWQ_QUANT_ASYMMETRIC && mode != AWQ_QUANT_SYMMETRIC) return AWQ_ERR_CONFIG;
     awq_status st = check_dims(N, K, group_size);
     if (st != AWQ_OK) return st;
     if (N * K > kMaxElems) return AWQ_ERR_SHAPE;
@@ -97,9 +98,16 @@ awq_status awq_quantize(const void* w_f16, const float* channel_scale, int64_t N
         return AWQ_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(scales_f16) & 1) || (reinterpret_cast<uintptr_t>(zeros_f16) & 1))
         return AWQ_ERR_ALIGN;
-    return launch_quantize(static_cast<const half_t*>(w_f16), channel_scale, N, K, group_size, qweight,
-                           static_cast<half_t*>(scales_f16), static_cast<half_t*>(zeros_f16),
-                           as_stream(stream));
+    return launch_quantize(static_cast<const half_t*>(w_f16), channel_scale, N, K, group_size,
+                           mode == AWQ_QUANT_SYMMETRIC, qweight, static_cast<half_t*>(scales_f16),
+                           static_cast<half_t*>(zeros_f16), as_stream(stream));
+}
+
+awq_status awq_quantize(const void* w_f16, const float* channel_scale, int64_t N, int64_t K,
+                        int group_size, uint32_t* qweight, void* scales_f16, void* zeros_f16,
+                        void* stream) {
+    return awq_quantize_ex(w_f16, channel_scale, N, K, group_size, AWQ_QUANT_ASYMMETRIC, qweight, scales_f16,
+                           zeros_f16, stream);
 }
 
 size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -226,7 +234,8 @@ awq_status awq_scale_search(const void* w_f16, const void* x_f16, int64_t N, int
     const int64_t tiles = gemm_tile_count(T, N);
     for (int i = 0; i < n_alpha; ++i) {
         if ((st = launch_pow_scales(L.m, K, alphas[i], L.s, s)) != AWQ_OK) return st;
-        if ((st = launch_quantize(w, L.s, N, K, group_size, L.qweight, L.scales, L.zeros, s)) != AWQ_OK) return st;
+        if ((st = launch_quantize(w, L.s, N, K, group_size, false, L.qweight, L.scales, L.zeros, s)) != AWQ_OK)
+            return st;
         if ((st = launch_divide_columns(x, L.s, T, K, L.xs, s)) != AWQ_OK) return st;
         GemmArgs q;
         q.a = L.xs;

@@ -44,9 +44,10 @@ inline awq_status last_launch_status() { return hip_status(hipGetLastError()); }
 
 // ---- launchers (each returns after enqueueing on `stream`) ----
 
-// Group-wise INT4 quantization of W[N, K] (optionally times channel_scale[K]).
+// Group-wise INT4 quantization of W[N, K] (optionally times channel_scale[K]),
+// asymmetric (the group's [min, max]) or symmetric (max |w| -> +-7, zero 8).
 awq_status launch_quantize(const half_t* w, const float* channel_scale, int64_t N, int64_t K,
-                           int group_size, uint32_t* qweight, half_t* scales, half_t* zeros,
+                           int group_size, bool symmetric, uint32_t* qweight, half_t* scales, half_t* zeros,
                            hipStream_t stream);
 
 // Decode GEMV y[M, N] = x[M, K] . dequant(Wq)^T for M <= kGemvMaxM.

@@ -388,7 +388,7 @@ bool gemv_supported(int64_t M, int64_t K) {
 awq_status launch_gemv(const half_t* x, const uint32_t* qweight, const half_t* scales,
                        const half_t* zeros, int64_t M, int64_t N, int64_t K, int group_size,
                        half_t* y, hipStream_t stream) {
-    const int log2g = group_size == 128 ? 7 : 6;
+    const int log2g = 31 - __builtin_clz(static_cast<unsigned>(group_size));   // G is a power of two >= 32
     switch (M) {
         case 1: return launch_m<1>(x, qweight, scales, zeros, N, K, log2g, y, stream);
         case 2: return launch_m<2>(x, qweight, scales, zeros, N, K, log2g, y, stream);

@@ -1,9 +1,13 @@
-// Group-wise asymmetric INT4 quantization (min/max -> scale/zero -> codes -> pack).
+// Group-wise INT4 quantization (range -> scale/zero -> codes -> pack).
 //
 // The map is the one of "模型量化:GGUF/AWQ/GPTQ部署方案" §1.2 (q = clamp(round(x /
 // scale) + zero_point, 0, 15), scale from the weight range) with one scale and
 // zero-point per group of G consecutive input channels (§1.4; aissn.com
-// "量化粒度"), asymmetric (aissn.com "对称/非对称量化").
+// "量化粒度"). Asymmetric by default (aissn.com "对称/非对称量化": zero-point
+// != 0, the group's own [min, max]); the symmetric form of that section
+// (zero-point 0) maps the group's largest magnitude to +-7, s = max|w| / 7,
+// q = clamp(round(w / s), -8, 7), and stores q + 8 with zero-point 8, so the
+// same dequantization (q - z) * s serves both.
 //
 // Layout: one thread per packed word, i.e. 8 consecutive k of one row, read as
 // one 16-byte load. The G/8 threads of a group are adjacent lanes of one
@@ -18,14 +22,14 @@ namespace {
 
 #pragma clang fp contract(off)
 
-template <int G>
+template <int G, bool SYM>
 __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict__ w,
                                                        const float* __restrict__ channel_scale,
                                                        int64_t n_words, int64_t words_per_row,
                                                        uint32_t* __restrict__ qweight,
                                                        half_t* __restrict__ scales,
                                                        half_t* __restrict__ zeros) {
-    constexpr int kLanes = G / 8;  // threads per group: 8 (G=64) or 16 (G=128)
+    constexpr int kLanes = G / 8;  // threads per group: 4, 8, 16 or 32 (G = 32 .. 256)
     const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     // n_words is a multiple of kLanes and kLanes divides 64, so a group's
     // lanes are either all in range or all out of range.
@@ -59,12 +63,22 @@ __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict_
         hi = fmaxf(hi, __shfl_xor(hi, o, kLanes));
     }
 
-    const float range = fmaxf(hi - lo, kRangeFloor);
-    const float s32 = range / 15.0f;                 // IEEE divide
-    const half_t s16 = static_cast<half_t>(s32);      // round-to-nearest-even
+    float s32, z;
+    if constexpr (SYM) {
+        const float a = fmaxf(fmaxf(-lo, hi), kRangeFloor);   // max |w| (lo <= hi)
+        s32 = a / 7.0f;                                       // IEEE divide
+    } else {
+        const float range = fmaxf(hi - lo, kRangeFloor);
+        s32 = range / 15.0f;                                  // IEEE divide
+    }
+    const half_t s16 = static_cast<half_t>(s32);              // round-to-nearest-even
     const float sf = static_cast<float>(s16);
-    const int zi = static_cast<int>(fminf(fmaxf(rintf(-lo / sf), 0.0f), 15.0f));
-    const float z = static_cast<float>(zi);
+    if constexpr (SYM) {
+        z = 8.0f;
+    } else {
+        const int zi = static_cast<int>(fminf(fmaxf(rintf(-lo / sf), 0.0f), 15.0f));
+        z = static_cast<float>(zi);
+    }
 
     uint32_t packed = 0;
 #pragma unroll
@@ -80,23 +94,38 @@ __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict_
     }
 }
 
+template <int G, bool SYM>
+void launch_g(const half_t* w, const float* channel_scale, int64_t n_words, int64_t words_per_row,
+              uint32_t* qweight, half_t* scales, half_t* zeros, hipStream_t stream) {
+    const int threads = 256;
+    const int64_t blocks = ceil_div(n_words, threads);
+    hipLaunchKernelGGL((quantize_kernel<G, SYM>), dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream, w,
+                       channel_scale, n_words, words_per_row, qweight, scales, zeros);
+}
+
+template <bool SYM>
+void launch_sym(const half_t* w, const float* channel_scale, int64_t n_words, int64_t words_per_row,
+                int group_size, uint32_t* qweight, half_t* scales, half_t* zeros, hipStream_t stream) {
+    switch (group_size) {
+        case 32: launch_g<32, SYM>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, stream); break;
+        case 64: launch_g<64, SYM>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, stream); break;
+        case 128: launch_g<128, SYM>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, stream); break;
+        default: launch_g<256, SYM>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, stream); break;
+    }
+}
+
 }  // namespace
 
 awq_status launch_quantize(const half_t* w, const float* channel_scale, int64_t N, int64_t K,
-                           int group_size, uint32_t* qweight, half_t* scales, half_t* zeros,
+                           int group_size, bool symmetric, uint32_t* qweight, half_t* scales, half_t* zeros,
                            hipStream_t stream) {
     const int64_t words_per_row = K / 8;
     const int64_t n_words = N * words_per_row;
     if (n_words == 0) return AWQ_OK;
-    const int threads = 256;
-    const int64_t blocks = ceil_div(n_words, threads);
-    if (group_size == 128) {
-        hipLaunchKernelGGL(quantize_kernel<128>, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0,
-                           stream, w, channel_scale, n_words, words_per_row, qweight, scales, zeros);
-    } else {
-        hipLaunchKernelGGL(quantize_kernel<64>, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0,
-                           stream, w, channel_scale, n_words, words_per_row, qweight, scales, zeros);
-    }
+    if (symmetric)
+        launch_sym<true>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros, stream);
+    else
+        launch_sym<false>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros, stream);
     return last_launch_status();
 }
 

@@ -82,7 +82,7 @@ __device__ inline uint4 permute8(uint4 v) {
     return p;
 }
 
-// WPL packed words per lane per group: G / 32 (4 for G = 128, 2 for G = 64).
+// WPL packed words per lane per group: G / 32 (1, 2, 4, 8 for G = 32 .. 256).
 template <int WPL>
 struct GroupLoad {
     uint32_t w[2][WPL];     // two column tiles
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __r
                                                               int* __restrict__ counters) {
     constexpr int G = WPL * 32;
     constexpr int MP = 16 * MB;                          // padded rows
-    constexpr int kSkDepth = MB <= 2 ? 8 : 4;            // weight groups in flight per wave
+    constexpr int kSkDepth = (MB <= 2 && WPL <= 4) ? 8 : 4;   // weight groups in flight per wave
     extern __shared__ __attribute__((aligned(16))) half_t xs[];   // [MP][stride], then (s, z) pairs
     __shared__ int s_last;
 
@@ -150,14 +150,24 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __r
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const uint32_t wo = ok ? w_off[t] + static_cast<uint32_t>(g) * (G / 2) : w_bytes;
-            if constexpr (WPL == 4) {
+            if constexpr (WPL == 8) {
+                const u32x4 v0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 0, 0));
+                const u32x4 v1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 16, 0));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    gl.w[t][j] = v0[j];
+                    gl.w[t][4 + j] = v1[j];
+                }
+            } else if constexpr (WPL == 4) {
                 const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 0, 0));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) gl.w[t][j] = v[j];
-            } else {
+            } else if constexpr (WPL == 2) {
                 const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, wo, 0, 0));
 #pragma unroll
                 for (int j = 0; j < 2; ++j) gl.w[t][j] = v[j];
+            } else {
+                gl.w[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rw, wo, 0, 0);
             }
         }
     };
@@ -450,8 +460,12 @@ awq_status launch_skinny(const half_t* x, const uint32_t* qweight, const half_t*
     if (M == 0 || N == 0) return AWQ_OK;
     if (!skinny_supported(M, N, K, group_size, workspace != nullptr)) return AWQ_ERR_CONFIG;
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-    if (group_size == 128) return launch_wpl<4>(x, qweight, scales, zeros, m, n, k, y, workspace, stream);
-    return launch_wpl<2>(x, qweight, scales, zeros, m, n, k, y, workspace, stream);
+    switch (group_size) {
+        case 32: return launch_wpl<1>(x, qweight, scales, zeros, m, n, k, y, workspace, stream);
+        case 64: return launch_wpl<2>(x, qweight, scales, zeros, m, n, k, y, workspace, stream);
+        case 128: return launch_wpl<4>(x, qweight, scales, zeros, m, n, k, y, workspace, stream);
+        default: return launch_wpl<8>(x, qweight, scales, zeros, m, n, k, y, workspace, stream);
+    }
 }
 
 }  // namespace awq
