@@ -15,6 +15,12 @@ from .awq_oracle import (  # noqa: F401
     group_quantize,
     group_quantize_symmetric,
     quantize_symmetric,
+    clip_position,
+    clip_bounds,
+    group_quantize_clipped,
+    quantize_clipped,
+    clipped_weight,
+    clip_search,
     pack_codes,
     unpack_codes,
     quantize,

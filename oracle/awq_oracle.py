@@ -99,6 +99,77 @@ def group_quantize(w, group_size: int, channel_scale=None):
     return codes, s16, z.astype(np.float16)
 
 
+def clip_position(group_size: int, clip_fraction: float):
+    """Order-statistic position of the clip quantile: h = (G - 1) * p in
+    float64, split into the integer i = floor(h) and the fraction
+    f = float32(h - i). Positions past the middle of a group are refused."""
+    if not (0.0 <= clip_fraction < 0.25):
+        raise ValueError("clip_fraction must lie in [0, 0.25)")
+    h = (group_size - 1) * float(clip_fraction)
+    i = int(np.floor(h))
+    return i, np.float32(h - i)
+
+
+def clip_bounds(wg, group_size: int, clip_fraction: float):
+    """The clip step of [P5 §1.5]: cut the extreme p of each group's values
+    at both ends before the scale is taken (p = 1 % on the page).
+
+    Reading: the bounds are the p and 1 - p quantiles of the group's G
+    float32 values, linearly interpolated between order statistics (the
+    usual percentile definition, NumPy's default method), with the lower one
+    taken from the bottom and the upper one mirrored from the top, in this
+    exact float32 order (no fused multiply-add):
+      lo = x(i) + f * (x(i+1) - x(i))
+      hi = x(G-1-i) - f * (x(G-1-i) - x(G-2-i))
+    where x(0) <= ... <= x(G-1) are the sorted values and (i, f) come from
+    clip_position. p = 0 gives lo = min, hi = max exactly.
+
+    wg: float32 [N, groups, G] -> (lo, hi) float32 [N, groups]."""
+    i, f = clip_position(group_size, clip_fraction)
+    xs = np.sort(wg, axis=2)
+    a0, a1 = xs[:, :, i], xs[:, :, i + 1]
+    b0, b1 = xs[:, :, group_size - 1 - i], xs[:, :, group_size - 2 - i]
+    lo = a0 + f * (a1 - a0)
+    hi = b0 - f * (b0 - b1)
+    return lo.astype(np.float32), hi.astype(np.float32)
+
+
+def group_quantize_clipped(w, group_size: int, clip_fraction: float, channel_scale=None,
+                           symmetric: bool = False):
+    """Group-wise INT4 quantization after the clip step of [P5 §1.5]: the
+    scale and zero-point come from the clipped bounds (lo, hi) instead of
+    the group's min and max; values beyond them take the clamped codes 0 or
+    15 (that is the clipping). Asymmetric: range = hi - lo, zero from lo, as
+    in group_quantize. Symmetric: a = max(-lo, hi), as in
+    group_quantize_symmetric. clip_fraction = 0 reproduces both exactly."""
+    w32 = np.asarray(w).astype(np.float32)
+    N, K = w32.shape
+    _check_groups(K, group_size)
+    if channel_scale is not None:
+        cs = np.asarray(channel_scale, dtype=np.float32).reshape(1, K)
+        w32 = w32 * cs
+    wg = w32.reshape(N, K // group_size, group_size)
+    lo, hi = clip_bounds(wg, group_size, clip_fraction)
+    if symmetric:
+        a = np.maximum(np.maximum(-lo, hi), RANGE_FLOOR)
+        s16 = (a / np.float32(SYM_QMAX)).astype(np.float16)
+        sf = s16.astype(np.float32)
+        z = np.full(s16.shape, SYM_ZERO, dtype=np.float32)
+    else:
+        rng = np.maximum(hi - lo, RANGE_FLOOR)
+        s16 = (rng / np.float32(QMAX)).astype(np.float16)
+        sf = s16.astype(np.float32)
+        z = np.clip(np.rint(-lo / sf), 0, QMAX).astype(np.int32).astype(np.float32)
+    q = np.rint(wg / sf[:, :, None]) + z[:, :, None]
+    q = np.clip(q, 0, QMAX)
+    return q.reshape(N, K).astype(np.uint8), s16, z.astype(np.float16)
+
+
+def quantize_clipped(w, group_size: int, clip_fraction: float, channel_scale=None, symmetric: bool = False):
+    codes, s16, z16 = group_quantize_clipped(w, group_size, clip_fraction, channel_scale, symmetric)
+    return pack_codes(codes), s16, z16
+
+
 SYM_QMAX = 7                    # 2^(bits-1) - 1: the largest signed code used
 SYM_ZERO = 8                    # stored zero-point of the symmetric form
 
@@ -274,3 +345,34 @@ def scale_search(w, x, group_size: int, alphas=None, use_gram: bool = True):
             losses[i] = search_loss_direct(w, x, s32, group_size)
     best = int(np.argmin(losses))   # np.argmin returns the first minimum
     return losses, best, channel_scales(m, alphas[best])
+
+
+def clipped_weight(w, group_size: int, clip_fraction: float, s32=None) -> np.ndarray:
+    """W_hat_p = dequant(Q_p(W . diag(s))) / s in float64 [N, K], with Q_p
+    the clipped quantizer (s = 1 when s32 is None)."""
+    w = np.asarray(w)
+    K = w.shape[1]
+    qw, sc, zr = quantize_clipped(w, group_size, clip_fraction, channel_scale=s32)
+    w_hat = dequantize(qw, sc, zr, group_size, K)
+    if s32 is not None:
+        w_hat = w_hat / np.asarray(s32, np.float64)[None, :]
+    return w_hat
+
+
+def clip_search(w, x, group_size: int, fractions, s32=None, use_gram: bool = True):
+    """Search of the clip fraction p of [P5 §1.5] over a grid, by the same
+    output loss as the scale search: for each p,
+      L(p) = || Q_p(W diag(s)) (X / s)^T - W X^T ||_F^2
+    (s = 1 without channel scales). Returns (losses float64 [n], first index
+    of the minimum)."""
+    g = gram(x) if use_gram else None
+    w64 = np.asarray(w).astype(np.float64)
+    losses = np.empty(len(fractions), dtype=np.float64)
+    for i, p in enumerate(fractions):
+        d = clipped_weight(w, group_size, p, s32) - w64
+        if use_gram:
+            losses[i] = float(np.sum((d @ g) * d))
+        else:
+            e = np.asarray(x).astype(np.float64) @ d.T
+            losses[i] = float(np.sum(e * e))
+    return losses, int(np.argmin(losses))
