@@ -49,6 +49,8 @@ F16_MFMA_PEAK_TFLOPS = 2500.0
 G = 128
 ROOFLINE_SHAPE = (11008, 4096)     # gate/up projection, the step's largest launch
 COPY_BYTES = 1 << 30
+CLIP_BENCH_FRACTION = 0.01                                # the clip of xxmr.cn §1.5
+CLIP_GRID = [0.0, 0.001, 0.002, 0.005, 0.01, 0.02]       # clip-search fractions
 
 
 def gemv_bytes(M, N, K, g=G):
@@ -391,8 +393,18 @@ class Bench:
         tq = self.time(q, 50) / 50
         gbs = quantize_bytes(N, K) / tq / 1e9
         log(f"quantize {N}x{K}: {tq * 1e6:.1f} us, {gbs:.0f} GB/s")
+
+        def qc(i):
+            self.awq.awq_quantize(w16, G, out=outs, clip_fraction=CLIP_BENCH_FRACTION)
+
+        for i in range(5):
+            qc(i)
+        tc = self.time(qc, 50) / 50
+        log(f"clipped quantize {N}x{K} (p={CLIP_BENCH_FRACTION}): {tc * 1e6:.1f} us")
         return {"shape": f"{N}x{K}", "us": round(tq * 1e6, 2), "GB/s": round(gbs, 1),
-                "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+                "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "clipped": {"clip_fraction": CLIP_BENCH_FRACTION, "us": round(tc * 1e6, 2),
+                            "GB/s": round(quantize_bytes(N, K) / tc / 1e9, 1)}}
 
     # ------------------------------------------------------------ scale search
     def run_search(self):
@@ -406,13 +418,37 @@ class Bench:
         awq.awq_scale_search(ws, xs, G, workspace=wsp)   # warm-up
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        _, best, _ = awq.awq_scale_search(ws, xs, G, workspace=wsp)
+        _, best, best_s = awq.awq_scale_search(ws, xs, G, workspace=wsp)
         ts = time.perf_counter() - t0
         flop = 21 * 2.0 * xs.shape[0] * ws.shape[0] * ws.shape[1]
         log(f"scale search: {ts * 1e3:.1f} ms, alpha* = {best / 20}")
-        return {"ms": round(ts * 1e3, 2), "best_alpha": best / 20, "TFLOP/s": round(flop / ts / 1e12, 1),
-                "frac_of_f16_peak": round(flop / ts / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
-                "workload": "W[11008,4096], X[65536,4096], 20 alphas, G=128 (21 GEMMs)"}
+        out = {"ms": round(ts * 1e3, 2), "best_alpha": best / 20, "TFLOP/s": round(flop / ts / 1e12, 1),
+               "frac_of_f16_peak": round(flop / ts / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
+               "workload": "W[11008,4096], X[65536,4096], 20 alphas, G=128 (21 GEMMs)"}
+        del wsp
+        out["clip_search"] = self.run_clip_search(ws, xs, best_s)
+        return out
+
+    def run_clip_search(self, ws, xs, s):
+        """The clip search after the scale search: W diag(s) at the chosen
+        scales s, X / s, one reference GEMM and one quantize + loss GEMM per
+        fraction."""
+        torch, awq = self.torch, self.awq
+        N, K, T = ws.shape[0], ws.shape[1], xs.shape[0]
+        n = len(CLIP_GRID)
+        nb = awq.load().awq_clip_search_workspace_bytes(N, K, T, G, n, 1)
+        wsp = torch.empty(nb, dtype=torch.uint8, device=self.dev)
+        awq.awq_clip_search(ws, xs, CLIP_GRID, G, channel_scale=s, workspace=wsp)   # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        losses, best = awq.awq_clip_search(ws, xs, CLIP_GRID, G, channel_scale=s, workspace=wsp)
+        tc = time.perf_counter() - t0
+        flop = (n + 1) * 2.0 * T * N * K
+        log(f"clip search: {tc * 1e3:.1f} ms, p* = {CLIP_GRID[best]}")
+        return {"ms": round(tc * 1e3, 2), "fractions": CLIP_GRID, "best_fraction": CLIP_GRID[best],
+                "loss_ratio_best_to_unclipped": round(float(losses[best] / losses[0]), 6),
+                "TFLOP/s": round(flop / tc / 1e12, 1),
+                "workload": f"W[{N},{K}] diag(s), X[{T},{K}] / s, {n} fractions, G=128 ({n + 1} GEMMs)"}
 
     # ------------------------------------------------------------ HBM copy
     def run_copy(self):

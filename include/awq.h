@@ -94,7 +94,7 @@ awq_status awq_quantize(const void* w_f16, const float* channel_scale,
  * (aissn.com 对称/非对称量化: asymmetric allows a zero-point != 0;
  * symmetric has zero-point 0, simple and hardware friendly).
  *
- *   mode AWQ_QUANT_ASYMMETRIC (0): exactly awq_quantize.
+ *   mode AWQ_QUANT_ASYMMETRIC (0): as awq_quantize.
  *   mode AWQ_QUANT_SYMMETRIC (1): per row n and group g, in IEEE float32,
  *     a     = max(max |w'|, 1e-5)
  *     scale = fp16_rne(a / 7)                  (stored in scales[n, g])
@@ -102,14 +102,25 @@ awq_status awq_quantize(const void* w_f16, const float* channel_scale,
  *   i.e. the signed code q = code - 8 = rint(w' / scale) lies in -7..7 and
  *   q(-w) = -q(w). The stored layout is the asymmetric one, so awq_gemm and
  *   the other linear-layer calls apply unchanged.
- * Any other mode returns AWQ_ERR_CONFIG. Arguments otherwise as
- * awq_quantize.
+ *
+ *   clip_fraction p in [0, 0.25): the clip step of xxmr.cn §1.5 (cut the
+ *   extreme p of each group's values at both ends before the scale is
+ *   taken; the page uses 1 %). The group's min and max above are replaced
+ *   by the p and 1 - p quantiles, interpolated between its order statistics
+ *   x(0) <= ... <= x(G-1): with h = (G - 1) p in double, i = floor(h),
+ *   f = float(h - i), in float32 without fused multiply-adds,
+ *     lo = x(i) + f (x(i+1) - x(i)),  hi = x(G-1-i) - f (x(G-1-i) - x(G-2-i))
+ *   (asymmetric: range = hi - lo, zero from lo; symmetric: a = max(-lo,
+ *   hi)). Values beyond the bounds take the clamped codes. p = 0 is the
+ *   plain map, bit for bit.
+ * Any other mode or clip_fraction returns AWQ_ERR_CONFIG. Arguments
+ * otherwise as awq_quantize.
  */
 enum { AWQ_QUANT_ASYMMETRIC = 0, AWQ_QUANT_SYMMETRIC = 1 };
 awq_status awq_quantize_ex(const void* w_f16, const float* channel_scale,
                            int64_t N, int64_t K, int group_size, int mode,
-                           uint32_t* qweight, void* scales_f16, void* zeros_f16,
-                           void* stream);
+                           double clip_fraction, uint32_t* qweight,
+                           void* scales_f16, void* zeros_f16, void* stream);
 
 /*
  * awq_gemm - the W4A16 linear layer y = x . dequant(Wq)^T.
@@ -229,6 +240,43 @@ awq_status awq_scale_search(const void* w_f16, const void* x_f16,
                             void* workspace, size_t workspace_bytes,
                             double* losses, int* best_index,
                             float* best_scales, void* stream);
+
+/*
+ * awq_clip_search - the clip fraction of xxmr.cn §1.5, chosen by the scale
+ * search's own objective (rskf.cn §2.1: the difference between the
+ * quantized and the original output) over a caller-given grid.
+ *
+ * For every fraction p_i, with s = channel_scale (1 when NULL):
+ *   loss_i = || Q_p(W . diag(s)) . (x / s)^T  -  W . x^T ||_F^2
+ * where Q_p is awq_quantize_ex(mode, clip_fraction = p_i) with that channel
+ * scale, and the products are the library's W4A16 GEMM and fp16 MFMA
+ * reference (fp32 accumulation, fp64 loss sum). The best index is the first
+ * minimum (ties go to the earlier fraction).
+ *
+ *   w_f16, x_f16   device, fp16 [N, K] and [T, K]
+ *   channel_scale  device, fp32 [K] (e.g. awq_scale_search's best_scales)
+ *                  or NULL
+ *   N, K, T        N > 0, T > 0, K > 0, K % group_size == 0
+ *   group_size     32, 64, 128 or 256
+ *   mode           AWQ_QUANT_ASYMMETRIC or AWQ_QUANT_SYMMETRIC
+ *   fractions      host, double [n_fractions], each in [0, 0.25);
+ *                  1 <= n_fractions <= 64
+ *   workspace, workspace_bytes  device scratch of at least
+ *                  awq_clip_search_workspace_bytes(N, K, T, group_size,
+ *                  n_fractions, channel_scale != NULL) bytes, 16-byte aligned
+ *   losses         host, double [n_fractions] (output)
+ *   best_index     host (output)
+ * Synchronises `stream` once, to read the losses back.
+ */
+size_t awq_clip_search_workspace_bytes(int64_t N, int64_t K, int64_t T,
+                                        int group_size, int n_fractions,
+                                        int scaled);
+awq_status awq_clip_search(const void* w_f16, const void* x_f16,
+                           const float* channel_scale, int64_t N, int64_t K,
+                           int64_t T, int group_size, int mode,
+                           const double* fractions, int n_fractions,
+                           void* workspace, size_t workspace_bytes,
+                           double* losses, int* best_index, void* stream);
 
 #ifdef __cplusplus
 }

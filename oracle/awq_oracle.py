@@ -347,29 +347,29 @@ def scale_search(w, x, group_size: int, alphas=None, use_gram: bool = True):
     return losses, best, channel_scales(m, alphas[best])
 
 
-def clipped_weight(w, group_size: int, clip_fraction: float, s32=None) -> np.ndarray:
+def clipped_weight(w, group_size: int, clip_fraction: float, s32=None, symmetric: bool = False) -> np.ndarray:
     """W_hat_p = dequant(Q_p(W . diag(s))) / s in float64 [N, K], with Q_p
-    the clipped quantizer (s = 1 when s32 is None)."""
+    the clipped quantizer, asymmetric or symmetric (s = 1 when s32 is None)."""
     w = np.asarray(w)
     K = w.shape[1]
-    qw, sc, zr = quantize_clipped(w, group_size, clip_fraction, channel_scale=s32)
+    qw, sc, zr = quantize_clipped(w, group_size, clip_fraction, channel_scale=s32, symmetric=symmetric)
     w_hat = dequantize(qw, sc, zr, group_size, K)
     if s32 is not None:
         w_hat = w_hat / np.asarray(s32, np.float64)[None, :]
     return w_hat
 
 
-def clip_search(w, x, group_size: int, fractions, s32=None, use_gram: bool = True):
+def clip_search(w, x, group_size: int, fractions, s32=None, use_gram: bool = True, symmetric: bool = False):
     """Search of the clip fraction p of [P5 §1.5] over a grid, by the same
     output loss as the scale search: for each p,
       L(p) = || Q_p(W diag(s)) (X / s)^T - W X^T ||_F^2
-    (s = 1 without channel scales). Returns (losses float64 [n], first index
-    of the minimum)."""
+    (s = 1 without channel scales; Q_p asymmetric or symmetric). Returns
+    (losses float64 [n], first index of the minimum)."""
     g = gram(x) if use_gram else None
     w64 = np.asarray(w).astype(np.float64)
     losses = np.empty(len(fractions), dtype=np.float64)
     for i, p in enumerate(fractions):
-        d = clipped_weight(w, group_size, p, s32) - w64
+        d = clipped_weight(w, group_size, p, s32, symmetric) - w64
         if use_gram:
             losses[i] = float(np.sum((d @ g) * d))
         else:

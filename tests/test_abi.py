@@ -64,13 +64,40 @@ def test_quantize_shape_checks(L, N, K, G, expect):
 
 def test_quantize_ex_checks(L):
     q = L.awq_quantize_ex
-    assert q(FAKE, None, 16, 128, 64, 2, FAKE, FAKE, FAKE, None) == CONFIG     # unknown mode
-    assert q(FAKE, None, 16, 128, 64, -1, FAKE, FAKE, FAKE, None) == CONFIG
-    assert q(FAKE, None, 16, 128, 16, 1, FAKE, FAKE, FAKE, None) == CONFIG     # group size
-    assert q(FAKE, None, 16, 100, 64, 1, FAKE, FAKE, FAKE, None) == SHAPE
-    assert q(FAKE, None, 0, 128, 64, 1, FAKE, FAKE, FAKE, None) == OK          # empty N
-    assert q(None, None, 16, 128, 64, 1, FAKE, FAKE, FAKE, None) == NULL
-    assert q(FAKE_ODD, None, 16, 128, 64, 1, FAKE, FAKE, FAKE, None) == ALIGN
+    assert q(FAKE, None, 16, 128, 64, 2, 0.0, FAKE, FAKE, FAKE, None) == CONFIG     # unknown mode
+    assert q(FAKE, None, 16, 128, 64, -1, 0.0, FAKE, FAKE, FAKE, None) == CONFIG
+    assert q(FAKE, None, 16, 128, 64, 0, 0.25, FAKE, FAKE, FAKE, None) == CONFIG    # clip in [0, 0.25)
+    assert q(FAKE, None, 16, 128, 64, 0, -0.01, FAKE, FAKE, FAKE, None) == CONFIG
+    assert q(FAKE, None, 16, 128, 64, 1, float("nan"), FAKE, FAKE, FAKE, None) == CONFIG
+    assert q(FAKE, None, 16, 128, 16, 1, 0.0, FAKE, FAKE, FAKE, None) == CONFIG     # group size
+    assert q(FAKE, None, 16, 100, 64, 1, 0.01, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(FAKE, None, 0, 128, 64, 1, 0.01, FAKE, FAKE, FAKE, None) == OK         # empty N
+    assert q(None, None, 16, 128, 64, 1, 0.0, FAKE, FAKE, FAKE, None) == NULL
+    assert q(FAKE_ODD, None, 16, 128, 64, 1, 0.0, FAKE, FAKE, FAKE, None) == ALIGN
+
+
+def test_clip_search_checks(L):
+    fr = np.array([0.0, 0.01], dtype=np.float64)
+    f = fr.ctypes.data_as(ctypes.c_void_p)
+    losses = np.zeros(2)
+    lp = losses.ctypes.data_as(ctypes.c_void_p)
+    best = ctypes.c_int(-1)
+    bp = ctypes.addressof(best)
+    need = L.awq_clip_search_workspace_bytes(256, 512, 1024, 128, 2, 0)
+    need_s = L.awq_clip_search_workspace_bytes(256, 512, 1024, 128, 2, 1)
+    assert need >= 1024 * 256 * 4 + 256 * 512 // 2 and need_s >= need + 1024 * 512 * 2
+    assert L.awq_clip_search_workspace_bytes(256, 500, 1024, 128, 2, 0) == 0
+    c = L.awq_clip_search
+    assert c(FAKE, FAKE, None, 256, 512, 1024, 128, 0, f, 2, FAKE, need - 256, lp, bp, None) == WORKSPACE
+    assert c(FAKE, FAKE, FAKE, 256, 512, 1024, 128, 0, f, 2, FAKE, need, lp, bp, None) == WORKSPACE  # scaled needs x/s
+    assert c(FAKE, FAKE, None, 256, 512, 1024, 128, 3, f, 2, FAKE, need, lp, bp, None) == CONFIG
+    assert c(FAKE, FAKE, None, 256, 512, 1024, 128, 0, f, 0, FAKE, need, lp, bp, None) == CONFIG
+    bad = np.array([0.0, 0.3])
+    assert c(FAKE, FAKE, None, 256, 512, 1024, 128, 0, bad.ctypes.data_as(ctypes.c_void_p), 2, FAKE, need, lp, bp,
+             None) == CONFIG
+    assert c(FAKE, FAKE, None, 256, 512, 0, 128, 0, f, 2, FAKE, need, lp, bp, None) == SHAPE
+    assert c(FAKE, None, None, 256, 512, 1024, 128, 0, f, 2, FAKE, need, lp, bp, None) == NULL
+    assert c(FAKE, FAKE, FAKE_ODD, 256, 512, 1024, 128, 0, f, 2, FAKE, need_s, lp, bp, None) == ALIGN
 
 
 def test_quantize_null_and_alignment(L):

@@ -90,3 +90,18 @@ def test_clip_search_with_channel_scales_matches_scaled_loss():
     lc, _ = oracle.clip_search(lay["w"], lay["x"], 128, [0.0], s32=s32)
     ls = oracle.search_loss_gram(lay["w"], oracle.gram(lay["x"]), s32, 128)
     assert lc[0] == pytest.approx(ls, rel=1e-12)
+
+
+def test_symmetric_clip_search_at_zero_is_the_symmetric_loss():
+    """The symmetric search at p = 0 scores the plain symmetric quantizer:
+    its loss is || X (dequant(Q_sym(W)) - W)^T ||_F^2 computed directly, and
+    a nonzero clip changes the loss."""
+    lay = synth.make_layer(64, 256, 256, seed=[165], w_std=0.02, salient_frac=0.01)
+    w, x = lay["w"], lay["x"]
+    lc, _ = oracle.clip_search(w, x, 128, [0.0, 0.02], symmetric=True)
+    qw, sc, zr = oracle.quantize_symmetric(w, 128)
+    d = oracle.dequantize(qw, sc, zr, 128, 256) - np.asarray(w, np.float64)
+    e = np.asarray(x, np.float64) @ d.T
+    assert lc[0] == pytest.approx(float(np.sum(e * e)), rel=1e-10)
+    la, _ = oracle.clip_search(w, x, 128, [0.0])
+    assert lc[0] != la[0] and lc[1] != lc[0]

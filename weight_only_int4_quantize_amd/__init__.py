@@ -62,7 +62,12 @@ def load() -> ctypes.CDLL:
     L.awq_quantize.restype = c_int
     L.awq_quantize.argtypes = [c_vp, c_vp, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp]
     L.awq_quantize_ex.restype = c_int
-    L.awq_quantize_ex.argtypes = [c_vp, c_vp, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp]
+    L.awq_quantize_ex.argtypes = [c_vp, c_vp, c_i64, c_i64, c_int, c_int, ctypes.c_double, c_vp, c_vp, c_vp, c_vp]
+    L.awq_clip_search_workspace_bytes.restype = c_sz
+    L.awq_clip_search_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int]
+    L.awq_clip_search.restype = c_int
+    L.awq_clip_search.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_int, c_vp, c_sz,
+                                  c_vp, c_vp, c_vp]
     L.awq_gemm.restype = c_int
     L.awq_gemm.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_vp]
     L.awq_gemm_path.restype = c_int
@@ -124,9 +129,11 @@ def _need_gpu(name: str, t, dtype=None) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
-def awq_quantize(w, group_size: int = 128, channel_scale=None, out=None, symmetric: bool = False):
+def awq_quantize(w, group_size: int = 128, channel_scale=None, out=None, symmetric: bool = False,
+                 clip_fraction: float = 0.0):
     """Group-wise INT4 quantization of w[N, K] (fp16), asymmetric by default
-    (awq_quantize), symmetric with symmetric=True (awq_quantize_ex mode 1).
+    (awq_quantize); symmetric=True or clip_fraction > 0 go to
+    awq_quantize_ex (symmetric map; percentile clip of each group).
 
     Returns (qweight int32 [N, K/8] holding the uint32 words, scales fp16
     [N, K/G], zeros fp16 [N, K/G]). channel_scale: optional fp32 [K]."""
@@ -147,8 +154,9 @@ def awq_quantize(w, group_size: int = 128, channel_scale=None, out=None, symmetr
         zeros = torch.empty((N, ng), dtype=torch.float16, device=dev)
     else:
         qweight, scales, zeros = out
-    if symmetric:
-        st = load().awq_quantize_ex(_ptr(w), _ptr(channel_scale), N, K, group_size, QUANT_SYMMETRIC,
+    if symmetric or clip_fraction != 0.0:
+        mode = QUANT_SYMMETRIC if symmetric else QUANT_ASYMMETRIC
+        st = load().awq_quantize_ex(_ptr(w), _ptr(channel_scale), N, K, group_size, mode, float(clip_fraction),
                                     _ptr(qweight), _ptr(scales), _ptr(zeros), _stream(w.device))
         _check("awq_quantize_ex", st)
     else:
@@ -257,3 +265,31 @@ def awq_scale_search(w, x, group_size: int = 128, alphas=None, workspace=None):
                             _ptr(best_scales), _stream(w.device))
     _check("awq_scale_search", st)
     return losses, int(best.value), best_scales
+
+
+def awq_clip_search(w, x, fractions, group_size: int = 128, channel_scale=None, symmetric: bool = False,
+                    workspace=None):
+    """Clip-fraction search (awq_clip_search). Returns (losses: numpy float64
+    [n], best_index: int)."""
+    import numpy as np
+    torch = _torch()
+    _need_gpu("w", w, torch.float16)
+    _need_gpu("x", x, torch.float16)
+    if channel_scale is not None:
+        _need_gpu("channel_scale", channel_scale, torch.float32)
+    N, K = w.shape
+    T = x.shape[0]
+    fr = np.ascontiguousarray(fractions, dtype=np.float64)
+    n = int(fr.size)
+    L = load()
+    nbytes = L.awq_clip_search_workspace_bytes(N, K, T, group_size, n, int(channel_scale is not None))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=w.device)
+    losses = np.zeros(n, dtype=np.float64)
+    best = ctypes.c_int(-1)
+    mode = QUANT_SYMMETRIC if symmetric else QUANT_ASYMMETRIC
+    st = L.awq_clip_search(_ptr(w), _ptr(x), _ptr(channel_scale), N, K, T, group_size, mode,
+                           fr.ctypes.data_as(ctypes.c_void_p), n, _ptr(workspace), workspace.numel(),
+                           losses.ctypes.data_as(ctypes.c_void_p), ctypes.addressof(best), _stream(w.device))
+    _check("awq_clip_search", st)
+    return losses, int(best.value)

@@ -66,6 +66,65 @@ struct SearchLayout {
     }
 };
 
+// Lays out the clip-search workspace; with base == nullptr it only sizes it.
+struct ClipLayout {
+    uint32_t* qweight = nullptr;
+    half_t* scales = nullptr;
+    half_t* zeros = nullptr;
+    half_t* xs = nullptr;           // x / s, only with channel scales
+    float* yref = nullptr;
+    double* tile_partials = nullptr;
+    double* losses = nullptr;
+    size_t bytes = 0;
+
+    ClipLayout(void* base, int64_t N, int64_t K, int64_t T, int G, int n, bool scaled) {
+        Carve c(base);
+        qweight = c.take<uint32_t>(static_cast<size_t>(N) * (K / 8));
+        scales = c.take<half_t>(static_cast<size_t>(N) * (K / G));
+        zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
+        if (scaled) xs = c.take<half_t>(static_cast<size_t>(T) * K);
+        yref = c.take<float>(static_cast<size_t>(T) * N);
+        tile_partials = c.take<double>(gemm_tile_count(T, N));
+        losses = c.take<double>(n);
+        bytes = c.used;
+    }
+};
+
+// Y = x . W^T in fp32 (fp16 MFMA, fp32 accumulation), the unquantized
+// reference of both searches.
+awq_status reference_output(const half_t* x, const half_t* w, int64_t T, int64_t N, int64_t K, int G, float* y,
+                            hipStream_t s) {
+    GemmArgs ref;
+    ref.a = x;
+    ref.w = w;
+    ref.group_size = G;
+    ref.M = T;
+    ref.N = N;
+    ref.K = K;
+    ref.y32 = y;
+    return launch_gemm(ref, GemmB::kF16, GemmOut::kF32, s);
+}
+
+// loss_out = || x' . dequant(Wq)^T - yref ||_F^2 (fused epilogue + fixed-order sum)
+awq_status output_loss(const half_t* xa, const uint32_t* qw, const half_t* sc, const half_t* zr, int64_t T,
+                       int64_t N, int64_t K, int G, const float* yref, double* partials, double* loss_out,
+                       hipStream_t s) {
+    GemmArgs q;
+    q.a = xa;
+    q.qweight = qw;
+    q.scales = sc;
+    q.zeros = zr;
+    q.group_size = G;
+    q.M = T;
+    q.N = N;
+    q.K = K;
+    q.yref = yref;
+    q.partials = partials;
+    awq_status st = launch_gemm(q, GemmB::kInt4, GemmOut::kLoss, s);
+    if (st != AWQ_OK) return st;
+    return launch_sum_partials(partials, gemm_tile_count(T, N), loss_out, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -86,9 +145,10 @@ const char* awq_status_string(int status) {
 int awq_version(void) { return 100; }
 
 awq_status awq_quantize_ex(const void* w_f16, const float* channel_scale, int64_t N, int64_t K,
-                           int group_size, int mode, uint32_t* qweight, void* scales_f16, void* zeros_f16,
-                           void* stream) {
+                           int group_size, int mode, double clip_fraction, uint32_t* qweight, void* scales_f16,
+                           void* zeros_f16, void* stream) {
     if (mode != AWQ_QUANT_ASYMMETRIC && mode != AWQ_QUANT_SYMMETRIC) return AWQ_ERR_CONFIG;
+    if (!clip_fraction_ok(clip_fraction)) return AWQ_ERR_CONFIG;
     awq_status st = check_dims(N, K, group_size);
     if (st != AWQ_OK) return st;
     if (N * K > kMaxElems) return AWQ_ERR_SHAPE;
@@ -99,15 +159,15 @@ awq_status awq_quantize_ex(const void* w_f16, const float* channel_scale, int64_
     if ((reinterpret_cast<uintptr_t>(scales_f16) & 1) || (reinterpret_cast<uintptr_t>(zeros_f16) & 1))
         return AWQ_ERR_ALIGN;
     return launch_quantize(static_cast<const half_t*>(w_f16), channel_scale, N, K, group_size,
-                           mode == AWQ_QUANT_SYMMETRIC, qweight, static_cast<half_t*>(scales_f16),
+                           mode == AWQ_QUANT_SYMMETRIC, clip_fraction, qweight, static_cast<half_t*>(scales_f16),
                            static_cast<half_t*>(zeros_f16), as_stream(stream));
 }
 
 awq_status awq_quantize(const void* w_f16, const float* channel_scale, int64_t N, int64_t K,
                         int group_size, uint32_t* qweight, void* scales_f16, void* zeros_f16,
                         void* stream) {
-    return awq_quantize_ex(w_f16, channel_scale, N, K, group_size, AWQ_QUANT_ASYMMETRIC, qweight, scales_f16,
-                           zeros_f16, stream);
+    return awq_quantize_ex(w_f16, channel_scale, N, K, group_size, AWQ_QUANT_ASYMMETRIC, 0.0, qweight,
+                           scales_f16, zeros_f16, stream);
 }
 
 size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -221,35 +281,16 @@ awq_status awq_scale_search(const void* w_f16, const void* x_f16, int64_t N, int
     // m = mean |x| per input channel
     if ((st = launch_absmean(x, T, K, L.m, L.abs_partials, s)) != AWQ_OK) return st;
     // reference output W . x^T, once, in fp32
-    GemmArgs ref;
-    ref.a = x;
-    ref.w = w;
-    ref.group_size = group_size;
-    ref.M = T;
-    ref.N = N;
-    ref.K = K;
-    ref.y32 = L.yref;
-    if ((st = launch_gemm(ref, GemmB::kF16, GemmOut::kF32, s)) != AWQ_OK) return st;
-
-    const int64_t tiles = gemm_tile_count(T, N);
+    if ((st = reference_output(x, w, T, N, K, group_size, L.yref, s)) != AWQ_OK) return st;
     for (int i = 0; i < n_alpha; ++i) {
         if ((st = launch_pow_scales(L.m, K, alphas[i], L.s, s)) != AWQ_OK) return st;
-        if ((st = launch_quantize(w, L.s, N, K, group_size, false, L.qweight, L.scales, L.zeros, s)) != AWQ_OK)
+        if ((st = launch_quantize(w, L.s, N, K, group_size, false, 0.0, L.qweight, L.scales, L.zeros, s)) !=
+            AWQ_OK)
             return st;
         if ((st = launch_divide_columns(x, L.s, T, K, L.xs, s)) != AWQ_OK) return st;
-        GemmArgs q;
-        q.a = L.xs;
-        q.qweight = L.qweight;
-        q.scales = L.scales;
-        q.zeros = L.zeros;
-        q.group_size = group_size;
-        q.M = T;
-        q.N = N;
-        q.K = K;
-        q.yref = L.yref;
-        q.partials = L.tile_partials;
-        if ((st = launch_gemm(q, GemmB::kInt4, GemmOut::kLoss, s)) != AWQ_OK) return st;
-        if ((st = launch_sum_partials(L.tile_partials, tiles, L.losses + i, s)) != AWQ_OK) return st;
+        if ((st = output_loss(L.xs, L.qweight, L.scales, L.zeros, T, N, K, group_size, L.yref, L.tile_partials,
+                              L.losses + i, s)) != AWQ_OK)
+            return st;
     }
     if (hipMemcpyAsync(losses, L.losses, sizeof(double) * n_alpha, hipMemcpyDeviceToHost, s) != hipSuccess)
         return AWQ_ERR_HIP;
@@ -259,6 +300,58 @@ awq_status awq_scale_search(const void* w_f16, const void* x_f16, int64_t N, int
         if (losses[i] < losses[best]) best = i;   // strict: ties keep the smaller alpha
     *best_index = best;
     if ((st = launch_pow_scales(L.m, K, alphas[best], best_scales, s)) != AWQ_OK) return st;
+    return AWQ_OK;
+}
+
+size_t awq_clip_search_workspace_bytes(int64_t N, int64_t K, int64_t T, int group_size, int n_fractions,
+                                        int scaled) {
+    if (check_dims(N, K, group_size) != AWQ_OK || N <= 0 || T <= 0 || n_fractions < 1) return 0;
+    return ClipLayout(nullptr, N, K, T, group_size, n_fractions, scaled != 0).bytes;
+}
+
+awq_status awq_clip_search(const void* w_f16, const void* x_f16, const float* channel_scale, int64_t N, int64_t K,
+                           int64_t T, int group_size, int mode, const double* fractions, int n_fractions,
+                           void* workspace, size_t workspace_bytes, double* losses, int* best_index,
+                           void* stream) {
+    awq_status st = check_dims(N, K, group_size);
+    if (st != AWQ_OK) return st;
+    if (N <= 0 || T <= 0 || T > (int64_t(1) << 24)) return AWQ_ERR_SHAPE;
+    if (T > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return AWQ_ERR_SHAPE;
+    if (mode != AWQ_QUANT_ASYMMETRIC && mode != AWQ_QUANT_SYMMETRIC) return AWQ_ERR_CONFIG;
+    if (n_fractions < 1 || n_fractions > 64) return AWQ_ERR_CONFIG;
+    if (!w_f16 || !x_f16 || !fractions || !workspace || !losses || !best_index) return AWQ_ERR_NULL;
+    for (int i = 0; i < n_fractions; ++i)
+        if (!clip_fraction_ok(fractions[i])) return AWQ_ERR_CONFIG;
+    if (!aligned16(w_f16) || !aligned16(x_f16) || !aligned16(workspace) ||
+        (channel_scale && !aligned16(channel_scale)))
+        return AWQ_ERR_ALIGN;
+    ClipLayout L(workspace, N, K, T, group_size, n_fractions, channel_scale != nullptr);
+    if (workspace_bytes < L.bytes) return AWQ_ERR_WORKSPACE;
+    hipStream_t s = as_stream(stream);
+    const half_t* w = static_cast<const half_t*>(w_f16);
+    const half_t* x = static_cast<const half_t*>(x_f16);
+
+    if ((st = reference_output(x, w, T, N, K, group_size, L.yref, s)) != AWQ_OK) return st;
+    const half_t* xa = x;
+    if (channel_scale != nullptr) {
+        if ((st = launch_divide_columns(x, channel_scale, T, K, L.xs, s)) != AWQ_OK) return st;
+        xa = L.xs;
+    }
+    for (int i = 0; i < n_fractions; ++i) {
+        if ((st = launch_quantize(w, channel_scale, N, K, group_size, mode == AWQ_QUANT_SYMMETRIC, fractions[i],
+                                  L.qweight, L.scales, L.zeros, s)) != AWQ_OK)
+            return st;
+        if ((st = output_loss(xa, L.qweight, L.scales, L.zeros, T, N, K, group_size, L.yref, L.tile_partials,
+                              L.losses + i, s)) != AWQ_OK)
+            return st;
+    }
+    if (hipMemcpyAsync(losses, L.losses, sizeof(double) * n_fractions, hipMemcpyDeviceToHost, s) != hipSuccess)
+        return AWQ_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return AWQ_ERR_HIP;
+    int best = 0;
+    for (int i = 1; i < n_fractions; ++i)
+        if (losses[i] < losses[best]) best = i;   // strict: ties keep the earlier fraction
+    *best_index = best;
     return AWQ_OK;
 }
 

@@ -45,10 +45,12 @@ inline awq_status last_launch_status() { return hip_status(hipGetLastError()); }
 // ---- launchers (each returns after enqueueing on `stream`) ----
 
 // Group-wise INT4 quantization of W[N, K] (optionally times channel_scale[K]),
-// asymmetric (the group's [min, max]) or symmetric (max |w| -> +-7, zero 8).
+// asymmetric (the group's [min, max]) or symmetric (max |w| -> +-7, zero 8),
+// after an optional percentile clip of each group (clip_fraction in [0, 0.25)).
+bool clip_fraction_ok(double p);
 awq_status launch_quantize(const half_t* w, const float* channel_scale, int64_t N, int64_t K,
-                           int group_size, bool symmetric, uint32_t* qweight, half_t* scales, half_t* zeros,
-                           hipStream_t stream);
+                           int group_size, bool symmetric, double clip_fraction, uint32_t* qweight,
+                           half_t* scales, half_t* zeros, hipStream_t stream);
 
 // Decode GEMV y[M, N] = x[M, K] . dequant(Wq)^T for M <= kGemvMaxM.
 constexpr int kGemvMaxM = 8;

@@ -15,6 +15,8 @@
 // group min/max is a 3- or 4-step butterfly over lanes. Every arithmetic step
 // is IEEE fp32 (correctly rounded divide, round-half-to-even rint) so the
 // codes, scales and zeros are bit-identical to a plain fp32 evaluation.
+#include <cmath>
+
 #include "awq_internal.h"
 
 namespace awq {
@@ -22,13 +24,25 @@ namespace {
 
 #pragma clang fp contract(off)
 
-template <int G, bool SYM>
+// Clip step (xxmr.cn §1.5: cut the extreme p of the values at both ends
+// before the scale is taken). The bounds are the p and 1 - p quantiles of the
+// group, interpolated between order statistics x(0) <= ... <= x(G-1):
+//   lo = x(i) + f * (x(i+1) - x(i)),  hi = x(G-1-i) - f * (x(G-1-i) - x(G-2-i))
+// with (i, f) = (floor(h), h - floor(h)), h = (G - 1) * p, taken on the host.
+// The four order statistics are found by selection from both ends (see the
+// kernel), in O((i + 2) log G) group reductions rather than a sort.
+struct Clip {
+    int i = 0;          // lower order-statistic position
+    float f = 0.f;      // interpolation fraction
+};
+
+template <int G, bool SYM, bool CLIP>
 __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict__ w,
                                                        const float* __restrict__ channel_scale,
                                                        int64_t n_words, int64_t words_per_row,
                                                        uint32_t* __restrict__ qweight,
                                                        half_t* __restrict__ scales,
-                                                       half_t* __restrict__ zeros) {
+                                                       half_t* __restrict__ zeros, Clip clip) {
     constexpr int kLanes = G / 8;  // threads per group: 4, 8, 16 or 32 (G = 32 .. 256)
     const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     // n_words is a multiple of kLanes and kLanes divides 64, so a group's
@@ -51,16 +65,61 @@ __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict_
         v[4] = v[4] * c1.x; v[5] = v[5] * c1.y; v[6] = v[6] * c1.z; v[7] = v[7] * c1.w;
     }
 
-    float lo = v[0], hi = v[0];
+    float lo, hi;
+    if constexpr (CLIP) {
+        // Walk the distinct values upwards from the bottom and downwards from
+        // the top at once: each round takes the next value on each side
+        // (group min / max over what is left) and its multiplicity (group
+        // count of equal values), so after round r the ranks covered on each
+        // side are known. Every round covers at least one rank per side, so
+        // i + 2 rounds reach ranks i and i + 1 from both ends; the trip count
+        // is fixed by the launch, the same for every wave.
+        float cur_lo = -__builtin_inff(), cur_hi = __builtin_inff();
+        int below = 0, above = 0;            // ranks covered from the bottom / top
+        float c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
+        const int r0 = clip.i, r1 = clip.i + 1;
+        for (int it = 0; it < clip.i + 2; ++it) {
+            float nl = __builtin_inff(), nh = -__builtin_inff();
 #pragma unroll
-    for (int i = 1; i < 8; ++i) {
-        lo = fminf(lo, v[i]);
-        hi = fmaxf(hi, v[i]);
-    }
+            for (int j = 0; j < 8; ++j) {
+                nl = v[j] > cur_lo ? fminf(nl, v[j]) : nl;
+                nh = v[j] < cur_hi ? fmaxf(nh, v[j]) : nh;
+            }
 #pragma unroll
-    for (int o = 1; o < kLanes; o <<= 1) {
-        lo = fminf(lo, __shfl_xor(lo, o, kLanes));
-        hi = fmaxf(hi, __shfl_xor(hi, o, kLanes));
+            for (int o = 1; o < kLanes; o <<= 1) {
+                nl = fminf(nl, __shfl_xor(nl, o, kLanes));
+                nh = fmaxf(nh, __shfl_xor(nh, o, kLanes));
+            }
+            int cnt = 0;                     // low count | high count << 16
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cnt += (v[j] == nl ? 1 : 0) + (v[j] == nh ? 0x10000 : 0);
+#pragma unroll
+            for (int o = 1; o < kLanes; o <<= 1) cnt += __shfl_xor(cnt, o, kLanes);
+            const int cl = cnt & 0xFFFF, ch = cnt >> 16;
+            if (below <= r0 && r0 < below + cl) c0 = nl;
+            if (below <= r1 && r1 < below + cl) c1 = nl;
+            if (above <= r0 && r0 < above + ch) c2 = nh;
+            if (above <= r1 && r1 < above + ch) c3 = nh;
+            below += cl;
+            above += ch;
+            cur_lo = nl;
+            cur_hi = nh;
+        }
+        lo = c0 + clip.f * (c1 - c0);
+        hi = c2 - clip.f * (c2 - c3);
+    } else {
+        lo = v[0];
+        hi = v[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) {
+            lo = fminf(lo, v[i]);
+            hi = fmaxf(hi, v[i]);
+        }
+#pragma unroll
+        for (int o = 1; o < kLanes; o <<= 1) {
+            lo = fminf(lo, __shfl_xor(lo, o, kLanes));
+            hi = fmaxf(hi, __shfl_xor(hi, o, kLanes));
+        }
     }
 
     float s32, z;
@@ -94,38 +153,63 @@ __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict_
     }
 }
 
-template <int G, bool SYM>
+template <int G, bool SYM, bool CLIP>
 void launch_g(const half_t* w, const float* channel_scale, int64_t n_words, int64_t words_per_row,
-              uint32_t* qweight, half_t* scales, half_t* zeros, hipStream_t stream) {
+              uint32_t* qweight, half_t* scales, half_t* zeros, Clip clip, hipStream_t stream) {
     const int threads = 256;
     const int64_t blocks = ceil_div(n_words, threads);
-    hipLaunchKernelGGL((quantize_kernel<G, SYM>), dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream, w,
-                       channel_scale, n_words, words_per_row, qweight, scales, zeros);
+    hipLaunchKernelGGL((quantize_kernel<G, SYM, CLIP>), dim3(static_cast<unsigned>(blocks)), dim3(threads), 0,
+                       stream, w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip);
 }
 
-template <bool SYM>
+template <bool SYM, bool CLIP>
 void launch_sym(const half_t* w, const float* channel_scale, int64_t n_words, int64_t words_per_row,
-                int group_size, uint32_t* qweight, half_t* scales, half_t* zeros, hipStream_t stream) {
+                int group_size, uint32_t* qweight, half_t* scales, half_t* zeros, Clip clip,
+                hipStream_t stream) {
     switch (group_size) {
-        case 32: launch_g<32, SYM>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, stream); break;
-        case 64: launch_g<64, SYM>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, stream); break;
-        case 128: launch_g<128, SYM>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, stream); break;
-        default: launch_g<256, SYM>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, stream); break;
+        case 32:
+            launch_g<32, SYM, CLIP>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            break;
+        case 64:
+            launch_g<64, SYM, CLIP>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            break;
+        case 128:
+            launch_g<128, SYM, CLIP>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            break;
+        default:
+            launch_g<256, SYM, CLIP>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            break;
     }
 }
 
 }  // namespace
 
+bool clip_fraction_ok(double p) { return p >= 0.0 && p < 0.25; }
+
 awq_status launch_quantize(const half_t* w, const float* channel_scale, int64_t N, int64_t K,
-                           int group_size, bool symmetric, uint32_t* qweight, half_t* scales, half_t* zeros,
-                           hipStream_t stream) {
+                           int group_size, bool symmetric, double clip_fraction, uint32_t* qweight,
+                           half_t* scales, half_t* zeros, hipStream_t stream) {
     const int64_t words_per_row = K / 8;
     const int64_t n_words = N * words_per_row;
     if (n_words == 0) return AWQ_OK;
-    if (symmetric)
-        launch_sym<true>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros, stream);
+    if (!clip_fraction_ok(clip_fraction)) return AWQ_ERR_CONFIG;
+    Clip clip;
+    const double h = (group_size - 1) * clip_fraction;
+    clip.i = static_cast<int>(std::floor(h));
+    clip.f = static_cast<float>(h - clip.i);
+    const bool c = clip_fraction > 0.0;
+    if (symmetric && c)
+        launch_sym<true, true>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros, clip,
+                               stream);
+    else if (symmetric)
+        launch_sym<true, false>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros, clip,
+                                stream);
+    else if (c)
+        launch_sym<false, true>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros, clip,
+                                stream);
     else
-        launch_sym<false>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros, stream);
+        launch_sym<false, false>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros, clip,
+                                 stream);
     return last_launch_status();
 }
 
