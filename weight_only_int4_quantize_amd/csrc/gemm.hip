@@ -52,6 +52,13 @@ constexpr int LDK = BK;              // LDS row (halves): 64 bytes, 4 chunks of 
 __device__ __forceinline__ int swz(int r, int c) { return r * LDK + ((c ^ ((r >> 2) & 3)) << 3); }
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
+
+// Direct-B form (INT4 B, G >= 64): K steps of 64, A rows in LDS of 128 bytes
+// (eight 16-byte chunks). Chunk c of row r is stored at c ^ ((r >> 1) & 7):
+// 16 lanes reading one chunk of 16 consecutive rows, or writing the 8 chunks
+// of 2 rows, then hit 16 distinct 16-byte slots of the 256-byte bank window.
+constexpr int BKD = 64;
+__device__ __forceinline__ int swz64(int r, int c) { return r * BKD + ((c ^ ((r >> 1) & 7)) << 3); }
 // A zero group scale would make the rescale ratio infinite; it is taken as
 // the smallest positive fp16 value instead.
 constexpr float kTinyScale = 5.9604645e-08f;
@@ -81,11 +88,13 @@ __device__ inline uint4 unpack_word(uint32_t wq, half2_t zc_hi, half2_t zc_lo, c
     const half2_t c = as_h2((w8 & k.lo_mask) | k.lo_magic) - zc_hi;
     const half2_t d = as_h2((w8 & k.hi_mask) | k.hi_magic) - zc_lo;
     const uint32_t ua = as_u32(a), ub = as_u32(b), uc = as_u32(c), ud = as_u32(d);
+    // v_perm_b32 picks bytes of {hi: first, lo: second operand}: 0x05040100
+    // joins the low halves, 0x07060302 the high halves
     uint4 r;
-    r.x = (ua & 0xFFFFu) | (ub << 16);          // (k0, k1)
-    r.y = (uc & 0xFFFFu) | (ud << 16);          // (k2, k3)
-    r.z = (ua >> 16) | (ub & 0xFFFF0000u);      // (k4, k5)
-    r.w = (uc >> 16) | (ud & 0xFFFF0000u);      // (k6, k7)
+    r.x = __builtin_amdgcn_perm(ub, ua, 0x05040100u);   // (k0, k1)
+    r.y = __builtin_amdgcn_perm(ud, uc, 0x05040100u);   // (k2, k3)
+    r.z = __builtin_amdgcn_perm(ub, ua, 0x07060302u);   // (k4, k5)
+    r.w = __builtin_amdgcn_perm(ud, uc, 0x07060302u);   // (k6, k7)
     return r;
 }
 
@@ -181,10 +190,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* p) {
     return __builtin_amdgcn_make_buffer_rsrc(p, 0, 256 * 128 * 4, 0x00020000);
 }
 
-template <int BM, int BN, GemmB BMODE, GemmOut OMODE, bool STREAMK>
+// DIRECT (INT4 B with G >= 64 only): each wave reads its own B columns'
+// packed words straight into registers in the MFMA operand order and
+// dequantizes them there; only A goes through LDS.
+//
+// WGM: waves along M (the 4 waves form WGM x 4 / WGM).
+template <int BM, int BN, GemmB BMODE, GemmOut OMODE, bool STREAMK, bool DIRECT, int WGM = 2>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int tiles_n, StreamK sk) {
-    constexpr int WTM = BM / 2;                 // wave tile rows
-    constexpr int WTN = BN / 2;                 // wave tile cols
+    constexpr int WGN = kThreads / kWave / WGM;
+    constexpr int WTM = BM / WGM;               // wave tile rows
+    constexpr int WTN = BN / WGN;               // wave tile cols
     constexpr int TM = WTM / 32;                // 32x32 MFMA tiles per wave (M)
     constexpr int TN = WTN / 32;                // 32x32 MFMA tiles per wave (N)
     constexpr int A_VECS = BM * BK / 8 / kThreads;        // uint4 of A per thread per step
@@ -195,9 +210,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
     static_assert(TM >= 1 && TN >= 1 && A_VECS >= 1, "tile shape");
     static_assert(!INT4 || B_WORDS == 2, "int4 B staging: 2 words (16 codes) per thread");
     static_assert(INT4 || B_VECS >= 1, "fp16 B staging");
+    static_assert(!DIRECT || INT4, "the direct form is for INT4 B");
+    constexpr int LDS_A = DIRECT ? BM * BKD : BM * LDK;
+    constexpr int LDS_B = DIRECT ? 8 : BN * LDK;
 
-    __shared__ __attribute__((aligned(16))) half_t As[2][BM * LDK];
-    __shared__ __attribute__((aligned(16))) half_t Bs[2][BN * LDK];
+    __shared__ __attribute__((aligned(16))) half_t As[2][LDS_A];
+    __shared__ __attribute__((aligned(16))) half_t Bs[2][LDS_B];
     __shared__ int s_flag;
 
     const int M = static_cast<int>(args.M);
@@ -208,13 +226,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int wm = (wave >> 1) * WTM;
-    const int wn = (wave & 1) * WTN;
+    const int wm = (wave / WGN) * WTM;
+    const int wn = (wave % WGN) * WTN;
     const int lcol = lane & 31;
     const int lrow = lane & 31;
     const int lchunk = lane >> 5;          // which 8-k half of a 16-k MFMA step
     const UnpackConsts uk = unpack_consts();
-    const int nk = K / BK;
+    const int nk = K / (DIRECT ? BKD : BK);
     const int steps_per_group = INT4 ? G / BK : nk + 1;
     const int b_row = tid >> 1;            // int4 staging: row t / 2,
     const int b_half = tid & 1;            //   codes 16 * (t % 2) .. +15 of the step
@@ -341,6 +359,173 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
         }
     };
 
+    // K steps [kb, ke) of 64 of one tile into acc (direct-B form).
+    // Step kt: A(kt) is in LDS buffer kt & 1, A(kt + 1) in registers, B(kt)
+    // in registers. The step first writes A(kt + 1) to the other buffer
+    // (free since the barrier that ended step kt - 1), issues the loads of
+    // A(kt + 2) and B(kt + 1), then runs 4 slices of 16 k with 8 MFMAs each.
+    // Lane half h of the MFMA takes k = 32 h + 8 ks .. + 7 of the step in
+    // slice ks, in both operands, so one 16-byte load gives a lane its four
+    // B words of a column for the whole step.
+    auto run_segment_direct = [&](int tm, int tn, int kb, int ke) {
+        constexpr int AV = BM * BKD / 8 / kThreads;        // 16-byte A chunks per thread per step
+        const int lh = lane >> 5;
+        // Buffer loads from tile-relative bases (scalar) with 32-bit lane
+        // offsets; rows past M / N are clamped to the last row, so every
+        // access is inside the tensor and the range check never fires.
+        const int rows_a = min(BM, M - tm), cols_b = min(BN, N - tn);
+        const auto a_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(args.a) + static_cast<int64_t>(tm) * K,
+                                                            0, rows_a * K * 2, 0x00020000);
+        const auto b_rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t*>(args.qweight) + static_cast<int64_t>(tn) * (K / 8), 0, cols_b * (K / 2), 0x00020000);
+        const auto s_rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<half_t*>(args.scales) + static_cast<int64_t>(tn) * ngroups, 0, cols_b * ngroups * 2, 0x00020000);
+        const auto z_rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<half_t*>(args.zeros) + static_cast<int64_t>(tn) * ngroups, 0, cols_b * ngroups * 2, 0x00020000);
+        int a_off[AV];
+#pragma unroll
+        for (int i = 0; i < AV; ++i) a_off[i] = (min(tid / 8 + i * (kThreads / 8), rows_a - 1) * K + (tid % 8) * 8) * 2;
+        int b_off[TN], sz_off[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = min(wn + j * 32 + lcol, cols_b - 1);
+            b_off[j] = n * (K / 2) + lh * 16;
+            sz_off[j] = n * ngroups * 2;
+        }
+        auto s_bits_at = [&](int j, int gg) {
+            return static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(s_rs, sz_off[j], gg * 2, 0));
+        };
+        auto z_bits_at = [&](int j, int gg) {
+            return static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(z_rs, sz_off[j], gg * 2, 0));
+        };
+        auto to_scale = [](uint16_t bits) {
+            const float v = static_cast<float>(__builtin_bit_cast(half_t, bits));
+            return v == 0.f ? kTinyScale : v;
+        };
+
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+        const int last = ke - 1;
+        u32x4 areg[AV];
+        u32x4 b0[TN], b1[TN];
+        auto load_a = [&](int kt) {
+            const int k0 = uniform(min(kt, last) * BKD * 2);
+#pragma unroll
+            for (int i = 0; i < AV; ++i) areg[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off[i], k0, 0);
+        };
+        auto load_b = [&](u32x4 (&dst)[TN], int kt) {
+            const int w0 = uniform(min(kt, last) * (BKD / 2));
+#pragma unroll
+            for (int j = 0; j < TN; ++j) dst[j] = __builtin_amdgcn_raw_buffer_load_b128(b_rs, b_off[j], w0, 0);
+        };
+        auto store_a = [&](half_t* as) {
+#pragma unroll
+            for (int i = 0; i < AV; ++i)
+                *reinterpret_cast<u32x4*>(&as[swz64(tid / 8 + i * (kThreads / 8), tid % 8)]) = areg[i];
+        };
+
+        int g = (kb * BKD) / G;
+        float s_cur[TN];
+        uint16_t s_next[TN], z_next[TN];
+        half2_t zc_hi[TN], zc_lo[TN];
+        auto set_zero = [&](int j, uint16_t zb) {
+            const half_t z = __builtin_bit_cast(half_t, zb);
+            const half_t zh = static_cast<half_t>(1024.0f) + z;   // exact
+            const half_t zl = static_cast<half_t>(64.0f) + z;     // exact
+            zc_hi[j] = half2_t{zh, zh};
+            zc_lo[j] = half2_t{zl, zl};
+        };
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            s_cur[j] = to_scale(s_bits_at(j, g));
+            set_zero(j, z_bits_at(j, g));
+            s_next[j] = s_bits_at(j, min(g + 1, ngroups - 1));
+            z_next[j] = z_bits_at(j, min(g + 1, ngroups - 1));
+        }
+
+        auto step = [&](int kt, const half_t* cur, half_t* nxt, const u32x4 (&bw)[TN], u32x4 (&bn)[TN]) {
+            if (kt + 1 < ke) store_a(nxt);
+            load_a(kt + 2);
+            load_b(bn, kt + 1);
+            if (kt > kb && ((kt * BKD) % G) == 0) {
+                // entering the next group: C' <- C' * s_g / s_{g+1}
+                ++g;
+                float r[TN];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const float sn = to_scale(s_next[j]);
+                    r[j] = s_cur[j] / sn;
+                    s_cur[j] = sn;
+                    set_zero(j, z_next[j]);
+                }
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) acc[i][j][e] *= r[j];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    s_next[j] = s_bits_at(j, uniform(min(g + 1, ngroups - 1)));
+                    z_next[j] = z_bits_at(j, uniform(min(g + 1, ngroups - 1)));
+                }
+            }
+            // slice ks + 1's fragments are read (and its B unpacked) before
+            // slice ks's MFMAs, so LDS latency hides behind a whole slice
+            half8_t af[2][TM], bf[2][TN];
+            auto fetch = [&](int ks, half8_t (&a)[TM], half8_t (&b)[TN]) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    a[i] = *reinterpret_cast<const half8_t*>(&cur[swz64(wm + i * 32 + lrow, lh * 4 + ks)]);
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    b[j] = __builtin_bit_cast(half8_t, unpack_word(bw[j][ks], zc_hi[j], zc_lo[j], uk));
+            };
+            fetch(0, af[0], bf[0]);
+#pragma unroll
+            for (int ks = 0; ks < BKD / 16; ++ks) {
+                if (ks + 1 < BKD / 16) fetch(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks & 1][i], bf[ks & 1][j], acc[i][j],
+                                                                           0, 0, 0);
+            }
+        };
+
+        load_b(b0, kb);
+        load_a(kb);
+        store_a(As[0]);
+        load_a(kb + 1);
+        __syncthreads();
+        for (int kt = kb; kt < ke; kt += 2) {
+            step(kt, As[0], As[1], b0, b1);
+            __syncthreads();
+            if (kt + 1 < ke) {
+                step(kt + 1, As[1], As[0], b1, b0);
+                __syncthreads();
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] *= s_cur[j];
+    };
+    auto segment = [&](int tm, int tn, int kb, int ke) {
+        if constexpr (DIRECT)
+            run_segment_direct(tm, tn, kb, ke);
+        else
+            run_segment(tm, tn, kb, ke);
+    };
+
     // ---- epilogue ----
     // accumulator element e of MFMA tile (i, j) is output (row, col) =
     // (tm + wm + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, tn + wn + 32 j + lane % 32)
@@ -391,7 +576,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
         const int tile = xcd_tile(blockIdx.x, gridDim.x);
         const int tm = (tile / tiles_n) * BM;
         const int tn = (tile % tiles_n) * BN;
-        run_segment(tm, tn, 0, nk);
+        segment(tm, tn, 0, nk);
         finish_tile(tile, tm, tn);
     } else {
         // consecutive ranges (which share tiles) go to the same XCD
@@ -404,7 +589,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
             const int ke = uniform(min(sk.ipt, kb + (u1 - u)));
             const int tm = (tile / tiles_n) * BM;
             const int tn = (tile % tiles_n) * BN;
-            run_segment(tm, tn, kb, ke);
+            segment(tm, tn, kb, ke);
             u += ke - kb;
             if (kb == 0 && ke == sk.ipt) {
                 finish_tile(tile, tm, tn);
@@ -503,13 +688,13 @@ int64_t resident_slots() { return static_cast<int64_t>(kBlocksPerCu) * cu_count(
 // one tile per block would leave CUs idle or at one block each. With more
 // tiles, the last round's blocks run one per CU at close to the per-CU rate
 // of two, and splitting costs more in partial traffic than it recovers.
-bool use_stream_k(int64_t tiles, int64_t K) {
+bool use_stream_k(int64_t tiles, int64_t steps) {
     if (tiles >= resident_slots() || tiles > split_counter_slots()) return false;
-    return tiles * (K / BK) < (int64_t{1} << 31);
+    return tiles * steps < (int64_t{1} << 31);
 }
 
-int stream_k_grid(int64_t tiles, int64_t K) {
-    const int64_t total = tiles * (K / BK);
+int stream_k_grid(int64_t tiles, int64_t steps) {
+    const int64_t total = tiles * steps;
     int64_t g = std::min(resident_slots(), tiles * kMaxSplit);
     g = std::min(g, std::max<int64_t>(1, total / kMinSteps));
     return static_cast<int>(g);
@@ -520,25 +705,39 @@ size_t partials_bytes() {
     return round_up(static_cast<size_t>(resident_slots()) * 2 * kBM * kBN * sizeof(float), 256);
 }
 
-template <GemmB BMODE, GemmOut OMODE>
+template <GemmB BMODE, GemmOut OMODE, bool DIRECT, int WGM = 2>
 void launch_cfg(const GemmArgs& args, void* workspace, hipStream_t stream) {
     const int64_t tiles_n = ceil_div(args.N, kBN);
     const int64_t tiles = ceil_div(args.M, kBM) * tiles_n;
+    const int64_t steps = args.K / (DIRECT ? BKD : BK);
     StreamK sk;
-    if (workspace != nullptr && use_stream_k(tiles, args.K)) {
-        sk.ipt = static_cast<int>(args.K / BK);
+    if (workspace != nullptr && use_stream_k(tiles, steps)) {
+        sk.ipt = static_cast<int>(steps);
         sk.total = static_cast<int>(tiles * sk.ipt);
-        sk.grid = stream_k_grid(tiles, args.K);
+        sk.grid = stream_k_grid(tiles, steps);
         sk.q = sk.total / sk.grid;
         sk.r = sk.total % sk.grid;
         sk.counters = static_cast<int*>(workspace);
         sk.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_counter_bytes());
-        hipLaunchKernelGGL((gemm_kernel<kBM, kBN, BMODE, OMODE, true>), dim3(static_cast<unsigned>(sk.grid)),
+        hipLaunchKernelGGL((gemm_kernel<kBM, kBN, BMODE, OMODE, true, DIRECT, WGM>), dim3(static_cast<unsigned>(sk.grid)),
                            dim3(kThreads), 0, stream, args, static_cast<int>(tiles_n), sk);
         return;
     }
-    hipLaunchKernelGGL((gemm_kernel<kBM, kBN, BMODE, OMODE, false>), dim3(static_cast<unsigned>(tiles)),
+    hipLaunchKernelGGL((gemm_kernel<kBM, kBN, BMODE, OMODE, false, DIRECT, WGM>), dim3(static_cast<unsigned>(tiles)),
                        dim3(kThreads), 0, stream, args, static_cast<int>(tiles_n), sk);
+}
+
+// The direct-B form needs every K step of 64 inside one group, and 32-bit
+// byte offsets within a 256-row tile of A. Its 4 waves sit side by side
+// along N (256 x 32 each): a wave's unpack work per MFMA halves against the
+// 2 x 2 arrangement (whose wave pairs would unpack the same columns twice).
+constexpr int kDirectWgm = 1;
+template <GemmOut OMODE>
+void launch_int4(const GemmArgs& args, void* workspace, hipStream_t stream) {
+    if (args.group_size >= BKD && args.K * kBM * 2 < (int64_t{1} << 31))
+        launch_cfg<GemmB::kInt4, OMODE, true, kDirectWgm>(args, workspace, stream);
+    else
+        launch_cfg<GemmB::kInt4, OMODE, false>(args, workspace, stream);
 }
 
 }  // namespace
@@ -555,14 +754,14 @@ awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t s
     if (args.M == 0 || args.N == 0) return AWQ_OK;
     if (b == GemmB::kInt4) {
         switch (out) {
-            case GemmOut::kF16: launch_cfg<GemmB::kInt4, GemmOut::kF16>(args, workspace, stream); break;
-            case GemmOut::kF32: launch_cfg<GemmB::kInt4, GemmOut::kF32>(args, workspace, stream); break;
-            case GemmOut::kLoss: launch_cfg<GemmB::kInt4, GemmOut::kLoss>(args, workspace, stream); break;
+            case GemmOut::kF16: launch_int4<GemmOut::kF16>(args, workspace, stream); break;
+            case GemmOut::kF32: launch_int4<GemmOut::kF32>(args, workspace, stream); break;
+            case GemmOut::kLoss: launch_int4<GemmOut::kLoss>(args, workspace, stream); break;
         }
     } else {
         switch (out) {
-            case GemmOut::kF16: launch_cfg<GemmB::kF16, GemmOut::kF16>(args, workspace, stream); break;
-            case GemmOut::kF32: launch_cfg<GemmB::kF16, GemmOut::kF32>(args, workspace, stream); break;
+            case GemmOut::kF16: launch_cfg<GemmB::kF16, GemmOut::kF16, false>(args, workspace, stream); break;
+            case GemmOut::kF32: launch_cfg<GemmB::kF16, GemmOut::kF32, false>(args, workspace, stream); break;
             case GemmOut::kLoss: return AWQ_ERR_CONFIG;
         }
     }
