@@ -17,7 +17,7 @@ The same run also times, each in its own section:
   * the per-node floor of a graph of tiny kernels (launch cost context);
   * batched decode rows on the skinny MFMA kernel (M = 16 on the decode
     shapes, M = 32 on the 13B/70B sweep shapes);
-  * the roofline GEMV at group sizes 32, 64, 128 and 256;
+  * the roofline GEMV at group sizes 32, 64, 128, 256 and 512;
   * the prefill GEMM, x[2048, K] times the two MLP shapes;
   * the quantize kernel on 11008x4096;
   * one full scale search (W[11008, 4096], X[65536, 4096], 20 alphas);
@@ -272,7 +272,7 @@ class Bench:
         torch, awq = self.torch, self.awq
         N, K = ROOFLINE_SHAPE
         out = {}
-        for g in (32, 64, 128, 256):
+        for g in (32, 64, 128, 256, 512):
             lay = synth.decode_layer(N, K, 1, g)
             qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), g)
             x = self.d(lay["x"])

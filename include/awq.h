@@ -22,7 +22,7 @@
  * Conventions shared by every call:
  *   - Matrices are row-major and densely packed. W[N, K]: row n is output
  *     channel n, column k is input channel k. Groups of G consecutive k share
- *     one scale and one zero-point (G = 32, 64, 128 or 256).
+ *     one scale and one zero-point (G = 32, 64, 128, 256 or 512).
  *   - qweight is uint32 [N, K/8]: the 4-bit code of column k = 8c + j sits in
  *     bits 4j..4j+3 of word c. scales and zeros are fp16 [N, K/G]; every zero
  *     is an integer 0..15.
@@ -77,7 +77,7 @@ int awq_version(void);
  *   w_f16          device, fp16 [N, K]
  *   channel_scale  device, fp32 [K] or NULL (AWQ's W * diag(s), rskf.cn §2.1)
  *   N, K           N >= 0; K > 0, K % group_size == 0
- *   group_size     32, 64, 128 or 256
+ *   group_size     32, 64, 128, 256 or 512
  *   qweight        device, uint32 [N, K/8]            (output)
  *   scales_f16     device, fp16 [N, K/G]              (output)
  *   zeros_f16      device, fp16 [N, K/G]              (output)
@@ -133,7 +133,7 @@ awq_status awq_quantize_ex(const void* w_f16, const float* channel_scale,
  *                AWQ factor s, which is folded upstream: rskf.cn §2.3)
  *   qweight, scales_f16, zeros_f16   device, as written by awq_quantize
  *   M, N, K      M, N >= 0; K > 0, K % group_size == 0
- *   group_size   32, 64, 128 or 256
+ *   group_size   32, 64, 128, 256 or 512
  *   y_f16        device, fp16 [M, N] (output; must not alias the inputs)
  * M == 0 or N == 0 returns AWQ_OK without work. M <= 4 (decode) runs a
  * bandwidth-bound GEMV, 4 < M <= 64 (a batch of decode tokens) a skinny
@@ -148,7 +148,7 @@ awq_status awq_gemm(const void* x_f16, const uint32_t* qweight,
 /*
  * awq_gemm_path - awq_gemm with the kernel chosen by the caller:
  * path 0 = automatic (as awq_gemm), 1 = GEMV (requires M <= 8),
- * 2 = MFMA GEMM, 3 = skinny MFMA kernel (requires M <= 64, a packed
+ * 2 = MFMA GEMM, 3 = skinny MFMA kernel (requires M <= 64, G <= 256, a packed
  * matrix under 4 GiB, and without a workspace a K whose staged x and group
  * scales fit one block's LDS: for G = 128, K <= 3840 for M <= 16, 2048 for
  * M <= 32, 1024 for M <= 64; for G = 64, K <= 3200, 1920 and 1024).
@@ -224,7 +224,7 @@ awq_status awq_activation_absmean(const void* x_f16, int64_t T, int64_t K,
  *   w_f16         device, fp16 [N, K]
  *   x_f16         device, fp16 [T, K] (calibration activations)
  *   N, K, T       N > 0, T > 0, K > 0, K % group_size == 0
- *   group_size    32, 64, 128 or 256
+ *   group_size    32, 64, 128, 256 or 512
  *   alphas        host, float64 [n_alpha], every alpha finite (1 <= n_alpha <= 64)
  *   workspace     device, >= awq_scale_search_workspace_bytes(N, K, T, G, n_alpha)
  *   losses        host, float64 [n_alpha] (output)
@@ -257,7 +257,7 @@ awq_status awq_scale_search(const void* w_f16, const void* x_f16,
  *   channel_scale  device, fp32 [K] (e.g. awq_scale_search's best_scales)
  *                  or NULL
  *   N, K, T        N > 0, T > 0, K > 0, K % group_size == 0
- *   group_size     32, 64, 128 or 256
+ *   group_size     32, 64, 128, 256 or 512
  *   mode           AWQ_QUANT_ASYMMETRIC or AWQ_QUANT_SYMMETRIC
  *   fractions      host, double [n_fractions], each in [0, 0.25);
  *                  1 <= n_fractions <= 64

@@ -50,8 +50,8 @@ def test_status_strings(L):
 
 
 @pytest.mark.parametrize("N,K,G,expect", [
-    (16, 128, 16, CONFIG),      # unsupported group sizes (32, 64, 128, 256 are supported)
-    (16, 512, 512, CONFIG),
+    (16, 128, 16, CONFIG),      # unsupported group sizes (32 .. 512, powers of two, are supported)
+    (16, 1024, 1024, CONFIG),
     (16, 96, 48, CONFIG),
     (16, 100, 64, SHAPE),       # K not a multiple of G
     (16, 0, 64, SHAPE),         # empty K
@@ -115,6 +115,7 @@ def test_gemm_checks(L):
     assert g(FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 96, FAKE, 0, None) == CONFIG
     assert g(FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 64, FAKE, 4, None) == CONFIG
     assert g(FAKE, FAKE, FAKE, FAKE, 65, 16, 128, 64, FAKE, 3, None) == CONFIG  # skinny is M <= 64
+    assert g(FAKE, FAKE, FAKE, FAKE, 16, 16, 512, 512, FAKE, 3, None) == CONFIG  # and G <= 256
     assert g(FAKE, FAKE, FAKE, FAKE, 9, 16, 128, 64, FAKE, 1, None) == CONFIG   # GEMV is M <= 8
     assert g(FAKE, FAKE, FAKE, FAKE, 0, 16, 128, 64, FAKE, 0, None) == OK       # empty M
     assert g(FAKE, FAKE, FAKE, FAKE, 4, 0, 128, 64, FAKE, 0, None) == OK        # empty N

@@ -38,7 +38,7 @@ def heavy_tailed(N, K, seed, scale=0.02):
     return (rng.standard_t(3, size=(N, K)) * scale).astype(np.float16)
 
 
-@pytest.mark.parametrize("G", [32, 64, 128, 256])
+@pytest.mark.parametrize("G", [32, 64, 128, 256, 512])
 @pytest.mark.parametrize("symmetric", [False, True])
 @pytest.mark.parametrize("p", [0.01, 0.05, 0.2])
 def test_clipped_quantize_bit_exact(G, symmetric, p):
@@ -102,7 +102,7 @@ def check_clip_search(losses, best, losses_o, best_o, rtol=2e-3):
         assert (losses_o[best] - losses_o[best_o]) <= rtol * losses_o[best_o], (best, best_o)
 
 
-@pytest.mark.parametrize("G", [32, 64, 128, 256])
+@pytest.mark.parametrize("G", [32, 64, 128, 256, 512])
 @pytest.mark.parametrize("symmetric", [False, True])
 def test_clip_search_matches_oracle(G, symmetric):
     N, K, T = 512, 1024, 512

@@ -30,15 +30,17 @@ def gpu_quantize(w16, G, cs=None, symmetric=False):
     return host(qw).view(np.uint32), host(sc), host(zr)
 
 
-@pytest.mark.parametrize("G", [32, 256])
-@pytest.mark.parametrize("N,K", [(11008, 4096), (4096, 11008), (77, 768)])
+@pytest.mark.parametrize("G", [32, 256, 512])
+@pytest.mark.parametrize("N,K", [(11008, 4096), (4096, 11008), (77, 1536)])
 def test_quantize_group_sizes_bit_exact(N, K, G):
+    if K % G:
+        pytest.skip("K is not a multiple of G")
     lay = synth.decode_layer(N, K, 0, G)
     say("quantize G", G, N, K)
     assert_quant_equal(gpu_quantize(lay["w"], G), oracle.quantize(lay["w"], G))
 
 
-@pytest.mark.parametrize("G", [32, 64, 128, 256])
+@pytest.mark.parametrize("G", [32, 64, 128, 256, 512])
 @pytest.mark.parametrize("scaled", [False, True])
 def test_quantize_symmetric_bit_exact(G, scaled):
     N, K = 1000, 2048
@@ -92,7 +94,7 @@ def test_linear_paths_symmetric_smaller_groups(G, symmetric):
     assert_linear_close(host(y), oracle.linear_ref(lay["x"], qw, sc, zr, G))
 
 
-@pytest.mark.parametrize("G", [32, 256])
+@pytest.mark.parametrize("G", [32, 256, 512])
 def test_scale_search_group_sizes(G):
     lay = synth.make_layer(256, 512, 512, seed=[154, G], w_std=0.02, w_mult=1.0)
     w, x = lay["w"], lay["x"]
@@ -100,3 +102,28 @@ def test_scale_search_group_sizes(G):
     losses, best, s = awq.awq_scale_search(dev(w), dev(x), G)
     say("search G", G, "gpu", best, "oracle", best_o)
     check_search(losses, best, host(s), losses_o, best_o, s_o)
+
+
+@pytest.mark.parametrize("symmetric", [False, True])
+@pytest.mark.parametrize("case", [c for c in linear_cases() if c[0] != "skinny"] +
+                         [("auto", 16, 1000, 2048, awq.PATH_AUTO, False), ("auto", 40, 300, 1024, awq.PATH_AUTO, True)],
+                         ids=lambda c: f"{c[0]}-M{c[1]}-{c[2]}x{c[3]}")
+def test_linear_paths_group_512(case, symmetric):
+    """G = 512 (f3's largest group): GEMV, GEMM and its stream-K form; the
+    skinny kernel stops at G = 256, so batched decode shapes take the
+    automatic choice (GEMV or GEMM)."""
+    label, M, N, K, path, with_ws = case
+    G = 512
+    lay = synth.make_layer(N, K, M, seed=[155, M, N, K, int(symmetric)], w_std=0.02)
+    say("linear G=512", label, M, N, K, "sym" if symmetric else "asym")
+    qw, sc, zr = (oracle.quantize_symmetric if symmetric else oracle.quantize)(lay["w"], G)
+    ws = awq.gemm_workspace(M, N, K) if with_ws else None
+    y = awq.awq_gemm(dev(lay["x"]), dev(qw.view(np.int32)), dev(sc), dev(zr), G, path=path, workspace=ws)
+    assert_linear_close(host(y), oracle.linear_ref(lay["x"], qw, sc, zr, G))
+
+
+def test_skinny_refuses_group_512():
+    lay = synth.make_layer(64, 1024, 16, seed=[156], w_std=0.02)
+    qw, sc, zr = oracle.quantize(lay["w"], 512)
+    with pytest.raises(awq.AwqError):
+        awq.awq_gemm(dev(lay["x"]), dev(qw.view(np.int32)), dev(sc), dev(zr), 512, path=awq.PATH_SKINNY)

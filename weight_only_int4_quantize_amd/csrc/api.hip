@@ -13,7 +13,7 @@ namespace {
 constexpr int64_t kMaxDim = int64_t(1) << 30;      // any single extent
 constexpr int64_t kMaxElems = int64_t(1) << 40;    // any product of extents
 
-bool valid_group(int g) { return g == 32 || g == 64 || g == 128 || g == 256; }
+bool valid_group(int g) { return g == 32 || g == 64 || g == 128 || g == 256 || g == 512; }
 
 awq_status check_dims(int64_t N, int64_t K, int group_size) {
     if (!valid_group(group_size)) return AWQ_ERR_CONFIG;

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict_
                                                        uint32_t* __restrict__ qweight,
                                                        half_t* __restrict__ scales,
                                                        half_t* __restrict__ zeros, Clip clip) {
-    constexpr int kLanes = G / 8;  // threads per group: 4, 8, 16 or 32 (G = 32 .. 256)
+    constexpr int kLanes = G / 8;  // threads per group: 4 .. 64 (G = 32 .. 512)
     const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     // n_words is a multiple of kLanes and kLanes divides 64, so a group's
     // lanes are either all in range or all out of range.
@@ -176,8 +176,11 @@ void launch_sym(const half_t* w, const float* channel_scale, int64_t n_words, in
         case 128:
             launch_g<128, SYM, CLIP>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
             break;
-        default:
+        case 256:
             launch_g<256, SYM, CLIP>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            break;
+        default:
+            launch_g<512, SYM, CLIP>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
             break;
     }
 }

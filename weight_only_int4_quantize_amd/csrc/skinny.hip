@@ -441,6 +441,8 @@ awq_status launch_wpl(const half_t* x, const uint32_t* qweight, const half_t* sc
 bool skinny_supported(int64_t M, int64_t N, int64_t K, int group_size, bool have_workspace) {
     // buffer offsets are 32-bit: the packed matrix plus one row of slack
     // (the largest offset a zero-reading lane forms), and x, stay below 4 GiB
+    // group sizes 32 .. 256 (1 .. 8 packed words per lane and group)
+    if (group_size > 256) return false;
     if (M < 1 || M > kSkinnyMaxM || N < 1 || (N + 1) * (K / 2) + 64 >= (int64_t{1} << 32) ||
         M * K * 2 + 64 >= (int64_t{1} << 32))
         return false;
@@ -464,7 +466,8 @@ awq_status launch_skinny(const half_t* x, const uint32_t* qweight, const half_t*
         case 32: return launch_wpl<1>(x, qweight, scales, zeros, m, n, k, y, workspace, stream);
         case 64: return launch_wpl<2>(x, qweight, scales, zeros, m, n, k, y, workspace, stream);
         case 128: return launch_wpl<4>(x, qweight, scales, zeros, m, n, k, y, workspace, stream);
-        default: return launch_wpl<8>(x, qweight, scales, zeros, m, n, k, y, workspace, stream);
+        case 256: return launch_wpl<8>(x, qweight, scales, zeros, m, n, k, y, workspace, stream);
+        default: return AWQ_ERR_CONFIG;
     }
 }
 
