@@ -34,4 +34,11 @@ from .awq_oracle import (  # noqa: F401
     gram,
     search_loss_gram,
     scale_search,
+    salient_count,
+    salient_channels,
+    mixed_weight,
+    quantize_salient,
+    dequantize_salient,
+    linear_salient_ref,
+    salient_loss,
 )

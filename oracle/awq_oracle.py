@@ -376,3 +376,85 @@ def clip_search(w, x, group_size: int, fractions, s32=None, use_gram: bool = Tru
             e = np.asarray(x).astype(np.float64) @ d.T
             losses[i] = float(np.sum(e * e))
     return losses, int(np.argmin(losses))
+
+
+# ---------------------------------------------------------------------------
+# Mixed precision: salient weights kept in fp16   [P4 "技术实现" 1 and
+# "混合精度设计"], [P5 §2.2]
+# ---------------------------------------------------------------------------
+
+def salient_count(K: int, fraction: float = 0.01) -> int:
+    """Number of salient input channels: the pages keep about 1 % of the
+    weights; the reading is round(fraction * K) channels (41 of 4096)."""
+    return int(round(fraction * K))
+
+
+def salient_channels(m, n: int) -> np.ndarray:
+    """The n input channels with the largest activation statistic m[k]
+    (the pages pick the important weights from the activation distribution,
+    at the 99th percentile), listed by descending m; equal m go by ascending
+    channel index. A plain sort on the key (-m[k], k)."""
+    m = np.asarray(m, dtype=np.float64).ravel()
+    K = m.size
+    if not 0 <= n <= K:
+        raise ValueError("n must lie in [0, K]")
+    order = sorted(range(K), key=lambda k: (-m[k], k))
+    return np.asarray(order[:n], dtype=np.int64)
+
+
+def mixed_weight(w, group_size: int, idx, symmetric: bool = False) -> np.ndarray:
+    """The pages' recipe read literally, float64 [N, K]: quantize all of W
+    (every group's range over all its G weights, salient ones included),
+    dequantize, then put the original values back in the salient columns."""
+    w = np.asarray(w)
+    K = w.shape[1]
+    qw, sc, zr = (quantize_symmetric if symmetric else quantize)(w, group_size)
+    w_hat = dequantize(qw, sc, zr, group_size, K)
+    idx = np.asarray(idx, dtype=np.int64)
+    w_hat[:, idx] = w[:, idx].astype(np.float64)
+    return w_hat
+
+
+def quantize_salient(w, group_size: int, idx, symmetric: bool = False):
+    """The stored form of the mixed-precision layer: the quantizer of
+    group_quantize (or the symmetric one) on all of W, then the codes of the
+    salient columns set to their group's zero-point, so that they dequantize
+    to exactly 0, and the salient fp16 weights kept beside as
+    w_salient[j, n] = W[n, idx[j]] (float16 [n_salient, N]).
+    Returns (qweight, scales, zeros, w_salient)."""
+    w16 = np.asarray(w).astype(np.float16)
+    N, K = w16.shape
+    codes, s16, z16 = (group_quantize_symmetric if symmetric else group_quantize)(w16, group_size)
+    codes = codes.copy()
+    idx = np.asarray(idx, dtype=np.int64)
+    for k in idx:
+        codes[:, k] = z16[:, k // group_size].astype(np.uint8)
+    w_salient = np.ascontiguousarray(w16[:, idx].T)
+    return pack_codes(codes), s16, z16, w_salient
+
+
+def dequantize_salient(qweight, scales, zeros, group_size: int, K: int, idx, w_salient) -> np.ndarray:
+    """Effective weight of the stored form, float64 [N, K]: the INT4 part
+    (zero in the salient columns) plus the fp16 salient columns."""
+    w_hat = dequantize(qweight, scales, zeros, group_size, K)
+    idx = np.asarray(idx, dtype=np.int64)
+    w_hat[:, idx] += np.asarray(w_salient).astype(np.float64).T
+    return w_hat
+
+
+def linear_salient_ref(x, qweight, scales, zeros, group_size: int, idx, w_salient) -> np.ndarray:
+    """y = x . W_mixed^T in float64 [M, N]: the W4A16 product plus the
+    fp16 side product x[:, idx] . w_salient."""
+    x64 = np.asarray(x).astype(np.float64)
+    K = x64.shape[1]
+    return x64 @ dequantize_salient(qweight, scales, zeros, group_size, K, idx, w_salient).T
+
+
+def salient_loss(w, x, group_size: int, idx, use_gram: bool = True, symmetric: bool = False) -> float:
+    """Output loss of the mixed-precision layer, by the scale search's
+    measure: || X W_mixed^T - X W^T ||_F^2 (float64)."""
+    d = mixed_weight(w, group_size, idx, symmetric) - np.asarray(w).astype(np.float64)
+    if use_gram:
+        return float(np.sum((d @ gram(x)) * d))
+    e = np.asarray(x).astype(np.float64) @ d.T
+    return float(np.sum(e * e))
