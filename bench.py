@@ -20,7 +20,9 @@ The same run also times, each in its own section:
   * the roofline GEMV at group sizes 32, 64, 128, 256 and 512;
   * the prefill GEMM, x[2048, K] times the two MLP shapes;
   * the quantize kernel on 11008x4096;
-  * one full scale search (W[11008, 4096], X[65536, 4096], 20 alphas);
+  * one full scale search (W[11008, 4096], X[65536, 4096], 20 alphas), the
+    clip search after it, and the fp16-salient-channel ablation (output loss
+    of plain RTN, the searched scales and the mixed-precision layer);
   * an HBM copy of 1 GiB (context for the achievable bandwidth, and the
     calibration of the FETCH_SIZE / WRITE_SIZE counters);
   * the CPU oracle on a bounded sample (the CPU baseline).
@@ -418,7 +420,7 @@ class Bench:
         awq.awq_scale_search(ws, xs, G, workspace=wsp)   # warm-up
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        _, best, best_s = awq.awq_scale_search(ws, xs, G, workspace=wsp)
+        losses, best, best_s = awq.awq_scale_search(ws, xs, G, workspace=wsp)
         ts = time.perf_counter() - t0
         flop = 21 * 2.0 * xs.shape[0] * ws.shape[0] * ws.shape[1]
         log(f"scale search: {ts * 1e3:.1f} ms, alpha* = {best / 20}")
@@ -427,7 +429,42 @@ class Bench:
                "workload": "W[11008,4096], X[65536,4096], 20 alphas, G=128 (21 GEMMs)"}
         del wsp
         out["clip_search"] = self.run_clip_search(ws, xs, best_s)
+        out["salient_fp16_ablation"] = self.run_salient(ws, xs, float(losses[0]), float(losses[best]), best / 20)
         return out
+
+    def run_salient(self, ws, xs, loss_alpha0, loss_best, alpha):
+        """Mixed precision with the top 1 % channels in fp16 against plain
+        RTN and the searched scales, by the same output loss, plus the cost of
+        the fp16 side product at decode."""
+        torch, awq = self.torch, self.awq
+        N, K, T = ws.shape[0], ws.shape[1], xs.shape[0]
+        n = int(round(0.01 * K))
+        nb = awq.load().awq_salient_loss_workspace_bytes(N, K, T, G, n)
+        wsp = torch.empty(nb, dtype=torch.uint8, device=self.dev)
+        awq.awq_salient_loss(ws, xs, G, n, workspace=wsp)   # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        lr, ls, idx = awq.awq_salient_loss(ws, xs, G, n, workspace=wsp)
+        tl = time.perf_counter() - t0
+        del wsp
+        log(f"salient fp16 ablation: rtn {lr:.4g}, awq alpha={alpha} {loss_best:.4g}, salient {ls:.4g} "
+            f"({tl * 1e3:.1f} ms)")
+        # decode: side product of the mixed gate/up layer at M = 1
+        x1 = xs[:1].contiguous()
+        qw, sc, zr, w_sal = awq.awq_quantize_salient(ws, G, idx)
+        y = torch.empty((1, N), dtype=torch.float16, device=self.dev)
+        for i in range(5):
+            awq.awq_salient_apply(x1, idx, w_sal, y)
+        reps = 200
+        g = self.capture(lambda i: awq.awq_salient_apply(x1, idx, w_sal, y), reps)
+        g.replay()
+        t_apply = self.time(lambda i: g.replay()) / reps
+        log(f"salient side product M=1 {N}x{n}: {t_apply * 1e6:.2f} us")
+        return {"n_salient": n, "loss_rtn": lr, "loss_awq_best": loss_best, "awq_best_alpha": alpha,
+                "loss_salient_fp16": ls, "rtn_equals_alpha0": abs(lr - loss_alpha0) <= 2e-3 * loss_alpha0,
+                "ms": round(tl * 1e3, 2), "side_product_m1_us": round(t_apply * 1e6, 2),
+                "side_bytes_m1": n * N * 2 + n * 2 + N * 4,
+                "workload": f"W[{N},{K}], X[{T},{K}], G=128, top {n} channels by mean |x| kept in fp16"}
 
     def run_clip_search(self, ws, xs, s):
         """The clip search after the scale search: W diag(s) at the chosen

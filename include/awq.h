@@ -278,6 +278,103 @@ awq_status awq_clip_search(const void* w_f16, const void* x_f16,
                            void* workspace, size_t workspace_bytes,
                            double* losses, int* best_index, void* stream);
 
+/*
+ * Mixed precision with fp16 salient weights ("AWQ 模型量化技术：激活感知的
+ * 权重量化革命", 技术实现 1 and 混合精度设计: the important 1 % of the
+ * weights, picked from the activation distribution, stay in fp16 and the
+ * rest is quantized to 4 bits; xxmr.cn §2.2). The layer is
+ *   y = x . dequant(Wq)^T + x[:, idx] . w_salient
+ * where Wq is the usual group-wise INT4 matrix of all of W whose codes in
+ * the salient input channels are set to the group's zero-point (so they
+ * dequantize to exactly 0), and w_salient[j, n] = W[n, idx[j]] in fp16.
+ */
+
+/*
+ * awq_select_salient - idx[0 .. n_salient) = the n_salient input channels
+ * with the largest m[k] (awq_activation_absmean's mean |x|), by descending
+ * m; equal m go by ascending channel index.
+ *
+ *   m_f64      device, double [K], 8-byte aligned; finite values
+ *   K          1 <= K <= 131072
+ *   n_salient  0 <= n_salient <= K (0 does nothing)
+ *   idx        device, int32 [n_salient] (output), 4-byte aligned
+ * Asynchronous on `stream`.
+ */
+awq_status awq_select_salient(const double* m_f64, int64_t K, int n_salient,
+                              int* idx, void* stream);
+
+/*
+ * awq_quantize_salient - the stored mixed-precision form: awq_quantize_ex
+ * (mode, no clip) of all of W, then the codes of the channels idx[j] set to
+ * their group's zero-point and w_salient[j, n] = W[n, idx[j]].
+ *
+ *   w_f16          device, fp16 [N, K], 16-byte aligned
+ *   N, K, group_size, mode   as awq_quantize_ex
+ *   idx            device, int32 [n_salient]: distinct channels in [0, K)
+ *                  (an index outside it is skipped and its w_salient row is
+ *                  0; a repeated index would be counted twice by
+ *                  awq_salient_apply)
+ *   n_salient      0 <= n_salient <= K
+ *   qweight, scales_f16, zeros_f16   outputs, as awq_quantize
+ *   w_salient_f16  device, fp16 [n_salient, N] (output)
+ * Asynchronous on `stream`.
+ */
+awq_status awq_quantize_salient(const void* w_f16, int64_t N, int64_t K,
+                                int group_size, int mode, const int* idx,
+                                int n_salient, uint32_t* qweight,
+                                void* scales_f16, void* zeros_f16,
+                                void* w_salient_f16, void* stream);
+
+/*
+ * awq_salient_apply - the fp16 side product of the mixed layer, added in
+ * place: y[m, n] = fp16(y[m, n] + sum_j x[m, idx[j]] * w_salient[j, n]),
+ * the sum in fp32. Run it after awq_gemm on the same stream to get the
+ * mixed layer's output.
+ *
+ *   x_f16          device, fp16 [M, K]
+ *   idx            device, int32 [n_salient] (as awq_quantize_salient)
+ *   w_salient_f16  device, fp16 [n_salient, N]
+ *   y_f16          device, fp16 [M, N] (input and output)
+ * M == 0, N == 0 or n_salient == 0 return AWQ_OK without work.
+ * Asynchronous on `stream`.
+ */
+awq_status awq_salient_apply(const void* x_f16, const int* idx,
+                             const void* w_salient_f16, int64_t M, int64_t N,
+                             int64_t K, int n_salient, void* y_f16,
+                             void* stream);
+
+/*
+ * awq_salient_loss - the ablation of the mixed form against the plain
+ * quantizer, by the scale search's objective (rskf.cn §2.1):
+ *   loss_rtn     = || Q(W) . x^T - W . x^T ||_F^2
+ *   loss_salient = || W_mixed . x^T - W . x^T ||_F^2
+ * with the salient channels chosen by awq_select_salient from x's mean |x|
+ * and Q the quantizer of `mode` (no channel scale). The products are the
+ * library's W4A16 GEMM, the fp16 MFMA reference and the side product
+ * (fp32), the sums in fp64.
+ *
+ *   w_f16, x_f16   device, fp16 [N, K] and [T, K], 16-byte aligned
+ *   N, K, T        N > 0, 0 < T <= 2^24, K % 8 == 0, K <= 131072,
+ *                  K % group_size == 0
+ *   group_size     32, 64, 128, 256 or 512
+ *   mode           AWQ_QUANT_ASYMMETRIC or AWQ_QUANT_SYMMETRIC
+ *   n_salient      0 <= n_salient <= K
+ *   workspace, workspace_bytes  device scratch of at least
+ *                  awq_salient_loss_workspace_bytes(N, K, T, group_size,
+ *                  n_salient) bytes, 16-byte aligned
+ *   loss_rtn, loss_salient  host, double (outputs)
+ *   idx_out        device, int32 [n_salient] (output: the chosen channels)
+ *                  or NULL
+ * Synchronises `stream` once, to read the losses back.
+ */
+size_t awq_salient_loss_workspace_bytes(int64_t N, int64_t K, int64_t T,
+                                         int group_size, int n_salient);
+awq_status awq_salient_loss(const void* w_f16, const void* x_f16, int64_t N,
+                            int64_t K, int64_t T, int group_size, int mode,
+                            int n_salient, void* workspace,
+                            size_t workspace_bytes, double* loss_rtn,
+                            double* loss_salient, int* idx_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -196,3 +196,43 @@ def test_oracle_is_not_reachable_from_the_package():
                 with open(os.path.join(root, f), encoding="utf-8") as fh:
                     text = fh.read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_salient_checks(L):
+    """Argument checks of the mixed-precision entry points (no launch)."""
+    sel = L.awq_select_salient
+    assert sel(FAKE, 0, 1, FAKE, None) == SHAPE
+    assert sel(FAKE, (1 << 17) + 8, 1, FAKE, None) == SHAPE          # K^2 selection is bounded
+    assert sel(FAKE, 64, 65, FAKE, None) == SHAPE
+    assert sel(FAKE, 64, -1, FAKE, None) == SHAPE
+    assert sel(None, 64, 4, FAKE, None) == NULL
+    assert sel(FAKE + 4, 64, 4, FAKE, None) == ALIGN
+    assert sel(None, 64, 0, None, None) == OK                         # nothing to select
+    q = L.awq_quantize_salient
+    assert q(FAKE, 16, 256, 64, 2, FAKE, 4, FAKE, FAKE, FAKE, FAKE, None) == CONFIG   # mode
+    assert q(FAKE, 16, 256, 48, 0, FAKE, 4, FAKE, FAKE, FAKE, FAKE, None) == CONFIG   # group size
+    assert q(FAKE, 16, 256, 64, 0, FAKE, 257, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(FAKE, 16, 256, 64, 0, None, 4, FAKE, FAKE, FAKE, FAKE, None) == NULL
+    assert q(FAKE, 16, 256, 64, 0, FAKE, 4, FAKE, FAKE, FAKE, None, None) == NULL
+    assert q(FAKE_ODD, 16, 256, 64, 0, FAKE, 4, FAKE, FAKE, FAKE, FAKE, None) == ALIGN
+    assert q(FAKE, 0, 256, 64, 0, FAKE, 4, FAKE, FAKE, FAKE, FAKE, None) == OK        # empty N
+    a = L.awq_salient_apply
+    assert a(FAKE, FAKE, FAKE, 4, 16, 64, 65, FAKE, None) == SHAPE
+    assert a(FAKE, FAKE, FAKE, -1, 16, 64, 4, FAKE, None) == SHAPE
+    assert a(FAKE, None, FAKE, 4, 16, 64, 4, FAKE, None) == NULL
+    assert a(FAKE + 1, FAKE, FAKE, 4, 16, 64, 4, FAKE, None) == ALIGN
+    assert a(None, None, None, 0, 16, 64, 4, None, None) == OK                       # empty M
+    assert a(None, None, None, 4, 16, 64, 0, None, None) == OK                       # no salient channel
+    need = L.awq_salient_loss_workspace_bytes(256, 512, 1024, 128, 5)
+    assert need >= 1024 * 256 * 4 + 256 * 512 // 2 + 5 * 256 * 2
+    assert L.awq_salient_loss_workspace_bytes(256, 512, 1024, 128, 513) == 0
+    lr, ls = ctypes.c_double(), ctypes.c_double()
+    pr, ps = ctypes.addressof(lr), ctypes.addressof(ls)
+    s = L.awq_salient_loss
+    assert s(FAKE, FAKE, 256, 512, 1024, 128, 0, 5, FAKE, need - 256, pr, ps, None, None) == WORKSPACE
+    assert s(FAKE, FAKE, 256, 512, 1024, 128, 2, 5, FAKE, need, pr, ps, None, None) == CONFIG
+    assert s(FAKE, FAKE, 256, 1 << 18, 1024, 128, 0, 5, FAKE, need, pr, ps, None, None) == SHAPE
+    assert s(FAKE, FAKE, 256, 512, 1024, 128, 0, 513, FAKE, need, pr, ps, None, None) == SHAPE
+    assert s(FAKE, None, 256, 512, 1024, 128, 0, 5, FAKE, need, pr, ps, None, None) == NULL
+    assert s(FAKE, FAKE, 256, 512, 1024, 128, 0, 5, FAKE, need, None, ps, None, None) == NULL
+    assert s(FAKE, FAKE_ODD, 256, 512, 1024, 128, 0, 5, FAKE, need, pr, ps, None, None) == ALIGN

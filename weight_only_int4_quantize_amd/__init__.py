@@ -85,6 +85,17 @@ def load() -> ctypes.CDLL:
     L.awq_scale_search.restype = c_int
     L.awq_scale_search.argtypes = [c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_int, c_vp, c_sz,
                                    c_vp, c_vp, c_vp, c_vp]
+    L.awq_select_salient.restype = c_int
+    L.awq_select_salient.argtypes = [c_vp, c_i64, c_int, c_vp, c_vp]
+    L.awq_quantize_salient.restype = c_int
+    L.awq_quantize_salient.argtypes = [c_vp, c_i64, c_i64, c_int, c_int, c_vp, c_int, c_vp, c_vp, c_vp, c_vp, c_vp]
+    L.awq_salient_apply.restype = c_int
+    L.awq_salient_apply.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_vp]
+    L.awq_salient_loss_workspace_bytes.restype = c_sz
+    L.awq_salient_loss_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_int, c_int]
+    L.awq_salient_loss.restype = c_int
+    L.awq_salient_loss.argtypes = [c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_sz, c_vp, c_vp,
+                                   c_vp, c_vp]
     _lib = L
     return L
 
@@ -293,3 +304,85 @@ def awq_clip_search(w, x, fractions, group_size: int = 128, channel_scale=None, 
                            losses.ctypes.data_as(ctypes.c_void_p), ctypes.addressof(best), _stream(w.device))
     _check("awq_clip_search", st)
     return losses, int(best.value)
+
+
+# ---------------------------------------------------------------- mixed precision (fp16 salient channels)
+
+def select_salient(m, n_salient: int):
+    """awq_select_salient: int32 [n_salient] channel indices, largest m first
+    (m: fp64 GPU tensor [K], e.g. awq_activation_absmean's)."""
+    torch = _torch()
+    _need_gpu("m", m, torch.float64)
+    idx = torch.empty(max(n_salient, 1), dtype=torch.int32, device=m.device)[:n_salient]
+    _check("awq_select_salient", load().awq_select_salient(_ptr(m), m.numel(), n_salient, _ptr(idx),
+                                                           _stream(m.device)))
+    return idx
+
+
+def awq_quantize_salient(w, group_size: int, idx, symmetric: bool = False):
+    """awq_quantize_salient: (qweight, scales, zeros, w_salient fp16
+    [n_salient, N]) for the channels idx (int32 GPU tensor)."""
+    torch = _torch()
+    _need_gpu("w", w, torch.float16)
+    _need_gpu("idx", idx, torch.int32)
+    N, K = w.shape
+    n = idx.numel()
+    dev = w.device
+    qweight = torch.empty((N, max(K // 8, 0)), dtype=torch.int32, device=dev)
+    ng = K // group_size if group_size > 0 else 0
+    scales = torch.empty((N, ng), dtype=torch.float16, device=dev)
+    zeros = torch.empty((N, ng), dtype=torch.float16, device=dev)
+    w_sal = torch.empty((n, N), dtype=torch.float16, device=dev)
+    mode = QUANT_SYMMETRIC if symmetric else QUANT_ASYMMETRIC
+    st = load().awq_quantize_salient(_ptr(w), N, K, group_size, mode, _ptr(idx), n, _ptr(qweight), _ptr(scales),
+                                     _ptr(zeros), _ptr(w_sal), _stream(dev))
+    _check("awq_quantize_salient", st)
+    return qweight, scales, zeros, w_sal
+
+
+def awq_salient_apply(x, idx, w_salient, y):
+    """awq_salient_apply: y (fp16 [M, N]) += x[:, idx] . w_salient, in place."""
+    torch = _torch()
+    _need_gpu("x", x, torch.float16)
+    _need_gpu("idx", idx, torch.int32)
+    _need_gpu("w_salient", w_salient, torch.float16)
+    _need_gpu("y", y, torch.float16)
+    M, K = x.shape
+    n, N = w_salient.shape
+    if idx.numel() != n or y.shape != (M, N):
+        raise ValueError("shapes: idx [n], w_salient [n, N], y [M, N]")
+    _check("awq_salient_apply", load().awq_salient_apply(_ptr(x), _ptr(idx), _ptr(w_salient), M, N, K, n, _ptr(y),
+                                                         _stream(x.device)))
+    return y
+
+
+def awq_gemm_salient(x, qweight, scales, zeros, idx, w_salient, group_size: int = 128, path: int = PATH_AUTO,
+                     out=None, workspace=None):
+    """The mixed layer: awq_gemm then awq_salient_apply on the same stream."""
+    y = awq_gemm(x, qweight, scales, zeros, group_size, path=path, out=out, workspace=workspace)
+    return awq_salient_apply(x, idx, w_salient, y)
+
+
+def awq_salient_loss(w, x, group_size: int = 128, n_salient: int | None = None, symmetric: bool = False,
+                     workspace=None):
+    """awq_salient_loss: (loss_rtn, loss_salient, idx int32 GPU tensor).
+    n_salient defaults to round(K / 100), the pages' 1 %."""
+    import numpy as np
+    torch = _torch()
+    _need_gpu("w", w, torch.float16)
+    _need_gpu("x", x, torch.float16)
+    N, K = w.shape
+    T = x.shape[0]
+    n = int(round(0.01 * K)) if n_salient is None else int(n_salient)
+    L = load()
+    nbytes = L.awq_salient_loss_workspace_bytes(N, K, T, group_size, n)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=w.device)
+    idx = torch.empty(max(n, 1), dtype=torch.int32, device=w.device)[:n]
+    lr, ls = np.zeros(1), np.zeros(1)
+    mode = QUANT_SYMMETRIC if symmetric else QUANT_ASYMMETRIC
+    st = L.awq_salient_loss(_ptr(w), _ptr(x), N, K, T, group_size, mode, n, _ptr(workspace), workspace.numel(),
+                            lr.ctypes.data_as(ctypes.c_void_p), ls.ctypes.data_as(ctypes.c_void_p), _ptr(idx),
+                            _stream(w.device))
+    _check("awq_salient_loss", st)
+    return float(lr[0]), float(ls[0]), idx

@@ -66,6 +66,39 @@ struct SearchLayout {
     }
 };
 
+// Lays out the salient-loss workspace; with base == nullptr it only sizes it.
+struct SalientLayout {
+    double* m = nullptr;
+    double* abs_partials = nullptr;
+    int* idx = nullptr;
+    uint32_t* qweight = nullptr;
+    half_t* scales = nullptr;
+    half_t* zeros = nullptr;
+    half_t* w_sal = nullptr;
+    float* yref = nullptr;
+    double* tile_partials = nullptr;
+    double* losses = nullptr;
+    size_t bytes = 0;
+
+    SalientLayout(void* base, int64_t N, int64_t K, int64_t T, int G, int n_sal) {
+        Carve c(base);
+        m = c.take<double>(K);
+        abs_partials = c.take<double>(absmean_workspace_bytes(T, K) / sizeof(double));
+        idx = c.take<int>(std::max(n_sal, 1));
+        qweight = c.take<uint32_t>(static_cast<size_t>(N) * (K / 8));
+        scales = c.take<half_t>(static_cast<size_t>(N) * (K / G));
+        zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
+        w_sal = c.take<half_t>(static_cast<size_t>(std::max(n_sal, 1)) * N);
+        yref = c.take<float>(static_cast<size_t>(T) * N);
+        tile_partials = c.take<double>(gemm_tile_count(T, N));
+        losses = c.take<double>(2);
+        bytes = c.used;
+    }
+};
+
+// Channels the K^2 selection accepts (a few milliseconds at the largest).
+constexpr int64_t kMaxSelectK = int64_t(1) << 17;
+
 // Lays out the clip-search workspace; with base == nullptr it only sizes it.
 struct ClipLayout {
     uint32_t* qweight = nullptr;
@@ -352,6 +385,104 @@ awq_status awq_clip_search(const void* w_f16, const void* x_f16, const float* ch
     for (int i = 1; i < n_fractions; ++i)
         if (losses[i] < losses[best]) best = i;   // strict: ties keep the earlier fraction
     *best_index = best;
+    return AWQ_OK;
+}
+
+awq_status awq_select_salient(const double* m_f64, int64_t K, int n_salient, int* idx, void* stream) {
+    if (K <= 0 || K > kMaxSelectK || n_salient < 0 || n_salient > K) return AWQ_ERR_SHAPE;
+    if (n_salient == 0) return AWQ_OK;
+    if (!m_f64 || !idx) return AWQ_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(m_f64) & 7) || (reinterpret_cast<uintptr_t>(idx) & 3)) return AWQ_ERR_ALIGN;
+    return launch_select_salient(m_f64, K, n_salient, idx, as_stream(stream));
+}
+
+awq_status awq_quantize_salient(const void* w_f16, int64_t N, int64_t K, int group_size, int mode, const int* idx,
+                                int n_salient, uint32_t* qweight, void* scales_f16, void* zeros_f16,
+                                void* w_salient_f16, void* stream) {
+    awq_status st = check_dims(N, K, group_size);
+    if (st != AWQ_OK) return st;
+    if (N * K > kMaxElems || n_salient < 0 || n_salient > K) return AWQ_ERR_SHAPE;
+    if (mode != AWQ_QUANT_ASYMMETRIC && mode != AWQ_QUANT_SYMMETRIC) return AWQ_ERR_CONFIG;
+    if (N == 0) return AWQ_OK;
+    if (!w_f16 || !qweight || !scales_f16 || !zeros_f16 || (n_salient > 0 && (!idx || !w_salient_f16)))
+        return AWQ_ERR_NULL;
+    if (!aligned16(w_f16) || !aligned16(qweight) || (reinterpret_cast<uintptr_t>(scales_f16) & 1) ||
+        (reinterpret_cast<uintptr_t>(zeros_f16) & 1) || (reinterpret_cast<uintptr_t>(idx) & 3) ||
+        (reinterpret_cast<uintptr_t>(w_salient_f16) & 1))
+        return AWQ_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    const half_t* w = static_cast<const half_t*>(w_f16);
+    if ((st = launch_quantize(w, nullptr, N, K, group_size, mode == AWQ_QUANT_SYMMETRIC, 0.0, qweight,
+                              static_cast<half_t*>(scales_f16), static_cast<half_t*>(zeros_f16), s)) != AWQ_OK)
+        return st;
+    return launch_salient_fix(w, N, K, group_size, idx, n_salient, qweight, static_cast<const half_t*>(zeros_f16),
+                              static_cast<half_t*>(w_salient_f16), s);
+}
+
+awq_status awq_salient_apply(const void* x_f16, const int* idx, const void* w_salient_f16, int64_t M, int64_t N,
+                             int64_t K, int n_salient, void* y_f16, void* stream) {
+    if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || n_salient < 0 || n_salient > K)
+        return AWQ_ERR_SHAPE;
+    if (M == 0 || N == 0 || n_salient == 0) return AWQ_OK;
+    if (!x_f16 || !idx || !w_salient_f16 || !y_f16) return AWQ_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(x_f16) & 1) || (reinterpret_cast<uintptr_t>(idx) & 3) ||
+        (reinterpret_cast<uintptr_t>(w_salient_f16) & 1) || (reinterpret_cast<uintptr_t>(y_f16) & 1))
+        return AWQ_ERR_ALIGN;
+    return launch_salient_apply(static_cast<const half_t*>(x_f16), idx, static_cast<const half_t*>(w_salient_f16), M,
+                                N, K, n_salient, static_cast<half_t*>(y_f16), as_stream(stream));
+}
+
+size_t awq_salient_loss_workspace_bytes(int64_t N, int64_t K, int64_t T, int group_size, int n_salient) {
+    if (check_dims(N, K, group_size) != AWQ_OK || N <= 0 || T <= 0 || n_salient < 0 || n_salient > K) return 0;
+    return SalientLayout(nullptr, N, K, T, group_size, n_salient).bytes;
+}
+
+awq_status awq_salient_loss(const void* w_f16, const void* x_f16, int64_t N, int64_t K, int64_t T, int group_size,
+                            int mode, int n_salient, void* workspace, size_t workspace_bytes, double* loss_rtn,
+                            double* loss_salient, int* idx_out, void* stream) {
+    awq_status st = check_dims(N, K, group_size);
+    if (st != AWQ_OK) return st;
+    if (N <= 0 || T <= 0 || T > (int64_t(1) << 24) || K % 8 != 0) return AWQ_ERR_SHAPE;
+    if (T > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return AWQ_ERR_SHAPE;
+    if (K > kMaxSelectK || n_salient < 0 || n_salient > K) return AWQ_ERR_SHAPE;
+    if (mode != AWQ_QUANT_ASYMMETRIC && mode != AWQ_QUANT_SYMMETRIC) return AWQ_ERR_CONFIG;
+    if (!w_f16 || !x_f16 || !workspace || !loss_rtn || !loss_salient) return AWQ_ERR_NULL;
+    if (!aligned16(w_f16) || !aligned16(x_f16) || !aligned16(workspace) ||
+        (reinterpret_cast<uintptr_t>(idx_out) & 3))
+        return AWQ_ERR_ALIGN;
+    SalientLayout L(workspace, N, K, T, group_size, n_salient);
+    if (workspace_bytes < L.bytes) return AWQ_ERR_WORKSPACE;
+    hipStream_t s = as_stream(stream);
+    const half_t* w = static_cast<const half_t*>(w_f16);
+    const half_t* x = static_cast<const half_t*>(x_f16);
+    const bool sym = mode == AWQ_QUANT_SYMMETRIC;
+
+    // salient channels from m = mean |x|
+    if ((st = launch_absmean(x, T, K, L.m, L.abs_partials, s)) != AWQ_OK) return st;
+    if ((st = launch_select_salient(L.m, K, n_salient, L.idx, s)) != AWQ_OK) return st;
+    // reference W . x^T; the plain quantizer's loss
+    if ((st = reference_output(x, w, T, N, K, group_size, L.yref, s)) != AWQ_OK) return st;
+    if ((st = launch_quantize(w, nullptr, N, K, group_size, sym, 0.0, L.qweight, L.scales, L.zeros, s)) != AWQ_OK)
+        return st;
+    if ((st = output_loss(x, L.qweight, L.scales, L.zeros, T, N, K, group_size, L.yref, L.tile_partials, L.losses,
+                          s)) != AWQ_OK)
+        return st;
+    // mixed layer: INT4 part with the salient codes at the zero-point, fp16
+    // side part moved to the reference: || x Q0^T - (W x^T - x_S W_S^T) ||^2
+    if ((st = launch_salient_fix(w, N, K, group_size, L.idx, n_salient, L.qweight, L.zeros, L.w_sal, s)) != AWQ_OK)
+        return st;
+    if ((st = launch_salient_subtract(x, L.idx, L.w_sal, T, N, K, n_salient, L.yref, s)) != AWQ_OK) return st;
+    if ((st = output_loss(x, L.qweight, L.scales, L.zeros, T, N, K, group_size, L.yref, L.tile_partials,
+                          L.losses + 1, s)) != AWQ_OK)
+        return st;
+    if (idx_out && n_salient > 0 &&
+        hipMemcpyAsync(idx_out, L.idx, sizeof(int) * n_salient, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return AWQ_ERR_HIP;
+    double host[2];
+    if (hipMemcpyAsync(host, L.losses, sizeof(host), hipMemcpyDeviceToHost, s) != hipSuccess) return AWQ_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return AWQ_ERR_HIP;
+    *loss_rtn = host[0];
+    *loss_salient = host[1];
     return AWQ_OK;
 }
 

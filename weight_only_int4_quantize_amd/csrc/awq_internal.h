@@ -101,6 +101,15 @@ awq_status launch_skinny(const half_t* x, const uint32_t* qweight, const half_t*
                          const half_t* zeros, int64_t M, int64_t N, int64_t K, int group_size,
                          half_t* y, void* workspace, hipStream_t stream);
 
+// Mixed precision with fp16 salient channels.
+awq_status launch_select_salient(const double* m, int64_t K, int n, int* idx, hipStream_t stream);
+awq_status launch_salient_fix(const half_t* w, int64_t N, int64_t K, int group_size, const int* idx, int n_sal,
+                              uint32_t* qweight, const half_t* zeros, half_t* w_sal, hipStream_t stream);
+awq_status launch_salient_apply(const half_t* x, const int* idx, const half_t* w_sal, int64_t M, int64_t N,
+                                int64_t K, int n_sal, half_t* y, hipStream_t stream);
+awq_status launch_salient_subtract(const half_t* x, const int* idx, const half_t* w_sal, int64_t M, int64_t N,
+                                   int64_t K, int n_sal, float* y32, hipStream_t stream);
+
 // Scale-search helpers.
 size_t absmean_workspace_bytes(int64_t T, int64_t K);
 awq_status launch_absmean(const half_t* x, int64_t T, int64_t K, double* m, double* partials,
