@@ -41,4 +41,10 @@ from .awq_oracle import (  # noqa: F401
     dequantize_salient,
     linear_salient_ref,
     salient_loss,
+    group_quantize_bits,
+    pack_codes8,
+    unpack_codes8,
+    quantize_w8,
+    dequantize_w8,
+    linear_ref_w8,
 )
