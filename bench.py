@@ -18,6 +18,7 @@ The same run also times, each in its own section:
   * batched decode rows on the skinny MFMA kernel (M = 16 on the decode
     shapes, M = 32 on the 13B/70B sweep shapes);
   * the roofline GEMV at group sizes 32, 64, 128, 256 and 512;
+  * the W8A16 form (8-bit weights): the roofline GEMV and the prefill GEMM;
   * the prefill GEMM, x[2048, K] times the two MLP shapes;
   * the quantize kernel on 11008x4096;
   * one full scale search (W[11008, 4096], X[65536, 4096], 20 alphas), the
@@ -296,6 +297,43 @@ class Bench:
         torch.cuda.synchronize()
         return out
 
+    def run_w8(self):
+        """W8A16 (8-bit weights, fp16 activations): the decode GEMV on the
+        roofline shape (weights rotated over copies) and the prefill GEMM."""
+        torch, awq = self.torch, self.awq
+        N, K = ROOFLINE_SHAPE
+        lay = synth.decode_layer(N, K, 1, G)
+        qw, sc, zr = awq.awq_quantize_w8(self.d(lay["w"]), G)
+        x = self.d(lay["x"])
+        nbytes = N * K + N * (K // G) * 4 + K * 2 + N * 2
+        n_copies = max(2, int(np.ceil(1.2e9 / nbytes)))
+        cps = [(qw.clone(), sc.clone(), zr.clone()) for _ in range(n_copies)]
+        y = torch.empty((1, N), dtype=torch.float16, device=self.dev)
+
+        def one(i):
+            q = cps[i % len(cps)]
+            awq.awq_gemm_w8(x, q[0], q[1], q[2], G, out=y)
+
+        gr = self.capture(one, 4 * n_copies)
+        gr.replay()
+        t = self.time(lambda _: gr.replay()) / (4 * n_copies)
+        log(f"w8 gemv {N}x{K}: {t * 1e6:.2f} us, {nbytes / t / 1e9:.0f} GB/s")
+        del cps, gr
+        out = {"gemv_m1": {"shape": f"{N}x{K}", "us": round(t * 1e6, 2), "bytes": nbytes,
+                           "GB/s": round(nbytes / t / 1e9, 1), "frac_of_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}}
+        M = synth.PREFILL_M
+        lay = synth.prefill_layer(N, K)
+        qw, sc, zr = awq.awq_quantize_w8(self.d(lay["w"]), G)
+        xm = self.d(lay["x"])
+        ym = torch.empty((M, N), dtype=torch.float16, device=self.dev)
+        for i in range(5):
+            awq.awq_gemm_w8(xm, qw, sc, zr, G, out=ym)
+        t = self.time(lambda i: awq.awq_gemm_w8(xm, qw, sc, zr, G, out=ym), 50) / 50
+        flop = 2.0 * M * N * K
+        log(f"w8 gemm M={M} {N}x{K}: {t * 1e6:.1f} us, {flop / t / 1e12:.0f} TFLOP/s")
+        out["gemm_m2048"] = {"shape": f"{M}x{N}x{K}", "us": round(t * 1e6, 2), "TFLOP/s": round(flop / t / 1e12, 1)}
+        return out
+
     def run_launch_floor(self):
         """Per-node cost of a HIP graph of tiny kernels (a one-element fill):
         the floor under every back-to-back launch timed here."""
@@ -540,7 +578,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true")
     ap.add_argument("--only", choices=["decode", "decode-fused", "gemv-roofline", "skinny", "gemm", "quantize",
-                                       "search", "copy"],
+                                       "search", "copy", "w8"],
                     help="run one section (for profiler runs); timings go to stderr")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -566,6 +604,8 @@ def main():
             b.run_quantize()
         elif args.only == "search":
             b.run_search()
+        elif args.only == "w8":
+            b.run_w8()
         else:
             b.run_copy()
         return
@@ -579,6 +619,7 @@ def main():
     floor_us = b.run_launch_floor()
     skinny = b.run_skinny()
     groups = b.run_group_sizes()
+    w8 = b.run_w8()
     copy = b.run_copy()
     gemm = b.run_gemm()
     quant = b.run_quantize()
@@ -616,6 +657,7 @@ def main():
         "decode_fused": fused,
         "skinny_batched_decode": skinny,
         "gemv_group_sizes": groups,
+        "w8a16": w8,
         "gemm": gemm,
         "quantize": quant,
         "scale_search": search,

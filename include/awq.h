@@ -375,6 +375,52 @@ awq_status awq_salient_loss(const void* w_f16, const void* x_f16, int64_t N,
                             size_t workspace_bytes, double* loss_rtn,
                             double* loss_salient, int* idx_out, void* stream);
 
+/*
+ * W8A16: 8-bit weights with fp16 activations (aissn.com "INT8 vs INT4" and
+ * "INT8 实战": the steadier choice, weight INT8 with activations kept in
+ * fp16). The map of xxmr.cn §1.2 with 2^8 levels, group-wise as the INT4
+ * form: asymmetric scale = range / 255, zero-point in [0, 255]; symmetric
+ * scale = max|w| / 127, code = q + 128, zero-point 128. Four codes per
+ * uint32 along K, the code of column k = 4c + j in bits 8j..8j+7 of word c.
+ */
+
+/*
+ * awq_quantize_w8 - group-wise 8-bit quantization of W[N, K].
+ *
+ *   w_f16          device, fp16 [N, K], 16-byte aligned
+ *   channel_scale  device, fp32 [K] (quantize W . diag(s)) or NULL
+ *   N, K           N >= 0, K > 0, K % group_size == 0
+ *   group_size     64, 128, 256 or 512
+ *   mode           AWQ_QUANT_ASYMMETRIC or AWQ_QUANT_SYMMETRIC
+ *   qweight        device, uint32 [N, K/4] (output), 16-byte aligned
+ *   scales_f16, zeros_f16   device, fp16 [N, K/group_size] (outputs)
+ * Asynchronous on `stream`.
+ */
+awq_status awq_quantize_w8(const void* w_f16, const float* channel_scale,
+                           int64_t N, int64_t K, int group_size, int mode,
+                           uint32_t* qweight, void* scales_f16,
+                           void* zeros_f16, void* stream);
+
+/*
+ * awq_gemm_w8 - the W8A16 linear layer y = x . dequant(Wq)^T (fp32
+ * accumulation, fp16 output), Wq from awq_quantize_w8.
+ *
+ *   x_f16        device, fp16 [M, K], 16-byte aligned
+ *   qweight      device, uint32 [N, K/4], 16-byte aligned
+ *   scales_f16, zeros_f16   device, fp16 [N, K/group_size]
+ *   group_size   64, 128, 256 or 512
+ *   y_f16        device, fp16 [M, N] (output)
+ *   path         0 = automatic (the GEMV for M <= 8, else the MFMA GEMM),
+ *                1 = GEMV (M <= 8), 2 = MFMA GEMM (K * 512 < 2^31)
+ *   workspace    as awq_gemm_ex (stream-K splits of the GEMM) or NULL
+ * M == 0 or N == 0 returns AWQ_OK without work. Asynchronous on `stream`.
+ */
+awq_status awq_gemm_w8(const void* x_f16, const uint32_t* qweight,
+                       const void* scales_f16, const void* zeros_f16,
+                       int64_t M, int64_t N, int64_t K, int group_size,
+                       void* y_f16, int path, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

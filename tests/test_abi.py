@@ -236,3 +236,23 @@ def test_salient_checks(L):
     assert s(FAKE, None, 256, 512, 1024, 128, 0, 5, FAKE, need, pr, ps, None, None) == NULL
     assert s(FAKE, FAKE, 256, 512, 1024, 128, 0, 5, FAKE, need, None, ps, None, None) == NULL
     assert s(FAKE, FAKE_ODD, 256, 512, 1024, 128, 0, 5, FAKE, need, pr, ps, None, None) == ALIGN
+
+
+def test_w8_checks(L):
+    q = L.awq_quantize_w8
+    assert q(FAKE, None, 16, 256, 32, 0, FAKE, FAKE, FAKE, None) == CONFIG      # W8 takes G >= 64
+    assert q(FAKE, None, 16, 256, 64, 2, FAKE, FAKE, FAKE, None) == CONFIG      # mode
+    assert q(FAKE, None, 16, 200, 64, 0, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(None, None, 16, 256, 64, 0, FAKE, FAKE, FAKE, None) == NULL
+    assert q(FAKE, FAKE_ODD, 16, 256, 64, 0, FAKE, FAKE, FAKE, None) == ALIGN
+    assert q(FAKE, None, 0, 256, 64, 0, FAKE, FAKE, FAKE, None) == OK           # empty N
+    g = L.awq_gemm_w8
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 16, 256, 32, FAKE, 0, None, 0, None) == CONFIG
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 16, 256, 64, FAKE, 3, None, 0, None) == CONFIG   # no skinny path
+    assert g(FAKE, FAKE, FAKE, FAKE, 9, 16, 256, 64, FAKE, 1, None, 0, None) == CONFIG   # GEMV is M <= 8
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 16, 1 << 22, 64, FAKE, 2, None, 0, None) == CONFIG
+    assert g(FAKE, FAKE, FAKE, FAKE, -1, 16, 256, 64, FAKE, 0, None, 0, None) == SHAPE
+    assert g(FAKE, None, FAKE, FAKE, 4, 16, 256, 64, FAKE, 0, None, 0, None) == NULL
+    assert g(FAKE_ODD, FAKE, FAKE, FAKE, 4, 16, 256, 64, FAKE, 0, None, 0, None) == ALIGN
+    assert g(FAKE, FAKE, FAKE, FAKE, 100, 16, 256, 64, FAKE, 2, FAKE, 16, None) == WORKSPACE
+    assert g(FAKE, FAKE, FAKE, FAKE, 0, 16, 256, 64, FAKE, 0, None, 0, None) == OK

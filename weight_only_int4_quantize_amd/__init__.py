@@ -96,6 +96,10 @@ def load() -> ctypes.CDLL:
     L.awq_salient_loss.restype = c_int
     L.awq_salient_loss.argtypes = [c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_sz, c_vp, c_vp,
                                    c_vp, c_vp]
+    L.awq_quantize_w8.restype = c_int
+    L.awq_quantize_w8.argtypes = [c_vp, c_vp, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp]
+    L.awq_gemm_w8.restype = c_int
+    L.awq_gemm_w8.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_int, c_vp, c_sz, c_vp]
     _lib = L
     return L
 
@@ -386,3 +390,46 @@ def awq_salient_loss(w, x, group_size: int = 128, n_salient: int | None = None, 
                             _stream(w.device))
     _check("awq_salient_loss", st)
     return float(lr[0]), float(ls[0]), idx
+
+
+# ---------------------------------------------------------------- W8A16
+
+def awq_quantize_w8(w, group_size: int = 128, channel_scale=None, symmetric: bool = False, out=None):
+    """awq_quantize_w8: (qweight int32 [N, K/4] holding the uint32 words,
+    scales fp16 [N, K/G], zeros fp16 [N, K/G])."""
+    torch = _torch()
+    _need_gpu("w", w, torch.float16)
+    N, K = w.shape
+    if channel_scale is not None:
+        _need_gpu("channel_scale", channel_scale, torch.float32)
+    if out is None:
+        ng = K // group_size if group_size > 0 else 0
+        out = (torch.empty((N, max(K // 4, 0)), dtype=torch.int32, device=w.device),
+               torch.empty((N, ng), dtype=torch.float16, device=w.device),
+               torch.empty((N, ng), dtype=torch.float16, device=w.device))
+    qweight, scales, zeros = out
+    mode = QUANT_SYMMETRIC if symmetric else QUANT_ASYMMETRIC
+    st = load().awq_quantize_w8(_ptr(w), _ptr(channel_scale), N, K, group_size, mode, _ptr(qweight), _ptr(scales),
+                                _ptr(zeros), _stream(w.device))
+    _check("awq_quantize_w8", st)
+    return qweight, scales, zeros
+
+
+def awq_gemm_w8(x, qweight, scales, zeros, group_size: int = 128, path: int = PATH_AUTO, out=None, workspace=None):
+    """awq_gemm_w8: y = x . dequant(Wq)^T for the W8 form (path 0 auto,
+    1 GEMV, 2 GEMM)."""
+    torch = _torch()
+    _need_gpu("x", x, torch.float16)
+    _need_gpu("qweight", qweight, torch.int32)
+    _need_gpu("scales", scales, torch.float16)
+    _need_gpu("zeros", zeros, torch.float16)
+    M, K = x.shape
+    N = qweight.shape[0]
+    if qweight.shape != (N, K // 4):
+        raise ValueError("qweight must be [N, K/4]")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
+    nbytes = workspace.numel() if workspace is not None else 0
+    st = load().awq_gemm_w8(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), M, N, K, group_size, _ptr(y), path,
+                            _ptr(workspace), nbytes, _stream(x.device))
+    _check("awq_gemm_w8", st)
+    return y

@@ -486,4 +486,63 @@ awq_status awq_salient_loss(const void* w_f16, const void* x_f16, int64_t N, int
     return AWQ_OK;
 }
 
+awq_status awq_quantize_w8(const void* w_f16, const float* channel_scale, int64_t N, int64_t K, int group_size,
+                           int mode, uint32_t* qweight, void* scales_f16, void* zeros_f16, void* stream) {
+    awq_status st = check_dims(N, K, group_size);
+    if (st != AWQ_OK) return st;
+    if (group_size < 64) return AWQ_ERR_CONFIG;
+    if (N * K > kMaxElems) return AWQ_ERR_SHAPE;
+    if (mode != AWQ_QUANT_ASYMMETRIC && mode != AWQ_QUANT_SYMMETRIC) return AWQ_ERR_CONFIG;
+    if (N == 0) return AWQ_OK;
+    if (!w_f16 || !qweight || !scales_f16 || !zeros_f16) return AWQ_ERR_NULL;
+    if (!aligned16(w_f16) || !aligned16(qweight) || (channel_scale && !aligned16(channel_scale)) ||
+        (reinterpret_cast<uintptr_t>(scales_f16) & 1) || (reinterpret_cast<uintptr_t>(zeros_f16) & 1))
+        return AWQ_ERR_ALIGN;
+    return launch_quantize(static_cast<const half_t*>(w_f16), channel_scale, N, K, group_size,
+                           mode == AWQ_QUANT_SYMMETRIC, 0.0, qweight, static_cast<half_t*>(scales_f16),
+                           static_cast<half_t*>(zeros_f16), as_stream(stream), 8);
+}
+
+awq_status awq_gemm_w8(const void* x_f16, const uint32_t* qweight, const void* scales_f16, const void* zeros_f16,
+                       int64_t M, int64_t N, int64_t K, int group_size, void* y_f16, int path, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    awq_status st = check_dims(N, K, group_size);
+    if (st != AWQ_OK) return st;
+    if (group_size < 64) return AWQ_ERR_CONFIG;
+    if (path < 0 || path > 2) return AWQ_ERR_CONFIG;
+    if (M < 0 || M > kMaxDim) return AWQ_ERR_SHAPE;
+    if (M > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return AWQ_ERR_SHAPE;
+    if (M == 0 || N == 0) return AWQ_OK;
+    if (!x_f16 || !qweight || !scales_f16 || !zeros_f16 || !y_f16) return AWQ_ERR_NULL;
+    if (!aligned16(x_f16) || !aligned16(qweight) || (reinterpret_cast<uintptr_t>(scales_f16) & 1) ||
+        (reinterpret_cast<uintptr_t>(zeros_f16) & 1) || (reinterpret_cast<uintptr_t>(y_f16) & 1))
+        return AWQ_ERR_ALIGN;
+    const half_t* x = static_cast<const half_t*>(x_f16);
+    const half_t* sc = static_cast<const half_t*>(scales_f16);
+    const half_t* zr = static_cast<const half_t*>(zeros_f16);
+    half_t* y = static_cast<half_t*>(y_f16);
+    const bool gemv_ok = gemv_supported(M, K, 8);
+    if (path == 1 && !gemv_ok) return AWQ_ERR_CONFIG;
+    // the MFMA form needs 32-bit byte offsets within a 256-row tile of x
+    if (path == 2 && K * 256 * 2 >= (int64_t(1) << 31)) return AWQ_ERR_CONFIG;
+    if (path == 1 || (path == 0 && gemv_ok))
+        return launch_gemv(x, qweight, sc, zr, M, N, K, group_size, y, as_stream(stream), 8);
+    if (K * 256 * 2 >= (int64_t(1) << 31)) return AWQ_ERR_SHAPE;
+    if (workspace != nullptr) {
+        if (reinterpret_cast<uintptr_t>(workspace) & 255) return AWQ_ERR_ALIGN;
+        if (workspace_bytes < gemm_workspace_bytes(M, N)) return AWQ_ERR_WORKSPACE;
+    }
+    GemmArgs a;
+    a.a = x;
+    a.qweight = qweight;
+    a.scales = sc;
+    a.zeros = zr;
+    a.group_size = group_size;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.y16 = y;
+    return launch_gemm(a, GemmB::kInt8, GemmOut::kF16, as_stream(stream), workspace);
+}
+
 }  // extern "C"

@@ -48,19 +48,21 @@ inline awq_status last_launch_status() { return hip_status(hipGetLastError()); }
 // asymmetric (the group's [min, max]) or symmetric (max |w| -> +-7, zero 8),
 // after an optional percentile clip of each group (clip_fraction in [0, 0.25)).
 bool clip_fraction_ok(double p);
+// bits = 8 gives the W8A16 form (4 codes per word, 255 levels).
 awq_status launch_quantize(const half_t* w, const float* channel_scale, int64_t N, int64_t K,
                            int group_size, bool symmetric, double clip_fraction, uint32_t* qweight,
-                           half_t* scales, half_t* zeros, hipStream_t stream);
+                           half_t* scales, half_t* zeros, hipStream_t stream, int bits = 4);
 
 // Decode GEMV y[M, N] = x[M, K] . dequant(Wq)^T for M <= kGemvMaxM.
 constexpr int kGemvMaxM = 8;
-bool gemv_supported(int64_t M, int64_t K);
+// bits = 8: the W8A16 form (qweight [N, K/4], four byte codes per word).
+bool gemv_supported(int64_t M, int64_t K, int bits = 4);
 awq_status launch_gemv(const half_t* x, const uint32_t* qweight, const half_t* scales,
                        const half_t* zeros, int64_t M, int64_t N, int64_t K, int group_size,
-                       half_t* y, hipStream_t stream);
+                       half_t* y, hipStream_t stream, int bits = 4);
 
-// MFMA GEMM. The B operand is either INT4 (qweight/scales/zeros) or fp16 W[N, K].
-enum class GemmB { kInt4, kF16 };
+// MFMA GEMM. The B operand is INT4 or W8 (qweight/scales/zeros) or fp16 W[N, K].
+enum class GemmB { kInt4, kF16, kInt8 };
 enum class GemmOut { kF16, kF32, kLoss };
 struct GemmArgs {
     const half_t* a = nullptr;        // [M, K]

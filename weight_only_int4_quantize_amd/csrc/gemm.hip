@@ -98,6 +98,21 @@ __device__ inline uint4 unpack_word(uint32_t wq, half2_t zc_hi, half2_t zc_lo, c
     return r;
 }
 
+// Two W8 words (byte codes k0..k7) -> 8 exact fp16 values (b - z), natural k
+// order. zc = 1024 + z (exact): (w & 0x00FF00FF) | 0x64006400 is
+// (1024 + b0, 1024 + b2), the same on w >> 8 gives (1024 + b1, 1024 + b3).
+__device__ inline uint4 unpack_bytes(uint32_t w0, uint32_t w1, half2_t zc) {
+    const uint32_t mask = 0x00FF00FFu, magic = 0x64006400u;
+    const uint32_t a0 = as_u32(as_h2((w0 & mask) | magic) - zc), b0 = as_u32(as_h2(((w0 >> 8) & mask) | magic) - zc);
+    const uint32_t a1 = as_u32(as_h2((w1 & mask) | magic) - zc), b1 = as_u32(as_h2(((w1 >> 8) & mask) | magic) - zc);
+    uint4 r;
+    r.x = __builtin_amdgcn_perm(b0, a0, 0x05040100u);   // (k0, k1)
+    r.y = __builtin_amdgcn_perm(b0, a0, 0x07060302u);   // (k2, k3)
+    r.z = __builtin_amdgcn_perm(b1, a1, 0x05040100u);   // (k4, k5)
+    r.w = __builtin_amdgcn_perm(b1, a1, 0x07060302u);   // (k6, k7)
+    return r;
+}
+
 // Registers carrying one K step from global memory to LDS.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -204,13 +219,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
     constexpr int TN = WTN / 32;                // 32x32 MFMA tiles per wave (N)
     constexpr int A_VECS = BM * BK / 8 / kThreads;        // uint4 of A per thread per step
     constexpr bool INT4 = BMODE == GemmB::kInt4;
+    constexpr int BITS = BMODE == GemmB::kInt8 ? 8 : 4;     // direct form: code width of B
+    constexpr int BW = BITS / 4;                            // 16-byte B loads per column and step
     constexpr int B_WORDS = BN * BK / 8 / kThreads;       // packed words per thread per step
     constexpr int B_VECS = BN * BK / 8 / kThreads;        // fp16 B: uint4 per thread per step (int4: unused)
     constexpr int ACC = TM * TN * 16;                     // accumulators per lane
     static_assert(TM >= 1 && TN >= 1 && A_VECS >= 1, "tile shape");
     static_assert(!INT4 || B_WORDS == 2, "int4 B staging: 2 words (16 codes) per thread");
     static_assert(INT4 || B_VECS >= 1, "fp16 B staging");
-    static_assert(!DIRECT || INT4, "the direct form is for INT4 B");
+    static_assert(!DIRECT || BMODE != GemmB::kF16, "the direct form is for quantized B");
+    static_assert(DIRECT || BMODE != GemmB::kInt8, "W8 B runs the direct form only");
     constexpr int LDS_A = DIRECT ? BM * BKD : BM * LDK;
     constexpr int LDS_B = DIRECT ? 8 : BN * LDK;
 
@@ -377,7 +395,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
         const auto a_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(args.a) + static_cast<int64_t>(tm) * K,
                                                             0, rows_a * K * 2, 0x00020000);
         const auto b_rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint32_t*>(args.qweight) + static_cast<int64_t>(tn) * (K / 8), 0, cols_b * (K / 2), 0x00020000);
+            const_cast<uint32_t*>(args.qweight) + static_cast<int64_t>(tn) * (K * BITS / 32), 0,
+            cols_b * (K * BITS / 8), 0x00020000);
         const auto s_rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<half_t*>(args.scales) + static_cast<int64_t>(tn) * ngroups, 0, cols_b * ngroups * 2, 0x00020000);
         const auto z_rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -389,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int n = min(wn + j * 32 + lcol, cols_b - 1);
-            b_off[j] = n * (K / 2) + lh * 16;
+            b_off[j] = n * (K * BITS / 8) + lh * (4 * BITS);
             sz_off[j] = n * ngroups * 2;
         }
         auto s_bits_at = [&](int j, int gg) {
@@ -412,16 +431,19 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
 
         const int last = ke - 1;
         u32x4 areg[AV];
-        u32x4 b0[TN], b1[TN];
+        u32x4 b0[TN][BW], b1[TN][BW];
         auto load_a = [&](int kt) {
             const int k0 = uniform(min(kt, last) * BKD * 2);
 #pragma unroll
             for (int i = 0; i < AV; ++i) areg[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off[i], k0, 0);
         };
-        auto load_b = [&](u32x4 (&dst)[TN], int kt) {
-            const int w0 = uniform(min(kt, last) * (BKD / 2));
+        auto load_b = [&](u32x4 (&dst)[TN][BW], int kt) {
+            const int w0 = uniform(min(kt, last) * (BKD * BITS / 8));
 #pragma unroll
-            for (int j = 0; j < TN; ++j) dst[j] = __builtin_amdgcn_raw_buffer_load_b128(b_rs, b_off[j], w0, 0);
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int v = 0; v < BW; ++v)
+                    dst[j][v] = __builtin_amdgcn_raw_buffer_load_b128(b_rs, b_off[j] + 16 * v, w0, 0);
         };
         auto store_a = [&](half_t* as) {
 #pragma unroll
@@ -448,7 +470,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
             z_next[j] = z_bits_at(j, min(g + 1, ngroups - 1));
         }
 
-        auto step = [&](int kt, const half_t* cur, half_t* nxt, const u32x4 (&bw)[TN], u32x4 (&bn)[TN]) {
+        auto step = [&](int kt, const half_t* cur, half_t* nxt, const u32x4 (&bw)[TN][BW], u32x4 (&bn)[TN][BW]) {
             if (kt + 1 < ke) store_a(nxt);
             load_a(kt + 2);
             load_b(bn, kt + 1);
@@ -483,8 +505,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
                 for (int i = 0; i < TM; ++i)
                     a[i] = *reinterpret_cast<const half8_t*>(&cur[swz64(wm + i * 32 + lrow, lh * 4 + ks)]);
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    b[j] = __builtin_bit_cast(half8_t, unpack_word(bw[j][ks], zc_hi[j], zc_lo[j], uk));
+                for (int j = 0; j < TN; ++j) {
+                    if constexpr (BITS == 4)
+                        b[j] = __builtin_bit_cast(half8_t, unpack_word(bw[j][0][ks], zc_hi[j], zc_lo[j], uk));
+                    else
+                        b[j] = __builtin_bit_cast(half8_t, unpack_bytes(bw[j][ks / 2][(ks % 2) * 2],
+                                                                        bw[j][ks / 2][(ks % 2) * 2 + 1], zc_hi[j]));
+                }
             };
             fetch(0, af[0], bf[0]);
 #pragma unroll
@@ -732,9 +759,11 @@ void launch_cfg(const GemmArgs& args, void* workspace, hipStream_t stream) {
 // along N (256 x 32 each): a wave's unpack work per MFMA halves against the
 // 2 x 2 arrangement (whose wave pairs would unpack the same columns twice).
 constexpr int kDirectWgm = 1;
+bool direct_ok(const GemmArgs& args) { return args.group_size >= BKD && args.K * kBM * 2 < (int64_t{1} << 31); }
+
 template <GemmOut OMODE>
 void launch_int4(const GemmArgs& args, void* workspace, hipStream_t stream) {
-    if (args.group_size >= BKD && args.K * kBM * 2 < (int64_t{1} << 31))
+    if (direct_ok(args))
         launch_cfg<GemmB::kInt4, OMODE, true, kDirectWgm>(args, workspace, stream);
     else
         launch_cfg<GemmB::kInt4, OMODE, false>(args, workspace, stream);
@@ -752,7 +781,11 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N) {
 
 awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t stream, void* workspace) {
     if (args.M == 0 || args.N == 0) return AWQ_OK;
-    if (b == GemmB::kInt4) {
+    if (b == GemmB::kInt8) {
+        // W8 B: the direct form only, fp16 output
+        if (!direct_ok(args) || out != GemmOut::kF16) return AWQ_ERR_CONFIG;
+        launch_cfg<GemmB::kInt8, GemmOut::kF16, true, kDirectWgm>(args, workspace, stream);
+    } else if (b == GemmB::kInt4) {
         switch (out) {
             case GemmOut::kF16: launch_int4<GemmOut::kF16>(args, workspace, stream); break;
             case GemmOut::kF32: launch_int4<GemmOut::kF32>(args, workspace, stream); break;

@@ -1,4 +1,5 @@
 // Decode GEMV of the W4A16 linear layer, y[M, N] = x[M, K] . dequant(Wq)^T
+// (and of the W8A16 form, BITS = 8: a 16-byte chunk holds 16 byte codes)
 // for small M (single-stream decode: the "GEMV" kernel choice of the rskf.cn
 // AWQ article, §3.3; the dequantize-in-the-matmul step of §1.3). Decode is
 // bound by streaming the packed weights from HBM, so the kernel is built to
@@ -52,8 +53,10 @@ __device__ inline float h_hi(uint32_t u) {
 struct UnpackConsts {
     uint32_t lo_mask, hi_mask, lo_magic, hi_magic;
 };
+template <int BITS>
 __device__ inline UnpackConsts unpack_consts() {
-    UnpackConsts k{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
+    UnpackConsts k = BITS == 4 ? UnpackConsts{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u}
+                               : UnpackConsts{0x00FF00FFu, 0x00FF00FFu, 0x64006400u, 0x64006400u};
     asm volatile("" : "+v"(k.lo_mask), "+v"(k.hi_mask), "+v"(k.lo_magic), "+v"(k.hi_magic));
     return k;
 }
@@ -72,6 +75,24 @@ __device__ inline float word_dot(uint32_t wq, const uint4& p, float acc, const U
     return acc;
 }
 
+// dot of one W8 word (4 byte codes) with its 2 x pairs (x0, x2), (x1, x3):
+//   (w & 0x00FF00FF) | 0x64006400 = (1024 + b0, 1024 + b2), the same on w >> 8
+__device__ inline float byte_dot(uint32_t wq, uint32_t p_even, uint32_t p_odd, float acc, const UnpackConsts& k) {
+    const uint32_t a = (wq & k.lo_mask) | k.lo_magic;
+    const uint32_t b = ((wq >> 8) & k.hi_mask) | k.hi_magic;
+    acc = __builtin_amdgcn_fdot2(as_h2(a), as_h2(p_even), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(b), as_h2(p_odd), acc, false);
+    return acc;
+}
+
+// Chunk geometry: a chunk is one 16-byte load of packed weights per lane:
+// 32 INT4 or 16 W8 weights, staged against XV uint4 of x pairs.
+template <int BITS>
+struct Chunk {
+    static constexpr int kShift = BITS == 4 ? 5 : 4;     // log2(weights per chunk)
+    static constexpr int kXV = BITS == 4 ? 4 : 2;        // uint4 of x pairs per chunk
+};
+
 template <int RPW, int CPL>
 struct WeightBatch {
     uint4 w[RPW][CPL];
@@ -89,7 +110,7 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* p, int bytes) {
 // Issues the loads of one item: RPW rows x CPL chunks per lane (chunk
 // c = base + lane + 64 j), with each chunk's scale and zero-point. Rows past
 // N or items past the wave's last (valid == false) read as zero.
-template <int RPW, int CPL>
+template <int BITS, int RPW, int CPL>
 __device__ inline void load_batch(WeightBatch<RPW, CPL>& b, const uint32_t* __restrict__ qweight,
                                   const half_t* __restrict__ scales, const half_t* __restrict__ zeros,
                                   int row0, bool valid, int N, int nchunk, int ngroups, int log2g, int base,
@@ -105,7 +126,7 @@ __device__ inline void load_batch(WeightBatch<RPW, CPL>& b, const uint32_t* __re
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = base + lane + 64 * j;
-            const int g = (c << 5) >> log2g;
+            const int g = (c << Chunk<BITS>::kShift) >> log2g;
             b.w[i][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, c * 16, 0, 0));
             b.s[i][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, g * 2, 0, 0);
             b.z[i][j] = __builtin_amdgcn_raw_buffer_load_b16(rz, g * 2, 0, 0);
@@ -115,7 +136,7 @@ __device__ inline void load_batch(WeightBatch<RPW, CPL>& b, const uint32_t* __re
 
 // Consumes one item: chunks past the row end have scale 0 (zero-filled
 // loads) and read a clamped, in-range slot of the staged x.
-template <int MT, int RPW, int CPL>
+template <int BITS, int MT, int RPW, int CPL>
 __device__ inline void compute_batch(const WeightBatch<RPW, CPL>& b, const uint4* __restrict__ xp,
                                      const float2* __restrict__ xo, float (&acc)[RPW][MT], int nchunk,
                                      int base, int lane, const UnpackConsts& k) {
@@ -124,16 +145,25 @@ __device__ inline void compute_batch(const WeightBatch<RPW, CPL>& b, const uint4
         const int c = min(base + lane + 64 * j, nchunk - 1);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const uint4* pp = xp + (m * nchunk + c) * 4;
-            const uint4 p0 = pp[0], p1 = pp[1], p2 = pp[2], p3 = pp[3];
+            const uint4* pp = xp + (m * nchunk + c) * Chunk<BITS>::kXV;
             const float2 o = xo[m * nchunk + c];
+            uint4 p[Chunk<BITS>::kXV];
+#pragma unroll
+            for (int v = 0; v < Chunk<BITS>::kXV; ++v) p[v] = pp[v];
 #pragma unroll
             for (int i = 0; i < RPW; ++i) {
                 float d = 0.f;
-                d = word_dot(b.w[i][j].x, p0, d, k);
-                d = word_dot(b.w[i][j].y, p1, d, k);
-                d = word_dot(b.w[i][j].z, p2, d, k);
-                d = word_dot(b.w[i][j].w, p3, d, k);
+                if constexpr (BITS == 4) {
+                    d = word_dot(b.w[i][j].x, p[0], d, k);
+                    d = word_dot(b.w[i][j].y, p[1], d, k);
+                    d = word_dot(b.w[i][j].z, p[2], d, k);
+                    d = word_dot(b.w[i][j].w, p[Chunk<BITS>::kXV - 1], d, k);
+                } else {
+                    d = byte_dot(b.w[i][j].x, p[0].x, p[0].y, d, k);
+                    d = byte_dot(b.w[i][j].y, p[0].z, p[0].w, d, k);
+                    d = byte_dot(b.w[i][j].z, p[Chunk<BITS>::kXV - 1].x, p[Chunk<BITS>::kXV - 1].y, d, k);
+                    d = byte_dot(b.w[i][j].w, p[Chunk<BITS>::kXV - 1].z, p[Chunk<BITS>::kXV - 1].w, d, k);
+                }
                 const float s = static_cast<float>(__builtin_bit_cast(half_t, b.s[i][j]));
                 const float z = static_cast<float>(__builtin_bit_cast(half_t, b.z[i][j]));
                 acc[i][m] += s * (d - (o.x + z * o.y));
@@ -167,7 +197,7 @@ __device__ inline float wave_sum_lane63(float v) {
 // DEPTH - 1 are still loading, and its slot is refilled with item t + DEPTH
 // right after. The loads are branch-free, so the compiler's wait counts track
 // the ring exactly. Finished rows go to LDS and are written out at the end.
-template <int MT, int RPW, int CPL, int DEPTH, bool ONESHOT>
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT>
 __global__ __launch_bounds__(256) void gemv_kernel(const half_t* __restrict__ x,
                                                    const uint32_t* __restrict__ qweight,
                                                    const half_t* __restrict__ scales,
@@ -175,9 +205,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const half_t* __restrict__ x,
                                                    half_t* __restrict__ y, int N, int K,
                                                    int log2g, int max_sets) {
     extern __shared__ uint4 smem[];
-    const int nchunk = K >> 5;                      // 32 weights per chunk
-    uint4* xp = smem;                               // [MT][nchunk][4] x pairs
-    float2* xo = reinterpret_cast<float2*>(smem + MT * nchunk * 4);  // [MT][nchunk] (off, xs)
+    constexpr int XV = Chunk<BITS>::kXV;
+    const int nchunk = K >> Chunk<BITS>::kShift;    // 32 (INT4) or 16 (W8) weights per chunk
+    uint4* xp = smem;                               // [MT][nchunk][XV] x pairs
+    float2* xo = reinterpret_cast<float2*>(smem + MT * nchunk * XV);  // [MT][nchunk] (off, xs)
     float* yl = reinterpret_cast<float*>(xo + MT * nchunk);          // [4][max_sets][RPW][MT]
 
     // wave index as a scalar: the buffer descriptors built from it must be
@@ -196,31 +227,43 @@ __global__ __launch_bounds__(256) void gemv_kernel(const half_t* __restrict__ x,
     // x staging: one chunk of x (32 values per activation row) is loaded,
     // rearranged into the pairs word_dot expects and written to LDS with its
     // two sums.
-    auto load_x = [&](int c, uint4 (&r)[MT][4]) {
+    auto load_x = [&](int c, uint4 (&r)[MT][XV]) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const uint4* src = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(m) * K) + c * 4;
+            const uint4* src = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(m) * K) + c * XV;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) r[m][j] = src[j];
+            for (int j = 0; j < XV; ++j) r[m][j] = src[j];
         }
     };
-    auto store_x = [&](int c, const uint4 (&r)[MT][4]) {
+    auto store_x = [&](int c, const uint4 (&r)[MT][XV]) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             float even = 0.f, odd = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < XV; ++j) {
                 const uint4 v = r[m][j];  // halves (0,1) (2,3) (4,5) (6,7)
                 uint4 p;
-                p.x = (v.x & 0xFFFFu) | (v.z << 16);            // (x0, x4)
-                p.y = (v.x >> 16) | (v.z & 0xFFFF0000u);        // (x1, x5)
-                p.z = (v.y & 0xFFFFu) | (v.w << 16);            // (x2, x6)
-                p.w = (v.y >> 16) | (v.w & 0xFFFF0000u);        // (x3, x7)
-                xp[(m * nchunk + c) * 4 + j] = p;
+                if constexpr (BITS == 4) {
+                    // the pairs of one packed word: (x0, x4) (x1, x5) (x2, x6) (x3, x7)
+                    p.x = (v.x & 0xFFFFu) | (v.z << 16);
+                    p.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+                    p.z = (v.y & 0xFFFFu) | (v.w << 16);
+                    p.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+                } else {
+                    // the pairs of two W8 words: (x0, x2) (x1, x3) (x4, x6) (x5, x7)
+                    p.x = (v.x & 0xFFFFu) | (v.y << 16);
+                    p.y = (v.x >> 16) | (v.y & 0xFFFF0000u);
+                    p.z = (v.z & 0xFFFFu) | (v.w << 16);
+                    p.w = (v.z >> 16) | (v.w & 0xFFFF0000u);
+                }
+                xp[(m * nchunk + c) * XV + j] = p;
                 even += (h_lo(v.x) + h_lo(v.y)) + (h_lo(v.z) + h_lo(v.w));
                 odd += (h_hi(v.x) + h_hi(v.y)) + (h_hi(v.z) + h_hi(v.w));
             }
-            xo[m * nchunk + c] = make_float2(1024.0f * even + 64.0f * odd, even + odd);
+            // offsets the magic constants add: 1024 on even halves and 64 on
+            // odd halves of an INT4 word, 1024 on every W8 byte
+            const float off = BITS == 4 ? 1024.0f * even + 64.0f * odd : 1024.0f * (even + odd);
+            xo[m * nchunk + c] = make_float2(off, even + odd);
         }
     };
 
@@ -229,7 +272,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const half_t* __restrict__ x,
     //    first and can be consumed without waiting for the weights)
     constexpr int XPRE = MT <= 2 ? 2 : 1;
     const int c0 = threadIdx.x;
-    uint4 xr[XPRE][MT][4];
+    uint4 xr[XPRE][MT][XV];
 #pragma unroll
     for (int p = 0; p < XPRE; ++p)
         if (c0 + p * 256 < nchunk) load_x(c0 + p * 256, xr[p]);
@@ -237,7 +280,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const half_t* __restrict__ x,
     WeightBatch<RPW, CPL> ring[DEPTH];
     int l_item = 0, l_set = 0, l_kb = 0;            // load cursor
     auto issue = [&](WeightBatch<RPW, CPL>& b) {
-        load_batch(b, qweight, scales, zeros, (wid + l_set * W) * RPW, l_item < n_items, N, nchunk, ngroups,
+        load_batch<BITS>(b, qweight, scales, zeros, (wid + l_set * W) * RPW, l_item < n_items, N, nchunk, ngroups,
                    log2g, l_kb * 64 * CPL, lane);
         ++l_item;
         if (++l_kb == kbs) { l_kb = 0; ++l_set; }
@@ -262,12 +305,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(const half_t* __restrict__ x,
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[i][m] = 0.f;
     int c_set = 0, c_kb = 0;            // compute cursor
-    const UnpackConsts uk = unpack_consts();
+    const UnpackConsts uk = unpack_consts<BITS>();
     for (int t = 0; t < n_items; t += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             if (t + d < n_items) {
-                compute_batch(ring[d], xp, xo, acc, nchunk, c_kb * 64 * CPL, lane, uk);
+                compute_batch<BITS>(ring[d], xp, xo, acc, nchunk, c_kb * 64 * CPL, lane, uk);
                 if (++c_kb == kbs) {
                     // row set finished: reduce; lane 63 stores the sums (one-shot)
                     // or parks them in LDS (streaming: no stores among the loads)
@@ -328,15 +371,18 @@ int max_shared_bytes() {
     return cached;
 }
 
-size_t gemv_lds_bytes(int64_t M, int64_t K) { return static_cast<size_t>(M) * static_cast<size_t>(K / 32) * 72; }
+size_t gemv_lds_bytes(int64_t M, int64_t K, int bits) {
+    return bits == 4 ? static_cast<size_t>(M) * static_cast<size_t>(K / 32) * 72
+                     : static_cast<size_t>(M) * static_cast<size_t>(K / 16) * 40;
+}
 
-template <int MT, int RPW, int CPL, int DEPTH, bool ONESHOT = false>
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT = false>
 awq_status launch_t(const half_t* x, const uint32_t* qweight, const half_t* scales,
                     const half_t* zeros, int64_t N, int64_t K, int log2g, half_t* y,
                     int64_t blocks, hipStream_t stream) {
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<MT, RPW, CPL, DEPTH, ONESHOT>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, max_shared_bytes()) != hipSuccess)
             return AWQ_ERR_HIP;
         attr_set = true;
@@ -344,10 +390,11 @@ awq_status launch_t(const half_t* x, const uint32_t* qweight, const half_t* scal
     const int64_t sets = ceil_div(N, RPW);
     blocks = std::max<int64_t>(1, std::min<int64_t>(blocks, ceil_div(sets, 4)));
     const int64_t max_sets = ceil_div(sets, blocks * 4);
-    if (ONESHOT && max_sets * ceil_div(K / 32, 64 * CPL) > DEPTH) return AWQ_ERR_SHAPE;   // launch-shape bug
-    const size_t lds = gemv_lds_bytes(MT, K) + (ONESHOT ? 0 : static_cast<size_t>(4 * max_sets * RPW * MT) * sizeof(float));
+    const int64_t nchunk = K >> Chunk<BITS>::kShift;
+    if (ONESHOT && max_sets * ceil_div(nchunk, 64 * CPL) > DEPTH) return AWQ_ERR_SHAPE;   // launch-shape bug
+    const size_t lds = gemv_lds_bytes(MT, K, BITS) + (ONESHOT ? 0 : static_cast<size_t>(4 * max_sets * RPW * MT) * sizeof(float));
     if (lds > static_cast<size_t>(max_shared_bytes())) return AWQ_ERR_SHAPE;
-    hipLaunchKernelGGL((gemv_kernel<MT, RPW, CPL, DEPTH, ONESHOT>), dim3(static_cast<unsigned>(blocks)), dim3(256), lds,
+    hipLaunchKernelGGL((gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT>), dim3(static_cast<unsigned>(blocks)), dim3(256), lds,
                        stream, x, qweight, scales, zeros, y, static_cast<int>(N), static_cast<int>(K),
                        log2g, static_cast<int>(max_sets));
     return last_launch_status();
@@ -360,46 +407,56 @@ awq_status launch_t(const half_t* x, const uint32_t* qweight, const half_t* scal
 //  * Longer rows: a persistent grid of a few blocks per CU, so that staging
 //    x (2 bytes per input channel per block) stays small against the
 //    weights, each wave streaming its rows through a 4-deep ring.
-template <int MT>
+template <int BITS, int MT>
 awq_status launch_m(const half_t* x, const uint32_t* qweight, const half_t* scales,
                     const half_t* zeros, int64_t N, int64_t K, int log2g, half_t* y,
                     hipStream_t stream) {
-    const int64_t kbs = ceil_div(K / 32, 128);
+    const int64_t kbs = ceil_div(K >> Chunk<BITS>::kShift, 128);
     if (kbs == 1) {
         if (ceil_div(N, 8) >= 512)
-            return launch_t<MT, 2, 2, 1, true>(x, qweight, scales, zeros, N, K, log2g, y, ceil_div(N, 8), stream);
-        return launch_t<MT, 1, 2, 1, true>(x, qweight, scales, zeros, N, K, log2g, y, ceil_div(N, 4), stream);
+            return launch_t<BITS, MT, 2, 2, 1, true>(x, qweight, scales, zeros, N, K, log2g, y, ceil_div(N, 8),
+                                                     stream);
+        return launch_t<BITS, MT, 1, 2, 1, true>(x, qweight, scales, zeros, N, K, log2g, y, ceil_div(N, 4), stream);
     }
     if (kbs == 2)
-        return launch_t<MT, 1, 2, 2, true>(x, qweight, scales, zeros, N, K, log2g, y, ceil_div(N, 4), stream);
-    const int64_t x_lds = static_cast<int64_t>(gemv_lds_bytes(MT, K));
+        return launch_t<BITS, MT, 1, 2, 2, true>(x, qweight, scales, zeros, N, K, log2g, y, ceil_div(N, 4), stream);
+    const int64_t x_lds = static_cast<int64_t>(gemv_lds_bytes(MT, K, BITS));
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kGemvBlocksPerCu, max_shared_bytes() / (x_lds + 2048)));
-    return launch_t<MT, 1, 2, 4>(x, qweight, scales, zeros, N, K, log2g, y, per_cu * cu_count(), stream);
+    return launch_t<BITS, MT, 1, 2, 4>(x, qweight, scales, zeros, N, K, log2g, y, per_cu * cu_count(), stream);
 }
 
 }  // namespace
 
-bool gemv_supported(int64_t M, int64_t K) {
+bool gemv_supported(int64_t M, int64_t K, int bits) {
     if (M < 1 || M > kGemvMaxM) return false;
-    if (K % 32 != 0 || K > (int64_t(1) << 30)) return false;
-    return gemv_lds_bytes(M, K) <= static_cast<size_t>(max_shared_bytes());
+    if (K % (bits == 4 ? 32 : 16) != 0 || K > (int64_t(1) << 30)) return false;
+    return gemv_lds_bytes(M, K, bits) <= static_cast<size_t>(max_shared_bytes());
 }
+
+namespace {
+template <int BITS>
+awq_status launch_gemv_bits(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros,
+                            int64_t M, int64_t N, int64_t K, int log2g, half_t* y, hipStream_t stream) {
+    switch (M) {
+        case 1: return launch_m<BITS, 1>(x, qweight, scales, zeros, N, K, log2g, y, stream);
+        case 2: return launch_m<BITS, 2>(x, qweight, scales, zeros, N, K, log2g, y, stream);
+        case 3: return launch_m<BITS, 3>(x, qweight, scales, zeros, N, K, log2g, y, stream);
+        case 4: return launch_m<BITS, 4>(x, qweight, scales, zeros, N, K, log2g, y, stream);
+        case 5: return launch_m<BITS, 5>(x, qweight, scales, zeros, N, K, log2g, y, stream);
+        case 6: return launch_m<BITS, 6>(x, qweight, scales, zeros, N, K, log2g, y, stream);
+        case 7: return launch_m<BITS, 7>(x, qweight, scales, zeros, N, K, log2g, y, stream);
+        case 8: return launch_m<BITS, 8>(x, qweight, scales, zeros, N, K, log2g, y, stream);
+        default: return AWQ_ERR_SHAPE;
+    }
+}
+}  // namespace
 
 awq_status launch_gemv(const half_t* x, const uint32_t* qweight, const half_t* scales,
                        const half_t* zeros, int64_t M, int64_t N, int64_t K, int group_size,
-                       half_t* y, hipStream_t stream) {
+                       half_t* y, hipStream_t stream, int bits) {
     const int log2g = 31 - __builtin_clz(static_cast<unsigned>(group_size));   // G is a power of two >= 32
-    switch (M) {
-        case 1: return launch_m<1>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        case 2: return launch_m<2>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        case 3: return launch_m<3>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        case 4: return launch_m<4>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        case 5: return launch_m<5>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        case 6: return launch_m<6>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        case 7: return launch_m<7>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        case 8: return launch_m<8>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        default: return AWQ_ERR_SHAPE;
-    }
+    if (bits == 8) return launch_gemv_bits<8>(x, qweight, scales, zeros, M, N, K, log2g, y, stream);
+    return launch_gemv_bits<4>(x, qweight, scales, zeros, M, N, K, log2g, y, stream);
 }
 
 }  // namespace awq

@@ -7,10 +7,12 @@
 // != 0, the group's own [min, max]); the symmetric form of that section
 // (zero-point 0) maps the group's largest magnitude to +-7, s = max|w| / 7,
 // q = clamp(round(w / s), -8, 7), and stores q + 8 with zero-point 8, so the
-// same dequantization (q - z) * s serves both.
+// same dequantization (q - z) * s serves both. The W8A16 form (aissn.com
+// "INT8 实战": 8-bit weights, fp16 activations) is the same map with 255
+// levels (symmetric at +-127, stored as q + 128), four codes per word.
 //
-// Layout: one thread per packed word, i.e. 8 consecutive k of one row, read as
-// one 16-byte load. The G/8 threads of a group are adjacent lanes of one
+// Layout: one thread per 8 consecutive k of one row (one packed INT4 word, or
+// two W8 words), read as one 16-byte load. The G/8 threads of a group are adjacent lanes of one
 // wavefront, so a wave streams 64 * 16 B = 1 KB of contiguous weights and the
 // group min/max is a 3- or 4-step butterfly over lanes. Every arithmetic step
 // is IEEE fp32 (correctly rounded divide, round-half-to-even rint) so the
@@ -36,7 +38,9 @@ struct Clip {
     float f = 0.f;      // interpolation fraction
 };
 
-template <int G, bool SYM, bool CLIP>
+// BITS = 4 (INT4: 8 codes per word) or 8 (W8A16: 4 codes per word, the
+// same map with 255 levels; symmetric at +-127 stored as code + 128).
+template <int G, bool SYM, bool CLIP, int BITS>
 __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict__ w,
                                                        const float* __restrict__ channel_scale,
                                                        int64_t n_words, int64_t words_per_row,
@@ -44,6 +48,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict_
                                                        half_t* __restrict__ scales,
                                                        half_t* __restrict__ zeros, Clip clip) {
     constexpr int kLanes = G / 8;  // threads per group: 4 .. 64 (G = 32 .. 512)
+    constexpr float kQ = static_cast<float>((1 << BITS) - 1);            // 15 or 255
+    constexpr float kSymQ = static_cast<float>((1 << (BITS - 1)) - 1);   // 7 or 127
+    constexpr float kSymZero = static_cast<float>(1 << (BITS - 1));      // 8 or 128
     const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     // n_words is a multiple of kLanes and kLanes divides 64, so a group's
     // lanes are either all in range or all out of range.
@@ -125,27 +132,33 @@ __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict_
     float s32, z;
     if constexpr (SYM) {
         const float a = fmaxf(fmaxf(-lo, hi), kRangeFloor);   // max |w| (lo <= hi)
-        s32 = a / 7.0f;                                       // IEEE divide
+        s32 = a / kSymQ;                                      // IEEE divide
     } else {
         const float range = fmaxf(hi - lo, kRangeFloor);
-        s32 = range / 15.0f;                                  // IEEE divide
+        s32 = range / kQ;                                     // IEEE divide
     }
     const half_t s16 = static_cast<half_t>(s32);              // round-to-nearest-even
     const float sf = static_cast<float>(s16);
     if constexpr (SYM) {
-        z = 8.0f;
+        z = kSymZero;
     } else {
-        const int zi = static_cast<int>(fminf(fmaxf(rintf(-lo / sf), 0.0f), 15.0f));
+        const int zi = static_cast<int>(fminf(fmaxf(rintf(-lo / sf), 0.0f), kQ));
         z = static_cast<float>(zi);
     }
 
-    uint32_t packed = 0;
+    uint32_t code[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float q = fminf(fmaxf(rintf(v[j] / sf) + z, 0.0f), 15.0f);
-        packed |= static_cast<uint32_t>(q) << (4 * j);
+    for (int j = 0; j < 8; ++j) code[j] = static_cast<uint32_t>(fminf(fmaxf(rintf(v[j] / sf) + z, 0.0f), kQ));
+    if constexpr (BITS == 4) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) packed |= code[j] << (4 * j);
+        qweight[t] = packed;
+    } else {
+        const uint2 packed = make_uint2(code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
+                                        code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24));
+        reinterpret_cast<uint2*>(qweight)[t] = packed;
     }
-    qweight[t] = packed;
     if ((t & (kLanes - 1)) == 0) {
         const int64_t gi = t / kLanes;
         scales[gi] = s16;
@@ -153,36 +166,54 @@ __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict_
     }
 }
 
-template <int G, bool SYM, bool CLIP>
+template <int G, bool SYM, bool CLIP, int BITS>
 void launch_g(const half_t* w, const float* channel_scale, int64_t n_words, int64_t words_per_row,
               uint32_t* qweight, half_t* scales, half_t* zeros, Clip clip, hipStream_t stream) {
     const int threads = 256;
     const int64_t blocks = ceil_div(n_words, threads);
-    hipLaunchKernelGGL((quantize_kernel<G, SYM, CLIP>), dim3(static_cast<unsigned>(blocks)), dim3(threads), 0,
+    hipLaunchKernelGGL((quantize_kernel<G, SYM, CLIP, BITS>), dim3(static_cast<unsigned>(blocks)), dim3(threads), 0,
                        stream, w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip);
 }
 
-template <bool SYM, bool CLIP>
+template <bool SYM, bool CLIP, int BITS>
 void launch_sym(const half_t* w, const float* channel_scale, int64_t n_words, int64_t words_per_row,
                 int group_size, uint32_t* qweight, half_t* scales, half_t* zeros, Clip clip,
                 hipStream_t stream) {
     switch (group_size) {
         case 32:
-            launch_g<32, SYM, CLIP>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            launch_g<32, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
             break;
         case 64:
-            launch_g<64, SYM, CLIP>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            launch_g<64, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
             break;
         case 128:
-            launch_g<128, SYM, CLIP>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            launch_g<128, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
             break;
         case 256:
-            launch_g<256, SYM, CLIP>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            launch_g<256, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
             break;
         default:
-            launch_g<512, SYM, CLIP>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            launch_g<512, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
             break;
     }
+}
+
+template <int BITS>
+void launch_bits(const half_t* w, const float* channel_scale, int64_t n_words, int64_t words_per_row,
+                 int group_size, bool symmetric, bool c, uint32_t* qweight, half_t* scales, half_t* zeros,
+                 Clip clip, hipStream_t stream) {
+    if (symmetric && c)
+        launch_sym<true, true, BITS>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros,
+                                     clip, stream);
+    else if (symmetric)
+        launch_sym<true, false, BITS>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros,
+                                      clip, stream);
+    else if (c)
+        launch_sym<false, true, BITS>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros,
+                                      clip, stream);
+    else
+        launch_sym<false, false, BITS>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales,
+                                       zeros, clip, stream);
 }
 
 }  // namespace
@@ -191,7 +222,7 @@ bool clip_fraction_ok(double p) { return p >= 0.0 && p < 0.25; }
 
 awq_status launch_quantize(const half_t* w, const float* channel_scale, int64_t N, int64_t K,
                            int group_size, bool symmetric, double clip_fraction, uint32_t* qweight,
-                           half_t* scales, half_t* zeros, hipStream_t stream) {
+                           half_t* scales, half_t* zeros, hipStream_t stream, int bits) {
     const int64_t words_per_row = K / 8;
     const int64_t n_words = N * words_per_row;
     if (n_words == 0) return AWQ_OK;
@@ -201,18 +232,12 @@ awq_status launch_quantize(const half_t* w, const float* channel_scale, int64_t 
     clip.i = static_cast<int>(std::floor(h));
     clip.f = static_cast<float>(h - clip.i);
     const bool c = clip_fraction > 0.0;
-    if (symmetric && c)
-        launch_sym<true, true>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros, clip,
-                               stream);
-    else if (symmetric)
-        launch_sym<true, false>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros, clip,
-                                stream);
-    else if (c)
-        launch_sym<false, true>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros, clip,
-                                stream);
+    if (bits == 8)
+        launch_bits<8>(w, channel_scale, n_words, words_per_row, group_size, symmetric, c, qweight, scales, zeros,
+                       clip, stream);
     else
-        launch_sym<false, false>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros, clip,
-                                 stream);
+        launch_bits<4>(w, channel_scale, n_words, words_per_row, group_size, symmetric, c, qweight, scales, zeros,
+                       clip, stream);
     return last_launch_status();
 }
 
