@@ -39,6 +39,13 @@ constexpr int kSkThreads = 512;         // 8 waves
 constexpr int kSkBN = 256;              // output columns per block
 constexpr int kSkLds = 152 * 1024;      // LDS budget for the staged x
 constexpr int kSkXP = 19;               // x pieces (16 bytes) per thread at most
+// The prologue's loads are issued unconditionally (past-the-end offsets read
+// zero without touching memory), so their count is a compile-time bound.
+// Every unneeded load still costs address and TA cycles, which dominate the
+// short splits, so the kernel comes in three prologue sizes (FORM 0, 1, 2:
+// x pieces kSkXPForm[FORM], (scale, zero) pairs kSkSZForm[FORM] per thread)
+// and the launch takes the smallest that covers the block's K range.
+constexpr int kSkXPForm[3] = {4, 8, 19};
 constexpr int kSc1 = 16;                // cache-policy bit sc1 (device scope)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -100,8 +107,9 @@ __host__ __device__ inline int sk_lds_bytes(int mb, int krange, int group_size) 
     return 16 * mb * sk_stride(krange) * 2 + kSkBN * sk_szst(krange / group_size) * 4;
 }
 constexpr int kSkSZ = 32;               // (scale, zero) pairs per thread at most
+constexpr int kSkSZForm[3] = {4, 8, 32};
 
-template <int MB, int WPL>
+template <int MB, int WPL, int FORM>
 __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __restrict__ x,
                                                               const uint32_t* __restrict__ qweight,
                                                               const half_t* __restrict__ scales,
@@ -112,6 +120,9 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __r
     constexpr int G = WPL * 32;
     constexpr int MP = 16 * MB;                          // padded rows
     constexpr int kSkDepth = (MB <= 2 && WPL <= 4) ? 8 : 4;   // weight groups in flight per wave
+    constexpr int XPN = kSkXPForm[FORM];
+    constexpr int SZN = kSkSZForm[FORM];
+    static_assert(kSkXPForm[2] == kSkXP && kSkSZForm[2] == kSkSZ, "the largest form is the bound sk_kmax uses");
     extern __shared__ __attribute__((aligned(16))) half_t xs[];   // [MP][stride], then (s, z) pairs
     __shared__ int s_last;
 
@@ -180,9 +191,9 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __r
     const int szst = sk_szst(ngb);
     const int nsz = kSkBN * ngb;
     uint32_t* szs = reinterpret_cast<uint32_t*>(xs + MP * stride);
-    uint16_t sr[kSkSZ], zr[kSkSZ];
+    uint16_t sr[SZN], zr[SZN];
 #pragma unroll
-    for (int i = 0; i < kSkSZ; ++i) {
+    for (int i = 0; i < SZN; ++i) {
         const int e = tid + i * kSkThreads;
         const int c = e / ngb, gi = e - c * ngb;
         const int n = tile * kSkBN + c;
@@ -197,9 +208,9 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __r
     const auto rx = rsrc(x, x_bytes);
     const int pr = (k1 - k0) / 8;                        // pieces per row
     const int pieces = MP * pr;
-    uint4 xr[kSkXP];
+    uint4 xr[XPN];
 #pragma unroll
-    for (int i = 0; i < kSkXP; ++i) {
+    for (int i = 0; i < XPN; ++i) {
         const int p = tid + i * kSkThreads;
         const int r = p / pr, c8 = p - r * pr;
         const bool ok = p < pieces && r < M;
@@ -207,7 +218,7 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __r
         xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
     }
 #pragma unroll
-    for (int i = 0; i < kSkSZ; ++i) {
+    for (int i = 0; i < SZN; ++i) {
         const int e = tid + i * kSkThreads;
         if (e < nsz) {
             const int c = e / ngb, gi = e - c * ngb;
@@ -225,7 +236,7 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __r
         __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int i = 0; i < kSkXP; ++i) {
+    for (int i = 0; i < XPN; ++i) {
         const int p = tid + i * kSkThreads;
         if (p < pieces) {
             const int r = p / pr, c8 = p - r * pr;
@@ -398,16 +409,26 @@ int sk_splits(int64_t M, int64_t N, int64_t K, int group_size, bool have_workspa
     return static_cast<int>(std::max<int64_t>(1, s));
 }
 
-template <int MB, int WPL>
-awq_status launch_cfg(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
-                      int N, int K, half_t* y, void* workspace, hipStream_t stream) {
+template <int MB, int WPL, int FORM>
+awq_status launch_form(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
+                       int N, int K, half_t* y, int splits, float* partials, int* counters, size_t lds,
+                       hipStream_t stream) {
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<MB, WPL>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<MB, WPL, FORM>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kSkLds) != hipSuccess)
             return AWQ_ERR_HIP;
         attr_set = true;
     }
+    const int64_t blocks = sk_tiles(N) * splits;
+    hipLaunchKernelGGL((skinny_kernel<MB, WPL, FORM>), dim3(static_cast<unsigned>(blocks)), dim3(kSkThreads), lds,
+                       stream, x, qweight, scales, zeros, y, M, N, K, splits, partials, counters);
+    return last_launch_status();
+}
+
+template <int MB, int WPL>
+awq_status launch_cfg(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
+                      int N, int K, half_t* y, void* workspace, hipStream_t stream) {
     const int splits = sk_splits(M, N, K, WPL * 32, workspace != nullptr);
     if (splits == 0) return AWQ_ERR_CONFIG;
     float* partials = nullptr;
@@ -420,10 +441,17 @@ awq_status launch_cfg(const half_t* x, const uint32_t* qweight, const half_t* sc
     const int ng = K / (WPL * 32);
     const int gmax_split = (ng + splits - 1) / splits;
     const size_t lds = static_cast<size_t>(sk_lds_bytes(MB, gmax_split * WPL * 32, WPL * 32));
-    const int64_t blocks = sk_tiles(N) * splits;
-    hipLaunchKernelGGL((skinny_kernel<MB, WPL>), dim3(static_cast<unsigned>(blocks)), dim3(kSkThreads), lds, stream,
-                       x, qweight, scales, zeros, y, M, N, K, splits, partials, counters);
-    return last_launch_status();
+    // the smallest prologue that stages 16 MB rows of the block's K range
+    // and its (scale, zero) pairs
+    auto fits = [&](int form) {
+        return 16 * MB * (gmax_split * WPL * 32 / 8) <= kSkXPForm[form] * kSkThreads &&
+               kSkBN * gmax_split <= kSkSZForm[form] * kSkThreads;
+    };
+    if (fits(0))
+        return launch_form<MB, WPL, 0>(x, qweight, scales, zeros, M, N, K, y, splits, partials, counters, lds, stream);
+    if (fits(1))
+        return launch_form<MB, WPL, 1>(x, qweight, scales, zeros, M, N, K, y, splits, partials, counters, lds, stream);
+    return launch_form<MB, WPL, 2>(x, qweight, scales, zeros, M, N, K, y, splits, partials, counters, lds, stream);
 }
 
 template <int WPL>
