@@ -26,6 +26,8 @@ namespace {
 
 #pragma clang fp contract(off)
 
+constexpr float kTieBand = 1e-3f;   // |frac(v / s) - 1/2| below which the exact divide decides
+
 // Clip step (xxmr.cn §1.5: cut the extreme p of the values at both ends
 // before the scale is taken). The bounds are the p and 1 - p quantiles of the
 // group, interpolated between order statistics x(0) <= ... <= x(G-1):
@@ -146,9 +148,20 @@ __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict_
         z = static_cast<float>(zi);
     }
 
+    // rint(v / s) with the correctly rounded quotient, taken through the
+    // product v * (1 / s): its error is below 1e-4 for |v / s| <= 256 (the
+    // reciprocal and the product each round once), so away from the
+    // half-way points it rounds to the same integer. Within kTieBand of a
+    // half-way point the exact IEEE divide decides.
+    const float rinv = 1.0f / sf;
     uint32_t code[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) code[j] = static_cast<uint32_t>(fminf(fmaxf(rintf(v[j] / sf) + z, 0.0f), kQ));
+    for (int j = 0; j < 8; ++j) {
+        const float r = v[j] * rinv;
+        float q = rintf(r);
+        if (fabsf(fabsf(r - q) - 0.5f) < kTieBand) q = rintf(v[j] / sf);
+        code[j] = static_cast<uint32_t>(fminf(fmaxf(q + z, 0.0f), kQ));
+    }
     if constexpr (BITS == 4) {
         uint32_t packed = 0;
 #pragma unroll
