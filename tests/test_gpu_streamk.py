@@ -128,3 +128,30 @@ def test_stream_k_graph_replay_matches_eager():
         awq.awq_quantize(w2, 128)
         torch.cuda.synchronize()
         assert torch.equal(y, e), r
+
+
+@pytest.mark.parametrize("M,N,K,G", [
+    (8192, 8192, 4096, 128),     # 1024 tiles of 256 x 256: the one-block-per-CU geometry
+    (12000, 17000, 1024, 64),    # ragged rows and columns on that geometry
+])
+def test_wide_tiles_sampled(M, N, K, G):
+    """Shapes with at least three rounds of 256 x 256 tiles take the
+    512-thread geometry without a workspace: sampled output columns against
+    the oracle, and the same values as the stream-K form."""
+    lay = synth.make_layer(N, K, M, seed=[121, M, N, K, G], w_std=0.02)
+    say("wide tiles", M, N, K, G)
+    x = dev(lay["x"])
+    qw, sc, zr = awq.awq_quantize(dev(lay["w"]), G)
+    y = awq.awq_gemm(x, qw, sc, zr, G, path=awq.PATH_GEMM)
+    rows = sampled_rows(N, 160, N + 11)
+    eq = oracle.quantize(lay["w"][rows], G)
+    assert_linear_close(host(y)[:, rows], oracle.linear_ref(lay["x"], *eq, G))
+
+
+def test_wide_tiles_w8():
+    M, N, K, G = 8192, 8192, 1024, 128
+    lay = synth.make_layer(N, K, M, seed=[122], w_std=0.02)
+    qw, sc, zr = oracle.quantize_w8(lay["w"], G)
+    y = awq.awq_gemm_w8(dev(lay["x"]), dev(qw.view(np.int32)), dev(sc), dev(zr), G, path=awq.PATH_GEMM)
+    rows = sampled_rows(N, 160, N + 13)
+    assert_linear_close(host(y)[:, rows], oracle.linear_ref_w8(lay["x"], qw[rows], sc[rows], zr[rows], G))

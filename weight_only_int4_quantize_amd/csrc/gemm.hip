@@ -201,8 +201,8 @@ __device__ __forceinline__ int sk_block_of(const StreamK& sk, int u) {
 constexpr int kSc1 = 16;   // cache-policy bit sc1 of buffer loads/stores (device scope)
 
 // buffer descriptor over one BM x BN fp32 partial tile
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* p) {
-    return __builtin_amdgcn_make_buffer_rsrc(p, 0, 256 * 128 * 4, 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, bytes, 0x00020000);
 }
 
 // DIRECT (INT4 B with G >= 64 only): each wave reads its own B columns'
@@ -210,13 +210,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* p) {
 // dequantizes them there; only A goes through LDS.
 //
 // WGM: waves along M (the 4 waves form WGM x 4 / WGM).
-template <int BM, int BN, GemmB BMODE, GemmOut OMODE, bool STREAMK, bool DIRECT, int WGM = 2>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int tiles_n, StreamK sk) {
-    constexpr int WGN = kThreads / kWave / WGM;
+template <int BM, int BN, GemmB BMODE, GemmOut OMODE, bool STREAMK, bool DIRECT, int WGM = 2, int NT = kThreads>
+__global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int tiles_n, StreamK sk) {
+    constexpr int WGN = NT / kWave / WGM;
     constexpr int WTM = BM / WGM;               // wave tile rows
     constexpr int WTN = BN / WGN;               // wave tile cols
     constexpr int TM = WTM / 32;                // 32x32 MFMA tiles per wave (M)
     constexpr int TN = WTN / 32;                // 32x32 MFMA tiles per wave (N)
+    static_assert(DIRECT || NT == kThreads, "the older form runs 256-thread blocks");
     constexpr int A_VECS = BM * BK / 8 / kThreads;        // uint4 of A per thread per step
     constexpr bool INT4 = BMODE == GemmB::kInt4;
     constexpr int BITS = BMODE == GemmB::kInt8 ? 8 : 4;     // direct form: code width of B
@@ -225,8 +226,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
     constexpr int B_VECS = BN * BK / 8 / kThreads;        // fp16 B: uint4 per thread per step (int4: unused)
     constexpr int ACC = TM * TN * 16;                     // accumulators per lane
     static_assert(TM >= 1 && TN >= 1 && A_VECS >= 1, "tile shape");
-    static_assert(!INT4 || B_WORDS == 2, "int4 B staging: 2 words (16 codes) per thread");
-    static_assert(INT4 || B_VECS >= 1, "fp16 B staging");
+    static_assert(DIRECT || !INT4 || B_WORDS == 2, "int4 B staging: 2 words (16 codes) per thread");
+    static_assert(DIRECT || INT4 || B_VECS >= 1, "fp16 B staging");
     static_assert(!DIRECT || BMODE != GemmB::kF16, "the direct form is for quantized B");
     static_assert(DIRECT || BMODE != GemmB::kInt8, "W8 B runs the direct form only");
     constexpr int LDS_A = DIRECT ? BM * BKD : BM * LDK;
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
     // slice ks, in both operands, so one 16-byte load gives a lane its four
     // B words of a column for the whole step.
     auto run_segment_direct = [&](int tm, int tn, int kb, int ke) {
-        constexpr int AV = BM * BKD / 8 / kThreads;        // 16-byte A chunks per thread per step
+        constexpr int AV = BM * BKD / 8 / NT;              // 16-byte A chunks per thread per step
         const int lh = lane >> 5;
         // Buffer loads from tile-relative bases (scalar) with 32-bit lane
         // offsets; rows past M / N are clamped to the last row, so every
@@ -403,7 +404,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
             const_cast<half_t*>(args.zeros) + static_cast<int64_t>(tn) * ngroups, 0, cols_b * ngroups * 2, 0x00020000);
         int a_off[AV];
 #pragma unroll
-        for (int i = 0; i < AV; ++i) a_off[i] = (min(tid / 8 + i * (kThreads / 8), rows_a - 1) * K + (tid % 8) * 8) * 2;
+        for (int i = 0; i < AV; ++i) a_off[i] = (min(tid / 8 + i * (NT / 8), rows_a - 1) * K + (tid % 8) * 8) * 2;
         int b_off[TN], sz_off[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -448,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
         auto store_a = [&](half_t* as) {
 #pragma unroll
             for (int i = 0; i < AV; ++i)
-                *reinterpret_cast<u32x4*>(&as[swz64(tid / 8 + i * (kThreads / 8), tid % 8)]) = areg[i];
+                *reinterpret_cast<u32x4*>(&as[swz64(tid / 8 + i * (NT / 8), tid % 8)]) = areg[i];
         };
 
         int g = (kb * BKD) / G;
@@ -574,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
     };
     auto finish_loss = [&](int tile, float sq) {
         if constexpr (OMODE == GemmOut::kLoss) {
-            __shared__ double red[kThreads / kWave];
+            __shared__ double red[NT / kWave];
             double v = static_cast<double>(sq);
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
@@ -582,7 +583,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
             __syncthreads();
             if (tid == 0) {
                 double t = 0.0;
-                for (int w = 0; w < kThreads / kWave; ++w) t += red[w];
+                for (int w = 0; w < NT / kWave; ++w) t += red[w];
                 args.partials[tile] = t;
             }
             __syncthreads();
@@ -638,7 +639,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
             {
                 // chunk-major layout [(i, j, e / 4)][thread][4]: one coalesced
                 // 1 KB row per wave and chunk, addressed by a scalar offset
-                const auto rs = partial_rsrc(slot_of(b));
+                const auto rs = partial_rsrc(slot_of(b), BM * BN * 4);
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -648,7 +649,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
                             const float4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                                 acc[i][j][4 * q + 3]};
                             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, tid * 16,
-                                                                   ((i * TN + j) * 4 + q) * kThreads * 16, kSc1);
+                                                                   ((i * TN + j) * 4 + q) * NT * 16, kSc1);
                         }
             }
             // The parts are written and read with the sc1 (device-coherent)
@@ -678,12 +679,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
 #pragma unroll
                     for (int c = 0; c < kBatch; ++c) sum[c] = float4_t{0.f, 0.f, 0.f, 0.f};
                     for (int bb = b_first; bb <= b_last; ++bb) {
-                        const auto rs = partial_rsrc(slot_of(bb));
+                        const auto rs = partial_rsrc(slot_of(bb), BM * BN * 4);
                         float4_t v[kBatch];
 #pragma unroll
                         for (int c = 0; c < kBatch; ++c)
                             v[c] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                    rs, tid * 16, (c0 + c) * kThreads * 16, kSc1));
+                                                                    rs, tid * 16, (c0 + c) * NT * 16, kSc1));
 #pragma unroll
                         for (int c = 0; c < kBatch; ++c) sum[c] += v[c];
                     }
@@ -704,74 +705,118 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args, int ti
 
 constexpr int kBM = 256;
 constexpr int kBN = 128;
-constexpr int kBlocksPerCu = 2;
+
+// Block geometries: 256 x 128 tiles of 256 threads, two blocks per CU (every
+// form), and 256 x 256 tiles of 512 threads (8 waves of 256 x 32), one block
+// per CU (direct form), which stages each A step once for twice the columns.
+struct Geometry {
+    int bm, bn, threads, per_cu;
+};
+constexpr Geometry kNarrowTile{256, 128, 256, 2};
+constexpr Geometry kWideTile{256, 256, 512, 1};
 
 constexpr int kMaxSplit = 4;        // segments per tile at most
 constexpr int kMinSteps = 8;        // K steps per block at least
 
-int64_t resident_slots() { return static_cast<int64_t>(kBlocksPerCu) * cu_count(); }
+int64_t resident_slots(const Geometry& g) { return static_cast<int64_t>(g.per_cu) * cu_count(); }
+int64_t tiles_of(const Geometry& g, int64_t M, int64_t N) { return ceil_div(M, g.bm) * ceil_div(N, g.bn); }
 
 // Stream-K pays off when there are fewer tiles than resident block slots:
 // one tile per block would leave CUs idle or at one block each. With more
-// tiles, the last round's blocks run one per CU at close to the per-CU rate
-// of two, and splitting costs more in partial traffic than it recovers.
-bool use_stream_k(int64_t tiles, int64_t steps) {
-    if (tiles >= resident_slots() || tiles > split_counter_slots()) return false;
+// 256 x 128 tiles, the last round's blocks run one per CU at close to the
+// per-CU rate of two, and splitting costs more in partial traffic than it
+// recovers.
+// Stream-K for shapes under one round of tiles, or two with the wide tile:
+// its last round runs one block per CU, so a split tail beats it (measured).
+bool use_stream_k(const Geometry& g, int64_t tiles, int64_t steps) {
+    const int64_t rounds = g.per_cu == 1 ? 2 : 1;
+    if (tiles >= rounds * resident_slots(g) || tiles > split_counter_slots()) return false;
     return tiles * steps < (int64_t{1} << 31);
 }
 
-int stream_k_grid(int64_t tiles, int64_t steps) {
+int stream_k_grid(const Geometry& g, int64_t tiles, int64_t steps) {
     const int64_t total = tiles * steps;
-    int64_t g = std::min(resident_slots(), tiles * kMaxSplit);
-    g = std::min(g, std::max<int64_t>(1, total / kMinSteps));
-    return static_cast<int>(g);
+    int64_t gr = std::min(resident_slots(g), tiles * kMaxSplit);
+    gr = std::min(gr, std::max<int64_t>(1, total / kMinSteps));
+    return static_cast<int>(gr);
 }
 
-// two fp32 partial tiles per resident block
+// two fp32 partial tiles per resident block, for either geometry
 size_t partials_bytes() {
-    return round_up(static_cast<size_t>(resident_slots()) * 2 * kBM * kBN * sizeof(float), 256);
+    const size_t a = static_cast<size_t>(resident_slots(kNarrowTile)) * 2 * kNarrowTile.bm * kNarrowTile.bn;
+    const size_t b = static_cast<size_t>(resident_slots(kWideTile)) * 2 * kWideTile.bm * kWideTile.bn;
+    return round_up(std::max(a, b) * sizeof(float), 256);
 }
 
-template <GemmB BMODE, GemmOut OMODE, bool DIRECT, int WGM = 2>
+template <const Geometry& GEO, GemmB BMODE, GemmOut OMODE, bool DIRECT, int WGM = 2>
 void launch_cfg(const GemmArgs& args, void* workspace, hipStream_t stream) {
-    const int64_t tiles_n = ceil_div(args.N, kBN);
-    const int64_t tiles = ceil_div(args.M, kBM) * tiles_n;
+    const int64_t tiles_n = ceil_div(args.N, GEO.bn);
+    const int64_t tiles = ceil_div(args.M, GEO.bm) * tiles_n;
     const int64_t steps = args.K / (DIRECT ? BKD : BK);
     StreamK sk;
-    if (workspace != nullptr && use_stream_k(tiles, steps)) {
+    if (workspace != nullptr && use_stream_k(GEO, tiles, steps)) {
         sk.ipt = static_cast<int>(steps);
         sk.total = static_cast<int>(tiles * sk.ipt);
-        sk.grid = stream_k_grid(tiles, steps);
+        sk.grid = stream_k_grid(GEO, tiles, steps);
         sk.q = sk.total / sk.grid;
         sk.r = sk.total % sk.grid;
         sk.counters = static_cast<int*>(workspace);
         sk.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_counter_bytes());
-        hipLaunchKernelGGL((gemm_kernel<kBM, kBN, BMODE, OMODE, true, DIRECT, WGM>), dim3(static_cast<unsigned>(sk.grid)),
-                           dim3(kThreads), 0, stream, args, static_cast<int>(tiles_n), sk);
+        hipLaunchKernelGGL((gemm_kernel<GEO.bm, GEO.bn, BMODE, OMODE, true, DIRECT, WGM, GEO.threads>),
+                           dim3(static_cast<unsigned>(sk.grid)), dim3(GEO.threads), 0, stream, args,
+                           static_cast<int>(tiles_n), sk);
         return;
     }
-    hipLaunchKernelGGL((gemm_kernel<kBM, kBN, BMODE, OMODE, false, DIRECT, WGM>), dim3(static_cast<unsigned>(tiles)),
-                       dim3(kThreads), 0, stream, args, static_cast<int>(tiles_n), sk);
+    hipLaunchKernelGGL((gemm_kernel<GEO.bm, GEO.bn, BMODE, OMODE, false, DIRECT, WGM, GEO.threads>),
+                       dim3(static_cast<unsigned>(tiles)), dim3(GEO.threads), 0, stream, args,
+                       static_cast<int>(tiles_n), sk);
 }
 
 // The direct-B form needs every K step of 64 inside one group, and 32-bit
-// byte offsets within a 256-row tile of A. Its 4 waves sit side by side
-// along N (256 x 32 each): a wave's unpack work per MFMA halves against the
-// 2 x 2 arrangement (whose wave pairs would unpack the same columns twice).
+// byte offsets within a 256-row tile of A. Its waves sit side by side along
+// N (256 x 32 each): a wave's unpack work per MFMA halves against the 2 x 2
+// arrangement (whose wave pairs would unpack the same columns twice).
 constexpr int kDirectWgm = 1;
 bool direct_ok(const GemmArgs& args) { return args.group_size >= BKD && args.K * kBM * 2 < (int64_t{1} << 31); }
+
+// The wide tile when its tiles fill at least kWideRounds rounds of the GPU
+// (one block per CU), so the last partial round costs little, or when a
+// workspace lets stream-K spread a short shape over every CU.
+constexpr int64_t kWideRounds = 3;
+bool use_wide(const GemmArgs& args, bool have_workspace) {
+    const int64_t t = tiles_of(kWideTile, args.M, args.N);
+    if (t >= kWideRounds * cu_count()) return true;
+    const int64_t steps = args.K / BKD;
+    return have_workspace && use_stream_k(kWideTile, t, steps);
+}
+
+template <GemmB BMODE, GemmOut OMODE>
+void launch_direct(const GemmArgs& args, void* workspace, hipStream_t stream) {
+    if (use_wide(args, workspace != nullptr))
+        launch_cfg<kWideTile, BMODE, OMODE, true, kDirectWgm>(args, workspace, stream);
+    else
+        launch_cfg<kNarrowTile, BMODE, OMODE, true, kDirectWgm>(args, workspace, stream);
+}
 
 template <GemmOut OMODE>
 void launch_int4(const GemmArgs& args, void* workspace, hipStream_t stream) {
     if (direct_ok(args))
-        launch_cfg<GemmB::kInt4, OMODE, true, kDirectWgm>(args, workspace, stream);
+        launch_direct<GemmB::kInt4, OMODE>(args, workspace, stream);
     else
-        launch_cfg<GemmB::kInt4, OMODE, false>(args, workspace, stream);
+        launch_cfg<kNarrowTile, GemmB::kInt4, OMODE, false>(args, workspace, stream);
 }
 
 }  // namespace
 
-int64_t gemm_tile_count(int64_t M, int64_t N) { return ceil_div(M, kBM) * ceil_div(N, kBN); }
+int64_t gemm_tile_count(int64_t M, int64_t N, int64_t K, int group_size) {
+    GemmArgs a;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.group_size = group_size;
+    // the loss launches run without a workspace
+    return tiles_of(direct_ok(a) && use_wide(a, false) ? kWideTile : kNarrowTile, M, N);
+}
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N) {
     (void)M;
@@ -784,7 +829,7 @@ awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t s
     if (b == GemmB::kInt8) {
         // W8 B: the direct form only, fp16 output
         if (!direct_ok(args) || out != GemmOut::kF16) return AWQ_ERR_CONFIG;
-        launch_cfg<GemmB::kInt8, GemmOut::kF16, true, kDirectWgm>(args, workspace, stream);
+        launch_direct<GemmB::kInt8, GemmOut::kF16>(args, workspace, stream);
     } else if (b == GemmB::kInt4) {
         switch (out) {
             case GemmOut::kF16: launch_int4<GemmOut::kF16>(args, workspace, stream); break;
@@ -793,8 +838,8 @@ awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t s
         }
     } else {
         switch (out) {
-            case GemmOut::kF16: launch_cfg<GemmB::kF16, GemmOut::kF16, false>(args, workspace, stream); break;
-            case GemmOut::kF32: launch_cfg<GemmB::kF16, GemmOut::kF32, false>(args, workspace, stream); break;
+            case GemmOut::kF16: launch_cfg<kNarrowTile, GemmB::kF16, GemmOut::kF16, false>(args, workspace, stream); break;
+            case GemmOut::kF32: launch_cfg<kNarrowTile, GemmB::kF16, GemmOut::kF32, false>(args, workspace, stream); break;
             case GemmOut::kLoss: return AWQ_ERR_CONFIG;
         }
     }
