@@ -60,7 +60,7 @@ struct SearchLayout {
         zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         xs = c.take<half_t>(static_cast<size_t>(T) * K);
         yref = c.take<float>(static_cast<size_t>(T) * N);
-        tile_partials = c.take<double>(gemm_tile_count(T, N, K, G));
+        tile_partials = c.take<double>(gemm_tile_count(T, N));
         losses = c.take<double>(n_alpha);
         bytes = c.used;
     }
@@ -90,7 +90,7 @@ struct SalientLayout {
         zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         w_sal = c.take<half_t>(static_cast<size_t>(std::max(n_sal, 1)) * N);
         yref = c.take<float>(static_cast<size_t>(T) * N);
-        tile_partials = c.take<double>(gemm_tile_count(T, N, K, G));
+        tile_partials = c.take<double>(gemm_tile_count(T, N));
         losses = c.take<double>(2);
         bytes = c.used;
     }
@@ -117,7 +117,7 @@ struct ClipLayout {
         zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         if (scaled) xs = c.take<half_t>(static_cast<size_t>(T) * K);
         yref = c.take<float>(static_cast<size_t>(T) * N);
-        tile_partials = c.take<double>(gemm_tile_count(T, N, K, G));
+        tile_partials = c.take<double>(gemm_tile_count(T, N));
         losses = c.take<double>(n);
         bytes = c.used;
     }
@@ -155,7 +155,7 @@ awq_status output_loss(const half_t* xa, const uint32_t* qw, const half_t* sc, c
     q.partials = partials;
     awq_status st = launch_gemm(q, GemmB::kInt4, GemmOut::kLoss, s);
     if (st != AWQ_OK) return st;
-    return launch_sum_partials(partials, gemm_tile_count(T, N, K, G), loss_out, s);
+    return launch_sum_partials(partials, gemm_tile_count(T, N), loss_out, s);
 }
 
 }  // namespace

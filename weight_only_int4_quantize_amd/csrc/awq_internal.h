@@ -85,8 +85,8 @@ struct GemmArgs {
 inline int split_counter_slots() { return 4 * cu_count(); }
 inline size_t split_counter_bytes() { return round_up(static_cast<size_t>(split_counter_slots()) * sizeof(int), 256); }
 
-// Output tiles of the INT4 GEMM launch for this shape (one loss partial each).
-int64_t gemm_tile_count(int64_t M, int64_t N, int64_t K, int group_size);
+// Output tiles of the loss-form GEMM launch (one loss partial each).
+int64_t gemm_tile_count(int64_t M, int64_t N);
 // Workspace of the stream-K launch (fp32 partial tiles + per-tile counters);
 // with workspace == nullptr launch_gemm runs one tile per block.
 size_t gemm_workspace_bytes(int64_t M, int64_t N);

@@ -726,11 +726,12 @@ int64_t tiles_of(const Geometry& g, int64_t M, int64_t N) { return ceil_div(M, g
 // 256 x 128 tiles, the last round's blocks run one per CU at close to the
 // per-CU rate of two, and splitting costs more in partial traffic than it
 // recovers.
-// Stream-K for shapes under one round of tiles, or two with the wide tile:
-// its last round runs one block per CU, so a split tail beats it (measured).
+// Stream-K for shapes under one round of tiles. Over more rounds nearly every
+// tile would be split and its fp32 partials moved through memory: measured on
+// 2048 x 11008 x 4096 with 256 x 256 tiles, 831 MB of traffic per launch
+// against 282 MB unsplit, for a few percent of time.
 bool use_stream_k(const Geometry& g, int64_t tiles, int64_t steps) {
-    const int64_t rounds = g.per_cu == 1 ? 2 : 1;
-    if (tiles >= rounds * resident_slots(g) || tiles > split_counter_slots()) return false;
+    if (tiles >= resident_slots(g) || tiles > split_counter_slots()) return false;
     return tiles * steps < (int64_t{1} << 31);
 }
 
@@ -781,7 +782,7 @@ bool direct_ok(const GemmArgs& args) { return args.group_size >= BKD && args.K *
 
 // The wide tile when its tiles fill at least kWideRounds rounds of the GPU
 // (one block per CU), so the last partial round costs little, or when a
-// workspace lets stream-K spread a short shape over every CU.
+// workspace lets stream-K spread a shape of under one round over every CU.
 constexpr int64_t kWideRounds = 3;
 bool use_wide(const GemmArgs& args, bool have_workspace) {
     const int64_t t = tiles_of(kWideTile, args.M, args.N);
@@ -790,12 +791,18 @@ bool use_wide(const GemmArgs& args, bool have_workspace) {
     return have_workspace && use_stream_k(kWideTile, t, steps);
 }
 
+// The loss form stays on the 256 x 128 tile: its epilogue streams an fp32
+// reference tile, which two blocks per CU overlap with each other's MFMAs
+// (the full-size scale search measured 153 ms there against 156 ms wide).
 template <GemmB BMODE, GemmOut OMODE>
 void launch_direct(const GemmArgs& args, void* workspace, hipStream_t stream) {
-    if (use_wide(args, workspace != nullptr))
-        launch_cfg<kWideTile, BMODE, OMODE, true, kDirectWgm>(args, workspace, stream);
-    else
-        launch_cfg<kNarrowTile, BMODE, OMODE, true, kDirectWgm>(args, workspace, stream);
+    if constexpr (OMODE != GemmOut::kLoss) {
+        if (use_wide(args, workspace != nullptr)) {
+            launch_cfg<kWideTile, BMODE, OMODE, true, kDirectWgm>(args, workspace, stream);
+            return;
+        }
+    }
+    launch_cfg<kNarrowTile, BMODE, OMODE, true, kDirectWgm>(args, workspace, stream);
 }
 
 template <GemmOut OMODE>
@@ -808,15 +815,7 @@ void launch_int4(const GemmArgs& args, void* workspace, hipStream_t stream) {
 
 }  // namespace
 
-int64_t gemm_tile_count(int64_t M, int64_t N, int64_t K, int group_size) {
-    GemmArgs a;
-    a.M = M;
-    a.N = N;
-    a.K = K;
-    a.group_size = group_size;
-    // the loss launches run without a workspace
-    return tiles_of(direct_ok(a) && use_wide(a, false) ? kWideTile : kNarrowTile, M, N);
-}
+int64_t gemm_tile_count(int64_t M, int64_t N) { return tiles_of(kNarrowTile, M, N); }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N) {
     (void)M;
