@@ -59,6 +59,13 @@ constexpr int kXcds = 8;
 // of 2 rows, then hit 16 distinct 16-byte slots of the 256-byte bank window.
 constexpr int BKD = 64;
 __device__ __forceinline__ int swz64(int r, int c) { return r * BKD + ((c ^ ((r >> 1) & 7)) << 3); }
+// 16-byte load from global memory straight into LDS: lane L's bytes land at
+// lds + 16 L (lds is wave-uniform). The builtin exists only in the device pass.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, half_t* lds, int voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+#endif
+}
 // A zero group scale would make the rescale ratio infinite; it is taken as
 // the smallest positive fp16 value instead.
 constexpr float kTinyScale = 5.9604645e-08f;
@@ -379,15 +386,22 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
     };
 
     // K steps [kb, ke) of 64 of one tile into acc (direct-B form).
-    // Step kt: A(kt) is in LDS buffer kt & 1, A(kt + 1) in registers, B(kt)
-    // in registers. The step first writes A(kt + 1) to the other buffer
-    // (free since the barrier that ended step kt - 1), issues the loads of
-    // A(kt + 2) and B(kt + 1), then runs 4 slices of 16 k with 8 MFMAs each.
+    // Step kt: A(kt) is in LDS buffer kt & 1, B(kt) in registers. In the
+    // DMA form the step issues the LDS-DMA loads of A(kt + 1) into the other
+    // buffer (free since the barrier that ended step kt - 1) and the loads
+    // of B(kt + 1), and waits for all of them before its closing barrier.
+    // In the register form A(kt + 1) is already in registers: the step
+    // writes it to the other buffer and loads A(kt + 2) and B(kt + 1).
+    // Either way it then runs 4 slices of 16 k with 8 MFMAs each.
     // Lane half h of the MFMA takes k = 32 h + 8 ks .. + 7 of the step in
     // slice ks, in both operands, so one 16-byte load gives a lane its four
     // B words of a column for the whole step.
     auto run_segment_direct = [&](int tm, int tn, int kb, int ke) {
         constexpr int AV = BM * BKD / 8 / NT;              // 16-byte A chunks per thread per step
+        // A goes to LDS by LDS-DMA loads, except under stream-K, where the
+        // register round trip measured faster (2048x4096x11008: 185 us
+        // against 196 us; without stream-K the DMA form is 4-12 % faster)
+        constexpr bool DMA = !STREAMK;
         const int lh = lane >> 5;
         // Buffer loads from tile-relative bases (scalar) with 32-bit lane
         // offsets; rows past M / N are clamped to the last row, so every
@@ -404,7 +418,13 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
             const_cast<half_t*>(args.zeros) + static_cast<int64_t>(tn) * ngroups, 0, cols_b * ngroups * 2, 0x00020000);
         int a_off[AV];
 #pragma unroll
-        for (int i = 0; i < AV; ++i) a_off[i] = (min(tid / 8 + i * (NT / 8), rows_a - 1) * K + (tid % 8) * 8) * 2;
+        for (int i = 0; i < AV; ++i) {
+            const int row = tid / 8 + i * (NT / 8);
+            // an LDS-DMA load writes lane L's 16 bytes at slot L of the wave's
+            // 1 KB (8 rows): that slot holds logical chunk (L % 8) ^ swizzle
+            const int chunk = DMA ? ((tid % 8) ^ ((row >> 1) & 7)) : tid % 8;
+            a_off[i] = (min(row, rows_a - 1) * K + chunk * 8) * 2;
+        }
         int b_off[TN], sz_off[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -471,9 +491,21 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
             z_next[j] = z_bits_at(j, min(g + 1, ngroups - 1));
         }
 
+        auto dma_a = [&](half_t* as, int kt) {
+            const int k0 = uniform(min(kt, last) * BKD * 2);
+#pragma unroll
+            for (int i = 0; i < AV; ++i) {
+                half_t* dst = as + (wave * (kWave / 8) + i * (NT / 8)) * BKD;   // the wave's 8 rows
+                load_lds16(a_rs, dst, a_off[i], k0);
+            }
+        };
         auto step = [&](int kt, const half_t* cur, half_t* nxt, const u32x4 (&bw)[TN][BW], u32x4 (&bn)[TN][BW]) {
-            if (kt + 1 < ke) store_a(nxt);
-            load_a(kt + 2);
+            if constexpr (DMA) {
+                if (kt + 1 < ke) dma_a(nxt, kt + 1);
+            } else {
+                if (kt + 1 < ke) store_a(nxt);
+                load_a(kt + 2);
+            }
             load_b(bn, kt + 1);
             if (kt > kb && ((kt * BKD) % G) == 0) {
                 // entering the next group: C' <- C' * s_g / s_{g+1}
@@ -528,15 +560,22 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
         };
 
         load_b(b0, kb);
-        load_a(kb);
-        store_a(As[0]);
-        load_a(kb + 1);
+        if constexpr (DMA) {
+            dma_a(As[0], kb);
+            __builtin_amdgcn_s_waitcnt(0);
+        } else {
+            load_a(kb);
+            store_a(As[0]);
+            load_a(kb + 1);
+        }
         __syncthreads();
         for (int kt = kb; kt < ke; kt += 2) {
             step(kt, As[0], As[1], b0, b1);
+            if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0);   // this step's DMA has landed
             __syncthreads();
             if (kt + 1 < ke) {
                 step(kt + 1, As[1], As[0], b1, b0);
+                if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
             }
         }
