@@ -491,17 +491,18 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
             z_next[j] = z_bits_at(j, min(g + 1, ngroups - 1));
         }
 
-        auto dma_a = [&](half_t* as, int kt) {
+        // LDS-DMA loads i in [i0, i1) of A(kt) into buffer as
+        auto dma_a = [&](half_t* as, int kt, int i0, int i1) {
             const int k0 = uniform(min(kt, last) * BKD * 2);
 #pragma unroll
-            for (int i = 0; i < AV; ++i) {
+            for (int i = i0; i < i1; ++i) {
                 half_t* dst = as + (wave * (kWave / 8) + i * (NT / 8)) * BKD;   // the wave's 8 rows
                 load_lds16(a_rs, dst, a_off[i], k0);
             }
         };
         auto step = [&](int kt, const half_t* cur, half_t* nxt, const u32x4 (&bw)[TN][BW], u32x4 (&bn)[TN][BW]) {
             if constexpr (DMA) {
-                if (kt + 1 < ke) dma_a(nxt, kt + 1);
+                if (kt + 1 < ke) dma_a(nxt, kt + 1, 0, AV);
             } else {
                 if (kt + 1 < ke) store_a(nxt);
                 load_a(kt + 2);
@@ -550,6 +551,10 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
 #pragma unroll
             for (int ks = 0; ks < BKD / 16; ++ks) {
                 if (ks + 1 < BKD / 16) fetch(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+                // keeps slice ks + 1's LDS reads ahead of slice ks's MFMAs
+                // (the scheduler otherwise sinks each read next to its use);
+                // the register form has no VGPRs to spare for it
+                if constexpr (DMA) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -561,7 +566,7 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
 
         load_b(b0, kb);
         if constexpr (DMA) {
-            dma_a(As[0], kb);
+            dma_a(As[0], kb, 0, AV);
             __builtin_amdgcn_s_waitcnt(0);
         } else {
             load_a(kb);
