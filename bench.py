@@ -28,7 +28,7 @@ The same run also times, each in its own section:
     calibration of the FETCH_SIZE / WRITE_SIZE counters);
   * the CPU oracle on a bounded sample (the CPU baseline).
 
-    python bench.py [--gpus 1] [--steps 240] [--warmup 20] [--only SECTION]
+    python bench.py [--gpus 1] [--steps 2400] [--warmup 20] [--only SECTION]
 """
 
 from __future__ import annotations
@@ -118,6 +118,16 @@ class Bench:
         stop.record(self.stream)
         stop.synchronize()
         return start.elapsed_time(stop) / 1e3   # seconds
+
+    def warm(self, fn, ms=50.0):
+        """Untimed calls of fn until `ms` of GPU time has passed. The clocks
+        ramp up over the first ~20 ms of sustained MFMA load: a GEMM timed
+        right after a few warm-up launches reads 10-15% slower than in
+        steady state."""
+        done, i = 0.0, 0
+        while done < ms * 1e-3:
+            done += self.time(lambda j: fn(i + j), 8)
+            i += 8
 
     def capture(self, fn, count):
         """HIP graph of `count` calls fn(0..count-1)."""
@@ -326,8 +336,7 @@ class Bench:
         qw, sc, zr = awq.awq_quantize_w8(self.d(lay["w"]), G)
         xm = self.d(lay["x"])
         ym = torch.empty((M, N), dtype=torch.float16, device=self.dev)
-        for i in range(5):
-            awq.awq_gemm_w8(xm, qw, sc, zr, G, out=ym)
+        self.warm(lambda i: awq.awq_gemm_w8(xm, qw, sc, zr, G, out=ym))
         t = self.time(lambda i: awq.awq_gemm_w8(xm, qw, sc, zr, G, out=ym), 50) / 50
         flop = 2.0 * M * N * K
         log(f"w8 gemm M={M} {N}x{K}: {t * 1e6:.1f} us, {flop / t / 1e12:.0f} TFLOP/s")
@@ -385,8 +394,7 @@ class Bench:
             def g(i, x=x, qw=qw, sc=sc, zr=zr, y=y):
                 awq.awq_gemm(x, qw, sc, zr, G, out=y, workspace=ws)
 
-            for i in range(5):
-                g(i)
+            self.warm(g)
             reps = 50
             t = self.time(g, reps) / reps
             flop = 2.0 * synth.PREFILL_M * N * K
@@ -408,8 +416,7 @@ class Bench:
             def g(i, x=x, qw=qw, sc=sc, zr=zr, y=y):
                 awq.awq_gemm(x, qw, sc, zr, G, out=y, workspace=ws)
 
-            for i in range(3):
-                g(i)
+            self.warm(g)
             t = self.time(g, 20) / 20
             flop = 2.0 * M * N * K
             sweep[f"{M}x{N}x{K}"] = {"us": round(t * 1e6, 2), "TFLOP/s": round(flop / t / 1e12, 1)}
@@ -428,8 +435,7 @@ class Bench:
         def q(i):
             self.awq.awq_quantize(w16, G, out=outs)
 
-        for i in range(5):
-            q(i)
+        self.warm(q)
         tq = self.time(q, 50) / 50
         gbs = quantize_bytes(N, K) / tq / 1e9
         log(f"quantize {N}x{K}: {tq * 1e6:.1f} us, {gbs:.0f} GB/s")
@@ -437,8 +443,7 @@ class Bench:
         def qc(i):
             self.awq.awq_quantize(w16, G, out=outs, clip_fraction=CLIP_BENCH_FRACTION)
 
-        for i in range(5):
-            qc(i)
+        self.warm(qc)
         tc = self.time(qc, 50) / 50
         log(f"clipped quantize {N}x{K} (p={CLIP_BENCH_FRACTION}): {tc * 1e6:.1f} us")
         return {"shape": f"{N}x{K}", "us": round(tq * 1e6, 2), "GB/s": round(gbs, 1),
@@ -573,7 +578,7 @@ class Bench:
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--steps", type=int, default=2400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true")
