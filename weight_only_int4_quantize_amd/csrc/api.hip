@@ -59,7 +59,7 @@ struct SearchLayout {
         scales = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         xs = c.take<half_t>(static_cast<size_t>(T) * K);
-        yref = c.take<float>(static_cast<size_t>(T) * N);
+        yref = c.take<float>(static_cast<size_t>(ref_tiled_floats(T, N)));
         tile_partials = c.take<double>(gemm_tile_count(T, N));
         losses = c.take<double>(n_alpha);
         bytes = c.used;
@@ -89,7 +89,7 @@ struct SalientLayout {
         scales = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         w_sal = c.take<half_t>(static_cast<size_t>(std::max(n_sal, 1)) * N);
-        yref = c.take<float>(static_cast<size_t>(T) * N);
+        yref = c.take<float>(static_cast<size_t>(ref_tiled_floats(T, N)));
         tile_partials = c.take<double>(gemm_tile_count(T, N));
         losses = c.take<double>(2);
         bytes = c.used;
@@ -116,7 +116,7 @@ struct ClipLayout {
         scales = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         if (scaled) xs = c.take<half_t>(static_cast<size_t>(T) * K);
-        yref = c.take<float>(static_cast<size_t>(T) * N);
+        yref = c.take<float>(static_cast<size_t>(ref_tiled_floats(T, N)));
         tile_partials = c.take<double>(gemm_tile_count(T, N));
         losses = c.take<double>(n);
         bytes = c.used;
@@ -124,7 +124,7 @@ struct ClipLayout {
 };
 
 // Y = x . W^T in fp32 (fp16 MFMA, fp32 accumulation), the unquantized
-// reference of both searches.
+// reference of the searches, written in the tiled layout of ref_offset.
 awq_status reference_output(const half_t* x, const half_t* w, int64_t T, int64_t N, int64_t K, int G, float* y,
                             hipStream_t s) {
     GemmArgs ref;

@@ -64,6 +64,31 @@ awq_status launch_gemv(const half_t* x, const uint32_t* qweight, const half_t* s
 // MFMA GEMM. The B operand is INT4 or W8 (qweight/scales/zeros) or fp16 W[N, K].
 enum class GemmB { kInt4, kF16, kInt8 };
 enum class GemmOut { kF16, kF32, kLoss };
+// The searches' fp32 reference output (kF32 results, kLoss references) is
+// kept in the accumulator order of v_mfma_f32_32x32x16: 256 x 128 tiles
+// (row-major over ceil(N / 128) tile columns), each of 32 sub-tiles of
+// 32 x 32 ordered by (column block of 32, row block of 32), each sub-tile
+// 64 lanes x 16 floats, lane L and element e holding row
+// 8 (e / 4) + 4 (L / 32) + e % 4 and column L % 32 of the sub-tile. A lane
+// thus reads or writes its 16 values of a sub-tile as four 16-byte
+// accesses. The buffer holds whole tiles (rows padded to 256, columns to
+// 128); padding positions hold nothing meaningful.
+constexpr int kRefTileM = 256;
+constexpr int kRefTileN = 128;
+__host__ __device__ inline int64_t ref_tiled_floats(int64_t M, int64_t N) {
+    return (M + kRefTileM - 1) / kRefTileM * kRefTileM * ((N + kRefTileN - 1) / kRefTileN * kRefTileN);
+}
+// first float of the 32 x 32 sub-tile starting at (m0, n0), both multiples of 32
+__host__ __device__ inline int64_t ref_subtile_base(int64_t m0, int64_t n0, int64_t tiles_n) {
+    const int64_t tile = (m0 / kRefTileM) * tiles_n + n0 / kRefTileN;
+    return (tile * 32 + ((n0 % kRefTileN) / 32) * 8 + (m0 % kRefTileM) / 32) * 1024;
+}
+__host__ __device__ inline int64_t ref_offset(int64_t m, int64_t n, int64_t tiles_n) {
+    const int64_t lane = n % 32 + 32 * ((m % 8) / 4);
+    const int64_t e = ((m % 32) / 8) * 4 + m % 4;
+    return ref_subtile_base(m / 32 * 32, n / 32 * 32, tiles_n) + lane * 16 + e;
+}
+
 struct GemmArgs {
     const half_t* a = nullptr;        // [M, K]
     const uint32_t* qweight = nullptr;
@@ -73,8 +98,8 @@ struct GemmArgs {
     int group_size = 128;
     int64_t M = 0, N = 0, K = 0;
     half_t* y16 = nullptr;            // kF16 output [M, N]
-    float* y32 = nullptr;             // kF32 output [M, N]
-    const float* yref = nullptr;      // kLoss reference [M, N]
+    float* y32 = nullptr;             // kF32 output [M, N], tiled (ref_offset)
+    const float* yref = nullptr;      // kLoss reference [M, N], tiled (ref_offset)
     double* partials = nullptr;       // kLoss: one double per tile
 };
 // Workspaces of the split kernels (GEMM stream-K, skinny K splits) start

@@ -602,17 +602,18 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
     // accumulator element e of MFMA tile (i, j) is output (row, col) =
     // (tm + wm + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, tn + wn + 32 j + lane % 32)
     const int lrow4 = (lane >> 5) * 4;
+    // fp32 results and loss references use the tiled layout of ref_offset
+    const int64_t ref_tiles_n = (N + kRefTileN - 1) / kRefTileN;
     auto emit = [&](int tm, int tn, int i, int j, int e, float v, float& sq) {
         const int n = tn + wn + j * 32 + lcol;
         const int m = tm + wm + i * 32 + (e >> 2) * 8 + lrow4 + (e & 3);
         if (m < M && n < N) {
-            const int64_t off = static_cast<int64_t>(m) * N + n;
             if constexpr (OMODE == GemmOut::kF16) {
-                args.y16[off] = static_cast<half_t>(v);
+                args.y16[static_cast<int64_t>(m) * N + n] = static_cast<half_t>(v);
             } else if constexpr (OMODE == GemmOut::kF32) {
-                args.y32[off] = v;
+                args.y32[ref_offset(m, n, ref_tiles_n)] = v;
             } else {
-                const float d = v - args.yref[off];
+                const float d = v - args.yref[ref_offset(m, n, ref_tiles_n)];
                 sq += d * d;
             }
         }
@@ -635,12 +636,47 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
     };
     auto finish_tile = [&](int tile, int tm, int tn) {
         float sq = 0.f;
+        if constexpr (OMODE == GemmOut::kF16) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+                for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) emit(tm, tn, i, j, e, acc[i][j][e], sq);
+                    for (int e = 0; e < 16; ++e) emit(tm, tn, i, j, e, acc[i][j][e], sq);
+        } else {
+            // tiled layout: a lane's 16 values of a sub-tile are contiguous.
+            // Sub-tiles that start inside [0, M) x [0, N) lie inside the
+            // padded buffer; their positions past M or N are padding.
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int m0 = tm + wm + i * 32, n0 = tn + wn + j * 32;
+                    if (m0 >= M || n0 >= N) continue;
+                    float4_t* p = reinterpret_cast<float4_t*>(
+                        (OMODE == GemmOut::kF32 ? args.y32 : const_cast<float*>(args.yref)) +
+                        ref_subtile_base(m0, n0, ref_tiles_n) + lane * 16);
+                    if constexpr (OMODE == GemmOut::kF32) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            p[q] = float4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                            acc[i][j][4 * q + 3]};
+                    } else {
+                        float4_t r[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) r[q] = p[q];
+                        const int n = n0 + lcol;
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int m = m0 + (e >> 2) * 8 + lrow4 + (e & 3);
+                            if (m < M && n < N) {
+                                const float d = acc[i][j][e] - r[e >> 2][e & 3];
+                                sq += d * d;
+                            }
+                        }
+                    }
+                }
+        }
         finish_loss(tile, sq);
     };
 

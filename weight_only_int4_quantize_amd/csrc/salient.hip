@@ -22,7 +22,8 @@
 //    LDS in chunks of 32 channels, each thread keeps 32 row accumulators for
 //    its column and reads w_salient coalesced. The fp16 form rounds
 //    fp32(y) + sum once; the fp32 form subtracts the sum from a reference
-//    output (the loss of the mixed layer against W x^T). Decode batches
+//    output kept in the tiled layout of ref_offset (the loss of the mixed
+//    layer against W x^T). Decode batches
 //    (M <= 8) take a narrower form with more blocks (see apply_small_kernel).
 #include "awq_internal.h"
 
@@ -112,13 +113,26 @@ __global__ __launch_bounds__(kApCols) void apply_kernel(const half_t* __restrict
         __syncthreads();
     }
     if (n >= N) return;
+    if constexpr (F32_SUB) {
+        // the tiled reference layout (ref_offset): the 32 rows are one
+        // sub-tile's; its lane n % 32 holds rows 8q + 0..3 as 16 contiguous
+        // floats, lane n % 32 + 32 rows 8q + 4..7. Rows past M are padding.
+        float4_t* p = reinterpret_cast<float4_t*>(
+            y32 + ref_subtile_base(m0, n / 32 * 32, (N + kRefTileN - 1) / kRefTileN) + (n % 32) * 16);
 #pragma unroll
-    for (int r = 0; r < kApRows; ++r) {
-        const int64_t mm = m0 + r;
-        if (mm < M) {
-            if constexpr (F32_SUB) {
-                y32[mm * N + n] -= acc[r];
-            } else {
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float4_t v = p[h * 32 * 4 + q];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[k] -= acc[q * 8 + h * 4 + k];
+                p[h * 32 * 4 + q] = v;
+            }
+    } else {
+#pragma unroll
+        for (int r = 0; r < kApRows; ++r) {
+            const int64_t mm = m0 + r;
+            if (mm < M) {
                 const float v = static_cast<float>(y16[mm * N + n]) + acc[r];
                 y16[mm * N + n] = static_cast<half_t>(v);
             }
@@ -176,7 +190,7 @@ __global__ __launch_bounds__(256) void apply_small_kernel(const half_t* __restri
         if (r < M) {
             const float v = ((red[0][r][lane] + red[1][r][lane]) + red[2][r][lane]) + red[3][r][lane];
             if constexpr (F32_SUB) {
-                y32[static_cast<int64_t>(r) * N + n] -= v;
+                y32[ref_offset(r, n, (N + kRefTileN - 1) / kRefTileN)] -= v;
             } else {
                 y16[static_cast<int64_t>(r) * N + n] = static_cast<half_t>(static_cast<float>(
                                                            y16[static_cast<int64_t>(r) * N + n]) + v);
