@@ -246,16 +246,18 @@ class Bench:
                 "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "per_launch": per_launch}
 
     def run_skinny(self):
-        """Batched decode rows on the skinny MFMA kernel (awq_gemm_ex with a
-        workspace): M = 16 on the decode shapes, M = 32 on the sweep shapes,
-        weights rotated over copies like the decode step."""
+        """Batched decode rows (awq_gemm_ex with a workspace): M = 4 on the
+        decode shapes (the GEMV), M = 16 on the decode shapes and M = 32 on
+        the sweep shapes (the skinny MFMA kernel), weights rotated over
+        copies like the decode step."""
         torch, awq = self.torch, self.awq
         ws = awq.gemm_workspace(64, 1, 1, self.dev)
         out = {}
-        cases = [(16, N, K, 128) for (N, K) in synth.DECODE_SHAPES] + \
+        cases = [(4, N, K, 128) for (N, K) in synth.DECODE_SHAPES] + \
+                [(16, N, K, 128) for (N, K) in synth.DECODE_SHAPES] + \
                 [(32, N, K, 128) for (N, K) in synth.SWEEP_SHAPES]
         for (M, N, K, g) in cases:
-            lay = synth.decode_layer(N, K, M) if M == 16 else synth.sweep_layer(N, K, M, g)
+            lay = synth.decode_layer(N, K, M) if M <= 16 else synth.sweep_layer(N, K, M, g)
             qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), g)
             x = self.d(lay["x"])
             nbytes = gemv_bytes(M, N, K, g)
@@ -272,8 +274,9 @@ class Bench:
             t = self.time(lambda _: gr.replay()) / (2 * n_copies)
             key = f"M{M}_{N}x{K}"
             out[key] = {"us": round(t * 1e6, 2), "GB/s": round(nbytes / t / 1e9, 1),
-                        "frac_of_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
-            log(f"skinny {key}: {t * 1e6:.2f} us, {nbytes / t / 1e9:.0f} GB/s")
+                        "frac_of_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                        "kernel": "gemv" if M <= 4 else "skinny"}
+            log(f"batched decode {key}: {t * 1e6:.2f} us, {nbytes / t / 1e9:.0f} GB/s")
             del cps, gr
         torch.cuda.synchronize()
         return out

@@ -246,6 +246,24 @@ def test_linear_ragged_both_paths(M, N, K, G):
         assert_linear_close(run_linear(lay["x"], qw, sc, zr, G, awq.PATH_GEMV), y_ref)
 
 
+@pytest.mark.parametrize("M,N,K,G", [
+    (3, 4099, 1024, 64),      # 4 weight rows per wave, a ragged last row set
+    (5, 4100, 2048, 128),
+    (8, 4111, 512, 32),
+    (2, 1001, 8448, 128),     # streaming form, 2 weight rows per wave, odd N
+    (4, 4097, 11008, 128),
+])
+def test_gemv_multirow_ragged(M, N, K, G):
+    """Several activation rows on the GEMV: the launch shapes that share each
+    staged x read among 4 (one-shot) or 2 (streaming) weight rows per wave,
+    with row counts that leave the last wave's set partly empty."""
+    lay = synth.make_layer(N, K, M, seed=[109, M, N, K, G], w_std=0.02)
+    say("gemv multirow", M, N, K, G)
+    qw, sc, zr = oracle.quantize(lay["w"], G)
+    y_ref = oracle.linear_ref(lay["x"], qw, sc, zr, G)
+    assert_linear_close(run_linear(lay["x"], qw, sc, zr, G, awq.PATH_GEMV), y_ref)
+
+
 @pytest.mark.parametrize("path", [awq.PATH_GEMV, awq.PATH_GEMM])
 def test_one_hot_input_returns_dequantized_column(path):
     """x = e_k: y = fp16 of the dequantized column k. Exact on the GEMV path
