@@ -13,17 +13,24 @@
 // (one v_mul per accumulator element per group); the end multiplies by the
 // last scale. Each step rounds once in fp32, ~1e-7 relative per group.
 //
-// Tiling (gfx950, 160 KB LDS, 4 SIMDs per CU):
-//  * a 256-thread block owns a BM x BN tile of y, 4 wavefronts in a 2 x 2
-//    arrangement; the 256 x 128 shape gives each wave 128 x 64 outputs as
-//    4 x 2 v_mfma_f32_32x32x16_f16 accumulators (128 VGPRs, VGPR form), so
-//    every 16-byte fragment read from LDS feeds 2-4 MFMAs;
-//  * K advances in steps of BK = 32. A (fp16) moves global -> registers ->
-//    LDS; B (packed INT4) is read as raw words, turned into exact fp16
-//    (q - z) once per block and written to LDS in natural k order (the
-//    fp16-B variant copies W). The next step's global loads are in flight
-//    while the current step's MFMAs run (two LDS stages, 60 KB, so two
-//    blocks fit on a CU);
+// Two forms share the epilogues and the scheduling below.
+//  * Direct-B form (quantized B with G >= 64, the default): a block owns a
+//    256 x 128 tile (4 waves, 2 blocks per CU) or a 256 x 256 tile (8 waves,
+//    1 per CU); each wave owns 256 x 32 outputs as 8 accumulators. K moves
+//    in steps of 64. Each lane loads its column's packed words for the
+//    step straight into registers in MFMA operand order and dequantizes
+//    them there; only A goes through LDS, by LDS-DMA loads (see
+//    run_segment_direct).
+//  * Older form (G = 32, and the fp16-B reference of the scale search):
+//    a 256-thread block owns a 256 x 128 tile, 4 wavefronts in a 2 x 2
+//    arrangement, each with 128 x 64 outputs as 4 x 2
+//    v_mfma_f32_32x32x16_f16 accumulators (128 VGPRs), so every 16-byte
+//    fragment read from LDS feeds 2-4 MFMAs. K advances in steps of BK = 32.
+//    A (fp16) moves global -> registers -> LDS; B (packed INT4) is read as
+//    raw words, turned into exact fp16 (q - z) once per block and written
+//    to LDS in natural k order (the fp16-B variant copies W). The next
+//    step's global loads are in flight while the current step's MFMAs run
+//    (two LDS stages, 60 KB, so two blocks fit on a CU);
 //  * LDS rows are 64 bytes with an XOR swizzle of their four 16-byte chunks
 //    (see swz), so fragment reads and staging writes are bank-conflict free;
 //  * blocks are dealt to the 8 XCDs round-robin by the dispatcher; the tile
