@@ -35,7 +35,7 @@
 
 namespace awq {
 
-constexpr int64_t kGemvBlocksPerCu = 2;
+constexpr int64_t kGemvBlocksPerCu = 1;
 namespace {
 
 __device__ inline half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
@@ -407,9 +407,11 @@ awq_status launch_t(const half_t* x, const uint32_t* qweight, const half_t* scal
 //    more activation rows, every weight costs one LDS read of x per row, so
 //    4 weight rows per wave share each read (2 in the streaming form):
 //    M = 4 on 11008 x 4096 takes 12.5 us against 14.4 us with 2.
-//  * Longer rows: a persistent grid of a few blocks per CU, so that staging
+//  * Longer rows: a persistent grid of one block per CU, so that staging
 //    x (2 bytes per input channel per block) stays small against the
-//    weights, each wave streaming its rows through a 4-deep ring.
+//    weights, each wave streaming its rows through a 4-deep ring, 2 rows at
+//    a time for rows of more than 3 items. Against 2 blocks per CU and 1 row
+//    at a time: 4096 x 11008 9.0 -> 8.2 us, 8192 x 28672 29 -> 27 us.
 template <int BITS, int MT>
 awq_status launch_m(const half_t* x, const uint32_t* qweight, const half_t* scales,
                     const half_t* zeros, int64_t N, int64_t K, int log2g, half_t* y,
@@ -428,7 +430,7 @@ awq_status launch_m(const half_t* x, const uint32_t* qweight, const half_t* scal
         return launch_t<BITS, MT, 1, 2, 2, true>(x, qweight, scales, zeros, N, K, log2g, y, ceil_div(N, 4), stream);
     const int64_t x_lds = static_cast<int64_t>(gemv_lds_bytes(MT, K, BITS));
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kGemvBlocksPerCu, max_shared_bytes() / (x_lds + 2048)));
-    if (MT >= 2)
+    if (MT >= 2 || kbs > 3)
         return launch_t<BITS, MT, 2, 2, 4>(x, qweight, scales, zeros, N, K, log2g, y, per_cu * cu_count(), stream);
     return launch_t<BITS, MT, 1, 2, 4>(x, qweight, scales, zeros, N, K, log2g, y, per_cu * cu_count(), stream);
 }
