@@ -148,13 +148,13 @@ awq_status awq_gemm(const void* x_f16, const uint32_t* qweight,
 /*
  * awq_gemm_path - awq_gemm with the kernel chosen by the caller:
  * path 0 = automatic (as awq_gemm), 1 = GEMV (requires M <= 8),
- * 2 = MFMA GEMM, 3 = skinny MFMA kernel (requires M <= 64, G <= 256, a packed
- * matrix under 4 GiB, and without a workspace a K whose staged x and group
- * scales fit one block's LDS: for G = 128, K <= 3840 for M <= 16, 2048 for
- * M <= 32, 1024 for M <= 64; for G = 64, K <= 3200, 1920 and 1024).
+ * 2 = MFMA GEMM, 3 = skinny MFMA kernel (requires M <= 64, G <= 256 and a
+ * packed matrix under 4 GiB; without a workspace each block walks all of K,
+ * staging it in LDS-sized phases).
  * Any other path, or a path whose requirement fails, returns AWQ_ERR_CONFIG.
- * The automatic choice takes the GEMV for M <= 4, the skinny kernel for
- * M <= 64 where it applies, then the GEMV for M <= 8, then the GEMM.
+ * The automatic choice takes the GEMV for M <= 4; the skinny kernel for
+ * M <= 64, except for M <= 8 where it would have to stage K in phases and
+ * the GEMV can run (then the GEMV); then the GEMM.
  */
 awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight,
                          const void* scales_f16, const void* zeros_f16,

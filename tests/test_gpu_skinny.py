@@ -1,8 +1,10 @@
 """Parity of the skinny MFMA kernel (4 < M <= 64, path 3 and the automatic
 choice for that range) with the CPU oracle: relative Frobenius error <= 1e-3
-and |y - y_ref| <= 1e-2 * (|y_ref| + 1) per element, with and without the
-K splits a workspace enables. A one-hot input reproduces the dequantized
-column exactly (one nonzero term, one scale multiply, one fp16 rounding).
+and |y - y_ref| <= 1e-2 * (|y_ref| + 1) per element, with the K splits a
+workspace enables and without them (one block per column tile, K staged in
+LDS-sized phases when it does not fit at once). A one-hot input reproduces
+the dequantized column exactly (one nonzero term, one scale multiply, one
+fp16 rounding).
 """
 
 import numpy as np
@@ -23,21 +25,16 @@ def skinny(x, qw, sc, zr, G, ws=None, out=None, path=awq.PATH_SKINNY):
     return awq.awq_gemm(x, qw, sc, zr, G, path=path, out=out, workspace=ws)
 
 
-def skinny_or_config(args, ws=None):
-    """Path 3 either runs or, without a workspace and with a K whose staged
-    x does not fit one block's LDS, refuses with AWQ_ERR_CONFIG."""
-    try:
-        return host(skinny(*args, ws=ws))
-    except awq.AwqError as e:
-        assert ws is None and e.status == 4, e
-        return None
+def skinny_no_workspace(args):
+    """Path 3 without a workspace: one block per column tile over all of K."""
+    return host(skinny(*args))
 
 
 @pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("N,K", synth.DECODE_SHAPES)
 def test_decode_m16_against_oracle(N, K, split):
     """With a workspace the skinny kernel splits K; without one the
-    automatic choice runs it whole (K = 4096) or falls back (K = 11008)."""
+    automatic choice runs one block per column tile over K in phases."""
     lay = synth.decode_layer(N, K, 16)
     say("skinny decode M=16", N, K, "split" if split else "auto, no workspace")
     qw, sc, zr = oracle.quantize(lay["w"], 128)
@@ -77,11 +74,44 @@ def test_skinny_ragged_against_oracle(M, N, K, G):
     qw, sc, zr = oracle.quantize(lay["w"], G)
     y_ref = oracle.linear_ref(lay["x"], qw, sc, zr, G)
     args = (dev(lay["x"]), dev(qw.view(np.int32)), dev(sc), dev(zr), G)
-    y = skinny_or_config(args)
-    if y is not None:
-        assert_linear_close(y, y_ref)
+    assert_linear_close(skinny_no_workspace(args), y_ref)
     assert_linear_close(host(skinny(*args, ws=awq.gemm_workspace(M, N, K))), y_ref)
     assert_linear_close(host(awq.awq_gemm(*args)), y_ref)     # automatic choice
+
+
+@pytest.mark.parametrize("M,N,K,G", [
+    (16, 300, 8192, 128),     # 3 phases of 24 groups (ring depth 8)
+    (9, 257, 11008, 64),
+    (33, 130, 6144, 256),     # 4 row blocks of 16, ring depth 4
+    (64, 100, 5120, 32),
+    (17, 513, 28672, 128),
+    (6, 4096, 11008, 128),    # the decode down projection at a small batch
+])
+def test_skinny_phases_against_oracle(M, N, K, G):
+    """K beyond one block's LDS without a workspace: staged in phases that
+    are a multiple of the weight ring's depth, the last one partial."""
+    lay = synth.make_layer(N, K, M, seed=[133, M, N, K, G], w_std=0.02)
+    say("skinny phases", M, N, K, G)
+    qw, sc, zr = oracle.quantize(lay["w"], G)
+    y_ref = oracle.linear_ref(lay["x"], qw, sc, zr, G)
+    args = (dev(lay["x"]), dev(qw.view(np.int32)), dev(sc), dev(zr), G)
+    assert_linear_close(skinny_no_workspace(args), y_ref)
+    assert_linear_close(host(awq.awq_gemm(*args)), y_ref)     # automatic choice, no workspace
+
+
+def test_skinny_phases_one_hot_is_exact():
+    """One-hot rows over a K of 3 phases pick single dequantized columns in
+    every phase, exactly."""
+    N, K, G = 200, 8192, 128
+    lay = synth.make_layer(N, K, 0, seed=[134], w_std=0.02)
+    qw, sc, zr = oracle.quantize(lay["w"], G)
+    w_hat = oracle.dequantize(qw, sc, zr, G, K)
+    ks = [0, 1, 3071, 3072, 3073, 5000, 6143, 6144, 8191, 4096, 128, 7000, 2047, 6200, 999, 7999]
+    x = np.zeros((len(ks), K), dtype=np.float16)
+    for i, k in enumerate(ks):
+        x[i, k] = 1.0
+    y = host(skinny(dev(x), dev(qw.view(np.int32)), dev(sc), dev(zr), G))
+    assert np.array_equal(y, w_hat[:, ks].T.astype(np.float16))
 
 
 @pytest.mark.parametrize("split", [False, True])

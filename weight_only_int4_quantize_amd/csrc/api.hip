@@ -227,12 +227,15 @@ awq_status awq_gemm_ex(const void* x_f16, const uint32_t* qweight, const void* s
     const half_t* zr = static_cast<const half_t*>(zeros_f16);
     half_t* y = static_cast<half_t*>(y_f16);
     const bool gemv_ok = gemv_supported(M, K);
-    const bool skinny_ok = skinny_supported(M, N, K, group_size, workspace != nullptr);
+    bool skinny_phased = false;
+    const bool skinny_ok = skinny_supported(M, N, K, group_size, workspace != nullptr, &skinny_phased);
     if (path == 1 && !gemv_ok) return AWQ_ERR_CONFIG;
     if (path == 3 && !skinny_ok) return AWQ_ERR_CONFIG;
-    // automatic: the GEMV up to 4 rows, the skinny kernel up to 64 where it
-    // applies, else the GEMV up to 8 rows, else the GEMM
-    const bool use_skinny = path == 3 || (path == 0 && M > 4 && skinny_ok);
+    // automatic: the GEMV up to 4 rows; the skinny kernel up to 64 rows, but
+    // below 9 rows only where it runs without K phases if the GEMV can run
+    // (the phased form, one block per column tile, is 2-3x slower than the
+    // GEMV there and 2-3x faster than the GEMM tile everywhere); else the GEMM
+    const bool use_skinny = path == 3 || (path == 0 && M > 4 && skinny_ok && !(skinny_phased && gemv_ok));
     const bool use_gemv = path == 1 || (path == 0 && gemv_ok && !use_skinny);
     if (use_gemv) return launch_gemv(x, qweight, sc, zr, M, N, K, group_size, y, as_stream(stream));
     if (workspace != nullptr) {

@@ -120,10 +120,13 @@ awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t s
 
 // Skinny MFMA GEMM for 4 < M <= 64 (decode batches): 16x16x32 MFMAs whose B
 // operand is one packed word per lane, K optionally split across blocks
-// (workspace != nullptr) with a fixed-order in-kernel fixup. Without a
-// workspace only shapes whose whole K fits one block's LDS are supported.
+// (workspace != nullptr) with a fixed-order in-kernel fixup. Without K
+// splits a block walks all of K, in LDS-sized phases if need be.
 constexpr int kSkinnyMaxM = 64;
-bool skinny_supported(int64_t M, int64_t N, int64_t K, int group_size, bool have_workspace);
+// phased (optional): set when the call would walk K in LDS-sized phases on
+// one block per column tile (no K splits), the slow form.
+bool skinny_supported(int64_t M, int64_t N, int64_t K, int group_size, bool have_workspace,
+                      bool* phased = nullptr);
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K);
 awq_status launch_skinny(const half_t* x, const uint32_t* qweight, const half_t* scales,
                          const half_t* zeros, int64_t M, int64_t N, int64_t K, int group_size,

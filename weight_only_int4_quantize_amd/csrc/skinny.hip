@@ -23,11 +23,15 @@
 //   weights, streamed straight into registers through a ring of groups in
 //   flight. Vector-memory loads complete in order, so keeping x out of the
 //   loop is what lets the ring stay deep.
-// * The K range of a block is bounded by the LDS; beyond that, and to fill
-//   the GPU when there are few column tiles, K is split across blocks (this
-//   needs a workspace). A block parks its fp32 partial tile, bumps a
-//   per-column-tile counter, and the last block to arrive adds every split
-//   in order and writes y: deterministic, and nobody waits on anybody.
+// * To fill the GPU when there are few column tiles, K is split across
+//   blocks (this needs a workspace). A block parks its fp32 partial tile,
+//   bumps a per-column-tile counter, and the last block to arrive adds every
+//   split in order and writes y: deterministic, and nobody waits on anybody.
+// * A K range larger than the LDS holds (no workspace, or more column tiles
+//   than it counts) is walked in phases: stage a phase's x and pairs, stream
+//   its groups, and stage the next phase between two barriers. The weight
+//   ring runs on across the phases; they are a multiple of its depth long,
+//   so each starts on slot 0.
 #include <algorithm>
 
 #include "awq_internal.h"
@@ -107,6 +111,8 @@ __host__ __device__ inline int sk_lds_bytes(int mb, int krange, int group_size) 
     return 16 * mb * sk_stride(krange) * 2 + kSkBN * sk_szst(krange / group_size) * 4;
 }
 constexpr int kSkSZ = 32;               // (scale, zero) pairs per thread at most
+// weight groups in flight per wave (the ring depth)
+__host__ __device__ constexpr int sk_depth(int mb, int wpl) { return (mb <= 2 && wpl <= 4) ? 8 : 4; }
 constexpr int kSkSZForm[3] = {4, 8, 32};
 
 template <int MB, int WPL, int FORM>
@@ -115,11 +121,12 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __r
                                                               const half_t* __restrict__ scales,
                                                               const half_t* __restrict__ zeros,
                                                               half_t* __restrict__ y, int M, int N, int K,
-                                                              int splits, float* __restrict__ partials,
+                                                              int splits, int phase_groups,
+                                                              float* __restrict__ partials,
                                                               int* __restrict__ counters) {
     constexpr int G = WPL * 32;
     constexpr int MP = 16 * MB;                          // padded rows
-    constexpr int kSkDepth = (MB <= 2 && WPL <= 4) ? 8 : 4;   // weight groups in flight per wave
+    constexpr int kSkDepth = sk_depth(MB, WPL);
     constexpr int XPN = kSkXPForm[FORM];
     constexpr int SZN = kSkSZForm[FORM];
     static_assert(kSkXPForm[2] == kSkXP && kSkSZForm[2] == kSkSZ, "the largest form is the bound sk_kmax uses");
@@ -137,8 +144,11 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __r
     const int ng = K / G;
     const int g0 = static_cast<int>(static_cast<int64_t>(split) * ng / splits);
     const int g1 = static_cast<int>(static_cast<int64_t>(split + 1) * ng / splits);
-    const int k0 = g0 * G, k1 = g1 * G;
-    const int stride = sk_stride(k1 - k0);
+    // The K range is staged in phases of at most phase_groups groups (one
+    // phase unless the range exceeds the LDS; then phase_groups is a
+    // multiple of the ring depth, so every phase starts on slot 0)
+    const int pg = min(phase_groups, g1 - g0);
+    const int stride = sk_stride(pg * G);
 
     // ---- weights: buffer loads; an offset at or past a buffer's size
     //      reads zero, which is how columns past N and groups past the
@@ -187,8 +197,8 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __r
     //      consecutive groups of one column, so these loads are coalesced
     //      (one 2-byte load per lane and group in the main loop would cost a
     //      cache-line request each) ----
-    const int ngb = g1 - g0;
-    const int szst = sk_szst(ngb);
+    const int ngb = pg;                                  // groups of the first phase
+    const int szst = sk_szst(pg);
     const int nsz = kSkBN * ngb;
     uint32_t* szs = reinterpret_cast<uint32_t*>(xs + MP * stride);
     uint16_t sr[SZN], zr[SZN];
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __r
     //      loads, no branches) ----
     const uint32_t x_bytes = static_cast<uint32_t>(static_cast<int64_t>(M) * K * 2);
     const auto rx = rsrc(x, x_bytes);
-    const int pr = (k1 - k0) / 8;                        // pieces per row
+    const int pr = pg * G / 8;                           // pieces per row
     const int pieces = MP * pr;
     uint4 xr[XPN];
 #pragma unroll
@@ -214,7 +224,7 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __r
         const int p = tid + i * kSkThreads;
         const int r = p / pr, c8 = p - r * pr;
         const bool ok = p < pieces && r < M;
-        const uint32_t off = ok ? (static_cast<uint32_t>(r) * K + k0 + c8 * 8) * 2 : x_bytes;
+        const uint32_t off = ok ? (static_cast<uint32_t>(r) * K + g0 * G + c8 * 8) * 2 : x_bytes;
         xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
     }
 #pragma unroll
@@ -255,51 +265,74 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __r
     // Ring slot d holds group g0 + gb + d. Refills are issued
     // unconditionally at a fixed place, so the compiler's wait counts track
     // the ring exactly; only the compute of groups past the range is skipped.
-    const int nblk = g1 - g0;
     const half_t* xcol = &xs[col * stride + 8 * lg * WPL];
     const uint32_t* szcol = &szs[(wave * 32 + col) * szst];
-    for (int gb = 0; gb < nblk; gb += kSkDepth) {
+    for (int h0 = 0; h0 < g1 - g0; h0 += pg) {
+        const int h1 = min(g1 - g0, h0 + pg);                // this phase: groups g0 + [h0, h1)
+        if (h0 > 0) {
+            // every wave is done with the previous phase's x and pairs
+            __syncthreads();
+            const int nsz_h = kSkBN * (h1 - h0), pr_h = (h1 - h0) * G / 8, pieces_h = MP * pr_h;
+            for (int e = tid; e < nsz_h; e += kSkThreads) {
+                const int c = e / (h1 - h0), gi = e - c * (h1 - h0);
+                const int n = tile * kSkBN + c;
+                const uint32_t so = n < N ? (static_cast<uint32_t>(n) * ng + g0 + h0 + gi) * 2 : sz_bytes;
+                const uint16_t sv = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
+                const uint16_t zv = __builtin_amdgcn_raw_buffer_load_b16(rz, so, 0, 0);
+                szs[c * szst + gi] = static_cast<uint32_t>(sv) | (static_cast<uint32_t>(zv) << 16);
+            }
+            for (int pc = tid; pc < pieces_h; pc += kSkThreads) {
+                const int r = pc / pr_h, c8 = pc - r * pr_h;
+                const uint32_t off = r < M ? (static_cast<uint32_t>(r) * K + (g0 + h0) * G + c8 * 8) * 2 : x_bytes;
+                *reinterpret_cast<uint4*>(&xs[r * stride + c8 * 8]) =
+                    permute8(__builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0)));
+            }
+            __syncthreads();
+        }
+        for (int gb = h0; gb < h1; gb += kSkDepth) {
 #pragma unroll
-        for (int d = 0; d < kSkDepth; ++d) {
-            const int gi = gb + d;
-            GroupLoad<WPL>& gl = ring[d];
-            if (gi < nblk) {
-                half8_t bf[2][WPL];
-                float s[2];
+            for (int d = 0; d < kSkDepth; ++d) {
+                const int gi = gb + d;                       // group g0 + gi, slot d
+                GroupLoad<WPL>& gl = ring[d];
+                if (gi < h1) {
+                    half8_t bf[2][WPL];
+                    float s[2];
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const uint32_t sz = szcol[t * 16 * szst + gi];
-                    const half_t z = __builtin_bit_cast(half_t, static_cast<uint16_t>(sz >> 16));
-                    const half_t zh = static_cast<half_t>(1024.0f) + z;   // exact
-                    const half_t zl = static_cast<half_t>(64.0f) + z;     // exact
+                    for (int t = 0; t < 2; ++t) {
+                        const uint32_t sz = szcol[t * 16 * szst + gi - h0];
+                        const half_t z = __builtin_bit_cast(half_t, static_cast<uint16_t>(sz >> 16));
+                        const half_t zh = static_cast<half_t>(1024.0f) + z;   // exact
+                        const half_t zl = static_cast<half_t>(64.0f) + z;     // exact
 #pragma unroll
-                    for (int j = 0; j < WPL; ++j) bf[t][j] = unpack8(gl.w[t][j], half2_t{zh, zh}, half2_t{zl, zl}, uk);
-                    s[t] = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(sz & 0xFFFFu)));
-                }
-                const half_t* xb = xcol + gi * G;
-                float4_t part[MB][2];
+                        for (int j = 0; j < WPL; ++j)
+                            bf[t][j] = unpack8(gl.w[t][j], half2_t{zh, zh}, half2_t{zl, zl}, uk);
+                        s[t] = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(sz & 0xFFFFu)));
+                    }
+                    const half_t* xb = xcol + (gi - h0) * G;
+                    float4_t part[MB][2];
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
+                    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) part[mb][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+                        for (int t = 0; t < 2; ++t) part[mb][t] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < WPL; ++j) {
+                    for (int j = 0; j < WPL; ++j) {
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) {
-                        const half8_t a = *reinterpret_cast<const half8_t*>(xb + 16 * mb * stride + 8 * j);
+                        for (int mb = 0; mb < MB; ++mb) {
+                            const half8_t a = *reinterpret_cast<const half8_t*>(xb + 16 * mb * stride + 8 * j);
+#pragma unroll
+                            for (int t = 0; t < 2; ++t)
+                                part[mb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[t][j], part[mb][t], 0, 0, 0);
+                        }
+                    }
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                         for (int t = 0; t < 2; ++t)
-                            part[mb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[t][j], part[mb][t], 0, 0, 0);
-                    }
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[mb][t][e] += s[t] * part[mb][t][e];
                 }
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[mb][t][e] += s[t] * part[mb][t][e];
+                load_group(gl, g0 + gi + kSkDepth);              // refill the slot
             }
-            load_group(gl, g0 + gi + kSkDepth);              // refill the slot
         }
     }
 
@@ -392,29 +425,44 @@ int64_t sk_max_parts() { return 3 * static_cast<int64_t>(cu_count()); }
 
 size_t sk_partial_bytes(int64_t M) { return static_cast<size_t>(sk_mb(M)) * 2 * kSkThreads * 16; }
 
-// Splits of K: at least enough for each block's x range to fit the LDS;
-// with a workspace, as many more as fill one block per CU, each split
-// keeping at least 512 of K (shorter splits cost more in their partial
-// tiles and fixup than they add in parallelism: M = 16 on 4096 x 4096 takes
-// 10.4 us with 8 splits against 12.1 us with 16). 0 = this shape cannot
-// run here.
-int sk_splits(int64_t M, int64_t N, int64_t K, int group_size, bool have_workspace) {
+// How a shape runs: K splits across blocks (with a workspace) and, within a
+// block, phases of at most `pg` groups staged in LDS one after the other.
+// With a workspace, as many splits as fill one block per CU, each keeping
+// at least 512 of K (shorter splits cost more in their partial tiles and
+// fixup than they add in parallelism: M = 16 on 4096 x 4096 takes 10.4 us
+// with 8 splits against 12.1 us with 16), and never fewer than keep each
+// split inside the LDS, so every split is one phase. Without one (or with
+// more column tiles than the workspace counts), one block per column tile
+// walks all of K, in phases of a multiple of the ring depth when K exceeds
+// the LDS. false = this shape cannot run here.
+bool sk_plan(int64_t M, int64_t N, int64_t K, int group_size, bool have_workspace, int& splits, int& pg) {
     const int64_t tiles = sk_tiles(N);
     const int64_t ng = K / group_size;
     const int64_t gmax = sk_kmax(M, group_size) / group_size;
-    if (gmax < 1) return 0;
+    if (gmax < 1) return false;
     const int64_t s_min = (ng + gmax - 1) / gmax;
-    if (!have_workspace) return s_min == 1 ? 1 : 0;
-    if (tiles > split_counter_slots()) return s_min == 1 ? 1 : 0;
-    int64_t s = std::max<int64_t>(s_min, std::min<int64_t>(cu_count() / tiles, std::max<int64_t>(1, K / 512)));
-    while (s > s_min && s * tiles > sk_max_parts()) --s;
-    if (s > 1 && s * tiles > sk_max_parts()) return 0;
-    return static_cast<int>(std::max<int64_t>(1, s));
+    if (have_workspace && tiles <= split_counter_slots()) {
+        int64_t s = std::max<int64_t>(s_min, std::min<int64_t>(cu_count() / tiles, std::max<int64_t>(1, K / 512)));
+        while (s > s_min && s * tiles > sk_max_parts()) --s;
+        if (s == 1 || s * tiles <= sk_max_parts()) {
+            splits = static_cast<int>(s);
+            pg = static_cast<int>((ng + s - 1) / s);
+            return true;
+        }
+    }
+    splits = 1;
+    if (ng <= gmax) {
+        pg = static_cast<int>(ng);
+        return true;
+    }
+    const int64_t depth = sk_depth(sk_mb(M), group_size / 32);
+    pg = static_cast<int>(gmax / depth * depth);
+    return pg >= depth;
 }
 
 template <int MB, int WPL, int FORM>
 awq_status launch_form(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
-                       int N, int K, half_t* y, int splits, float* partials, int* counters, size_t lds,
+                       int N, int K, half_t* y, int splits, int pg, float* partials, int* counters, size_t lds,
                        hipStream_t stream) {
     static bool attr_set = false;
     if (!attr_set) {
@@ -425,36 +473,37 @@ awq_status launch_form(const half_t* x, const uint32_t* qweight, const half_t* s
     }
     const int64_t blocks = sk_tiles(N) * splits;
     hipLaunchKernelGGL((skinny_kernel<MB, WPL, FORM>), dim3(static_cast<unsigned>(blocks)), dim3(kSkThreads), lds,
-                       stream, x, qweight, scales, zeros, y, M, N, K, splits, partials, counters);
+                       stream, x, qweight, scales, zeros, y, M, N, K, splits, pg, partials, counters);
     return last_launch_status();
 }
 
 template <int MB, int WPL>
 awq_status launch_cfg(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
                       int N, int K, half_t* y, void* workspace, hipStream_t stream) {
-    const int splits = sk_splits(M, N, K, WPL * 32, workspace != nullptr);
-    if (splits == 0) return AWQ_ERR_CONFIG;
+    int splits = 0, pg = 0;
+    if (!sk_plan(M, N, K, WPL * 32, workspace != nullptr, splits, pg)) return AWQ_ERR_CONFIG;
     float* partials = nullptr;
     int* counters = nullptr;
     if (splits > 1) {
         counters = static_cast<int*>(workspace);
         partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_counter_bytes());
     }
-    // the longest range of any split sets the LDS
-    const int ng = K / (WPL * 32);
-    const int gmax_split = (ng + splits - 1) / splits;
-    const size_t lds = static_cast<size_t>(sk_lds_bytes(MB, gmax_split * WPL * 32, WPL * 32));
-    // the smallest prologue that stages 16 MB rows of the block's K range
-    // and its (scale, zero) pairs
+    // the longest phase sets the LDS
+    const size_t lds = static_cast<size_t>(sk_lds_bytes(MB, pg * WPL * 32, WPL * 32));
+    // the smallest prologue that stages 16 MB rows of a phase's K range and
+    // its (scale, zero) pairs
     auto fits = [&](int form) {
-        return 16 * MB * (gmax_split * WPL * 32 / 8) <= kSkXPForm[form] * kSkThreads &&
-               kSkBN * gmax_split <= kSkSZForm[form] * kSkThreads;
+        return 16 * MB * (pg * WPL * 32 / 8) <= kSkXPForm[form] * kSkThreads &&
+               kSkBN * pg <= kSkSZForm[form] * kSkThreads;
     };
     if (fits(0))
-        return launch_form<MB, WPL, 0>(x, qweight, scales, zeros, M, N, K, y, splits, partials, counters, lds, stream);
+        return launch_form<MB, WPL, 0>(x, qweight, scales, zeros, M, N, K, y, splits, pg, partials, counters, lds,
+                                          stream);
     if (fits(1))
-        return launch_form<MB, WPL, 1>(x, qweight, scales, zeros, M, N, K, y, splits, partials, counters, lds, stream);
-    return launch_form<MB, WPL, 2>(x, qweight, scales, zeros, M, N, K, y, splits, partials, counters, lds, stream);
+        return launch_form<MB, WPL, 1>(x, qweight, scales, zeros, M, N, K, y, splits, pg, partials, counters, lds,
+                                          stream);
+    return launch_form<MB, WPL, 2>(x, qweight, scales, zeros, M, N, K, y, splits, pg, partials, counters, lds,
+                                      stream);
 }
 
 template <int WPL>
@@ -469,7 +518,7 @@ awq_status launch_wpl(const half_t* x, const uint32_t* qweight, const half_t* sc
 
 }  // namespace
 
-bool skinny_supported(int64_t M, int64_t N, int64_t K, int group_size, bool have_workspace) {
+bool skinny_supported(int64_t M, int64_t N, int64_t K, int group_size, bool have_workspace, bool* phased) {
     // buffer offsets are 32-bit: the packed matrix plus one row of slack
     // (the largest offset a zero-reading lane forms), and x, stay below 4 GiB
     // group sizes 32 .. 256 (1 .. 8 packed words per lane and group)
@@ -477,7 +526,10 @@ bool skinny_supported(int64_t M, int64_t N, int64_t K, int group_size, bool have
     if (M < 1 || M > kSkinnyMaxM || N < 1 || (N + 1) * (K / 2) + 64 >= (int64_t{1} << 32) ||
         M * K * 2 + 64 >= (int64_t{1} << 32))
         return false;
-    return sk_splits(M, N, K, group_size, have_workspace) > 0;
+    int splits = 0, pg = 0;
+    if (!sk_plan(M, N, K, group_size, have_workspace, splits, pg)) return false;
+    if (phased != nullptr) *phased = splits == 1 && pg < K / group_size;
+    return true;
 }
 
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K) {
