@@ -71,6 +71,8 @@ __device__ __forceinline__ int swz64(int r, int c) { return r * BKD + ((c ^ ((r 
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, half_t* lds, int voff, int soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+#else
+    (void)rs, (void)lds, (void)voff, (void)soff;
 #endif
 }
 // A zero group scale would make the rescale ratio infinite; it is taken as
@@ -266,7 +268,6 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
     const int lchunk = lane >> 5;          // which 8-k half of a 16-k MFMA step
     const UnpackConsts uk = unpack_consts();
     const int nk = K / (DIRECT ? BKD : BK);
-    const int steps_per_group = INT4 ? G / BK : nk + 1;
     const int b_row = tid >> 1;            // int4 staging: row t / 2,
     const int b_half = tid & 1;            //   codes 16 * (t % 2) .. +15 of the step
 
@@ -791,7 +792,6 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
 }
 
 constexpr int kBM = 256;
-constexpr int kBN = 128;
 
 // Block geometries: 256 x 128 tiles of 256 threads, two blocks per CU (every
 // form), and 256 x 256 tiles of 512 threads (8 waves of 256 x 32), one block
