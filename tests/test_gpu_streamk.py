@@ -155,3 +155,33 @@ def test_wide_tiles_w8():
     y = awq.awq_gemm_w8(dev(lay["x"]), dev(qw.view(np.int32)), dev(sc), dev(zr), G, path=awq.PATH_GEMM)
     rows = sampled_rows(N, 160, N + 13)
     assert_linear_close(host(y)[:, rows], oracle.linear_ref_w8(lay["x"], qw[rows], sc[rows], zr[rows], G))
+
+
+@pytest.mark.parametrize("M,N,K,G", [
+    (1536, 11008, 4096, 128),   # 516 tiles: 512 whole, the last 4 split over every slot
+    (2048, 8320, 1024, 128),    # 520 tiles, a tail of 8
+    (2000, 8300, 2048, 64),     # the same with ragged rows and columns
+    (1792, 11008, 4096, 128),   # 602 tiles, a tail of 90
+])
+def test_hybrid_tail_sampled(M, N, K, G):
+    """More than one round of tiles with a short last round: the whole rounds
+    run one tile per block and only the last round's tiles are split.
+    Sampled output columns against the oracle (the last tiles' columns
+    included), repeated calls bit-identical, and within fp32 summation order
+    of the unsplit GEMM."""
+    lay = synth.make_layer(N, K, M, seed=[140, M, N, K, G], w_std=0.02)
+    say("hybrid tail", M, N, K, G)
+    x = dev(lay["x"])
+    qw, sc, zr = awq.awq_quantize(dev(lay["w"]), G)
+    ws = awq.gemm_workspace(M, N, K)
+    y1 = gemm_ws(x, qw, sc, zr, G, ws).clone()
+    y2 = gemm_ws(x, qw, sc, zr, G, ws)
+    y0 = awq.awq_gemm(x, qw, sc, zr, G, path=awq.PATH_GEMM)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    rows = np.unique(np.concatenate([sampled_rows(N, 160, M + N), np.arange(max(0, N - 300), N)]))
+    eq = oracle.quantize(lay["w"][rows], G)
+    assert_linear_close(host(y1)[:, rows], oracle.linear_ref(lay["x"], *eq, G))
+    d = (y1.float() - y0.float()).abs()
+    assert float(d.max()) <= float(1e-2 * (y0.float().abs().max() + 1))
+    assert float(torch.linalg.norm(y1.float() - y0.float())) <= 1e-3 * float(torch.linalg.norm(y0.float()))

@@ -200,10 +200,11 @@ __device__ inline int xcd_tile(int block, int tiles) {
 struct StreamK {
     float* partials = nullptr;   // [grid][2][BM * BN] fp32
     int* counters = nullptr;     // [tiles], zero between launches
-    int total = 0;               // tiles * ipt
+    int total = 0;               // split tiles * ipt
     int ipt = 0;                 // K steps per tile
-    int grid = 0;
+    int grid = 0;                // blocks over the split tiles
     int q = 0, r = 0;            // total = q * grid + r, q >= 1
+    int dp_tiles = 0;            // tiles [0, dp_tiles) go whole to the first dp_tiles blocks
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -226,7 +227,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* p, int byt
 // dequantizes them there; only A goes through LDS.
 //
 // WGM: waves along M (the 4 waves form WGM x 4 / WGM).
-template <int BM, int BN, GemmB BMODE, GemmOut OMODE, bool STREAMK, bool DIRECT, int WGM = 2, int NT = kThreads>
+template <int BM, int BN, GemmB BMODE, GemmOut OMODE, bool STREAMK, bool DIRECT, int WGM = 2, int NT = kThreads,
+          bool SKDMA = false>
 __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int tiles_n, StreamK sk) {
     constexpr int WGN = NT / kWave / WGM;
     constexpr int WTM = BM / WGM;               // wave tile rows
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
         // A goes to LDS by LDS-DMA loads, except under stream-K, where the
         // register round trip measured faster (2048x4096x11008: 185 us
         // against 196 us; without stream-K the DMA form is 4-12 % faster)
-        constexpr bool DMA = !STREAMK;
+        constexpr bool DMA = !STREAMK || SKDMA;
         const int lh = lane >> 5;
         // Buffer loads from tile-relative bases (scalar) with 32-bit lane
         // offsets; rows past M / N are clamped to the last row, so every
@@ -695,12 +697,24 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
         segment(tm, tn, 0, nk);
         finish_tile(tile, tm, tn);
     } else {
-        // consecutive ranges (which share tiles) go to the same XCD
-        const int b = uniform(xcd_tile(blockIdx.x, gridDim.x));
-        const int u1 = uniform(sk_start(sk, b + 1));
-        int u = uniform(sk_start(sk, b));
+        // Units u = (tile, K step) = tile * ipt + step over all tiles. A block
+        // of the data-parallel head owns one whole tile; the others own a
+        // stream-K range of the split tiles' units (consecutive ranges,
+        // which share tiles, go to the same XCD). One loop serves both.
+        const int head = sk.dp_tiles * sk.ipt;
+        int u, u1;
+        int b = 0;
+        if (static_cast<int>(blockIdx.x) < sk.dp_tiles) {
+            u = uniform(xcd_tile(blockIdx.x, sk.dp_tiles) * sk.ipt);
+            u1 = u + sk.ipt;
+        } else {
+            b = uniform(xcd_tile(blockIdx.x - sk.dp_tiles, gridDim.x - sk.dp_tiles));
+            u = uniform(head + sk_start(sk, b));
+            u1 = uniform(head + sk_start(sk, b + 1));
+        }
         while (u < u1) {
             const int tile = uniform(u / sk.ipt);
+            const int lt = tile - sk.dp_tiles;               // tile within the split range
             const int kb = uniform(u - tile * sk.ipt);
             const int ke = uniform(min(sk.ipt, kb + (u1 - u)));
             const int tm = (tile / tiles_n) * BM;
@@ -715,13 +729,13 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
             // blocks to arrive adds every part in segment order (so the
             // result does not depend on arrival order), finishes the tile and
             // resets its counter. Nobody waits on anybody.
-            const int u_first = tile * sk.ipt;
+            const int u_first = lt * sk.ipt;
             const int b_first = uniform(sk_block_of(sk, u_first));
             const int b_last = uniform(sk_block_of(sk, u_first + sk.ipt - 1));
             // a block holds at most two partial tiles: the one it starts in
             // (slot 0) and the one it ends in (slot 1)
             auto slot_of = [&](int bb) {
-                const int slot = uniform(bb * 2 + (sk_start(sk, bb) / sk.ipt == tile ? 0 : 1));
+                const int slot = uniform(bb * 2 + (sk_start(sk, bb) / sk.ipt == lt ? 0 : 1));
                 return sk.partials + static_cast<int64_t>(slot) * (BM * BN);
             };
             {
@@ -808,17 +822,30 @@ constexpr int kMinSteps = 8;        // K steps per block at least
 int64_t resident_slots(const Geometry& g) { return static_cast<int64_t>(g.per_cu) * cu_count(); }
 int64_t tiles_of(const Geometry& g, int64_t M, int64_t N) { return ceil_div(M, g.bm) * ceil_div(N, g.bn); }
 
-// Stream-K pays off when there are fewer tiles than resident block slots:
-// one tile per block would leave CUs idle or at one block each. With more
-// 256 x 128 tiles, the last round's blocks run one per CU at close to the
-// per-CU rate of two, and splitting costs more in partial traffic than it
-// recovers.
-// Stream-K for shapes under one round of tiles. Over more rounds nearly every
-// tile would be split and its fp32 partials moved through memory: measured on
-// 2048 x 11008 x 4096 with 256 x 256 tiles, 831 MB of traffic per launch
-// against 282 MB unsplit, for a few percent of time.
+// Stream-K pays off when there are well under one round of tiles: one tile
+// per block would leave CUs idle or at one block each. Over more rounds
+// nearly every tile would be split and its fp32 partials moved through
+// memory: measured on 2048 x 11008 x 4096 with 256 x 256 tiles, 831 MB of
+// traffic per launch against 282 MB unsplit, for a few percent of time
+// (use_hybrid splits only a short last round instead).
 bool use_stream_k(const Geometry& g, int64_t tiles, int64_t steps) {
-    if (tiles >= resident_slots(g) || tiles > split_counter_slots()) return false;
+    // up to two thirds of a round: nearer a full round, one tile per block
+    // is faster than the partials (M = 1280 x 11008 x 4096: 129 us one tile
+    // per block against 147 us split)
+    if (tiles * 3 > resident_slots(g) * 2 || tiles > split_counter_slots()) return false;
+    return tiles * steps < (int64_t{1} << 31);
+}
+
+// Over more than one round with a short last round (at most a quarter of
+// the slots), the whole rounds run data-parallel and only the last round's
+// tiles are split (stream-K over the resident slots), so the tail no longer
+// runs at one block per CU: 516 tiles of 1536 x 11008 x 4096 take 158 us
+// against 189 us. With longer tails the partials cost more than they save
+// (688 tiles of 2048 x 11008 x 4096: 208 against 196 us).
+bool use_hybrid(const Geometry& g, int64_t tiles, int64_t steps) {
+    const int64_t slots = resident_slots(g);
+    const int64_t tail = tiles % slots;
+    if (tiles <= slots || tail == 0 || tail * 4 > slots || tiles > split_counter_slots()) return false;
     return tiles * steps < (int64_t{1} << 31);
 }
 
@@ -854,6 +881,23 @@ void launch_cfg(const GemmArgs& args, void* workspace, hipStream_t stream) {
                            dim3(static_cast<unsigned>(sk.grid)), dim3(GEO.threads), 0, stream, args,
                            static_cast<int>(tiles_n), sk);
         return;
+    }
+    if constexpr (DIRECT) {
+        if (workspace != nullptr && use_hybrid(GEO, tiles, steps)) {
+            sk.dp_tiles = static_cast<int>(tiles / resident_slots(GEO) * resident_slots(GEO));
+            const int64_t tail = tiles - sk.dp_tiles;
+            sk.ipt = static_cast<int>(steps);
+            sk.total = static_cast<int>(tail * sk.ipt);
+            sk.grid = stream_k_grid(GEO, tail, steps);
+            sk.q = sk.total / sk.grid;
+            sk.r = sk.total % sk.grid;
+            sk.counters = static_cast<int*>(workspace);
+            sk.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_counter_bytes());
+            hipLaunchKernelGGL((gemm_kernel<GEO.bm, GEO.bn, BMODE, OMODE, true, DIRECT, WGM, GEO.threads, true>),
+                               dim3(static_cast<unsigned>(sk.dp_tiles + sk.grid)), dim3(GEO.threads), 0, stream, args,
+                               static_cast<int>(tiles_n), sk);
+            return;
+        }
     }
     hipLaunchKernelGGL((gemm_kernel<GEO.bm, GEO.bn, BMODE, OMODE, false, DIRECT, WGM, GEO.threads>),
                        dim3(static_cast<unsigned>(tiles)), dim3(GEO.threads), 0, stream, args,
