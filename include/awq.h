@@ -166,8 +166,9 @@ awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight,
  * lets the MFMA kernels split the K loop of output tiles across thread
  * blocks when the tile count would leave the GPU's resident blocks partly
  * idle: a stream-K decomposition for the GEMM (e.g. the M = 2048 prefill of
- * a 4096-wide layer) and fixed K splits for the skinny kernel (e.g. M = 16
- * on a 4096-wide layer, 32 column tiles). Same operation, arguments and
+ * a 4096-wide layer, or only the tiles of a short last round behind whole
+ * tiles), and fixed K splits for the skinny kernel (e.g. M = 16 on a
+ * 4096-wide layer, 32 column tiles). Same operation, arguments and
  * results as awq_gemm (rskf.cn §3.3 GEMM kernel), up to fp32 summation
  * order; the partial sums of a split tile are added in a fixed order, so
  * results do not depend on scheduling.
