@@ -1,4 +1,4 @@
-"""Format variants (SURVEY f3; aissn.com 量化粒度 and 对称/非对称量化): group
+"""Format variants (aissn.com 量化粒度 and 对称/非对称量化): group
 sizes 32 and 256 beside 64 and 128, and the symmetric map (zero-point 0 as
 the signed code, stored as code + 8 with zero-point 8).
 
@@ -109,7 +109,7 @@ def test_scale_search_group_sizes(G):
                          [("auto", 16, 1000, 2048, awq.PATH_AUTO, False), ("auto", 40, 300, 1024, awq.PATH_AUTO, True)],
                          ids=lambda c: f"{c[0]}-M{c[1]}-{c[2]}x{c[3]}")
 def test_linear_paths_group_512(case, symmetric):
-    """G = 512 (f3's largest group): GEMV, GEMM and its stream-K form; the
+    """G = 512 (the largest group size): GEMV, GEMM and its stream-K form; the
     skinny kernel stops at G = 256, so batched decode shapes take the
     automatic choice (GEMV or GEMM)."""
     label, M, N, K, path, with_ws = case
