@@ -133,11 +133,13 @@ def test_stream_k_graph_replay_matches_eager():
 @pytest.mark.parametrize("M,N,K,G", [
     (8192, 8192, 4096, 128),     # 1024 tiles of 256 x 256: the one-block-per-CU geometry
     (12000, 17000, 1024, 64),    # ragged rows and columns on that geometry
+    (1280, 8320, 1024, 128),     # 165 tiles: one round, cheaper wide than as 330 narrow tiles
+    (1100, 8000, 2048, 64),      # the same with ragged rows and columns
 ])
 def test_wide_tiles_sampled(M, N, K, G):
-    """Shapes with at least three rounds of 256 x 256 tiles take the
-    512-thread geometry without a workspace: sampled output columns against
-    the oracle, and the same values as the stream-K form."""
+    """Shapes whose rounds of 256 x 256 tiles cost less than those of the
+    256 x 128 tile take the 512-thread geometry without a workspace:
+    sampled output columns against the oracle."""
     lay = synth.make_layer(N, K, M, seed=[121, M, N, K, G], w_std=0.02)
     say("wide tiles", M, N, K, G)
     x = dev(lay["x"])

@@ -911,15 +911,25 @@ void launch_cfg(const GemmArgs& args, void* workspace, hipStream_t stream) {
 constexpr int kDirectWgm = 1;
 bool direct_ok(const GemmArgs& args) { return args.group_size >= BKD && args.K * kBM * 2 < (int64_t{1} << 31); }
 
-// The wide tile when its tiles fill at least kWideRounds rounds of the GPU
-// (one block per CU), so the last partial round costs little, or when a
-// workspace lets stream-K spread a shape of under one round over every CU.
-constexpr int64_t kWideRounds = 3;
+// Narrow or wide tile, by the time of the rounds each takes (one-tile-per-
+// block launches). In units where a round of the wide tile (one 256 x 256
+// tile per CU) costs 20, a full round of the narrow tile (two 256 x 128 tiles
+// per CU, the same area) costs 22 and a last round of at most one narrow tile
+// per CU costs 12. Measured at N = 11008, K = 4096 (us, narrow against wide):
+// M = 1024: 114 / 101; 1280: 125 / 112; 2048: 191 / 210; 3072: 307 / 330;
+// 4096: 368 / 336. With a workspace, a shape of under two thirds of a round
+// takes the wide tile under stream-K.
+int64_t narrow_rounds_cost(int64_t tiles) {
+    const int64_t cu = cu_count(), slots = resident_slots(kNarrowTile);
+    const int64_t tail = tiles % slots;
+    return tiles / slots * 22 + (tail == 0 ? 0 : tail <= cu ? 12 : 22);
+}
+int64_t wide_rounds_cost(int64_t tiles) { return ceil_div(tiles, resident_slots(kWideTile)) * 20; }
 bool use_wide(const GemmArgs& args, bool have_workspace) {
     const int64_t t = tiles_of(kWideTile, args.M, args.N);
-    if (t >= kWideRounds * cu_count()) return true;
     const int64_t steps = args.K / BKD;
-    return have_workspace && use_stream_k(kWideTile, t, steps);
+    if (have_workspace && use_stream_k(kWideTile, t, steps)) return true;
+    return wide_rounds_cost(t) < narrow_rounds_cost(tiles_of(kNarrowTile, args.M, args.N));
 }
 
 // The loss form stays on the 256 x 128 tile: its epilogue streams an fp32
