@@ -245,6 +245,52 @@ class Bench:
                 "weight_copies": n_copies, "us_per_step": round(us, 2), "GB/s": round(gbs, 1),
                 "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "per_launch": per_launch}
 
+    def run_decode_model(self, n_layers=32):
+        """Every linear layer of a Llama-7B-shaped model at M = 1, layer after
+        layer, each layer with weights of its own (32 x 107.7 MB, far past
+        every cache), unfused (7 launches per layer) and with fused q/k/v and
+        gate/up (4 per layer). One token's pass is one graph; its time bounds
+        the decode rate the linear layers allow (attention, norms and
+        sampling not included)."""
+        torch, awq, args = self.torch, self.awq, self.args
+        out = {}
+        for label, layer in (("unfused", synth.LLAMA7B_LAYER), ("fused", synth.LLAMA7B_LAYER_FUSED)):
+            log(f"setup {n_layers}-layer decode pass ({label})")
+            layer = list(layer)
+            base = []
+            for (_, N, K) in layer:
+                lay = synth.decode_layer(N, K, 1)
+                qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), G)
+                base.append((qw, sc, zr, self.d(lay["x"]), N, K))
+            model = [[(qw.clone(), sc.clone(), zr.clone(), x,
+                       torch.empty((1, N), dtype=torch.float16, device=self.dev), N, K)
+                      for (qw, sc, zr, x, N, K) in base] for _ in range(n_layers)]
+            torch.cuda.synchronize()
+
+            def token(_):
+                for lin in model:
+                    for (qw, sc, zr, x, y, N, K) in lin:
+                        awq.awq_gemm(x, qw, sc, zr, G, out=y)
+
+            for i in range(max(args.warmup, 1)):
+                token(i)
+            g = self.capture(token, 1)
+            g.replay()
+            reps = 50
+            t = self.time(lambda _: [g.replay() for _r in range(reps)])
+            us = t / reps * 1e6
+            token_bytes = n_layers * sum(gemv_bytes(1, N, K) for (_, N, K) in layer)
+            out[label] = {"launches_per_token": n_layers * len(layer), "us_per_token": round(us, 1),
+                          "tokens_per_s": round(1e6 / us, 1), "bytes_per_token": token_bytes,
+                          "GB/s": round(token_bytes / (us * 1e-6) / 1e9, 1)}
+            log(f"{n_layers}-layer decode pass ({label}): {us:.1f} us/token, {1e6 / us:.0f} tok/s")
+            del model, base, g
+            torch.cuda.synchronize()
+        out["workload"] = f"llama7b_{n_layers}_layers_linears_m1_int4_g128"
+        out["note"] = ("linear layers only; the pages quote 58 tok/s for a GPTQ-4bit 7B model on an A10G "
+                       "(whole model, other hardware): context, not a target")
+        return out
+
     def run_skinny(self):
         """Batched decode rows (awq_gemm_ex with a workspace): M = 4 on the
         decode shapes (the GEMV), M = 16 on the decode shapes and M = 32 on
@@ -585,7 +631,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true")
-    ap.add_argument("--only", choices=["decode", "decode-fused", "gemv-roofline", "skinny", "gemm", "quantize",
+    ap.add_argument("--only", choices=["decode", "decode-fused", "decode-model", "gemv-roofline", "skinny", "gemm", "quantize",
                                        "search", "copy", "w8"],
                     help="run one section (for profiler runs); timings go to stderr")
     args = ap.parse_args()
@@ -604,6 +650,8 @@ def main():
                 b.run_gemv_shapes([ROOFLINE_SHAPE])
         elif args.only == "decode-fused":
             b.run_decode_fused()
+        elif args.only == "decode-model":
+            b.run_decode_model()
         elif args.only == "skinny":
             b.run_skinny()
         elif args.only == "gemm":
@@ -624,6 +672,7 @@ def main():
     roof = per_shape[f"{ROOFLINE_SHAPE[0]}x{ROOFLINE_SHAPE[1]}"]
     del b.copies
     fused = b.run_decode_fused()
+    model = b.run_decode_model()
     floor_us = b.run_launch_floor()
     skinny = b.run_skinny()
     groups = b.run_group_sizes()
@@ -663,6 +712,7 @@ def main():
         "hbm_copy_1GiB": copy,
         "gemv_per_shape": per_shape,
         "decode_fused": fused,
+        "decode_model": model,
         "skinny_batched_decode": skinny,
         "gemv_group_sizes": groups,
         "w8a16": w8,
