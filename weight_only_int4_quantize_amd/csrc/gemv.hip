@@ -7,8 +7,8 @@
 // loads, and to keep everything else on chip.
 //
 // Work split:
-//  * a block (4 wavefronts) owns 4 * RPW consecutive output rows; a wavefront
-//    owns RPW rows. Lane l handles the 32-weight chunks c = l + 64 j
+//  * a block of NW wavefronts (4, or 8 in the persistent form) owns NW * RPW
+//    consecutive output rows at a time; a wavefront owns RPW rows. Lane l handles the 32-weight chunks c = l + 64 j
 //    (j < CPL), one uint4 of qweight per row and chunk, so each wave-wide load
 //    is 1 KB of contiguous packed weights;
 //  * the wave first issues all RPW * CPL weight loads (plus the matching
@@ -197,8 +197,8 @@ __device__ inline float wave_sum_lane63(float v) {
 // DEPTH - 1 are still loading, and its slot is refilled with item t + DEPTH
 // right after. The loads are branch-free, so the compiler's wait counts track
 // the ring exactly. Finished rows go to LDS and are written out at the end.
-template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT>
-__global__ __launch_bounds__(256) void gemv_kernel(const half_t* __restrict__ x,
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT, int NW>
+__global__ __launch_bounds__(NW * 64) void gemv_kernel(const half_t* __restrict__ x,
                                                    const uint32_t* __restrict__ qweight,
                                                    const half_t* __restrict__ scales,
                                                    const half_t* __restrict__ zeros,
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const half_t* __restrict__ x,
     const int nchunk = K >> Chunk<BITS>::kShift;    // 32 (INT4) or 16 (W8) weights per chunk
     uint4* xp = smem;                               // [MT][nchunk][XV] x pairs
     float2* xo = reinterpret_cast<float2*>(smem + MT * nchunk * XV);  // [MT][nchunk] (off, xs)
-    float* yl = reinterpret_cast<float*>(xo + MT * nchunk);          // [4][max_sets][RPW][MT]
+    float* yl = reinterpret_cast<float*>(xo + MT * nchunk);          // [NW][max_sets][RPW][MT]
 
     // wave index as a scalar: the buffer descriptors built from it must be
     // wave-uniform
@@ -219,8 +219,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(const half_t* __restrict__ x,
 
     const int kbs = (nchunk + 64 * CPL - 1) / (64 * CPL);      // k-batches per row
     const int nsets = (N + RPW - 1) / RPW;                      // row sets
-    const int W = gridDim.x * 4;
-    const int wid = blockIdx.x * 4 + wave;
+    const int W = gridDim.x * NW;
+    const int wid = blockIdx.x * NW + wave;
     const int my_sets = wid < nsets ? (nsets - 1 - wid) / W + 1 : 0;
     const int n_items = my_sets * kbs;
 
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const half_t* __restrict__ x,
     uint4 xr[XPRE][MT][XV];
 #pragma unroll
     for (int p = 0; p < XPRE; ++p)
-        if (c0 + p * 256 < nchunk) load_x(c0 + p * 256, xr[p]);
+        if (c0 + p * NW * 64 < nchunk) load_x(c0 + p * NW * 64, xr[p]);
 
     WeightBatch<RPW, CPL> ring[DEPTH];
     int l_item = 0, l_set = 0, l_kb = 0;            // load cursor
@@ -291,8 +291,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(const half_t* __restrict__ x,
     // 2. stage x in LDS while the weights are in flight
 #pragma unroll
     for (int p = 0; p < XPRE; ++p)
-        if (c0 + p * 256 < nchunk) store_x(c0 + p * 256, xr[p]);
-    for (int c = c0 + XPRE * 256; c < nchunk; c += 256) {
+        if (c0 + p * NW * 64 < nchunk) store_x(c0 + p * NW * 64, xr[p]);
+    for (int c = c0 + XPRE * NW * 64; c < nchunk; c += NW * 64) {
         load_x(c, xr[0]);
         store_x(c, xr[0]);
     }
@@ -340,13 +340,13 @@ __global__ __launch_bounds__(256) void gemv_kernel(const half_t* __restrict__ x,
 
     // 4. write the block's rows
     __syncthreads();
-    const int slots = 4 * max_sets * RPW;
-    for (int sl = threadIdx.x; sl < slots; sl += 256) {
+    const int slots = NW * max_sets * RPW;
+    for (int sl = threadIdx.x; sl < slots; sl += NW * 64) {
         const int w = sl / (max_sets * RPW);
         const int rem = sl - w * max_sets * RPW;
         const int cs = rem / RPW;
         const int i = rem - cs * RPW;
-        const int wg = blockIdx.x * 4 + w;
+        const int wg = blockIdx.x * NW + w;
         const int sets_w = wg < nsets ? (nsets - 1 - wg) / W + 1 : 0;
         const int row = (wg + cs * W) * RPW + i;
         if (cs < sets_w && row < N) {
@@ -376,25 +376,25 @@ size_t gemv_lds_bytes(int64_t M, int64_t K, int bits) {
                      : static_cast<size_t>(M) * static_cast<size_t>(K / 16) * 40;
 }
 
-template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT = false>
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT = false, int NW = 4>
 awq_status launch_t(const half_t* x, const uint32_t* qweight, const half_t* scales,
                     const half_t* zeros, int64_t N, int64_t K, int log2g, half_t* y,
                     int64_t blocks, hipStream_t stream) {
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, max_shared_bytes()) != hipSuccess)
             return AWQ_ERR_HIP;
         attr_set = true;
     }
     const int64_t sets = ceil_div(N, RPW);
-    blocks = std::max<int64_t>(1, std::min<int64_t>(blocks, ceil_div(sets, 4)));
-    const int64_t max_sets = ceil_div(sets, blocks * 4);
+    blocks = std::max<int64_t>(1, std::min<int64_t>(blocks, ceil_div(sets, NW)));
+    const int64_t max_sets = ceil_div(sets, blocks * NW);
     const int64_t nchunk = K >> Chunk<BITS>::kShift;
     if (ONESHOT && max_sets * ceil_div(nchunk, 64 * CPL) > DEPTH) return AWQ_ERR_SHAPE;   // launch-shape bug
-    const size_t lds = gemv_lds_bytes(MT, K, BITS) + (ONESHOT ? 0 : static_cast<size_t>(4 * max_sets * RPW * MT) * sizeof(float));
+    const size_t lds = gemv_lds_bytes(MT, K, BITS) + (ONESHOT ? 0 : static_cast<size_t>(NW * max_sets * RPW * MT) * sizeof(float));
     if (lds > static_cast<size_t>(max_shared_bytes())) return AWQ_ERR_SHAPE;
-    hipLaunchKernelGGL((gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT>), dim3(static_cast<unsigned>(blocks)), dim3(256), lds,
+    hipLaunchKernelGGL((gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), lds,
                        stream, x, qweight, scales, zeros, y, static_cast<int>(N), static_cast<int>(K),
                        log2g, static_cast<int>(max_sets));
     return last_launch_status();
@@ -407,11 +407,13 @@ awq_status launch_t(const half_t* x, const uint32_t* qweight, const half_t* scal
 //    more activation rows, every weight costs one LDS read of x per row, so
 //    4 weight rows per wave share each read (2 in the streaming form):
 //    M = 4 on 11008 x 4096 takes 12.5 us against 14.4 us with 2.
-//  * Longer rows: a persistent grid of one block per CU, so that staging
-//    x (2 bytes per input channel per block) stays small against the
-//    weights, each wave streaming its rows through a 4-deep ring, 2 rows at
-//    a time for rows of more than 3 items. Against 2 blocks per CU and 1 row
-//    at a time: 4096 x 11008 9.0 -> 8.2 us, 8192 x 28672 29 -> 27 us.
+//  * Longer rows: a persistent grid of one 8-wave block per CU, so that
+//    staging x (2 bytes per input channel per block) stays small against the
+//    weights while two waves per SIMD hide each other's unpack latency, each
+//    wave streaming its rows through a 2-deep ring, 2 rows at a time for rows
+//    of more than 3 items. Against 4 waves with a 4-deep ring (the same bytes
+//    in flight): 4096 x 11008 7.85 -> 7.13 us, 8192 x 28672 25.4 -> 24.1 us;
+//    8 waves with a 4-deep ring or 16 waves with a 2-deep one are slower.
 template <int BITS, int MT>
 awq_status launch_m(const half_t* x, const uint32_t* qweight, const half_t* scales,
                     const half_t* zeros, int64_t N, int64_t K, int log2g, half_t* y,
@@ -431,8 +433,9 @@ awq_status launch_m(const half_t* x, const uint32_t* qweight, const half_t* scal
     const int64_t x_lds = static_cast<int64_t>(gemv_lds_bytes(MT, K, BITS));
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kGemvBlocksPerCu, max_shared_bytes() / (x_lds + 2048)));
     if (MT >= 2 || kbs > 3)
-        return launch_t<BITS, MT, 2, 2, 4>(x, qweight, scales, zeros, N, K, log2g, y, per_cu * cu_count(), stream);
-    return launch_t<BITS, MT, 1, 2, 4>(x, qweight, scales, zeros, N, K, log2g, y, per_cu * cu_count(), stream);
+        return launch_t<BITS, MT, 2, 2, 2, false, 8>(x, qweight, scales, zeros, N, K, log2g, y, per_cu * cu_count(),
+                                                     stream);
+    return launch_t<BITS, MT, 1, 2, 2, false, 8>(x, qweight, scales, zeros, N, K, log2g, y, per_cu * cu_count(), stream);
 }
 
 }  // namespace
