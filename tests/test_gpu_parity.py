@@ -235,6 +235,7 @@ def test_sweep_linear_full_size_sampled(N, K, G, M):
 @pytest.mark.parametrize("M,N,K,G", [
     (1, 1, 64, 64), (3, 17, 128, 64), (8, 130, 256, 128), (9, 64, 64, 64),
     (127, 129, 192, 64), (300, 200, 384, 128), (257, 255, 640, 64),
+    (1, 1001, 6144, 64), (1, 3001, 8192, 128),    # rows of two items: the persistent GEMV at M = 1
 ])
 def test_linear_ragged_both_paths(M, N, K, G):
     lay = synth.make_layer(N, K, M, seed=[104, M, N, K, G], w_std=0.02)
