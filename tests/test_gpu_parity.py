@@ -253,6 +253,8 @@ def test_linear_ragged_both_paths(M, N, K, G):
     (8, 4111, 512, 32),
     (2, 1001, 8448, 128),     # streaming form, 2 weight rows per wave, odd N
     (4, 4097, 11008, 128),
+    (4, 1003, 6144, 64),      # rows of two items: the persistent form
+    (7, 2049, 8192, 128),
 ])
 def test_gemv_multirow_ragged(M, N, K, G):
     """Several activation rows on the GEMV: the launch shapes that share each

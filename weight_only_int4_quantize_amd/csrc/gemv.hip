@@ -401,15 +401,16 @@ awq_status launch_t(const half_t* x, const uint32_t* qweight, const half_t* scal
 }
 
 // Launch shape. Items are RPW rows x 2 chunks (64 packed words) per lane.
-//  * Rows of one item (4096 weights), or of two for W8 or M >= 2: one row set per
+//  * Rows of one item (4096 weights), or of two for W8: one row set per
 //    wavefront and all of it in flight from the start; 2 rows per wave share
 //    each staged x read, as long as that leaves >= 512 blocks. With two or
 //    more activation rows, every weight costs one LDS read of x per row, so
 //    4 weight rows per wave share each read (2 in the streaming form):
 //    M = 4 on 11008 x 4096 takes 12.5 us against 14.4 us with 2.
-//  * Longer rows (and INT4 rows of 2 items at M = 1: 13824 x 5120 11.5 ->
-//    11.0 us, 11008 x 8192 11.7 -> 10.8 us; W8 rows of 2 items are faster
-//    one-shot): a persistent grid of one 8-wave block per CU, so that
+//  * Longer rows, and INT4 rows of 2 items (13824 x 5120: M = 1 11.5 ->
+//    11.0 us, M = 4 32.9 -> 21.8 us; 11008 x 8192, M = 1: 11.7 -> 10.8 us;
+//    W8 rows of 2 items are faster one-shot): a persistent grid of one
+//    8-wave block per CU, so that
 //    staging x (2 bytes per input channel per block) stays small against the
 //    weights while two waves per SIMD hide each other's unpack latency, each
 //    wave streaming its rows through a 2-deep ring, 2 rows at a time for rows
@@ -430,7 +431,7 @@ awq_status launch_m(const half_t* x, const uint32_t* qweight, const half_t* scal
                                                      stream);
         return launch_t<BITS, MT, 1, 2, 1, true>(x, qweight, scales, zeros, N, K, log2g, y, ceil_div(N, 4), stream);
     }
-    if (kbs == 2 && (BITS == 8 || MT > 1))
+    if (kbs == 2 && BITS == 8)
         return launch_t<BITS, MT, 1, 2, 2, true>(x, qweight, scales, zeros, N, K, log2g, y, ceil_div(N, 4), stream);
     const int64_t x_lds = static_cast<int64_t>(gemv_lds_bytes(MT, K, BITS));
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kGemvBlocksPerCu, max_shared_bytes() / (x_lds + 2048)));
