@@ -31,6 +31,8 @@ from .awq_oracle import (  # noqa: F401
     channel_scales,
     searched_weight,
     search_loss_direct,
+    scaled_activations_f16,
+    search_loss_f16_activations,
     gram,
     search_loss_gram,
     scale_search,

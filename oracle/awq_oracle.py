@@ -312,6 +312,41 @@ def search_loss_direct(w, x, s32, group_size: int) -> float:
     return float(np.sum(d * d))
 
 
+def scaled_activations_f16(x, s32) -> np.ndarray:
+    """fp16(X / s): the scaled activations as the W4A16 layer takes them.
+
+    The search runs Q(W diag(s)) (X / s)^T on the W4A16 product, whose
+    activations are fp16 (the "A16" of the layer, [P1 §1.3]), so X / s enters
+    it rounded to fp16. Reading: one IEEE float32 division x / s per element
+    (x is fp16, s float32), then round-to-nearest-even to fp16. Returned as
+    float64 (exact)."""
+    x32 = np.asarray(x).astype(np.float32)
+    s = np.asarray(s32, dtype=np.float32).reshape(1, -1)
+    return (x32 / s).astype(np.float16).astype(np.float64)
+
+
+def search_loss_f16_activations(w, x, s32, group_size: int, clip_fraction: float = 0.0,
+                                symmetric: bool = False) -> float:
+    """L = || Q(W diag(s)) fp16(X / s)^T - W X^T ||_F^2 in float64, direct
+    form: the scale search's loss with the scaled activations rounded to the
+    fp16 the W4A16 layer takes (see scaled_activations_f16). It differs from
+    search_loss_direct only by that rounding; with s a power of two per
+    channel (or s = 1) the rounding is exact and the two agree.
+    Q is the plain quantizer, or the clipped one when clip_fraction > 0 or
+    symmetric is set."""
+    w = np.asarray(w)
+    K = w.shape[1]
+    if clip_fraction == 0.0 and not symmetric:
+        qw, sc, zr = quantize(w, group_size, channel_scale=s32)
+    else:
+        qw, sc, zr = quantize_clipped(w, group_size, clip_fraction, channel_scale=s32, symmetric=symmetric)
+    w_q = dequantize(qw, sc, zr, group_size, K)
+    y = np.asarray(x).astype(np.float64) @ w.astype(np.float64).T
+    y_hat = scaled_activations_f16(x, s32) @ w_q.T
+    d = y_hat - y
+    return float(np.sum(d * d))
+
+
 def gram(x) -> np.ndarray:
     """G = X^T X in float64 [K, K]."""
     x64 = np.asarray(x).astype(np.float64)
@@ -325,21 +360,25 @@ def search_loss_gram(w, g, s32, group_size: int) -> float:
     return float(np.sum((d @ g) * d))
 
 
-def scale_search(w, x, group_size: int, alphas=None, use_gram: bool = True):
+def scale_search(w, x, group_size: int, alphas=None, use_gram: bool = True, f16_activations: bool = False):
     """AWQ's per-input-channel scale search over an alpha grid.
 
     For every alpha: s = mean|x|^alpha, quantize W diag(s), and measure the
     squared output error against the unquantized layer. Returns
     (losses float64 [n_alpha], best index, best scales float32 [K]).
-    The best index is the first minimum (ties go to the smallest alpha)."""
+    The best index is the first minimum (ties go to the smallest alpha).
+    f16_activations=True measures each loss with X / s rounded to fp16
+    (search_loss_f16_activations, direct form) instead of exactly."""
     if alphas is None:
         alphas = alpha_grid(20)
     m = activation_absmean(x)
-    g = gram(x) if use_gram else None
+    g = gram(x) if (use_gram and not f16_activations) else None
     losses = np.empty(len(alphas), dtype=np.float64)
     for i, a in enumerate(alphas):
         s32 = channel_scales(m, a)
-        if use_gram:
+        if f16_activations:
+            losses[i] = search_loss_f16_activations(w, x, s32, group_size)
+        elif use_gram:
             losses[i] = search_loss_gram(w, g, s32, group_size)
         else:
             losses[i] = search_loss_direct(w, x, s32, group_size)
@@ -359,16 +398,23 @@ def clipped_weight(w, group_size: int, clip_fraction: float, s32=None, symmetric
     return w_hat
 
 
-def clip_search(w, x, group_size: int, fractions, s32=None, use_gram: bool = True, symmetric: bool = False):
+def clip_search(w, x, group_size: int, fractions, s32=None, use_gram: bool = True, symmetric: bool = False,
+                f16_activations: bool = False):
     """Search of the clip fraction p of [P5 §1.5] over a grid, by the same
     output loss as the scale search: for each p,
       L(p) = || Q_p(W diag(s)) (X / s)^T - W X^T ||_F^2
     (s = 1 without channel scales; Q_p asymmetric or symmetric). Returns
-    (losses float64 [n], first index of the minimum)."""
-    g = gram(x) if use_gram else None
+    (losses float64 [n], first index of the minimum). f16_activations=True
+    (with s32) rounds X / s to fp16 as the W4A16 layer takes it, in the
+    direct form."""
+    g = gram(x) if (use_gram and not f16_activations) else None
     w64 = np.asarray(w).astype(np.float64)
     losses = np.empty(len(fractions), dtype=np.float64)
     for i, p in enumerate(fractions):
+        if f16_activations:
+            ones = np.ones(w64.shape[1], np.float32) if s32 is None else s32
+            losses[i] = search_loss_f16_activations(w, x, ones, group_size, p, symmetric)
+            continue
         d = clipped_weight(w, group_size, p, s32, symmetric) - w64
         if use_gram:
             losses[i] = float(np.sum((d @ g) * d))

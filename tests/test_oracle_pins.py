@@ -361,6 +361,60 @@ def test_gram_identity():
         assert abs(ld - lg) <= 1e-10 * ld
 
 
+def test_f16_activation_loss_equals_exact_when_rounding_is_exact():
+    """X / s rounded to fp16 is exact for s = 1 (alpha = 0) and for s a
+    power of two per channel (no underflow at these magnitudes), so the
+    fp16-activation loss then equals the exact direct loss (up to the fp64
+    summation order of the two products, ~1e-11 relative here)."""
+    lay = synth.make_layer(96, 256, 80, seed=[27], w_std=0.02)
+    w, x = lay["w"], lay["x"]
+    ones = np.ones(256, np.float32)
+    la = oracle.search_loss_f16_activations(w, x, ones, 64)
+    assert abs(la - oracle.search_loss_direct(w, x, ones, 64)) <= 1e-9 * la
+    p2 = (2.0 ** np.random.default_rng(28).integers(-3, 4, 256)).astype(np.float32)
+    lp = oracle.search_loss_f16_activations(w, x, p2, 64)
+    assert abs(lp - oracle.search_loss_direct(w, x, p2, 64)) <= 1e-9 * lp
+    # a generic s rounds: the two differ, by far less than the loss
+    s = oracle.channel_scales(oracle.activation_absmean(x), 0.5)
+    lg, ld = oracle.search_loss_f16_activations(w, x, s, 64), oracle.search_loss_direct(w, x, s, 64)
+    assert lg != ld and abs(lg - ld) <= 1e-3 * ld
+
+
+def test_f16_activation_loss_matches_brute_force():
+    """Element-by-element loop on a tiny case: fp16(float32(x) / s) per
+    activation, the dequantized weight per element, squared error summed."""
+    lay = synth.make_layer(5, 64, 3, seed=[29], w_std=0.02)
+    w, x = lay["w"], lay["x"]
+    s = oracle.channel_scales(oracle.activation_absmean(x), 0.7)
+    qw, sc, zr = oracle.quantize(w, 32, channel_scale=s)
+    codes = oracle.unpack_codes(qw, 64)
+    total = 0.0
+    for t in range(3):
+        for n in range(5):
+            yh = 0.0
+            y = 0.0
+            for k in range(64):
+                xs = float(np.float16(np.float32(x[t, k]) / np.float32(s[k])))
+                wq = (float(codes[n, k]) - float(zr[n, k // 32])) * float(sc[n, k // 32])
+                yh += xs * wq
+                y += float(x[t, k]) * float(w[n, k])
+            total += (yh - y) ** 2
+    got = oracle.search_loss_f16_activations(w, x, s, 32)
+    assert abs(got - total) <= 1e-11 * total
+
+
+def test_f16_activation_search_matches_exact_choice():
+    """On the small search cases the fp16 rounding of X / s moves the losses
+    by under 1e-4 relative, far below the gap between the best two alphas,
+    so both forms pick the same alpha."""
+    lay = synth.make_layer(128, 512, 256, seed=[8], w_std=0.02, w_mult=1.0)
+    w, x = lay["w"], lay["x"]
+    le, be, _ = oracle.scale_search(w, x, 128)
+    lf, bf, _ = oracle.scale_search(w, x, 128, f16_activations=True)
+    assert be == bf
+    assert np.all(np.abs(lf - le) <= 1e-4 * le)
+
+
 def test_loss_invariant_to_power_of_two_factor_on_s():
     """Scaling every s by 2 changes no code, only the scales (exactly), so the
     loss does not depend on a global factor and s needs no normalisation."""
