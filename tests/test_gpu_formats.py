@@ -30,11 +30,10 @@ def gpu_quantize(w16, G, cs=None, symmetric=False):
     return host(qw).view(np.uint32), host(sc), host(zr)
 
 
-@pytest.mark.parametrize("G", [32, 256, 512])
-@pytest.mark.parametrize("N,K", [(11008, 4096), (4096, 11008), (77, 1536)])
+@pytest.mark.parametrize("N,K,G", [(N, K, G) for G in (32, 256, 512)
+                                   for (N, K) in ((11008, 4096), (4096, 11008), (77, 1536)) if K % G == 0])
 def test_quantize_group_sizes_bit_exact(N, K, G):
-    if K % G:
-        pytest.skip("K is not a multiple of G")
+    """Every shape whose K the group size divides (11008 = 43 * 256)."""
     lay = synth.decode_layer(N, K, 0, G)
     say("quantize G", G, N, K)
     assert_quant_equal(gpu_quantize(lay["w"], G), oracle.quantize(lay["w"], G))
@@ -99,9 +98,10 @@ def test_scale_search_group_sizes(G):
     lay = synth.make_layer(256, 512, 512, seed=[154, G], w_std=0.02, w_mult=1.0)
     w, x = lay["w"], lay["x"]
     losses_o, best_o, s_o = oracle.scale_search(w, x, G)
+    losses_f, _, _ = oracle.scale_search(w, x, G, f16_activations=True)
     losses, best, s = awq.awq_scale_search(dev(w), dev(x), G)
     say("search G", G, "gpu", best, "oracle", best_o)
-    check_search(losses, best, host(s), losses_o, best_o, s_o)
+    check_search(losses, best, host(s), losses_o, best_o, s_o, losses_f)
 
 
 @pytest.mark.parametrize("symmetric", [False, True])

@@ -4,7 +4,8 @@ and "混合精度设计"; xxmr.cn §2.2), through the C ABI against the oracle.
 Selection and the stored form: bit-exact (indices, packed codes, scales,
 zero-points, fp16 side columns). Mixed linear layer: relative Frobenius
 error <= 1e-3 and |y - y_ref| <= 1e-2 * (|y_ref| + 1) per element on every
-path. Losses: within 2e-3 relative of the oracle, the same channels.
+path. Losses: within 1e-5 relative of the oracle (no activation is rescaled
+here, so only fp32 accumulation separates them), the same channels.
 """
 
 import base64
@@ -23,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 import weight_only_int4_quantize_amd as awq  # noqa: E402
 
-from test_gpu_parity import assert_linear_close, dev, host, say  # noqa: E402
+from test_gpu_parity import LOSS_RTOL_F16, assert_linear_close, dev, host, say  # noqa: E402
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -120,8 +121,8 @@ def test_salient_loss_matches_oracle(G, symmetric):
     lr_o = oracle.salient_loss(w, x, G, [], symmetric=symmetric)
     ls_o = oracle.salient_loss(w, x, G, idx_o, symmetric=symmetric)
     say("rtn", lr, lr_o, "salient", ls, ls_o)
-    assert abs(lr - lr_o) <= 2e-3 * lr_o
-    assert abs(ls - ls_o) <= 2e-3 * ls_o
+    assert abs(lr - lr_o) <= LOSS_RTOL_F16 * lr_o
+    assert abs(ls - ls_o) <= LOSS_RTOL_F16 * ls_o
     assert ls < lr
 
 
@@ -149,8 +150,8 @@ def test_salient_loss_full_size():
     idx_o = np.frombuffer(base64.b64decode(g["idx_i64_b64"]), dtype="<i8")
     assert np.array_equal(host(idx).astype(np.int64), idx_o)
     say("rtn", lr, g["loss_rtn"], "salient", ls, g["loss_salient"])
-    assert abs(lr - g["loss_rtn"]) <= 2e-3 * g["loss_rtn"]
-    assert abs(ls - g["loss_salient"]) <= 2e-3 * g["loss_salient"]
+    assert abs(lr - g["loss_rtn"]) <= LOSS_RTOL_F16 * g["loss_rtn"]
+    assert abs(ls - g["loss_salient"]) <= LOSS_RTOL_F16 * g["loss_salient"]
 
 
 def test_salient_loss_few_tokens():
@@ -161,4 +162,4 @@ def test_salient_loss_few_tokens():
     idx_o = oracle.salient_channels(oracle.activation_absmean(x), 10)
     assert np.array_equal(host(idx).astype(np.int64), idx_o)
     ls_o = oracle.salient_loss(w, x, 128, idx_o, use_gram=False)
-    assert abs(ls - ls_o) <= 2e-3 * ls_o
+    assert abs(ls - ls_o) <= LOSS_RTOL_F16 * ls_o
