@@ -42,18 +42,40 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every HIP source into one shared library; returns its path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), *sources(), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    if verbose and res.stderr.strip():
-        sys.stderr.write(res.stderr)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+
+
+def _finish(proc, verbose) -> None:
+    out, err = proc.communicate()
+    if proc.returncode != 0:
+        sys.stderr.write(out + err)
+        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
+    if verbose and err.strip():
+        sys.stderr.write(err)
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every HIP source (one hipcc process per translation unit, in
+    parallel) and link them into one shared library; returns its path."""
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"] + list(extra_flags or [])
+    objs, procs = [], []
+    jobs = max(1, min(len(sources()), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    for src in sources():
+        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        procs.append(_run([hipcc(), *compile_flags, "-c", src, "-o", obj], verbose))
+        if len(procs) >= jobs:
+            _finish(procs.pop(0), verbose)
+    for p in procs:
+        _finish(p, verbose)
+    tmp = LIB_PATH + ".tmp"
+    link = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _finish(link, verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
