@@ -51,7 +51,7 @@ typedef enum {
     AWQ_ERR_NULL = 1,      /* a required pointer is NULL */
     AWQ_ERR_SHAPE = 2,     /* negative size, K not a multiple of G, ... */
     AWQ_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned */
-    AWQ_ERR_CONFIG = 4,    /* group_size not 64/128, bad alpha grid, ... */
+    AWQ_ERR_CONFIG = 4,    /* unsupported group_size, path, mode, grid, ... */
     AWQ_ERR_WORKSPACE = 5, /* workspace smaller than the size query says */
     AWQ_ERR_HIP = 6        /* the HIP runtime reported an error */
 } awq_status;
@@ -137,8 +137,10 @@ awq_status awq_quantize_ex(const void* w_f16, const float* channel_scale,
  *   y_f16        device, fp16 [M, N] (output; must not alias the inputs)
  * M == 0 or N == 0 returns AWQ_OK without work. M <= 4 (decode) runs a
  * bandwidth-bound GEMV, 4 < M <= 64 (a batch of decode tokens) a skinny
- * MFMA kernel that streams the packed weights straight into registers, and
- * larger M the MFMA GEMM. Results do not depend on run-to-run scheduling.
+ * MFMA kernel that streams the packed weights straight into registers (so
+ * does M <= 4 when the GEMV's staged x would not fit the LDS, e.g. M = 4 at
+ * K = 28672), and larger M the MFMA GEMM. Results do not depend on
+ * run-to-run scheduling.
  */
 awq_status awq_gemm(const void* x_f16, const uint32_t* qweight,
                     const void* scales_f16, const void* zeros_f16,
@@ -152,9 +154,9 @@ awq_status awq_gemm(const void* x_f16, const uint32_t* qweight,
  * packed matrix under 4 GiB; without a workspace each block walks all of K,
  * staging it in LDS-sized phases).
  * Any other path, or a path whose requirement fails, returns AWQ_ERR_CONFIG.
- * The automatic choice takes the GEMV for M <= 4; the skinny kernel for
- * M <= 64, except for M <= 8 where it would have to stage K in phases and
- * the GEMV can run (then the GEMV); then the GEMM.
+ * The automatic choice takes the GEMV for M <= 4 where it can run; the
+ * skinny kernel for M <= 64, except for M <= 8 where it would have to stage
+ * K in phases and the GEMV can run (then the GEMV); then the GEMM.
  */
 awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight,
                          const void* scales_f16, const void* zeros_f16,
@@ -226,7 +228,9 @@ awq_status awq_activation_absmean(const void* x_f16, int64_t T, int64_t K,
  *   x_f16         device, fp16 [T, K] (calibration activations)
  *   N, K, T       N > 0, T > 0, K > 0, K % group_size == 0
  *   group_size    32, 64, 128, 256 or 512
- *   alphas        host, float64 [n_alpha], every alpha finite (1 <= n_alpha <= 64)
+ *   alphas        host, float64 [n_alpha], every alpha finite (1 <= n_alpha <= 64);
+ *                 NULL takes the grid alpha_i = i / n_alpha (n_alpha = 20:
+ *                 0, 0.05, ..., 0.95)
  *   workspace     device, >= awq_scale_search_workspace_bytes(N, K, T, G, n_alpha)
  *   losses        host, float64 [n_alpha] (output)
  *   best_index    host, int (output)
@@ -359,15 +363,24 @@ awq_status awq_salient_apply(const void* x_f16, const int* idx,
  *                  K % group_size == 0
  *   group_size     32, 64, 128, 256 or 512
  *   mode           AWQ_QUANT_ASYMMETRIC or AWQ_QUANT_SYMMETRIC
- *   n_salient      0 <= n_salient <= K
+ *   n_salient      0 <= n_salient <= K, or negative for the pages' 1 %:
+ *                  awq_salient_count(K) channels
  *   workspace, workspace_bytes  device scratch of at least
  *                  awq_salient_loss_workspace_bytes(N, K, T, group_size,
- *                  n_salient) bytes, 16-byte aligned
+ *                  n_salient) bytes (the same negative n_salient allowed),
+ *                  16-byte aligned
  *   loss_rtn, loss_salient  host, double (outputs)
  *   idx_out        device, int32 [n_salient] (output: the chosen channels)
  *                  or NULL
  * Synchronises `stream` once, to read the losses back.
  */
+/*
+ * awq_salient_count - the number of salient input channels the pages keep,
+ * about 1 % ("AWQ 模型量化技术", 技术实现 1): round(K / 100), ties to even
+ * (41 of 4096). K <= 0 gives 0.
+ */
+int64_t awq_salient_count(int64_t K);
+
 size_t awq_salient_loss_workspace_bytes(int64_t N, int64_t K, int64_t T,
                                          int group_size, int n_salient);
 awq_status awq_salient_loss(const void* w_f16, const void* x_f16, int64_t N,

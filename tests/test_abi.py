@@ -173,11 +173,25 @@ def test_scale_search_checks(L):
     assert s(FAKE, FAKE, 0, 512, 1024, 128, a, 20, FAKE, need, lp, bp, FAKE, None) == SHAPE
     assert s(FAKE, FAKE, 256, 512, 0, 128, a, 20, FAKE, need, lp, bp, FAKE, None) == SHAPE
     assert s(FAKE, None, 256, 512, 1024, 128, a, 20, FAKE, need, lp, bp, FAKE, None) == NULL
-    assert s(FAKE, FAKE, 256, 512, 1024, 128, None, 20, FAKE, need, lp, bp, FAKE, None) == NULL
+    # no grid (alphas NULL) is accepted: the call then fails only on the short workspace
+    assert s(FAKE, FAKE, 256, 512, 1024, 128, None, 20, FAKE, need - 256, lp, bp, FAKE, None) == WORKSPACE
+    assert s(FAKE, FAKE, 256, 512, 1024, 128, None, 0, FAKE, need, lp, bp, FAKE, None) == CONFIG
     bad = np.array([0.0, np.nan])
     assert s(FAKE, FAKE, 256, 512, 1024, 128, bad.ctypes.data_as(ctypes.c_void_p), 2, FAKE, need, lp, bp,
              FAKE, None) == CONFIG
     assert s(FAKE_ODD, FAKE, 256, 512, 1024, 128, a, 20, FAKE, need, lp, bp, FAKE, None) == ALIGN
+
+
+def test_salient_count_is_the_oracles(L):
+    """The library's default salient-channel count (round(K / 100), ties to
+    even) equals the oracle's for every width of the workloads and at ties."""
+    import oracle
+    L.awq_salient_count.restype = ctypes.c_int64
+    L.awq_salient_count.argtypes = [ctypes.c_int64]
+    for K in (1, 50, 150, 250, 512, 4096, 5120, 11008, 13824, 28672):
+        assert L.awq_salient_count(K) == oracle.salient_count(K), K
+    assert L.awq_salient_count(0) == 0
+    assert L.awq_salient_count(4096) == 41
 
 
 def test_binding_refuses_cpu_tensors():

@@ -91,6 +91,8 @@ def load() -> ctypes.CDLL:
     L.awq_quantize_salient.argtypes = [c_vp, c_i64, c_i64, c_int, c_int, c_vp, c_int, c_vp, c_vp, c_vp, c_vp, c_vp]
     L.awq_salient_apply.restype = c_int
     L.awq_salient_apply.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_vp]
+    L.awq_salient_count.restype = c_i64
+    L.awq_salient_count.argtypes = [c_i64]
     L.awq_salient_loss_workspace_bytes.restype = c_sz
     L.awq_salient_loss_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_int, c_int]
     L.awq_salient_loss.restype = c_int
@@ -144,6 +146,19 @@ def _need_gpu(name: str, t, dtype=None) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _need_out(qweight, scales, zeros, q_shape, sz_shape, device) -> None:
+    """Caller-given quantize outputs: int32 qweight and fp16 scales / zeros of
+    exactly the shapes the call writes, contiguous, on the input's device."""
+    torch = _torch()
+    for name, t, dtype, shape in (("qweight", qweight, torch.int32, q_shape), ("scales", scales, torch.float16, sz_shape),
+                                  ("zeros", zeros, torch.float16, sz_shape)):
+        _need_gpu(name, t, dtype)
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+        if t.device != device:
+            raise ValueError(f"{name} must be on {device}")
+
+
 def awq_quantize(w, group_size: int = 128, channel_scale=None, out=None, symmetric: bool = False,
                  clip_fraction: float = 0.0):
     """Group-wise INT4 quantization of w[N, K] (fp16), asymmetric by default
@@ -161,14 +176,15 @@ def awq_quantize(w, group_size: int = 128, channel_scale=None, out=None, symmetr
         _need_gpu("channel_scale", channel_scale, torch.float32)
         if channel_scale.numel() != K:
             raise ValueError("channel_scale must have K elements")
+    ng = K // group_size if group_size > 0 else 0
     if out is None:
         dev = w.device
         qweight = torch.empty((N, max(K // 8, 0)), dtype=torch.int32, device=dev)
-        ng = K // group_size if group_size > 0 else 0
         scales = torch.empty((N, ng), dtype=torch.float16, device=dev)
         zeros = torch.empty((N, ng), dtype=torch.float16, device=dev)
     else:
         qweight, scales, zeros = out
+        _need_out(qweight, scales, zeros, (N, K // 8), (N, ng), w.device)
     if symmetric or clip_fraction != 0.0:
         mode = QUANT_SYMMETRIC if symmetric else QUANT_ASYMMETRIC
         st = load().awq_quantize_ex(_ptr(w), _ptr(channel_scale), N, K, group_size, mode, float(clip_fraction),
@@ -249,7 +265,7 @@ def scale_search_workspace_bytes(N: int, K: int, T: int, group_size: int = 128, 
     return int(load().awq_scale_search_workspace_bytes(N, K, T, group_size, n_alpha))
 
 
-def awq_scale_search(w, x, group_size: int = 128, alphas=None, workspace=None):
+def awq_scale_search(w, x, group_size: int = 128, alphas=None, workspace=None, n_alpha: int = 20):
     """AWQ scale search over an alpha grid.
 
     Returns (losses: numpy float64 [n_alpha], best_index: int,
@@ -262,10 +278,10 @@ def awq_scale_search(w, x, group_size: int = 128, alphas=None, workspace=None):
     T = x.shape[0]
     if x.shape[1] != K:
         raise ValueError("x must be [T, K] with the K of w")
-    if alphas is None:
-        alphas = np.arange(20, dtype=np.float64) / 20.0
-    alphas = np.ascontiguousarray(alphas, dtype=np.float64)
-    n_alpha = int(alphas.size)
+    # no grid given: the library's default grid of n_alpha points
+    if alphas is not None:
+        alphas = np.ascontiguousarray(alphas, dtype=np.float64)
+    n_alpha = int(alphas.size) if alphas is not None else int(n_alpha)
     L = load()
     nbytes = L.awq_scale_search_workspace_bytes(N, K, T, group_size, n_alpha)
     if workspace is None:
@@ -274,7 +290,7 @@ def awq_scale_search(w, x, group_size: int = 128, alphas=None, workspace=None):
     best = ctypes.c_int(-1)
     best_scales = torch.empty(K, dtype=torch.float32, device=w.device)
     st = L.awq_scale_search(_ptr(w), _ptr(x), N, K, T, group_size,
-                            alphas.ctypes.data_as(ctypes.c_void_p), n_alpha,
+                            None if alphas is None else alphas.ctypes.data_as(ctypes.c_void_p), n_alpha,
                             _ptr(workspace), workspace.numel(),
                             losses.ctypes.data_as(ctypes.c_void_p), ctypes.addressof(best),
                             _ptr(best_scales), _stream(w.device))
@@ -290,10 +306,12 @@ def awq_clip_search(w, x, fractions, group_size: int = 128, channel_scale=None, 
     torch = _torch()
     _need_gpu("w", w, torch.float16)
     _need_gpu("x", x, torch.float16)
-    if channel_scale is not None:
-        _need_gpu("channel_scale", channel_scale, torch.float32)
     N, K = w.shape
     T = x.shape[0]
+    if channel_scale is not None:
+        _need_gpu("channel_scale", channel_scale, torch.float32)
+        if channel_scale.numel() != K:
+            raise ValueError("channel_scale must have K elements")
     fr = np.ascontiguousarray(fractions, dtype=np.float64)
     n = int(fr.size)
     L = load()
@@ -370,15 +388,15 @@ def awq_gemm_salient(x, qweight, scales, zeros, idx, w_salient, group_size: int 
 def awq_salient_loss(w, x, group_size: int = 128, n_salient: int | None = None, symmetric: bool = False,
                      workspace=None):
     """awq_salient_loss: (loss_rtn, loss_salient, idx int32 GPU tensor).
-    n_salient defaults to round(K / 100), the pages' 1 %."""
+    n_salient defaults to the library's awq_salient_count(K), the pages' 1 %."""
     import numpy as np
     torch = _torch()
     _need_gpu("w", w, torch.float16)
     _need_gpu("x", x, torch.float16)
     N, K = w.shape
     T = x.shape[0]
-    n = int(round(0.01 * K)) if n_salient is None else int(n_salient)
     L = load()
+    n = int(L.awq_salient_count(K)) if n_salient is None else int(n_salient)
     nbytes = L.awq_salient_loss_workspace_bytes(N, K, T, group_size, n)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=w.device)
@@ -402,12 +420,15 @@ def awq_quantize_w8(w, group_size: int = 128, channel_scale=None, symmetric: boo
     N, K = w.shape
     if channel_scale is not None:
         _need_gpu("channel_scale", channel_scale, torch.float32)
+        if channel_scale.numel() != K:
+            raise ValueError("channel_scale must have K elements")
+    ng = K // group_size if group_size > 0 else 0
     if out is None:
-        ng = K // group_size if group_size > 0 else 0
         out = (torch.empty((N, max(K // 4, 0)), dtype=torch.int32, device=w.device),
                torch.empty((N, ng), dtype=torch.float16, device=w.device),
                torch.empty((N, ng), dtype=torch.float16, device=w.device))
     qweight, scales, zeros = out
+    _need_out(qweight, scales, zeros, (N, K // 4), (N, ng), w.device)
     mode = QUANT_SYMMETRIC if symmetric else QUANT_ASYMMETRIC
     st = load().awq_quantize_w8(_ptr(w), _ptr(channel_scale), N, K, group_size, mode, _ptr(qweight), _ptr(scales),
                                 _ptr(zeros), _stream(w.device))
@@ -425,9 +446,16 @@ def awq_gemm_w8(x, qweight, scales, zeros, group_size: int = 128, path: int = PA
     _need_gpu("zeros", zeros, torch.float16)
     M, K = x.shape
     N = qweight.shape[0]
-    if qweight.shape != (N, K // 4):
+    if qweight.shape != (N, K // 4) or K % 4:
         raise ValueError("qweight must be [N, K/4]")
+    if scales.shape != (N, K // group_size) or zeros.shape != scales.shape:
+        raise ValueError("scales/zeros must be [N, K/group_size]")
     y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _need_gpu("out", y, torch.float16)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    if workspace is not None:
+        _need_gpu("workspace", workspace, torch.uint8)
     nbytes = workspace.numel() if workspace is not None else 0
     st = load().awq_gemm_w8(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), M, N, K, group_size, _ptr(y), path,
                             _ptr(workspace), nbytes, _stream(x.device))

@@ -158,6 +158,61 @@ awq_status output_loss(const half_t* xa, const uint32_t* qw, const half_t* sc, c
     return launch_sum_partials(partials, gemm_tile_count(T, N), loss_out, s);
 }
 
+// The linear layer behind awq_gemm_ex: checks, then the kernel choice.
+// workspace (may be NULL) feeds the skinny kernel's K splits and, when
+// split_gemm is set, the GEMM's stream-K partials.
+awq_status gemm_dispatch(const void* x_f16, const uint32_t* qweight, const void* scales_f16, const void* zeros_f16,
+                         int64_t M, int64_t N, int64_t K, int group_size, void* y_f16, int path, void* workspace,
+                         size_t workspace_bytes, bool split_gemm, hipStream_t stream) {
+    awq_status st = check_dims(N, K, group_size);
+    if (st != AWQ_OK) return st;
+    if (path < 0 || path > 3) return AWQ_ERR_CONFIG;
+    if (M < 0 || M > kMaxDim) return AWQ_ERR_SHAPE;
+    // The MFMA kernel indexes with 32-bit row/column numbers and 64-bit offsets.
+    if (M > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return AWQ_ERR_SHAPE;
+    if (M == 0 || N == 0) return AWQ_OK;
+    if (!x_f16 || !qweight || !scales_f16 || !zeros_f16 || !y_f16) return AWQ_ERR_NULL;
+    if (!aligned16(x_f16) || !aligned16(qweight) || (reinterpret_cast<uintptr_t>(scales_f16) & 1) ||
+        (reinterpret_cast<uintptr_t>(zeros_f16) & 1) || (reinterpret_cast<uintptr_t>(y_f16) & 1))
+        return AWQ_ERR_ALIGN;
+    const half_t* x = static_cast<const half_t*>(x_f16);
+    const half_t* sc = static_cast<const half_t*>(scales_f16);
+    const half_t* zr = static_cast<const half_t*>(zeros_f16);
+    half_t* y = static_cast<half_t*>(y_f16);
+    const bool gemv_ok = gemv_supported(M, K);
+    bool skinny_phased = false;
+    const bool skinny_ok = skinny_supported(M, N, K, group_size, workspace != nullptr, &skinny_phased);
+    if (path == 1 && !gemv_ok) return AWQ_ERR_CONFIG;
+    if (path == 3 && !skinny_ok) return AWQ_ERR_CONFIG;
+    // automatic: the GEMV up to 4 rows; the skinny kernel up to 64 rows (and
+    // below 5 rows where the GEMV's staged x does not fit the LDS), but
+    // below 9 rows only where it runs without K phases if the GEMV can run
+    // (the phased form, one block per column tile, is 2-3x slower than the
+    // GEMV there and 2-3x faster than the GEMM tile everywhere); else the GEMM
+    const bool use_skinny =
+        path == 3 || (path == 0 && skinny_ok && (M > 4 || !gemv_ok) && !(skinny_phased && gemv_ok));
+    const bool use_gemv = path == 1 || (path == 0 && gemv_ok && !use_skinny);
+    if (use_gemv) return launch_gemv(x, qweight, sc, zr, M, N, K, group_size, y, stream);
+    if (!use_skinny && !split_gemm) workspace = nullptr;
+    if (workspace != nullptr) {
+        if (reinterpret_cast<uintptr_t>(workspace) & 255) return AWQ_ERR_ALIGN;
+        const size_t need = use_skinny ? skinny_workspace_bytes(M, N, K) : gemm_workspace_bytes(M, N);
+        if (workspace_bytes < need) return AWQ_ERR_WORKSPACE;
+    }
+    if (use_skinny) return launch_skinny(x, qweight, sc, zr, M, N, K, group_size, y, workspace, stream);
+    GemmArgs a;
+    a.a = x;
+    a.qweight = qweight;
+    a.scales = sc;
+    a.zeros = zr;
+    a.group_size = group_size;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.y16 = y;
+    return launch_gemm(a, GemmB::kInt4, GemmOut::kF16, stream, workspace);
+}
+
 }  // namespace
 
 extern "C" {
@@ -211,51 +266,8 @@ size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 awq_status awq_gemm_ex(const void* x_f16, const uint32_t* qweight, const void* scales_f16,
                        const void* zeros_f16, int64_t M, int64_t N, int64_t K, int group_size,
                        void* y_f16, int path, void* workspace, size_t workspace_bytes, void* stream) {
-    awq_status st = check_dims(N, K, group_size);
-    if (st != AWQ_OK) return st;
-    if (path < 0 || path > 3) return AWQ_ERR_CONFIG;
-    if (M < 0 || M > kMaxDim) return AWQ_ERR_SHAPE;
-    // The MFMA kernel indexes with 32-bit row/column numbers and 64-bit offsets.
-    if (M > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return AWQ_ERR_SHAPE;
-    if (M == 0 || N == 0) return AWQ_OK;
-    if (!x_f16 || !qweight || !scales_f16 || !zeros_f16 || !y_f16) return AWQ_ERR_NULL;
-    if (!aligned16(x_f16) || !aligned16(qweight) || (reinterpret_cast<uintptr_t>(scales_f16) & 1) ||
-        (reinterpret_cast<uintptr_t>(zeros_f16) & 1) || (reinterpret_cast<uintptr_t>(y_f16) & 1))
-        return AWQ_ERR_ALIGN;
-    const half_t* x = static_cast<const half_t*>(x_f16);
-    const half_t* sc = static_cast<const half_t*>(scales_f16);
-    const half_t* zr = static_cast<const half_t*>(zeros_f16);
-    half_t* y = static_cast<half_t*>(y_f16);
-    const bool gemv_ok = gemv_supported(M, K);
-    bool skinny_phased = false;
-    const bool skinny_ok = skinny_supported(M, N, K, group_size, workspace != nullptr, &skinny_phased);
-    if (path == 1 && !gemv_ok) return AWQ_ERR_CONFIG;
-    if (path == 3 && !skinny_ok) return AWQ_ERR_CONFIG;
-    // automatic: the GEMV up to 4 rows; the skinny kernel up to 64 rows, but
-    // below 9 rows only where it runs without K phases if the GEMV can run
-    // (the phased form, one block per column tile, is 2-3x slower than the
-    // GEMV there and 2-3x faster than the GEMM tile everywhere); else the GEMM
-    const bool use_skinny = path == 3 || (path == 0 && M > 4 && skinny_ok && !(skinny_phased && gemv_ok));
-    const bool use_gemv = path == 1 || (path == 0 && gemv_ok && !use_skinny);
-    if (use_gemv) return launch_gemv(x, qweight, sc, zr, M, N, K, group_size, y, as_stream(stream));
-    if (workspace != nullptr) {
-        if (reinterpret_cast<uintptr_t>(workspace) & 255) return AWQ_ERR_ALIGN;
-        const size_t need = use_skinny ? skinny_workspace_bytes(M, N, K) : gemm_workspace_bytes(M, N);
-        if (workspace_bytes < need) return AWQ_ERR_WORKSPACE;
-    }
-    if (use_skinny)
-        return launch_skinny(x, qweight, sc, zr, M, N, K, group_size, y, workspace, as_stream(stream));
-    GemmArgs a;
-    a.a = x;
-    a.qweight = qweight;
-    a.scales = sc;
-    a.zeros = zr;
-    a.group_size = group_size;
-    a.M = M;
-    a.N = N;
-    a.K = K;
-    a.y16 = y;
-    return launch_gemm(a, GemmB::kInt4, GemmOut::kF16, as_stream(stream), workspace);
+    return gemm_dispatch(x_f16, qweight, scales_f16, zeros_f16, M, N, K, group_size, y_f16, path, workspace,
+                         workspace_bytes, true, as_stream(stream));
 }
 
 awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight, const void* scales_f16,
@@ -302,10 +314,13 @@ awq_status awq_scale_search(const void* w_f16, const void* x_f16, int64_t N, int
     if (N <= 0 || T <= 0 || T > (int64_t(1) << 24)) return AWQ_ERR_SHAPE;
     if (T > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return AWQ_ERR_SHAPE;
     if (n_alpha < 1 || n_alpha > 64) return AWQ_ERR_CONFIG;
-    if (!w_f16 || !x_f16 || !alphas || !workspace || !losses || !best_index || !best_scales)
-        return AWQ_ERR_NULL;
-    for (int i = 0; i < n_alpha; ++i)
-        if (!std::isfinite(alphas[i])) return AWQ_ERR_CONFIG;
+    if (!w_f16 || !x_f16 || !workspace || !losses || !best_index || !best_scales) return AWQ_ERR_NULL;
+    // no grid given: alpha_i = i / n_alpha (n_alpha = 20: 0, 0.05, ..., 0.95)
+    std::vector<double> grid(n_alpha);
+    for (int i = 0; i < n_alpha; ++i) {
+        grid[i] = alphas ? alphas[i] : static_cast<double>(i) / static_cast<double>(n_alpha);
+        if (!std::isfinite(grid[i])) return AWQ_ERR_CONFIG;
+    }
     if (!aligned16(w_f16) || !aligned16(x_f16) || !aligned16(workspace) || (reinterpret_cast<uintptr_t>(best_scales) & 3))
         return AWQ_ERR_ALIGN;
     SearchLayout L(workspace, N, K, T, group_size, n_alpha);
@@ -319,7 +334,7 @@ awq_status awq_scale_search(const void* w_f16, const void* x_f16, int64_t N, int
     // reference output W . x^T, once, in fp32
     if ((st = reference_output(x, w, T, N, K, group_size, L.yref, s)) != AWQ_OK) return st;
     for (int i = 0; i < n_alpha; ++i) {
-        if ((st = launch_pow_scales(L.m, K, alphas[i], L.s, s)) != AWQ_OK) return st;
+        if ((st = launch_pow_scales(L.m, K, grid[i], L.s, s)) != AWQ_OK) return st;
         if ((st = launch_quantize(w, L.s, N, K, group_size, false, 0.0, L.qweight, L.scales, L.zeros, s)) !=
             AWQ_OK)
             return st;
@@ -335,7 +350,7 @@ awq_status awq_scale_search(const void* w_f16, const void* x_f16, int64_t N, int
     for (int i = 1; i < n_alpha; ++i)
         if (losses[i] < losses[best]) best = i;   // strict: ties keep the smaller alpha
     *best_index = best;
-    if ((st = launch_pow_scales(L.m, K, alphas[best], best_scales, s)) != AWQ_OK) return st;
+    if ((st = launch_pow_scales(L.m, K, grid[best], best_scales, s)) != AWQ_OK) return st;
     return AWQ_OK;
 }
 
@@ -435,8 +450,15 @@ awq_status awq_salient_apply(const void* x_f16, const int* idx, const void* w_sa
                                 N, K, n_salient, static_cast<half_t*>(y_f16), as_stream(stream));
 }
 
+int64_t awq_salient_count(int64_t K) {
+    if (K <= 0) return 0;
+    // round(K / 100), ties to even (the default rounding mode)
+    return static_cast<int64_t>(std::nearbyint(0.01 * static_cast<double>(K)));
+}
+
 size_t awq_salient_loss_workspace_bytes(int64_t N, int64_t K, int64_t T, int group_size, int n_salient) {
-    if (check_dims(N, K, group_size) != AWQ_OK || N <= 0 || T <= 0 || n_salient < 0 || n_salient > K) return 0;
+    if (n_salient < 0) n_salient = static_cast<int>(awq_salient_count(K));
+    if (check_dims(N, K, group_size) != AWQ_OK || N <= 0 || T <= 0 || n_salient > K) return 0;
     return SalientLayout(nullptr, N, K, T, group_size, n_salient).bytes;
 }
 
@@ -447,6 +469,7 @@ awq_status awq_salient_loss(const void* w_f16, const void* x_f16, int64_t N, int
     if (st != AWQ_OK) return st;
     if (N <= 0 || T <= 0 || T > (int64_t(1) << 24) || K % 8 != 0) return AWQ_ERR_SHAPE;
     if (T > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return AWQ_ERR_SHAPE;
+    if (n_salient < 0 && K <= kMaxSelectK) n_salient = static_cast<int>(awq_salient_count(K));
     if (K > kMaxSelectK || n_salient < 0 || n_salient > K) return AWQ_ERR_SHAPE;
     if (mode != AWQ_QUANT_ASYMMETRIC && mode != AWQ_QUANT_SYMMETRIC) return AWQ_ERR_CONFIG;
     if (!w_f16 || !x_f16 || !workspace || !loss_rtn || !loss_salient) return AWQ_ERR_NULL;

@@ -869,7 +869,10 @@ void launch_cfg(const GemmArgs& args, void* workspace, hipStream_t stream) {
     const int64_t tiles = ceil_div(args.M, GEO.bm) * tiles_n;
     const int64_t steps = args.K / (DIRECT ? BKD : BK);
     StreamK sk;
-    if (workspace != nullptr && use_stream_k(GEO, tiles, steps)) {
+    // Only fp16-output products take a workspace (the searches' fp32 and
+    // loss forms never split), so the split instances exist for them alone.
+    if constexpr (OMODE != GemmOut::kF16) workspace = nullptr;
+    if (OMODE == GemmOut::kF16 && workspace != nullptr && use_stream_k(GEO, tiles, steps)) {
         sk.ipt = static_cast<int>(steps);
         sk.total = static_cast<int>(tiles * sk.ipt);
         sk.grid = stream_k_grid(GEO, tiles, steps);
@@ -877,12 +880,13 @@ void launch_cfg(const GemmArgs& args, void* workspace, hipStream_t stream) {
         sk.r = sk.total % sk.grid;
         sk.counters = static_cast<int*>(workspace);
         sk.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_counter_bytes());
-        hipLaunchKernelGGL((gemm_kernel<GEO.bm, GEO.bn, BMODE, OMODE, true, DIRECT, WGM, GEO.threads>),
-                           dim3(static_cast<unsigned>(sk.grid)), dim3(GEO.threads), 0, stream, args,
-                           static_cast<int>(tiles_n), sk);
+        if constexpr (OMODE == GemmOut::kF16)
+            hipLaunchKernelGGL((gemm_kernel<GEO.bm, GEO.bn, BMODE, OMODE, true, DIRECT, WGM, GEO.threads>),
+                               dim3(static_cast<unsigned>(sk.grid)), dim3(GEO.threads), 0, stream, args,
+                               static_cast<int>(tiles_n), sk);
         return;
     }
-    if constexpr (DIRECT) {
+    if constexpr (DIRECT && OMODE == GemmOut::kF16) {
         if (workspace != nullptr && use_hybrid(GEO, tiles, steps)) {
             sk.dp_tiles = static_cast<int>(tiles / resident_slots(GEO) * resident_slots(GEO));
             const int64_t tail = tiles - sk.dp_tiles;
