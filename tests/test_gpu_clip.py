@@ -6,7 +6,7 @@ Clipped quantize: bit-exact against the oracle for every group size, both
 maps, with and without channel scales, including groups full of ties.
 Clip search: the scale search's bar. The oracle's best index, unless its two
 lowest losses lie within 1e-6 relative (then either of them); losses within
-1e-4 of the exact oracle and 1e-5 of its fp16-activation form.
+1e-4 of the exact oracle and 2e-6 of its fp16-activation form.
 """
 
 import numpy as np

@@ -6,7 +6,7 @@ over every output of the prefill products; where the oracle samples output
 columns (the larger sweep), every 128-column block contributes one. Scale
 search: the same alpha as the oracle, unless the oracle's two lowest losses
 lie within 1e-6 relative of each other (then either of them); the losses
-within 1e-4 of the exact oracle and within 1e-5 of the oracle's loss with
+within 1e-4 of the exact oracle and within 2e-6 of the oracle's loss with
 X / s rounded to fp16 as the W4A16 layer takes it. Inputs come from the
 seeded generators; expected values come only from the oracle (or from
 golden files written by a script that calls only the oracle).
@@ -41,9 +41,11 @@ NEAR_TIE = 1e-6
 # fp16, which the oracle's own fp16-activation form shows moves the loss by
 # at most ~5e-5 relative on the small cases (1.1e-5 at full size).
 LOSS_RTOL_EXACT = 1e-4
-# Losses against the oracle's fp16-activation form: only the fp32
-# accumulation of the two products and of the squared differences remains.
-LOSS_RTOL_F16 = 1e-5
+# Losses against the oracle's fp16-activation form (and the losses of the
+# salient ablation, where no activation is rescaled): only the fp32
+# accumulation of the two products and of the squared differences remains,
+# measured at most 4.3e-7 relative.
+LOSS_RTOL_F16 = 2e-6
 
 
 def say(*a):
