@@ -28,8 +28,9 @@
  *     is an integer 0..15.
  *   - Pointers marked "device" point to GPU memory of the current HIP device;
  *     they must be 16-byte aligned. The caller allocates and owns every
- *     buffer; the library keeps no state between calls and allocates no
- *     device memory (the scale search takes a caller-provided workspace).
+ *     buffer; the library allocates no device memory (the scale search takes
+ *     a caller-provided workspace) and keeps no state between calls, except
+ *     the static scratch array of awq_gemm_noalloc.
  *   - stream is a hipStream_t (NULL means the null stream). awq_quantize,
  *     awq_gemm and awq_activation_absmean only enqueue work on it and return.
  *   - Argument checks run on the host before anything is enqueued; a failed
@@ -194,6 +195,37 @@ awq_status awq_gemm_ex(const void* x_f16, const uint32_t* qweight,
                        int64_t M, int64_t N, int64_t K, int group_size,
                        void* y_f16, int path, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * awq_gemm_noalloc - awq_gemm_ex for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. The same operation and arguments as awq_gemm_path;
+ * the split scratch comes from a library-held device array instead of a
+ * caller's workspace, and the call allocates nothing.
+ *
+ *   - The skinny kernel (4 < M <= 64, and M <= 4 where the GEMV's staged x
+ *     does not fit) splits K as awq_gemm_ex does with a workspace, so the
+ *     results are those of awq_gemm_ex bit for bit. Its partial tiles and
+ *     tile counters live in a static device array of 49 MiB, one per device
+ *     the library runs on, held until the process ends. A split plan that
+ *     would need more (none on a 256-CU MI355X) returns AWQ_ERR_WORKSPACE
+ *     before any work.
+ *   - The MFMA GEMM (larger M) runs without stream-K splits, whose fp32
+ *     partials would need up to 134 MB; the GEMV uses no scratch.
+ *   - The first call on a device that runs the skinny kernel (after every
+ *     argument check has passed) takes the array's device address and
+ *     enqueues one small kernel on `stream`, ahead of its own, that clears
+ *     the tile counters; every split kernel leaves them at zero when it
+ *     ends.
+ *   - All calls on one device share the array: calls that may run at the
+ *     same time on one device (different streams, graphs replayed
+ *     concurrently) race and give wrong results. Serialise them.
+ * Returns AWQ_ERR_HIP if the array cannot be set up on the current device.
+ */
+awq_status awq_gemm_noalloc(const void* x_f16, const uint32_t* qweight,
+                            const void* scales_f16, const void* zeros_f16,
+                            int64_t M, int64_t N, int64_t K, int group_size,
+                            void* y_f16, int path, void* stream);
 
 /*
  * awq_activation_absmean - m[k] = max(mean_t |x[t, k]|, 1e-8), the

@@ -76,6 +76,8 @@ def load() -> ctypes.CDLL:
     L.awq_gemm_workspace_bytes.argtypes = [c_i64, c_i64, c_i64]
     L.awq_gemm_ex.restype = c_int
     L.awq_gemm_ex.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_int, c_vp, c_sz, c_vp]
+    L.awq_gemm_noalloc.restype = c_int
+    L.awq_gemm_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_int, c_vp]
     L.awq_activation_absmean_workspace_bytes.restype = c_sz
     L.awq_activation_absmean_workspace_bytes.argtypes = [c_i64, c_i64]
     L.awq_activation_absmean.restype = c_int
@@ -244,6 +246,32 @@ def awq_gemm(x, qweight, scales, zeros, group_size: int = 128, path: int = PATH_
         st = load().awq_gemm_ex(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), M, N, K, group_size,
                                 _ptr(y), int(path), _ptr(workspace), workspace.numel(), _stream(x.device))
         _check("awq_gemm_ex", st)
+    return y
+
+
+def awq_gemm_noalloc(x, qweight, scales, zeros, group_size: int = 128, path: int = PATH_AUTO, out=None):
+    """awq_gemm_noalloc: awq_gemm with the skinny kernel's K-split scratch
+    held by the library (no workspace, no device allocation in the call;
+    calls on one device must not overlap). Pass `out` to keep the binding
+    from allocating y."""
+    torch = _torch()
+    _need_gpu("x", x, torch.float16)
+    _need_gpu("qweight", qweight, torch.int32)
+    _need_gpu("scales", scales, torch.float16)
+    _need_gpu("zeros", zeros, torch.float16)
+    M, K = x.shape
+    N = qweight.shape[0]
+    if qweight.shape != (N, K // 8) or K % 8:
+        raise ValueError(f"qweight must be [N, K/8] = [{N}, {K // 8}]")
+    if scales.shape != (N, K // group_size) or zeros.shape != scales.shape:
+        raise ValueError("scales/zeros must be [N, K/group_size]")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _need_gpu("out", y, torch.float16)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    st = load().awq_gemm_noalloc(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), M, N, K, group_size, _ptr(y),
+                                 int(path), _stream(x.device))
+    _check("awq_gemm_noalloc", st)
     return y
 
 

@@ -2,6 +2,7 @@
 // host, then kernels enqueued on the caller's stream.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "awq_internal.h"
@@ -158,12 +159,63 @@ awq_status output_loss(const half_t* xa, const uint32_t* qw, const half_t* sc, c
     return launch_sum_partials(partials, gemm_tile_count(T, N), loss_out, s);
 }
 
-// The linear layer behind awq_gemm_ex: checks, then the kernel choice.
-// workspace (may be NULL) feeds the skinny kernel's K splits and, when
-// split_gemm is set, the GEMM's stream-K partials.
+// ---- the library-held scratch of awq_gemm_noalloc ----
+// Callers that cannot allocate device memory (code under HIP graph capture,
+// tight serving loops) get the skinny kernel's K-split partial tiles and
+// tile counters from this array instead of a workspace. 49 MiB holds the
+// split plan of every M <= 64 on a 256-CU device (4 KiB of counters + 768
+// partial tiles of up to 64 KiB). Each device the library runs on holds its
+// own copy until the process ends.
+constexpr size_t kNoAllocScratchBytes = size_t(49) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;         // the device address of `scratch` on this device
+    awq_status status = AWQ_OK;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch` (its device address, taken once per
+// device with that device current). The first call on a device also clears
+// the tile counters (a fill kernel on `stream`, ahead of the call's own
+// work); every split kernel leaves them at zero when it ends.
+awq_status device_scratch(void** out, hipStream_t stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return AWQ_ERR_HIP;
+    ScratchSlot& slot = g_scratch[dev];
+    std::call_once(slot.once, [&] {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            slot.status = AWQ_ERR_HIP;
+            return;
+        }
+        const int64_t words = static_cast<int64_t>(split_counter_bytes() / sizeof(uint32_t));
+        hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<unsigned>(ceil_div(words, 256))), dim3(256), 0, stream,
+                           static_cast<uint32_t*>(p), words);
+        slot.status = last_launch_status();
+        if (slot.status == AWQ_OK) slot.ptr = p;
+    });
+    if (slot.status != AWQ_OK) return slot.status;
+    *out = slot.ptr;
+    return AWQ_OK;
+}
+
+// The linear layer behind awq_gemm_ex and awq_gemm_noalloc: checks, then
+// the kernel choice. workspace (may be NULL) feeds the skinny kernel's K
+// splits and, when split_gemm is set, the GEMM's stream-K partials. With
+// library_scratch the skinny kernel's splits take the device's `scratch`
+// instead (set up only once every check has passed); the GEMM then runs
+// unsplit.
 awq_status gemm_dispatch(const void* x_f16, const uint32_t* qweight, const void* scales_f16, const void* zeros_f16,
                          int64_t M, int64_t N, int64_t K, int group_size, void* y_f16, int path, void* workspace,
-                         size_t workspace_bytes, bool split_gemm, hipStream_t stream) {
+                         size_t workspace_bytes, bool split_gemm, bool library_scratch, hipStream_t stream) {
     awq_status st = check_dims(N, K, group_size);
     if (st != AWQ_OK) return st;
     if (path < 0 || path > 3) return AWQ_ERR_CONFIG;
@@ -181,7 +233,8 @@ awq_status gemm_dispatch(const void* x_f16, const uint32_t* qweight, const void*
     half_t* y = static_cast<half_t*>(y_f16);
     const bool gemv_ok = gemv_supported(M, K);
     bool skinny_phased = false;
-    const bool skinny_ok = skinny_supported(M, N, K, group_size, workspace != nullptr, &skinny_phased);
+    const bool skinny_ok =
+        skinny_supported(M, N, K, group_size, workspace != nullptr || library_scratch, &skinny_phased);
     if (path == 1 && !gemv_ok) return AWQ_ERR_CONFIG;
     if (path == 3 && !skinny_ok) return AWQ_ERR_CONFIG;
     // automatic: the GEMV up to 4 rows; the skinny kernel up to 64 rows (and
@@ -194,6 +247,11 @@ awq_status gemm_dispatch(const void* x_f16, const uint32_t* qweight, const void*
     const bool use_gemv = path == 1 || (path == 0 && gemv_ok && !use_skinny);
     if (use_gemv) return launch_gemv(x, qweight, sc, zr, M, N, K, group_size, y, stream);
     if (!use_skinny && !split_gemm) workspace = nullptr;
+    if (use_skinny && library_scratch) {
+        if (skinny_workspace_bytes(M, N, K) > kNoAllocScratchBytes) return AWQ_ERR_WORKSPACE;
+        if ((st = device_scratch(&workspace, stream)) != AWQ_OK) return st;
+        workspace_bytes = kNoAllocScratchBytes;
+    }
     if (workspace != nullptr) {
         if (reinterpret_cast<uintptr_t>(workspace) & 255) return AWQ_ERR_ALIGN;
         const size_t need = use_skinny ? skinny_workspace_bytes(M, N, K) : gemm_workspace_bytes(M, N);
@@ -267,7 +325,7 @@ awq_status awq_gemm_ex(const void* x_f16, const uint32_t* qweight, const void* s
                        const void* zeros_f16, int64_t M, int64_t N, int64_t K, int group_size,
                        void* y_f16, int path, void* workspace, size_t workspace_bytes, void* stream) {
     return gemm_dispatch(x_f16, qweight, scales_f16, zeros_f16, M, N, K, group_size, y_f16, path, workspace,
-                         workspace_bytes, true, as_stream(stream));
+                         workspace_bytes, true, false, as_stream(stream));
 }
 
 awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight, const void* scales_f16,
@@ -275,6 +333,13 @@ awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight, const void*
                          void* y_f16, int path, void* stream) {
     return awq_gemm_ex(x_f16, qweight, scales_f16, zeros_f16, M, N, K, group_size, y_f16, path, nullptr, 0,
                        stream);
+}
+
+awq_status awq_gemm_noalloc(const void* x_f16, const uint32_t* qweight, const void* scales_f16,
+                            const void* zeros_f16, int64_t M, int64_t N, int64_t K, int group_size, void* y_f16,
+                            int path, void* stream) {
+    return gemm_dispatch(x_f16, qweight, scales_f16, zeros_f16, M, N, K, group_size, y_f16, path, nullptr, 0,
+                         false, true, as_stream(stream));
 }
 
 awq_status awq_gemm(const void* x_f16, const uint32_t* qweight, const void* scales_f16,
