@@ -57,10 +57,13 @@ def _finish(proc, verbose) -> None:
         sys.stderr.write(err)
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
+def build(verbose: bool = False, extra_flags=None, out_path: str = LIB_PATH, obj_dir: str = None) -> str:
     """Compile every HIP source (one hipcc process per translation unit, in
-    parallel) and link them into one shared library; returns its path."""
-    obj_dir = os.path.join(HERE, "_build")
+    parallel) and link them into one shared library; returns its path.
+    extra_flags go to every compile and to the link (e.g. host-only
+    sanitizers, each -fsanitize= after -Xarch_host); out_path and obj_dir
+    place a variant build elsewhere."""
+    obj_dir = obj_dir or os.path.join(HERE, "_build")
     os.makedirs(obj_dir, exist_ok=True)
     compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"] + list(extra_flags or [])
     objs, procs = [], []
@@ -73,11 +76,12 @@ def build(verbose: bool = False, extra_flags=None) -> str:
             _finish(procs.pop(0), verbose)
     for p in procs:
         _finish(p, verbose)
-    tmp = LIB_PATH + ".tmp"
-    link = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    tmp = out_path + ".tmp"
+    link = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *list(extra_flags or []), *objs, "-o", tmp],
+                verbose)
     _finish(link, verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    return out_path
 
 
 if __name__ == "__main__":
