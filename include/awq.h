@@ -136,12 +136,13 @@ awq_status awq_quantize_ex(const void* w_f16, const float* channel_scale,
  *   M, N, K      M, N >= 0; K > 0, K % group_size == 0
  *   group_size   32, 64, 128, 256 or 512
  *   y_f16        device, fp16 [M, N] (output; must not alias the inputs)
- * M == 0 or N == 0 returns AWQ_OK without work. M <= 4 (decode) runs a
- * bandwidth-bound GEMV, 4 < M <= 64 (a batch of decode tokens) a skinny
- * MFMA kernel that streams the packed weights straight into registers (so
- * does M <= 4 when the GEMV's staged x would not fit the LDS, e.g. M = 4 at
- * K = 28672), and larger M the MFMA GEMM. Results do not depend on
- * run-to-run scheduling.
+ * M == 0 or N == 0 returns AWQ_OK without work. Decode (M <= 2) runs a
+ * bandwidth-bound GEMV; a batch of decode tokens (M <= 64) one of two MFMA
+ * kernels that stream the packed weights straight into registers: column
+ * tiles (one block per 16 output columns over all of K; M <= 32, chosen for
+ * 3 <= M <= 4 and for layers of up to 48 Mi weights) or the skinny kernel
+ * (256 columns per block, K split across blocks with a workspace); larger M
+ * the MFMA GEMM. Results do not depend on run-to-run scheduling.
  */
 awq_status awq_gemm(const void* x_f16, const uint32_t* qweight,
                     const void* scales_f16, const void* zeros_f16,
@@ -153,11 +154,15 @@ awq_status awq_gemm(const void* x_f16, const uint32_t* qweight,
  * path 0 = automatic (as awq_gemm), 1 = GEMV (requires M <= 8),
  * 2 = MFMA GEMM, 3 = skinny MFMA kernel (requires M <= 64, G <= 256 and a
  * packed matrix under 4 GiB; without a workspace each block walks all of K,
- * staging it in LDS-sized phases).
+ * staging it in LDS-sized phases), 4 = column-tile MFMA kernel (requires
+ * M <= 32, G <= 256, M * K * 2 < 2^31 and the tile's (scale, zero) pairs in
+ * LDS; no workspace).
  * Any other path, or a path whose requirement fails, returns AWQ_ERR_CONFIG.
- * The automatic choice takes the GEMV for M <= 4 where it can run; the
- * skinny kernel for M <= 64, except for M <= 8 where it would have to stage
- * K in phases and the GEMV can run (then the GEMV); then the GEMM.
+ * The automatic choice takes the column tiles for 3 <= M <= 4, for
+ * M <= 16 on layers of up to 48 Mi weights and for M <= 32 on such layers
+ * of up to 8192 columns; otherwise the GEMV for M <= 4 where it can run;
+ * the skinny kernel for M <= 64, except for M <= 8 where it would have to
+ * stage K in phases and the GEMV can run (then the GEMV); then the GEMM.
  */
 awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight,
                          const void* scales_f16, const void* zeros_f16,

@@ -65,15 +65,15 @@ int main() {
            AWQ_OK);
 
     // linear layer (every path and both workspace forms)
-    for (int path = 0; path < 5; ++path) {
+    for (int path = 0; path < 6; ++path) {
         expect("gemm null x", awq_gemm_path(nullptr, (uint32_t*)F, F, F, 16, 64, 128, 128, F, path, nullptr),
-               path == 4 ? AWQ_ERR_CONFIG : AWQ_ERR_NULL);
+               path == 5 ? AWQ_ERR_CONFIG : AWQ_ERR_NULL);
         expect("gemm huge M", awq_gemm_path(F, (uint32_t*)F, F, F, huge, 64, 128, 128, F, path, nullptr),
-               path == 4 ? AWQ_ERR_CONFIG : AWQ_ERR_SHAPE);
+               path == 5 ? AWQ_ERR_CONFIG : AWQ_ERR_SHAPE);
         expect("gemm huge N", awq_gemm_path(F, (uint32_t*)F, F, F, 4, huge, 128, 128, F, path, nullptr),
                AWQ_ERR_SHAPE);
         expect("noalloc null y", awq_gemm_noalloc(F, (uint32_t*)F, F, F, 16, 64, 128, 128, nullptr, path, nullptr),
-               path == 4 ? AWQ_ERR_CONFIG : AWQ_ERR_NULL);
+               path == 5 ? AWQ_ERR_CONFIG : AWQ_ERR_NULL);
     }
     expect("gemm align x", awq_gemm(ODD, (uint32_t*)F, F, F, 4, 64, 128, 128, F, nullptr), AWQ_ERR_ALIGN);
     expect("gemm align y", awq_gemm(F, (uint32_t*)F, F, F, 4, 64, 128, 128, fake(0x10001), nullptr),

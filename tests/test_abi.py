@@ -113,7 +113,9 @@ def test_gemm_checks(L):
     assert g(FAKE, FAKE, FAKE, FAKE, 1, 16, 100, 64, FAKE, 0, None) == SHAPE
     assert g(FAKE, FAKE, FAKE, FAKE, -1, 16, 128, 64, FAKE, 0, None) == SHAPE
     assert g(FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 96, FAKE, 0, None) == CONFIG
-    assert g(FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 64, FAKE, 4, None) == CONFIG
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 64, FAKE, 5, None) == CONFIG
+    assert g(FAKE, FAKE, FAKE, FAKE, 33, 16, 128, 64, FAKE, 4, None) == CONFIG  # column tiles: M <= 32
+    assert g(FAKE, FAKE, FAKE, FAKE, 16, 16, 512, 512, FAKE, 4, None) == CONFIG  # and G <= 256
     assert g(FAKE, FAKE, FAKE, FAKE, 65, 16, 128, 64, FAKE, 3, None) == CONFIG  # skinny is M <= 64
     assert g(FAKE, FAKE, FAKE, FAKE, 16, 16, 512, 512, FAKE, 3, None) == CONFIG  # and G <= 256
     assert g(FAKE, FAKE, FAKE, FAKE, 9, 16, 128, 64, FAKE, 1, None) == CONFIG   # GEMV is M <= 8

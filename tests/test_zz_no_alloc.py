@@ -55,7 +55,7 @@ def run_pair(M, N, K, seed):
 @pytest.mark.parametrize("first,second", [
     ((16, 11008, 4096), (9, 4096, 4096)),       # skinny, K split: 43 then 16 column tiles
     ((48, 5120, 13824), (33, 4096, 11008)),     # skinny, 4 row blocks, long K
-    ((3, 4096, 28672), (2, 1024, 28672)),       # M <= 4 whose x does not fit the GEMV: skinny
+    ((3, 4096, 28672), (2, 1024, 28672)),       # long K: column tiles, then the skinny kernel (M = 2)
     ((1, 11008, 4096), (1, 4096, 4096)),        # GEMV: no scratch
     ((300, 2048, 1024), (130, 700, 512)),       # MFMA GEMM, unsplit here
 ])

@@ -28,7 +28,7 @@ STATUS_NAMES = {
     0: "AWQ_OK", 1: "AWQ_ERR_NULL", 2: "AWQ_ERR_SHAPE", 3: "AWQ_ERR_ALIGN",
     4: "AWQ_ERR_CONFIG", 5: "AWQ_ERR_WORKSPACE", 6: "AWQ_ERR_HIP",
 }
-PATH_AUTO, PATH_GEMV, PATH_GEMM, PATH_SKINNY = 0, 1, 2, 3
+PATH_AUTO, PATH_GEMV, PATH_GEMM, PATH_SKINNY, PATH_COLTILE = 0, 1, 2, 3, 4
 QUANT_ASYMMETRIC, QUANT_SYMMETRIC = 0, 1
 
 _lib = None

@@ -61,7 +61,7 @@ struct SearchLayout {
         zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         xs = c.take<half_t>(static_cast<size_t>(T) * K);
         yref = c.take<float>(static_cast<size_t>(ref_tiled_floats(T, N)));
-        tile_partials = c.take<double>(gemm_tile_count(T, N));
+        tile_partials = c.take<double>(gemm_tile_count(T, N) + kLossSumBlocks);
         losses = c.take<double>(n_alpha);
         bytes = c.used;
     }
@@ -91,7 +91,7 @@ struct SalientLayout {
         zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         w_sal = c.take<half_t>(static_cast<size_t>(std::max(n_sal, 1)) * N);
         yref = c.take<float>(static_cast<size_t>(ref_tiled_floats(T, N)));
-        tile_partials = c.take<double>(gemm_tile_count(T, N));
+        tile_partials = c.take<double>(gemm_tile_count(T, N) + kLossSumBlocks);
         losses = c.take<double>(2);
         bytes = c.used;
     }
@@ -118,7 +118,7 @@ struct ClipLayout {
         zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         if (scaled) xs = c.take<half_t>(static_cast<size_t>(T) * K);
         yref = c.take<float>(static_cast<size_t>(ref_tiled_floats(T, N)));
-        tile_partials = c.take<double>(gemm_tile_count(T, N));
+        tile_partials = c.take<double>(gemm_tile_count(T, N) + kLossSumBlocks);
         losses = c.take<double>(n);
         bytes = c.used;
     }
@@ -218,7 +218,7 @@ awq_status gemm_dispatch(const void* x_f16, const uint32_t* qweight, const void*
                          size_t workspace_bytes, bool split_gemm, bool library_scratch, hipStream_t stream) {
     awq_status st = check_dims(N, K, group_size);
     if (st != AWQ_OK) return st;
-    if (path < 0 || path > 3) return AWQ_ERR_CONFIG;
+    if (path < 0 || path > 4) return AWQ_ERR_CONFIG;
     if (M < 0 || M > kMaxDim) return AWQ_ERR_SHAPE;
     // The MFMA kernel indexes with 32-bit row/column numbers and 64-bit offsets.
     if (M > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return AWQ_ERR_SHAPE;
@@ -237,7 +237,11 @@ awq_status gemm_dispatch(const void* x_f16, const uint32_t* qweight, const void*
         skinny_supported(M, N, K, group_size, workspace != nullptr || library_scratch, &skinny_phased);
     if (path == 1 && !gemv_ok) return AWQ_ERR_CONFIG;
     if (path == 3 && !skinny_ok) return AWQ_ERR_CONFIG;
-    // automatic: the GEMV up to 4 rows; the skinny kernel up to 64 rows (and
+    if (path == 4 && !coltile_supported(M, N, K, group_size)) return AWQ_ERR_CONFIG;
+    if (path == 4 || (path == 0 && coltile_preferred(M, N, K, group_size)))
+        return launch_coltile(x, qweight, sc, zr, M, N, K, group_size, y, stream);
+    // automatic: the column tiles where they measured fastest (above);
+    // otherwise the GEMV up to 4 rows; the skinny kernel up to 64 rows (and
     // below 5 rows where the GEMV's staged x does not fit the LDS), but
     // below 9 rows only where it runs without K phases if the GEMV can run
     // (the phased form, one block per column tile, is 2-3x slower than the

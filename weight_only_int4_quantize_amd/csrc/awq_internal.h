@@ -132,6 +132,18 @@ awq_status launch_skinny(const half_t* x, const uint32_t* qweight, const half_t*
                          const half_t* zeros, int64_t M, int64_t N, int64_t K, int group_size,
                          half_t* y, void* workspace, hipStream_t stream);
 
+// Column-tile MFMA kernel for small batches (M <= kColTileMaxM): one block
+// per 16 output columns over all of K, x read straight into the MFMA A
+// operand, the waves' K ranges added in LDS; no workspace.
+constexpr int kColTileMaxM = 32;
+bool coltile_supported(int64_t M, int64_t N, int64_t K, int group_size);
+// whether the automatic choice takes it (by measured times against the GEMV
+// and the skinny kernel)
+bool coltile_preferred(int64_t M, int64_t N, int64_t K, int group_size);
+awq_status launch_coltile(const half_t* x, const uint32_t* qweight, const half_t* scales,
+                          const half_t* zeros, int64_t M, int64_t N, int64_t K, int group_size,
+                          half_t* y, hipStream_t stream);
+
 // Mixed precision with fp16 salient channels.
 awq_status launch_select_salient(const double* m, int64_t K, int n, int* idx, hipStream_t stream);
 awq_status launch_salient_fix(const half_t* w, int64_t N, int64_t K, int group_size, const int* idx, int n_sal,
@@ -148,6 +160,9 @@ awq_status launch_absmean(const half_t* x, int64_t T, int64_t K, double* m, doub
 awq_status launch_pow_scales(const double* m, int64_t K, double alpha, float* s, hipStream_t stream);
 awq_status launch_divide_columns(const half_t* x, const float* s, int64_t T, int64_t K, half_t* xs,
                                  hipStream_t stream);
-awq_status launch_sum_partials(const double* partials, int64_t n, double* out, hipStream_t stream);
+// Sum of n per-tile loss partials into *out, in a fixed order. The buffer
+// holds kLossSumBlocks doubles of scratch behind the n partials.
+constexpr int kLossSumBlocks = 256;
+awq_status launch_sum_partials(double* partials, int64_t n, double* out, hipStream_t stream);
 
 }  // namespace awq

@@ -1,0 +1,386 @@
+// Column-tile W4A16 kernel for small decode batches, y[M, N] = x[M, K] .
+// dequant(Wq)^T with 2 <= M <= 32 (the W4A16 linear layer of the rskf.cn AWQ
+// article, §1.3 / §3.3, at a handful of tokens; the dequantization map of
+// xxmr.cn §1.2).
+//
+// At these M the layer is bound by streaming the packed weights from HBM,
+// and every weight feeds M outputs, which the fp16 matrix cores take: one
+// v_mfma_f32_16x16x32_f16 multiplies 16 rows of x by 16 columns of W over
+// 32 k. The layout puts the whole K range of one 16-column tile in one
+// thread block, so no partial sums leave the block:
+//  * a block of NW waves owns 16 output columns and all of K; wave w takes
+//    the groups [w ng / NW, (w + 1) ng / NW) and keeps a 16 x 16 accumulator
+//    per 16 rows of x; the waves' accumulators are added through LDS in a
+//    fixed order at the end (deterministic);
+//  * within a group a lane of k-quarter q (lane / 16) takes the G / 4
+//    consecutive k of words [q WPL, (q + 1) WPL) of its column, WPL = G / 32
+//    packed words, so its weights are one contiguous 4 WPL-byte load and its
+//    x one contiguous 16 WPL-byte load per row. The MFMA's k order is free
+//    as long as both operands follow it: step j of the group pairs word
+//    q WPL + j of every column with the same 8 k of x;
+//  * x is read straight from global memory (L2) into the A operand, no LDS:
+//    each 16-column tile uses each x value once, so staging would not save a
+//    byte. x costs M / 4 times the weight bytes, from L2 rather than HBM;
+//  * weights and x stream through a ring of DEPTH groups in flight per wave;
+//    the loads are issued unconditionally at fixed places (past-the-end
+//    offsets read zero without touching memory), so the compiler's wait
+//    counts follow the ring;
+//  * the group's scale and zero-point come from LDS, staged once per block
+//    with coalesced loads; the scale is applied per group in fp32,
+//    acc += s * (x . (q - z)), the inner sum exact in the MFMA.
+// Nibble unpack: (w & 0x000F000F) | 0x6400_6400 = (1024 + q0, 1024 + q4) and
+// (w & 0x00F000F0) | 0x5400_5400 = (64 + q1, 64 + q5), the same on w >> 8
+// for (q2, q6) and (q3, q7); minus (1024 + z) or (64 + z) this is the exact
+// fp16 (q - z) in the order (0,4,1,5,2,6,3,7), and x is permuted to match.
+#include <algorithm>
+
+#include "awq_internal.h"
+
+namespace awq {
+namespace {
+
+constexpr int kCtCols = 16;
+constexpr int kCtSZ = 4;          // (scale, zero) pairs per thread loaded ahead of the ring
+// LDS: the (scale, zero) pairs [16][ng | 1] words, then (16-byte aligned) the
+// waves' x buffers, later reused for the waves' sums
+__host__ __device__ inline int ct_x_offset(int ng) { return (kCtCols * (ng | 1) + 3) & ~3; }
+
+__device__ inline half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), static_cast<int>(bytes),
+                                             0x00020000);
+}
+
+struct CtConsts {
+    uint32_t lo_mask, hi_mask, lo_magic, hi_magic;
+};
+// In VGPRs: gfx9 VOP3 takes no 32-bit literal, so (w & mask) | magic is one
+// v_and_or_b32 only with register operands.
+__device__ inline CtConsts ct_consts() {
+    CtConsts k{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
+    asm volatile("" : "+v"(k.lo_mask), "+v"(k.hi_mask), "+v"(k.lo_magic), "+v"(k.hi_magic));
+    return k;
+}
+
+// one packed word -> 8 exact fp16 (q - z) in the order (0,4,1,5,2,6,3,7)
+__device__ inline half8_t unpack8(uint32_t w, half2_t zc_hi, half2_t zc_lo, const CtConsts& k) {
+    const uint32_t w8 = w >> 8;
+    const half2_t a = as_h2((w & k.lo_mask) | k.lo_magic) - zc_hi;   // (q0, q4)
+    const half2_t b = as_h2((w & k.hi_mask) | k.hi_magic) - zc_lo;   // (q1, q5)
+    const half2_t c = as_h2((w8 & k.lo_mask) | k.lo_magic) - zc_hi;  // (q2, q6)
+    const half2_t d = as_h2((w8 & k.hi_mask) | k.hi_magic) - zc_lo;  // (q3, q7)
+    return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// 8 consecutive x values (natural order) -> the order (0,4,1,5,2,6,3,7)
+__device__ inline half8_t permute8(uint4 v) {
+    uint4 p;
+    p.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);   // (x0, x4)
+    p.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);   // (x1, x5)
+    p.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);   // (x2, x6)
+    p.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);   // (x3, x7)
+    return __builtin_bit_cast(half8_t, p);
+}
+
+// One group's operands of a lane: WPL packed words of its column, and MB WPL
+// 16-byte pieces of the group's x in row-run order.
+template <int WPL, int XP>
+struct CtSlot {
+    uint32_t w[WPL];
+    uint4 x[XP];           // coalesced pieces of the group's x, re-laid through LDS
+};
+
+// XR: rows of x staged (M rounded up to 4, 8, 16 or 32); MB = XR / 16
+// rounded up MFMA row blocks; XP 16-byte x pieces per lane and group.
+template <int XR, int WPL, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(XR * WPL <= 64 ? 4 : 2))) void coltile_kernel(const half_t* __restrict__ x,
+                                                         const uint32_t* __restrict__ qweight,
+                                                         const half_t* __restrict__ scales,
+                                                         const half_t* __restrict__ zeros,
+                                                         half_t* __restrict__ y, int M, int N, int K) {
+    constexpr int G = WPL * 32;
+    constexpr int MB = (XR + 15) / 16;
+    constexpr int XPIECES = XR * (G / 8);                       // 16-byte pieces of x per group
+    constexpr int XP = (XPIECES + 63) / 64;
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];   // (s, z) pairs [16][szst], then sums
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15;
+    const int kq = lane >> 4;                       // k-quarter of every group
+    const int n0 = blockIdx.x * kCtCols;
+    const int ng = K / G;
+    const int szst = ng | 1;                        // odd: 16 columns at one group hit distinct banks
+
+    // ---- the tile's (scale, zero) pairs: consecutive threads read
+    //      consecutive groups of one column (coalesced). The first
+    //      kCtSZ per thread are loaded into registers before the ring's
+    //      loads are issued and written to LDS after them (loads complete in
+    //      order, so that write waits for these loads only); any rest
+    //      (more than kCtSZ * 64 NW pairs) is staged after the ring's loads ----
+    const int cols = min(kCtCols, N - n0);
+    const uint32_t sz_bytes = static_cast<uint32_t>(cols) * static_cast<uint32_t>(ng) * 2;
+    const auto rs = rsrc(scales + static_cast<int64_t>(n0) * ng, sz_bytes);
+    const auto rz = rsrc(zeros + static_cast<int64_t>(n0) * ng, sz_bytes);
+    uint16_t sr[kCtSZ], zr[kCtSZ];
+#pragma unroll
+    for (int i = 0; i < kCtSZ; ++i) {
+        const int e = tid + i * NW * 64;       // column e / ng, group e % ng
+        const uint32_t so = e < kCtCols * ng ? static_cast<uint32_t>(e) * 2 : sz_bytes;
+        sr[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
+        zr[i] = __builtin_amdgcn_raw_buffer_load_b16(rz, so, 0, 0);
+    }
+
+    // ---- this wave's groups and buffer offsets; offsets at or past a
+    //      buffer's size read zero without touching memory ----
+    const int g0 = static_cast<int>(static_cast<int64_t>(wave) * ng / NW);
+    const int g1 = static_cast<int>(static_cast<int64_t>(wave + 1) * ng / NW);
+    const uint32_t w_bytes = static_cast<uint32_t>(cols) * static_cast<uint32_t>(K / 2);
+    const auto rw = rsrc(qweight + static_cast<int64_t>(n0) * (K / 8), w_bytes);
+    // weights are loaded with the lanes of a quad on one column (lane l:
+    // column l / 4, quarter l % 4), so each quad reads one contiguous run,
+    // and moved to the MFMA's lane order (column l % 16, quarter l / 16)
+    // with a lane permute
+    const int lcol = lane >> 2, lq = lane & 3;
+    const uint32_t w_lane = lcol < cols ? static_cast<uint32_t>(lcol) * (K / 2) + lq * WPL * 4 : w_bytes;
+    const int w_src = 4 * ((col * 4 + kq) & 63);    // byte address of the source lane: 4 (4 col + kq)
+    // x of one group, XR rows x G values, as XP 16-byte pieces per lane:
+    // piece p = lane + 64 i is 16 bytes of row p / (G / 8), so each load
+    // instruction reads whole rows' runs (coalesced)
+    const uint32_t x_bytes = static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2;
+    const auto rx = rsrc(x, x_bytes);
+    uint32_t x_piece[XP];
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+        const int p = lane + 64 * i;
+        const int row = p / (G / 8), c8 = p % (G / 8);
+        x_piece[i] = p < XPIECES && row < M ? (static_cast<uint32_t>(row) * K + c8 * 8) * 2 : x_bytes;
+    }
+    auto load = [&](CtSlot<WPL, XP>& sl, int g) {
+        const bool ok = g < g1;
+        const uint32_t wo = ok ? w_lane + static_cast<uint32_t>(g) * (G / 2) : w_bytes;
+        if constexpr (WPL == 8) {
+            const uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 0, 0));
+            const uint4 b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 16, 0));
+            sl.w[0] = a.x; sl.w[1] = a.y; sl.w[2] = a.z; sl.w[3] = a.w;
+            sl.w[4] = b.x; sl.w[5] = b.y; sl.w[6] = b.z; sl.w[7] = b.w;
+        } else if constexpr (WPL == 4) {
+            const uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 0, 0));
+            sl.w[0] = a.x; sl.w[1] = a.y; sl.w[2] = a.z; sl.w[3] = a.w;
+        } else if constexpr (WPL == 2) {
+            const uint2 a = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, wo, 0, 0));
+            sl.w[0] = a.x; sl.w[1] = a.y;
+        } else {
+            sl.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, wo, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < XP; ++i) {
+            const uint32_t xo = ok && x_piece[i] < x_bytes ? x_piece[i] + static_cast<uint32_t>(g) * (G * 2) : x_bytes;
+            sl.x[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0));
+        }
+    };
+
+    CtSlot<WPL, XP> ring[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+        load(ring[d], g0 + d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < kCtSZ; ++i) {
+        const int e = tid + i * NW * 64;
+        if (e < kCtCols * ng) {
+            const int c = e / ng, g = e - c * ng;
+            lds[c * szst + g] = static_cast<uint32_t>(sr[i]) | (static_cast<uint32_t>(zr[i]) << 16);
+        }
+    }
+    for (int e = tid + kCtSZ * NW * 64; e < kCtCols * ng; e += NW * 64) {
+        const int c = e / ng, g = e - c * ng;
+        const uint32_t so = static_cast<uint32_t>(e) * 2;
+        lds[c * szst + g] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0)) |
+                            (static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rz, so, 0, 0)) << 16);
+    }
+    __syncthreads();   // the (scale, zero) pairs are in LDS
+
+    float4_t acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    const CtConsts uk = ct_consts();
+    const uint32_t* szcol = lds + col * szst;
+    // the wave's x buffer: XR rows of G values, rows padded by 16 bytes so
+    // the 16 rows of an MFMA operand read hit distinct banks; operand rows
+    // past XR are zero and not read
+    constexpr int XST = G + 8;
+    half_t* xw = reinterpret_cast<half_t*>(lds + ct_x_offset(ng)) + wave * (XR * XST);
+    for (int gb = g0; gb < g1; gb += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int g = gb + d;
+            CtSlot<WPL, XP>& sl = ring[d];
+            if (g < g1) {
+                const uint32_t sz = szcol[g];
+                const half_t z = __builtin_bit_cast(half_t, static_cast<uint16_t>(sz >> 16));
+                const half_t zh = static_cast<half_t>(1024.0f) + z;   // exact
+                const half_t zl = static_cast<half_t>(64.0f) + z;     // exact
+                const float s = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(sz & 0xFFFFu)));
+                float4_t part[MB];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) part[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+                // x pieces to the wave's LDS rows, then back in operand order:
+                // lane (row col, quarter kq) takes 8 values at k = 8 (kq WPL + j)
+                // (one wave's LDS accesses execute in order, so no barrier)
+#pragma unroll
+                for (int i = 0; i < XP; ++i) {
+                    const int p = lane + 64 * i;
+                    if (XPIECES % 64 == 0 || p < XPIECES)
+                        *reinterpret_cast<uint4*>(&xw[(p / (G / 8)) * XST + (p % (G / 8)) * 8]) = sl.x[i];
+                }
+#pragma unroll
+                for (int j = 0; j < WPL; ++j) {
+                    const uint32_t wj = static_cast<uint32_t>(
+                        __builtin_amdgcn_ds_bpermute(w_src, static_cast<int>(sl.w[j])));
+                    const half8_t b = unpack8(wj, half2_t{zh, zh}, half2_t{zl, zl}, uk);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        uint4 xv = {0u, 0u, 0u, 0u};
+                        if (XR % 16 == 0 || 16 * mb + col < XR)
+                            xv = *reinterpret_cast<const uint4*>(&xw[(16 * mb + col) * XST + (kq * WPL + j) * 8]);
+                        part[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(permute8(xv), b, part[mb], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[mb][e] += s * part[mb][e];
+            }
+            load(sl, g + DEPTH);                          // refill the slot
+        }
+    }
+
+    // ---- the waves' sums, added in wave order: lane l holds rows
+    //      16 mb + 4 (l / 16) + e of column l % 16 (over the x buffers,
+    //      which every wave is done with after the barrier) ----
+    __syncthreads();
+    float4_t* red = reinterpret_cast<float4_t*>(lds + ct_x_offset(ng));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) red[(wave * MB + mb) * 64 + lane] = acc[mb];
+    __syncthreads();
+    for (int i = tid; i < MB * 256; i += NW * 64) {
+        const int mb = i >> 8, l = (i >> 2) & 63, e = i & 3;
+        float sum = 0.f;
+        for (int w = 0; w < NW; ++w) sum += red[(w * MB + mb) * 64 + l][e];
+        const int row = 16 * mb + 4 * (l >> 4) + e;
+        const int n = n0 + (l & 15);
+        if (row < M && n < N) y[static_cast<int64_t>(row) * N + n] = static_cast<half_t>(sum);
+    }
+}
+
+// rows of x a launch stages: M rounded up to 4, 8, 16 or 32
+int ct_rows(int64_t M) { return M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : 32; }
+// 8 waves per block while the column tiles alone leave CUs with few waves;
+// 4 from 2.5 tiles per CU up (all blocks resident at once). Measured at
+// M = 2 (us, 8 against 4 waves): 4096 x 4096 6.2 / 6.7, 4096 x 11008
+// 10.4 / 14.0, 8192 x 28672 34.4 / 39.3; 11008 x 4096 10.2 / 10.0,
+// 13824 x 5120 15.4 / 14.6.
+int ct_waves(int64_t N, int64_t K, int group_size) {
+    if (K / group_size < 16) return 4;
+    return ceil_div(N, kCtCols) * 2 >= 5 * static_cast<int64_t>(cu_count()) ? 4 : 8;
+}
+
+size_t ct_lds_bytes(int64_t K, int group_size, int xr, int nw) {
+    const size_t pairs = static_cast<size_t>(ct_x_offset(static_cast<int>(K / group_size))) * 4;
+    const size_t xbuf = static_cast<size_t>(nw) * xr * (group_size + 8) * 2;
+    const size_t sums = static_cast<size_t>(nw) * ((xr + 15) / 16) * 64 * 16;
+    return pairs + std::max(xbuf, sums);
+}
+
+int ct_max_shared() {
+    static int cached = -1;
+    if (cached < 0) {
+        int dev = 0, v = 65536;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            v = 65536;
+        cached = v;
+    }
+    return cached;
+}
+
+template <int XR, int WPL, int NW>
+awq_status launch_ct(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
+                     int N, int K, half_t* y, hipStream_t stream) {
+    constexpr int DEPTH = XR * WPL <= 64 ? 4 : 2;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&coltile_kernel<XR, WPL, NW, DEPTH>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, ct_max_shared()) != hipSuccess)
+            return AWQ_ERR_HIP;
+        attr_set = true;
+    }
+    const size_t lds = ct_lds_bytes(K, WPL * 32, XR, NW);
+    const int64_t blocks = ceil_div(N, kCtCols);
+    hipLaunchKernelGGL((coltile_kernel<XR, WPL, NW, DEPTH>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), lds,
+                       stream, x, qweight, scales, zeros, y, M, N, K);
+    return last_launch_status();
+}
+
+template <int XR, int WPL>
+awq_status launch_ct_nw(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
+                        int N, int K, half_t* y, hipStream_t stream) {
+    if (ct_waves(N, K, WPL * 32) == 8) return launch_ct<XR, WPL, 8>(x, qweight, scales, zeros, M, N, K, y, stream);
+    return launch_ct<XR, WPL, 4>(x, qweight, scales, zeros, M, N, K, y, stream);
+}
+
+template <int WPL>
+awq_status launch_ct_mb(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
+                        int N, int K, half_t* y, hipStream_t stream) {
+    switch (ct_rows(M)) {
+        case 4: return launch_ct_nw<4, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
+        case 8: return launch_ct_nw<8, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
+        case 16: return launch_ct_nw<16, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
+        default: return launch_ct_nw<32, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
+    }
+}
+
+}  // namespace
+
+// The automatic kernel choice (awq_gemm): column tiles where they beat the
+// GEMV and the skinny kernel (us, best of the others in brackets, weights
+// past every cache): M = 4 on 4096 x 11008 10.5 (14.2), 13824 x 5120 15.5
+// (16.5); M = 8 on 4096 x 4096 6.5 (10.3), 11008 x 4096 12.1 (13.2); M = 16
+// on 4096 x 4096 7.3 (10.6), 4096 x 11008 13.1 (15.4); M = 32 on 4096 x 4096
+// 9.1 (13.0). The skinny kernel stays ahead on large layers from M = 8 up
+// (8192 x 28672 at M = 16: 35 against 49) and the GEMV at M = 2 on most.
+bool coltile_preferred(int64_t M, int64_t N, int64_t K, int group_size) {
+    if (M < 3 || !coltile_supported(M, N, K, group_size)) return false;
+    const int64_t weights = N * K;
+    if (M <= 4) return true;
+    if (M <= 16) return weights <= (int64_t{48} << 20);
+    return weights <= (int64_t{48} << 20) && ceil_div(N, kCtCols) <= 2 * static_cast<int64_t>(cu_count());
+}
+
+bool coltile_supported(int64_t M, int64_t N, int64_t K, int group_size) {
+    if (group_size < 32 || group_size > 256) return false;
+    if (M < 1 || M > kColTileMaxM || N < 1 || K < group_size || K % group_size != 0) return false;
+    // 32-bit buffer offsets: x, and one 16-column tile of packed weights
+    if (M * K * 2 >= (int64_t{1} << 31) || kCtCols * (K / 2) >= (int64_t{1} << 31)) return false;
+    return ct_lds_bytes(K, group_size, ct_rows(M), ct_waves(N, K, group_size)) <=
+           static_cast<size_t>(ct_max_shared());
+}
+
+awq_status launch_coltile(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros,
+                          int64_t M, int64_t N, int64_t K, int group_size, half_t* y, hipStream_t stream) {
+    if (M == 0 || N == 0) return AWQ_OK;
+    if (!coltile_supported(M, N, K, group_size)) return AWQ_ERR_CONFIG;
+    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    switch (group_size) {
+        case 32: return launch_ct_mb<1>(x, qweight, scales, zeros, m, n, k, y, stream);
+        case 64: return launch_ct_mb<2>(x, qweight, scales, zeros, m, n, k, y, stream);
+        case 128: return launch_ct_mb<4>(x, qweight, scales, zeros, m, n, k, y, stream);
+        case 256: return launch_ct_mb<8>(x, qweight, scales, zeros, m, n, k, y, stream);
+        default: return AWQ_ERR_CONFIG;
+    }
+}
+
+}  // namespace awq

@@ -12,7 +12,8 @@
 //    of an fp64 sum and independent of scheduling.
 //  * pow_scales: s[k] = float32(m[k] ^ alpha) with fp64 pow.
 //  * divide_columns: x'[t, k] = fp16(x[t, k] / s[k]) (IEEE fp32 divide).
-//  * sum_partials: deterministic fixed-order sum of per-tile loss partials.
+//  * sum_partials: deterministic fixed-order sum of per-tile loss partials,
+//    over many blocks when they are many.
 #include "awq_internal.h"
 
 namespace awq {
@@ -99,18 +100,24 @@ __global__ __launch_bounds__(256) void divide_columns_kernel(const half_t* __res
     reinterpret_cast<uint4*>(xs)[t] = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// Fixed-order sum of n doubles: block b adds the slice [b n / B, (b + 1) n / B)
+// (each thread a strided part, then a tree over the block) into out[b]; with
+// one block the slice is the whole range. Run as B blocks, then one block
+// over the B block sums, the result depends on n and B only.
 __global__ __launch_bounds__(256) void sum_partials_kernel(const double* __restrict__ partials, int64_t n,
                                                            double* __restrict__ out) {
     __shared__ double red[256];
+    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * n / gridDim.x;
+    const int64_t i1 = static_cast<int64_t>(blockIdx.x + 1) * n / gridDim.x;
     double s = 0.0;
-    for (int64_t i = threadIdx.x; i < n; i += 256) s += partials[i];
+    for (int64_t i = i0 + threadIdx.x; i < i1; i += 256) s += partials[i];
     red[threadIdx.x] = s;
     __syncthreads();
     for (int w = 128; w >= 1; w >>= 1) {
         if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
-    if (threadIdx.x == 0) *out = red[0];
+    if (threadIdx.x == 0) out[blockIdx.x] = red[0];
 }
 
 }  // namespace
@@ -148,7 +155,17 @@ awq_status launch_divide_columns(const half_t* x, const float* s, int64_t T, int
     return last_launch_status();
 }
 
-awq_status launch_sum_partials(const double* partials, int64_t n, double* out, hipStream_t stream) {
+awq_status launch_sum_partials(double* partials, int64_t n, double* out, hipStream_t stream) {
+    // large counts: kLossSumBlocks blocks into the scratch behind the
+    // partials, then one block over those
+    if (n >= 64 * 256) {
+        hipLaunchKernelGGL(sum_partials_kernel, dim3(kLossSumBlocks), dim3(256), 0, stream, partials, n, partials + n);
+        const awq_status st = last_launch_status();
+        if (st != AWQ_OK) return st;
+        hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(256), 0, stream, partials + n,
+                           static_cast<int64_t>(kLossSumBlocks), out);
+        return last_launch_status();
+    }
     hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(256), 0, stream, partials, n, out);
     return last_launch_status();
 }
