@@ -71,24 +71,34 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic():
-    """HBM bytes per launch of the roofline kernel, from the FETCH_SIZE and
-    WRITE_SIZE counter runs recorded under profiles/ (scaled by the same
-    counters read on a copy of known size). None once the kernel source has
-    changed since the counters were taken."""
+COUNTERS_FILE = os.path.join("profiles", "counters_gemv_gemm.json")
+GEMV_SOURCE = os.path.join("weight_only_int4_quantize_amd", "csrc", "gemv.hip")
+
+
+def source_sha256(rel):
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", "gemv_m1_11008x4096_counters.json")
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(linears):
+    """HBM bytes of one decode step, from the FETCH_SIZE and WRITE_SIZE
+    counter runs summarized under profiles/ (each scaled by the same counter
+    read on a copy of known size), summed over the step's launches. None
+    once the GEMV source has changed since the counters were taken."""
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, COUNTERS_FILE)) as f:
             rec = json.load(f)
-        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-            current = hashlib.sha256(f.read()).hexdigest()
-    except (OSError, KeyError, ValueError):
+        if source_sha256(GEMV_SOURCE) != rec.get("gemv_source_sha256"):
+            return None, None
+        by_shape = {(g["N"], g["K"]): g for g in rec["groups"] if g["kind"] == "gemv"}
+        total = sum(by_shape[(N, K)]["traffic_bytes"] for (_, N, K) in linears)
+        calib = next(g for g in rec["groups"] if g["kind"] == "copy")
+    except (OSError, KeyError, ValueError, StopIteration):
         return None, None
-    if current != rec.get("source_sha256"):
-        return None, None
-    return int(rec["traffic_bytes_per_launch"]), rec["copy_calibration"]
+    return int(total), {"copy_bytes": calib["bytes"], "fetch_factor": calib.get("fetch_factor"),
+                        "write_factor": calib.get("write_factor")}
 
 
 class Bench:
@@ -326,6 +336,108 @@ class Bench:
             del cps, gr
         torch.cuda.synchronize()
         return out
+
+    def rotated_product(self, M, N, K, g, lay, workspace=None, reps_per_copy=2):
+        """Back-to-back launches of one W4A16 product with the weights rotated
+        over enough copies (> 1.2 GB) that no cache holds them; returns the
+        time per launch in seconds."""
+        torch, awq = self.torch, self.awq
+        qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), g)
+        x = self.d(lay["x"])
+        nbytes = gemv_bytes(M, N, K, g)
+        n_copies = max(2, int(np.ceil(1.2e9 / nbytes)))
+        cps = [(qw.clone(), sc.clone(), zr.clone()) for _ in range(n_copies)]
+        del qw, sc, zr
+        y = torch.empty((M, N), dtype=torch.float16, device=self.dev)
+
+        def one(i):
+            q = cps[i % len(cps)]
+            awq.awq_gemm(x, q[0], q[1], q[2], g, out=y, workspace=workspace)
+
+        for i in range(4):
+            one(i)
+        gr = self.capture(one, reps_per_copy * n_copies)
+        gr.replay()
+        t = min(self.time(lambda _: gr.replay()) for _ in range(3)) / (reps_per_copy * n_copies)
+        del cps, gr
+        torch.cuda.synchronize()
+        return t
+
+    def run_sweep(self):
+        """The larger shapes and group sizes of the 13B / 70B sweep: M = 1 (the
+        GEMV) and M = 32 (the skinny kernel) at group sizes 64 and 128, in
+        effective HBM GB/s with the weights rotated past every cache, and
+        M = 512 (the MFMA GEMM) at group size 64 in TFLOP/s (group size 128
+        is in the GEMM section)."""
+        ws = self.awq.gemm_workspace(512, 1, 1, self.dev)
+        out = {}
+        for (N, K) in synth.SWEEP_SHAPES:
+            for g in synth.SWEEP_G:
+                for M in (1, 32):
+                    lay = synth.sweep_layer(N, K, M, g)
+                    t = self.rotated_product(M, N, K, g, lay, workspace=ws)
+                    b = gemv_bytes(M, N, K, g)
+                    key = f"M{M}_{N}x{K}_G{g}"
+                    out[key] = {"us": round(t * 1e6, 2), "bytes": b, "GB/s": round(b / t / 1e9, 1),
+                                "frac_of_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+                                "kernel": "gemv" if M == 1 else "skinny"}
+                    log(f"sweep {key}: {t * 1e6:.2f} us, {b / t / 1e9:.0f} GB/s")
+            M, g = 512, 64
+            lay = synth.sweep_layer(N, K, M, g)
+            qw, sc, zr = self.awq.awq_quantize(self.d(lay["w"]), g)
+            x = self.d(lay["x"])
+            y = self.torch.empty((M, N), dtype=self.torch.float16, device=self.dev)
+
+            def gm(i, x=x, qw=qw, sc=sc, zr=zr, y=y, g=g):
+                self.awq.awq_gemm(x, qw, sc, zr, g, out=y, workspace=ws)
+
+            self.warm(gm)
+            t = self.time(gm, 20) / 20
+            flop = 2.0 * M * N * K
+            key = f"M{M}_{N}x{K}_G{g}"
+            out[key] = {"us": round(t * 1e6, 2), "TFLOP/s": round(flop / t / 1e12, 1),
+                        "frac_of_f16_peak": round(flop / t / 1e12 / F16_MFMA_PEAK_TFLOPS, 4), "kernel": "gemm"}
+            log(f"sweep {key}: {t * 1e6:.1f} us, {flop / t / 1e12:.0f} TFLOP/s")
+        return out
+
+    def run_shard(self):
+        """One GPU's share of the decode layer under 8-way column (output)
+        parallelism: every projection keeps 1/8 of its rows (q/k/v/o
+        512x4096, gate/up 1376x4096, down 512x11008), so each GPU streams
+        1/8 of the weights with the same GEMV; the step's seven launches are
+        timed as in the decode step. The all-gather of y is not part of it
+        (one GPU)."""
+        torch, awq = self.torch, self.awq
+        layer = [(n, N // 8, K) for (n, N, K) in synth.LLAMA7B_LAYER]
+        step_bytes = sum(gemv_bytes(1, N, K) for (_, N, K) in layer)
+        n_copies = max(2, int(np.ceil(1.2e9 / step_bytes)))
+        base = {}
+        for (_, N, K) in layer:
+            if (N, K) not in base:
+                lay = synth.make_layer(N, K, 1, seed=[8, N, K], w_std=0.02)
+                qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), G)
+                base[(N, K)] = (qw, sc, zr, self.d(lay["x"]))
+        copies = [[(*[t.clone() for t in base[(N, K)][:3]], base[(N, K)][3],
+                    torch.empty((1, N), dtype=torch.float16, device=self.dev)) for (_, N, K) in layer]
+                  for _ in range(n_copies)]
+
+        def step(i):
+            for (qw, sc, zr, x, y) in copies[i % n_copies]:
+                awq.awq_gemm(x, qw, sc, zr, G, out=y)
+
+        for i in range(4):
+            step(i)
+        g = self.capture(step, n_copies)
+        g.replay()
+        reps = 20
+        t = min(self.time(lambda _: [g.replay() for _r in range(reps)]) for _ in range(3)) / (reps * n_copies)
+        del copies, g
+        torch.cuda.synchronize()
+        log(f"tp8 shard step: {t * 1e6:.2f} us, {step_bytes / t / 1e9:.0f} GB/s")
+        return {"workload": "llama7b_decoder_layer_m1_int4_g128, one GPU's share under 8-way column parallelism",
+                "linears": [f"{n}:{N}x{K}" for (n, N, K) in layer], "step_bytes": step_bytes,
+                "us_per_step": round(t * 1e6, 2), "GB/s": round(step_bytes / t / 1e9, 1),
+                "frac_of_hbm_peak": round(step_bytes / t / 1e9 / HBM_PEAK_GBS, 4)}
 
     def run_group_sizes(self):
         """The roofline GEMV shape (11008x4096, M = 1) at every supported group
@@ -593,13 +705,73 @@ class Bench:
         return {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES, "us": round(t * 1e6, 1),
                 "GB/s": round(gbs, 1)}
 
+    # ------------------------------------------------------------ counter runs
+    def run_counters(self, reps=4):
+        """Fixed launches in a known order for rocprofv3 --pmc runs (one counter
+        pass per run): a 1 GiB copy (the FETCH_SIZE / WRITE_SIZE calibration),
+        the decode and fused GEMV shapes at M = 1 (weights rotated over `reps`
+        copies, so every launch fetches from HBM), the prefill GEMM shapes at
+        M = 2048 and the sweep at M = 512. Prints the manifest (label, work
+        and launch count per group, in order) as one JSON line on stdout; the
+        summary mode matches it to the counter rows."""
+        torch, awq = self.torch, self.awq
+        manifest = []
+        a = torch.empty(COPY_BYTES // 2, dtype=torch.float16, device=self.dev)
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            b.copy_(a)
+        manifest.append({"label": "copy_1GiB", "kind": "copy", "bytes": COPY_BYTES, "launches": 2})
+        del a, b
+        torch.cuda.synchronize()
+        gemv_shapes = list(synth.DECODE_SHAPES) + [(N, K) for (_, N, K) in synth.LLAMA7B_LAYER_FUSED
+                                                    if (N, K) not in synth.DECODE_SHAPES]
+        for (N, K) in gemv_shapes:
+            lay = synth.decode_layer(N, K, 1)
+            qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), G)
+            x = self.d(lay["x"])
+            cps = [(qw.clone(), sc.clone(), zr.clone()) for _ in range(reps)]
+            y = torch.empty((1, N), dtype=torch.float16, device=self.dev)
+            torch.cuda.synchronize()
+            for i in range(reps):
+                awq.awq_gemm(x, *cps[i], G, out=y)
+            torch.cuda.synchronize()
+            manifest.append({"label": f"gemv_M1_{N}x{K}", "kind": "gemv", "M": 1, "N": N, "K": K,
+                             "bytes": gemv_bytes(1, N, K), "launches": reps})
+            del cps, qw, sc, zr
+        ws = awq.gemm_workspace(synth.PREFILL_M, 11008, 11008, self.dev)
+        gemm_shapes = [(synth.PREFILL_M, N, K) for (N, K) in synth.PREFILL_SHAPES] + \
+                      [(512, N, K) for (N, K) in synth.SWEEP_SHAPES]
+        for (M, N, K) in gemm_shapes:
+            lay = synth.prefill_layer(N, K) if M == synth.PREFILL_M else synth.sweep_layer(N, K, M, G)
+            qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), G)
+            x = self.d(lay["x"])
+            y = torch.empty((M, N), dtype=torch.float16, device=self.dev)
+            torch.cuda.synchronize()
+            for i in range(reps):
+                awq.awq_gemm(x, qw, sc, zr, G, out=y, workspace=ws)
+            torch.cuda.synchronize()
+            manifest.append({"label": f"gemm_{M}x{N}x{K}", "kind": "gemm", "M": M, "N": N, "K": K,
+                             "flop": 2 * M * N * K, "launches": reps})
+        print(json.dumps({"manifest": manifest}))
+
     # ------------------------------------------------------------ CPU oracle
     def run_cpu_baseline(self):
+        """The oracle as it stands, timed on this host's cores: its BLAS uses
+        as many threads as the process may run on (os.sched_getaffinity);
+        the record names that count and the BLAS library."""
         import oracle
 
+        cores = len(os.sched_getaffinity(0))
+        blas = "unknown"
         try:
-            from threadpoolctl import threadpool_info
-            blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+            from threadpoolctl import threadpool_info, threadpool_limits
+            threadpool_limits(limits=cores, user_api="blas")
+            info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+            blas_threads = max([p.get("num_threads", 1) for p in info] or [1])
+            if info:
+                blas = f"{info[0].get('internal_api')} {info[0].get('version')} ({info[0].get('threading_layer')})"
         except Exception:
             blas_threads = 1
         t_cpu, b_cpu, n = 0.0, 0, 0
@@ -619,9 +791,128 @@ class Bench:
         value = b_cpu / t_cpu / 1e9
         log(f"cpu oracle: {value:.2f} GB/s over {n} products")
         return {"value": round(value, 3), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+                "affinity_cores": cores, "blas": blas,
                 "sample": f"{n} M=1 products over the 7 Llama-7B linear shapes, each the oracle's fp64 "
-                          f"dequantize (single-threaded NumPy) + fp64 matrix-vector product "
-                          f"({blas_threads} BLAS threads); {t_cpu:.1f} s of CPU work"}
+                          f"dequantize (NumPy elementwise, one thread) + fp64 matrix-vector product "
+                          f"({blas_threads} BLAS threads, {blas}); {t_cpu:.1f} s of CPU work"}
+
+
+# ---------------------------------------------------------------- profile summaries
+# Run on the CSV output of rocprofv3 (--output-format csv -d DIR); they read
+# nothing else and touch no GPU.
+
+def _csv_rows(dirs, suffix):
+    import csv
+    import glob
+
+    rows = []
+    for d in dirs:
+        for path in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+            with open(path, newline="") as f:
+                rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _short(name, n=90):
+    return name if len(name) <= n else name[:n - 3] + "..."
+
+
+def summarize_trace(dirs, out_path, command):
+    """Per (kernel, grid) dispatch counts and start-to-end durations of a
+    --kernel-trace run, sorted by total time, as markdown."""
+    rows = _csv_rows(dirs, "kernel_trace.csv")
+    groups = {}
+    for r in rows:
+        grid = int(r.get("Grid_Size_X", r.get("Grid_Size", 0))) * int(r.get("Grid_Size_Y", 1) or 1) * \
+            int(r.get("Grid_Size_Z", 1) or 1)
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault((r["Kernel_Name"], grid), []).append(dur)
+    lines = ["# Kernel trace", "", "Command (from the repository root, on one MI355X):", "", f"    {command}",
+             "", "Per (kernel, grid): dispatches and start-to-end durations, sorted by total time.", "",
+             "| kernel | grid (threads) | dispatches | avg us | median us | total ms |", "|---|---|---|---|---|---|"]
+    for (name, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        d = np.array(d)
+        lines.append(f"| `{_short(name)}` | {grid} | {d.size} | {d.mean():.2f} | {np.median(d):.2f} | "
+                     f"{d.sum() / 1e3:.2f} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def summarize_counters(dirs, manifest_path, out_path, commands):
+    """Counter values per manifest group of a `bench.py --only counters` run:
+    the dispatches of each group are the next `launches` dispatches whose
+    kernel matches the group's kind, in dispatch order. Writes JSON with the
+    per-dispatch averages and the derived figures (HBM bytes from
+    FETCH_SIZE / WRITE_SIZE scaled by the copy calibration; MFMA FLOPs from
+    SQ_INSTS_MFMA x 32768, checked against 2MNK; MFMA-busy % = 100 x
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs))."""
+    with open(manifest_path) as f:
+        text = f.read()
+    manifest = json.loads([ln for ln in text.splitlines() if ln.startswith('{"manifest"')][-1])["manifest"]
+    match = {"copy": ("copy", "Copy"), "gemv": ("gemv_kernel", "skinny_kernel"),
+             "gemm": ("gemm_kernel", "skinny_kernel")}
+    out = [dict(g, avg={}) for g in manifest]
+    for d in dirs:                     # one counter pass (one run of the same launches) per directory
+        per_dispatch = {}
+        for r in _csv_rows([d], "counter_collection.csv"):
+            key = int(r["Dispatch_Id"])
+            e = per_dispatch.setdefault(key, {"kernel": r["Kernel_Name"], "grid": int(r.get("Grid_Size", 0)),
+                                              "counters": {}})
+            e["counters"][r["Counter_Name"]] = e["counters"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                e["counters"]["duration_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        order = sorted(per_dispatch)
+        pos = 0
+        for o in out:
+            picked = []
+            while pos < len(order) and len(picked) < o["launches"]:
+                e = per_dispatch[order[pos]]
+                pos += 1
+                if any(m in e["kernel"] for m in match[o["kind"]]):
+                    picked.append(e)
+            if len(picked) < o["launches"]:
+                raise SystemExit(f"{d}: counter rows end before group {o['label']}")
+            if o.get("grid", picked[0]["grid"]) != picked[0]["grid"]:
+                raise SystemExit(f"{d}: group {o['label']} matched another grid")
+            o["kernel"], o["grid"] = _short(picked[0]["kernel"], 120), picked[0]["grid"]
+            for c in sorted({c for e in picked for c in e["counters"]}):
+                o["avg"][c] = float(np.mean([e["counters"].get(c, 0.0) for e in picked]))
+    calib = next((o for o in out if o["kind"] == "copy"), None)
+    if calib is not None:
+        fk, wk = calib["avg"].get("FETCH_SIZE"), calib["avg"].get("WRITE_SIZE")
+        fetch_factor = calib["bytes"] / (fk * 1024) if fk else None
+        write_factor = calib["bytes"] / (wk * 1024) if wk else None
+        for o in out:
+            if o["kind"] != "gemv":
+                continue
+            if fetch_factor and "FETCH_SIZE" in o["avg"]:
+                o["fetch_bytes"] = round(o["avg"]["FETCH_SIZE"] * 1024 * fetch_factor)
+            if write_factor and "WRITE_SIZE" in o["avg"]:
+                o["write_bytes"] = round(o["avg"]["WRITE_SIZE"] * 1024 * write_factor)
+            if "fetch_bytes" in o and "write_bytes" in o:
+                o["traffic_bytes"] = o["fetch_bytes"] + o["write_bytes"]
+                o["traffic_over_algorithmic"] = round(o["traffic_bytes"] / o["bytes"], 4)
+        calib["fetch_factor"], calib["write_factor"] = fetch_factor, write_factor
+    simds = 4 * 256
+    for o in out:
+        c = o["avg"]
+        if "SQ_INSTS_MFMA" in c:
+            o["mfma_flop"] = c["SQ_INSTS_MFMA"] * 32768
+            if "flop" in o:
+                o["mfma_flop_equals_2MNK"] = abs(o["mfma_flop"] - o["flop"]) <= 1e-9 * o["flop"]
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and c.get("GRBM_GUI_ACTIVE"):
+            o["mfma_busy_pct"] = round(100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * simds), 2)
+        if "MfmaUtil" in c:
+            o["mfma_util_pct"] = round(c["MfmaUtil"], 2)      # rocprofv3's own derived metric
+        if "TA_BUSY_avr" in c and c.get("GRBM_GUI_ACTIVE"):
+            o["ta_busy_pct"] = round(100.0 * c["TA_BUSY_avr"] / c["GRBM_GUI_ACTIVE"], 2)
+        if c.get("GRBM_GUI_ACTIVE") and c.get("duration_us"):
+            o["gui_active_cycles_per_us"] = round(c["GRBM_GUI_ACTIVE"] / c["duration_us"], 1)
+    with open(out_path, "w") as f:
+        json.dump({"commands": commands, "gemv_source_sha256": source_sha256(GEMV_SOURCE),
+                   "gemm_source_sha256": source_sha256(os.path.join("weight_only_int4_quantize_amd", "csrc",
+                                                                    "gemm.hip")),
+                   "groups": out}, f, indent=1)
 
 
 def main():
@@ -632,9 +923,22 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true")
     ap.add_argument("--only", choices=["decode", "decode-fused", "decode-model", "gemv-roofline", "skinny", "gemm", "quantize",
-                                       "search", "copy", "w8"],
+                                       "search", "copy", "w8", "sweep", "shard", "counters"],
                     help="run one section (for profiler runs); timings go to stderr")
+    ap.add_argument("--summarize-trace", nargs="+", metavar="DIR",
+                    help="summarize rocprofv3 kernel-trace CSVs under DIR into --out (no GPU)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="summarize rocprofv3 counter CSVs under DIR (a --only counters run) into --out")
+    ap.add_argument("--manifest", help="stdout of the --only counters run (its manifest line)")
+    ap.add_argument("--out", help="summary file to write")
+    ap.add_argument("--command", action="append", default=[], help="profiling command(s) to record in the summary")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, " ; ".join(args.command))
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.manifest, args.out, args.command)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the library has no multi-GPU "
                                    "path (--gpus must be 1)"}))
@@ -662,6 +966,12 @@ def main():
             b.run_search()
         elif args.only == "w8":
             b.run_w8()
+        elif args.only == "sweep":
+            b.run_sweep()
+        elif args.only == "shard":
+            b.run_shard()
+        elif args.only == "counters":
+            b.run_counters()
         else:
             b.run_copy()
         return
@@ -669,12 +979,13 @@ def main():
     b.setup_decode()
     value, ms_per_step = b.run_decode()
     per_shape = b.run_gemv_shapes(synth.DECODE_SHAPES)
-    roof = per_shape[f"{ROOFLINE_SHAPE[0]}x{ROOFLINE_SHAPE[1]}"]
     del b.copies
     fused = b.run_decode_fused()
     model = b.run_decode_model()
     floor_us = b.run_launch_floor()
     skinny = b.run_skinny()
+    sweep = b.run_sweep()
+    shard = b.run_shard()
     groups = b.run_group_sizes()
     w8 = b.run_w8()
     copy = b.run_copy()
@@ -683,7 +994,7 @@ def main():
     search = None if args.no_search else b.run_search()
     cpu = None if args.no_cpu_baseline else b.run_cpu_baseline()
 
-    traffic, calib = measured_traffic()
+    traffic, calib = measured_traffic(b.linears)
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -700,13 +1011,15 @@ def main():
         "config": {"workload": "llama7b_decoder_layer_decode_m1_int4_g128", "M": 1, "group_size": G,
                    "linears": [f"{n}:{N}x{K}" for (n, N, K) in b.linears], "weight_copies": b.n_copies,
                    "step_bytes": b.step_bytes},
-        "roofline": {"bound": "hbm", "achieved": roof["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(roof["GB/s"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "traffic_unit": "bytes per launch (FETCH_SIZE x fetch_factor + WRITE_SIZE x write_factor)",
+        "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "HBM bytes per step: FETCH_SIZE x fetch_factor + WRITE_SIZE x "
+                                     "write_factor summed over the step's seven GEMV launches",
                      "traffic_calibration": calib,
-                     "kernel": f"gemv M=1 {ROOFLINE_SHAPE[0]}x{ROOFLINE_SHAPE[1]} (gate/up projection)",
-                     "bytes_per_launch": roof["bytes"], "launch_us": roof["us"],
-                     "frac_of_copy_bandwidth": round(roof["GB/s"] / copy["GB/s"], 4),
+                     "kernel": "gemv, the seven M=1 launches of one decode step (one graph replay)",
+                     "bytes_per_launch": b.step_bytes, "launch_us": round(ms_per_step * 1e3, 3),
+                     "per_shape": {k: {**v, "frac": round(v["GB/s"] / HBM_PEAK_GBS, 4)} for k, v in per_shape.items()},
+                     "frac_of_copy_bandwidth": round(value / copy["GB/s"], 4),
                      "graph_launch_floor_us": floor_us},
         "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "hbm_copy_1GiB": copy,
@@ -714,6 +1027,8 @@ def main():
         "decode_fused": fused,
         "decode_model": model,
         "skinny_batched_decode": skinny,
+        "sweep_13b_70b": sweep,
+        "tp8_shard_1gpu": shard,
         "gemv_group_sizes": groups,
         "w8a16": w8,
         "gemm": gemm,
