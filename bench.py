@@ -331,7 +331,7 @@ class Bench:
             key = f"M{M}_{N}x{K}"
             out[key] = {"us": round(t * 1e6, 2), "GB/s": round(nbytes / t / 1e9, 1),
                         "frac_of_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
-                        "kernel": "gemv" if M <= 4 else "skinny"}
+                        "kernel": awq.gemm_kernel(M, N, K, g, workspace=True)}
             log(f"batched decode {key}: {t * 1e6:.2f} us, {nbytes / t / 1e9:.0f} GB/s")
             del cps, gr
         torch.cuda.synchronize()
@@ -380,7 +380,7 @@ class Bench:
                     key = f"M{M}_{N}x{K}_G{g}"
                     out[key] = {"us": round(t * 1e6, 2), "bytes": b, "GB/s": round(b / t / 1e9, 1),
                                 "frac_of_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
-                                "kernel": "gemv" if M == 1 else "skinny"}
+                                "kernel": self.awq.gemm_kernel(M, N, K, g, workspace=True)}
                     log(f"sweep {key}: {t * 1e6:.2f} us, {b / t / 1e9:.0f} GB/s")
             M, g = 512, 64
             lay = synth.sweep_layer(N, K, M, g)

@@ -170,6 +170,16 @@ awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight,
                          void* y_f16, int path, void* stream);
 
 /*
+ * awq_gemm_kernel - the kernel a linear-layer call of this shape runs:
+ * 1 = GEMV, 2 = MFMA GEMM, 3 = skinny MFMA kernel, 4 = column tiles; -1
+ * when the requested path cannot take it or an argument is invalid.
+ * path as awq_gemm_path (0 = automatic); have_workspace != 0 for a call
+ * with a workspace (awq_gemm_ex) or for awq_gemm_noalloc. No GPU work.
+ */
+int awq_gemm_kernel(int64_t M, int64_t N, int64_t K, int group_size, int path,
+                    int have_workspace);
+
+/*
  * awq_gemm_ex - awq_gemm_path with a caller-owned device workspace, which
  * lets the MFMA kernels split the K loop of output tiles across thread
  * blocks when the tile count would leave the GPU's resident blocks partly

@@ -184,6 +184,24 @@ def test_scale_search_checks(L):
     assert s(FAKE_ODD, FAKE, 256, 512, 1024, 128, a, 20, FAKE, need, lp, bp, FAKE, None) == ALIGN
 
 
+def test_kernel_choice(L):
+    """awq_gemm_kernel names the kernel each path takes, and refuses what a
+    path cannot run (host logic only)."""
+    k = L.awq_gemm_kernel
+    k.restype = ctypes.c_int
+    k.argtypes = [ctypes.c_int64] * 3 + [ctypes.c_int] * 3
+    assert k(1, 4096, 4096, 128, 0, 0) == 1            # decode: the GEMV
+    assert k(4, 4096, 11008, 128, 0, 0) == 4           # column tiles
+    assert k(16, 4096, 4096, 128, 0, 1) == 4
+    assert k(16, 8192, 28672, 128, 0, 1) == 3          # large layer: the skinny kernel
+    assert k(2048, 11008, 4096, 128, 0, 1) == 2        # prefill: the GEMM
+    assert k(9, 64, 128, 64, 1, 0) == -1               # GEMV is M <= 8
+    assert k(33, 64, 128, 64, 4, 0) == -1              # column tiles are M <= 32
+    assert k(16, 64, 512, 512, 4, 0) == -1             # and G <= 256
+    assert k(4, 64, 100, 64, 0, 0) == -1               # K % G
+    assert k(0, 64, 128, 64, 0, 0) == -1
+
+
 def test_salient_count_is_the_oracles(L):
     """The library's default salient-channel count (round(K / 100), ties to
     even) equals the oracle's for every width of the workloads and at ties."""

@@ -76,6 +76,8 @@ def load() -> ctypes.CDLL:
     L.awq_gemm_workspace_bytes.argtypes = [c_i64, c_i64, c_i64]
     L.awq_gemm_ex.restype = c_int
     L.awq_gemm_ex.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_int, c_vp, c_sz, c_vp]
+    L.awq_gemm_kernel.restype = c_int
+    L.awq_gemm_kernel.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int]
     L.awq_gemm_noalloc.restype = c_int
     L.awq_gemm_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_int, c_vp]
     L.awq_activation_absmean_workspace_bytes.restype = c_sz
@@ -197,6 +199,18 @@ def awq_quantize(w, group_size: int = 128, channel_scale=None, out=None, symmetr
                                  _ptr(scales), _ptr(zeros), _stream(w.device))
         _check("awq_quantize", st)
     return qweight, scales, zeros
+
+
+KERNEL_NAMES = {1: "gemv", 2: "gemm", 3: "skinny", 4: "coltile"}
+
+
+def gemm_kernel(M: int, N: int, K: int, group_size: int = 128, path: int = PATH_AUTO,
+                workspace: bool = False) -> str:
+    """Name of the kernel awq_gemm runs for this shape (awq_gemm_kernel)."""
+    k = int(load().awq_gemm_kernel(M, N, K, group_size, path, int(workspace)))
+    if k < 0:
+        raise AwqError("awq_gemm_kernel", 4, "the path cannot take this shape")
+    return KERNEL_NAMES[k]
 
 
 def gemm_workspace_bytes(M: int, N: int, K: int) -> int:

@@ -207,6 +207,30 @@ awq_status device_scratch(void** out, hipStream_t stream) {
     return AWQ_OK;
 }
 
+// The kernel a linear-layer call runs (1 GEMV, 2 GEMM, 3 skinny, 4 column
+// tiles), or -1 when the requested path cannot take the shape. Automatic
+// (path 0): the column tiles where they measured fastest; otherwise the GEMV
+// up to 4 rows; the skinny kernel up to 64 rows (and below 5 rows where the
+// GEMV's staged x does not fit the LDS), but below 9 rows only where it runs
+// without K phases if the GEMV can run (the phased form, one block per
+// column tile, is 2-3x slower than the GEMV there and 2-3x faster than the
+// GEMM tile everywhere); else the GEMM.
+int choose_path(int64_t M, int64_t N, int64_t K, int group_size, int path, bool have_workspace) {
+    const bool gemv_ok = gemv_supported(M, K);
+    bool skinny_phased = false;
+    const bool skinny_ok = skinny_supported(M, N, K, group_size, have_workspace, &skinny_phased);
+    switch (path) {
+        case 1: return gemv_ok ? 1 : -1;
+        case 2: return 2;
+        case 3: return skinny_ok ? 3 : -1;
+        case 4: return coltile_supported(M, N, K, group_size) ? 4 : -1;
+        default: break;
+    }
+    if (coltile_preferred(M, N, K, group_size)) return 4;
+    if (skinny_ok && (M > 4 || !gemv_ok) && !(skinny_phased && gemv_ok)) return 3;
+    return gemv_ok ? 1 : 2;
+}
+
 // The linear layer behind awq_gemm_ex and awq_gemm_noalloc: checks, then
 // the kernel choice. workspace (may be NULL) feeds the skinny kernel's K
 // splits and, when split_gemm is set, the GEMM's stream-K partials. With
@@ -231,25 +255,11 @@ awq_status gemm_dispatch(const void* x_f16, const uint32_t* qweight, const void*
     const half_t* sc = static_cast<const half_t*>(scales_f16);
     const half_t* zr = static_cast<const half_t*>(zeros_f16);
     half_t* y = static_cast<half_t*>(y_f16);
-    const bool gemv_ok = gemv_supported(M, K);
-    bool skinny_phased = false;
-    const bool skinny_ok =
-        skinny_supported(M, N, K, group_size, workspace != nullptr || library_scratch, &skinny_phased);
-    if (path == 1 && !gemv_ok) return AWQ_ERR_CONFIG;
-    if (path == 3 && !skinny_ok) return AWQ_ERR_CONFIG;
-    if (path == 4 && !coltile_supported(M, N, K, group_size)) return AWQ_ERR_CONFIG;
-    if (path == 4 || (path == 0 && coltile_preferred(M, N, K, group_size)))
-        return launch_coltile(x, qweight, sc, zr, M, N, K, group_size, y, stream);
-    // automatic: the column tiles where they measured fastest (above);
-    // otherwise the GEMV up to 4 rows; the skinny kernel up to 64 rows (and
-    // below 5 rows where the GEMV's staged x does not fit the LDS), but
-    // below 9 rows only where it runs without K phases if the GEMV can run
-    // (the phased form, one block per column tile, is 2-3x slower than the
-    // GEMV there and 2-3x faster than the GEMM tile everywhere); else the GEMM
-    const bool use_skinny =
-        path == 3 || (path == 0 && skinny_ok && (M > 4 || !gemv_ok) && !(skinny_phased && gemv_ok));
-    const bool use_gemv = path == 1 || (path == 0 && gemv_ok && !use_skinny);
-    if (use_gemv) return launch_gemv(x, qweight, sc, zr, M, N, K, group_size, y, stream);
+    const int chosen = choose_path(M, N, K, group_size, path, workspace != nullptr || library_scratch);
+    if (chosen < 0) return AWQ_ERR_CONFIG;
+    const bool use_skinny = chosen == 3;
+    if (chosen == 4) return launch_coltile(x, qweight, sc, zr, M, N, K, group_size, y, stream);
+    if (chosen == 1) return launch_gemv(x, qweight, sc, zr, M, N, K, group_size, y, stream);
     if (!use_skinny && !split_gemm) workspace = nullptr;
     if (use_skinny && library_scratch) {
         if (skinny_workspace_bytes(M, N, K) > kNoAllocScratchBytes) return AWQ_ERR_WORKSPACE;
@@ -337,6 +347,12 @@ awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight, const void*
                          void* y_f16, int path, void* stream) {
     return awq_gemm_ex(x_f16, qweight, scales_f16, zeros_f16, M, N, K, group_size, y_f16, path, nullptr, 0,
                        stream);
+}
+
+int awq_gemm_kernel(int64_t M, int64_t N, int64_t K, int group_size, int path, int have_workspace) {
+    if (check_dims(N, K, group_size) != AWQ_OK || path < 0 || path > 4) return -1;
+    if (M < 1 || N < 1 || M > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return -1;
+    return choose_path(M, N, K, group_size, path, have_workspace != 0);
 }
 
 awq_status awq_gemm_noalloc(const void* x_f16, const uint32_t* qweight, const void* scales_f16,
