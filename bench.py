@@ -883,7 +883,7 @@ def summarize_counters(dirs, manifest_path, out_path, commands):
         fetch_factor = calib["bytes"] / (fk * 1024) if fk else None
         write_factor = calib["bytes"] / (wk * 1024) if wk else None
         for o in out:
-            if o["kind"] != "gemv":
+            if o["kind"] == "copy":
                 continue
             if fetch_factor and "FETCH_SIZE" in o["avg"]:
                 o["fetch_bytes"] = round(o["avg"]["FETCH_SIZE"] * 1024 * fetch_factor)
@@ -891,23 +891,54 @@ def summarize_counters(dirs, manifest_path, out_path, commands):
                 o["write_bytes"] = round(o["avg"]["WRITE_SIZE"] * 1024 * write_factor)
             if "fetch_bytes" in o and "write_bytes" in o:
                 o["traffic_bytes"] = o["fetch_bytes"] + o["write_bytes"]
-                o["traffic_over_algorithmic"] = round(o["traffic_bytes"] / o["bytes"], 4)
+                if "bytes" in o:
+                    o["traffic_over_algorithmic"] = round(o["traffic_bytes"] / o["bytes"], 4)
+                elif o["kind"] == "gemm":
+                    # x, packed weights, fp16 scale and zero per group (G = 128), y
+                    M, N, K = o["M"], o["N"], o["K"]
+                    o["algorithmic_bytes"] = M * K * 2 + N * K // 2 + N * (K // G) * 4 + M * N * 2
+                    o["traffic_over_algorithmic"] = round(o["traffic_bytes"] / o["algorithmic_bytes"], 4)
         calib["fetch_factor"], calib["write_factor"] = fetch_factor, write_factor
-    simds = 4 * 256
+    # The CSV's GRBM_GUI_ACTIVE is the sum over the 8 XCDs' GRBMs (its rate
+    # per us of dispatch is 8 x the clock), so one XCD's active cycles, the
+    # denominator of a busy percentage, are an eighth of it (rocprofv3's
+    # MfmaUtil takes the max over the XCDs, which agrees).
+    xcds, simds = 8, 4 * 256
     for o in out:
         c = o["avg"]
         if "SQ_INSTS_MFMA" in c:
             o["mfma_flop"] = c["SQ_INSTS_MFMA"] * 32768
             if "flop" in o:
                 o["mfma_flop_equals_2MNK"] = abs(o["mfma_flop"] - o["flop"]) <= 1e-9 * o["flop"]
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and c.get("GRBM_GUI_ACTIVE"):
-            o["mfma_busy_pct"] = round(100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * simds), 2)
+        active = c.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and active:
+            o["mfma_busy_pct"] = round(100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * simds), 2)
         if "MfmaUtil" in c:
             o["mfma_util_pct"] = round(c["MfmaUtil"], 2)      # rocprofv3's own derived metric
-        if "TA_BUSY_avr" in c and c.get("GRBM_GUI_ACTIVE"):
-            o["ta_busy_pct"] = round(100.0 * c["TA_BUSY_avr"] / c["GRBM_GUI_ACTIVE"], 2)
-        if c.get("GRBM_GUI_ACTIVE") and c.get("duration_us"):
-            o["gui_active_cycles_per_us"] = round(c["GRBM_GUI_ACTIVE"] / c["duration_us"], 1)
+        if "TA_BUSY_avr" in c and active:
+            o["ta_busy_pct"] = round(100.0 * c["TA_BUSY_avr"] / active, 2)
+        if active and c.get("duration_us") and o["kind"] != "gemv":
+            # one XCD's active cycles per us of dispatch (long dispatches only:
+            # the active count also covers a dispatch's start-up)
+            o["clock_mhz"] = round(active / c["duration_us"], 1)
+    lines = ["# Counters of the GEMV and GEMM launches", "", "Commands (from the repository root, on one MI355X):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "Per launch (average over the group's dispatches). HBM bytes = FETCH_SIZE x fetch factor + "
+              "WRITE_SIZE x write factor (both from the 1 GiB copy); algorithmic bytes as in bench.py. "
+              "MFMA FLOPs = SQ_INSTS_MFMA x 32768. MfmaUtil is rocprofv3's derived metric.", "",
+              "| launch | grid | HBM bytes | / algorithmic | MFMA FLOPs = 2MNK | MfmaUtil % | TA busy % | clock MHz |",
+              "|---|---|---|---|---|---|---|---|"]
+    for o in out:
+        if o["kind"] == "copy":
+            lines.append(f"| copy 1 GiB (calibration: fetch x{o.get('fetch_factor', 0):.3f}, write "
+                         f"x{o.get('write_factor', 0):.3f}) | {o['grid']} | | | | | {o.get('ta_busy_pct', '')} | "
+                         f"{o.get('clock_mhz', '')} |")
+            continue
+        lines.append(f"| {o['label']} | {o['grid']} | {o.get('traffic_bytes', '')} | {o.get('traffic_over_algorithmic', '')} "
+                     f"| {o.get('mfma_flop_equals_2MNK', '')} | {o.get('mfma_util_pct', '')} | {o.get('ta_busy_pct', '')} "
+                     f"| {o.get('clock_mhz', '')} |")
+    with open(os.path.splitext(out_path)[0] + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
     with open(out_path, "w") as f:
         json.dump({"commands": commands, "gemv_source_sha256": source_sha256(GEMV_SOURCE),
                    "gemm_source_sha256": source_sha256(os.path.join("weight_only_int4_quantize_amd", "csrc",
