@@ -138,13 +138,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(XR * WP
     const int g1 = static_cast<int>(static_cast<int64_t>(wave + 1) * ng / NW);
     const uint32_t w_bytes = static_cast<uint32_t>(cols) * static_cast<uint32_t>(K / 2);
     const auto rw = rsrc(qweight + static_cast<int64_t>(n0) * (K / 8), w_bytes);
-    // weights are loaded with the lanes of a quad on one column (lane l:
-    // column l / 4, quarter l % 4), so each quad reads one contiguous run,
-    // and moved to the MFMA's lane order (column l % 16, quarter l / 16)
-    // with a lane permute
-    const int lcol = lane >> 2, lq = lane & 3;
-    const uint32_t w_lane = lcol < cols ? static_cast<uint32_t>(lcol) * (K / 2) + lq * WPL * 4 : w_bytes;
-    const int w_src = 4 * ((col * 4 + kq) & 63);    // byte address of the source lane: 4 (4 col + kq)
+    const uint32_t w_lane = col < cols ? static_cast<uint32_t>(col) * (K / 2) + kq * WPL * 4 : w_bytes;
     // x of one group, XR rows x G values, as XP 16-byte pieces per lane:
     // piece p = lane + 64 i is 16 bytes of row p / (G / 8), so each load
     // instruction reads whole rows' runs (coalesced)
@@ -238,9 +232,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(XR * WP
                 }
 #pragma unroll
                 for (int j = 0; j < WPL; ++j) {
-                    const uint32_t wj = static_cast<uint32_t>(
-                        __builtin_amdgcn_ds_bpermute(w_src, static_cast<int>(sl.w[j])));
-                    const half8_t b = unpack8(wj, half2_t{zh, zh}, half2_t{zl, zl}, uk);
+                    const half8_t b = unpack8(sl.w[j], half2_t{zh, zh}, half2_t{zl, zl}, uk);
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) {
                         uint4 xv = {0u, 0u, 0u, 0u};

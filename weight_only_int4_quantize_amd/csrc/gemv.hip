@@ -145,11 +145,10 @@ __device__ inline void compute_batch(const WeightBatch<RPW, CPL>& b, const uint4
         const int c = min(base + lane + 64 * j, nchunk - 1);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const uint4* pp = xp + (m * nchunk + c) * Chunk<BITS>::kXV;
             const float2 o = xo[m * nchunk + c];
             uint4 p[Chunk<BITS>::kXV];
 #pragma unroll
-            for (int v = 0; v < Chunk<BITS>::kXV; ++v) p[v] = pp[v];
+            for (int v = 0; v < Chunk<BITS>::kXV; ++v) p[v] = xp[(m * Chunk<BITS>::kXV + v) * nchunk + c];
 #pragma unroll
             for (int i = 0; i < RPW; ++i) {
                 float d = 0.f;
@@ -207,7 +206,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const half_t* __restrict_
     extern __shared__ uint4 smem[];
     constexpr int XV = Chunk<BITS>::kXV;
     const int nchunk = K >> Chunk<BITS>::kShift;    // 32 (INT4) or 16 (W8) weights per chunk
-    uint4* xp = smem;                               // [MT][nchunk][XV] x pairs
+    // x pairs [MT][XV][nchunk]: lanes reading one v of consecutive chunks
+    // hit consecutive 16-byte slots (no bank conflicts)
+    uint4* xp = smem;
     float2* xo = reinterpret_cast<float2*>(smem + MT * nchunk * XV);  // [MT][nchunk] (off, xs)
     float* yl = reinterpret_cast<float*>(xo + MT * nchunk);          // [NW][max_sets][RPW][MT]
 
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const half_t* __restrict_
                     p.z = (v.z & 0xFFFFu) | (v.w << 16);
                     p.w = (v.z >> 16) | (v.w & 0xFFFF0000u);
                 }
-                xp[(m * nchunk + c) * XV + j] = p;
+                xp[(m * XV + j) * nchunk + c] = p;
                 even += (h_lo(v.x) + h_lo(v.y)) + (h_lo(v.z) + h_lo(v.w));
                 odd += (h_hi(v.x) + h_hi(v.y)) + (h_hi(v.z) + h_hi(v.w));
             }
