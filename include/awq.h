@@ -139,10 +139,11 @@ awq_status awq_quantize_ex(const void* w_f16, const float* channel_scale,
  * M == 0 or N == 0 returns AWQ_OK without work. Decode (M <= 2) runs a
  * bandwidth-bound GEMV; a batch of decode tokens (M <= 64) one of two MFMA
  * kernels that stream the packed weights straight into registers: column
- * tiles (one block per 16 output columns over all of K; M <= 32, chosen for
- * 3 <= M <= 4 and for layers of up to 48 Mi weights) or the skinny kernel
- * (256 columns per block, K split across blocks with a workspace); larger M
- * the MFMA GEMM. Results do not depend on run-to-run scheduling.
+ * tiles (one block per 16, 32 or 64 output columns over all of K; M <= 32,
+ * chosen from M = 3 up on layers of up to 48 Mi weights, or 96 Mi with
+ * K <= 8192, and on every shape when no workspace is given) or the skinny
+ * kernel (256 columns per block, K split across blocks with a workspace);
+ * larger M the MFMA GEMM. Results do not depend on run-to-run scheduling.
  */
 awq_status awq_gemm(const void* x_f16, const uint32_t* qweight,
                     const void* scales_f16, const void* zeros_f16,
@@ -158,11 +159,12 @@ awq_status awq_gemm(const void* x_f16, const uint32_t* qweight,
  * M <= 32, G <= 256, M * K * 2 < 2^31 and the tile's (scale, zero) pairs in
  * LDS; no workspace).
  * Any other path, or a path whose requirement fails, returns AWQ_ERR_CONFIG.
- * The automatic choice takes the column tiles for 3 <= M <= 4, for
- * M <= 16 on layers of up to 48 Mi weights and for M <= 32 on such layers
- * of up to 8192 columns; otherwise the GEMV for M <= 4 where it can run;
- * the skinny kernel for M <= 64, except for M <= 8 where it would have to
- * stage K in phases and the GEMV can run (then the GEMV); then the GEMM.
+ * The automatic choice takes the column tiles for 3 <= M <= 32 on layers
+ * of up to 48 Mi weights, or up to 96 Mi with K <= 8192, and on any shape
+ * they support when the call has no workspace; otherwise the GEMV for
+ * M <= 4 where it can run; the skinny kernel for M <= 64, except for M <= 8
+ * where it would have to stage K in phases and the GEMV can run (then the
+ * GEMV); then the GEMM.
  */
 awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight,
                          const void* scales_f16, const void* zeros_f16,
@@ -185,8 +187,8 @@ int awq_gemm_kernel(int64_t M, int64_t N, int64_t K, int group_size, int path,
  * blocks when the tile count would leave the GPU's resident blocks partly
  * idle: a stream-K decomposition for the GEMM (e.g. the M = 2048 prefill of
  * a 4096-wide layer, or only the tiles of a short last round behind whole
- * tiles), and fixed K splits for the skinny kernel (e.g. M = 16 on a
- * 4096-wide layer, 32 column tiles). Same operation, arguments and
+ * tiles), and fixed K splits for the skinny kernel (e.g. M = 16 on an
+ * 8192 x 28672 layer). Same operation, arguments and
  * results as awq_gemm (rskf.cn §3.3 GEMM kernel), up to fp32 summation
  * order; the partial sums of a split tile are added in a fixed order, so
  * results do not depend on scheduling.

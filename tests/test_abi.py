@@ -194,6 +194,10 @@ def test_kernel_choice(L):
     assert k(4, 4096, 11008, 128, 0, 0) == 4           # column tiles
     assert k(16, 4096, 4096, 128, 0, 1) == 4
     assert k(16, 8192, 28672, 128, 0, 1) == 3          # large layer: the skinny kernel
+    assert k(16, 8192, 28672, 128, 0, 0) == 4          # ... which without a workspace walks K in phases
+    assert k(16, 5120, 13824, 128, 0, 1) == 3
+    assert k(16, 13824, 5120, 128, 0, 1) == 4
+    assert k(32, 11008, 4096, 128, 0, 1) == 4
     assert k(2048, 11008, 4096, 128, 0, 1) == 2        # prefill: the GEMM
     assert k(9, 64, 128, 64, 1, 0) == -1               # GEMV is M <= 8
     assert k(33, 64, 128, 64, 4, 0) == -1              # column tiles are M <= 32

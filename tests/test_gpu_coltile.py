@@ -1,8 +1,9 @@
-"""Parity of the column-tile MFMA kernel (path 4: one block per 16 output
-columns over all of K, for 2 <= M <= 32) with the CPU oracle: relative
+"""Parity of the column-tile MFMA kernel (path 4: one block per 16, 32 or 64
+output columns over all of K, for 2 <= M <= 32) with the CPU oracle: relative
 Frobenius error <= 1e-3 and |y - y_ref| <= 1e-2 * (|y_ref| + 1) per element,
 on the decode shapes, ragged shapes (N not a multiple of 16, rows past M,
-few groups per wave, every group size it takes) and a one-hot input, which
+few groups per wave, every group size it takes, blocks of several tiles
+whose last tiles lie partly or wholly past N) and a one-hot input, which
 reproduces the dequantized column exactly (one nonzero product per
 column, one scale multiply, one fp16 rounding)."""
 
@@ -44,6 +45,13 @@ def test_decode_shapes_against_oracle(N, K, M):
     (17, 333, 1536, 64),      # two row blocks, rows past M in the second
     (32, 4111, 4096, 128),
     (9, 77, 28672, 128),      # long K: 28 groups per wave
+    # several 16-column tiles per block (each x operand read feeds them all)
+    (16, 11000, 4096, 128),   # four tiles per block; the last block's last tile 8 columns wide
+    (16, 6000, 4096, 128),    # two tiles per block; the last block's second tile past N
+    (8, 13800, 5120, 128),    # two tiles at 8 rows (rows of 40 groups)
+    (32, 10250, 4096, 128),   # four tiles, 32 rows; the last block holds 10 columns
+    (16, 11000, 4096, 256),   # four tiles at G = 256 (two groups in flight)
+    (32, 11000, 4096, 256),   # 32 rows at G = 256: two tiles
 ])
 def test_ragged_against_oracle(M, N, K, G):
     lay = synth.make_layer(N, K, M, seed=[220, M, N, K, G], w_std=0.02)
@@ -73,9 +81,9 @@ def test_one_hot_rows_return_dequantized_columns():
     assert np.array_equal(y, w_hat[:, ks].T.astype(np.float16))
 
 
-def test_guard_band_and_repeatability():
-    M, N, K, G = 13, 45, 1024, 128
-    lay = synth.make_layer(N, K, M, seed=[223], w_std=0.02)
+@pytest.mark.parametrize("M,N,K,G", [(13, 45, 1024, 128), (16, 10250, 4096, 128)])
+def test_guard_band_and_repeatability(M, N, K, G):
+    lay = synth.make_layer(N, K, M, seed=[223, M, N], w_std=0.02)
     qw, sc, zr = oracle.quantize(lay["w"], G)
     buf = torch.full((M * N + 2048,), 7.0, dtype=torch.float16, device="cuda")
     y = buf[1024:1024 + M * N].view(M, N)

@@ -4,7 +4,7 @@ through the C ABI, on two calls in a row (the second with a smaller input):
 the linear-layer bar (relative Frobenius error <= 1e-3 and |y - y_ref| <=
 1e-2 * (|y_ref| + 1) per element) against both awq_gemm_ex and the oracle,
 and the same bits as awq_gemm_ex where both run the same split plan (the
-skinny kernel and the GEMV).
+skinny kernel, the column tiles and the GEMV).
 """
 
 import ctypes
@@ -53,7 +53,8 @@ def run_pair(M, N, K, seed):
 
 
 @pytest.mark.parametrize("first,second", [
-    ((16, 11008, 4096), (9, 4096, 4096)),       # skinny, K split: 43 then 16 column tiles
+    ((64, 4096, 4096), (40, 2048, 4096)),       # skinny, K split: 16 then 8 column tiles
+    ((16, 11008, 4096), (9, 4096, 4096)),       # column tiles: no scratch
     ((48, 5120, 13824), (33, 4096, 11008)),     # skinny, 4 row blocks, long K
     ((3, 4096, 28672), (2, 1024, 28672)),       # long K: column tiles, then the skinny kernel (M = 2)
     ((1, 11008, 4096), (1, 4096, 4096)),        # GEMV: no scratch

@@ -226,7 +226,7 @@ int choose_path(int64_t M, int64_t N, int64_t K, int group_size, int path, bool 
         case 4: return coltile_supported(M, N, K, group_size) ? 4 : -1;
         default: break;
     }
-    if (coltile_preferred(M, N, K, group_size)) return 4;
+    if (coltile_preferred(M, N, K, group_size, have_workspace)) return 4;
     if (skinny_ok && (M > 4 || !gemv_ok) && !(skinny_phased && gemv_ok)) return 3;
     return gemv_ok ? 1 : 2;
 }

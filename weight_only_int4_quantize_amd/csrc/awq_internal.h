@@ -138,8 +138,8 @@ awq_status launch_skinny(const half_t* x, const uint32_t* qweight, const half_t*
 constexpr int kColTileMaxM = 32;
 bool coltile_supported(int64_t M, int64_t N, int64_t K, int group_size);
 // whether the automatic choice takes it (by measured times against the GEMV
-// and the skinny kernel)
-bool coltile_preferred(int64_t M, int64_t N, int64_t K, int group_size);
+// and the skinny kernel, which has K splits only with a workspace)
+bool coltile_preferred(int64_t M, int64_t N, int64_t K, int group_size, bool have_workspace);
 awq_status launch_coltile(const half_t* x, const uint32_t* qweight, const half_t* scales,
                           const half_t* zeros, int64_t M, int64_t N, int64_t K, int group_size,
                           half_t* y, hipStream_t stream);

@@ -6,12 +6,13 @@
 // At these M the layer is bound by streaming the packed weights from HBM,
 // and every weight feeds M outputs, which the fp16 matrix cores take: one
 // v_mfma_f32_16x16x32_f16 multiplies 16 rows of x by 16 columns of W over
-// 32 k. The layout puts the whole K range of one 16-column tile in one
+// 32 k. The layout puts the whole K range of CT 16-column tiles in one
 // thread block, so no partial sums leave the block:
-//  * a block of NW waves owns 16 output columns and all of K; wave w takes
-//    the groups [w ng / NW, (w + 1) ng / NW) and keeps a 16 x 16 accumulator
-//    per 16 rows of x; the waves' accumulators are added through LDS in a
-//    fixed order at the end (deterministic);
+//  * a block of NW waves owns 16 CT output columns and all of K; wave w
+//    takes the groups [w ng / NW, (w + 1) ng / NW) and keeps a 16 x 16
+//    accumulator per 16 rows of x and tile; every x operand a wave reads
+//    feeds the CT tiles' MFMAs; the waves' accumulators are added through
+//    LDS in a fixed order at the end (deterministic);
 //  * within a group a lane of k-quarter q (lane / 16) takes the G / 4
 //    consecutive k of words [q WPL, (q + 1) WPL) of its column, WPL = G / 32
 //    packed words, so its weights are one contiguous 4 WPL-byte load and its
@@ -39,11 +40,11 @@
 namespace awq {
 namespace {
 
-constexpr int kCtCols = 16;
+constexpr int kCtCols = 16;      // columns of one MFMA tile
 constexpr int kCtSZ = 4;          // (scale, zero) pairs per thread loaded ahead of the ring
-// LDS: the (scale, zero) pairs [16][ng | 1] words, then (16-byte aligned) the
-// waves' x buffers, later reused for the waves' sums
-__host__ __device__ inline int ct_x_offset(int ng) { return (kCtCols * (ng | 1) + 3) & ~3; }
+// LDS: the (scale, zero) pairs [16 ct][ng | 1] words, then (16-byte aligned)
+// the waves' x buffers, later reused for the waves' sums
+__host__ __device__ inline int ct_x_offset(int ng, int ct) { return (kCtCols * ct * (ng | 1) + 3) & ~3; }
 
 __device__ inline half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
@@ -83,33 +84,43 @@ __device__ inline half8_t permute8(uint4 v) {
     return __builtin_bit_cast(half8_t, p);
 }
 
+// Ring depth and occupancy of a kernel instance: four groups in flight while
+// a slot (CT WPL weight words and XP 16-byte x pieces) is at most 24 VGPRs,
+// else two; four waves per SIMD (128 VGPRs) for the single-tile instances
+// with small slots, else two.
+constexpr int ct_xp(int xr, int wpl) { return (xr * wpl * 4 + 63) / 64; }
+constexpr int ct_depth(int xr, int wpl, int ct) { return ct * wpl + 4 * ct_xp(xr, wpl) <= 24 ? 4 : 2; }
+constexpr int ct_waves_per_eu(int xr, int wpl, int ct, int nw) {
+    return nw >= 16 || (ct == 1 && xr * wpl <= 64) ? 4 : 2;
+}
+
 // One group's operands of a lane: WPL packed words of its column, and MB WPL
 // 16-byte pieces of the group's x in row-run order.
-template <int WPL, int XP>
+template <int WPL, int XP, int CT>
 struct CtSlot {
-    uint32_t w[WPL];
+    uint32_t w[CT][WPL];   // per column tile
     uint4 x[XP];           // coalesced pieces of the group's x, re-laid through LDS
 };
 
 // XR: rows of x staged (M rounded up to 4, 8, 16 or 32); MB = XR / 16
-// rounded up MFMA row blocks; XP 16-byte x pieces per lane and group.
-template <int XR, int WPL, int NW, int DEPTH>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(XR * WPL <= 64 ? 4 : 2))) void coltile_kernel(const half_t* __restrict__ x,
-                                                         const uint32_t* __restrict__ qweight,
-                                                         const half_t* __restrict__ scales,
-                                                         const half_t* __restrict__ zeros,
-                                                         half_t* __restrict__ y, int M, int N, int K) {
+// rounded up MFMA row blocks; XP 16-byte x pieces per lane and group; CT
+// 16-column MFMA tiles per block, which share every x operand read.
+template <int XR, int WPL, int NW, int DEPTH, int CT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ct_waves_per_eu(XR, WPL, CT, NW)))) void coltile_kernel(
+    const half_t* __restrict__ x, const uint32_t* __restrict__ qweight, const half_t* __restrict__ scales,
+    const half_t* __restrict__ zeros, half_t* __restrict__ y, int M, int N, int K) {
     constexpr int G = WPL * 32;
     constexpr int MB = (XR + 15) / 16;
+    constexpr int COLS = kCtCols * CT;
     constexpr int XPIECES = XR * (G / 8);                       // 16-byte pieces of x per group
     constexpr int XP = (XPIECES + 63) / 64;
-    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];   // (s, z) pairs [16][szst], then sums
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];   // (s, z) pairs [COLS][szst], then sums
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15;
     const int kq = lane >> 4;                       // k-quarter of every group
-    const int n0 = blockIdx.x * kCtCols;
+    const int n0 = blockIdx.x * COLS;
     const int ng = K / G;
     const int szst = ng | 1;                        // odd: 16 columns at one group hit distinct banks
 
@@ -119,7 +130,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(XR * WP
     //      loads are issued and written to LDS after them (loads complete in
     //      order, so that write waits for these loads only); any rest
     //      (more than kCtSZ * 64 NW pairs) is staged after the ring's loads ----
-    const int cols = min(kCtCols, N - n0);
+    const int cols = min(COLS, N - n0);
     const uint32_t sz_bytes = static_cast<uint32_t>(cols) * static_cast<uint32_t>(ng) * 2;
     const auto rs = rsrc(scales + static_cast<int64_t>(n0) * ng, sz_bytes);
     const auto rz = rsrc(zeros + static_cast<int64_t>(n0) * ng, sz_bytes);
@@ -127,7 +138,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(XR * WP
 #pragma unroll
     for (int i = 0; i < kCtSZ; ++i) {
         const int e = tid + i * NW * 64;       // column e / ng, group e % ng
-        const uint32_t so = e < kCtCols * ng ? static_cast<uint32_t>(e) * 2 : sz_bytes;
+        const uint32_t so = e < COLS * ng ? static_cast<uint32_t>(e) * 2 : sz_bytes;
         sr[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
         zr[i] = __builtin_amdgcn_raw_buffer_load_b16(rz, so, 0, 0);
     }
@@ -138,7 +149,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(XR * WP
     const int g1 = static_cast<int>(static_cast<int64_t>(wave + 1) * ng / NW);
     const uint32_t w_bytes = static_cast<uint32_t>(cols) * static_cast<uint32_t>(K / 2);
     const auto rw = rsrc(qweight + static_cast<int64_t>(n0) * (K / 8), w_bytes);
-    const uint32_t w_lane = col < cols ? static_cast<uint32_t>(col) * (K / 2) + kq * WPL * 4 : w_bytes;
+    // weights in MFMA lane order: lane (col, kq) of tile t reads words
+    // [kq WPL, (kq + 1) WPL) of the group in column 16 t + col
+    uint32_t w_lane[CT];
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
+        const int c = kCtCols * t + col;
+        w_lane[t] = c < cols ? static_cast<uint32_t>(c) * (K / 2) + kq * WPL * 4 : w_bytes;
+    }
     // x of one group, XR rows x G values, as XP 16-byte pieces per lane:
     // piece p = lane + 64 i is 16 bytes of row p / (G / 8), so each load
     // instruction reads whole rows' runs (coalesced)
@@ -151,22 +169,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(XR * WP
         const int row = p / (G / 8), c8 = p % (G / 8);
         x_piece[i] = p < XPIECES && row < M ? (static_cast<uint32_t>(row) * K + c8 * 8) * 2 : x_bytes;
     }
-    auto load = [&](CtSlot<WPL, XP>& sl, int g) {
+    auto load = [&](CtSlot<WPL, XP, CT>& sl, int g) {
         const bool ok = g < g1;
-        const uint32_t wo = ok ? w_lane + static_cast<uint32_t>(g) * (G / 2) : w_bytes;
-        if constexpr (WPL == 8) {
-            const uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 0, 0));
-            const uint4 b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 16, 0));
-            sl.w[0] = a.x; sl.w[1] = a.y; sl.w[2] = a.z; sl.w[3] = a.w;
-            sl.w[4] = b.x; sl.w[5] = b.y; sl.w[6] = b.z; sl.w[7] = b.w;
-        } else if constexpr (WPL == 4) {
-            const uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 0, 0));
-            sl.w[0] = a.x; sl.w[1] = a.y; sl.w[2] = a.z; sl.w[3] = a.w;
-        } else if constexpr (WPL == 2) {
-            const uint2 a = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, wo, 0, 0));
-            sl.w[0] = a.x; sl.w[1] = a.y;
-        } else {
-            sl.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, wo, 0, 0);
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+            const uint32_t wo = ok && w_lane[t] < w_bytes ? w_lane[t] + static_cast<uint32_t>(g) * (G / 2) : w_bytes;
+            if constexpr (WPL == 8) {
+                const uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 0, 0));
+                const uint4 b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 16, 0));
+                sl.w[t][0] = a.x; sl.w[t][1] = a.y; sl.w[t][2] = a.z; sl.w[t][3] = a.w;
+                sl.w[t][4] = b.x; sl.w[t][5] = b.y; sl.w[t][6] = b.z; sl.w[t][7] = b.w;
+            } else if constexpr (WPL == 4) {
+                const uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 0, 0));
+                sl.w[t][0] = a.x; sl.w[t][1] = a.y; sl.w[t][2] = a.z; sl.w[t][3] = a.w;
+            } else if constexpr (WPL == 2) {
+                const uint2 a = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, wo, 0, 0));
+                sl.w[t][0] = a.x; sl.w[t][1] = a.y;
+            } else {
+                sl.w[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rw, wo, 0, 0);
+            }
         }
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
@@ -175,7 +196,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(XR * WP
         }
     };
 
-    CtSlot<WPL, XP> ring[DEPTH];
+    CtSlot<WPL, XP, CT> ring[DEPTH];
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
         load(ring[d], g0 + d);
@@ -184,12 +205,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(XR * WP
 #pragma unroll
     for (int i = 0; i < kCtSZ; ++i) {
         const int e = tid + i * NW * 64;
-        if (e < kCtCols * ng) {
+        if (e < COLS * ng) {
             const int c = e / ng, g = e - c * ng;
             lds[c * szst + g] = static_cast<uint32_t>(sr[i]) | (static_cast<uint32_t>(zr[i]) << 16);
         }
     }
-    for (int e = tid + kCtSZ * NW * 64; e < kCtCols * ng; e += NW * 64) {
+    for (int e = tid + kCtSZ * NW * 64; e < COLS * ng; e += NW * 64) {
         const int c = e / ng, g = e - c * ng;
         const uint32_t so = static_cast<uint32_t>(e) * 2;
         lds[c * szst + g] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0)) |
@@ -197,30 +218,40 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(XR * WP
     }
     __syncthreads();   // the (scale, zero) pairs are in LDS
 
-    float4_t acc[MB];
+    float4_t acc[CT][MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < CT; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[t][mb] = float4_t{0.f, 0.f, 0.f, 0.f};
     const CtConsts uk = ct_consts();
-    const uint32_t* szcol = lds + col * szst;
     // the wave's x buffer: XR rows of G values, rows padded by 16 bytes so
     // the 16 rows of an MFMA operand read hit distinct banks; operand rows
     // past XR are zero and not read
     constexpr int XST = G + 8;
-    half_t* xw = reinterpret_cast<half_t*>(lds + ct_x_offset(ng)) + wave * (XR * XST);
+    half_t* xw = reinterpret_cast<half_t*>(lds + ct_x_offset(ng, CT)) + wave * (XR * XST);
     for (int gb = g0; gb < g1; gb += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             const int g = gb + d;
-            CtSlot<WPL, XP>& sl = ring[d];
+            CtSlot<WPL, XP, CT>& sl = ring[d];
             if (g < g1) {
-                const uint32_t sz = szcol[g];
-                const half_t z = __builtin_bit_cast(half_t, static_cast<uint16_t>(sz >> 16));
-                const half_t zh = static_cast<half_t>(1024.0f) + z;   // exact
-                const half_t zl = static_cast<half_t>(64.0f) + z;     // exact
-                const float s = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(sz & 0xFFFFu)));
-                float4_t part[MB];
+                float s[CT];
+                half2_t zh[CT], zl[CT];
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) part[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < CT; ++t) {
+                    const uint32_t sz = lds[(kCtCols * t + col) * szst + g];
+                    const half_t z = __builtin_bit_cast(half_t, static_cast<uint16_t>(sz >> 16));
+                    const half_t h = static_cast<half_t>(1024.0f) + z;   // exact
+                    const half_t l = static_cast<half_t>(64.0f) + z;     // exact
+                    zh[t] = half2_t{h, h};
+                    zl[t] = half2_t{l, l};
+                    s[t] = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(sz & 0xFFFFu)));
+                }
+                float4_t part[CT][MB];
+#pragma unroll
+                for (int t = 0; t < CT; ++t)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) part[t][mb] = float4_t{0.f, 0.f, 0.f, 0.f};
                 // x pieces to the wave's LDS rows, then back in operand order:
                 // lane (row col, quarter kq) takes 8 values at k = 8 (kq WPL + j)
                 // (one wave's LDS accesses execute in order, so no barrier)
@@ -232,132 +263,202 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(XR * WP
                 }
 #pragma unroll
                 for (int j = 0; j < WPL; ++j) {
-                    const half8_t b = unpack8(sl.w[j], half2_t{zh, zh}, half2_t{zl, zl}, uk);
+                    half8_t b[CT];
+#pragma unroll
+                    for (int t = 0; t < CT; ++t) b[t] = unpack8(sl.w[t][j], zh[t], zl[t], uk);
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) {
                         uint4 xv = {0u, 0u, 0u, 0u};
                         if (XR % 16 == 0 || 16 * mb + col < XR)
                             xv = *reinterpret_cast<const uint4*>(&xw[(16 * mb + col) * XST + (kq * WPL + j) * 8]);
-                        part[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(permute8(xv), b, part[mb], 0, 0, 0);
+                        const half8_t a = permute8(xv);
+#pragma unroll
+                        for (int t = 0; t < CT; ++t)
+                            part[t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[t], part[t][mb], 0, 0, 0);
                     }
                 }
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
+                for (int t = 0; t < CT; ++t)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[mb][e] += s * part[mb][e];
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[t][mb][e] += s[t] * part[t][mb][e];
             }
             load(sl, g + DEPTH);                          // refill the slot
         }
     }
 
     // ---- the waves' sums, added in wave order: lane l holds rows
-    //      16 mb + 4 (l / 16) + e of column l % 16 (over the x buffers,
-    //      which every wave is done with after the barrier) ----
+    //      16 mb + 4 (l / 16) + e of column 16 t + l % 16 (over the x
+    //      buffers, which every wave is done with after the barrier) ----
     __syncthreads();
-    float4_t* red = reinterpret_cast<float4_t*>(lds + ct_x_offset(ng));
+    float4_t* red = reinterpret_cast<float4_t*>(lds + ct_x_offset(ng, CT));
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) red[(wave * MB + mb) * 64 + lane] = acc[mb];
+    for (int t = 0; t < CT; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) red[((wave * CT + t) * MB + mb) * 64 + lane] = acc[t][mb];
     __syncthreads();
-    for (int i = tid; i < MB * 256; i += NW * 64) {
-        const int mb = i >> 8, l = (i >> 2) & 63, e = i & 3;
+    for (int i = tid; i < CT * MB * 256; i += NW * 64) {
+        const int t = i / (MB * 256), r = i - t * (MB * 256);
+        const int mb = r >> 8, l = (r >> 2) & 63, e = r & 3;
         float sum = 0.f;
-        for (int w = 0; w < NW; ++w) sum += red[(w * MB + mb) * 64 + l][e];
+        for (int w = 0; w < NW; ++w) sum += red[((w * CT + t) * MB + mb) * 64 + l][e];
         const int row = 16 * mb + 4 * (l >> 4) + e;
-        const int n = n0 + (l & 15);
+        const int n = n0 + kCtCols * t + (l & 15);
         if (row < M && n < N) y[static_cast<int64_t>(row) * N + n] = static_cast<half_t>(sum);
     }
 }
 
 // rows of x a launch stages: M rounded up to 4, 8, 16 or 32
 int ct_rows(int64_t M) { return M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : 32; }
-// 8 waves per block while the column tiles alone leave CUs with few waves;
-// 4 from 2.5 tiles per CU up (all blocks resident at once). Measured at
-// M = 2 (us, 8 against 4 waves): 4096 x 4096 6.2 / 6.7, 4096 x 11008
-// 10.4 / 14.0, 8192 x 28672 34.4 / 39.3; 11008 x 4096 10.2 / 10.0,
-// 13824 x 5120 15.4 / 14.6.
-int ct_waves(int64_t N, int64_t K, int group_size) {
-    if (K / group_size < 16) return 4;
-    return ceil_div(N, kCtCols) * 2 >= 5 * static_cast<int64_t>(cu_count()) ? 4 : 8;
+// largest tile count an instance takes without spilling
+constexpr int ct_max_tiles(int xr, int wpl) { return xr * wpl >= 256 ? 2 : 4; }
+// 16-column tiles per block. Each extra tile reuses every x operand read
+// (x costs M / 4 times the weight bytes per tile), but leaves fewer blocks.
+// From 16 rows of x up: 4 tiles from 2.5 column tiles per CU, 2 from 1.25;
+// below: 2 from 1.25 column tiles per CU on rows of 40 groups and more.
+// Measured (us, weights past every cache; 1 / 2 / 4 tiles, best wave count
+// of each): M = 16 on 11008 x 4096 13.5 / 13.4 / 11.7, 13824 x 5120
+// 22.0 / 17.3 / 16.1, 5120 x 13824 25.8 / 22.2 / 32.3, 8192 x 28672
+// 51.9 / 44.1 / 64.2, 4096 x 4096 6.5 / 8.2 / 11.1; M = 4 on 13824 x 5120
+// 15.5 / 14.4 / 17.4, 11008 x 4096 10.3 / 10.9 / 13.3.
+int ct_tiles(int64_t M, int64_t N, int64_t K, int group_size) {
+    const int64_t cu = cu_count();
+    const int64_t tiles = ceil_div(N, kCtCols);
+    const int xr = ct_rows(M);
+    int ct;
+    if (xr >= 16)
+        ct = tiles * 2 >= 5 * cu ? 4 : tiles * 4 >= 5 * cu ? 2 : 1;
+    else
+        ct = tiles * 4 >= 5 * cu && K / group_size >= 40 ? 2 : 1;
+    return std::min(ct, ct_max_tiles(xr, group_size / 32));
+}
+// 16-wave blocks (4 per SIMD, 128 VGPRs) only for instances whose ring fits
+constexpr bool ct_sixteen_ok(int xr, int wpl, int ct) { return ct == 1 && xr * wpl <= 64; }
+// Waves per block, splitting K: 4 once the blocks fill the CUs (2.5 single-
+// tile blocks or 1.6 multi-tile blocks per CU), else 8; single-tile blocks
+// on rows of at most 32 groups take 4 from 16 rows of x up and 16 at 4 rows.
+// Measured (us, 4 / 8 / 16 waves): 4096 x 4096 M = 4 6.8 / 6.3 / 5.9,
+// M = 16 6.5 / 7.1 / 8.9; 4096 x 11008 M = 4 13.4 / 10.0 / 11.1;
+// 13824 x 5120 at M = 4 on 2 tiles 14.4 / 15.9; 8192 x 28672 at M = 16 on
+// 2 tiles 49.1 / 44.1.
+int ct_waves(int64_t M, int64_t N, int64_t K, int group_size, int ct) {
+    const int64_t ng = K / group_size;
+    if (ng < 16) return 4;
+    const int64_t cu = cu_count();
+    const int64_t blocks = ceil_div(N, kCtCols * ct);
+    const int xr = ct_rows(M);
+    if (ct > 1) return blocks * 5 >= 8 * cu ? 4 : 8;
+    if (blocks * 2 >= 5 * cu) return 4;
+    if (ng <= 32) {
+        if (xr >= 16) return 4;
+        if (xr <= 4 && ct_sixteen_ok(xr, group_size / 32, 1)) return 16;
+    }
+    return 8;
 }
 
-size_t ct_lds_bytes(int64_t K, int group_size, int xr, int nw) {
-    const size_t pairs = static_cast<size_t>(ct_x_offset(static_cast<int>(K / group_size))) * 4;
+size_t ct_lds_bytes(int64_t K, int group_size, int xr, int nw, int ct) {
+    const size_t pairs = static_cast<size_t>(ct_x_offset(static_cast<int>(K / group_size), ct)) * 4;
     const size_t xbuf = static_cast<size_t>(nw) * xr * (group_size + 8) * 2;
-    const size_t sums = static_cast<size_t>(nw) * ((xr + 15) / 16) * 64 * 16;
+    const size_t sums = static_cast<size_t>(nw) * ct * ((xr + 15) / 16) * 64 * 16;
     return pairs + std::max(xbuf, sums);
 }
 
+// LDS bytes a block may take: the device's limit, or gfx950's 160 KB when
+// no device can be queried (host-only kernel-choice queries)
+constexpr int kGfx950Lds = 160 * 1024;
 int ct_max_shared() {
     static int cached = -1;
     if (cached < 0) {
-        int dev = 0, v = 65536;
+        int dev = 0, v = kGfx950Lds;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-            v = 65536;
+            v = kGfx950Lds;
         cached = v;
     }
     return cached;
 }
 
-template <int XR, int WPL, int NW>
+template <int XR, int WPL, int NW, int CT>
 awq_status launch_ct(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
                      int N, int K, half_t* y, hipStream_t stream) {
-    constexpr int DEPTH = XR * WPL <= 64 ? 4 : 2;
+    constexpr int DEPTH = ct_depth(XR, WPL, CT);
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&coltile_kernel<XR, WPL, NW, DEPTH>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&coltile_kernel<XR, WPL, NW, DEPTH, CT>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, ct_max_shared()) != hipSuccess)
             return AWQ_ERR_HIP;
         attr_set = true;
     }
-    const size_t lds = ct_lds_bytes(K, WPL * 32, XR, NW);
-    const int64_t blocks = ceil_div(N, kCtCols);
-    hipLaunchKernelGGL((coltile_kernel<XR, WPL, NW, DEPTH>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), lds,
-                       stream, x, qweight, scales, zeros, y, M, N, K);
+    const size_t lds = ct_lds_bytes(K, WPL * 32, XR, NW, CT);
+    const int64_t blocks = ceil_div(N, kCtCols * CT);
+    hipLaunchKernelGGL((coltile_kernel<XR, WPL, NW, DEPTH, CT>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64),
+                       lds, stream, x, qweight, scales, zeros, y, M, N, K);
     return last_launch_status();
 }
 
-template <int XR, int WPL>
+template <int XR, int WPL, int CT>
 awq_status launch_ct_nw(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
                         int N, int K, half_t* y, hipStream_t stream) {
-    if (ct_waves(N, K, WPL * 32) == 8) return launch_ct<XR, WPL, 8>(x, qweight, scales, zeros, M, N, K, y, stream);
-    return launch_ct<XR, WPL, 4>(x, qweight, scales, zeros, M, N, K, y, stream);
+    switch (ct_waves(M, N, K, WPL * 32, CT)) {
+        case 16:
+            if constexpr (ct_sixteen_ok(XR, WPL, CT))
+                return launch_ct<XR, WPL, 16, CT>(x, qweight, scales, zeros, M, N, K, y, stream);
+            return launch_ct<XR, WPL, 8, CT>(x, qweight, scales, zeros, M, N, K, y, stream);
+        case 8: return launch_ct<XR, WPL, 8, CT>(x, qweight, scales, zeros, M, N, K, y, stream);
+        default: return launch_ct<XR, WPL, 4, CT>(x, qweight, scales, zeros, M, N, K, y, stream);
+    }
+}
+
+template <int XR, int WPL>
+awq_status launch_ct_tiles(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros,
+                           int M, int N, int K, half_t* y, hipStream_t stream) {
+    switch (ct_tiles(M, N, K, WPL * 32)) {
+        case 1: return launch_ct_nw<XR, WPL, 1>(x, qweight, scales, zeros, M, N, K, y, stream);
+        case 2: return launch_ct_nw<XR, WPL, 2>(x, qweight, scales, zeros, M, N, K, y, stream);
+        default: return launch_ct_nw<XR, WPL, ct_max_tiles(XR, WPL)>(x, qweight, scales, zeros, M, N, K, y, stream);
+    }
 }
 
 template <int WPL>
 awq_status launch_ct_mb(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
                         int N, int K, half_t* y, hipStream_t stream) {
     switch (ct_rows(M)) {
-        case 4: return launch_ct_nw<4, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
-        case 8: return launch_ct_nw<8, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
-        case 16: return launch_ct_nw<16, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
-        default: return launch_ct_nw<32, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
+        case 4: return launch_ct_tiles<4, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
+        case 8: return launch_ct_tiles<8, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
+        case 16: return launch_ct_tiles<16, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
+        default: return launch_ct_tiles<32, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
     }
 }
 
 }  // namespace
 
-// The automatic kernel choice (awq_gemm): column tiles where they beat the
-// GEMV and the skinny kernel (us, best of the others in brackets, weights
-// past every cache): M = 4 on 4096 x 11008 10.5 (14.2), 13824 x 5120 15.5
-// (16.5); M = 8 on 4096 x 4096 6.5 (10.3), 11008 x 4096 12.1 (13.2); M = 16
-// on 4096 x 4096 7.3 (10.6), 4096 x 11008 13.1 (15.4); M = 32 on 4096 x 4096
-// 9.1 (13.0). The skinny kernel stays ahead on large layers from M = 8 up
-// (8192 x 28672 at M = 16: 35 against 49) and the GEMV at M = 2 on most.
-bool coltile_preferred(int64_t M, int64_t N, int64_t K, int group_size) {
+// The automatic kernel choice (awq_gemm): column tiles from 3 rows of x up
+// where they beat the GEMV and the skinny kernel. Measured (us, weights past
+// every cache; column tiles against the skinny kernel with K splits):
+// 4096 x 4096 at M = 4 / 16 / 32 5.9 / 6.5 / 8.6 (10.5 / 10.6 / 13.0);
+// 11008 x 4096 10.2 / 11.7 / 15.4 (13.4 / 13.7 / 16.4); 4096 x 11008
+// 10.2 / 13.2 / 18.0 (15.1 / 15.3 / 19.6); 13824 x 5120 14.7 / 16.2 / 20.3
+// (17.3 / 16.7 / 22.2); the skinny kernel leads on long rows of large
+// layers: 5120 x 13824 18.0 / 22.2 / 27.7 (17.5 / 17.8 / 24.6), 8192 x
+// 28672 37.6 / 45.0 / 55.3 (35.7 / 35.8 / 53.8). The GEMV leads at M = 2;
+// at M = 4 it takes 6.2 us on 4096 x 4096 and 12.6 on 11008 x 4096. Without
+// a workspace the skinny kernel walks K in phases (2-5x slower), so column
+// tiles take every shape they support.
+bool coltile_preferred(int64_t M, int64_t N, int64_t K, int group_size, bool have_workspace) {
     if (M < 3 || !coltile_supported(M, N, K, group_size)) return false;
+    if (!have_workspace) return true;
     const int64_t weights = N * K;
-    if (M <= 4) return true;
-    if (M <= 16) return weights <= (int64_t{48} << 20);
-    return weights <= (int64_t{48} << 20) && ceil_div(N, kCtCols) <= 2 * static_cast<int64_t>(cu_count());
+    return weights <= (int64_t{48} << 20) || (K <= 8192 && weights <= (int64_t{96} << 20));
 }
 
 bool coltile_supported(int64_t M, int64_t N, int64_t K, int group_size) {
     if (group_size < 32 || group_size > 256) return false;
     if (M < 1 || M > kColTileMaxM || N < 1 || K < group_size || K % group_size != 0) return false;
     // 32-bit buffer offsets: x, and one 16-column tile of packed weights
-    if (M * K * 2 >= (int64_t{1} << 31) || kCtCols * (K / 2) >= (int64_t{1} << 31)) return false;
-    return ct_lds_bytes(K, group_size, ct_rows(M), ct_waves(N, K, group_size)) <=
+    const int ct = ct_tiles(M, N, K, group_size);
+    if (M * K * 2 >= (int64_t{1} << 31) || kCtCols * ct * (K / 2) >= (int64_t{1} << 31)) return false;
+    return ct_lds_bytes(K, group_size, ct_rows(M), ct_waves(M, N, K, group_size, ct), ct) <=
            static_cast<size_t>(ct_max_shared());
 }
 
