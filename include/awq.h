@@ -245,6 +245,34 @@ awq_status awq_gemm_noalloc(const void* x_f16, const uint32_t* qweight,
                             void* y_f16, int path, void* stream);
 
 /*
+ * awq_gemm_grouped - several linear layers that read the same activations,
+ * y_i = x . dequant(Wq_i)^T for i < n_layers: the independent projections of
+ * a decoder layer (q / k / v, gate / up), which the pages' deployment fuses
+ * (rskf.cn §3.4 fuse_layers), kept as separate tensors (rskf.cn §1.3 / §3.3
+ * GEMV kernel). Where awq_gemm would run the GEMV on the layers' stacked
+ * rows (M <= 2), one launch computes all of them, the rows of layer i after
+ * those of layers 0 .. i - 1; otherwise each layer is an awq_gemm call, in
+ * order. Each y_i equals that layer's awq_gemm result bit for bit.
+ *
+ *   x_f16        device, fp16 [M, K], shared by every layer
+ *   n_layers     1 .. 4
+ *   qweight, scales_f16, zeros_f16, y_f16
+ *                host arrays of n_layers device pointers, layer i's tensors
+ *                as in awq_gemm ([N[i], K / 8], [N[i], K / G], [N[i], K / G],
+ *                output [M, N[i]]); outputs must not alias any input or
+ *                each other
+ *   N            host array of n_layers row counts, each >= 0, summing to
+ *                less than 2^31 - 256
+ *   M, K, group_size  as in awq_gemm, common to every layer
+ * n_layers outside 1 .. 4 returns AWQ_ERR_CONFIG; a NULL array or device
+ * pointer AWQ_ERR_NULL; every layer is checked before anything is enqueued.
+ */
+awq_status awq_gemm_grouped(const void* x_f16, int n_layers, const uint32_t* const* qweight,
+                            const void* const* scales_f16, const void* const* zeros_f16,
+                            const int64_t* N, int64_t M, int64_t K, int group_size,
+                            void* const* y_f16, void* stream);
+
+/*
  * awq_activation_absmean - m[k] = max(mean_t |x[t, k]|, 1e-8), the
  * per-input-channel activation statistic AWQ's scale is built from
  * (rskf.cn §2.1-2.2; "AWQ 模型量化技术", Per-channel Scaling 优化).

@@ -294,3 +294,24 @@ def test_w8_checks(L):
     assert g(FAKE_ODD, FAKE, FAKE, FAKE, 4, 16, 256, 64, FAKE, 0, None, 0, None) == ALIGN
     assert g(FAKE, FAKE, FAKE, FAKE, 100, 16, 256, 64, FAKE, 2, FAKE, 16, None) == WORKSPACE
     assert g(FAKE, FAKE, FAKE, FAKE, 0, 16, 256, 64, FAKE, 0, None, 0, None) == OK
+
+
+def test_grouped_rejects_bad_arguments(L):
+    """awq_gemm_grouped's host checks, before any launch (host logic only)."""
+    import ctypes as C
+    g = L.awq_gemm_grouped
+    g.restype = C.c_int
+    g.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
+                  C.c_int, C.c_void_p, C.c_void_p]
+    P = C.c_void_p * 4
+    ptrs = P(None, None, None, None)
+    ns = (C.c_int64 * 4)(64, 64, 64, 64)
+    assert g(None, 0, ptrs, ptrs, ptrs, ns, 1, 128, 64, ptrs, None) == 4      # n_layers < 1
+    assert g(None, 5, ptrs, ptrs, ptrs, ns, 1, 128, 64, ptrs, None) == 4      # n_layers > 4
+    assert g(None, 2, None, ptrs, ptrs, ns, 1, 128, 64, ptrs, None) == 1      # NULL array
+    assert g(None, 2, ptrs, ptrs, ptrs, ns, 1, 100, 64, ptrs, None) == 2      # K % G
+    assert g(None, 2, ptrs, ptrs, ptrs, ns, 1, 128, 96, ptrs, None) == 4      # group size
+    assert g(None, 2, ptrs, ptrs, ptrs, ns, 1, 128, 64, ptrs, None) == 1      # NULL device pointers
+    assert g(None, 2, ptrs, ptrs, ptrs, ns, 0, 128, 64, ptrs, None) == 0      # M = 0: no work
+    big = (C.c_int64 * 4)(1 << 30, 1 << 30, 0, 0)
+    assert g(None, 2, ptrs, ptrs, ptrs, big, 0, 128, 64, ptrs, None) == 2     # stacked rows past 2^31

@@ -1,0 +1,92 @@
+"""awq_gemm_grouped: layers that read the same activations (a decoder
+layer's q / k / v and gate / up projections, which the rskf.cn AWQ
+article's deployment fuses, §3.4) in one GEMV launch over their stacked
+rows, each layer kept as its own tensors.
+
+Every y_i must equal the layer's own awq_gemm result bit for bit (the same
+per-row arithmetic in the same order) and meet the linear-layer bar against
+the oracle (relative Frobenius error <= 1e-3 and |y - y_ref| <= 1e-2 *
+(|y_ref| + 1) per element); outputs packed side by side in one buffer show
+that no layer writes past its own rows. Batches the GEMV does not take run
+the layers one awq_gemm call each, with the same bits.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import weight_only_int4_quantize_amd as awq  # noqa: E402
+
+from test_gpu_parity import assert_linear_close, dev, host, say  # noqa: E402
+
+
+def layers_of(Ns, K, M, G, seed):
+    """Layers with weights of their own seeds and one shared x."""
+    lays = [synth.make_layer(N, K, 0, seed=[230, seed, j, N, K], w_std=0.02) for j, N in enumerate(Ns)]
+    x = synth.make_layer(1, K, M, seed=[231, seed, M, K], w_std=0.02)["x"]
+    qs = [oracle.quantize(lay["w"], G) for lay in lays]
+    return x, qs
+
+
+def run_grouped(x, qs, G):
+    xd = dev(x)
+    dl = [(dev(q[0].view(np.int32)), dev(q[1]), dev(q[2])) for q in qs]
+    M = x.shape[0]
+    Ns = [q[0].shape[0] for q in qs]
+    # outputs side by side in one buffer between sentinels
+    total = sum(M * N for N in Ns)
+    buf = torch.full((total + 2048,), 7.0, dtype=torch.float16, device="cuda")
+    outs, off = [], 1024
+    for N in Ns:
+        outs.append(buf[off:off + M * N].view(M, N))
+        off += M * N
+    awq.awq_gemm_grouped(xd, dl, G, outs=outs)
+    singles = [awq.awq_gemm(xd, *d, G) for d in dl]
+    torch.cuda.synchronize()
+    b = host(buf)
+    assert np.all(b[:1024] == 7.0) and np.all(b[1024 + total:] == 7.0)
+    return [host(o) for o in outs], [host(s) for s in singles]
+
+
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("Ns", [(4096, 4096, 4096), (11008, 11008)], ids=["qkv", "gate_up"])
+def test_decode_projections(Ns, M):
+    K, G = 4096, 128
+    say("grouped", Ns, K, M)
+    x, qs = layers_of(Ns, K, M, G, 0)
+    got, singles = run_grouped(x, qs, G)
+    for q, g, s in zip(qs, got, singles):
+        assert np.array_equal(g.view(np.uint16), s.view(np.uint16))
+        assert_linear_close(g, oracle.linear_ref(x, *q, G))
+
+
+@pytest.mark.parametrize("Ns,K,G,M", [
+    ((100, 37, 0, 1000), 512, 64, 1),     # ragged layers, one empty
+    ((1, 2, 3), 1536, 128, 2),            # rows fewer than a wave's
+    ((1000, 3000), 11008, 128, 1),        # long rows: the persistent form
+    ((777,), 4096, 32, 2),                # one layer
+    ((300, 500, 700, 900), 2048, 256, 1), # four layers
+])
+def test_ragged_layers(Ns, K, G, M):
+    say("grouped ragged", Ns, K, G, M)
+    x, qs = layers_of(Ns, K, M, G, 1)
+    got, singles = run_grouped(x, qs, G)
+    for q, g, s in zip(qs, got, singles):
+        assert np.array_equal(g.view(np.uint16), s.view(np.uint16))
+        if q[0].shape[0]:
+            assert_linear_close(g, oracle.linear_ref(x, *q, G))
+
+
+@pytest.mark.parametrize("M", [4, 16])
+def test_batches_past_the_gemv_run_per_layer(M):
+    Ns, K, G = (4096, 1024), 4096, 128
+    x, qs = layers_of(Ns, K, M, G, 2)
+    got, singles = run_grouped(x, qs, G)
+    for q, g, s in zip(qs, got, singles):
+        assert np.array_equal(g.view(np.uint16), s.view(np.uint16))
+        assert_linear_close(g, oracle.linear_ref(x, *q, G))

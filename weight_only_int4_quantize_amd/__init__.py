@@ -80,6 +80,8 @@ def load() -> ctypes.CDLL:
     L.awq_gemm_kernel.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int]
     L.awq_gemm_noalloc.restype = c_int
     L.awq_gemm_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_int, c_vp]
+    L.awq_gemm_grouped.restype = c_int
+    L.awq_gemm_grouped.argtypes = [c_vp, c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_vp, c_vp]
     L.awq_activation_absmean_workspace_bytes.restype = c_sz
     L.awq_activation_absmean_workspace_bytes.argtypes = [c_i64, c_i64]
     L.awq_activation_absmean.restype = c_int
@@ -287,6 +289,45 @@ def awq_gemm_noalloc(x, qweight, scales, zeros, group_size: int = 128, path: int
                                  int(path), _stream(x.device))
     _check("awq_gemm_noalloc", st)
     return y
+
+
+def awq_gemm_grouped(x, layers, group_size: int = 128, outs=None):
+    """y_i = x . dequant(Wq_i)^T for layers [(qweight, scales, zeros), ...]
+    (1 to 4) that share x: one GEMV launch over their stacked rows where
+    awq_gemm would take the GEMV, else one awq_gemm per layer. Returns the
+    list of y_i (`outs`, when given, receives them)."""
+    torch = _torch()
+    _need_gpu("x", x, torch.float16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, K = x.shape
+    n = len(layers)
+    ys = list(outs) if outs is not None else [None] * n
+    if len(ys) != n:
+        raise ValueError("outs must hold one tensor per layer")
+    Ns = []
+    for i, (qw, sc, zr) in enumerate(layers):
+        _need_gpu("qweight", qw, torch.int32)
+        _need_gpu("scales", sc, torch.float16)
+        _need_gpu("zeros", zr, torch.float16)
+        N = qw.shape[0]
+        if qw.dim() != 2 or qw.shape[1] * 8 != K:
+            raise ValueError(f"layer {i}: qweight must be [N, K/8] with K = {K}")
+        if sc.shape != (N, K // group_size) or zr.shape != sc.shape:
+            raise ValueError(f"layer {i}: scales/zeros must be [N, K/group_size]")
+        if ys[i] is None:
+            ys[i] = torch.empty((M, N), dtype=torch.float16, device=x.device)
+        _need_gpu("out", ys[i], torch.float16)
+        if tuple(ys[i].shape) != (M, N):
+            raise ValueError(f"layer {i}: out must be [M, N]")
+        Ns.append(N)
+    arr = ctypes.c_void_p * max(n, 1)
+    st = load().awq_gemm_grouped(
+        _ptr(x), n, arr(*[_ptr(l[0]) for l in layers]), arr(*[_ptr(l[1]) for l in layers]),
+        arr(*[_ptr(l[2]) for l in layers]), (ctypes.c_int64 * max(n, 1))(*Ns), M, K, group_size,
+        arr(*[_ptr(y) for y in ys]), _stream(x.device))
+    _check("awq_gemm_grouped", st)
+    return ys
 
 
 def awq_activation_absmean(x):

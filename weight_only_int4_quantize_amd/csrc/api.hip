@@ -355,6 +355,52 @@ int awq_gemm_kernel(int64_t M, int64_t N, int64_t K, int group_size, int path, i
     return choose_path(M, N, K, group_size, path, have_workspace != 0);
 }
 
+awq_status awq_gemm_grouped(const void* x_f16, int n_layers, const uint32_t* const* qweight,
+                            const void* const* scales_f16, const void* const* zeros_f16, const int64_t* N,
+                            int64_t M, int64_t K, int group_size, void* const* y_f16, void* stream) {
+    if (n_layers < 1 || n_layers > kGemvMaxLayers) return AWQ_ERR_CONFIG;
+    if (!qweight || !scales_f16 || !zeros_f16 || !N || !y_f16) return AWQ_ERR_NULL;
+    if (M < 0 || M > kMaxDim) return AWQ_ERR_SHAPE;
+    int64_t total = 0;
+    for (int i = 0; i < n_layers; ++i) {
+        const awq_status st = check_dims(N[i], K, group_size);
+        if (st != AWQ_OK) return st;
+        total += N[i];
+        if (M > 0 && N[i] > 0) {
+            if (!x_f16 || !qweight[i] || !scales_f16[i] || !zeros_f16[i] || !y_f16[i]) return AWQ_ERR_NULL;
+            if (!aligned16(x_f16) || !aligned16(qweight[i]) || (reinterpret_cast<uintptr_t>(scales_f16[i]) & 1) ||
+                (reinterpret_cast<uintptr_t>(zeros_f16[i]) & 1) || (reinterpret_cast<uintptr_t>(y_f16[i]) & 1))
+                return AWQ_ERR_ALIGN;
+        }
+    }
+    if (total > (int64_t(1) << 31) - 256) return AWQ_ERR_SHAPE;
+    if (M == 0 || total == 0) return AWQ_OK;
+    const hipStream_t s = as_stream(stream);
+    if (M <= kGemvGroupedMaxM && choose_path(M, total, K, group_size, 0, false) == 1) {
+        GemvLayers L{};
+        int r = 0;
+        for (int i = 0; i < n_layers; ++i) {
+            if (N[i] == 0) continue;
+            L.qweight[L.n] = qweight[i];
+            L.scales[L.n] = static_cast<const half_t*>(scales_f16[i]);
+            L.zeros[L.n] = static_cast<const half_t*>(zeros_f16[i]);
+            L.y[L.n] = static_cast<half_t*>(y_f16[i]);
+            L.row0[L.n] = r;
+            r += static_cast<int>(N[i]);
+            ++L.n;
+        }
+        L.row0[L.n] = r;
+        for (int i = L.n + 1; i <= kGemvMaxLayers; ++i) L.row0[i] = INT32_MAX;
+        return launch_gemv_grouped(static_cast<const half_t*>(x_f16), L, M, K, group_size, s);
+    }
+    for (int i = 0; i < n_layers; ++i) {
+        const awq_status st = gemm_dispatch(x_f16, qweight[i], scales_f16[i], zeros_f16[i], M, N[i], K, group_size,
+                                            y_f16[i], 0, nullptr, 0, false, false, s);
+        if (st != AWQ_OK) return st;
+    }
+    return AWQ_OK;
+}
+
 awq_status awq_gemm_noalloc(const void* x_f16, const uint32_t* qweight, const void* scales_f16,
                             const void* zeros_f16, int64_t M, int64_t N, int64_t K, int group_size, void* y_f16,
                             int path, void* stream) {

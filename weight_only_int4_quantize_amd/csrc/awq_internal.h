@@ -60,6 +60,22 @@ bool gemv_supported(int64_t M, int64_t K, int bits = 4);
 awq_status launch_gemv(const half_t* x, const uint32_t* qweight, const half_t* scales,
                        const half_t* zeros, int64_t M, int64_t N, int64_t K, int group_size,
                        half_t* y, hipStream_t stream, int bits = 4);
+// Several INT4 layers that share x (and K, G) in one GEMV launch: their rows
+// stacked in order, layer i < n owning rows [row0[i], row0[i + 1]), each row
+// read from and written to its own layer's tensors; row0[n] is the total and
+// the entries past it are INT_MAX. M <= kGemvGroupedMaxM.
+constexpr int kGemvMaxLayers = 4;
+constexpr int kGemvGroupedMaxM = 2;
+struct GemvLayers {
+    const uint32_t* qweight[kGemvMaxLayers];
+    const half_t* scales[kGemvMaxLayers];
+    const half_t* zeros[kGemvMaxLayers];
+    half_t* y[kGemvMaxLayers];
+    int row0[kGemvMaxLayers + 1];
+    int n;
+};
+awq_status launch_gemv_grouped(const half_t* x, const GemvLayers& layers, int64_t M, int64_t K, int group_size,
+                               hipStream_t stream);
 
 // MFMA GEMM. The B operand is INT4 or W8 (qweight/scales/zeros) or fp16 W[N, K].
 enum class GemmB { kInt4, kF16, kInt8 };

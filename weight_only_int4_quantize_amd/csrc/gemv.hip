@@ -107,22 +107,59 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), bytes, 0x00020000);
 }
 
+// The layer of stacked row r in a grouped launch (wave-uniform): its
+// tensors, first stacked row and row count. Every field is read
+// unconditionally and picked with selects, so the kernel-argument loads
+// issue together (unused layers start at INT_MAX and are never picked).
+struct LayerRow {
+    const uint32_t* qweight;
+    const half_t* scales;
+    const half_t* zeros;
+    half_t* y;
+    int row0, rows;
+};
+__device__ inline LayerRow layer_of(const GemvLayers& L, int r) {
+    LayerRow o{L.qweight[0], L.scales[0], L.zeros[0], L.y[0], 0, L.row0[1]};
+#pragma unroll
+    for (int i = 1; i < kGemvMaxLayers; ++i) {
+        const bool in = r >= L.row0[i];
+        o.qweight = in ? L.qweight[i] : o.qweight;
+        o.scales = in ? L.scales[i] : o.scales;
+        o.zeros = in ? L.zeros[i] : o.zeros;
+        o.y = in ? L.y[i] : o.y;
+        o.rows = in ? L.row0[i + 1] - L.row0[i] : o.rows;
+        o.row0 = in ? L.row0[i] : o.row0;
+    }
+    return o;
+}
+
 // Issues the loads of one item: RPW rows x CPL chunks per lane (chunk
 // c = base + lane + 64 j), with each chunk's scale and zero-point. Rows past
-// N or items past the wave's last (valid == false) read as zero.
-template <int BITS, int RPW, int CPL>
+// N or items past the wave's last (valid == false) read as zero. GROUPED:
+// row r is row r - row0 of its layer's tensors.
+template <int BITS, int RPW, int CPL, bool GROUPED>
 __device__ inline void load_batch(WeightBatch<RPW, CPL>& b, const uint32_t* __restrict__ qweight,
                                   const half_t* __restrict__ scales, const half_t* __restrict__ zeros,
-                                  int row0, bool valid, int N, int nchunk, int ngroups, int log2g, int base,
-                                  int lane) {
+                                  const GemvLayers& L, int row0, bool valid, int N, int nchunk, int ngroups,
+                                  int log2g, int base, int lane) {
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int row = row0 + i;
         const bool ok = valid && row < N;
-        const int64_t r = ok ? row : 0;
-        const auto rw = rsrc(qweight + r * (nchunk * 4), ok ? nchunk * 16 : 0);
-        const auto rs = rsrc(scales + r * ngroups, ok ? ngroups * 2 : 0);
-        const auto rz = rsrc(zeros + r * ngroups, ok ? ngroups * 2 : 0);
+        int64_t r = ok ? row : 0;
+        const uint32_t* qw = qweight;
+        const half_t* sc = scales;
+        const half_t* zr = zeros;
+        if constexpr (GROUPED) {
+            const LayerRow lr = layer_of(L, static_cast<int>(r));
+            qw = lr.qweight;
+            sc = lr.scales;
+            zr = lr.zeros;
+            r -= lr.row0;
+        }
+        const auto rw = rsrc(qw + r * (nchunk * 4), ok ? nchunk * 16 : 0);
+        const auto rs = rsrc(sc + r * ngroups, ok ? ngroups * 2 : 0);
+        const auto rz = rsrc(zr + r * ngroups, ok ? ngroups * 2 : 0);
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = base + lane + 64 * j;
@@ -196,13 +233,16 @@ __device__ inline float wave_sum_lane63(float v) {
 // DEPTH - 1 are still loading, and its slot is refilled with item t + DEPTH
 // right after. The loads are branch-free, so the compiler's wait counts track
 // the ring exactly. Finished rows go to LDS and are written out at the end.
-template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT, int NW>
+//
+// GROUPED: the rows of several layers sharing x, stacked (L); N is the
+// total, and each row's weights and output belong to its layer.
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT, int NW, bool GROUPED>
 __global__ __launch_bounds__(NW * 64) void gemv_kernel(const half_t* __restrict__ x,
                                                    const uint32_t* __restrict__ qweight,
                                                    const half_t* __restrict__ scales,
                                                    const half_t* __restrict__ zeros,
                                                    half_t* __restrict__ y, int N, int K,
-                                                   int log2g, int max_sets) {
+                                                   int log2g, int max_sets, GemvLayers L) {
     extern __shared__ uint4 smem[];
     constexpr int XV = Chunk<BITS>::kXV;
     const int nchunk = K >> Chunk<BITS>::kShift;    // 32 (INT4) or 16 (W8) weights per chunk
@@ -281,8 +321,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const half_t* __restrict_
     WeightBatch<RPW, CPL> ring[DEPTH];
     int l_item = 0, l_set = 0, l_kb = 0;            // load cursor
     auto issue = [&](WeightBatch<RPW, CPL>& b) {
-        load_batch<BITS>(b, qweight, scales, zeros, (wid + l_set * W) * RPW, l_item < n_items, N, nchunk, ngroups,
-                   log2g, l_kb * 64 * CPL, lane);
+        load_batch<BITS, RPW, CPL, GROUPED>(b, qweight, scales, zeros, L, (wid + l_set * W) * RPW, l_item < n_items,
+                                            N, nchunk, ngroups, log2g, l_kb * 64 * CPL, lane);
         ++l_item;
         if (++l_kb == kbs) { l_kb = 0; ++l_set; }
     };
@@ -298,6 +338,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const half_t* __restrict_
         store_x(c, xr[0]);
     }
     __syncthreads();
+
+    // output element (m, stacked row r)
+    auto store_y = [&](int m, int r, float v) {
+        if constexpr (GROUPED) {
+            const LayerRow lr = layer_of(L, r);
+            lr.y[static_cast<int64_t>(m) * lr.rows + (r - lr.row0)] = static_cast<half_t>(v);
+        } else {
+            y[static_cast<int64_t>(m) * N + r] = static_cast<half_t>(v);
+        }
+    };
 
     // 3. stream
     float acc[RPW][MT];
@@ -322,8 +372,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const half_t* __restrict_
                         for (int m = 0; m < MT; ++m) {
                             const float v = wave_sum_lane63(acc[i][m]);
                             if (ONESHOT) {
-                                if (lane == 63 && r0 + i < N)
-                                    y[static_cast<int64_t>(m) * N + r0 + i] = static_cast<half_t>(v);
+                                if (lane == 63 && r0 + i < N) store_y(m, r0 + i, v);
                             } else if (lane == 63) {
                                 yl[((wave * max_sets + c_set) * RPW + i) * MT + m] = v;
                             }
@@ -352,8 +401,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const half_t* __restrict_
         const int row = (wg + cs * W) * RPW + i;
         if (cs < sets_w && row < N) {
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
-                y[static_cast<int64_t>(m) * N + row] = static_cast<half_t>(yl[sl * MT + m]);
+            for (int m = 0; m < MT; ++m) store_y(m, row, yl[sl * MT + m]);
         }
     }
 }
@@ -377,14 +425,25 @@ size_t gemv_lds_bytes(int64_t M, int64_t K, int bits) {
                      : static_cast<size_t>(M) * static_cast<size_t>(K / 16) * 40;
 }
 
-template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT = false, int NW = 4>
-awq_status launch_t(const half_t* x, const uint32_t* qweight, const half_t* scales,
-                    const half_t* zeros, int64_t N, int64_t K, int log2g, half_t* y,
+// A launch: one layer (qweight, scales, zeros, y of N rows), or with
+// GROUPED the stacked layers of L (N rows in all).
+template <bool GROUPED>
+struct GemvTarget {
+    const uint32_t* qweight;
+    const half_t* scales;
+    const half_t* zeros;
+    half_t* y;
+    GemvLayers L;
+};
+
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT = false, int NW = 4, bool GROUPED = false>
+awq_status launch_t(const half_t* x, const GemvTarget<GROUPED>& tg, int64_t N, int64_t K, int log2g,
                     int64_t blocks, hipStream_t stream) {
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, max_shared_bytes()) != hipSuccess)
+        if (hipFuncSetAttribute(
+                reinterpret_cast<const void*>(&gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, GROUPED>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, max_shared_bytes()) != hipSuccess)
             return AWQ_ERR_HIP;
         attr_set = true;
     }
@@ -395,9 +454,10 @@ awq_status launch_t(const half_t* x, const uint32_t* qweight, const half_t* scal
     if (ONESHOT && max_sets * ceil_div(nchunk, 64 * CPL) > DEPTH) return AWQ_ERR_SHAPE;   // launch-shape bug
     const size_t lds = gemv_lds_bytes(MT, K, BITS) + (ONESHOT ? 0 : static_cast<size_t>(NW * max_sets * RPW * MT) * sizeof(float));
     if (lds > static_cast<size_t>(max_shared_bytes())) return AWQ_ERR_SHAPE;
-    hipLaunchKernelGGL((gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), lds,
-                       stream, x, qweight, scales, zeros, y, static_cast<int>(N), static_cast<int>(K),
-                       log2g, static_cast<int>(max_sets));
+    hipLaunchKernelGGL((gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, GROUPED>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), lds, stream, x, tg.qweight, tg.scales,
+                       tg.zeros, tg.y, static_cast<int>(N), static_cast<int>(K), log2g, static_cast<int>(max_sets),
+                       tg.L);
     return last_launch_status();
 }
 
@@ -418,28 +478,24 @@ awq_status launch_t(const half_t* x, const uint32_t* qweight, const half_t* scal
 //    of more than 3 items. Against 4 waves with a 4-deep ring (the same bytes
 //    in flight): 4096 x 11008 7.85 -> 7.13 us, 8192 x 28672 25.4 -> 24.1 us;
 //    8 waves with a 4-deep ring or 16 waves with a 2-deep one are slower.
-template <int BITS, int MT>
-awq_status launch_m(const half_t* x, const uint32_t* qweight, const half_t* scales,
-                    const half_t* zeros, int64_t N, int64_t K, int log2g, half_t* y,
+template <int BITS, int MT, bool GROUPED = false>
+awq_status launch_m(const half_t* x, const GemvTarget<GROUPED>& tg, int64_t N, int64_t K, int log2g,
                     hipStream_t stream) {
     const int64_t kbs = ceil_div(K >> Chunk<BITS>::kShift, 128);
     if (kbs == 1) {
         if (MT >= 2 && ceil_div(N, 16) >= 256)
-            return launch_t<BITS, MT, 4, 2, 1, true>(x, qweight, scales, zeros, N, K, log2g, y, ceil_div(N, 16),
-                                                     stream);
+            return launch_t<BITS, MT, 4, 2, 1, true, 4, GROUPED>(x, tg, N, K, log2g, ceil_div(N, 16), stream);
         if (ceil_div(N, 8) >= 512)
-            return launch_t<BITS, MT, 2, 2, 1, true>(x, qweight, scales, zeros, N, K, log2g, y, ceil_div(N, 8),
-                                                     stream);
-        return launch_t<BITS, MT, 1, 2, 1, true>(x, qweight, scales, zeros, N, K, log2g, y, ceil_div(N, 4), stream);
+            return launch_t<BITS, MT, 2, 2, 1, true, 4, GROUPED>(x, tg, N, K, log2g, ceil_div(N, 8), stream);
+        return launch_t<BITS, MT, 1, 2, 1, true, 4, GROUPED>(x, tg, N, K, log2g, ceil_div(N, 4), stream);
     }
     if (kbs == 2 && BITS == 8)
-        return launch_t<BITS, MT, 1, 2, 2, true>(x, qweight, scales, zeros, N, K, log2g, y, ceil_div(N, 4), stream);
+        return launch_t<BITS, MT, 1, 2, 2, true, 4, GROUPED>(x, tg, N, K, log2g, ceil_div(N, 4), stream);
     const int64_t x_lds = static_cast<int64_t>(gemv_lds_bytes(MT, K, BITS));
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kGemvBlocksPerCu, max_shared_bytes() / (x_lds + 2048)));
     if (MT >= 2 || kbs > 3)
-        return launch_t<BITS, MT, 2, 2, 2, false, 8>(x, qweight, scales, zeros, N, K, log2g, y, per_cu * cu_count(),
-                                                     stream);
-    return launch_t<BITS, MT, 1, 2, 2, false, 8>(x, qweight, scales, zeros, N, K, log2g, y, per_cu * cu_count(), stream);
+        return launch_t<BITS, MT, 2, 2, 2, false, 8, GROUPED>(x, tg, N, K, log2g, per_cu * cu_count(), stream);
+    return launch_t<BITS, MT, 1, 2, 2, false, 8, GROUPED>(x, tg, N, K, log2g, per_cu * cu_count(), stream);
 }
 
 }  // namespace
@@ -454,15 +510,16 @@ namespace {
 template <int BITS>
 awq_status launch_gemv_bits(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros,
                             int64_t M, int64_t N, int64_t K, int log2g, half_t* y, hipStream_t stream) {
+    const GemvTarget<false> tg{qweight, scales, zeros, y, GemvLayers{}};
     switch (M) {
-        case 1: return launch_m<BITS, 1>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        case 2: return launch_m<BITS, 2>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        case 3: return launch_m<BITS, 3>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        case 4: return launch_m<BITS, 4>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        case 5: return launch_m<BITS, 5>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        case 6: return launch_m<BITS, 6>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        case 7: return launch_m<BITS, 7>(x, qweight, scales, zeros, N, K, log2g, y, stream);
-        case 8: return launch_m<BITS, 8>(x, qweight, scales, zeros, N, K, log2g, y, stream);
+        case 1: return launch_m<BITS, 1>(x, tg, N, K, log2g, stream);
+        case 2: return launch_m<BITS, 2>(x, tg, N, K, log2g, stream);
+        case 3: return launch_m<BITS, 3>(x, tg, N, K, log2g, stream);
+        case 4: return launch_m<BITS, 4>(x, tg, N, K, log2g, stream);
+        case 5: return launch_m<BITS, 5>(x, tg, N, K, log2g, stream);
+        case 6: return launch_m<BITS, 6>(x, tg, N, K, log2g, stream);
+        case 7: return launch_m<BITS, 7>(x, tg, N, K, log2g, stream);
+        case 8: return launch_m<BITS, 8>(x, tg, N, K, log2g, stream);
         default: return AWQ_ERR_SHAPE;
     }
 }
@@ -474,6 +531,18 @@ awq_status launch_gemv(const half_t* x, const uint32_t* qweight, const half_t* s
     const int log2g = 31 - __builtin_clz(static_cast<unsigned>(group_size));   // G is a power of two >= 32
     if (bits == 8) return launch_gemv_bits<8>(x, qweight, scales, zeros, M, N, K, log2g, y, stream);
     return launch_gemv_bits<4>(x, qweight, scales, zeros, M, N, K, log2g, y, stream);
+}
+
+awq_status launch_gemv_grouped(const half_t* x, const GemvLayers& layers, int64_t M, int64_t K, int group_size,
+                               hipStream_t stream) {
+    const int log2g = 31 - __builtin_clz(static_cast<unsigned>(group_size));
+    const int64_t N = layers.row0[layers.n];
+    const GemvTarget<true> tg{nullptr, nullptr, nullptr, nullptr, layers};
+    switch (M) {
+        case 1: return launch_m<4, 1, true>(x, tg, N, K, log2g, stream);
+        case 2: return launch_m<4, 2, true>(x, tg, N, K, log2g, stream);
+        default: return AWQ_ERR_SHAPE;
+    }
 }
 
 }  // namespace awq
