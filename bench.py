@@ -3,15 +3,18 @@ prefill GEMM TFLOP/s (M = 2048), each against its roofline.
 
 A step is one decode pass over the seven linear layers of a Llama-7B-shaped
 decoder layer (q/k/v/o 4096x4096, gate/up 11008x4096, down 4096x11008; INT4,
-group 128, zero-points) at M = 1 through awq_gemm. The weights rotate over
+group 128, zero-points; seven weight tensors) at M = 1, in the order a
+decoder layer allows: q/k/v in one awq_gemm_grouped launch (they read the
+same x), o, gate/up in one grouped launch, down. The weights rotate over
 enough copies (> 1.2 GB) that the 256 MB last-level cache cannot hold them,
 so every step streams its weights from HBM; the steps are replayed from HIP
 graphs, so host launch cost is outside the timed kernels. `value` is the
 step's algorithmic bytes over its time.
 
 The same run also times, each in its own section:
-  * the roofline kernel: the gate/up GEMV (11008x4096, the largest launch of
-    the step) back to back over the rotated copies;
+  * the same step as seven awq_gemm launches, one per layer;
+  * each GEMV launch of the step on its own, back to back over the rotated
+    copies (the per-launch roofline fractions);
   * the same layer with fused q/k/v (12288x4096) and gate/up (22016x4096)
     projections, four launches per step;
   * the per-node floor of a graph of tiny kernels (launch cost context);
@@ -51,6 +54,9 @@ HBM_PEAK_GBS = 8000.0
 F16_MFMA_PEAK_TFLOPS = 2500.0
 G = 128
 ROOFLINE_SHAPE = (11008, 4096)     # gate/up projection, the step's largest launch
+# The decode step's launches: layers of synth.LLAMA7B_LAYER by index; q/k/v
+# and gate/up read the same x and run as one grouped launch each.
+DECODE_GROUPS = (("qkv", (0, 1, 2)), ("o_proj", (3,)), ("gate_up", (4, 5)), ("down_proj", (6,)))
 COPY_BYTES = 1 << 30
 CLIP_BENCH_FRACTION = 0.01                                # the clip of xxmr.cn §1.5
 CLIP_GRID = [0.0, 0.001, 0.002, 0.005, 0.01, 0.02]       # clip-search fractions
@@ -60,6 +66,24 @@ def gemv_bytes(M, N, K, g=G):
     """Algorithmic bytes of one W4A16 product: packed codes, fp16 scale and
     zero per group, fp16 x in, fp16 y out."""
     return N * K // 2 + N * (K // g) * 4 + M * K * 2 + M * N * 2
+
+
+def grouped_bytes(M, shapes, g=G):
+    """Algorithmic bytes of one grouped launch over layers (N, K) sharing x:
+    every layer's codes, scales, zeros and y, and x once."""
+    K = shapes[0][1]
+    return sum(N * K // 2 + N * (K // g) * 4 + M * N * 2 for (N, _) in shapes) + M * K * 2
+
+
+def step_launches(linears):
+    """(label, layer indices, algorithmic bytes) of each launch of the decode
+    step."""
+    out = []
+    for name, idx in DECODE_GROUPS:
+        shapes = [(linears[j][1], linears[j][2]) for j in idx]
+        label = f"{len(idx)}x{shapes[0][0]}x{shapes[0][1]}" if len(idx) > 1 else f"{shapes[0][0]}x{shapes[0][1]}"
+        out.append((label, idx, grouped_bytes(1, shapes)))
+    return out
 
 
 def quantize_bytes(N, K, g=G):
@@ -92,8 +116,8 @@ def measured_traffic(linears):
             rec = json.load(f)
         if source_sha256(GEMV_SOURCE) != rec.get("gemv_source_sha256"):
             return None, None
-        by_shape = {(g["N"], g["K"]): g for g in rec["groups"] if g["kind"] == "gemv"}
-        total = sum(by_shape[(N, K)]["traffic_bytes"] for (_, N, K) in linears)
+        by_label = {g["label"]: g for g in rec["groups"] if g["kind"] == "gemv"}
+        total = sum(by_label[f"gemv_M1_{label}"]["traffic_bytes"] for (label, _, _) in step_launches(linears))
         calib = next(g for g in rec["groups"] if g["kind"] == "copy")
     except (OSError, KeyError, ValueError, StopIteration):
         return None, None
@@ -163,7 +187,9 @@ class Bench:
             qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), G)
             shapes[(N, K)] = (qw, sc, zr, self.d(lay["x"]))
         self.linears = list(synth.LLAMA7B_LAYER)
-        self.step_bytes = sum(gemv_bytes(1, N, K) for (_, N, K) in self.linears)
+        self.launches = step_launches(self.linears)
+        self.step_bytes = sum(b for (_, _, b) in self.launches)
+        self.step_bytes_seven = sum(gemv_bytes(1, N, K) for (_, N, K) in self.linears)
         self.n_copies = max(2, int(np.ceil(1.2e9 / self.step_bytes)))
         self.copies = []
         for _ in range(self.n_copies):
@@ -175,20 +201,37 @@ class Bench:
             self.copies.append(layer)
         torch.cuda.synchronize()
 
+    def launch(self, layer, idx):
+        """One launch of the step: the layers idx of a copy (one awq_gemm, or
+        one awq_gemm_grouped when they share x)."""
+        if len(idx) == 1:
+            qw, sc, zr, x, y, _, _ = layer[idx[0]]
+            self.awq.awq_gemm(x, qw, sc, zr, G, out=y)
+        else:
+            self.awq.awq_gemm_grouped(layer[idx[0]][3], [layer[j][:3] for j in idx], G,
+                                      outs=[layer[j][4] for j in idx])
+
     def decode_step(self, i):
+        layer = self.copies[i % self.n_copies]
+        for (_, idx, _) in self.launches:
+            self.launch(layer, idx)
+
+    def decode_step_seven(self, i):
         for (qw, sc, zr, x, y, N, K) in self.copies[i % self.n_copies]:
             self.awq.awq_gemm(x, qw, sc, zr, G, out=y)
 
-    def run_decode(self):
+    def run_decode(self, step_fn=None, step_bytes=None, label="decode layer"):
         args = self.args
+        step_fn = step_fn or self.decode_step
+        step_bytes = step_bytes or self.step_bytes
         for i in range(max(args.warmup, 1)):
-            self.decode_step(i)
+            step_fn(i)
         self.torch.cuda.synchronize()
         # one graph per full rotation over the copies, one for the rest, so
         # that exactly args.steps steps are timed
-        g_full = self.capture(self.decode_step, self.n_copies)
+        g_full = self.capture(step_fn, self.n_copies)
         rem = args.steps % self.n_copies
-        g_rem = self.capture(self.decode_step, rem) if rem else None
+        g_rem = self.capture(step_fn, rem) if rem else None
         n_full = args.steps // self.n_copies
 
         def steps(_):
@@ -200,9 +243,15 @@ class Bench:
         g_full.replay()
         t = self.time(steps)
         ms = t / args.steps * 1e3
-        value = self.step_bytes * args.steps / t / 1e9
-        log(f"decode layer: {ms * 1e3:.2f} us/step, {value:.0f} GB/s")
+        value = step_bytes * args.steps / t / 1e9
+        log(f"{label}: {ms * 1e3:.2f} us/step, {value:.0f} GB/s")
         return value, ms
+
+    def run_decode_seven(self):
+        """The same step as seven awq_gemm launches, one per layer."""
+        value, ms = self.run_decode(self.decode_step_seven, self.step_bytes_seven, "decode layer, seven launches")
+        return {"launches": 7, "us_per_step": round(ms * 1e3, 2), "step_bytes": self.step_bytes_seven,
+                "GB/s": round(value, 1), "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)}
 
     def run_decode_fused(self):
         """The decoder layer with fused q/k/v and gate/up projections: four
@@ -516,6 +565,25 @@ class Bench:
         log(f"graph launch floor: {us:.2f} us per node")
         return round(us, 3)
 
+    def run_step_launches(self):
+        """Each launch of the decode step on its own, back to back over the
+        rotated copies."""
+        out = {}
+        for (label, idx, b) in self.launches:
+            def one(i, idx=idx):
+                self.launch(self.copies[i % self.n_copies], idx)
+
+            reps = 8 * self.n_copies
+            g1 = self.capture(one, reps)
+            g1.replay()
+            t = self.time(lambda _: g1.replay(), 4) / (4 * reps)
+            out[label] = {"us": round(t * 1e6, 3), "GB/s": round(b / t / 1e9, 1), "bytes": b,
+                          "launches_timed": 4 * reps,
+                          "layers": [self.linears[j][0] for j in idx]}
+            log(f"step launch {label}: {t * 1e6:.2f} us, {b / t / 1e9:.0f} GB/s")
+            del g1
+        return out
+
     def run_gemv_shapes(self, shapes):
         """Back-to-back launches of one shape over the rotated copies."""
         out = {}
@@ -740,6 +808,27 @@ class Bench:
             manifest.append({"label": f"gemv_M1_{N}x{K}", "kind": "gemv", "M": 1, "N": N, "K": K,
                              "bytes": gemv_bytes(1, N, K), "launches": reps})
             del cps, qw, sc, zr
+        # the decode step's grouped launches (layers of their own weights, one x)
+        for (label, idx, nbytes) in step_launches(list(synth.LLAMA7B_LAYER)):
+            if len(idx) == 1:
+                continue
+            shapes = [synth.LLAMA7B_LAYER[j][1:] for j in idx]
+            K = shapes[0][1]
+            parts = []
+            for j, (N, _) in enumerate(shapes):
+                lay = synth.decode_layer(N, K, 1)
+                qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), G)
+                parts.append([(qw.clone(), sc.clone(), zr.clone()) for _ in range(reps)])
+                x = self.d(lay["x"])
+            ys = [torch.empty((1, N), dtype=torch.float16, device=self.dev) for (N, _) in shapes]
+            torch.cuda.synchronize()
+            for i in range(reps):
+                awq.awq_gemm_grouped(x, [p[i] for p in parts], G, outs=ys)
+            torch.cuda.synchronize()
+            manifest.append({"label": f"gemv_M1_{label}", "kind": "gemv", "M": 1,
+                             "N": sum(N for (N, _) in shapes), "K": K, "layers": len(idx), "bytes": nbytes,
+                             "launches": reps})
+            del parts
         ws = awq.gemm_workspace(synth.PREFILL_M, 11008, 11008, self.dev)
         gemm_shapes = [(synth.PREFILL_M, N, K) for (N, K) in synth.PREFILL_SHAPES] + \
                       [(512, N, K) for (N, K) in synth.SWEEP_SHAPES]
@@ -1009,6 +1098,8 @@ def main():
 
     b.setup_decode()
     value, ms_per_step = b.run_decode()
+    seven = b.run_decode_seven()
+    per_launch = b.run_step_launches()
     per_shape = b.run_gemv_shapes(synth.DECODE_SHAPES)
     del b.copies
     fused = b.run_decode_fused()
@@ -1040,21 +1131,24 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": "llama7b_decoder_layer_decode_m1_int4_g128", "M": 1, "group_size": G,
-                   "linears": [f"{n}:{N}x{K}" for (n, N, K) in b.linears], "weight_copies": b.n_copies,
-                   "step_bytes": b.step_bytes},
+                   "linears": [f"{n}:{N}x{K}" for (n, N, K) in b.linears],
+                   "launches": [f"{name}:{label}" for (name, _), (label, _, _) in zip(DECODE_GROUPS, b.launches)],
+                   "weight_copies": b.n_copies, "step_bytes": b.step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_unit": "HBM bytes per step: FETCH_SIZE x fetch_factor + WRITE_SIZE x "
-                                     "write_factor summed over the step's seven GEMV launches",
+                                     "write_factor summed over the step's four GEMV launches",
                      "traffic_calibration": calib,
-                     "kernel": "gemv, the seven M=1 launches of one decode step (one graph replay)",
+                     "kernel": "gemv, the four M=1 launches of one decode step (q/k/v grouped, o, gate/up "
+                               "grouped, down; one graph replay)",
                      "bytes_per_launch": b.step_bytes, "launch_us": round(ms_per_step * 1e3, 3),
-                     "per_shape": {k: {**v, "frac": round(v["GB/s"] / HBM_PEAK_GBS, 4)} for k, v in per_shape.items()},
+                     "per_launch": {k: {**v, "frac": round(v["GB/s"] / HBM_PEAK_GBS, 4)} for k, v in per_launch.items()},
                      "frac_of_copy_bandwidth": round(value / copy["GB/s"], 4),
                      "graph_launch_floor_us": floor_us},
         "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "decode_seven_launches": seven,
         "hbm_copy_1GiB": copy,
-        "gemv_per_shape": per_shape,
+        "gemv_per_shape": {k: {**v, "frac": round(v["GB/s"] / HBM_PEAK_GBS, 4)} for k, v in per_shape.items()},
         "decode_fused": fused,
         "decode_model": model,
         "skinny_batched_decode": skinny,

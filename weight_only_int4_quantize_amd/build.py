@@ -31,6 +31,17 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source flags. The decode kernels (GEMV, column tiles, skinny) are
+# short and launched back to back, so a wave's first kernel-argument load
+# sits on the critical path of every launch; the hardware preloads the
+# arguments into SGPRs instead, as many as fit beside the argument pointer
+# (14 dwords; the rest are loaded as usual). Measured on the GEMV (us, M = 1):
+# 4096 x 4096 4.09 -> 3.83, 11008 x 4096 6.71 -> 6.30, 4096 x 11008
+# 7.55 -> 7.18.
+_PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
+SOURCE_FLAGS = {"gemv.hip": _PRELOAD, "coltile.hip": _PRELOAD, "skinny.hip": _PRELOAD}
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -71,7 +82,8 @@ def build(verbose: bool = False, extra_flags=None, out_path: str = LIB_PATH, obj
     for src in sources():
         obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
         objs.append(obj)
-        procs.append(_run([hipcc(), *compile_flags, "-c", src, "-o", obj], verbose))
+        flags = compile_flags + SOURCE_FLAGS.get(os.path.basename(src), [])
+        procs.append(_run([hipcc(), *flags, "-c", src, "-o", obj], verbose))
         if len(procs) >= jobs:
             _finish(procs.pop(0), verbose)
     for p in procs:

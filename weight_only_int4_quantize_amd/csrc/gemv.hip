@@ -30,6 +30,7 @@
 // so sum_k x_k (q_k - z) = dot - off - z * xs, then scaled by the group's
 // scale in fp32. The weight is never rounded to fp16.
 #include <algorithm>
+#include <type_traits>
 
 #include "awq_internal.h"
 
@@ -137,10 +138,10 @@ __device__ inline LayerRow layer_of(const GemvLayers& L, int r) {
 // c = base + lane + 64 j), with each chunk's scale and zero-point. Rows past
 // N or items past the wave's last (valid == false) read as zero. GROUPED:
 // row r is row r - row0 of its layer's tensors.
-template <int BITS, int RPW, int CPL, bool GROUPED>
+template <int BITS, int RPW, int CPL, bool GROUPED, typename LT>
 __device__ inline void load_batch(WeightBatch<RPW, CPL>& b, const uint32_t* __restrict__ qweight,
                                   const half_t* __restrict__ scales, const half_t* __restrict__ zeros,
-                                  const GemvLayers& L, int row0, bool valid, int N, int nchunk, int ngroups,
+                                  const LT& L, int row0, bool valid, int N, int nchunk, int ngroups,
                                   int log2g, int base, int lane) {
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
@@ -236,15 +237,25 @@ __device__ inline float wave_sum_lane63(float v) {
 //
 // GROUPED: the rows of several layers sharing x, stacked (L); N is the
 // total, and each row's weights and output belong to its layer.
+struct NoLayers {};
+template <bool GROUPED>
+using LayersArg = std::conditional_t<GROUPED, GemvLayers, NoLayers>;
+
 template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT, int NW, bool GROUPED>
-__global__ __launch_bounds__(NW * 64) void gemv_kernel(const half_t* __restrict__ x,
-                                                   const uint32_t* __restrict__ qweight,
-                                                   const half_t* __restrict__ scales,
-                                                   const half_t* __restrict__ zeros,
-                                                   half_t* __restrict__ y, int N, int K,
-                                                   int log2g, int max_sets, GemvLayers L) {
+__device__ __forceinline__ void gemv_body(const half_t* __restrict__ x, const uint32_t* __restrict__ qweight,
+                                          const half_t* __restrict__ scales, const half_t* __restrict__ zeros,
+                                          half_t* __restrict__ y, int N, int K, int log2g, int max_sets,
+                                          int nblocks, const LayersArg<GROUPED>& L) {
     extern __shared__ uint4 smem[];
     constexpr int XV = Chunk<BITS>::kXV;
+    if constexpr (GROUPED) {
+        // the layer table is wanted before the first weight load: fetch all
+        // of it with the other arguments, in one round trip
+#pragma unroll
+        for (int i = 0; i < kGemvMaxLayers; ++i)
+            asm volatile("" ::"s"(L.qweight[i]), "s"(L.scales[i]), "s"(L.zeros[i]), "s"(L.y[i]), "s"(L.row0[i]));
+        asm volatile("" ::"s"(L.row0[kGemvMaxLayers]));
+    }
     const int nchunk = K >> Chunk<BITS>::kShift;    // 32 (INT4) or 16 (W8) weights per chunk
     // x pairs [MT][XV][nchunk]: lanes reading one v of consecutive chunks
     // hit consecutive 16-byte slots (no bank conflicts)
@@ -260,7 +271,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const half_t* __restrict_
 
     const int kbs = (nchunk + 64 * CPL - 1) / (64 * CPL);      // k-batches per row
     const int nsets = (N + RPW - 1) / RPW;                      // row sets
-    const int W = gridDim.x * NW;
+    const int W = nblocks * NW;
     const int wid = blockIdx.x * NW + wave;
     const int my_sets = wid < nsets ? (nsets - 1 - wid) / W + 1 : 0;
     const int n_items = my_sets * kbs;
@@ -406,6 +417,30 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const half_t* __restrict_
     }
 }
 
+// The kernels. Every argument of the single-layer form, the grid size
+// included (nblocks == gridDim.x), is in its first 14 dwords (log2 G and
+// max_sets share one: shape = log2g | max_sets << 8), which the build has the
+// hardware preload into SGPRs, so no wave waits on a kernel-argument load.
+// Reading past them costs: a launch that also read the hidden grid-size
+// argument, on a second 64-byte line, took 4-9% longer on the one-shot
+// shapes (4096 x 4096: 4.06 -> 4.42 us).
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT, int NW>
+__global__ __launch_bounds__(NW * 64) void gemv_kernel(const half_t* __restrict__ x,
+                                                   const uint32_t* __restrict__ qweight,
+                                                   const half_t* __restrict__ scales,
+                                                   const half_t* __restrict__ zeros,
+                                                   half_t* __restrict__ y, int N, int K, int shape,
+                                                   int nblocks) {
+    gemv_body<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, false>(x, qweight, scales, zeros, y, N, K, shape & 0xFF,
+                                                              shape >> 8, nblocks, NoLayers{});
+}
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT, int NW>
+__global__ __launch_bounds__(NW * 64) void gemv_grouped_kernel(const half_t* __restrict__ x, int N, int K,
+                                                           int log2g, int max_sets, int nblocks, GemvLayers L) {
+    gemv_body<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, true>(x, nullptr, nullptr, nullptr, nullptr, N, K, log2g,
+                                                             max_sets, nblocks, L);
+}
+
 int max_shared_bytes() {
     static int cached = -1;
     if (cached < 0) {
@@ -433,17 +468,17 @@ struct GemvTarget {
     const half_t* scales;
     const half_t* zeros;
     half_t* y;
-    GemvLayers L;
+    LayersArg<GROUPED> L;
 };
 
 template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT = false, int NW = 4, bool GROUPED = false>
 awq_status launch_t(const half_t* x, const GemvTarget<GROUPED>& tg, int64_t N, int64_t K, int log2g,
                     int64_t blocks, hipStream_t stream) {
+    const void* kern = GROUPED ? reinterpret_cast<const void*>(&gemv_grouped_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>)
+                               : reinterpret_cast<const void*>(&gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>);
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute(
-                reinterpret_cast<const void*>(&gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, GROUPED>),
-                hipFuncAttributeMaxDynamicSharedMemorySize, max_shared_bytes()) != hipSuccess)
+        if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, max_shared_bytes()) != hipSuccess)
             return AWQ_ERR_HIP;
         attr_set = true;
     }
@@ -452,12 +487,17 @@ awq_status launch_t(const half_t* x, const GemvTarget<GROUPED>& tg, int64_t N, i
     const int64_t max_sets = ceil_div(sets, blocks * NW);
     const int64_t nchunk = K >> Chunk<BITS>::kShift;
     if (ONESHOT && max_sets * ceil_div(nchunk, 64 * CPL) > DEPTH) return AWQ_ERR_SHAPE;   // launch-shape bug
+    if (max_sets >= (int64_t{1} << 23)) return AWQ_ERR_SHAPE;                              // packed with log2 G
     const size_t lds = gemv_lds_bytes(MT, K, BITS) + (ONESHOT ? 0 : static_cast<size_t>(NW * max_sets * RPW * MT) * sizeof(float));
     if (lds > static_cast<size_t>(max_shared_bytes())) return AWQ_ERR_SHAPE;
-    hipLaunchKernelGGL((gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, GROUPED>),
-                       dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), lds, stream, x, tg.qweight, tg.scales,
-                       tg.zeros, tg.y, static_cast<int>(N), static_cast<int>(K), log2g, static_cast<int>(max_sets),
-                       tg.L);
+    if constexpr (GROUPED)
+        hipLaunchKernelGGL((gemv_grouped_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>),
+                           dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), lds, stream, x, static_cast<int>(N),
+                           static_cast<int>(K), log2g, static_cast<int>(max_sets), static_cast<int>(blocks), tg.L);
+    else
+        hipLaunchKernelGGL((gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(NW * 64), lds, stream, x, tg.qweight, tg.scales, tg.zeros, tg.y, static_cast<int>(N),
+                           static_cast<int>(K), log2g | static_cast<int>(max_sets << 8), static_cast<int>(blocks));
     return last_launch_status();
 }
 
@@ -510,7 +550,7 @@ namespace {
 template <int BITS>
 awq_status launch_gemv_bits(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros,
                             int64_t M, int64_t N, int64_t K, int log2g, half_t* y, hipStream_t stream) {
-    const GemvTarget<false> tg{qweight, scales, zeros, y, GemvLayers{}};
+    const GemvTarget<false> tg{qweight, scales, zeros, y, NoLayers{}};
     switch (M) {
         case 1: return launch_m<BITS, 1>(x, tg, N, K, log2g, stream);
         case 2: return launch_m<BITS, 2>(x, tg, N, K, log2g, stream);
