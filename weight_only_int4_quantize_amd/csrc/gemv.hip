@@ -108,66 +108,96 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), bytes, 0x00020000);
 }
 
-// The layer of stacked row r in a grouped launch (wave-uniform): its
-// tensors, first stacked row and row count. Every field is read
-// unconditionally and picked with selects, so the kernel-argument loads
-// issue together (unused layers start at INT_MAX and are never picked).
-struct LayerRow {
-    const uint32_t* qweight;
-    const half_t* scales;
-    const half_t* zeros;
-    half_t* y;
-    int row0, rows;
+// The layer table of a grouped launch of up to four layers (built in the
+// kernel from its arguments, as scalars: an array indexed by the layer
+// number went to scratch memory). The layers' packed-weight pointers and
+// the first stacked rows of layers 1-3 arrive in preloaded SGPRs (up to
+// three layers), so a wave's weight loads wait for no scalar load; the
+// scale, zero-point and output pointers come by scalar loads issued at the
+// start, which the weight loads do not wait for.
+struct GemvLayerTable {
+    const uint32_t *q0, *q1, *q2, *q3;
+    const half_t *s0, *s1, *s2, *s3;
+    const half_t *z0, *z1, *z2, *z3;
+    half_t *y0, *y1, *y2, *y3;
+    int b1, b2, b3;   // first stacked rows of layers 1-3
 };
-__device__ inline LayerRow layer_of(const GemvLayers& L, int r) {
-    LayerRow o{L.qweight[0], L.scales[0], L.zeros[0], L.y[0], 0, L.row0[1]};
-#pragma unroll
-    for (int i = 1; i < kGemvMaxLayers; ++i) {
-        const bool in = r >= L.row0[i];
-        o.qweight = in ? L.qweight[i] : o.qweight;
-        o.scales = in ? L.scales[i] : o.scales;
-        o.zeros = in ? L.zeros[i] : o.zeros;
-        o.y = in ? L.y[i] : o.y;
-        o.rows = in ? L.row0[i + 1] - L.row0[i] : o.rows;
-        o.row0 = in ? L.row0[i] : o.row0;
-    }
-    return o;
+// the value of stacked row r's layer among NL: selects on compares with
+// the bounds (a select chain on a layer number was turned into an indexed
+// stack array, in scratch memory)
+template <int NL, typename T>
+__device__ inline T pick_row(const GemvLayerTable& L, int r, T a0, T a1, T a2, T a3) {
+    T v = a0;
+    if constexpr (NL > 1) v = r >= L.b1 ? a1 : v;
+    if constexpr (NL > 2) v = r >= L.b2 ? a2 : v;
+    if constexpr (NL > 3) v = r >= L.b3 ? a3 : v;
+    return v;
 }
+struct NoLayers {};
+template <int NL>
+using LayersArg = std::conditional_t<(NL > 0), GemvLayerTable, NoLayers>;
 
 // Issues the loads of one item: RPW rows x CPL chunks per lane (chunk
 // c = base + lane + 64 j), with each chunk's scale and zero-point. Rows past
-// N or items past the wave's last (valid == false) read as zero. GROUPED:
-// row r is row r - row0 of its layer's tensors.
-template <int BITS, int RPW, int CPL, bool GROUPED, typename LT>
+// N or items past the wave's last (valid == false) read as zero. NL > 0 (a
+// grouped launch): row r is row r - start of its layer's tensors, and every
+// weight load is issued before the scale and zero-point loads, whose
+// pointers come later.
+template <int BITS, int RPW, int CPL, int NL>
 __device__ inline void load_batch(WeightBatch<RPW, CPL>& b, const uint32_t* __restrict__ qweight,
                                   const half_t* __restrict__ scales, const half_t* __restrict__ zeros,
-                                  const LT& L, int row0, bool valid, int N, int nchunk, int ngroups,
+                                  const LayersArg<NL>& L, int row0, bool valid, int N, int nchunk, int ngroups,
                                   int log2g, int base, int lane) {
+    if constexpr (NL > 0) {
+        int lay[RPW];   // the stacked row
+        int64_t lr[RPW];
+        bool ok[RPW];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int row = row0 + i;
-        const bool ok = valid && row < N;
-        int64_t r = ok ? row : 0;
-        const uint32_t* qw = qweight;
-        const half_t* sc = scales;
-        const half_t* zr = zeros;
-        if constexpr (GROUPED) {
-            const LayerRow lr = layer_of(L, static_cast<int>(r));
-            qw = lr.qweight;
-            sc = lr.scales;
-            zr = lr.zeros;
-            r -= lr.row0;
+        for (int i = 0; i < RPW; ++i) {
+            const int row = row0 + i;
+            ok[i] = valid && row < N;
+            const int r = ok[i] ? row : 0;
+            lay[i] = r;
+            lr[i] = r - pick_row<NL>(L, r, 0, L.b1, L.b2, L.b3);
+            const auto rw = rsrc(pick_row<NL>(L, r, L.q0, L.q1, L.q2, L.q3) + lr[i] * (nchunk * 4),
+                                 ok[i] ? nchunk * 16 : 0);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j)
+                b.w[i][j] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, (base + lane + 64 * j) * 16, 0, 0));
         }
-        const auto rw = rsrc(qw + r * (nchunk * 4), ok ? nchunk * 16 : 0);
-        const auto rs = rsrc(sc + r * ngroups, ok ? ngroups * 2 : 0);
-        const auto rz = rsrc(zr + r * ngroups, ok ? ngroups * 2 : 0);
+        // keeps the scale and zero-point addressing (which waits for the
+        // scalar loads of their pointers) behind every weight load
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const int c = base + lane + 64 * j;
-            const int g = (c << Chunk<BITS>::kShift) >> log2g;
-            b.w[i][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, c * 16, 0, 0));
-            b.s[i][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, g * 2, 0, 0);
-            b.z[i][j] = __builtin_amdgcn_raw_buffer_load_b16(rz, g * 2, 0, 0);
+        for (int i = 0; i < RPW; ++i) {
+            const int r = lay[i];
+            const auto rs = rsrc(pick_row<NL>(L, r, L.s0, L.s1, L.s2, L.s3) + lr[i] * ngroups, ok[i] ? ngroups * 2 : 0);
+            const auto rz = rsrc(pick_row<NL>(L, r, L.z0, L.z1, L.z2, L.z3) + lr[i] * ngroups, ok[i] ? ngroups * 2 : 0);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int g = ((base + lane + 64 * j) << Chunk<BITS>::kShift) >> log2g;
+                b.s[i][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, g * 2, 0, 0);
+                b.z[i][j] = __builtin_amdgcn_raw_buffer_load_b16(rz, g * 2, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int row = row0 + i;
+            const bool ok = valid && row < N;
+            const int64_t r = ok ? row : 0;
+            const auto rw = rsrc(qweight + r * (nchunk * 4), ok ? nchunk * 16 : 0);
+            const auto rs = rsrc(scales + r * ngroups, ok ? ngroups * 2 : 0);
+            const auto rz = rsrc(zeros + r * ngroups, ok ? ngroups * 2 : 0);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int c = base + lane + 64 * j;
+                const int g = (c << Chunk<BITS>::kShift) >> log2g;
+                b.w[i][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, c * 16, 0, 0));
+                b.s[i][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, g * 2, 0, 0);
+                b.z[i][j] = __builtin_amdgcn_raw_buffer_load_b16(rz, g * 2, 0, 0);
+            }
         }
     }
 }
@@ -235,27 +265,15 @@ __device__ inline float wave_sum_lane63(float v) {
 // right after. The loads are branch-free, so the compiler's wait counts track
 // the ring exactly. Finished rows go to LDS and are written out at the end.
 //
-// GROUPED: the rows of several layers sharing x, stacked (L); N is the
-// total, and each row's weights and output belong to its layer.
-struct NoLayers {};
-template <bool GROUPED>
-using LayersArg = std::conditional_t<GROUPED, GemvLayers, NoLayers>;
-
-template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT, int NW, bool GROUPED>
+// NL > 0: the rows of NL layers sharing x, stacked (L); N is the total, and
+// each row's weights and output belong to its layer.
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT, int NW, int NL>
 __device__ __forceinline__ void gemv_body(const half_t* __restrict__ x, const uint32_t* __restrict__ qweight,
                                           const half_t* __restrict__ scales, const half_t* __restrict__ zeros,
                                           half_t* __restrict__ y, int N, int K, int log2g, int max_sets,
-                                          int nblocks, const LayersArg<GROUPED>& L) {
+                                          int nblocks, const LayersArg<NL>& L) {
     extern __shared__ uint4 smem[];
     constexpr int XV = Chunk<BITS>::kXV;
-    if constexpr (GROUPED) {
-        // the layer table is wanted before the first weight load: fetch all
-        // of it with the other arguments, in one round trip
-#pragma unroll
-        for (int i = 0; i < kGemvMaxLayers; ++i)
-            asm volatile("" ::"s"(L.qweight[i]), "s"(L.scales[i]), "s"(L.zeros[i]), "s"(L.y[i]), "s"(L.row0[i]));
-        asm volatile("" ::"s"(L.row0[kGemvMaxLayers]));
-    }
     const int nchunk = K >> Chunk<BITS>::kShift;    // 32 (INT4) or 16 (W8) weights per chunk
     // x pairs [MT][XV][nchunk]: lanes reading one v of consecutive chunks
     // hit consecutive 16-byte slots (no bank conflicts)
@@ -332,7 +350,7 @@ __device__ __forceinline__ void gemv_body(const half_t* __restrict__ x, const ui
     WeightBatch<RPW, CPL> ring[DEPTH];
     int l_item = 0, l_set = 0, l_kb = 0;            // load cursor
     auto issue = [&](WeightBatch<RPW, CPL>& b) {
-        load_batch<BITS, RPW, CPL, GROUPED>(b, qweight, scales, zeros, L, (wid + l_set * W) * RPW, l_item < n_items,
+        load_batch<BITS, RPW, CPL, NL>(b, qweight, scales, zeros, L, (wid + l_set * W) * RPW, l_item < n_items,
                                             N, nchunk, ngroups, log2g, l_kb * 64 * CPL, lane);
         ++l_item;
         if (++l_kb == kbs) { l_kb = 0; ++l_set; }
@@ -352,9 +370,11 @@ __device__ __forceinline__ void gemv_body(const half_t* __restrict__ x, const ui
 
     // output element (m, stacked row r)
     auto store_y = [&](int m, int r, float v) {
-        if constexpr (GROUPED) {
-            const LayerRow lr = layer_of(L, r);
-            lr.y[static_cast<int64_t>(m) * lr.rows + (r - lr.row0)] = static_cast<half_t>(v);
+        if constexpr (NL > 0) {
+            const int start = pick_row<NL>(L, r, 0, L.b1, L.b2, L.b3);
+            const int end = pick_row<NL>(L, r, NL > 1 ? L.b1 : N, NL > 2 ? L.b2 : N, NL > 3 ? L.b3 : N, N);
+            pick_row<NL>(L, r, L.y0, L.y1, L.y2, L.y3)[static_cast<int64_t>(m) * (end - start) + (r - start)] =
+                static_cast<half_t>(v);
         } else {
             y[static_cast<int64_t>(m) * N + r] = static_cast<half_t>(v);
         }
@@ -431,14 +451,35 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const half_t* __restrict_
                                                    const half_t* __restrict__ zeros,
                                                    half_t* __restrict__ y, int N, int K, int shape,
                                                    int nblocks) {
-    gemv_body<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, false>(x, qweight, scales, zeros, y, N, K, shape & 0xFF,
-                                                              shape >> 8, nblocks, NoLayers{});
+    gemv_body<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, 0>(x, qweight, scales, zeros, y, N, K, shape & 0xFF,
+                                                          shape >> 8, nblocks, NoLayers{});
 }
-template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT, int NW>
-__global__ __launch_bounds__(NW * 64) void gemv_grouped_kernel(const half_t* __restrict__ x, int N, int K,
-                                                           int log2g, int max_sets, int nblocks, GemvLayers L) {
-    gemv_body<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, true>(x, nullptr, nullptr, nullptr, nullptr, N, K, log2g,
-                                                             max_sets, nblocks, L);
+// The grouped form takes the weight pointers of up to four layers and the
+// first stacked rows of layers 1-3 as separate arguments: preloading covers
+// scalar arguments only (not an aggregate), and with up to three layers
+// these end within the 14 preloaded dwords. The rest of the table (scales,
+// zero-points, outputs) is an aggregate loaded as usual.
+template <int NL>
+struct GemvLayerTail {
+    const half_t* scales[NL];
+    const half_t* zeros[NL];
+    half_t* y[NL];
+};
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT, int NW, int NL>
+__global__ __launch_bounds__(NW * 64) void gemv_grouped_kernel(const half_t* __restrict__ x, int N, int K, int shape,
+                                                           int nblocks, const uint32_t* q0, const uint32_t* q1,
+                                                           const uint32_t* q2, int b1, int b2,
+                                                           const uint32_t* q3, int b3, GemvLayerTail<NL> tail) {
+    const GemvLayerTable L{q0, q1, q2, q3,
+                           tail.scales[0], NL > 1 ? tail.scales[NL > 1 ? 1 : 0] : nullptr,
+                           NL > 2 ? tail.scales[NL > 2 ? 2 : 0] : nullptr, NL > 3 ? tail.scales[NL > 3 ? 3 : 0] : nullptr,
+                           tail.zeros[0], NL > 1 ? tail.zeros[NL > 1 ? 1 : 0] : nullptr,
+                           NL > 2 ? tail.zeros[NL > 2 ? 2 : 0] : nullptr, NL > 3 ? tail.zeros[NL > 3 ? 3 : 0] : nullptr,
+                           tail.y[0], NL > 1 ? tail.y[NL > 1 ? 1 : 0] : nullptr,
+                           NL > 2 ? tail.y[NL > 2 ? 2 : 0] : nullptr, NL > 3 ? tail.y[NL > 3 ? 3 : 0] : nullptr,
+                           b1, b2, b3};
+    gemv_body<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, NL>(x, nullptr, nullptr, nullptr, nullptr, N, K, shape & 0xFF,
+                                                           shape >> 8, nblocks, L);
 }
 
 int max_shared_bytes() {
@@ -460,22 +501,25 @@ size_t gemv_lds_bytes(int64_t M, int64_t K, int bits) {
                      : static_cast<size_t>(M) * static_cast<size_t>(K / 16) * 40;
 }
 
-// A launch: one layer (qweight, scales, zeros, y of N rows), or with
-// GROUPED the stacked layers of L (N rows in all).
-template <bool GROUPED>
+// A launch: one layer (qweight, scales, zeros, y of N rows), or with NL > 0
+// the stacked layers of L (N rows in all).
+template <int NL>
 struct GemvTarget {
     const uint32_t* qweight;
     const half_t* scales;
     const half_t* zeros;
     half_t* y;
-    LayersArg<GROUPED> L;
+    LayersArg<NL> L;
 };
 
-template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT = false, int NW = 4, bool GROUPED = false>
-awq_status launch_t(const half_t* x, const GemvTarget<GROUPED>& tg, int64_t N, int64_t K, int log2g,
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT = false, int NW = 4, int NL = 0>
+awq_status launch_t(const half_t* x, const GemvTarget<NL>& tg, int64_t N, int64_t K, int log2g,
                     int64_t blocks, hipStream_t stream) {
-    const void* kern = GROUPED ? reinterpret_cast<const void*>(&gemv_grouped_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>)
-                               : reinterpret_cast<const void*>(&gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>);
+    const void* kern;
+    if constexpr (NL > 0)
+        kern = reinterpret_cast<const void*>(&gemv_grouped_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, NL>);
+    else
+        kern = reinterpret_cast<const void*>(&gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>);
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, max_shared_bytes()) != hipSuccess)
@@ -490,10 +534,22 @@ awq_status launch_t(const half_t* x, const GemvTarget<GROUPED>& tg, int64_t N, i
     if (max_sets >= (int64_t{1} << 23)) return AWQ_ERR_SHAPE;                              // packed with log2 G
     const size_t lds = gemv_lds_bytes(MT, K, BITS) + (ONESHOT ? 0 : static_cast<size_t>(NW * max_sets * RPW * MT) * sizeof(float));
     if (lds > static_cast<size_t>(max_shared_bytes())) return AWQ_ERR_SHAPE;
-    if constexpr (GROUPED)
-        hipLaunchKernelGGL((gemv_grouped_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>),
+    if constexpr (NL > 0) {
+        const GemvLayerTable& T = tg.L;
+        GemvLayerTail<NL> tail;
+        const half_t* sc[4] = {T.s0, T.s1, T.s2, T.s3};
+        const half_t* zr[4] = {T.z0, T.z1, T.z2, T.z3};
+        half_t* yy[4] = {T.y0, T.y1, T.y2, T.y3};
+        for (int i = 0; i < NL; ++i) {
+            tail.scales[i] = sc[i];
+            tail.zeros[i] = zr[i];
+            tail.y[i] = yy[i];
+        }
+        hipLaunchKernelGGL((gemv_grouped_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, NL>),
                            dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), lds, stream, x, static_cast<int>(N),
-                           static_cast<int>(K), log2g, static_cast<int>(max_sets), static_cast<int>(blocks), tg.L);
+                           static_cast<int>(K), log2g | static_cast<int>(max_sets << 8), static_cast<int>(blocks),
+                           T.q0, T.q1, T.q2, T.b1, T.b2, T.q3, T.b3, tail);
+    }
     else
         hipLaunchKernelGGL((gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>), dim3(static_cast<unsigned>(blocks)),
                            dim3(NW * 64), lds, stream, x, tg.qweight, tg.scales, tg.zeros, tg.y, static_cast<int>(N),
@@ -518,24 +574,24 @@ awq_status launch_t(const half_t* x, const GemvTarget<GROUPED>& tg, int64_t N, i
 //    of more than 3 items. Against 4 waves with a 4-deep ring (the same bytes
 //    in flight): 4096 x 11008 7.85 -> 7.13 us, 8192 x 28672 25.4 -> 24.1 us;
 //    8 waves with a 4-deep ring or 16 waves with a 2-deep one are slower.
-template <int BITS, int MT, bool GROUPED = false>
-awq_status launch_m(const half_t* x, const GemvTarget<GROUPED>& tg, int64_t N, int64_t K, int log2g,
+template <int BITS, int MT, int NL = 0>
+awq_status launch_m(const half_t* x, const GemvTarget<NL>& tg, int64_t N, int64_t K, int log2g,
                     hipStream_t stream) {
     const int64_t kbs = ceil_div(K >> Chunk<BITS>::kShift, 128);
     if (kbs == 1) {
         if (MT >= 2 && ceil_div(N, 16) >= 256)
-            return launch_t<BITS, MT, 4, 2, 1, true, 4, GROUPED>(x, tg, N, K, log2g, ceil_div(N, 16), stream);
+            return launch_t<BITS, MT, 4, 2, 1, true, 4, NL>(x, tg, N, K, log2g, ceil_div(N, 16), stream);
         if (ceil_div(N, 8) >= 512)
-            return launch_t<BITS, MT, 2, 2, 1, true, 4, GROUPED>(x, tg, N, K, log2g, ceil_div(N, 8), stream);
-        return launch_t<BITS, MT, 1, 2, 1, true, 4, GROUPED>(x, tg, N, K, log2g, ceil_div(N, 4), stream);
+            return launch_t<BITS, MT, 2, 2, 1, true, 4, NL>(x, tg, N, K, log2g, ceil_div(N, 8), stream);
+        return launch_t<BITS, MT, 1, 2, 1, true, 4, NL>(x, tg, N, K, log2g, ceil_div(N, 4), stream);
     }
     if (kbs == 2 && BITS == 8)
-        return launch_t<BITS, MT, 1, 2, 2, true, 4, GROUPED>(x, tg, N, K, log2g, ceil_div(N, 4), stream);
+        return launch_t<BITS, MT, 1, 2, 2, true, 4, NL>(x, tg, N, K, log2g, ceil_div(N, 4), stream);
     const int64_t x_lds = static_cast<int64_t>(gemv_lds_bytes(MT, K, BITS));
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kGemvBlocksPerCu, max_shared_bytes() / (x_lds + 2048)));
     if (MT >= 2 || kbs > 3)
-        return launch_t<BITS, MT, 2, 2, 2, false, 8, GROUPED>(x, tg, N, K, log2g, per_cu * cu_count(), stream);
-    return launch_t<BITS, MT, 1, 2, 2, false, 8, GROUPED>(x, tg, N, K, log2g, per_cu * cu_count(), stream);
+        return launch_t<BITS, MT, 2, 2, 2, false, 8, NL>(x, tg, N, K, log2g, per_cu * cu_count(), stream);
+    return launch_t<BITS, MT, 1, 2, 2, false, 8, NL>(x, tg, N, K, log2g, per_cu * cu_count(), stream);
 }
 
 }  // namespace
@@ -550,7 +606,7 @@ namespace {
 template <int BITS>
 awq_status launch_gemv_bits(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros,
                             int64_t M, int64_t N, int64_t K, int log2g, half_t* y, hipStream_t stream) {
-    const GemvTarget<false> tg{qweight, scales, zeros, y, NoLayers{}};
+    const GemvTarget<0> tg{qweight, scales, zeros, y, NoLayers{}};
     switch (M) {
         case 1: return launch_m<BITS, 1>(x, tg, N, K, log2g, stream);
         case 2: return launch_m<BITS, 2>(x, tg, N, K, log2g, stream);
@@ -573,15 +629,38 @@ awq_status launch_gemv(const half_t* x, const uint32_t* qweight, const half_t* s
     return launch_gemv_bits<4>(x, qweight, scales, zeros, M, N, K, log2g, y, stream);
 }
 
+namespace {
+template <int NL>
+awq_status launch_grouped_n(const half_t* x, const GemvLayers& layers, int64_t M, int64_t K, int log2g,
+                            hipStream_t stream) {
+    auto at = [&](auto a, int i) { return i < layers.n ? a[i] : nullptr; };
+    const GemvLayerTable T{at(layers.qweight, 0), at(layers.qweight, 1), at(layers.qweight, 2), at(layers.qweight, 3),
+                           at(layers.scales, 0),  at(layers.scales, 1),  at(layers.scales, 2),  at(layers.scales, 3),
+                           at(layers.zeros, 0),   at(layers.zeros, 1),   at(layers.zeros, 2),   at(layers.zeros, 3),
+                           at(layers.y, 0),       at(layers.y, 1),       at(layers.y, 2),       at(layers.y, 3),
+                           layers.n > 1 ? layers.row0[1] : INT32_MAX, layers.n > 2 ? layers.row0[2] : INT32_MAX,
+                           layers.n > 3 ? layers.row0[3] : INT32_MAX};
+    const GemvTarget<NL> tg{nullptr, nullptr, nullptr, nullptr, T};
+    const int64_t N = layers.row0[NL];
+    switch (M) {
+        case 1: return launch_m<4, 1, NL>(x, tg, N, K, log2g, stream);
+        case 2: return launch_m<4, 2, NL>(x, tg, N, K, log2g, stream);
+        default: return AWQ_ERR_SHAPE;
+    }
+}
+}  // namespace
+
 awq_status launch_gemv_grouped(const half_t* x, const GemvLayers& layers, int64_t M, int64_t K, int group_size,
                                hipStream_t stream) {
     const int log2g = 31 - __builtin_clz(static_cast<unsigned>(group_size));
-    const int64_t N = layers.row0[layers.n];
-    const GemvTarget<true> tg{nullptr, nullptr, nullptr, nullptr, layers};
-    switch (M) {
-        case 1: return launch_m<4, 1, true>(x, tg, N, K, log2g, stream);
-        case 2: return launch_m<4, 2, true>(x, tg, N, K, log2g, stream);
-        default: return AWQ_ERR_SHAPE;
+    switch (layers.n) {
+        case 1:
+            return launch_gemv(x, layers.qweight[0], layers.scales[0], layers.zeros[0], M, layers.row0[1], K,
+                               group_size, layers.y[0], stream);
+        case 2: return launch_grouped_n<2>(x, layers, M, K, log2g, stream);
+        case 3: return launch_grouped_n<3>(x, layers, M, K, log2g, stream);
+        case 4: return launch_grouped_n<4>(x, layers, M, K, log2g, stream);
+        default: return AWQ_ERR_CONFIG;
     }
 }
 
