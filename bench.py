@@ -1006,6 +1006,17 @@ def summarize_counters(dirs, manifest_path, out_path, commands):
             o["mfma_util_pct"] = round(c["MfmaUtil"], 2)      # rocprofv3's own derived metric
         if "TA_BUSY_avr" in c and active:
             o["ta_busy_pct"] = round(100.0 * c["TA_BUSY_avr"] / active, 2)
+            # TD_TD_BUSY and TA_TA_BUSY are summed over the same CU
+            # instances: the texture-data unit's busy share is the address
+            # unit's scaled by their ratio
+            if c.get("TA_TA_BUSY") and "TD_TD_BUSY" in c:
+                o["td_busy_pct"] = round(o["ta_busy_pct"] * c["TD_TD_BUSY"] / c["TA_TA_BUSY"], 2)
+        if c.get("SQ_WAVE_CYCLES"):
+            # shares of the waves' resident time (both counters in quad-cycles)
+            for k, name in (("SQ_WAIT_INST_ANY", "wave_wait_issue_pct"), ("SQ_ACTIVE_INST_VALU", "wave_valu_pct"),
+                            ("SQ_ACTIVE_INST_LDS", "wave_lds_pct")):
+                if k in c:
+                    o[name] = round(100.0 * c[k] / c["SQ_WAVE_CYCLES"], 2)
         if active and c.get("duration_us") and o["kind"] != "gemv":
             # one XCD's active cycles per us of dispatch (long dispatches only:
             # the active count also covers a dispatch's start-up)
@@ -1014,17 +1025,22 @@ def summarize_counters(dirs, manifest_path, out_path, commands):
     lines += [f"    {c}" for c in commands]
     lines += ["", "Per launch (average over the group's dispatches). HBM bytes = FETCH_SIZE x fetch factor + "
               "WRITE_SIZE x write factor (both from the 1 GiB copy); algorithmic bytes as in bench.py. "
-              "MFMA FLOPs = SQ_INSTS_MFMA x 32768. MfmaUtil is rocprofv3's derived metric.", "",
-              "| launch | grid | HBM bytes | / algorithmic | MFMA FLOPs = 2MNK | MfmaUtil % | TA busy % | clock MHz |",
-              "|---|---|---|---|---|---|---|---|"]
+              "MFMA FLOPs = SQ_INSTS_MFMA x 32768. MfmaUtil is rocprofv3's derived metric. TA busy = "
+              "TA_BUSY_avr over one XCD's active cycles; TD busy = TA busy x TD_TD_BUSY / TA_TA_BUSY (both "
+              "summed over the same CUs). Waiting to issue and in VALU: SQ_WAIT_INST_ANY and SQ_ACTIVE_INST_VALU "
+              "over SQ_WAVE_CYCLES (shares of the waves' resident time).", "",
+              "| launch | grid | HBM bytes | / algorithmic | MFMA FLOPs = 2MNK | MfmaUtil % | TA busy % | TD busy % "
+              "| waves waiting to issue % | waves in VALU % | clock MHz |",
+              "|---|---|---|---|---|---|---|---|---|---|---|"]
     for o in out:
         if o["kind"] == "copy":
             lines.append(f"| copy 1 GiB (calibration: fetch x{o.get('fetch_factor', 0):.3f}, write "
                          f"x{o.get('write_factor', 0):.3f}) | {o['grid']} | | | | | {o.get('ta_busy_pct', '')} | "
-                         f"{o.get('clock_mhz', '')} |")
+                         f"{o.get('td_busy_pct', '')} | | | {o.get('clock_mhz', '')} |")
             continue
         lines.append(f"| {o['label']} | {o['grid']} | {o.get('traffic_bytes', '')} | {o.get('traffic_over_algorithmic', '')} "
                      f"| {o.get('mfma_flop_equals_2MNK', '')} | {o.get('mfma_util_pct', '')} | {o.get('ta_busy_pct', '')} "
+                     f"| {o.get('td_busy_pct', '')} | {o.get('wave_wait_issue_pct', '')} | {o.get('wave_valu_pct', '')} "
                      f"| {o.get('clock_mhz', '')} |")
     with open(os.path.splitext(out_path)[0] + ".md", "w") as f:
         f.write("\n".join(lines) + "\n")
