@@ -63,6 +63,8 @@ def test_prefill_stream_k_full_size_sampled(N, K):
     (513, 257, 640, 64),       # K steps = 20: segment edges fall inside groups
     (1000, 700, 1216, 64),     # 19 K steps per tile, odd segment lengths
     (2048, 640, 4096, 128),    # 40 tiles
+    (300, 640, 13824, 128),    # 216 K steps per tile: six segments of 36
+    (513, 257, 12288, 64),     # 192 K steps: six segments of 32, ragged tiles
 ])
 def test_stream_k_ragged_against_oracle(M, N, K, G):
     lay = synth.make_layer(N, K, M, seed=[120, M, N, K, G], w_std=0.02)
