@@ -453,9 +453,10 @@ class Bench:
         """One GPU's share of the decode layer under 8-way column (output)
         parallelism: every projection keeps 1/8 of its rows (q/k/v/o
         512x4096, gate/up 1376x4096, down 512x11008), so each GPU streams
-        1/8 of the weights with the same GEMV; the step's seven launches are
-        timed as in the decode step. The all-gather of y is not part of it
-        (one GPU)."""
+        1/8 of the weights with the same GEMV; the step's four launches
+        (q/k/v and gate/up grouped) are timed as in the decode step, and the
+        seven single launches beside them. The all-gather of y is not part of
+        it (one GPU)."""
         torch, awq = self.torch, self.awq
         layer = [(n, N // 8, K) for (n, N, K) in synth.LLAMA7B_LAYER]
         step_bytes = sum(gemv_bytes(1, N, K) for (_, N, K) in layer)
@@ -466,27 +467,40 @@ class Bench:
                 lay = synth.make_layer(N, K, 1, seed=[8, N, K], w_std=0.02)
                 qw, sc, zr = awq.awq_quantize(self.d(lay["w"]), G)
                 base[(N, K)] = (qw, sc, zr, self.d(lay["x"]))
+        # (qw, sc, zr, x, y, N, K) per linear; layers of one shape share x
         copies = [[(*[t.clone() for t in base[(N, K)][:3]], base[(N, K)][3],
-                    torch.empty((1, N), dtype=torch.float16, device=self.dev)) for (_, N, K) in layer]
+                    torch.empty((1, N), dtype=torch.float16, device=self.dev), N, K) for (_, N, K) in layer]
                   for _ in range(n_copies)]
+        groups = [idx for (_, idx) in DECODE_GROUPS]
 
         def step(i):
-            for (qw, sc, zr, x, y) in copies[i % n_copies]:
+            for idx in groups:
+                self.launch(copies[i % n_copies], idx)
+
+        def step_seven(i):
+            for (qw, sc, zr, x, y, _, _) in copies[i % n_copies]:
                 awq.awq_gemm(x, qw, sc, zr, G, out=y)
 
-        for i in range(4):
-            step(i)
-        g = self.capture(step, n_copies)
-        g.replay()
-        reps = 20
-        t = min(self.time(lambda _: [g.replay() for _r in range(reps)]) for _ in range(3)) / (reps * n_copies)
-        del copies, g
+        def timed(fn):
+            for i in range(4):
+                fn(i)
+            g = self.capture(fn, n_copies)
+            g.replay()
+            reps = 20
+            t = min(self.time(lambda _: [g.replay() for _r in range(reps)]) for _ in range(3)) / (reps * n_copies)
+            del g
+            return t
+
+        t = timed(step)
+        t7 = timed(step_seven)
+        del copies
         torch.cuda.synchronize()
-        log(f"tp8 shard step: {t * 1e6:.2f} us, {step_bytes / t / 1e9:.0f} GB/s")
+        log(f"tp8 shard step: {t * 1e6:.2f} us, {step_bytes / t / 1e9:.0f} GB/s (seven launches {t7 * 1e6:.2f} us)")
         return {"workload": "llama7b_decoder_layer_m1_int4_g128, one GPU's share under 8-way column parallelism",
                 "linears": [f"{n}:{N}x{K}" for (n, N, K) in layer], "step_bytes": step_bytes,
-                "us_per_step": round(t * 1e6, 2), "GB/s": round(step_bytes / t / 1e9, 1),
-                "frac_of_hbm_peak": round(step_bytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+                "launches": len(groups), "us_per_step": round(t * 1e6, 2), "GB/s": round(step_bytes / t / 1e9, 1),
+                "frac_of_hbm_peak": round(step_bytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                "seven_launches_us_per_step": round(t7 * 1e6, 2)}
 
     def run_group_sizes(self):
         """The roofline GEMV shape (11008x4096, M = 1) at every supported group

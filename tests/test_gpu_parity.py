@@ -275,7 +275,7 @@ def test_sweep_linear_full_size_sampled(N, K, G, M):
 @pytest.mark.parametrize("M,N,K,G", [
     (1, 1, 64, 64), (3, 17, 128, 64), (8, 130, 256, 128), (9, 64, 64, 64),
     (127, 129, 192, 64), (300, 200, 384, 128), (257, 255, 640, 64),
-    (1, 1001, 6144, 64), (1, 3001, 8192, 128),    # rows of two items: the persistent GEMV at M = 1
+    (1, 1001, 6144, 64), (1, 3001, 8192, 128),    # rows of two items at M = 1, few rows (one-shot)
 ])
 def test_linear_ragged_both_paths(M, N, K, G):
     lay = synth.make_layer(N, K, M, seed=[104, M, N, K, G], w_std=0.02)
@@ -285,6 +285,28 @@ def test_linear_ragged_both_paths(M, N, K, G):
     assert_linear_close(run_linear(lay["x"], qw, sc, zr, G, awq.PATH_AUTO), y_ref)
     if M <= 8:
         assert_linear_close(run_linear(lay["x"], qw, sc, zr, G, awq.PATH_GEMV), y_ref)
+
+
+@pytest.mark.parametrize("N,K,G", [
+    (512, 11008, 128),    # three items per row, few rows: one-shot, every item in flight
+    (37, 13824, 64),      # four items, a ragged handful of rows
+    (2048, 13824, 128),   # four items, one round of resident waves
+    (2049, 13824, 128),   # one row more: the persistent form
+    (1001, 6144, 256),    # two items, ragged
+    (4500, 5120, 128),    # two items past one round: persistent
+    (1500, 12288, 32),    # three items at G = 32
+])
+def test_gemv_m1_long_rows(N, K, G):
+    """M = 1 on rows of 2-4 items (4096 < K <= 16384): layers of few rows
+    (one GPU's share of a split layer) take the one-shot form with every item
+    in flight, larger ones the persistent streaming form; both against the
+    oracle, element by element."""
+    lay = synth.make_layer(N, K, 1, seed=[110, N, K, G], w_std=0.02)
+    say("gemv m1 long rows", N, K, G)
+    qw, sc, zr = oracle.quantize(lay["w"], G)
+    y_ref = oracle.linear_ref(lay["x"], qw, sc, zr, G)
+    assert_linear_close(run_linear(lay["x"], qw, sc, zr, G, awq.PATH_GEMV), y_ref)
+    assert_linear_close(run_linear(lay["x"], qw, sc, zr, G, awq.PATH_AUTO), y_ref)
 
 
 @pytest.mark.parametrize("M,N,K,G", [
