@@ -46,12 +46,16 @@ def test_decode_shapes_against_oracle(N, K, M):
     (32, 4111, 4096, 128),
     (9, 77, 28672, 128),      # long K: 28 groups per wave
     # several 16-column tiles per block (each x operand read feeds them all)
-    (16, 11000, 4096, 128),   # four tiles per block; the last block's last tile 8 columns wide
+    (16, 11000, 4096, 128),   # three tiles per block; the last block holds one tile, 8 columns wide
     (16, 6000, 4096, 128),    # two tiles per block; the last block's second tile past N
     (8, 13800, 5120, 128),    # two tiles at 8 rows (rows of 40 groups)
-    (32, 10250, 4096, 128),   # four tiles, 32 rows; the last block holds 10 columns
-    (16, 11000, 4096, 256),   # four tiles at G = 256 (two groups in flight)
+    (32, 10250, 4096, 128),   # three tiles, 32 rows; the last block's second tile 10 columns wide
+    (16, 11000, 4096, 256),   # three tiles at G = 256 (two groups in flight)
     (32, 11000, 4096, 256),   # 32 rows at G = 256: two tiles
+    (16, 13800, 2048, 128),   # four tiles (one round of blocks); the last block's third tile 8 wide
+    (32, 14000, 1024, 64),    # four tiles at 32 rows
+    (32, 9000, 2048, 64),     # three tiles, G = 64, a ragged last tile
+    (24, 20000, 512, 32),     # three tiles over two rounds of blocks, G = 32
 ])
 def test_ragged_against_oracle(M, N, K, G):
     lay = synth.make_layer(N, K, M, seed=[220, M, N, K, G], w_std=0.02)

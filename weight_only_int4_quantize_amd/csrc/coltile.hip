@@ -315,23 +315,37 @@ int ct_rows(int64_t M) { return M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : 32; }
 constexpr int ct_max_tiles(int xr, int wpl) { return xr * wpl >= 256 ? 2 : 4; }
 // 16-column tiles per block. Each extra tile reuses every x operand read
 // (x costs M / 4 times the weight bytes per tile), but leaves fewer blocks.
-// From 16 rows of x up: 4 tiles from 2.5 column tiles per CU, 2 from 1.25;
-// below: 2 from 1.25 column tiles per CU on rows of 40 groups and more.
-// Measured (us, weights past every cache; 1 / 2 / 4 tiles, best wave count
-// of each): M = 16 on 11008 x 4096 13.5 / 13.4 / 11.7, 13824 x 5120
-// 22.0 / 17.3 / 16.1, 5120 x 13824 25.8 / 22.2 / 32.3, 8192 x 28672
-// 51.9 / 44.1 / 64.2, 4096 x 4096 6.5 / 8.2 / 11.1; M = 4 on 13824 x 5120
-// 15.5 / 14.4 / 17.4, 11008 x 4096 10.3 / 10.9 / 13.3.
+// From 16 rows of x up, the count that minimises the busiest CU's work in
+// tile units: its blocks (one per CU per round) times each block's weights
+// (ct tiles) and x (xr / 4 tiles). Measured (us, weights past every cache;
+// 1 / 2 / 3 / 4 tiles): M = 16 on 11008 x 4096 13.5 / 13.4 / 9.8 / 11.5,
+// 12288 x 4096 - / - / 10.1 / 11.7, 22016 x 4096 - / - / 16.3 / 21.8,
+// 13824 x 5120 22.0 / 17.3 / 21.3 / 15.8, 5120 x 13824 25.8 / 22.2 / - /
+// 32.3, 8192 x 28672 51.9 / 44.1 / - / 64.2, 4096 x 4096 6.5 / 8.2 / - /
+// 11.1; M = 32 on 11008 x 4096 - / - / 13.1 / 15.1, 13824 x 5120
+// - / - / 29.9 / 19.7; each the model's choice. Below 16 rows (weights
+// dominate, and more waves per CU matter more): 2 from 1.25 column tiles
+// per CU on rows of 40 groups and more, else 1; M = 4 on 13824 x 5120
+// 15.5 / 14.4 / - / 17.4, 11008 x 4096 10.3 / 10.9 / - / 13.3.
 int ct_tiles(int64_t M, int64_t N, int64_t K, int group_size) {
     const int64_t cu = cu_count();
     const int64_t tiles = ceil_div(N, kCtCols);
     const int xr = ct_rows(M);
-    int ct;
-    if (xr >= 16)
-        ct = tiles * 2 >= 5 * cu ? 4 : tiles * 4 >= 5 * cu ? 2 : 1;
-    else
-        ct = tiles * 4 >= 5 * cu && K / group_size >= 40 ? 2 : 1;
-    return std::min(ct, ct_max_tiles(xr, group_size / 32));
+    const int most = ct_max_tiles(xr, group_size / 32);
+    if (xr >= 16) {
+        int best = 1;
+        int64_t best_cost = INT64_MAX;
+        for (int ct = 1; ct <= most; ++ct) {
+            const int64_t cost = ceil_div(ceil_div(tiles, ct), cu) * (ct + xr / 4);
+            if (cost < best_cost) {
+                best_cost = cost;
+                best = ct;
+            }
+        }
+        return best;
+    }
+    const int ct = tiles * 4 >= 5 * cu && K / group_size >= 40 ? 2 : 1;
+    return std::min(ct, most);
 }
 // 16-wave blocks (4 per SIMD, 128 VGPRs) only for instances whose ring fits
 constexpr bool ct_sixteen_ok(int xr, int wpl, int ct) { return ct == 1 && xr * wpl <= 64; }
@@ -416,6 +430,10 @@ awq_status launch_ct_tiles(const half_t* x, const uint32_t* qweight, const half_
     switch (ct_tiles(M, N, K, WPL * 32)) {
         case 1: return launch_ct_nw<XR, WPL, 1>(x, qweight, scales, zeros, M, N, K, y, stream);
         case 2: return launch_ct_nw<XR, WPL, 2>(x, qweight, scales, zeros, M, N, K, y, stream);
+        case 3:
+            if constexpr (ct_max_tiles(XR, WPL) >= 3 && XR >= 16)
+                return launch_ct_nw<XR, WPL, 3>(x, qweight, scales, zeros, M, N, K, y, stream);
+            return AWQ_ERR_CONFIG;
         default: return launch_ct_nw<XR, WPL, ct_max_tiles(XR, WPL)>(x, qweight, scales, zeros, M, N, K, y, stream);
     }
 }
