@@ -139,7 +139,7 @@ awq_status awq_quantize_ex(const void* w_f16, const float* channel_scale,
  * M == 0 or N == 0 returns AWQ_OK without work. Decode (M <= 2) runs a
  * bandwidth-bound GEMV; a batch of decode tokens (M <= 64) one of two MFMA
  * kernels that stream the packed weights straight into registers: column
- * tiles (one block per 16, 32 or 64 output columns over all of K; M <= 32,
+ * tiles (one block per 16, 32, 48 or 64 output columns over all of K; M <= 32,
  * chosen from M = 3 up on layers of up to 48 Mi weights, or 96 Mi with
  * K <= 8192, and on every shape when no workspace is given) or the skinny
  * kernel (256 columns per block, K split across blocks with a workspace);
