@@ -350,6 +350,53 @@ class Bench:
                        "(whole model, other hardware): context, not a target")
         return out
 
+    def run_decode_batched(self):
+        """The decode step at a batch of M = 4 and 16 tokens, as a serving
+        loop calls it (no workspace): the seven linears as four launches
+        (q/k/v and gate/up grouped: one column-tile launch over the stacked
+        layers) and as seven awq_gemm calls, weights rotated over the decode
+        step's copies. Layers of one launch group share x."""
+        torch, awq = self.torch, self.awq
+        out = {}
+        group_of = {}
+        for gi, (_, idx) in enumerate(DECODE_GROUPS):
+            for j in idx:
+                group_of[j] = gi
+        for M in (4, 16):
+            xs = [self.d(synth.make_layer(1, self.linears[idx[0]][2], M, seed=[12, M, gi], w_std=0.02)["x"])
+                  for gi, (_, idx) in enumerate(DECODE_GROUPS)]
+            copies = [[(qw, sc, zr, xs[group_of[j]], torch.empty((M, N), dtype=torch.float16, device=self.dev), N, K)
+                       for j, (qw, sc, zr, _, _, N, K) in enumerate(layer)] for layer in self.copies]
+            groups = [idx for (_, idx) in DECODE_GROUPS]
+            bytes4 = sum(grouped_bytes(M, [(self.linears[j][1], self.linears[j][2]) for j in idx]) for idx in groups)
+            bytes7 = sum(gemv_bytes(M, N, K) for (_, N, K) in self.linears)
+
+            def step(i, copies=copies):
+                for idx in groups:
+                    self.launch(copies[i % len(copies)], idx)
+
+            def step_seven(i, copies=copies):
+                for (qw, sc, zr, x, y, _, _) in copies[i % len(copies)]:
+                    awq.awq_gemm(x, qw, sc, zr, G, out=y)
+
+            res = {}
+            for label, fn, nbytes in (("grouped_4_launches", step, bytes4), ("seven_launches", step_seven, bytes7)):
+                for i in range(4):
+                    fn(i)
+                g = self.capture(fn, len(copies))
+                g.replay()
+                reps = 10
+                t = min(self.time(lambda _: [g.replay() for _r in range(reps)]) for _ in range(3)) / (reps * len(copies))
+                del g
+                res[label] = {"us_per_step": round(t * 1e6, 2), "GB/s": round(nbytes / t / 1e9, 1),
+                              "frac_of_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+                log(f"decode step M={M}, {label}: {t * 1e6:.2f} us, {nbytes / t / 1e9:.0f} GB/s")
+            res["kernel"] = awq.gemm_kernel(M, 12288, 4096, G)
+            out[f"M{M}"] = res
+            del copies
+        torch.cuda.synchronize()
+        return out
+
     def run_skinny(self):
         """Batched decode rows (awq_gemm_ex with a workspace): M = 4 on the
         decode shapes (the GEMV), M = 16 on the decode shapes and M = 32 on
@@ -1073,7 +1120,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true")
     ap.add_argument("--only", choices=["decode", "decode-fused", "decode-model", "gemv-roofline", "skinny", "gemm", "quantize",
-                                       "search", "copy", "w8", "sweep", "shard", "counters"],
+                                       "search", "copy", "w8", "sweep", "shard", "counters", "decode-batched"],
                     help="run one section (for profiler runs); timings go to stderr")
     ap.add_argument("--summarize-trace", nargs="+", metavar="DIR",
                     help="summarize rocprofv3 kernel-trace CSVs under DIR into --out (no GPU)")
@@ -1096,10 +1143,12 @@ def main():
 
     b = Bench(args)
     if args.only:
-        if args.only in ("decode", "gemv-roofline"):
+        if args.only in ("decode", "gemv-roofline", "decode-batched"):
             b.setup_decode()
             if args.only == "decode":
                 b.run_decode()
+            elif args.only == "decode-batched":
+                b.run_decode_batched()
             else:
                 b.run_gemv_shapes([ROOFLINE_SHAPE])
         elif args.only == "decode-fused":
@@ -1131,6 +1180,7 @@ def main():
     seven = b.run_decode_seven()
     per_launch = b.run_step_launches()
     per_shape = b.run_gemv_shapes(synth.DECODE_SHAPES)
+    batched = b.run_decode_batched()
     del b.copies
     fused = b.run_decode_fused()
     model = b.run_decode_model()
@@ -1184,6 +1234,7 @@ def main():
         "skinny_batched_decode": skinny,
         "sweep_13b_70b": sweep,
         "tp8_shard_1gpu": shard,
+        "decode_batched": batched,
         "gemv_group_sizes": groups,
         "w8a16": w8,
         "gemm": gemm,

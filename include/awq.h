@@ -249,10 +249,17 @@ awq_status awq_gemm_noalloc(const void* x_f16, const uint32_t* qweight,
  * y_i = x . dequant(Wq_i)^T for i < n_layers: the independent projections of
  * a decoder layer (q / k / v, gate / up), which the pages' deployment fuses
  * (rskf.cn §3.4 fuse_layers), kept as separate tensors (rskf.cn §1.3 / §3.3
- * GEMV kernel). Where awq_gemm would run the GEMV on the layers' stacked
- * rows (M <= 2), one launch computes all of them, the rows of layer i after
- * those of layers 0 .. i - 1; otherwise each layer is an awq_gemm call, in
- * order. Each y_i equals that layer's awq_gemm result bit for bit.
+ * GEMV kernel). Where awq_gemm (without a workspace) would run the GEMV or
+ * the column tiles on the layers' stacked rows, one launch computes all of
+ * them, the rows of layer i after those of layers 0 .. i - 1; otherwise each
+ * layer is an awq_gemm call, in order.
+ *   - GEMV (M <= 2): each y_i equals that layer's awq_gemm result bit for
+ *     bit (a row's arithmetic does not depend on the launch shape).
+ *   - Column tiles (3 <= M <= 32): each layer on whole blocks of its own
+ *     columns; the tile and wave counts follow the stacked rows, so the
+ *     fp32 order of a layer's sums (and its last bits) may differ from its
+ *     own awq_gemm call. Results are the same run to run.
+ *   - Otherwise (one awq_gemm per layer): the same bits as those calls.
  *
  *   x_f16        device, fp16 [M, K], shared by every layer
  *   n_layers     1 .. 4

@@ -3,12 +3,14 @@ layer's q / k / v and gate / up projections, which the rskf.cn AWQ
 article's deployment fuses, §3.4) in one GEMV launch over their stacked
 rows, each layer kept as its own tensors.
 
-Every y_i must equal the layer's own awq_gemm result bit for bit (the same
-per-row arithmetic in the same order) and meet the linear-layer bar against
-the oracle (relative Frobenius error <= 1e-3 and |y - y_ref| <= 1e-2 *
-(|y_ref| + 1) per element); outputs packed side by side in one buffer show
-that no layer writes past its own rows. Batches the GEMV does not take run
-the layers one awq_gemm call each, with the same bits.
+Every y_i meets the linear-layer bar against the oracle (relative Frobenius
+error <= 1e-3 and |y - y_ref| <= 1e-2 * (|y_ref| + 1) per element), and
+outputs packed side by side in one buffer show that no layer writes past its
+own rows. At M <= 2 (one GEMV launch) each y_i also equals the layer's own
+awq_gemm result bit for bit (the same per-row arithmetic in the same order);
+at 3 <= M <= 32 (one column-tile launch) the stacked rows set the tile and
+wave counts, so only repeatability is exact; larger batches run the layers
+one awq_gemm call each, with the same bits.
 """
 
 import numpy as np
@@ -85,8 +87,52 @@ def test_ragged_layers(Ns, K, G, M):
             assert_linear_close(g, oracle.linear_ref(x, *q, G))
 
 
+def run_grouped_twice(x, qs, G):
+    """The grouped call's outputs (between sentinels) and whether a second
+    call gives the same bits."""
+    got, _ = run_grouped(x, qs, G)
+    again, _ = run_grouped(x, qs, G)
+    same = all(np.array_equal(a.view(np.uint16), b.view(np.uint16)) for a, b in zip(got, again))
+    return got, same
+
+
 @pytest.mark.parametrize("M", [4, 16])
-def test_batches_past_the_gemv_run_per_layer(M):
+@pytest.mark.parametrize("Ns", [(4096, 4096, 4096), (11008, 11008)], ids=["qkv", "gate_up"])
+def test_batched_decode_projections(Ns, M):
+    """3 <= M <= 32: one column-tile launch over the stacked layers, each
+    layer on whole blocks of its own columns. The tile and wave counts follow
+    the stacked rows, so the waves' K ranges (and the fp32 summation order)
+    may differ from a single-layer call: each layer meets the linear-layer bar
+    against the oracle, and repeated calls give the same bits."""
+    K, G = 4096, 128
+    say("grouped batched", Ns, K, M)
+    x, qs = layers_of(Ns, K, M, G, 3)
+    got, same = run_grouped_twice(x, qs, G)
+    assert same
+    for q, g in zip(qs, got):
+        assert_linear_close(g, oracle.linear_ref(x, *q, G))
+
+
+@pytest.mark.parametrize("Ns,K,G,M", [
+    ((100, 37, 0, 1000), 512, 64, 3),      # ragged layers, one empty
+    ((5, 17, 33), 1024, 32, 8),            # layers narrower than one tile
+    ((777, 1500), 6144, 256, 16),          # G = 256
+    ((300, 500, 700, 900), 2048, 128, 32), # four layers, 32 rows of x
+    ((2000, 3000, 1000), 4096, 128, 12),   # several tiles per block, from the stacked rows
+])
+def test_batched_ragged_layers(Ns, K, G, M):
+    say("grouped batched ragged", Ns, K, G, M)
+    x, qs = layers_of(Ns, K, M, G, 4)
+    got, same = run_grouped_twice(x, qs, G)
+    assert same
+    for q, g in zip(qs, got):
+        if q[0].shape[0]:
+            assert_linear_close(g, oracle.linear_ref(x, *q, G))
+
+
+@pytest.mark.parametrize("M", [40, 64])
+def test_batches_past_the_column_tiles_run_per_layer(M):
+    """M > 32: one awq_gemm per layer, with its bits."""
     Ns, K, G = (4096, 1024), 4096, 128
     x, qs = layers_of(Ns, K, M, G, 2)
     got, singles = run_grouped(x, qs, G)

@@ -293,9 +293,9 @@ def awq_gemm_noalloc(x, qweight, scales, zeros, group_size: int = 128, path: int
 
 def awq_gemm_grouped(x, layers, group_size: int = 128, outs=None):
     """y_i = x . dequant(Wq_i)^T for layers [(qweight, scales, zeros), ...]
-    (1 to 4) that share x: one GEMV launch over their stacked rows where
-    awq_gemm would take the GEMV, else one awq_gemm per layer. Returns the
-    list of y_i (`outs`, when given, receives them)."""
+    (1 to 4) that share x: one GEMV or column-tile launch over their
+    stacked rows where awq_gemm would take that kernel, else one awq_gemm
+    per layer. Returns the list of y_i (`outs`, when given, receives them)."""
     torch = _torch()
     _need_gpu("x", x, torch.float16)
     if x.dim() != 2:

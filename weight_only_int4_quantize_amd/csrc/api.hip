@@ -376,7 +376,8 @@ awq_status awq_gemm_grouped(const void* x_f16, int n_layers, const uint32_t* con
     if (total > (int64_t(1) << 31) - 256) return AWQ_ERR_SHAPE;
     if (M == 0 || total == 0) return AWQ_OK;
     const hipStream_t s = as_stream(stream);
-    if (M <= kGemvGroupedMaxM && choose_path(M, total, K, group_size, 0, false) == 1) {
+    const int chosen = choose_path(M, total, K, group_size, 0, false);
+    if ((chosen == 1 && M <= kGemvGroupedMaxM) || chosen == 4) {
         GemvLayers L{};
         int r = 0;
         for (int i = 0; i < n_layers; ++i) {
@@ -391,7 +392,9 @@ awq_status awq_gemm_grouped(const void* x_f16, int n_layers, const uint32_t* con
         }
         L.row0[L.n] = r;
         for (int i = L.n + 1; i <= kGemvMaxLayers; ++i) L.row0[i] = INT32_MAX;
-        return launch_gemv_grouped(static_cast<const half_t*>(x_f16), L, M, K, group_size, s);
+        const half_t* x = static_cast<const half_t*>(x_f16);
+        if (chosen == 4) return launch_coltile_grouped(x, L, M, K, group_size, s);
+        return launch_gemv_grouped(x, L, M, K, group_size, s);
     }
     for (int i = 0; i < n_layers; ++i) {
         const awq_status st = gemm_dispatch(x_f16, qweight[i], scales_f16[i], zeros_f16[i], M, N[i], K, group_size,

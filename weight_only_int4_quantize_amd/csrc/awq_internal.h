@@ -159,6 +159,11 @@ bool coltile_preferred(int64_t M, int64_t N, int64_t K, int group_size, bool hav
 awq_status launch_coltile(const half_t* x, const uint32_t* qweight, const half_t* scales,
                           const half_t* zeros, int64_t M, int64_t N, int64_t K, int group_size,
                           half_t* y, hipStream_t stream);
+// The layers of `layers` (as for launch_gemv_grouped), sharing x, in one
+// column-tile launch: each layer on whole blocks of its own columns, the
+// tile and wave counts those of their total rows.
+awq_status launch_coltile_grouped(const half_t* x, const GemvLayers& layers, int64_t M, int64_t K,
+                                  int group_size, hipStream_t stream);
 
 // Mixed precision with fp16 salient channels.
 awq_status launch_select_salient(const double* m, int64_t K, int n, int* idx, hipStream_t stream);

@@ -105,10 +105,11 @@ struct CtSlot {
 // XR: rows of x staged (M rounded up to 4, 8, 16 or 32); MB = XR / 16
 // rounded up MFMA row blocks; XP 16-byte x pieces per lane and group; CT
 // 16-column MFMA tiles per block, which share every x operand read.
+// The block's work: block `blk` of the layer (qweight, scales, zeros, y, N).
 template <int XR, int WPL, int NW, int DEPTH, int CT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ct_waves_per_eu(XR, WPL, CT, NW)))) void coltile_kernel(
-    const half_t* __restrict__ x, const uint32_t* __restrict__ qweight, const half_t* __restrict__ scales,
-    const half_t* __restrict__ zeros, half_t* __restrict__ y, int M, int N, int K) {
+__device__ __forceinline__ void coltile_body(const half_t* __restrict__ x, const uint32_t* __restrict__ qweight,
+                                             const half_t* __restrict__ scales, const half_t* __restrict__ zeros,
+                                             half_t* __restrict__ y, int M, int N, int K, int blk) {
     constexpr int G = WPL * 32;
     constexpr int MB = (XR + 15) / 16;
     constexpr int COLS = kCtCols * CT;
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ct_wave
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15;
     const int kq = lane >> 4;                       // k-quarter of every group
-    const int n0 = blockIdx.x * COLS;
+    const int n0 = blk * COLS;
     const int ng = K / G;
     const int szst = ng | 1;                        // odd: 16 columns at one group hit distinct banks
 
@@ -309,6 +310,47 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ct_wave
     }
 }
 
+template <int XR, int WPL, int NW, int DEPTH, int CT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ct_waves_per_eu(XR, WPL, CT, NW)))) void coltile_kernel(
+    const half_t* __restrict__ x, const uint32_t* __restrict__ qweight, const half_t* __restrict__ scales,
+    const half_t* __restrict__ zeros, half_t* __restrict__ y, int M, int N, int K) {
+    coltile_body<XR, WPL, NW, DEPTH, CT>(x, qweight, scales, zeros, y, M, N, K, blockIdx.x);
+}
+
+// Several layers that share x in one launch: layer i owns the blocks
+// [first[i], first[i + 1]) (first[0] = 0; entries past the last layer are
+// INT_MAX), each block working on its own layer's tensors. The layer comes
+// from compares of the (uniform) block index with the bounds and scalar
+// selects; an array indexed by a layer number would go to scratch memory.
+struct CtLayerTable {
+    const uint32_t* qweight[kGemvMaxLayers];
+    const half_t* scales[kGemvMaxLayers];
+    const half_t* zeros[kGemvMaxLayers];
+    half_t* y[kGemvMaxLayers];
+    int n[kGemvMaxLayers];
+    int first[kGemvMaxLayers];
+};
+template <typename T>
+__device__ inline T ct_pick(const CtLayerTable& L, int b, T a0, T a1, T a2, T a3) {
+    T v = a0;
+    v = b >= L.first[1] ? a1 : v;
+    v = b >= L.first[2] ? a2 : v;
+    v = b >= L.first[3] ? a3 : v;
+    return v;
+}
+template <int XR, int WPL, int NW, int DEPTH, int CT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ct_waves_per_eu(XR, WPL, CT, NW)))) void coltile_grouped_kernel(
+    const half_t* __restrict__ x, int M, int K, CtLayerTable L) {
+    const int b = blockIdx.x;
+    const uint32_t* q = ct_pick(L, b, L.qweight[0], L.qweight[1], L.qweight[2], L.qweight[3]);
+    const half_t* sc = ct_pick(L, b, L.scales[0], L.scales[1], L.scales[2], L.scales[3]);
+    const half_t* zr = ct_pick(L, b, L.zeros[0], L.zeros[1], L.zeros[2], L.zeros[3]);
+    half_t* y = ct_pick(L, b, L.y[0], L.y[1], L.y[2], L.y[3]);
+    const int n = ct_pick(L, b, L.n[0], L.n[1], L.n[2], L.n[3]);
+    const int f = ct_pick(L, b, L.first[0], L.first[1], L.first[2], L.first[3]);
+    coltile_body<XR, WPL, NW, DEPTH, CT>(x, q, sc, zr, y, M, n, K, b - f);
+}
+
 // rows of x a launch stages: M rounded up to 4, 8, 16 or 32
 int ct_rows(int64_t M) { return M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : 32; }
 // largest tile count an instance takes without spilling
@@ -393,59 +435,110 @@ int ct_max_shared() {
     return cached;
 }
 
+// What a launch computes: one layer (qweight, scales, zeros, y; N rows),
+// or with layers != nullptr the layers of that list, each on whole blocks
+// (N is then the layers' total, which sets the tile and wave counts).
+struct CtTarget {
+    const uint32_t* qweight;
+    const half_t* scales;
+    const half_t* zeros;
+    half_t* y;
+    const GemvLayers* layers;
+};
+
+template <typename Kernel>
+awq_status ct_allow_lds(Kernel* kern) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            ct_max_shared()) != hipSuccess)
+        return AWQ_ERR_HIP;
+    return AWQ_OK;
+}
+
 template <int XR, int WPL, int NW, int CT>
-awq_status launch_ct(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
-                     int N, int K, half_t* y, hipStream_t stream) {
+awq_status launch_ct(const half_t* x, const CtTarget& tg, int M, int N, int K, hipStream_t stream) {
     constexpr int DEPTH = ct_depth(XR, WPL, CT);
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&coltile_kernel<XR, WPL, NW, DEPTH, CT>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, ct_max_shared()) != hipSuccess)
-            return AWQ_ERR_HIP;
-        attr_set = true;
-    }
+    constexpr int COLS = kCtCols * CT;
     const size_t lds = ct_lds_bytes(K, WPL * 32, XR, NW, CT);
-    const int64_t blocks = ceil_div(N, kCtCols * CT);
-    hipLaunchKernelGGL((coltile_kernel<XR, WPL, NW, DEPTH, CT>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64),
-                       lds, stream, x, qweight, scales, zeros, y, M, N, K);
+    if (tg.layers == nullptr) {
+        static bool attr_set = false;
+        if (!attr_set) {
+            const awq_status st = ct_allow_lds(&coltile_kernel<XR, WPL, NW, DEPTH, CT>);
+            if (st != AWQ_OK) return st;
+            attr_set = true;
+        }
+        const int64_t blocks = ceil_div(N, COLS);
+        hipLaunchKernelGGL((coltile_kernel<XR, WPL, NW, DEPTH, CT>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(NW * 64), lds, stream, x, tg.qweight, tg.scales, tg.zeros, tg.y, M, N, K);
+        return last_launch_status();
+    }
+    static bool attr_set_grouped = false;
+    if (!attr_set_grouped) {
+        const awq_status st = ct_allow_lds(&coltile_grouped_kernel<XR, WPL, NW, DEPTH, CT>);
+        if (st != AWQ_OK) return st;
+        attr_set_grouped = true;
+    }
+    const GemvLayers& ly = *tg.layers;
+    CtLayerTable T{};
+    int64_t blocks = 0;
+    for (int i = 0; i < kGemvMaxLayers; ++i) {
+        if (i < ly.n) {
+            const int rows = ly.row0[i + 1] - ly.row0[i];
+            T.qweight[i] = ly.qweight[i];
+            T.scales[i] = ly.scales[i];
+            T.zeros[i] = ly.zeros[i];
+            T.y[i] = ly.y[i];
+            T.n[i] = rows;
+            T.first[i] = static_cast<int>(blocks);
+            blocks += ceil_div(rows, COLS);
+        } else {
+            T.first[i] = INT32_MAX;
+        }
+    }
+    hipLaunchKernelGGL((coltile_grouped_kernel<XR, WPL, NW, DEPTH, CT>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(NW * 64), lds, stream, x, M, K, T);
     return last_launch_status();
 }
 
 template <int XR, int WPL, int CT>
-awq_status launch_ct_nw(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
-                        int N, int K, half_t* y, hipStream_t stream) {
+awq_status launch_ct_nw(const half_t* x, const CtTarget& tg, int M, int N, int K, hipStream_t stream) {
     switch (ct_waves(M, N, K, WPL * 32, CT)) {
         case 16:
-            if constexpr (ct_sixteen_ok(XR, WPL, CT))
-                return launch_ct<XR, WPL, 16, CT>(x, qweight, scales, zeros, M, N, K, y, stream);
-            return launch_ct<XR, WPL, 8, CT>(x, qweight, scales, zeros, M, N, K, y, stream);
-        case 8: return launch_ct<XR, WPL, 8, CT>(x, qweight, scales, zeros, M, N, K, y, stream);
-        default: return launch_ct<XR, WPL, 4, CT>(x, qweight, scales, zeros, M, N, K, y, stream);
+            if constexpr (ct_sixteen_ok(XR, WPL, CT)) return launch_ct<XR, WPL, 16, CT>(x, tg, M, N, K, stream);
+            return launch_ct<XR, WPL, 8, CT>(x, tg, M, N, K, stream);
+        case 8: return launch_ct<XR, WPL, 8, CT>(x, tg, M, N, K, stream);
+        default: return launch_ct<XR, WPL, 4, CT>(x, tg, M, N, K, stream);
     }
 }
 
 template <int XR, int WPL>
-awq_status launch_ct_tiles(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros,
-                           int M, int N, int K, half_t* y, hipStream_t stream) {
+awq_status launch_ct_tiles(const half_t* x, const CtTarget& tg, int M, int N, int K, hipStream_t stream) {
     switch (ct_tiles(M, N, K, WPL * 32)) {
-        case 1: return launch_ct_nw<XR, WPL, 1>(x, qweight, scales, zeros, M, N, K, y, stream);
-        case 2: return launch_ct_nw<XR, WPL, 2>(x, qweight, scales, zeros, M, N, K, y, stream);
+        case 1: return launch_ct_nw<XR, WPL, 1>(x, tg, M, N, K, stream);
+        case 2: return launch_ct_nw<XR, WPL, 2>(x, tg, M, N, K, stream);
         case 3:
-            if constexpr (ct_max_tiles(XR, WPL) >= 3 && XR >= 16)
-                return launch_ct_nw<XR, WPL, 3>(x, qweight, scales, zeros, M, N, K, y, stream);
+            if constexpr (ct_max_tiles(XR, WPL) >= 3 && XR >= 16) return launch_ct_nw<XR, WPL, 3>(x, tg, M, N, K, stream);
             return AWQ_ERR_CONFIG;
-        default: return launch_ct_nw<XR, WPL, ct_max_tiles(XR, WPL)>(x, qweight, scales, zeros, M, N, K, y, stream);
+        default: return launch_ct_nw<XR, WPL, ct_max_tiles(XR, WPL)>(x, tg, M, N, K, stream);
     }
 }
 
 template <int WPL>
-awq_status launch_ct_mb(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros, int M,
-                        int N, int K, half_t* y, hipStream_t stream) {
+awq_status launch_ct_mb(const half_t* x, const CtTarget& tg, int M, int N, int K, hipStream_t stream) {
     switch (ct_rows(M)) {
-        case 4: return launch_ct_tiles<4, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
-        case 8: return launch_ct_tiles<8, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
-        case 16: return launch_ct_tiles<16, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
-        default: return launch_ct_tiles<32, WPL>(x, qweight, scales, zeros, M, N, K, y, stream);
+        case 4: return launch_ct_tiles<4, WPL>(x, tg, M, N, K, stream);
+        case 8: return launch_ct_tiles<8, WPL>(x, tg, M, N, K, stream);
+        case 16: return launch_ct_tiles<16, WPL>(x, tg, M, N, K, stream);
+        default: return launch_ct_tiles<32, WPL>(x, tg, M, N, K, stream);
+    }
+}
+
+awq_status launch_ct_g(const half_t* x, const CtTarget& tg, int M, int N, int K, int group_size, hipStream_t stream) {
+    switch (group_size) {
+        case 32: return launch_ct_mb<1>(x, tg, M, N, K, stream);
+        case 64: return launch_ct_mb<2>(x, tg, M, N, K, stream);
+        case 128: return launch_ct_mb<4>(x, tg, M, N, K, stream);
+        case 256: return launch_ct_mb<8>(x, tg, M, N, K, stream);
+        default: return AWQ_ERR_CONFIG;
     }
 }
 
@@ -484,14 +577,17 @@ awq_status launch_coltile(const half_t* x, const uint32_t* qweight, const half_t
                           int64_t M, int64_t N, int64_t K, int group_size, half_t* y, hipStream_t stream) {
     if (M == 0 || N == 0) return AWQ_OK;
     if (!coltile_supported(M, N, K, group_size)) return AWQ_ERR_CONFIG;
-    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-    switch (group_size) {
-        case 32: return launch_ct_mb<1>(x, qweight, scales, zeros, m, n, k, y, stream);
-        case 64: return launch_ct_mb<2>(x, qweight, scales, zeros, m, n, k, y, stream);
-        case 128: return launch_ct_mb<4>(x, qweight, scales, zeros, m, n, k, y, stream);
-        case 256: return launch_ct_mb<8>(x, qweight, scales, zeros, m, n, k, y, stream);
-        default: return AWQ_ERR_CONFIG;
-    }
+    const CtTarget tg{qweight, scales, zeros, y, nullptr};
+    return launch_ct_g(x, tg, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), group_size, stream);
+}
+
+awq_status launch_coltile_grouped(const half_t* x, const GemvLayers& layers, int64_t M, int64_t K, int group_size,
+                                  hipStream_t stream) {
+    const int64_t total = layers.row0[layers.n];
+    if (M == 0 || total == 0) return AWQ_OK;
+    if (!coltile_supported(M, total, K, group_size)) return AWQ_ERR_CONFIG;
+    const CtTarget tg{nullptr, nullptr, nullptr, nullptr, &layers};
+    return launch_ct_g(x, tg, static_cast<int>(M), static_cast<int>(total), static_cast<int>(K), group_size, stream);
 }
 
 }  // namespace awq
