@@ -74,6 +74,7 @@ def test_decode_projections(Ns, M):
     ((777,), 4096, 32, 2),                # one layer
     ((300, 500, 700, 900), 2048, 256, 1), # four layers
     ((512, 512, 512), 11008, 128, 1),     # a split layer's q/k/v share: one-shot, three items per row
+    ((512, 512, 512), 11008, 128, 2),     # the same at two rows of x
     ((1376, 1376), 5120, 64, 1),          # two items per row, one-shot
     ((640, 640, 640, 640), 13824, 128, 1),# stacked past one round (persistent), each alone one-shot
 ])

@@ -287,6 +287,7 @@ def test_linear_ragged_both_paths(M, N, K, G):
         assert_linear_close(run_linear(lay["x"], qw, sc, zr, G, awq.PATH_GEMV), y_ref)
 
 
+@pytest.mark.parametrize("M", [1, 2])
 @pytest.mark.parametrize("N,K,G", [
     (512, 11008, 128),    # three items per row, few rows: one-shot, every item in flight
     (37, 13824, 64),      # four items, a ragged handful of rows
@@ -296,13 +297,13 @@ def test_linear_ragged_both_paths(M, N, K, G):
     (4500, 5120, 128),    # two items past one round: persistent
     (1500, 12288, 32),    # three items at G = 32
 ])
-def test_gemv_m1_long_rows(N, K, G):
-    """M = 1 on rows of 2-4 items (4096 < K <= 16384): layers of few rows
+def test_gemv_long_rows(N, K, G, M):
+    """M <= 2 on rows of 2-4 items (4096 < K <= 16384): layers of few rows
     (one GPU's share of a split layer) take the one-shot form with every item
     in flight, larger ones the persistent streaming form; both against the
     oracle, element by element."""
-    lay = synth.make_layer(N, K, 1, seed=[110, N, K, G], w_std=0.02)
-    say("gemv m1 long rows", N, K, G)
+    lay = synth.make_layer(N, K, M, seed=[110, M, N, K, G], w_std=0.02)
+    say("gemv long rows", M, N, K, G)
     qw, sc, zr = oracle.quantize(lay["w"], G)
     y_ref = oracle.linear_ref(lay["x"], qw, sc, zr, G)
     assert_linear_close(run_linear(lay["x"], qw, sc, zr, G, awq.PATH_GEMV), y_ref)

@@ -574,7 +574,7 @@ awq_status launch_t(const half_t* x, const GemvTarget<NL>& tg, int64_t N, int64_
 //    of more than 3 items. Against 4 waves with a 4-deep ring (the same bytes
 //    in flight): 4096 x 11008 7.85 -> 7.13 us, 8192 x 28672 25.4 -> 24.1 us;
 //    8 waves with a 4-deep ring or 16 waves with a 2-deep one are slower.
-//  * Except INT4 rows of 2-4 items at M = 1 when all rows fit in one round
+//  * Except INT4 rows of 2-4 items at M <= 2 when all rows fit in one round
 //    of resident waves (layers of few rows, such as one GPU's share of a
 //    split layer): one-shot 8-wave blocks, one row per wave, every item in
 //    flight.
@@ -591,15 +591,17 @@ awq_status launch_m(const half_t* x, const GemvTarget<NL>& tg, int64_t N, int64_
     }
     if (kbs == 2 && BITS == 8)
         return launch_t<BITS, MT, 1, 2, 2, true, 4, NL>(x, tg, N, K, log2g, ceil_div(N, 4), stream);
-    // INT4 rows of 2-4 items, all rows within one round of resident waves
-    // (8-wave blocks of one row per wave: two per CU at 2 items, one at 3 or
-    // 4, by registers): every item in flight at once beats the persistent
-    // grid, whose few busy waves walk their rows through a 2-deep ring.
-    // Measured (us, M = 1): 512 x 13824 7.12 -> 4.70, 2048 x 13824
-    // 7.41 -> 5.79, 4096 x 5120 4.99 -> 4.45, 512 x 11008 4.41 -> 3.94; past
-    // one round it loses (3072 x 13824 7.90 -> 9.46, 2560 x 11008
-    // 6.28 -> 7.09). Rows of more items would spill.
-    if constexpr (BITS == 4 && MT == 1) {
+    // INT4 rows of 2-4 items at M <= 2, all rows within one round of
+    // resident waves (8-wave blocks of one row per wave: two per CU at 2
+    // items, one at 3 or 4, by registers): every item in flight at once
+    // beats the persistent grid, whose few busy waves walk their rows through
+    // a 2-deep ring. Measured (us): M = 1 512 x 13824 7.12 -> 4.70, 2048 x
+    // 13824 7.41 -> 5.79, 4096 x 5120 4.99 -> 4.45, 512 x 11008 4.41 -> 3.94;
+    // M = 2 512 x 5120 5.71 -> 3.62, 512 x 11008 7.92 -> 5.21, 2048 x 13824
+    // 9.55 -> 7.14; past one round it loses (M = 1: 3072 x 13824
+    // 7.90 -> 9.46, 2560 x 11008 6.28 -> 7.09). Rows of more items would
+    // spill.
+    if constexpr (BITS == 4 && MT <= 2) {
         if (kbs <= 4 && N <= 8 * cu_count() * (kbs == 2 ? 2 : 1)) {
             if (kbs == 2) return launch_t<BITS, MT, 1, 2, 2, true, 8, NL>(x, tg, N, K, log2g, ceil_div(N, 8), stream);
             if (kbs == 3) return launch_t<BITS, MT, 1, 2, 3, true, 8, NL>(x, tg, N, K, log2g, ceil_div(N, 8), stream);
