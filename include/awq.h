@@ -159,12 +159,14 @@ awq_status awq_gemm(const void* x_f16, const uint32_t* qweight,
  * M <= 32, G <= 256, M * K * 2 < 2^31 and the tile's (scale, zero) pairs in
  * LDS; no workspace).
  * Any other path, or a path whose requirement fails, returns AWQ_ERR_CONFIG.
- * The automatic choice takes the column tiles for 3 <= M <= 32 on layers
- * of up to 48 Mi weights, or up to 96 Mi with K <= 8192, and on any shape
- * they support when the call has no workspace; otherwise the GEMV for
- * M <= 4 where it can run; the skinny kernel for M <= 64, except for M <= 8
- * where it would have to stage K in phases and the GEMV can run (then the
- * GEMV); then the GEMM.
+ * The automatic choice takes the GEMV for M <= 2, and for M <= 4 on
+ * layers of few rows of 4096 < K <= 16384 (all rows within one round of
+ * its resident waves); the column tiles for 3 <= M <= 32 on layers of up
+ * to 48 Mi weights, or up to 96 Mi with K <= 8192, and on any shape they
+ * support when the call has no workspace; otherwise the GEMV for M <= 4
+ * where it can run; the skinny kernel for M <= 64, except for M <= 8 where
+ * it would have to stage K in phases and the GEMV can run (then the GEMV);
+ * then the GEMM.
  */
 awq_status awq_gemm_path(const void* x_f16, const uint32_t* qweight,
                          const void* scales_f16, const void* zeros_f16,

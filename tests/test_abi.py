@@ -192,6 +192,11 @@ def test_kernel_choice(L):
     k.argtypes = [ctypes.c_int64] * 3 + [ctypes.c_int] * 3
     assert k(1, 4096, 4096, 128, 0, 0) == 1            # decode: the GEMV
     assert k(4, 4096, 11008, 128, 0, 0) == 4           # column tiles
+    assert k(4, 512, 11008, 128, 0, 0) == 1            # few long rows at 4 rows of x: the GEMV one-shot
+    assert k(3, 1000, 8192, 64, 0, 1) == 1
+    assert k(4, 2049, 5120, 128, 0, 0) == 4            # past one round of resident waves: column tiles
+    assert k(4, 512, 4096, 128, 0, 0) == 4             # rows of one item: column tiles
+    assert k(5, 512, 11008, 128, 0, 0) == 4            # 5 rows of x: column tiles
     assert k(16, 4096, 4096, 128, 0, 1) == 4
     assert k(16, 8192, 28672, 128, 0, 1) == 3          # large layer: the skinny kernel
     assert k(16, 8192, 28672, 128, 0, 0) == 4          # ... which without a workspace walks K in phases

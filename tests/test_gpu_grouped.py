@@ -120,6 +120,7 @@ def test_batched_decode_projections(Ns, M):
     ((777, 1500), 6144, 256, 16),          # G = 256
     ((300, 500, 700, 900), 2048, 128, 32), # four layers, 32 rows of x
     ((2000, 3000, 1000), 4096, 128, 12),   # several tiles per block, from the stacked rows
+    ((512, 512, 512), 11008, 128, 4),      # few rows at 4 rows of x (alone each the GEMV): stacked column tiles
 ])
 def test_batched_ragged_layers(Ns, K, G, M):
     say("grouped batched ragged", Ns, K, G, M)

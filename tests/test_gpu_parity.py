@@ -311,6 +311,26 @@ def test_gemv_long_rows(N, K, G, M):
 
 
 @pytest.mark.parametrize("M,N,K,G", [
+    (3, 512, 11008, 128),     # few rows, three items per row: the automatic choice takes the GEMV
+    (4, 1000, 8192, 64),      # two items per row at 4 rows of x
+    (4, 2048, 13824, 128),    # four items, one round of resident waves
+    (4, 2049, 5120, 128),     # two items at M = 4 past one round: column tiles (and the GEMV persistent)
+])
+def test_gemv_few_rows_small_batches(M, N, K, G):
+    """3 <= M <= 4 on layers of few, long rows: the automatic choice takes the
+    GEMV's one-shot form where all rows fit in one round of resident waves,
+    else the column tiles; both, and the forced GEMV, against the oracle."""
+    lay = synth.make_layer(N, K, M, seed=[111, M, N, K, G], w_std=0.02)
+    say("gemv few rows", M, N, K, G)
+    qw, sc, zr = oracle.quantize(lay["w"], G)
+    y_ref = oracle.linear_ref(lay["x"], qw, sc, zr, G)
+    assert_linear_close(run_linear(lay["x"], qw, sc, zr, G, awq.PATH_AUTO), y_ref)
+    assert_linear_close(run_linear(lay["x"], qw, sc, zr, G, awq.PATH_GEMV), y_ref)
+    expect = "coltile" if N == 2049 else "gemv"
+    assert awq.gemm_kernel(M, N, K, G) == expect
+
+
+@pytest.mark.parametrize("M,N,K,G", [
     (3, 4099, 1024, 64),      # 4 weight rows per wave, a ragged last row set
     (5, 4100, 2048, 128),
     (8, 4111, 512, 32),

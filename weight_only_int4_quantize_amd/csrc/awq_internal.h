@@ -57,6 +57,9 @@ awq_status launch_quantize(const half_t* w, const float* channel_scale, int64_t 
 constexpr int kGemvMaxM = 8;
 // bits = 8: the W8A16 form (qweight [N, K/4], four byte codes per word).
 bool gemv_supported(int64_t M, int64_t K, int bits = 4);
+// Layers of few rows and long rows that the GEMV takes one-shot (every item
+// of a row in flight); the automatic choice prefers it there up to M = 4.
+bool gemv_few_rows(int64_t M, int64_t N, int64_t K, int bits = 4);
 awq_status launch_gemv(const half_t* x, const uint32_t* qweight, const half_t* scales,
                        const half_t* zeros, int64_t M, int64_t N, int64_t K, int group_size,
                        half_t* y, hipStream_t stream, int bits = 4);

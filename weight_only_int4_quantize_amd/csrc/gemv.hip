@@ -482,15 +482,38 @@ __global__ __launch_bounds__(NW * 64) void gemv_grouped_kernel(const half_t* __r
                                                            shape >> 8, nblocks, L);
 }
 
+}  // namespace
+
+// INT4 rows of 2-4 items (4096 < K <= 16384) at M <= 4, with every row within
+// one round of resident waves of the one-shot 8-wave instances (one row per
+// wave; two blocks per CU at 2 items and M <= 3, one otherwise, by their
+// registers: 97-102, 133-146 and 169-253 VGPRs). There every item in flight
+// at once beats the persistent grid, whose few busy waves walk their rows
+// through a 2-deep ring. Measured (us): M = 1 512 x 13824 7.12 -> 4.70,
+// 2048 x 13824 7.41 -> 5.79, 4096 x 5120 4.99 -> 4.45, 512 x 11008
+// 4.41 -> 3.94; M = 2 512 x 5120 5.71 -> 3.62, 512 x 11008 7.92 -> 5.21,
+// 2048 x 13824 9.55 -> 7.14; M = 4 512 x 11008 11.39 -> 7.92, 1024 x 8192
+// 8.36 -> 5.71. Past one round it loses (M = 1: 3072 x 13824 7.90 -> 9.46,
+// 2560 x 11008 6.28 -> 7.09). Rows of more items would spill.
+bool gemv_few_rows(int64_t M, int64_t N, int64_t K, int bits) {
+    if (bits != 4 || M < 1 || M > 4 || N < 1) return false;
+    const int64_t kbs = ceil_div(K >> 5, 128);
+    return kbs >= 2 && kbs <= 4 && N <= 8 * cu_count() * (kbs == 2 && M <= 3 ? 2 : 1);
+}
+
+namespace {
+
+// LDS bytes a block may take: the device's limit, or gfx950's 160 KB when no
+// device can be queried (host-only kernel-choice queries)
 int max_shared_bytes() {
     static int cached = -1;
     if (cached < 0) {
-        int dev = 0, v = 65536;
+        int dev = 0, v = 160 * 1024;
         if (hipGetDevice(&dev) == hipSuccess &&
             hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess) {
             cached = v;
         } else {
-            cached = 65536;
+            cached = 160 * 1024;
         }
     }
     return cached;
@@ -574,10 +597,10 @@ awq_status launch_t(const half_t* x, const GemvTarget<NL>& tg, int64_t N, int64_
 //    of more than 3 items. Against 4 waves with a 4-deep ring (the same bytes
 //    in flight): 4096 x 11008 7.85 -> 7.13 us, 8192 x 28672 25.4 -> 24.1 us;
 //    8 waves with a 4-deep ring or 16 waves with a 2-deep one are slower.
-//  * Except INT4 rows of 2-4 items at M <= 2 when all rows fit in one round
+//  * Except INT4 rows of 2-4 items at M <= 4 when all rows fit in one round
 //    of resident waves (layers of few rows, such as one GPU's share of a
 //    split layer): one-shot 8-wave blocks, one row per wave, every item in
-//    flight.
+//    flight (gemv_few_rows).
 template <int BITS, int MT, int NL = 0>
 awq_status launch_m(const half_t* x, const GemvTarget<NL>& tg, int64_t N, int64_t K, int log2g,
                     hipStream_t stream) {
@@ -591,18 +614,9 @@ awq_status launch_m(const half_t* x, const GemvTarget<NL>& tg, int64_t N, int64_
     }
     if (kbs == 2 && BITS == 8)
         return launch_t<BITS, MT, 1, 2, 2, true, 4, NL>(x, tg, N, K, log2g, ceil_div(N, 4), stream);
-    // INT4 rows of 2-4 items at M <= 2, all rows within one round of
-    // resident waves (8-wave blocks of one row per wave: two per CU at 2
-    // items, one at 3 or 4, by registers): every item in flight at once
-    // beats the persistent grid, whose few busy waves walk their rows through
-    // a 2-deep ring. Measured (us): M = 1 512 x 13824 7.12 -> 4.70, 2048 x
-    // 13824 7.41 -> 5.79, 4096 x 5120 4.99 -> 4.45, 512 x 11008 4.41 -> 3.94;
-    // M = 2 512 x 5120 5.71 -> 3.62, 512 x 11008 7.92 -> 5.21, 2048 x 13824
-    // 9.55 -> 7.14; past one round it loses (M = 1: 3072 x 13824
-    // 7.90 -> 9.46, 2560 x 11008 6.28 -> 7.09). Rows of more items would
-    // spill.
-    if constexpr (BITS == 4 && MT <= 2) {
-        if (kbs <= 4 && N <= 8 * cu_count() * (kbs == 2 ? 2 : 1)) {
+    // Layers of few rows (gemv_few_rows): one-shot 8-wave blocks.
+    if constexpr (BITS == 4 && MT <= 4) {
+        if (gemv_few_rows(MT, N, K, BITS)) {
             if (kbs == 2) return launch_t<BITS, MT, 1, 2, 2, true, 8, NL>(x, tg, N, K, log2g, ceil_div(N, 8), stream);
             if (kbs == 3) return launch_t<BITS, MT, 1, 2, 3, true, 8, NL>(x, tg, N, K, log2g, ceil_div(N, 8), stream);
             return launch_t<BITS, MT, 1, 2, 4, true, 8, NL>(x, tg, N, K, log2g, ceil_div(N, 8), stream);
