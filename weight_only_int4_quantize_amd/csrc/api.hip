@@ -380,29 +380,28 @@ awq_status awq_gemm_grouped(const void* x_f16, int n_layers, const uint32_t* con
     if (total > (int64_t(1) << 31) - 256) return AWQ_ERR_SHAPE;
     if (M == 0 || total == 0) return AWQ_OK;
     const hipStream_t s = as_stream(stream);
-    int chosen = choose_path(M, total, K, group_size, 0, false);
-    // 3-4 rows on few-row layers (which awq_gemm gives the GEMV one at a
-    // time): one column-tile launch over the stacked layers instead
-    if (chosen == 1 && M > kGemvGroupedMaxM && coltile_supported(M, total, K, group_size)) chosen = 4;
-    if ((chosen == 1 && M <= kGemvGroupedMaxM) || chosen == 4) {
-        GemvLayers L{};
-        int r = 0;
-        for (int i = 0; i < n_layers; ++i) {
-            if (N[i] == 0) continue;
-            L.qweight[L.n] = qweight[i];
-            L.scales[L.n] = static_cast<const half_t*>(scales_f16[i]);
-            L.zeros[L.n] = static_cast<const half_t*>(zeros_f16[i]);
-            L.y[L.n] = static_cast<half_t*>(y_f16[i]);
-            L.row0[L.n] = r;
-            r += static_cast<int>(N[i]);
-            ++L.n;
-        }
+    const int chosen = choose_path(M, total, K, group_size, 0, false);
+    GemvLayers L{};
+    int r = 0;
+    for (int i = 0; i < n_layers; ++i) {
+        if (N[i] == 0) continue;
+        L.qweight[L.n] = qweight[i];
+        L.scales[L.n] = static_cast<const half_t*>(scales_f16[i]);
+        L.zeros[L.n] = static_cast<const half_t*>(zeros_f16[i]);
+        L.y[L.n] = static_cast<half_t*>(y_f16[i]);
         L.row0[L.n] = r;
-        for (int i = L.n + 1; i <= kGemvMaxLayers; ++i) L.row0[i] = INT32_MAX;
-        const half_t* x = static_cast<const half_t*>(x_f16);
-        if (chosen == 4) return launch_coltile_grouped(x, L, M, K, group_size, s);
-        return launch_gemv_grouped(x, L, M, K, group_size, s);
+        r += static_cast<int>(N[i]);
+        ++L.n;
     }
+    L.row0[L.n] = r;
+    for (int i = L.n + 1; i <= kGemvMaxLayers; ++i) L.row0[i] = INT32_MAX;
+    const half_t* x = static_cast<const half_t*>(x_f16);
+    if (chosen == 1 && M <= kGemvGroupedMaxM) return launch_gemv_grouped(x, L, M, K, group_size, s);
+    // column tiles over the stacked layers where awq_gemm takes them, and at
+    // 3-4 rows of x on few-row layers (which awq_gemm gives the GEMV one at a
+    // time); the layers' own block counts must fit the launch
+    if ((chosen == 4 || (chosen == 1 && M > kGemvGroupedMaxM)) && coltile_grouped_supported(M, L, K, group_size))
+        return launch_coltile_grouped(x, L, M, K, group_size, s);
     for (int i = 0; i < n_layers; ++i) {
         const awq_status st = gemm_dispatch(x_f16, qweight[i], scales_f16[i], zeros_f16[i], M, N[i], K, group_size,
                                             y_f16[i], 0, nullptr, 0, false, false, s);

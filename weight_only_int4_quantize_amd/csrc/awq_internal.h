@@ -167,6 +167,9 @@ awq_status launch_coltile(const half_t* x, const uint32_t* qweight, const half_t
 // tile and wave counts those of their total rows.
 awq_status launch_coltile_grouped(const half_t* x, const GemvLayers& layers, int64_t M, int64_t K,
                                   int group_size, hipStream_t stream);
+// whether that launch can run (its tile and wave counts from the layers' own
+// blocks, and their LDS)
+bool coltile_grouped_supported(int64_t M, const GemvLayers& layers, int64_t K, int group_size);
 
 // Mixed precision with fp16 salient channels.
 awq_status launch_select_salient(const double* m, int64_t K, int n, int* idx, hipStream_t stream);

@@ -369,7 +369,15 @@ constexpr int ct_max_tiles(int xr, int wpl) { return xr * wpl >= 256 ? 2 : 4; }
 // dominate, and more waves per CU matter more): 2 from 1.25 column tiles
 // per CU on rows of 40 groups and more, else 1; M = 4 on 13824 x 5120
 // 15.5 / 14.4 / - / 17.4, 11008 x 4096 10.3 / 10.9 / - / 13.3.
-int ct_tiles(int64_t M, int64_t N, int64_t K, int group_size) {
+// Blocks of a launch at ct tiles per block: N rows of one layer, or with L
+// the layers of L, each on whole blocks of its own columns.
+int64_t ct_blocks(int64_t N, int ct, const GemvLayers* L) {
+    if (L == nullptr) return ceil_div(N, kCtCols * ct);
+    int64_t b = 0;
+    for (int i = 0; i < L->n; ++i) b += ceil_div(L->row0[i + 1] - L->row0[i], kCtCols * ct);
+    return b;
+}
+int ct_tiles(int64_t M, int64_t N, int64_t K, int group_size, const GemvLayers* L = nullptr) {
     const int64_t cu = cu_count();
     const int64_t tiles = ceil_div(N, kCtCols);
     const int xr = ct_rows(M);
@@ -378,7 +386,7 @@ int ct_tiles(int64_t M, int64_t N, int64_t K, int group_size) {
         int best = 1;
         int64_t best_cost = INT64_MAX;
         for (int ct = 1; ct <= most; ++ct) {
-            const int64_t cost = ceil_div(ceil_div(tiles, ct), cu) * (ct + xr / 4);
+            const int64_t cost = ceil_div(ct_blocks(N, ct, L), cu) * (ct + xr / 4);
             if (cost < best_cost) {
                 best_cost = cost;
                 best = ct;
@@ -398,11 +406,11 @@ constexpr bool ct_sixteen_ok(int xr, int wpl, int ct) { return ct == 1 && xr * w
 // M = 16 6.5 / 7.1 / 8.9; 4096 x 11008 M = 4 13.4 / 10.0 / 11.1;
 // 13824 x 5120 at M = 4 on 2 tiles 14.4 / 15.9; 8192 x 28672 at M = 16 on
 // 2 tiles 49.1 / 44.1.
-int ct_waves(int64_t M, int64_t N, int64_t K, int group_size, int ct) {
+int ct_waves(int64_t M, int64_t N, int64_t K, int group_size, int ct, const GemvLayers* L = nullptr) {
     const int64_t ng = K / group_size;
     if (ng < 16) return 4;
     const int64_t cu = cu_count();
-    const int64_t blocks = ceil_div(N, kCtCols * ct);
+    const int64_t blocks = ct_blocks(N, ct, L);
     const int xr = ct_rows(M);
     if (ct > 1) return blocks * 5 >= 8 * cu ? 4 : 8;
     if (blocks * 2 >= 5 * cu) return 4;
@@ -501,7 +509,7 @@ awq_status launch_ct(const half_t* x, const CtTarget& tg, int M, int N, int K, h
 
 template <int XR, int WPL, int CT>
 awq_status launch_ct_nw(const half_t* x, const CtTarget& tg, int M, int N, int K, hipStream_t stream) {
-    switch (ct_waves(M, N, K, WPL * 32, CT)) {
+    switch (ct_waves(M, N, K, WPL * 32, CT, tg.layers)) {
         case 16:
             if constexpr (ct_sixteen_ok(XR, WPL, CT)) return launch_ct<XR, WPL, 16, CT>(x, tg, M, N, K, stream);
             return launch_ct<XR, WPL, 8, CT>(x, tg, M, N, K, stream);
@@ -512,7 +520,7 @@ awq_status launch_ct_nw(const half_t* x, const CtTarget& tg, int M, int N, int K
 
 template <int XR, int WPL>
 awq_status launch_ct_tiles(const half_t* x, const CtTarget& tg, int M, int N, int K, hipStream_t stream) {
-    switch (ct_tiles(M, N, K, WPL * 32)) {
+    switch (ct_tiles(M, N, K, WPL * 32, tg.layers)) {
         case 1: return launch_ct_nw<XR, WPL, 1>(x, tg, M, N, K, stream);
         case 2: return launch_ct_nw<XR, WPL, 2>(x, tg, M, N, K, stream);
         case 3:
@@ -563,14 +571,24 @@ bool coltile_preferred(int64_t M, int64_t N, int64_t K, int group_size, bool hav
     return weights <= (int64_t{48} << 20) || (K <= 8192 && weights <= (int64_t{96} << 20));
 }
 
-bool coltile_supported(int64_t M, int64_t N, int64_t K, int group_size) {
+namespace {
+bool ct_supported(int64_t M, int64_t N, int64_t K, int group_size, const GemvLayers* L) {
     if (group_size < 32 || group_size > 256) return false;
     if (M < 1 || M > kColTileMaxM || N < 1 || K < group_size || K % group_size != 0) return false;
     // 32-bit buffer offsets: x, and one 16-column tile of packed weights
-    const int ct = ct_tiles(M, N, K, group_size);
+    const int ct = ct_tiles(M, N, K, group_size, L);
     if (M * K * 2 >= (int64_t{1} << 31) || kCtCols * ct * (K / 2) >= (int64_t{1} << 31)) return false;
-    return ct_lds_bytes(K, group_size, ct_rows(M), ct_waves(M, N, K, group_size, ct), ct) <=
+    return ct_lds_bytes(K, group_size, ct_rows(M), ct_waves(M, N, K, group_size, ct, L), ct) <=
            static_cast<size_t>(ct_max_shared());
+}
+}  // namespace
+
+bool coltile_supported(int64_t M, int64_t N, int64_t K, int group_size) {
+    return ct_supported(M, N, K, group_size, nullptr);
+}
+
+bool coltile_grouped_supported(int64_t M, const GemvLayers& layers, int64_t K, int group_size) {
+    return layers.n >= 1 && ct_supported(M, layers.row0[layers.n], K, group_size, &layers);
 }
 
 awq_status launch_coltile(const half_t* x, const uint32_t* qweight, const half_t* scales, const half_t* zeros,
@@ -585,7 +603,7 @@ awq_status launch_coltile_grouped(const half_t* x, const GemvLayers& layers, int
                                   hipStream_t stream) {
     const int64_t total = layers.row0[layers.n];
     if (M == 0 || total == 0) return AWQ_OK;
-    if (!coltile_supported(M, total, K, group_size)) return AWQ_ERR_CONFIG;
+    if (!coltile_grouped_supported(M, layers, K, group_size)) return AWQ_ERR_CONFIG;
     const CtTarget tg{nullptr, nullptr, nullptr, nullptr, &layers};
     return launch_ct_g(x, tg, static_cast<int>(M), static_cast<int>(total), static_cast<int>(K), group_size, stream);
 }
