@@ -48,6 +48,29 @@ LOSS_RTOL_EXACT = 1e-4
 LOSS_RTOL_F16 = 2e-6
 
 
+def fp32_loss_rtol(x, w, w_hat):
+    """Relative bar for a loss L = ||x w_hat^T - x w^T||_F^2 whose two
+    products are accumulated in fp32, from the arithmetic rather than from
+    one kernel's rounding order. Each output of a product takes K / 16
+    accumulator additions (each MFMA step adds 16 exact fp16 products), each
+    rounding by at most u = 2^-24 of a partial sum no larger than
+    S = sum_k |x_k w_k|; as independent rounding errors the two products
+    give an output error of root-mean-square sqrt(2) u sqrt(K / 16) S. The
+    loss moves by 2 sum e delta (e = the exact difference), whose
+    root-mean-square is 2 sqrt(2) u sqrt(K / 16) sqrt(sum e^2 S^2). The bar
+    is that figure relative to L, and never below LOSS_RTOL_F16. Few outputs
+    whose differences e are small against y (few tokens, salient channels)
+    make the figure large."""
+    x64 = np.asarray(x).astype(np.float64)
+    w64 = np.asarray(w).astype(np.float64)
+    e = x64 @ (np.asarray(w_hat, np.float64) - w64).T
+    S = np.abs(x64) @ np.abs(w64).T
+    K = x64.shape[1]
+    u = 2.0 ** -24
+    sigma = 2.0 * np.sqrt(2.0) * u * np.sqrt(K / 16.0) * np.sqrt(np.sum((e * S) ** 2)) / np.sum(e * e)
+    return max(LOSS_RTOL_F16, float(sigma))
+
+
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()

@@ -21,7 +21,10 @@
 //    step straight into registers in MFMA operand order and dequantizes
 //    them there; only A goes through LDS, by LDS-DMA loads (see
 //    run_segment_direct).
-//  * Older form (G = 32, and the fp16-B reference of the scale search):
+//  * The fp16-B reference of the searches runs the direct form too, its
+//    B columns loaded as 4 16-byte pieces per lane and step, already fp16.
+//  * Older form (G = 32, and the fp16-B reference when K is not a multiple
+//    of 64):
 //    a 256-thread block owns a 256 x 128 tile, 4 wavefronts in a 2 x 2
 //    arrangement, each with 128 x 64 outputs as 4 x 2
 //    v_mfma_f32_32x32x16_f16 accumulators (128 VGPRs), so every 16-byte
@@ -238,7 +241,10 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
     static_assert(DIRECT || NT == kThreads, "the older form runs 256-thread blocks");
     constexpr int A_VECS = BM * BK / 8 / kThreads;        // uint4 of A per thread per step
     constexpr bool INT4 = BMODE == GemmB::kInt4;
-    constexpr int BITS = BMODE == GemmB::kInt8 ? 8 : 4;     // direct form: code width of B
+    // direct form: bits per B element (16: the fp16-B reference product,
+    // which has no codes, zero-points or group scales)
+    constexpr int BITS = BMODE == GemmB::kInt8 ? 8 : BMODE == GemmB::kF16 ? 16 : 4;
+    constexpr bool QB = BMODE != GemmB::kF16;              // B carries codes and group scales
     constexpr int BW = BITS / 4;                            // 16-byte B loads per column and step
     constexpr int B_WORDS = BN * BK / 8 / kThreads;       // packed words per thread per step
     constexpr int B_VECS = BN * BK / 8 / kThreads;        // fp16 B: uint4 per thread per step (int4: unused)
@@ -246,7 +252,6 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
     static_assert(TM >= 1 && TN >= 1 && A_VECS >= 1, "tile shape");
     static_assert(DIRECT || !INT4 || B_WORDS == 2, "int4 B staging: 2 words (16 codes) per thread");
     static_assert(DIRECT || INT4 || B_VECS >= 1, "fp16 B staging");
-    static_assert(!DIRECT || BMODE != GemmB::kF16, "the direct form is for quantized B");
     static_assert(DIRECT || BMODE != GemmB::kInt8, "W8 B runs the direct form only");
     constexpr int LDS_A = DIRECT ? BM * BKD : BM * LDK;
     constexpr int LDS_B = DIRECT ? 8 : BN * LDK;
@@ -419,9 +424,10 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
         const int rows_a = min(BM, M - tm), cols_b = min(BN, N - tn);
         const auto a_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(args.a) + static_cast<int64_t>(tm) * K,
                                                             0, rows_a * K * 2, 0x00020000);
+        const char* b_src = QB ? reinterpret_cast<const char*>(args.qweight) : reinterpret_cast<const char*>(args.w);
         const auto b_rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint32_t*>(args.qweight) + static_cast<int64_t>(tn) * (K * BITS / 32), 0,
-            cols_b * (K * BITS / 8), 0x00020000);
+            const_cast<char*>(b_src) + static_cast<int64_t>(tn) * (K * BITS / 8), 0, cols_b * (K * BITS / 8),
+            0x00020000);
         const auto s_rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<half_t*>(args.scales) + static_cast<int64_t>(tn) * ngroups, 0, cols_b * ngroups * 2, 0x00020000);
         const auto z_rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -493,12 +499,14 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
             zc_hi[j] = half2_t{zh, zh};
             zc_lo[j] = half2_t{zl, zl};
         };
+        if constexpr (QB) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            s_cur[j] = to_scale(s_bits_at(j, g));
-            set_zero(j, z_bits_at(j, g));
-            s_next[j] = s_bits_at(j, min(g + 1, ngroups - 1));
-            z_next[j] = z_bits_at(j, min(g + 1, ngroups - 1));
+            for (int j = 0; j < TN; ++j) {
+                s_cur[j] = to_scale(s_bits_at(j, g));
+                set_zero(j, z_bits_at(j, g));
+                s_next[j] = s_bits_at(j, min(g + 1, ngroups - 1));
+                z_next[j] = z_bits_at(j, min(g + 1, ngroups - 1));
+            }
         }
 
         // LDS-DMA loads i in [i0, i1) of A(kt) into buffer as
@@ -518,7 +526,7 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
                 load_a(kt + 2);
             }
             load_b(bn, kt + 1);
-            if (kt > kb && ((kt * BKD) % G) == 0) {
+            if (QB && kt > kb && ((kt * BKD) % G) == 0) {
                 // entering the next group: C' <- C' * s_g / s_{g+1}
                 ++g;
                 float r[TN];
@@ -550,7 +558,9 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
                     a[i] = *reinterpret_cast<const half8_t*>(&cur[swz64(wm + i * 32 + lrow, lh * 4 + ks)]);
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    if constexpr (BITS == 4)
+                    if constexpr (BITS == 16)
+                        b[j] = __builtin_bit_cast(half8_t, bw[j][ks]);   // k = 32 h + 8 ks .. + 7
+                    else if constexpr (BITS == 4)
                         b[j] = __builtin_bit_cast(half8_t, unpack_word(bw[j][0][ks], zc_hi[j], zc_lo[j], uk));
                     else
                         b[j] = __builtin_bit_cast(half8_t, unpack_bytes(bw[j][ks / 2][(ks % 2) * 2],
@@ -594,12 +604,14 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
                 __syncthreads();
             }
         }
+        if constexpr (QB) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+                for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[i][j][e] *= s_cur[j];
+                    for (int e = 0; e < 16; ++e) acc[i][j][e] *= s_cur[j];
+        }
     };
     auto segment = [&](int tm, int tn, int kb, int ke) {
         if constexpr (DIRECT)
@@ -989,7 +1001,15 @@ awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t s
     } else {
         switch (out) {
             case GemmOut::kF16: launch_cfg<kNarrowTile, GemmB::kF16, GemmOut::kF16, false>(args, workspace, stream); break;
-            case GemmOut::kF32: launch_cfg<kNarrowTile, GemmB::kF16, GemmOut::kF32, false>(args, workspace, stream); break;
+            case GemmOut::kF32:
+                // the searches' reference W . x^T: the direct form whenever K
+                // is whole 64-k steps (fp16 B straight into the operand, no
+                // unpack and no group scale), the older form otherwise
+                if (args.K % BKD == 0 && args.K * kBM * 2 < (int64_t{1} << 31))
+                    launch_cfg<kNarrowTile, GemmB::kF16, GemmOut::kF32, true, kDirectWgm>(args, nullptr, stream);
+                else
+                    launch_cfg<kNarrowTile, GemmB::kF16, GemmOut::kF32, false>(args, workspace, stream);
+                break;
             case GemmOut::kLoss: return AWQ_ERR_CONFIG;
         }
     }
