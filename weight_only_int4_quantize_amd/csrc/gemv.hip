@@ -143,7 +143,7 @@ using LayersArg = std::conditional_t<(NL > 0), GemvLayerTable, NoLayers>;
 // grouped launch): row r is row r - start of its layer's tensors, and every
 // weight load is issued before the scale and zero-point loads, whose
 // pointers come later.
-template <int BITS, int RPW, int CPL, int NL>
+template <int BITS, int RPW, int CPL, int NL, bool SZL = false>
 __device__ inline void load_batch(WeightBatch<RPW, CPL>& b, const uint32_t* __restrict__ qweight,
                                   const half_t* __restrict__ scales, const half_t* __restrict__ zeros,
                                   const LayersArg<NL>& L, int row0, bool valid, int N, int nchunk, int ngroups,
@@ -195,8 +195,10 @@ __device__ inline void load_batch(WeightBatch<RPW, CPL>& b, const uint32_t* __re
                 const int c = base + lane + 64 * j;
                 const int g = (c << Chunk<BITS>::kShift) >> log2g;
                 b.w[i][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, c * 16, 0, 0));
-                b.s[i][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, g * 2, 0, 0);
-                b.z[i][j] = __builtin_amdgcn_raw_buffer_load_b16(rz, g * 2, 0, 0);
+                if constexpr (!SZL) {
+                    b.s[i][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, g * 2, 0, 0);
+                    b.z[i][j] = __builtin_amdgcn_raw_buffer_load_b16(rz, g * 2, 0, 0);
+                }
             }
         }
     }
@@ -204,13 +206,20 @@ __device__ inline void load_batch(WeightBatch<RPW, CPL>& b, const uint32_t* __re
 
 // Consumes one item: chunks past the row end have scale 0 (zero-filled
 // loads) and read a clamped, in-range slot of the staged x.
-template <int BITS, int MT, int RPW, int CPL>
+// SZL: the (scale, zero) pairs come from the block's LDS copy (szrow: the
+// item's first row, ngroups words per row), where chunks past the row end
+// read a clamped group and are masked to scale 0 instead.
+template <int BITS, int MT, int RPW, int CPL, bool SZL = false>
 __device__ inline void compute_batch(const WeightBatch<RPW, CPL>& b, const uint4* __restrict__ xp,
                                      const float2* __restrict__ xo, float (&acc)[RPW][MT], int nchunk,
-                                     int base, int lane, const UnpackConsts& k) {
+                                     int base, int lane, const UnpackConsts& k,
+                                     const uint32_t* __restrict__ szrow = nullptr, int ngroups = 0,
+                                     int log2g = 0) {
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
+        [[maybe_unused]] const bool in_row = base + lane + 64 * j < nchunk;
         const int c = min(base + lane + 64 * j, nchunk - 1);
+        [[maybe_unused]] const int g = (c << Chunk<BITS>::kShift) >> log2g;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const float2 o = xo[m * nchunk + c];
@@ -231,8 +240,16 @@ __device__ inline void compute_batch(const WeightBatch<RPW, CPL>& b, const uint4
                     d = byte_dot(b.w[i][j].z, p[Chunk<BITS>::kXV - 1].x, p[Chunk<BITS>::kXV - 1].y, d, k);
                     d = byte_dot(b.w[i][j].w, p[Chunk<BITS>::kXV - 1].z, p[Chunk<BITS>::kXV - 1].w, d, k);
                 }
-                const float s = static_cast<float>(__builtin_bit_cast(half_t, b.s[i][j]));
-                const float z = static_cast<float>(__builtin_bit_cast(half_t, b.z[i][j]));
+                float s, z;
+                if constexpr (SZL) {
+                    const uint32_t sz = szrow[i * ngroups + g];
+                    s = in_row ? static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(sz & 0xFFFFu)))
+                               : 0.f;
+                    z = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(sz >> 16)));
+                } else {
+                    s = static_cast<float>(__builtin_bit_cast(half_t, b.s[i][j]));
+                    z = static_cast<float>(__builtin_bit_cast(half_t, b.z[i][j]));
+                }
                 acc[i][m] += s * (d - (o.x + z * o.y));
             }
         }
@@ -267,7 +284,23 @@ __device__ inline float wave_sum_lane63(float v) {
 //
 // NL > 0: the rows of NL layers sharing x, stacked (L); N is the total, and
 // each row's weights and output belong to its layer.
-template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT, int NW, int NL>
+//
+// SZL (streaming, single layer): the (scale, zero) pairs of the block's rows
+// are staged once in LDS as packed words instead of being loaded with every
+// chunk (two 2-byte loads per 16-byte weight load). A wave's row sets are
+// set = wid + k W, so for each k the block's rows form one run of NW RPW
+// consecutive rows, whose pairs are contiguous in memory; run k lands at
+// word k NW RPW ngroups, so row i of wave w in set k is word
+// ((k NW + w) RPW + i) ngroups. Needs (N ngroups) % 8 == 0 (16-byte pieces
+// never straddle the end of the tensors) and NW RPW ngroups % 8 == 0.
+constexpr int kSzPre = 4;   // 16-byte (scale, zero) pieces per thread loaded ahead of the ring
+// word offset of the packed pairs in the block's LDS: after x pairs
+// [MT][XV][nchunk] (uint4), offsets [MT][nchunk] (float2) and the parked sums
+// [slots][MT] (float), rounded up to 16 bytes
+__host__ __device__ inline int gemv_sz_word_offset(int mt, int nchunk, int xv, int slots) {
+    return (mt * nchunk * xv * 4 + mt * nchunk * 2 + slots * mt + 3) & ~3;
+}
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT, int NW, int NL, bool SZL = false>
 __device__ __forceinline__ void gemv_body(const half_t* __restrict__ x, const uint32_t* __restrict__ qweight,
                                           const half_t* __restrict__ scales, const half_t* __restrict__ zeros,
                                           half_t* __restrict__ y, int N, int K, int log2g, int max_sets,
@@ -280,6 +313,8 @@ __device__ __forceinline__ void gemv_body(const half_t* __restrict__ x, const ui
     uint4* xp = smem;
     float2* xo = reinterpret_cast<float2*>(smem + MT * nchunk * XV);  // [MT][nchunk] (off, xs)
     float* yl = reinterpret_cast<float*>(xo + MT * nchunk);          // [NW][max_sets][RPW][MT]
+    // SZL: packed (s, z) words, 16-byte aligned after yl
+    uint32_t* szl = reinterpret_cast<uint32_t*>(smem) + gemv_sz_word_offset(MT, nchunk, XV, NW * max_sets * RPW);
 
     // wave index as a scalar: the buffer descriptors built from it must be
     // wave-uniform
@@ -347,11 +382,51 @@ __device__ __forceinline__ void gemv_body(const half_t* __restrict__ x, const ui
     for (int p = 0; p < XPRE; ++p)
         if (c0 + p * NW * 64 < nchunk) load_x(c0 + p * NW * 64, xr[p]);
 
+    // SZL: the block's (scale, zero) runs, 8 groups per 16-byte piece; the
+    // first kSzPre pieces per thread are in flight with the weights, offsets
+    // at or past the tensors' end read zero
+    [[maybe_unused]] const int sz_run = NW * RPW * ngroups;
+    [[maybe_unused]] const int sz_pieces = SZL ? max_sets * sz_run / 8 : 0;
+    [[maybe_unused]] const uint32_t sz_bytes = static_cast<uint32_t>(N) * static_cast<uint32_t>(ngroups) * 2u;
+    auto sz_offset = [&](int e) {
+        const int k = (8 * e) / sz_run;
+        const int off = 8 * e - k * sz_run;
+        const uint32_t row0 = static_cast<uint32_t>((blockIdx.x * NW + k * W) * RPW);
+        return e < sz_pieces && row0 < static_cast<uint32_t>(N)
+                   ? (row0 * static_cast<uint32_t>(ngroups) + static_cast<uint32_t>(off)) * 2u
+                   : sz_bytes;
+    };
+    auto sz_store = [&](int e, uint4 sv, uint4 zv) {
+        // word j = s_j | z_j << 16
+        uint4 lo, hi;
+        lo.x = __builtin_amdgcn_perm(zv.x, sv.x, 0x05040100u);
+        lo.y = __builtin_amdgcn_perm(zv.x, sv.x, 0x07060302u);
+        lo.z = __builtin_amdgcn_perm(zv.y, sv.y, 0x05040100u);
+        lo.w = __builtin_amdgcn_perm(zv.y, sv.y, 0x07060302u);
+        hi.x = __builtin_amdgcn_perm(zv.z, sv.z, 0x05040100u);
+        hi.y = __builtin_amdgcn_perm(zv.z, sv.z, 0x07060302u);
+        hi.z = __builtin_amdgcn_perm(zv.w, sv.w, 0x05040100u);
+        hi.w = __builtin_amdgcn_perm(zv.w, sv.w, 0x07060302u);
+        reinterpret_cast<uint4*>(szl)[2 * e] = lo;
+        reinterpret_cast<uint4*>(szl)[2 * e + 1] = hi;
+    };
+    [[maybe_unused]] const auto rs_sz = rsrc(scales, SZL ? static_cast<int>(sz_bytes) : 0);
+    [[maybe_unused]] const auto rz_sz = rsrc(zeros, SZL ? static_cast<int>(sz_bytes) : 0);
+    [[maybe_unused]] uint4 szv[SZL ? kSzPre : 1], zzv[SZL ? kSzPre : 1];
+    if constexpr (SZL) {
+#pragma unroll
+        for (int p = 0; p < kSzPre; ++p) {
+            const uint32_t o = sz_offset(static_cast<int>(threadIdx.x) + p * NW * 64);
+            szv[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_sz, o, 0, 0));
+            zzv[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rz_sz, o, 0, 0));
+        }
+    }
+
     WeightBatch<RPW, CPL> ring[DEPTH];
     int l_item = 0, l_set = 0, l_kb = 0;            // load cursor
     auto issue = [&](WeightBatch<RPW, CPL>& b) {
-        load_batch<BITS, RPW, CPL, NL>(b, qweight, scales, zeros, L, (wid + l_set * W) * RPW, l_item < n_items,
-                                            N, nchunk, ngroups, log2g, l_kb * 64 * CPL, lane);
+        load_batch<BITS, RPW, CPL, NL, SZL>(b, qweight, scales, zeros, L, (wid + l_set * W) * RPW,
+                                                 l_item < n_items, N, nchunk, ngroups, log2g, l_kb * 64 * CPL, lane);
         ++l_item;
         if (++l_kb == kbs) { l_kb = 0; ++l_set; }
     };
@@ -365,6 +440,18 @@ __device__ __forceinline__ void gemv_body(const half_t* __restrict__ x, const ui
     for (int c = c0 + XPRE * NW * 64; c < nchunk; c += NW * 64) {
         load_x(c, xr[0]);
         store_x(c, xr[0]);
+    }
+    if constexpr (SZL) {
+#pragma unroll
+        for (int p = 0; p < kSzPre; ++p) {
+            const int e = static_cast<int>(threadIdx.x) + p * NW * 64;
+            if (e < sz_pieces) sz_store(e, szv[p], zzv[p]);
+        }
+        for (int e = static_cast<int>(threadIdx.x) + kSzPre * NW * 64; e < sz_pieces; e += NW * 64) {
+            const uint32_t o = sz_offset(e);
+            sz_store(e, __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_sz, o, 0, 0)),
+                     __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rz_sz, o, 0, 0)));
+        }
     }
     __syncthreads();
 
@@ -392,7 +479,8 @@ __device__ __forceinline__ void gemv_body(const half_t* __restrict__ x, const ui
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             if (t + d < n_items) {
-                compute_batch<BITS>(ring[d], xp, xo, acc, nchunk, c_kb * 64 * CPL, lane, uk);
+                compute_batch<BITS, MT, RPW, CPL, SZL>(ring[d], xp, xo, acc, nchunk, c_kb * 64 * CPL, lane, uk,
+                                                       szl + (c_set * NW + wave) * RPW * ngroups, ngroups, log2g);
                 if (++c_kb == kbs) {
                     // row set finished: reduce; lane 63 stores the sums (one-shot)
                     // or parks them in LDS (streaming: no stores among the loads)
@@ -444,15 +532,15 @@ __device__ __forceinline__ void gemv_body(const half_t* __restrict__ x, const ui
 // Reading past them costs: a launch that also read the hidden grid-size
 // argument, on a second 64-byte line, took 4-9% longer on the one-shot
 // shapes (4096 x 4096: 4.06 -> 4.42 us).
-template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT, int NW>
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT, int NW, bool SZL = false>
 __global__ __launch_bounds__(NW * 64) void gemv_kernel(const half_t* __restrict__ x,
                                                    const uint32_t* __restrict__ qweight,
                                                    const half_t* __restrict__ scales,
                                                    const half_t* __restrict__ zeros,
                                                    half_t* __restrict__ y, int N, int K, int shape,
                                                    int nblocks) {
-    gemv_body<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, 0>(x, qweight, scales, zeros, y, N, K, shape & 0xFF,
-                                                          shape >> 8, nblocks, NoLayers{});
+    gemv_body<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, 0, SZL>(x, qweight, scales, zeros, y, N, K, shape & 0xFF,
+                                                               shape >> 8, nblocks, NoLayers{});
 }
 // The grouped form takes the weight pointers of up to four layers and the
 // first stacked rows of layers 1-3 as separate arguments: preloading covers
@@ -535,14 +623,33 @@ struct GemvTarget {
     LayersArg<NL> L;
 };
 
-template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT = false, int NW = 4, int NL = 0>
+// LDS of a streaming launch with its (scale, zero) pairs staged (SZL), or 0
+// when that form does not apply: single layer, whole 16-byte pieces of
+// pairs, 32-bit byte offsets, and one block per CU still fitting.
+template <int BITS, int MT, int RPW, int NW>
+size_t gemv_szl_lds_bytes(int64_t N, int64_t K, int log2g, int64_t blocks) {
+    const int64_t ngroups = K >> log2g;
+    const int64_t nchunk = K >> Chunk<BITS>::kShift;
+    if ((N * ngroups) % 8 != 0 || (NW * RPW * ngroups) % 8 != 0 || N * ngroups * 2 >= (int64_t{1} << 31)) return 0;
+    const int64_t sets = ceil_div(N, RPW);
+    const int64_t max_sets = ceil_div(sets, blocks * NW);
+    const int64_t words = gemv_sz_word_offset(MT, static_cast<int>(nchunk), Chunk<BITS>::kXV,
+                                              static_cast<int>(NW * max_sets * RPW)) +
+                          max_sets * NW * RPW * ngroups;
+    const size_t bytes = static_cast<size_t>(words) * 4;
+    return bytes <= static_cast<size_t>(max_shared_bytes()) ? bytes : 0;
+}
+
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, bool ONESHOT = false, int NW = 4, int NL = 0,
+          bool SZL = false>
 awq_status launch_t(const half_t* x, const GemvTarget<NL>& tg, int64_t N, int64_t K, int log2g,
                     int64_t blocks, hipStream_t stream) {
+    static_assert(!SZL || (!ONESHOT && NL == 0), "staged pairs: the single-layer streaming form");
     const void* kern;
     if constexpr (NL > 0)
         kern = reinterpret_cast<const void*>(&gemv_grouped_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, NL>);
     else
-        kern = reinterpret_cast<const void*>(&gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>);
+        kern = reinterpret_cast<const void*>(&gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, SZL>);
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, max_shared_bytes()) != hipSuccess)
@@ -555,7 +662,11 @@ awq_status launch_t(const half_t* x, const GemvTarget<NL>& tg, int64_t N, int64_
     const int64_t nchunk = K >> Chunk<BITS>::kShift;
     if (ONESHOT && max_sets * ceil_div(nchunk, 64 * CPL) > DEPTH) return AWQ_ERR_SHAPE;   // launch-shape bug
     if (max_sets >= (int64_t{1} << 23)) return AWQ_ERR_SHAPE;                              // packed with log2 G
-    const size_t lds = gemv_lds_bytes(MT, K, BITS) + (ONESHOT ? 0 : static_cast<size_t>(NW * max_sets * RPW * MT) * sizeof(float));
+    size_t lds = gemv_lds_bytes(MT, K, BITS) + (ONESHOT ? 0 : static_cast<size_t>(NW * max_sets * RPW * MT) * sizeof(float));
+    if constexpr (SZL) {
+        lds = gemv_szl_lds_bytes<BITS, MT, RPW, NW>(N, K, log2g, blocks);
+        if (lds == 0) return AWQ_ERR_SHAPE;   // launch-shape bug: the caller checks
+    }
     if (lds > static_cast<size_t>(max_shared_bytes())) return AWQ_ERR_SHAPE;
     if constexpr (NL > 0) {
         const GemvLayerTable& T = tg.L;
@@ -574,7 +685,7 @@ awq_status launch_t(const half_t* x, const GemvTarget<NL>& tg, int64_t N, int64_
                            T.q0, T.q1, T.q2, T.b1, T.b2, T.q3, T.b3, tail);
     }
     else
-        hipLaunchKernelGGL((gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW>), dim3(static_cast<unsigned>(blocks)),
+        hipLaunchKernelGGL((gemv_kernel<BITS, MT, RPW, CPL, DEPTH, ONESHOT, NW, SZL>), dim3(static_cast<unsigned>(blocks)),
                            dim3(NW * 64), lds, stream, x, tg.qweight, tg.scales, tg.zeros, tg.y, static_cast<int>(N),
                            static_cast<int>(K), log2g | static_cast<int>(max_sets << 8), static_cast<int>(blocks));
     return last_launch_status();
@@ -624,9 +735,25 @@ awq_status launch_m(const half_t* x, const GemvTarget<NL>& tg, int64_t N, int64_
     }
     const int64_t x_lds = static_cast<int64_t>(gemv_lds_bytes(MT, K, BITS));
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kGemvBlocksPerCu, max_shared_bytes() / (x_lds + 2048)));
-    if (MT >= 2 || kbs > 3)
-        return launch_t<BITS, MT, 2, 2, 2, false, 8, NL>(x, tg, N, K, log2g, per_cu * cu_count(), stream);
-    return launch_t<BITS, MT, 1, 2, 2, false, 8, NL>(x, tg, N, K, log2g, per_cu * cu_count(), stream);
+    const int64_t blocks = per_cu * cu_count();
+    // Staged (scale, zero) pairs (SZL) at M = 2, and at M = 1 on rows of 5
+    // items and more. Measured against per-chunk pairs (us, graph-timed,
+    // weights rotated, one process; outputs bit-identical): M = 2 4096 x 11008
+    // 9.37 -> 8.95, 8192 x 28672 27.26 -> 26.59; M = 1 8192 x 28672 23.76 ->
+    // 23.43 (G = 64: 24.88 -> 24.53). Shorter rows at M = 1 lose to the
+    // staging ahead of the first item: 4096 x 11008 6.69 -> 6.85, 13824 x
+    // 5120 10.68 -> 10.83, 11008 x 8192 10.29 -> 10.45.
+    const bool szl = NL == 0 && MT <= 2 && per_cu == 1 && (MT == 2 || kbs >= 5);
+    if (MT >= 2 || kbs > 3) {
+        if constexpr (NL == 0 && MT <= 2)
+            if (szl && gemv_szl_lds_bytes<BITS, MT, 2, 8>(N, K, log2g, blocks) != 0)
+                return launch_t<BITS, MT, 2, 2, 2, false, 8, NL, true>(x, tg, N, K, log2g, blocks, stream);
+        return launch_t<BITS, MT, 2, 2, 2, false, 8, NL>(x, tg, N, K, log2g, blocks, stream);
+    }
+    if constexpr (NL == 0 && MT <= 2)
+        if (szl && gemv_szl_lds_bytes<BITS, MT, 1, 8>(N, K, log2g, blocks) != 0)
+            return launch_t<BITS, MT, 1, 2, 2, false, 8, NL, true>(x, tg, N, K, log2g, blocks, stream);
+    return launch_t<BITS, MT, 1, 2, 2, false, 8, NL>(x, tg, N, K, log2g, blocks, stream);
 }
 
 }  // namespace
