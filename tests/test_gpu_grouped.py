@@ -141,3 +141,67 @@ def test_batches_past_the_column_tiles_run_per_layer(M):
     for q, g, s in zip(qs, got, singles):
         assert np.array_equal(g.view(np.uint16), s.view(np.uint16))
         assert_linear_close(g, oracle.linear_ref(x, *q, G))
+
+
+
+def _carve(buf, off, arr, dtype):
+    """A view of `buf` at byte offset `off` holding a copy of arr."""
+    a = np.ascontiguousarray(arr)
+    t = buf[off:off + a.nbytes].view(dtype).view(a.shape)
+    t.copy_(torch.from_numpy(a).view(dtype))
+    return t
+
+
+def _place(x, qs, gap):
+    """x and each layer's (qweight, scales, zeros) carved from one buffer,
+    layer j starting at byte j * gap (gap 0: packed one after another)."""
+    step = lambda n: (n + 255) // 256 * 256
+    sizes = [sum(step(a.nbytes) for a in q) for q in qs]
+    total = step(x.nbytes) + sum(max(gap, sz) for sz in sizes) + 256
+    buf = torch.empty(total, dtype=torch.uint8, device="cuda")
+    xd = _carve(buf, 0, x, torch.float16)
+    off, layers = step(x.nbytes), []
+    for q, sz in zip(qs, sizes):
+        o = off
+        qw = _carve(buf, o, q[0].view(np.int32), torch.int32)
+        o += step(q[0].nbytes)
+        sc = _carve(buf, o, q[1], torch.float16)
+        o += step(q[1].nbytes)
+        zr = _carve(buf, o, q[2], torch.float16)
+        layers.append((qw, sc, zr))
+        off += max(gap, sz)
+    return buf, xd, layers
+
+
+def _span(ts):
+    ptrs = [t.data_ptr() for t in ts]
+    return max(ptrs) - min(ptrs)
+
+
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("Ns", [(4096, 4096, 4096), (11008, 11008)], ids=["qkv", "gate_up"])
+def test_grouped_both_argument_forms(Ns, M):
+    """One-shot grouped launches pass every early pointer as a 32-bit offset
+    from the lowest when x and all layers' weights, scales and zero-points
+    lie within 4 GB of it, and as full pointers otherwise. The same layers
+    placed both ways (carved from one buffer, packed or 4.5 GiB apart) give
+    the same bits, equal to each layer's own awq_gemm."""
+    K, G = 4096, 128
+    x, qs = layers_of(Ns, K, M, G, 5)
+    results = []
+    for gap in (0, 4608 << 20):
+        buf, xd, layers = _place(x, qs, gap)
+        span = _span([xd] + [t for d in layers for t in d])
+        say("grouped argument forms: gap", gap, "span", span)
+        assert (span < (1 << 32)) == (gap == 0)
+        outs = [torch.empty((M, N), dtype=torch.float16, device="cuda") for N in Ns]
+        awq.awq_gemm_grouped(xd, layers, G, outs=outs)
+        singles = [awq.awq_gemm(xd, *d, G) for d in layers]
+        torch.cuda.synchronize()
+        results.append(([host(o) for o in outs], [host(t) for t in singles]))
+        del buf, xd, layers
+    for j, q in enumerate(qs):
+        near, far, single = results[0][0][j], results[1][0][j], results[0][1][j]
+        assert np.array_equal(near.view(np.uint16), single.view(np.uint16))
+        assert np.array_equal(far.view(np.uint16), single.view(np.uint16))
+        assert_linear_close(near, oracle.linear_ref(x, *q, G))

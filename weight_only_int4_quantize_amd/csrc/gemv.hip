@@ -570,6 +570,42 @@ __global__ __launch_bounds__(NW * 64) void gemv_grouped_kernel(const half_t* __r
                                                            shape >> 8, nblocks, L);
 }
 
+// One-shot grouped launches of 2 or 3 layers whose tensors (x, and each
+// layer's packed weights, scales and zero-points) all lie within 4 GB of the
+// lowest of them: every pointer the waves need before their first dot is a
+// 32-bit byte offset from that base, and with the sizes packed in two dwords
+// the whole set fits in the 14 preloaded argument dwords. No wave then waits
+// on a kernel-argument load until its outputs are stored (the output
+// pointers follow as an aggregate). nb1 = N | b1 << 16, b2k = b2 |
+// (K / 32) << 16 | (log2 G - 5) << 28 (N < 65536, K / 32 < 4096). The one-
+// shot launch shape gives every wave at most one row set, so the grid size
+// follows from N.
+template <int NL>
+struct GemvOutTail {
+    half_t* y[NL];
+};
+template <int BITS, int MT, int RPW, int CPL, int DEPTH, int NW, int NL>
+__global__ __launch_bounds__(NW * 64) void gemv_grouped_packed_kernel(
+    const char* base, uint32_t ox, uint32_t oq0, uint32_t oq1, uint32_t oq2, uint32_t os0, uint32_t os1,
+    uint32_t os2, uint32_t oz0, uint32_t oz1, uint32_t oz2, uint32_t nb1, uint32_t b2k, GemvOutTail<NL> tail) {
+    static_assert(NL == 2 || NL == 3, "two or three layers");
+    const int N = static_cast<int>(nb1 & 0xFFFFu);
+    const int K = static_cast<int>((b2k >> 16) & 0xFFFu) * 32;
+    const int log2g = static_cast<int>(b2k >> 28) + 5;
+    const int nblocks = ((N + RPW - 1) / RPW + NW - 1) / NW;
+    const GemvLayerTable L{reinterpret_cast<const uint32_t*>(base + oq0), reinterpret_cast<const uint32_t*>(base + oq1),
+                           NL > 2 ? reinterpret_cast<const uint32_t*>(base + oq2) : nullptr, nullptr,
+                           reinterpret_cast<const half_t*>(base + os0), reinterpret_cast<const half_t*>(base + os1),
+                           NL > 2 ? reinterpret_cast<const half_t*>(base + os2) : nullptr, nullptr,
+                           reinterpret_cast<const half_t*>(base + oz0), reinterpret_cast<const half_t*>(base + oz1),
+                           NL > 2 ? reinterpret_cast<const half_t*>(base + oz2) : nullptr, nullptr,
+                           tail.y[0], tail.y[1], NL > 2 ? tail.y[NL > 2 ? 2 : 0] : nullptr, nullptr,
+                           static_cast<int>(nb1 >> 16), NL > 2 ? static_cast<int>(b2k & 0xFFFFu) : INT32_MAX,
+                           INT32_MAX};
+    gemv_body<BITS, MT, RPW, CPL, DEPTH, true, NW, NL>(reinterpret_cast<const half_t*>(base + ox), nullptr, nullptr,
+                                                        nullptr, nullptr, N, K, log2g, 1, nblocks, L);
+}
+
 }  // namespace
 
 // INT4 rows of 2-4 items (4096 < K <= 16384) at M <= 4, with every row within
@@ -670,6 +706,45 @@ awq_status launch_t(const half_t* x, const GemvTarget<NL>& tg, int64_t N, int64_
     if (lds > static_cast<size_t>(max_shared_bytes())) return AWQ_ERR_SHAPE;
     if constexpr (NL > 0) {
         const GemvLayerTable& T = tg.L;
+        if constexpr (ONESHOT && (NL == 2 || NL == 3)) {
+            // the packed-offset entry when every early pointer is within 4 GB
+            // of the lowest and the sizes fit their fields
+            const void* ptrs[10] = {x, T.q0, T.q1, T.s0, T.s1, T.z0, T.z1, NL > 2 ? T.q2 : T.q0,
+                                    NL > 2 ? T.s2 : T.s0, NL > 2 ? T.z2 : T.z0};
+            uintptr_t lo = UINTPTR_MAX, hi = 0;
+            for (const void* p : ptrs) {
+                lo = std::min(lo, reinterpret_cast<uintptr_t>(p));
+                hi = std::max(hi, reinterpret_cast<uintptr_t>(p));
+            }
+            const int64_t nsets = ceil_div(N, RPW);
+            if (hi - lo < (uintptr_t{1} << 32) && N < 65536 && (K >> 5) < 4096 && log2g >= 5 && log2g < 21 &&
+                blocks == ceil_div(nsets, NW) && max_sets == 1) {
+                const char* base = reinterpret_cast<const char*>(lo);
+                auto off = [&](const void* p) {
+                    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) - lo);
+                };
+                static bool packed_attr_set = false;
+                if (!packed_attr_set) {
+                    if (hipFuncSetAttribute(
+                            reinterpret_cast<const void*>(&gemv_grouped_packed_kernel<BITS, MT, RPW, CPL, DEPTH, NW, NL>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, max_shared_bytes()) != hipSuccess)
+                        return AWQ_ERR_HIP;
+                    packed_attr_set = true;
+                }
+                GemvOutTail<NL> ytail;
+                ytail.y[0] = T.y0;
+                ytail.y[1] = T.y1;
+                if constexpr (NL > 2) ytail.y[2] = T.y2;
+                const uint32_t nb1 = static_cast<uint32_t>(N) | (static_cast<uint32_t>(T.b1) << 16);
+                const uint32_t b2k = (NL > 2 ? static_cast<uint32_t>(T.b2) : 0u) |
+                                     (static_cast<uint32_t>(K >> 5) << 16) | (static_cast<uint32_t>(log2g - 5) << 28);
+                hipLaunchKernelGGL((gemv_grouped_packed_kernel<BITS, MT, RPW, CPL, DEPTH, NW, NL>),
+                                   dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), lds, stream, base, off(x),
+                                   off(T.q0), off(T.q1), off(ptrs[7]), off(T.s0), off(T.s1), off(ptrs[8]), off(T.z0),
+                                   off(T.z1), off(ptrs[9]), nb1, b2k, ytail);
+                return last_launch_status();
+            }
+        }
         GemvLayerTail<NL> tail;
         const half_t* sc[4] = {T.s0, T.s1, T.s2, T.s3};
         const half_t* zr[4] = {T.z0, T.z1, T.z2, T.z3};
