@@ -205,3 +205,26 @@ def test_grouped_both_argument_forms(Ns, M):
         assert np.array_equal(near.view(np.uint16), single.view(np.uint16))
         assert np.array_equal(far.view(np.uint16), single.view(np.uint16))
         assert_linear_close(near, oracle.linear_ref(x, *q, G))
+
+
+@pytest.mark.parametrize("M", [4, 16])
+@pytest.mark.parametrize("Ns", [(4096, 4096, 4096), (11008, 11008)], ids=["qkv", "gate_up"])
+def test_grouped_column_tiles_both_argument_forms(Ns, M):
+    """The grouped column-tile launch (3 <= M <= 32) has the same two
+    argument forms: 32-bit offsets from the lowest tensor when a launch's
+    tensors lie within 4 GB, full pointers otherwise. The same layers placed
+    both ways give the same bits, and each layer meets the linear bar."""
+    K, G = 4096, 128
+    x, qs = layers_of(Ns, K, M, G, 6)
+    results = []
+    for gap in (0, 4608 << 20):
+        buf, xd, layers = _place(x, qs, gap)
+        assert (_span([xd] + [t for d in layers for t in d]) < (1 << 32)) == (gap == 0)
+        outs = [torch.empty((M, N), dtype=torch.float16, device="cuda") for N in Ns]
+        awq.awq_gemm_grouped(xd, layers, G, outs=outs)
+        torch.cuda.synchronize()
+        results.append([host(o) for o in outs])
+        del buf, xd, layers
+    for j, q in enumerate(qs):
+        assert np.array_equal(results[0][j].view(np.uint16), results[1][j].view(np.uint16))
+        assert_linear_close(results[0][j], oracle.linear_ref(x, *q, G))

@@ -351,6 +351,45 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ct_wave
     coltile_body<XR, WPL, NW, DEPTH, CT>(x, q, sc, zr, y, M, n, K, b - f);
 }
 
+// Two or three layers whose tensors (x, and each layer's packed weights,
+// scales and zero-points) lie within 4 GB of the lowest of them: those ten
+// pointers go as 32-bit byte offsets from that base and the sizes in two
+// dwords (mk = M | (K / 32) << 6 | n2 << 18, n01 = n0 | n1 << 16; M <= 32,
+// K / 32 < 4096, n2 < 16384, n0 and n1 < 65536), so every argument a wave
+// needs before its stores is in the 14 preloaded argument dwords; the
+// output pointers follow as an aggregate. A layer's first block follows
+// from the row counts, as the host computes it.
+template <int NL>
+struct CtOutTail {
+    half_t* y[NL];
+};
+template <int XR, int WPL, int NW, int DEPTH, int CT, int NL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ct_waves_per_eu(XR, WPL, CT, NW)))) void coltile_grouped_packed_kernel(
+    const char* base, uint32_t ox, uint32_t oq0, uint32_t oq1, uint32_t oq2, uint32_t os0, uint32_t os1, uint32_t os2,
+    uint32_t oz0, uint32_t oz1, uint32_t oz2, uint32_t mk, uint32_t n01, CtOutTail<NL> tail) {
+    static_assert(NL == 2 || NL == 3, "two or three layers");
+    constexpr int COLS = kCtCols * CT;
+    const int M = static_cast<int>(mk & 63u);
+    const int K = static_cast<int>((mk >> 6) & 0xFFFu) * 32;
+    const int n0 = static_cast<int>(n01 & 0xFFFFu), n1 = static_cast<int>(n01 >> 16);
+    const int n2 = static_cast<int>(mk >> 18);
+    const int f1 = (n0 + COLS - 1) / COLS;
+    const int f2 = f1 + (n1 + COLS - 1) / COLS;
+    const int b = blockIdx.x;
+    const bool in1 = b >= f1;
+    const bool in2 = NL > 2 && b >= f2;
+    const uint32_t oq = in2 ? oq2 : in1 ? oq1 : oq0;
+    const uint32_t os = in2 ? os2 : in1 ? os1 : os0;
+    const uint32_t oz = in2 ? oz2 : in1 ? oz1 : oz0;
+    half_t* y = in2 ? tail.y[NL > 2 ? 2 : 0] : in1 ? tail.y[1] : tail.y[0];
+    const int n = in2 ? n2 : in1 ? n1 : n0;
+    const int f = in2 ? f2 : in1 ? f1 : 0;
+    coltile_body<XR, WPL, NW, DEPTH, CT>(reinterpret_cast<const half_t*>(base + ox),
+                                         reinterpret_cast<const uint32_t*>(base + oq),
+                                         reinterpret_cast<const half_t*>(base + os),
+                                         reinterpret_cast<const half_t*>(base + oz), y, M, n, K, b - f);
+}
+
 // rows of x a launch stages: M rounded up to 4, 8, 16 or 32
 int ct_rows(int64_t M) { return M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : 32; }
 // largest tile count an instance takes without spilling
@@ -478,6 +517,57 @@ awq_status launch_ct(const half_t* x, const CtTarget& tg, int M, int N, int K, h
         hipLaunchKernelGGL((coltile_kernel<XR, WPL, NW, DEPTH, CT>), dim3(static_cast<unsigned>(blocks)),
                            dim3(NW * 64), lds, stream, x, tg.qweight, tg.scales, tg.zeros, tg.y, M, N, K);
         return last_launch_status();
+    }
+    const GemvLayers& lys = *tg.layers;
+    if (lys.n == 2 || lys.n == 3) {
+        // the packed-offset entry when every early pointer is within 4 GB of
+        // the lowest and the sizes fit their fields
+        const void* ptrs[10] = {x, lys.qweight[0], lys.qweight[1], lys.scales[0], lys.scales[1], lys.zeros[0],
+                                lys.zeros[1], lys.n > 2 ? lys.qweight[2] : lys.qweight[0],
+                                lys.n > 2 ? lys.scales[2] : lys.scales[0], lys.n > 2 ? lys.zeros[2] : lys.zeros[0]};
+        uintptr_t lo = UINTPTR_MAX, hi = 0;
+        for (const void* p : ptrs) {
+            lo = std::min(lo, reinterpret_cast<uintptr_t>(p));
+            hi = std::max(hi, reinterpret_cast<uintptr_t>(p));
+        }
+        const int rows0 = lys.row0[1] - lys.row0[0], rows1 = lys.row0[2] - lys.row0[1];
+        const int rows2 = lys.n > 2 ? lys.row0[3] - lys.row0[2] : 0;
+        if (hi - lo < (uintptr_t{1} << 32) && M <= 32 && (K >> 5) < 4096 && rows0 < 65536 && rows1 < 65536 &&
+            rows2 < 16384) {
+            auto off = [&](const void* p) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) - lo); };
+            const uint32_t mk = static_cast<uint32_t>(M) | (static_cast<uint32_t>(K >> 5) << 6) |
+                                (static_cast<uint32_t>(rows2) << 18);
+            const uint32_t n01 = static_cast<uint32_t>(rows0) | (static_cast<uint32_t>(rows1) << 16);
+            const int64_t blocks = ceil_div(rows0, COLS) + ceil_div(rows1, COLS) + ceil_div(rows2, COLS);
+            if (lys.n == 3) {
+                static bool attr3 = false;
+                if (!attr3) {
+                    const awq_status st = ct_allow_lds(&coltile_grouped_packed_kernel<XR, WPL, NW, DEPTH, CT, 3>);
+                    if (st != AWQ_OK) return st;
+                    attr3 = true;
+                }
+                CtOutTail<3> yt{{lys.y[0], lys.y[1], lys.y[2]}};
+                hipLaunchKernelGGL((coltile_grouped_packed_kernel<XR, WPL, NW, DEPTH, CT, 3>),
+                                   dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), lds, stream,
+                                   reinterpret_cast<const char*>(lo), off(x), off(ptrs[1]), off(ptrs[2]),
+                                   off(ptrs[7]), off(ptrs[3]), off(ptrs[4]), off(ptrs[8]), off(ptrs[5]),
+                                   off(ptrs[6]), off(ptrs[9]), mk, n01, yt);
+            } else {
+                static bool attr2 = false;
+                if (!attr2) {
+                    const awq_status st = ct_allow_lds(&coltile_grouped_packed_kernel<XR, WPL, NW, DEPTH, CT, 2>);
+                    if (st != AWQ_OK) return st;
+                    attr2 = true;
+                }
+                CtOutTail<2> yt{{lys.y[0], lys.y[1]}};
+                hipLaunchKernelGGL((coltile_grouped_packed_kernel<XR, WPL, NW, DEPTH, CT, 2>),
+                                   dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), lds, stream,
+                                   reinterpret_cast<const char*>(lo), off(x), off(ptrs[1]), off(ptrs[2]),
+                                   off(ptrs[7]), off(ptrs[3]), off(ptrs[4]), off(ptrs[8]), off(ptrs[5]),
+                                   off(ptrs[6]), off(ptrs[9]), mk, n01, yt);
+            }
+            return last_launch_status();
+        }
     }
     static bool attr_set_grouped = false;
     if (!attr_set_grouped) {
