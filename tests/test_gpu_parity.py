@@ -6,10 +6,12 @@ over every output of the prefill products; where the oracle samples output
 columns (the larger sweep), every 128-column block contributes one. Scale
 search: the same alpha as the oracle, unless the oracle's two lowest losses
 lie within 1e-6 relative of each other (then either of them); the losses
-within 1e-4 of the exact oracle and within 2e-6 of the oracle's loss with
-X / s rounded to fp16 as the W4A16 layer takes it. Inputs come from the
-seeded generators; expected values come only from the oracle (or from
-golden files written by a script that calls only the oracle).
+within 1e-4 of the exact oracle (or, where the oracle's fp16-activation form
+is computed, within its shift from the exact loss plus 2e-6) and within 2e-6
+of the oracle's loss with X / s rounded to fp16 as the W4A16 layer takes it.
+Inputs come from the seeded generators; expected values come only from the
+oracle (or from golden files written by a script that calls only the
+oracle).
 """
 
 import base64
@@ -39,7 +41,8 @@ ELEM = 1e-2
 NEAR_TIE = 1e-6
 # Losses against the exact oracle: the W4A16 product takes X / s rounded to
 # fp16, which the oracle's own fp16-activation form shows moves the loss by
-# at most ~5e-5 relative on the small cases (1.1e-5 at full size).
+# up to ~1.8e-4 relative on the small cases (1.1e-5 at full size); where that
+# form is computed the bar is its shift plus LOSS_RTOL_F16, else this.
 LOSS_RTOL_EXACT = 1e-4
 # Losses against the oracle's fp16-activation form (and the losses of the
 # salient ablation, where no activation is rescaled): only the fp32
@@ -460,6 +463,18 @@ def test_scale_search_small_interior_minimum():
     check_search(losses, best, host(s), losses_o, best_o, s_o, losses_f)
 
 
+def test_scale_search_ragged_rows():
+    """N = 300 is not a whole number of 32-row groups: the search's packed
+    words in the loss GEMM's tiled order end in a partial group."""
+    lay = synth.make_layer(300, 1024, 384, seed=[110], w_std=0.02)
+    w, x = lay["w"], lay["x"]
+    losses_o, best_o, s_o = oracle.scale_search(w, x, 64)
+    losses_f, _, _ = oracle.scale_search(w, x, 64, f16_activations=True)
+    losses, best, s = awq.awq_scale_search(dev(w), dev(x), 64)
+    say("search ragged rows: gpu", best, "oracle", best_o)
+    check_search(losses, best, host(s), losses_o, best_o, s_o, losses_f)
+
+
 def check_choice(losses, best, losses_o, best_o, losses_f16=None):
     """Losses within LOSS_RTOL_EXACT of the exact oracle (and LOSS_RTOL_F16
     of its fp16-activation form, when given); the same index as the oracle
@@ -469,7 +484,14 @@ def check_choice(losses, best, losses_o, best_o, losses_f16=None):
     losses_o = np.asarray(losses_o, np.float64)
     rel = np.abs(losses - losses_o) / losses_o
     say("loss deviation from the oracle", float(rel.max()))
-    assert np.all(rel <= LOSS_RTOL_EXACT), f"loss deviation {rel.max():.2e}"
+    bar = np.full_like(losses_o, LOSS_RTOL_EXACT)
+    if losses_f16 is not None:
+        # the fp16 rounding of X / s moves each loss by what the oracle's own
+        # fp16-activation form shows; the bar against the exact loss is at
+        # least that shift plus the fp32 level
+        shift = np.abs(np.asarray(losses_f16, np.float64) - losses_o) / losses_o
+        bar = np.maximum(bar, shift + LOSS_RTOL_F16)
+    assert np.all(rel <= bar), f"loss deviation {rel.max():.2e}"
     if losses_f16 is not None:
         rel16 = np.abs(losses - losses_f16) / losses_f16
         say("loss deviation from the fp16-activation oracle", float(rel16.max()))

@@ -56,7 +56,7 @@ struct SearchLayout {
         m = c.take<double>(K);
         abs_partials = c.take<double>(absmean_workspace_bytes(T, K) / sizeof(double));
         s = c.take<float>(K);
-        qweight = c.take<uint32_t>(static_cast<size_t>(N) * (K / 8));
+        qweight = c.take<uint32_t>(tiled_qweight_words(N, K));   // tiled order or row-major
         scales = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         xs = c.take<half_t>(static_cast<size_t>(T) * K);
@@ -113,7 +113,7 @@ struct ClipLayout {
 
     ClipLayout(void* base, int64_t N, int64_t K, int64_t T, int G, int n, bool scaled) {
         Carve c(base);
-        qweight = c.take<uint32_t>(static_cast<size_t>(N) * (K / 8));
+        qweight = c.take<uint32_t>(tiled_qweight_words(N, K));   // tiled order or row-major
         scales = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         if (scaled) xs = c.take<half_t>(static_cast<size_t>(T) * K);
@@ -140,9 +140,10 @@ awq_status reference_output(const half_t* x, const half_t* w, int64_t T, int64_t
 }
 
 // loss_out = || x' . dequant(Wq)^T - yref ||_F^2 (fused epilogue + fixed-order sum)
+// tiled: qw holds the words in the tiled order (GemmArgs::b_tiled)
 awq_status output_loss(const half_t* xa, const uint32_t* qw, const half_t* sc, const half_t* zr, int64_t T,
                        int64_t N, int64_t K, int G, const float* yref, double* partials, double* loss_out,
-                       hipStream_t s) {
+                       hipStream_t s, bool tiled = false) {
     GemmArgs q;
     q.a = xa;
     q.qweight = qw;
@@ -154,6 +155,7 @@ awq_status output_loss(const half_t* xa, const uint32_t* qw, const half_t* sc, c
     q.K = K;
     q.yref = yref;
     q.partials = partials;
+    q.b_tiled = tiled;
     awq_status st = launch_gemm(q, GemmB::kInt4, GemmOut::kLoss, s);
     if (st != AWQ_OK) return st;
     return launch_sum_partials(partials, gemm_tile_count(T, N), loss_out, s);
@@ -469,18 +471,21 @@ awq_status awq_scale_search(const void* w_f16, const void* x_f16, int64_t N, int
     const half_t* w = static_cast<const half_t*>(w_f16);
     const half_t* x = static_cast<const half_t*>(x_f16);
 
+    // the loss GEMM reads the quantized words in the tiled order where its
+    // direct form runs (one contiguous 1 KB piece per wave and K step)
+    const bool tiled = gemm_tiled_ok(K, group_size);
     // m = mean |x| per input channel
     if ((st = launch_absmean(x, T, K, L.m, L.abs_partials, s)) != AWQ_OK) return st;
     // reference output W . x^T, once, in fp32
     if ((st = reference_output(x, w, T, N, K, group_size, L.yref, s)) != AWQ_OK) return st;
     for (int i = 0; i < n_alpha; ++i) {
         if ((st = launch_pow_scales(L.m, K, grid[i], L.s, s)) != AWQ_OK) return st;
-        if ((st = launch_quantize(w, L.s, N, K, group_size, false, 0.0, L.qweight, L.scales, L.zeros, s)) !=
-            AWQ_OK)
+        if ((st = launch_quantize(w, L.s, N, K, group_size, false, 0.0, L.qweight, L.scales, L.zeros, s, 4,
+                                  tiled)) != AWQ_OK)
             return st;
         if ((st = launch_divide_columns(x, L.s, T, K, L.xs, s)) != AWQ_OK) return st;
         if ((st = output_loss(L.xs, L.qweight, L.scales, L.zeros, T, N, K, group_size, L.yref, L.tile_partials,
-                              L.losses + i, s)) != AWQ_OK)
+                              L.losses + i, s, tiled)) != AWQ_OK)
             return st;
     }
     if (hipMemcpyAsync(losses, L.losses, sizeof(double) * n_alpha, hipMemcpyDeviceToHost, s) != hipSuccess)
@@ -528,12 +533,13 @@ awq_status awq_clip_search(const void* w_f16, const void* x_f16, const float* ch
         if ((st = launch_divide_columns(x, channel_scale, T, K, L.xs, s)) != AWQ_OK) return st;
         xa = L.xs;
     }
+    const bool tiled = gemm_tiled_ok(K, group_size);   // as in the scale search
     for (int i = 0; i < n_fractions; ++i) {
         if ((st = launch_quantize(w, channel_scale, N, K, group_size, mode == AWQ_QUANT_SYMMETRIC, fractions[i],
-                                  L.qweight, L.scales, L.zeros, s)) != AWQ_OK)
+                                  L.qweight, L.scales, L.zeros, s, 4, tiled)) != AWQ_OK)
             return st;
         if ((st = output_loss(xa, L.qweight, L.scales, L.zeros, T, N, K, group_size, L.yref, L.tile_partials,
-                              L.losses + i, s)) != AWQ_OK)
+                              L.losses + i, s, tiled)) != AWQ_OK)
             return st;
     }
     if (hipMemcpyAsync(losses, L.losses, sizeof(double) * n_fractions, hipMemcpyDeviceToHost, s) != hipSuccess)

@@ -48,10 +48,12 @@ inline awq_status last_launch_status() { return hip_status(hipGetLastError()); }
 // asymmetric (the group's [min, max]) or symmetric (max |w| -> +-7, zero 8),
 // after an optional percentile clip of each group (clip_fraction in [0, 0.25)).
 bool clip_fraction_ok(double p);
-// bits = 8 gives the W8A16 form (4 codes per word, 255 levels).
+// bits = 8 gives the W8A16 form (4 codes per word, 255 levels). tiled (INT4,
+// K a multiple of 64): the packed words in the searches' loss-GEMM order
+// (kTiledB below) instead of row-major [N, K/8].
 awq_status launch_quantize(const half_t* w, const float* channel_scale, int64_t N, int64_t K,
                            int group_size, bool symmetric, double clip_fraction, uint32_t* qweight,
-                           half_t* scales, half_t* zeros, hipStream_t stream, int bits = 4);
+                           half_t* scales, half_t* zeros, hipStream_t stream, int bits = 4, bool tiled = false);
 
 // Decode GEMV y[M, N] = x[M, K] . dequant(Wq)^T for M <= kGemvMaxM.
 constexpr int kGemvMaxM = 8;
@@ -120,7 +122,18 @@ struct GemmArgs {
     float* y32 = nullptr;             // kF32 output [M, N], tiled (ref_offset)
     const float* yref = nullptr;      // kLoss reference [M, N], tiled (ref_offset)
     double* partials = nullptr;       // kLoss: one double per tile
+    // kLoss with INT4 B: qweight in the tiled order (word c of row n at
+    // ((n / 32 * K / 64 + c / 8) * 64 + (c / 4 % 2) * 32 + n % 32) * 4 + c % 4,
+    // ceil(N / 32) * 32 rows), so a wave's packed words of one 64-k step
+    // are one contiguous 1 KB piece
+    bool b_tiled = false;
 };
+// whether the loss form takes tiled B at this K and group size
+bool gemm_tiled_ok(int64_t K, int group_size);
+// words of a tiled packed-weight buffer of N rows
+inline size_t tiled_qweight_words(int64_t N, int64_t K) {
+    return static_cast<size_t>((N + 31) / 32 * 32) * static_cast<size_t>(K / 8);
+}
 // Workspaces of the split kernels (GEMM stream-K, skinny K splits) start
 // with one shared region of tile counters: the counters of any call sit at
 // offset 0 and are back at zero when its kernel ends, so one workspace

@@ -230,8 +230,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* p, int byt
 // dequantizes them there; only A goes through LDS.
 //
 // WGM: waves along M (the 4 waves form WGM x 4 / WGM).
+// TILEDB (INT4, the direct form's one-column-tile waves): B in the tiled
+// order of GemmArgs::b_tiled, so each wave's load of a K step is one
+// contiguous 1 KB piece (8 cache lines against 32 for the row-major words).
 template <int BM, int BN, GemmB BMODE, GemmOut OMODE, bool STREAMK, bool DIRECT, int WGM = 2, int NT = kThreads,
-          bool SKDMA = false>
+          bool SKDMA = false, bool TILEDB = false>
 __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int tiles_n, StreamK sk) {
     constexpr int WGN = NT / kWave / WGM;
     constexpr int WTM = BM / WGM;               // wave tile rows
@@ -253,6 +256,7 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
     static_assert(DIRECT || !INT4 || B_WORDS == 2, "int4 B staging: 2 words (16 codes) per thread");
     static_assert(DIRECT || INT4 || B_VECS >= 1, "fp16 B staging");
     static_assert(DIRECT || BMODE != GemmB::kInt8, "W8 B runs the direct form only");
+    static_assert(!TILEDB || (DIRECT && BMODE == GemmB::kInt4 && TN == 1 && WTN == 32), "tiled B: INT4, 32-column waves");
     constexpr int LDS_A = DIRECT ? BM * BKD : BM * LDK;
     constexpr int LDS_B = DIRECT ? 8 : BN * LDK;
 
@@ -425,9 +429,11 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
         const auto a_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(args.a) + static_cast<int64_t>(tm) * K,
                                                             0, rows_a * K * 2, 0x00020000);
         const char* b_src = QB ? reinterpret_cast<const char*>(args.qweight) : reinterpret_cast<const char*>(args.w);
+        // tiled B: the tile's 32-column groups, whole (rows past N are
+        // allocated and never stored from)
         const auto b_rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char*>(b_src) + static_cast<int64_t>(tn) * (K * BITS / 8), 0, cols_b * (K * BITS / 8),
-            0x00020000);
+            const_cast<char*>(b_src) + static_cast<int64_t>(tn) * (K * BITS / 8), 0,
+            (TILEDB ? (cols_b + 31) / 32 * 32 : cols_b) * (K * BITS / 8), 0x00020000);
         const auto s_rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<half_t*>(args.scales) + static_cast<int64_t>(tn) * ngroups, 0, cols_b * ngroups * 2, 0x00020000);
         const auto z_rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -445,7 +451,8 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int n = min(wn + j * 32 + lcol, cols_b - 1);
-            b_off[j] = n * (K * BITS / 8) + lh * (4 * BITS);
+            // tiled: piece (group (wn + 32 j) / 32, step 0), lane's 16 bytes
+            b_off[j] = TILEDB ? (wn + j * 32) / 32 * nk * 1024 + lane * 16 : n * (K * BITS / 8) + lh * (4 * BITS);
             sz_off[j] = n * ngroups * 2;
         }
         auto s_bits_at = [&](int j, int gg) {
@@ -475,7 +482,7 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
             for (int i = 0; i < AV; ++i) areg[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off[i], k0, 0);
         };
         auto load_b = [&](u32x4 (&dst)[TN][BW], int kt) {
-            const int w0 = uniform(min(kt, last) * (BKD * BITS / 8));
+            const int w0 = uniform(min(kt, last) * (TILEDB ? 1024 : BKD * BITS / 8));
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -883,6 +890,15 @@ size_t partials_bytes() {
 
 template <const Geometry& GEO, GemmB BMODE, GemmOut OMODE, bool DIRECT, int WGM = 2>
 void launch_cfg(const GemmArgs& args, void* workspace, hipStream_t stream) {
+    if constexpr (OMODE == GemmOut::kLoss && DIRECT && BMODE == GemmB::kInt4 && GEO.bn == 128) {
+        if (args.b_tiled) {
+            const int64_t tn = ceil_div(args.N, GEO.bn);
+            hipLaunchKernelGGL((gemm_kernel<GEO.bm, GEO.bn, BMODE, OMODE, false, true, WGM, GEO.threads, false, true>),
+                               dim3(static_cast<unsigned>(ceil_div(args.M, GEO.bm) * tn)), dim3(GEO.threads), 0,
+                               stream, args, static_cast<int>(tn), StreamK{});
+            return;
+        }
+    }
     const int64_t tiles_n = ceil_div(args.N, GEO.bn);
     const int64_t tiles = ceil_div(args.M, GEO.bm) * tiles_n;
     const int64_t steps = args.K / (DIRECT ? BKD : BK);
@@ -970,6 +986,7 @@ void launch_direct(const GemmArgs& args, void* workspace, hipStream_t stream) {
 
 template <GemmOut OMODE>
 void launch_int4(const GemmArgs& args, void* workspace, hipStream_t stream) {
+    if (args.b_tiled && (OMODE != GemmOut::kLoss || !direct_ok(args))) return;   // caller checks: see launch_gemm
     if (direct_ok(args))
         launch_direct<GemmB::kInt4, OMODE>(args, workspace, stream);
     else
@@ -980,6 +997,13 @@ void launch_int4(const GemmArgs& args, void* workspace, hipStream_t stream) {
 
 int64_t gemm_tile_count(int64_t M, int64_t N) { return tiles_of(kNarrowTile, M, N); }
 
+bool gemm_tiled_ok(int64_t K, int group_size) {
+    GemmArgs a;
+    a.K = K;
+    a.group_size = group_size;
+    return K % BKD == 0 && direct_ok(a);
+}
+
 size_t gemm_workspace_bytes(int64_t M, int64_t N) {
     (void)M;
     (void)N;
@@ -988,6 +1012,8 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N) {
 
 awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t stream, void* workspace) {
     if (args.M == 0 || args.N == 0) return AWQ_OK;
+    // tiled B: the loss form on the direct core only
+    if (args.b_tiled && (b != GemmB::kInt4 || out != GemmOut::kLoss || !direct_ok(args))) return AWQ_ERR_CONFIG;
     if (b == GemmB::kInt8) {
         // W8 B: the direct form only, fp16 output
         if (!direct_ok(args) || out != GemmOut::kF16) return AWQ_ERR_CONFIG;

@@ -48,7 +48,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict_
                                                        int64_t n_words, int64_t words_per_row,
                                                        uint32_t* __restrict__ qweight,
                                                        half_t* __restrict__ scales,
-                                                       half_t* __restrict__ zeros, Clip clip) {
+                                                       half_t* __restrict__ zeros, Clip clip,
+                                                       int64_t tiled_nk) {
     constexpr int kLanes = G / 8;  // threads per group: 4 .. 64 (G = 32 .. 512)
     constexpr float kQ = static_cast<float>((1 << BITS) - 1);            // 15 or 255
     constexpr float kSymQ = static_cast<float>((1 << (BITS - 1)) - 1);   // 7 or 127
@@ -166,7 +167,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict_
         uint32_t packed = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) packed |= code[j] << (4 * j);
-        qweight[t] = packed;
+        if (tiled_nk == 0) {
+            qweight[t] = packed;
+        } else {
+            // tiled order of the searches' loss GEMM: word c of row n goes to
+            // lane (c / 4 % 2) * 32 + n % 32 of the 1 KB piece of 32-row group
+            // n / 32 and 64-k step c / 8, at word c % 4 of the lane's 16 bytes
+            const int64_t n = t / words_per_row, c = t - n * words_per_row;
+            qweight[(((n >> 5) * tiled_nk + (c >> 3)) * 64 + ((c >> 2) & 1) * 32 + (n & 31)) * 4 + (c & 3)] = packed;
+        }
     } else {
         const uint2 packed = make_uint2(code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
                                         code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24));
@@ -181,32 +190,38 @@ __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict_
 
 template <int G, bool SYM, bool CLIP, int BITS>
 void launch_g(const half_t* w, const float* channel_scale, int64_t n_words, int64_t words_per_row,
-              uint32_t* qweight, half_t* scales, half_t* zeros, Clip clip, hipStream_t stream) {
+              uint32_t* qweight, half_t* scales, half_t* zeros, Clip clip, hipStream_t stream,
+              int64_t tiled_nk) {
     const int threads = 256;
     const int64_t blocks = ceil_div(n_words, threads);
     hipLaunchKernelGGL((quantize_kernel<G, SYM, CLIP, BITS>), dim3(static_cast<unsigned>(blocks)), dim3(threads), 0,
-                       stream, w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip);
+                       stream, w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, tiled_nk);
 }
 
 template <bool SYM, bool CLIP, int BITS>
 void launch_sym(const half_t* w, const float* channel_scale, int64_t n_words, int64_t words_per_row,
                 int group_size, uint32_t* qweight, half_t* scales, half_t* zeros, Clip clip,
-                hipStream_t stream) {
+                hipStream_t stream, int64_t tiled_nk) {
     switch (group_size) {
         case 32:
-            launch_g<32, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            launch_g<32, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip,
+                                      stream, tiled_nk);
             break;
         case 64:
-            launch_g<64, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            launch_g<64, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip,
+                                      stream, tiled_nk);
             break;
         case 128:
-            launch_g<128, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            launch_g<128, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip,
+                                      stream, tiled_nk);
             break;
         case 256:
-            launch_g<256, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            launch_g<256, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip,
+                                      stream, tiled_nk);
             break;
         default:
-            launch_g<512, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip, stream);
+            launch_g<512, SYM, CLIP, BITS>(w, channel_scale, n_words, words_per_row, qweight, scales, zeros, clip,
+                                      stream, tiled_nk);
             break;
     }
 }
@@ -214,19 +229,19 @@ void launch_sym(const half_t* w, const float* channel_scale, int64_t n_words, in
 template <int BITS>
 void launch_bits(const half_t* w, const float* channel_scale, int64_t n_words, int64_t words_per_row,
                  int group_size, bool symmetric, bool c, uint32_t* qweight, half_t* scales, half_t* zeros,
-                 Clip clip, hipStream_t stream) {
+                 Clip clip, hipStream_t stream, int64_t tiled_nk) {
     if (symmetric && c)
         launch_sym<true, true, BITS>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros,
-                                     clip, stream);
+                                     clip, stream, tiled_nk);
     else if (symmetric)
         launch_sym<true, false, BITS>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros,
-                                      clip, stream);
+                                      clip, stream, tiled_nk);
     else if (c)
         launch_sym<false, true, BITS>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales, zeros,
-                                      clip, stream);
+                                      clip, stream, tiled_nk);
     else
         launch_sym<false, false, BITS>(w, channel_scale, n_words, words_per_row, group_size, qweight, scales,
-                                       zeros, clip, stream);
+                                       zeros, clip, stream, tiled_nk);
 }
 
 }  // namespace
@@ -235,7 +250,7 @@ bool clip_fraction_ok(double p) { return p >= 0.0 && p < 0.25; }
 
 awq_status launch_quantize(const half_t* w, const float* channel_scale, int64_t N, int64_t K,
                            int group_size, bool symmetric, double clip_fraction, uint32_t* qweight,
-                           half_t* scales, half_t* zeros, hipStream_t stream, int bits) {
+                           half_t* scales, half_t* zeros, hipStream_t stream, int bits, bool tiled) {
     const int64_t words_per_row = K / 8;
     const int64_t n_words = N * words_per_row;
     if (n_words == 0) return AWQ_OK;
@@ -245,12 +260,15 @@ awq_status launch_quantize(const half_t* w, const float* channel_scale, int64_t 
     clip.i = static_cast<int>(std::floor(h));
     clip.f = static_cast<float>(h - clip.i);
     const bool c = clip_fraction > 0.0;
+    // the tiled order is for INT4 words whose rows are whole 64-k steps
+    if (tiled && (bits != 4 || K % 64 != 0)) return AWQ_ERR_CONFIG;
+    const int64_t tiled_nk = tiled ? K / 64 : 0;
     if (bits == 8)
         launch_bits<8>(w, channel_scale, n_words, words_per_row, group_size, symmetric, c, qweight, scales, zeros,
-                       clip, stream);
+                       clip, stream, tiled_nk);
     else
         launch_bits<4>(w, channel_scale, n_words, words_per_row, group_size, symmetric, c, qweight, scales, zeros,
-                       clip, stream);
+                       clip, stream, tiled_nk);
     return last_launch_status();
 }
 
