@@ -153,15 +153,22 @@ def _carve(buf, off, arr, dtype):
 
 
 def _place(x, qs, gap):
-    """x and each layer's (qweight, scales, zeros) carved from one buffer,
-    layer j starting at byte j * gap (gap 0: packed one after another)."""
+    """x and each layer's (qweight, scales, zeros) carved from one buffer:
+    x and layer 0 first, layers 1.. from byte `gap` on (gap 0: all packed
+    one after another)."""
     step = lambda n: (n + 255) // 256 * 256
     sizes = [sum(step(a.nbytes) for a in q) for q in qs]
-    total = step(x.nbytes) + sum(max(gap, sz) for sz in sizes) + 256
-    buf = torch.empty(total, dtype=torch.uint8, device="cuda")
+    head = step(x.nbytes) + sizes[0]
+    total = max(head, gap) + sum(sizes[1:]) + 256
+    try:
+        buf = torch.empty(total, dtype=torch.uint8, device="cuda")
+    except RuntimeError as e:   # a box without that much free device memory
+        pytest.skip(f"could not allocate {total} bytes: {e}")
     xd = _carve(buf, 0, x, torch.float16)
     off, layers = step(x.nbytes), []
-    for q, sz in zip(qs, sizes):
+    for j, q in enumerate(qs):
+        if j == 1:
+            off = max(off, gap)
         o = off
         qw = _carve(buf, o, q[0].view(np.int32), torch.int32)
         o += step(q[0].nbytes)
@@ -169,8 +176,12 @@ def _place(x, qs, gap):
         o += step(q[1].nbytes)
         zr = _carve(buf, o, q[2], torch.float16)
         layers.append((qw, sc, zr))
-        off += max(gap, sz)
+        off += sizes[j]
     return buf, xd, layers
+
+
+# Layers past 64 GiB of the lowest tensor take the full-pointer entries
+FAR = 65 << 30
 
 
 def _span(ts):
@@ -182,18 +193,18 @@ def _span(ts):
 @pytest.mark.parametrize("Ns", [(4096, 4096, 4096), (11008, 11008)], ids=["qkv", "gate_up"])
 def test_grouped_both_argument_forms(Ns, M):
     """One-shot grouped launches pass every early pointer as a 32-bit offset
-    from the lowest when x and all layers' weights, scales and zero-points
-    lie within 4 GB of it, and as full pointers otherwise. The same layers
-    placed both ways (carved from one buffer, packed or 4.5 GiB apart) give
-    the same bits, equal to each layer's own awq_gemm."""
+    (16-byte units) from the lowest when x and all layers' weights, scales
+    and zero-points lie within 64 GiB of it, and as full pointers otherwise.
+    The same layers placed both ways (carved from one buffer, packed or
+    65 GiB apart) give the same bits, equal to each layer's own awq_gemm."""
     K, G = 4096, 128
     x, qs = layers_of(Ns, K, M, G, 5)
     results = []
-    for gap in (0, 4608 << 20):
+    for gap in (0, FAR):
         buf, xd, layers = _place(x, qs, gap)
         span = _span([xd] + [t for d in layers for t in d])
         say("grouped argument forms: gap", gap, "span", span)
-        assert (span < (1 << 32)) == (gap == 0)
+        assert (span < (1 << 36)) == (gap == 0)
         outs = [torch.empty((M, N), dtype=torch.float16, device="cuda") for N in Ns]
         awq.awq_gemm_grouped(xd, layers, G, outs=outs)
         singles = [awq.awq_gemm(xd, *d, G) for d in layers]
@@ -211,15 +222,16 @@ def test_grouped_both_argument_forms(Ns, M):
 @pytest.mark.parametrize("Ns", [(4096, 4096, 4096), (11008, 11008)], ids=["qkv", "gate_up"])
 def test_grouped_column_tiles_both_argument_forms(Ns, M):
     """The grouped column-tile launch (3 <= M <= 32) has the same two
-    argument forms: 32-bit offsets from the lowest tensor when a launch's
-    tensors lie within 4 GB, full pointers otherwise. The same layers placed
-    both ways give the same bits, and each layer meets the linear bar."""
+    argument forms: 32-bit offsets (16-byte units) from the lowest tensor
+    when a launch's tensors lie within 64 GiB, full pointers otherwise. The
+    same layers placed both ways give the same bits, and each layer meets
+    the linear bar."""
     K, G = 4096, 128
     x, qs = layers_of(Ns, K, M, G, 6)
     results = []
-    for gap in (0, 4608 << 20):
+    for gap in (0, FAR):
         buf, xd, layers = _place(x, qs, gap)
-        assert (_span([xd] + [t for d in layers for t in d]) < (1 << 32)) == (gap == 0)
+        assert (_span([xd] + [t for d in layers for t in d]) < (1 << 36)) == (gap == 0)
         outs = [torch.empty((M, N), dtype=torch.float16, device="cuda") for N in Ns]
         awq.awq_gemm_grouped(xd, layers, G, outs=outs)
         torch.cuda.synchronize()

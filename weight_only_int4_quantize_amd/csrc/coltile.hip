@@ -352,8 +352,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ct_wave
 }
 
 // Two or three layers whose tensors (x, and each layer's packed weights,
-// scales and zero-points) lie within 4 GB of the lowest of them: those ten
-// pointers go as 32-bit byte offsets from that base and the sizes in two
+// scales and zero-points) lie within 64 GB of the lowest of them: those ten
+// pointers go as 32-bit offsets from that base in 16-byte units (each is
+// 16-byte aligned) and the sizes in two
 // dwords (mk = M | (K / 32) << 6 | n2 << 18, n01 = n0 | n1 << 16; M <= 32,
 // K / 32 < 4096, n2 < 16384, n0 and n1 < 65536), so every argument a wave
 // needs before its stores is in the 14 preloaded argument dwords; the
@@ -384,10 +385,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ct_wave
     half_t* y = in2 ? tail.y[NL > 2 ? 2 : 0] : in1 ? tail.y[1] : tail.y[0];
     const int n = in2 ? n2 : in1 ? n1 : n0;
     const int f = in2 ? f2 : in1 ? f1 : 0;
-    coltile_body<XR, WPL, NW, DEPTH, CT>(reinterpret_cast<const half_t*>(base + ox),
-                                         reinterpret_cast<const uint32_t*>(base + oq),
-                                         reinterpret_cast<const half_t*>(base + os),
-                                         reinterpret_cast<const half_t*>(base + oz), y, M, n, K, b - f);
+    auto at = [&](uint32_t off) { return base + (static_cast<uint64_t>(off) << 4); };
+    coltile_body<XR, WPL, NW, DEPTH, CT>(reinterpret_cast<const half_t*>(at(ox)),
+                                         reinterpret_cast<const uint32_t*>(at(oq)),
+                                         reinterpret_cast<const half_t*>(at(os)),
+                                         reinterpret_cast<const half_t*>(at(oz)), y, M, n, K, b - f);
 }
 
 // rows of x a launch stages: M rounded up to 4, 8, 16 or 32
@@ -520,21 +522,22 @@ awq_status launch_ct(const half_t* x, const CtTarget& tg, int M, int N, int K, h
     }
     const GemvLayers& lys = *tg.layers;
     if (lys.n == 2 || lys.n == 3) {
-        // the packed-offset entry when every early pointer is within 4 GB of
-        // the lowest and the sizes fit their fields
+        // the packed-offset entry when every early pointer is 16-byte aligned,
+        // within 64 GB of the lowest, and the sizes fit their fields
         const void* ptrs[10] = {x, lys.qweight[0], lys.qweight[1], lys.scales[0], lys.scales[1], lys.zeros[0],
                                 lys.zeros[1], lys.n > 2 ? lys.qweight[2] : lys.qweight[0],
                                 lys.n > 2 ? lys.scales[2] : lys.scales[0], lys.n > 2 ? lys.zeros[2] : lys.zeros[0]};
-        uintptr_t lo = UINTPTR_MAX, hi = 0;
+        uintptr_t lo = UINTPTR_MAX, hi = 0, bits = 0;
         for (const void* p : ptrs) {
             lo = std::min(lo, reinterpret_cast<uintptr_t>(p));
             hi = std::max(hi, reinterpret_cast<uintptr_t>(p));
+            bits |= reinterpret_cast<uintptr_t>(p);
         }
         const int rows0 = lys.row0[1] - lys.row0[0], rows1 = lys.row0[2] - lys.row0[1];
         const int rows2 = lys.n > 2 ? lys.row0[3] - lys.row0[2] : 0;
-        if (hi - lo < (uintptr_t{1} << 32) && M <= 32 && (K >> 5) < 4096 && rows0 < 65536 && rows1 < 65536 &&
+        if ((bits & 15) == 0 && (hi - lo) >> 4 < (uintptr_t{1} << 32) && M <= 32 && (K >> 5) < 4096 && rows0 < 65536 && rows1 < 65536 &&
             rows2 < 16384) {
-            auto off = [&](const void* p) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) - lo); };
+            auto off = [&](const void* p) { return static_cast<uint32_t>((reinterpret_cast<uintptr_t>(p) - lo) >> 4); };
             const uint32_t mk = static_cast<uint32_t>(M) | (static_cast<uint32_t>(K >> 5) << 6) |
                                 (static_cast<uint32_t>(rows2) << 18);
             const uint32_t n01 = static_cast<uint32_t>(rows0) | (static_cast<uint32_t>(rows1) << 16);

@@ -571,15 +571,15 @@ __global__ __launch_bounds__(NW * 64) void gemv_grouped_kernel(const half_t* __r
 }
 
 // One-shot grouped launches of 2 or 3 layers whose tensors (x, and each
-// layer's packed weights, scales and zero-points) all lie within 4 GB of the
+// layer's packed weights, scales and zero-points) all lie within 64 GB of the
 // lowest of them: every pointer the waves need before their first dot is a
-// 32-bit byte offset from that base, and with the sizes packed in two dwords
-// the whole set fits in the 14 preloaded argument dwords. No wave then waits
-// on a kernel-argument load until its outputs are stored (the output
-// pointers follow as an aggregate). nb1 = N | b1 << 16, b2k = b2 |
-// (K / 32) << 16 | (log2 G - 5) << 28 (N < 65536, K / 32 < 4096). The one-
-// shot launch shape gives every wave at most one row set, so the grid size
-// follows from N.
+// 32-bit offset from that base in 16-byte units (every such pointer is
+// 16-byte aligned), and with the sizes packed in two dwords the whole set
+// fits in the 14 preloaded argument dwords. No wave then waits on a
+// kernel-argument load until its outputs are stored (the output pointers
+// follow as an aggregate). nb1 = N | b1 << 16, b2k = b2 | (K / 32) << 16 |
+// (log2 G - 5) << 28 (N < 65536, K / 32 < 4096). The one-shot launch shape
+// gives every wave at most one row set, so the grid size follows from N.
 template <int NL>
 struct GemvOutTail {
     half_t* y[NL];
@@ -593,16 +593,17 @@ __global__ __launch_bounds__(NW * 64) void gemv_grouped_packed_kernel(
     const int K = static_cast<int>((b2k >> 16) & 0xFFFu) * 32;
     const int log2g = static_cast<int>(b2k >> 28) + 5;
     const int nblocks = ((N + RPW - 1) / RPW + NW - 1) / NW;
-    const GemvLayerTable L{reinterpret_cast<const uint32_t*>(base + oq0), reinterpret_cast<const uint32_t*>(base + oq1),
-                           NL > 2 ? reinterpret_cast<const uint32_t*>(base + oq2) : nullptr, nullptr,
-                           reinterpret_cast<const half_t*>(base + os0), reinterpret_cast<const half_t*>(base + os1),
-                           NL > 2 ? reinterpret_cast<const half_t*>(base + os2) : nullptr, nullptr,
-                           reinterpret_cast<const half_t*>(base + oz0), reinterpret_cast<const half_t*>(base + oz1),
-                           NL > 2 ? reinterpret_cast<const half_t*>(base + oz2) : nullptr, nullptr,
+    auto at = [&](uint32_t off) { return base + (static_cast<uint64_t>(off) << 4); };
+    const GemvLayerTable L{reinterpret_cast<const uint32_t*>(at(oq0)), reinterpret_cast<const uint32_t*>(at(oq1)),
+                           NL > 2 ? reinterpret_cast<const uint32_t*>(at(oq2)) : nullptr, nullptr,
+                           reinterpret_cast<const half_t*>(at(os0)), reinterpret_cast<const half_t*>(at(os1)),
+                           NL > 2 ? reinterpret_cast<const half_t*>(at(os2)) : nullptr, nullptr,
+                           reinterpret_cast<const half_t*>(at(oz0)), reinterpret_cast<const half_t*>(at(oz1)),
+                           NL > 2 ? reinterpret_cast<const half_t*>(at(oz2)) : nullptr, nullptr,
                            tail.y[0], tail.y[1], NL > 2 ? tail.y[NL > 2 ? 2 : 0] : nullptr, nullptr,
                            static_cast<int>(nb1 >> 16), NL > 2 ? static_cast<int>(b2k & 0xFFFFu) : INT32_MAX,
                            INT32_MAX};
-    gemv_body<BITS, MT, RPW, CPL, DEPTH, true, NW, NL>(reinterpret_cast<const half_t*>(base + ox), nullptr, nullptr,
+    gemv_body<BITS, MT, RPW, CPL, DEPTH, true, NW, NL>(reinterpret_cast<const half_t*>(at(ox)), nullptr, nullptr,
                                                         nullptr, nullptr, N, K, log2g, 1, nblocks, L);
 }
 
@@ -707,21 +708,22 @@ awq_status launch_t(const half_t* x, const GemvTarget<NL>& tg, int64_t N, int64_
     if constexpr (NL > 0) {
         const GemvLayerTable& T = tg.L;
         if constexpr (ONESHOT && (NL == 2 || NL == 3)) {
-            // the packed-offset entry when every early pointer is within 4 GB
-            // of the lowest and the sizes fit their fields
+            // the packed-offset entry when every early pointer is 16-byte
+            // aligned, within 64 GB of the lowest, and the sizes fit their fields
             const void* ptrs[10] = {x, T.q0, T.q1, T.s0, T.s1, T.z0, T.z1, NL > 2 ? T.q2 : T.q0,
                                     NL > 2 ? T.s2 : T.s0, NL > 2 ? T.z2 : T.z0};
-            uintptr_t lo = UINTPTR_MAX, hi = 0;
+            uintptr_t lo = UINTPTR_MAX, hi = 0, bits = 0;
             for (const void* p : ptrs) {
                 lo = std::min(lo, reinterpret_cast<uintptr_t>(p));
                 hi = std::max(hi, reinterpret_cast<uintptr_t>(p));
+                bits |= reinterpret_cast<uintptr_t>(p);
             }
             const int64_t nsets = ceil_div(N, RPW);
-            if (hi - lo < (uintptr_t{1} << 32) && N < 65536 && (K >> 5) < 4096 && log2g >= 5 && log2g < 21 &&
+            if ((bits & 15) == 0 && (hi - lo) >> 4 < (uintptr_t{1} << 32) && N < 65536 && (K >> 5) < 4096 && log2g >= 5 && log2g < 21 &&
                 blocks == ceil_div(nsets, NW) && max_sets == 1) {
                 const char* base = reinterpret_cast<const char*>(lo);
                 auto off = [&](const void* p) {
-                    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) - lo);
+                    return static_cast<uint32_t>((reinterpret_cast<uintptr_t>(p) - lo) >> 4);
                 };
                 static bool packed_attr_set = false;
                 if (!packed_attr_set) {
