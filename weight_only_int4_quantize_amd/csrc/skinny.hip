@@ -115,15 +115,21 @@ constexpr int kSkSZ = 32;               // (scale, zero) pairs per thread at mos
 __host__ __device__ constexpr int sk_depth(int mb, int wpl) { return (mb <= 2 && wpl <= 4) ? 8 : 4; }
 constexpr int kSkSZForm[3] = {4, 8, 32};
 
+// msp = M | splits << 7 | phase_groups << 16 (M < 128, splits < 512,
+// phase_groups < 65536): with it every argument the waves need before the
+// fixup is within the 14 preloaded argument dwords (the partial and counter
+// pointers, used last, follow)
 template <int MB, int WPL, int FORM>
 __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(const half_t* __restrict__ x,
                                                               const uint32_t* __restrict__ qweight,
                                                               const half_t* __restrict__ scales,
                                                               const half_t* __restrict__ zeros,
-                                                              half_t* __restrict__ y, int M, int N, int K,
-                                                              int splits, int phase_groups,
+                                                              half_t* __restrict__ y, int N, int K, uint32_t msp,
                                                               float* __restrict__ partials,
                                                               int* __restrict__ counters) {
+    const int M = static_cast<int>(msp & 127u);
+    const int splits = static_cast<int>((msp >> 7) & 511u);
+    const int phase_groups = static_cast<int>(msp >> 16);
     constexpr int G = WPL * 32;
     constexpr int MP = 16 * MB;                          // padded rows
     constexpr int kSkDepth = sk_depth(MB, WPL);
@@ -471,9 +477,13 @@ awq_status launch_form(const half_t* x, const uint32_t* qweight, const half_t* s
             return AWQ_ERR_HIP;
         attr_set = true;
     }
+    if (M >= 128 || splits >= 512 || pg >= 65536) return AWQ_ERR_SHAPE;   // the packed msp fields
     const int64_t blocks = sk_tiles(N) * splits;
     hipLaunchKernelGGL((skinny_kernel<MB, WPL, FORM>), dim3(static_cast<unsigned>(blocks)), dim3(kSkThreads), lds,
-                       stream, x, qweight, scales, zeros, y, M, N, K, splits, pg, partials, counters);
+                       stream, x, qweight, scales, zeros, y, N, K,
+                       static_cast<uint32_t>(M) | (static_cast<uint32_t>(splits) << 7) |
+                           (static_cast<uint32_t>(pg) << 16),
+                       partials, counters);
     return last_launch_status();
 }
 
