@@ -999,7 +999,7 @@ def summarize_counters(dirs, manifest_path, out_path, commands):
     with open(manifest_path) as f:
         text = f.read()
     manifest = json.loads([ln for ln in text.splitlines() if ln.startswith('{"manifest"')][-1])["manifest"]
-    match = {"copy": ("copy", "Copy"), "gemv": ("gemv_kernel", "gemv_grouped_kernel", "skinny_kernel"),
+    match = {"copy": ("copy", "Copy"), "gemv": ("gemv_kernel", "gemv_grouped_kernel", "gemv_grouped_packed_kernel", "skinny_kernel"),
              "gemm": ("gemm_kernel", "skinny_kernel")}
     out = [dict(g, avg={}) for g in manifest]
     for d in dirs:                     # one counter pass (one run of the same launches) per directory
