@@ -813,15 +813,29 @@ awq_status launch_m(const half_t* x, const GemvTarget<NL>& tg, int64_t N, int64_
     const int64_t x_lds = static_cast<int64_t>(gemv_lds_bytes(MT, K, BITS));
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kGemvBlocksPerCu, max_shared_bytes() / (x_lds + 2048)));
     const int64_t blocks = per_cu * cu_count();
-    // Staged (scale, zero) pairs (SZL) at M = 2, and at M = 1 on rows of 5
-    // items and more. Measured against per-chunk pairs (us, graph-timed,
-    // weights rotated, one process; outputs bit-identical): M = 2 4096 x 11008
-    // 9.37 -> 8.95, 8192 x 28672 27.26 -> 26.59; M = 1 8192 x 28672 23.76 ->
-    // 23.43 (G = 64: 24.88 -> 24.53). Shorter rows at M = 1 lose to the
-    // staging ahead of the first item: 4096 x 11008 6.69 -> 6.85, 13824 x
-    // 5120 10.68 -> 10.83, 11008 x 8192 10.29 -> 10.45.
-    const bool szl = NL == 0 && MT <= 2 && per_cu == 1 && (MT == 2 || kbs >= 5);
-    if (MT >= 2 || kbs > 3) {
+    // Rows per wave. Two rows per item share every x read from LDS, and a
+    // wave's two rows are in flight together; one row per wave balances
+    // better when it gives the busiest wave fewer rows (5120 rows over 2048
+    // waves: 3 rows against 2 sets of 2). Measured in one process (us,
+    // graph-timed, weights rotated, outputs bit-identical), two rows against
+    // one: M = 1 5120 x 13824 11.84 -> 9.94, 6144 x 16384 12.96 -> 11.29;
+    // M = 2 5120 x 13824 15.22 -> 13.10; with equal busiest waves two rows
+    // stay ahead or level: M = 2 8192 x 28672 26.55 against 28.68, 11008 x
+    // 8192 12.54 against 13.04, M = 1 2560 x 28672 (G = 64) 11.38 against
+    // 12.43. At M >= 3 two rows always.
+    const int64_t waves = blocks * 8;
+    const bool one_row = MT == 1 ? (kbs <= 3 || ceil_div(N, waves) < 2 * ceil_div(ceil_div(N, 2), waves))
+                                 : MT == 2 && ceil_div(N, waves) < 2 * ceil_div(ceil_div(N, 2), waves);
+    // Staged (scale, zero) pairs (SZL): at M = 1 on rows of 5 items and
+    // more, and at M = 2 with two rows per wave. Measured against per-chunk
+    // pairs (us, as above): M = 2 4096 x 11008 9.37 -> 8.95, 8192 x 28672
+    // 27.26 -> 26.59; M = 1 8192 x 28672 23.76 -> 23.43 (G = 64: 24.88 ->
+    // 24.53). Shorter rows at M = 1 lose to the staging ahead of the first
+    // item: 4096 x 11008 6.69 -> 6.85, 13824 x 5120 10.68 -> 10.83, 11008 x
+    // 8192 10.29 -> 10.45; so does one row per wave at M = 2 (5120 x 13824
+    // 13.10 -> 13.30, 13824 x 5120 13.84 -> 14.48).
+    const bool szl = NL == 0 && MT <= 2 && per_cu == 1 && (MT == 1 ? kbs >= 5 : !one_row);
+    if (!one_row) {
         if constexpr (NL == 0 && MT <= 2)
             if (szl && gemv_szl_lds_bytes<BITS, MT, 2, 8>(N, K, log2g, blocks) != 0)
                 return launch_t<BITS, MT, 2, 2, 2, false, 8, NL, true>(x, tg, N, K, log2g, blocks, stream);
