@@ -483,9 +483,11 @@ awq_status awq_scale_search(const void* w_f16, const void* x_f16, int64_t N, int
         if ((st = launch_quantize(w, L.s, N, K, group_size, false, 0.0, L.qweight, L.scales, L.zeros, s, 4,
                                   tiled)) != AWQ_OK)
             return st;
-        if ((st = launch_divide_columns(x, L.s, T, K, L.xs, s)) != AWQ_OK) return st;
-        if ((st = output_loss(L.xs, L.qweight, L.scales, L.zeros, T, N, K, group_size, L.yref, L.tile_partials,
-                              L.losses + i, s, tiled)) != AWQ_OK)
+        // s = 1 exactly at alpha = 0, where x / s is x itself, bit for bit
+        const bool identity = grid[i] == 0.0;
+        if (!identity && (st = launch_divide_columns(x, L.s, T, K, L.xs, s)) != AWQ_OK) return st;
+        if ((st = output_loss(identity ? x : L.xs, L.qweight, L.scales, L.zeros, T, N, K, group_size, L.yref,
+                              L.tile_partials, L.losses + i, s, tiled)) != AWQ_OK)
             return st;
     }
     if (hipMemcpyAsync(losses, L.losses, sizeof(double) * n_alpha, hipMemcpyDeviceToHost, s) != hipSuccess)

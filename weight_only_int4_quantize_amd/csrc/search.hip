@@ -73,7 +73,9 @@ __global__ __launch_bounds__(256) void pow_scales_kernel(const double* __restric
                                                          double alpha, float* __restrict__ s) {
     const int64_t k = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (k >= K) return;
-    s[k] = static_cast<float>(pow(m[k], alpha));
+    // alpha = 0 gives exactly 1 (the identity the search relies on to
+    // skip x / s there)
+    s[k] = alpha == 0.0 ? 1.0f : static_cast<float>(pow(m[k], alpha));
 }
 
 __global__ __launch_bounds__(256) void divide_columns_kernel(const half_t* __restrict__ x,
