@@ -37,6 +37,10 @@ struct Carve {
     }
 };
 
+// Halves of the reference's tiled copy of W: whole 64-k steps take it, other
+// K none (the reference then reads W in place).
+size_t reference_tiled_halves(int64_t N, int64_t K) { return gemm_ref_tiled_ok(K) ? tiled_fp16_halves(N, K) : 0; }
+
 // Lays out the scale-search workspace; with base == nullptr it only sizes it.
 struct SearchLayout {
     double* m = nullptr;
@@ -46,6 +50,7 @@ struct SearchLayout {
     half_t* scales = nullptr;
     half_t* zeros = nullptr;
     half_t* xs = nullptr;
+    half_t* wt = nullptr;   // W in the reference's tiled order (whole 64-k steps only)
     float* yref = nullptr;
     double* tile_partials = nullptr;
     double* losses = nullptr;
@@ -60,6 +65,7 @@ struct SearchLayout {
         scales = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         xs = c.take<half_t>(static_cast<size_t>(T) * K);
+        wt = c.take<half_t>(reference_tiled_halves(N, K));
         yref = c.take<float>(static_cast<size_t>(ref_tiled_floats(T, N)));
         tile_partials = c.take<double>(gemm_tile_count(T, N) + kLossSumBlocks);
         losses = c.take<double>(n_alpha);
@@ -76,6 +82,7 @@ struct SalientLayout {
     half_t* scales = nullptr;
     half_t* zeros = nullptr;
     half_t* w_sal = nullptr;
+    half_t* wt = nullptr;   // W in the reference's tiled order (whole 64-k steps only)
     float* yref = nullptr;
     double* tile_partials = nullptr;
     double* losses = nullptr;
@@ -90,6 +97,7 @@ struct SalientLayout {
         scales = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         w_sal = c.take<half_t>(static_cast<size_t>(std::max(n_sal, 1)) * N);
+        wt = c.take<half_t>(reference_tiled_halves(N, K));
         yref = c.take<float>(static_cast<size_t>(ref_tiled_floats(T, N)));
         tile_partials = c.take<double>(gemm_tile_count(T, N) + kLossSumBlocks);
         losses = c.take<double>(2);
@@ -106,6 +114,7 @@ struct ClipLayout {
     half_t* scales = nullptr;
     half_t* zeros = nullptr;
     half_t* xs = nullptr;           // x / s, only with channel scales
+    half_t* wt = nullptr;           // W in the reference's tiled order (whole 64-k steps only)
     float* yref = nullptr;
     double* tile_partials = nullptr;
     double* losses = nullptr;
@@ -117,6 +126,7 @@ struct ClipLayout {
         scales = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         zeros = c.take<half_t>(static_cast<size_t>(N) * (K / G));
         if (scaled) xs = c.take<half_t>(static_cast<size_t>(T) * K);
+        wt = c.take<half_t>(reference_tiled_halves(N, K));
         yref = c.take<float>(static_cast<size_t>(ref_tiled_floats(T, N)));
         tile_partials = c.take<double>(gemm_tile_count(T, N) + kLossSumBlocks);
         losses = c.take<double>(n);
@@ -125,9 +135,11 @@ struct ClipLayout {
 };
 
 // Y = x . W^T in fp32 (fp16 MFMA, fp32 accumulation), the unquantized
-// reference of the searches, written in the tiled layout of ref_offset.
+// reference of the searches, written in the tiled layout of ref_offset. With
+// K whole 64-k steps W is first copied into wt in the GEMM's tiled B order
+// (each wave's B of a step one contiguous piece); the products are the same.
 awq_status reference_output(const half_t* x, const half_t* w, int64_t T, int64_t N, int64_t K, int G, float* y,
-                            hipStream_t s) {
+                            half_t* wt, hipStream_t s) {
     GemmArgs ref;
     ref.a = x;
     ref.w = w;
@@ -136,6 +148,12 @@ awq_status reference_output(const half_t* x, const half_t* w, int64_t T, int64_t
     ref.N = N;
     ref.K = K;
     ref.y32 = y;
+    if (reference_tiled_halves(N, K) != 0 && T != 0 && N != 0) {
+        const awq_status st = launch_tile_fp16_b(w, N, K, wt, s);
+        if (st != AWQ_OK) return st;
+        ref.w = wt;
+        ref.b_tiled = true;
+    }
     return launch_gemm(ref, GemmB::kF16, GemmOut::kF32, s);
 }
 
@@ -477,7 +495,7 @@ awq_status awq_scale_search(const void* w_f16, const void* x_f16, int64_t N, int
     // m = mean |x| per input channel
     if ((st = launch_absmean(x, T, K, L.m, L.abs_partials, s)) != AWQ_OK) return st;
     // reference output W . x^T, once, in fp32
-    if ((st = reference_output(x, w, T, N, K, group_size, L.yref, s)) != AWQ_OK) return st;
+    if ((st = reference_output(x, w, T, N, K, group_size, L.yref, L.wt, s)) != AWQ_OK) return st;
     for (int i = 0; i < n_alpha; ++i) {
         if ((st = launch_pow_scales(L.m, K, grid[i], L.s, s)) != AWQ_OK) return st;
         if ((st = launch_quantize(w, L.s, N, K, group_size, false, 0.0, L.qweight, L.scales, L.zeros, s, 4,
@@ -529,7 +547,7 @@ awq_status awq_clip_search(const void* w_f16, const void* x_f16, const float* ch
     const half_t* w = static_cast<const half_t*>(w_f16);
     const half_t* x = static_cast<const half_t*>(x_f16);
 
-    if ((st = reference_output(x, w, T, N, K, group_size, L.yref, s)) != AWQ_OK) return st;
+    if ((st = reference_output(x, w, T, N, K, group_size, L.yref, L.wt, s)) != AWQ_OK) return st;
     const half_t* xa = x;
     if (channel_scale != nullptr) {
         if ((st = launch_divide_columns(x, channel_scale, T, K, L.xs, s)) != AWQ_OK) return st;
@@ -635,7 +653,7 @@ awq_status awq_salient_loss(const void* w_f16, const void* x_f16, int64_t N, int
     if ((st = launch_absmean(x, T, K, L.m, L.abs_partials, s)) != AWQ_OK) return st;
     if ((st = launch_select_salient(L.m, K, n_salient, L.idx, s)) != AWQ_OK) return st;
     // reference W . x^T; the plain quantizer's loss
-    if ((st = reference_output(x, w, T, N, K, group_size, L.yref, s)) != AWQ_OK) return st;
+    if ((st = reference_output(x, w, T, N, K, group_size, L.yref, L.wt, s)) != AWQ_OK) return st;
     if ((st = launch_quantize(w, nullptr, N, K, group_size, sym, 0.0, L.qweight, L.scales, L.zeros, s)) != AWQ_OK)
         return st;
     if ((st = output_loss(x, L.qweight, L.scales, L.zeros, T, N, K, group_size, L.yref, L.tile_partials, L.losses,

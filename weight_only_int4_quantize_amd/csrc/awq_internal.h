@@ -125,9 +125,21 @@ struct GemmArgs {
     // kLoss with INT4 B: qweight in the tiled order (word c of row n at
     // ((n / 32 * K / 64 + c / 8) * 64 + (c / 4 % 2) * 32 + n % 32) * 4 + c % 4,
     // ceil(N / 32) * 32 rows), so a wave's packed words of one 64-k step
-    // are one contiguous 1 KB piece
+    // are one contiguous 1 KB piece. kF32 with fp16 B: w in the tiled order
+    // of launch_tile_fp16_b.
     bool b_tiled = false;
 };
+// fp16 W[N, K] (K a multiple of 64) into the fp16-B reference's tiled order:
+// 16-byte piece (lane, v) of 32-row group g and 64-k step t, at piece index
+// ((g * K / 64 + t) * 4 + v) * 64 + lane, holds W[32 g + lane % 32]
+// [64 t + 32 (lane / 32) + 8 v .. + 7]; rows past N are zero. wt holds
+// tiled_fp16_halves(N, K) halves.
+inline size_t tiled_fp16_halves(int64_t N, int64_t K) {
+    return static_cast<size_t>((N + 31) / 32 * 32) * static_cast<size_t>(K);
+}
+awq_status launch_tile_fp16_b(const half_t* w, int64_t N, int64_t K, half_t* wt, hipStream_t stream);
+// whether the fp16-B reference takes tiled B at this K
+bool gemm_ref_tiled_ok(int64_t K);
 // whether the loss form takes tiled B at this K and group size
 bool gemm_tiled_ok(int64_t K, int group_size);
 // words of a tiled packed-weight buffer of N rows

@@ -230,9 +230,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* p, int byt
 // dequantizes them there; only A goes through LDS.
 //
 // WGM: waves along M (the 4 waves form WGM x 4 / WGM).
-// TILEDB (INT4, the direct form's one-column-tile waves): B in the tiled
-// order of GemmArgs::b_tiled, so each wave's load of a K step is one
-// contiguous 1 KB piece (8 cache lines against 32 for the row-major words).
+// TILEDB (INT4 or fp16 B, the direct form's one-column-tile waves): B in
+// the tiled order of GemmArgs::b_tiled, so each wave's load of a K step is
+// one contiguous 1 KB piece per 16 bytes a lane takes (8 cache lines against
+// 32 for row-major B).
 template <int BM, int BN, GemmB BMODE, GemmOut OMODE, bool STREAMK, bool DIRECT, int WGM = 2, int NT = kThreads,
           bool SKDMA = false, bool TILEDB = false>
 __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int tiles_n, StreamK sk) {
@@ -256,7 +257,8 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
     static_assert(DIRECT || !INT4 || B_WORDS == 2, "int4 B staging: 2 words (16 codes) per thread");
     static_assert(DIRECT || INT4 || B_VECS >= 1, "fp16 B staging");
     static_assert(DIRECT || BMODE != GemmB::kInt8, "W8 B runs the direct form only");
-    static_assert(!TILEDB || (DIRECT && BMODE == GemmB::kInt4 && TN == 1 && WTN == 32), "tiled B: INT4, 32-column waves");
+    static_assert(!TILEDB || (DIRECT && BMODE != GemmB::kInt8 && TN == 1 && WTN == 32),
+                  "tiled B: INT4 or fp16, 32-column waves");
     constexpr int LDS_A = DIRECT ? BM * BKD : BM * LDK;
     constexpr int LDS_B = DIRECT ? 8 : BN * LDK;
 
@@ -452,7 +454,7 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
         for (int j = 0; j < TN; ++j) {
             const int n = min(wn + j * 32 + lcol, cols_b - 1);
             // tiled: piece (group (wn + 32 j) / 32, step 0), lane's 16 bytes
-            b_off[j] = TILEDB ? (wn + j * 32) / 32 * nk * 1024 + lane * 16 : n * (K * BITS / 8) + lh * (4 * BITS);
+            b_off[j] = TILEDB ? (wn + j * 32) / 32 * nk * (1024 * BW) + lane * 16 : n * (K * BITS / 8) + lh * (4 * BITS);
             sz_off[j] = n * ngroups * 2;
         }
         auto s_bits_at = [&](int j, int gg) {
@@ -482,12 +484,12 @@ __global__ __launch_bounds__(NT, 512 / NT) void gemm_kernel(GemmArgs args, int t
             for (int i = 0; i < AV; ++i) areg[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off[i], k0, 0);
         };
         auto load_b = [&](u32x4 (&dst)[TN][BW], int kt) {
-            const int w0 = uniform(min(kt, last) * (TILEDB ? 1024 : BKD * BITS / 8));
+            const int w0 = uniform(min(kt, last) * (TILEDB ? 1024 * BW : BKD * BITS / 8));
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int v = 0; v < BW; ++v)
-                    dst[j][v] = __builtin_amdgcn_raw_buffer_load_b128(b_rs, b_off[j] + 16 * v, w0, 0);
+                    dst[j][v] = __builtin_amdgcn_raw_buffer_load_b128(b_rs, b_off[j] + (TILEDB ? 1024 : 16) * v, w0, 0);
         };
         auto store_a = [&](half_t* as) {
 #pragma unroll
@@ -890,7 +892,8 @@ size_t partials_bytes() {
 
 template <const Geometry& GEO, GemmB BMODE, GemmOut OMODE, bool DIRECT, int WGM = 2>
 void launch_cfg(const GemmArgs& args, void* workspace, hipStream_t stream) {
-    if constexpr (OMODE == GemmOut::kLoss && DIRECT && BMODE == GemmB::kInt4 && GEO.bn == 128) {
+    if constexpr (((OMODE == GemmOut::kLoss && BMODE == GemmB::kInt4) ||
+                   (OMODE == GemmOut::kF32 && BMODE == GemmB::kF16)) && DIRECT && GEO.bn == 128) {
         if (args.b_tiled) {
             const int64_t tn = ceil_div(args.N, GEO.bn);
             hipLaunchKernelGGL((gemm_kernel<GEO.bm, GEO.bn, BMODE, OMODE, false, true, WGM, GEO.threads, false, true>),
@@ -1004,6 +1007,37 @@ bool gemm_tiled_ok(int64_t K, int group_size) {
     return K % BKD == 0 && direct_ok(a);
 }
 
+namespace {
+
+// One thread per 16-byte piece of the tiled fp16 B (the order of
+// launch_tile_fp16_b); a block's 256 pieces are one 32-row, 64-k block of W,
+// so its reads are whole 128-byte rows.
+__global__ __launch_bounds__(256) void tile_fp16_b_kernel(const half_t* __restrict__ w, int64_t N, int64_t K,
+                                                          int64_t pieces, half_t* __restrict__ wt) {
+    const int64_t p = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (p >= pieces) return;
+    const int64_t nk = K / BKD;
+    const int lane = static_cast<int>(p & 63), v = static_cast<int>((p >> 6) & 3);
+    const int64_t t = (p >> 8) % nk, g = (p >> 8) / nk;
+    const int64_t row = g * 32 + (lane & 31), col = t * BKD + (lane >> 5) * 32 + v * 8;
+    u32x4 piece = {0u, 0u, 0u, 0u};
+    if (row < N) piece = *reinterpret_cast<const u32x4*>(w + row * K + col);
+    *reinterpret_cast<u32x4*>(wt + p * 8) = piece;
+}
+
+}  // namespace
+
+bool gemm_ref_tiled_ok(int64_t K) { return K % BKD == 0 && K * kBM * 2 < (int64_t{1} << 31); }
+
+awq_status launch_tile_fp16_b(const half_t* w, int64_t N, int64_t K, half_t* wt, hipStream_t stream) {
+    if (!gemm_ref_tiled_ok(K)) return AWQ_ERR_SHAPE;
+    const int64_t pieces = static_cast<int64_t>(tiled_fp16_halves(N, K) / 8);
+    if (pieces == 0) return AWQ_OK;
+    hipLaunchKernelGGL(tile_fp16_b_kernel, dim3(static_cast<unsigned>(ceil_div(pieces, 256))), dim3(256), 0, stream,
+                       w, N, K, pieces, wt);
+    return last_launch_status();
+}
+
 size_t gemm_workspace_bytes(int64_t M, int64_t N) {
     (void)M;
     (void)N;
@@ -1012,8 +1046,11 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N) {
 
 awq_status launch_gemm(const GemmArgs& args, GemmB b, GemmOut out, hipStream_t stream, void* workspace) {
     if (args.M == 0 || args.N == 0) return AWQ_OK;
-    // tiled B: the loss form on the direct core only
-    if (args.b_tiled && (b != GemmB::kInt4 || out != GemmOut::kLoss || !direct_ok(args))) return AWQ_ERR_CONFIG;
+    // tiled B: the loss form (INT4 B) and the fp16-B reference, both on the
+    // direct core only
+    if (args.b_tiled && !((b == GemmB::kInt4 && out == GemmOut::kLoss && direct_ok(args)) ||
+                          (b == GemmB::kF16 && out == GemmOut::kF32 && gemm_ref_tiled_ok(args.K))))
+        return AWQ_ERR_CONFIG;
     if (b == GemmB::kInt8) {
         // W8 B: the direct form only, fp16 output
         if (!direct_ok(args) || out != GemmOut::kF16) return AWQ_ERR_CONFIG;
