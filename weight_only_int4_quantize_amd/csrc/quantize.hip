@@ -14,9 +14,10 @@
 // Layout: one thread per 8 consecutive k of one row (one packed INT4 word, or
 // two W8 words), read as one 16-byte load. The G/8 threads of a group are adjacent lanes of one
 // wavefront, so a wave streams 64 * 16 B = 1 KB of contiguous weights and the
-// group min/max is a 3- or 4-step butterfly over lanes. Every arithmetic step
-// is IEEE fp32 (correctly rounded divide, round-half-to-even rint) so the
-// codes, scales and zeros are bit-identical to a plain fp32 evaluation.
+// group min/max is a 3- or 4-step butterfly over lanes. Codes, scales and
+// zeros are bit-identical to a plain IEEE fp32 evaluation (correctly rounded
+// divides, round-half-to-even rint), reached without the divide sequence
+// where that is provably the same (div_const, rint_plus).
 #include <cmath>
 
 #include "awq_internal.h"
@@ -27,6 +28,34 @@ namespace {
 #pragma clang fp contract(off)
 
 constexpr float kTieBand = 1e-3f;   // |frac(v / s) - 1/2| below which the exact divide decides
+constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23: in its binade the last bits are the integer part
+
+// a / d as the IEEE quotient for the constant divisors d = 7, 15, 127 and
+// 255: q0 = a * RN(1/d) is off by at most one unit; the fma gives its
+// residual a - q0 d exactly, and one more fma rounds q0 + residual / d. For
+// these four d this equals the correctly rounded a / d at every fp32
+// significand (checked exhaustively; a scale by 2^k scales every step
+// exactly), for any normal a.
+__device__ __forceinline__ float div_const(float a, float d) {
+    const float y = 1.0f / d;   // folded at compile time
+    const float q0 = a * y;
+    return fmaf(fmaf(-q0, d, a), y, q0);
+}
+
+// base + rint(x / s) with the correctly rounded quotient, base an integer in
+// [kMagic, kMagic + 255]. t = fma(x, 1/s, base) rounds the exact x * (1/s)
+// + base once, onto the integers of kMagic's binade; 1/s comes from the
+// hardware reciprocal (error within one unit, so x * (1/s) is within 2^-23
+// |x / s| of x / s). For |x / s| <= 1024 that, with the quotient's own
+// rounding, is under 2e-4, so unless x * (1/s) lies within kTieBand of a
+// half-way point (its distance from t - base is exact through the second
+// fma) both round to the same integer; near one the IEEE divide decides.
+// Beyond 1024 both clamp to the same end code (bits of t are monotonic).
+__device__ __forceinline__ float rint_plus(float x, float s, float rinv, float base) {
+    const float t = fmaf(x, rinv, base);
+    if (fabsf(fmaf(x, rinv, -(t - base))) > 0.5f - kTieBand) return base + rintf(x / s);
+    return t;
+}
 
 // Clip step (xxmr.cn §1.5: cut the extreme p of the values at both ends
 // before the scale is taken). The bounds are the p and 1 - p quantiles of the
@@ -132,41 +161,60 @@ __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict_
         }
     }
 
-    float s32, z;
+    // s = range / kQ (or max|w| / kSymQ) as the IEEE quotient, taken as the
+    // product by the rounded reciprocal of the constant plus one fma
+    // correction of its residual (div_const).
+    float s32;
     if constexpr (SYM) {
-        const float a = fmaxf(fmaxf(-lo, hi), kRangeFloor);   // max |w| (lo <= hi)
-        s32 = a / kSymQ;                                      // IEEE divide
+        s32 = div_const(fmaxf(fmaxf(-lo, hi), kRangeFloor), kSymQ);   // max |w| (lo <= hi)
     } else {
-        const float range = fmaxf(hi - lo, kRangeFloor);
-        s32 = range / kQ;                                     // IEEE divide
+        s32 = div_const(fmaxf(hi - lo, kRangeFloor), kQ);
     }
+    // the fp32 quotient is rounded to fp16 on its own (an empty asm keeps the
+    // last fma and the conversion from merging into one fp16-rounding fma)
+    asm volatile("" : "+v"(s32));
     const half_t s16 = static_cast<half_t>(s32);              // round-to-nearest-even
     const float sf = static_cast<float>(s16);
-    if constexpr (SYM) {
-        z = kSymZero;
-    } else {
-        const int zi = static_cast<int>(fminf(fmaxf(rintf(-lo / sf), 0.0f), kQ));
-        z = static_cast<float>(zi);
-    }
+    const float rinv = __builtin_amdgcn_rcpf(sf);
 
-    // rint(v / s) with the correctly rounded quotient, taken through the
-    // product v * (1 / s): its error is below 1e-4 for |v / s| <= 256 (the
-    // reciprocal and the product each round once), so away from the
-    // half-way points it rounds to the same integer. Within kTieBand of a
-    // half-way point the exact IEEE divide decides.
-    const float rinv = 1.0f / sf;
-    uint32_t code[8];
+    // base = kMagic + z: every code is then one fma, t = v * (1 / s) + base,
+    // whose bits are bits(kMagic) + rint(v / s) + z (see rint_plus)
+    float base;
+    if constexpr (SYM) {
+        base = kMagic + kSymZero;
+    } else {
+        const float tz = rint_plus(-lo, sf, rinv, kMagic);
+        base = fminf(fmaxf(tz, kMagic), kMagic + kQ);          // z = clamp(rint(-lo / s), 0, kQ)
+    }
+    const float z = base - kMagic;
+
+    float tq[8];
+    bool near_tie = false;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const float r = v[j] * rinv;
-        float q = rintf(r);
-        if (fabsf(fabsf(r - q) - 0.5f) < kTieBand) q = rintf(v[j] / sf);
-        code[j] = static_cast<uint32_t>(fminf(fmaxf(q + z, 0.0f), kQ));
+        tq[j] = fmaf(v[j], rinv, base);
+        near_tie |= fabsf(fmaf(v[j], rinv, -(tq[j] - base))) > 0.5f - kTieBand;
     }
-    if constexpr (BITS == 4) {
-        uint32_t packed = 0;
+    if (near_tie) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) packed |= code[j] << (4 * j);
+        for (int j = 0; j < 8; ++j) tq[j] = rint_plus(v[j], sf, rinv, base);
+    }
+    // clamp(rint(v / s) + z, 0, kQ) + bits(kMagic), on the bits as signed
+    // integers (order-preserving for the values that can occur, and any
+    // value below kMagic clamps to code 0)
+    constexpr int kLoBits = 0x4B400000;   // bits of kMagic
+    int32_t code[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int32_t b = __builtin_bit_cast(int32_t, tq[j]);
+        code[j] = min(max(b, kLoBits), kLoBits + static_cast<int32_t>(kQ));
+    }
+    // each code still carries bits(kMagic); the shifted sums drop it at once
+    // (arithmetic mod 2^32)
+    if constexpr (BITS == 4) {
+        uint32_t packed = 0u - static_cast<uint32_t>(kLoBits) * 0x11111111u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) packed += static_cast<uint32_t>(code[j]) << (4 * j);
         if (tiled_nk == 0) {
             qweight[t] = packed;
         } else {
@@ -177,8 +225,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(const half_t* __restrict_
             qweight[(((n >> 5) * tiled_nk + (c >> 3)) * 64 + ((c >> 2) & 1) * 32 + (n & 31)) * 4 + (c & 3)] = packed;
         }
     } else {
-        const uint2 packed = make_uint2(code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
-                                        code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24));
+        uint32_t lo_w = 0u - static_cast<uint32_t>(kLoBits) * 0x01010101u, hi_w = lo_w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            lo_w += static_cast<uint32_t>(code[j]) << (8 * j);
+            hi_w += static_cast<uint32_t>(code[4 + j]) << (8 * j);
+        }
+        const uint2 packed = make_uint2(lo_w, hi_w);
         reinterpret_cast<uint2*>(qweight)[t] = packed;
     }
     if ((t & (kLanes - 1)) == 0) {
