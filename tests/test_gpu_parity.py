@@ -475,6 +475,19 @@ def test_scale_search_ragged_rows():
     check_search(losses, best, host(s), losses_o, best_o, s_o, losses_f)
 
 
+def test_scale_search_k_not_whole_64_steps():
+    """K = 800 at G = 32: K is not a whole number of 64-k steps, so the
+    reference GEMM reads W in place (no tiled copy) and the loss GEMM takes
+    its older form; N = 200 ends in a partial 32-row group."""
+    lay = synth.make_layer(200, 800, 256, seed=[111], w_std=0.02)
+    w, x = lay["w"], lay["x"]
+    losses_o, best_o, s_o = oracle.scale_search(w, x, 32)
+    losses_f, _, _ = oracle.scale_search(w, x, 32, f16_activations=True)
+    losses, best, s = awq.awq_scale_search(dev(w), dev(x), 32)
+    say("search K=800: gpu", best, "oracle", best_o)
+    check_search(losses, best, host(s), losses_o, best_o, s_o, losses_f)
+
+
 def check_choice(losses, best, losses_o, best_o, losses_f16=None):
     """Losses within LOSS_RTOL_EXACT of the exact oracle (and LOSS_RTOL_F16
     of its fp16-activation form, when given); the same index as the oracle
