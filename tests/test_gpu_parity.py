@@ -178,6 +178,32 @@ def test_quantize_special_groups_bit_exact():
     assert oracle.unpack_codes(qw, K)[0, 2] == 12
 
 
+def extreme_quotient_rows(K):
+    """Groups whose quotients w / s leave the range where a code is decided:
+    constant groups far from zero (|w / s| near 3e7 at the floor scale, past
+    2^24 and below zero once the rounding offset 1.5 * 2^23 is added),
+    narrow groups offset to +-1000 and to the top of the fp16 range, and a
+    group of tiny values with one large outlier."""
+    k = np.arange(K)
+    return np.array([
+        [20.0] * K,
+        [-20.0] * K,
+        list(1000.0 + 0.5 * (k % 2)),
+        list(-1000.0 - 0.5 * (k % 2)),
+        list(60000.0 + 32.0 * (k % 2)),
+        [-0.001] * (K - 1) + [30000.0],
+        [20.0] * (K // 2) + list(np.linspace(-1, 1, K // 2)),
+    ], dtype=np.float16)
+
+
+def test_quantize_extreme_quotients_bit_exact():
+    """Codes clamp to the end values exactly where the plain fp32 map does,
+    also where the quotient is far outside [-1024, 1024]."""
+    w = extreme_quotient_rows(128)
+    for G in (32, 64, 128):
+        assert_quant_equal(gpu_quantize(w, G), oracle.quantize(w, G))
+
+
 def test_quantize_round_before_zero_point_tie():
     """w / s one fp32 step above a tie (made through the channel scale): the
     code is 9, not 8."""

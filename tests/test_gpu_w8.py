@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 import weight_only_int4_quantize_amd as awq  # noqa: E402
 
-from test_gpu_parity import assert_linear_close, dev, host, say  # noqa: E402
+from test_gpu_parity import assert_linear_close, dev, extreme_quotient_rows, host, say  # noqa: E402
 
 
 def gpu_quantize_w8(w16, G, cs=None, symmetric=False):
@@ -88,3 +88,12 @@ def test_w8_one_hot_is_exact_on_gemv():
     y = host(awq.awq_gemm_w8(dev(x), dev(qw.view(np.int32)), dev(sc), dev(zr), G, path=awq.PATH_GEMV))
     exp = w_hat[:, ks].T.astype(np.float16)
     assert np.array_equal(y.view(np.uint16), exp.view(np.uint16))
+
+
+@pytest.mark.parametrize("symmetric", [False, True])
+def test_quantize_w8_extreme_quotients_bit_exact(symmetric):
+    """The 255-level map on groups whose quotients are far from the codes
+    (constant, offset and outlier groups)."""
+    w = extreme_quotient_rows(128)
+    for G in (64, 128):   # W8 group sizes start at 64
+        assert_equal_bits(gpu_quantize_w8(w, G, symmetric=symmetric), oracle.quantize_w8(w, G, symmetric=symmetric))
