@@ -34,8 +34,8 @@ constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23: in its binade the last bi
 // 255: q0 = a * RN(1/d) is off by at most one unit; the fma gives its
 // residual a - q0 d exactly, and one more fma rounds q0 + residual / d. For
 // these four d this equals the correctly rounded a / d at every fp32
-// significand (checked exhaustively; a scale by 2^k scales every step
-// exactly), for any normal a.
+// significand (checked exhaustively in tests/test_quantize_arith_host.py; a
+// scale by 2^k scales every step exactly), for any normal a.
 __device__ __forceinline__ float div_const(float a, float d) {
     const float y = 1.0f / d;   // folded at compile time
     const float q0 = a * y;
@@ -74,7 +74,8 @@ __device__ __forceinline__ T group_reduce(T x, Op op) {
 // rounding, is under 2e-4, so unless x * (1/s) lies within kTieBand of a
 // half-way point (its distance from t - base is exact through the second
 // fma) both round to the same integer; near one the IEEE divide decides.
-// Beyond 1024 both clamp to the same end code (bits of t are monotonic).
+// Beyond 1024 both clamp to the same end code: read as signed integers, the
+// bits of t keep the order of every t >= 0 and put every t < 0 below code 0.
 __device__ __forceinline__ float rint_plus(float x, float s, float rinv, float base) {
     const float t = fmaf(x, rinv, base);
     if (fabsf(fmaf(x, rinv, -(t - base))) > 0.5f - kTieBand) return base + rintf(x / s);
